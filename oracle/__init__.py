@@ -1,0 +1,16 @@
+"""Test infrastructure: the fp64 CPU oracle and its brute-force cross-check.
+
+Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may use this package.  It shares no code with the HIP
+library and never imports it.
+"""
+
+from .longformer_oracle import (  # noqa: F401
+    attention,
+    attention_bh,
+    attention_sampled,
+    global_set,
+    mask_count,
+    mask_rows,
+    window_member,
+)

@@ -1,0 +1,179 @@
+"""Plain fp64 CPU oracle for Longformer window + global sparse self-attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library and imports nothing from it.
+
+What it computes (per batch b and head h, with inputs widened to float64):
+
+* Key set of query i (the attention pattern):
+  - sliding / dilated window: keys j = i + m*dil for m in [-w, w], 0 <= j < L.
+    Page "基于自注意力机制的长文本建模算法：Longformer详解" (Longformer explained),
+    §2 "local sliding window" (w neighbours on each side, e.g. 512 each side)
+    and §2 "dilated sliding window" (positions i-d*w ... i-d, i, i+d ... i+d*w).
+  - global, symmetric: a global query attends to every position and every
+    query attends to every global key.  Same page §2 "global attention"; page
+    "基于Block-Sparse Attention的Longformer" (Block-Sparse Longformer) §2 and §4,
+    which state both directions.
+  - the union of these sets (each key counted once), Longformer explained §4
+    (the three patterns are combined in one attention).
+  - key padding: a padded key is never attended to (library convention; the
+    pages only truncate inputs).
+* Scores S = Q K^T / sqrt(d_h), masked entries set to -inf, row softmax, then
+  O = P V: the textbook scaled dot-product attention of page
+  "Reformer哈希：突破Transformer计算瓶颈的高效注意力机制详解" (Reformer hashing),
+  §"core principle", restricted to the key set above.
+* A query row whose key set is empty gives an all-zero output row.
+
+The mask is built explicitly as dense boolean rows (R rows x L keys at a time)
+directly from the set definitions above; no banding, tiling or online softmax.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ROW_BLOCK = 512
+
+
+def _as_f64(x) -> np.ndarray:
+    """Widen a numpy array or a CPU torch tensor (any float dtype) to float64."""
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu")
+        import torch  # local: torch is only needed when handed a tensor
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def global_set(global_idx) -> np.ndarray:
+    """The designated global positions as a sorted set (duplicates ignored)."""
+    if global_idx is None:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.asarray(global_idx, dtype=np.int64).reshape(-1))
+
+
+def window_member(i: np.ndarray, j: np.ndarray, w: int, dil: int) -> np.ndarray:
+    """True where key j lies in query i's (dilated) window: j = i + m*dil, |m| <= w.
+
+    Longformer explained §2: the window reaches w positions on each side, and a
+    dilation factor d spaces the attended positions d apart (i-d*w ... i+d*w).
+    """
+    diff = j - i
+    return (np.abs(diff) <= w * dil) & (diff % dil == 0)
+
+
+def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray) -> np.ndarray:
+    """Explicit boolean mask M[r, j] for the query rows ``rows`` over all L keys.
+
+    M[i, j] = not pad[j] and (i in G or j in G or j in window(i)).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(L, dtype=np.int64)[None, :]
+    i = rows[:, None]
+    is_global_key = np.zeros(L, dtype=bool)
+    is_global_key[G] = True
+    is_global_query = is_global_key[rows][:, None]
+    m = window_member(i, j, w, dil) | is_global_key[None, :] | is_global_query
+    if pad_row is not None:
+        m &= ~np.asarray(pad_row, dtype=bool)[None, :]
+    return m
+
+
+def _attention_rows(q, k, v, m):
+    """Masked softmax attention of the query rows in ``q`` against all keys.
+
+    q: [R, d], k, v: [L, d], m: [R, L] boolean.  Returns (O [R, d], P [R, L]).
+    """
+    d = q.shape[1]
+    s = (q @ k.T) / math.sqrt(d)
+    s = np.where(m, s, -np.inf)
+    row_max = s.max(axis=1, keepdims=True)
+    has_key = np.isfinite(row_max)
+    row_max = np.where(has_key, row_max, 0.0)
+    e = np.where(m, np.exp(s - row_max), 0.0)
+    denom = e.sum(axis=1, keepdims=True)
+    p = np.where(has_key, e / np.where(has_key, denom, 1.0), 0.0)
+    return p @ v, p
+
+
+def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=None,
+                 return_probs: bool = False):
+    """Oracle for one (batch, head) slice.
+
+    q, k, v: [L, d] arrays (widened to float64).  ``rows`` selects query rows
+    (default: all).  Returns O [len(rows), d] float64, and the attention
+    weights P [len(rows), L] when ``return_probs``.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    L = k.shape[0]
+    if w < 0 or dil < 1:
+        raise ValueError("need w >= 0 and dil >= 1")
+    G = global_set(global_idx)
+    if G.size and (G.min() < 0 or G.max() >= L):
+        raise ValueError("global index out of range")
+    rows = np.arange(L, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, q.shape[1]), dtype=np.float64)
+    probs = np.zeros((rows.size, L), dtype=np.float64) if return_probs else None
+    for s0 in range(0, rows.size, ROW_BLOCK):
+        blk = rows[s0:s0 + ROW_BLOCK]
+        m = mask_rows(L, w, dil, G, pad_row, blk)
+        o, p = _attention_rows(q[blk], k, v, m)
+        out[s0:s0 + blk.size] = o
+        if return_probs:
+            probs[s0:s0 + blk.size] = p
+    return (out, probs) if return_probs else out
+
+
+def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None):
+    """Oracle for the full [B, H, L, d] problem.  Returns float64 [B, H, L, d].
+
+    ``dil_per_head`` has one dilation per head (w is shared by all heads);
+    ``global_idx`` is one set shared by every sequence and head;
+    ``key_pad_mask`` is [B, L], nonzero meaning a padded key (or None).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, L, d = q.shape
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    if len(dil) != H:
+        raise ValueError("need one dilation per head")
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    out = np.zeros((B, H, L, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
+                                     None if pad is None else pad[b])
+    return out
+
+
+def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, samples):
+    """Oracle output rows for a list of (b, h, i) samples, computed one by one.
+
+    Used to check full-size runs where the whole oracle would be too slow.
+    Returns float64 [len(samples), d].
+    """
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    res = []
+    for b, h, i in samples:
+        o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
+                         None if pad is None else pad[b], rows=[i])
+        res.append(o[0])
+    return np.stack(res) if res else np.zeros((0, q.shape[-1]))
+
+
+def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1) -> int:
+    """Number of attended (query, key) pairs, summed over batch and heads: sum of M."""
+    G = global_set(global_idx)
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    total = 0
+    for b in range(B):
+        for d in dil:
+            for s0 in range(0, L, ROW_BLOCK):
+                rows = np.arange(s0, min(L, s0 + ROW_BLOCK))
+                total += int(mask_rows(L, w, d, G, None if pad is None else pad[b], rows).sum())
+    return total

@@ -1,0 +1,102 @@
+"""Host-side accounting of the attention pattern: attended-pair counts.
+
+The effective work of one forward is 4*d_h FLOP per attended (query, key) pair
+(d_h multiply-adds for q.k and d_h for p.v); exponentials and masked tile
+entries are not counted.  Pair counts follow the pattern's complexity
+statements: O(n*w) for the window and O(n*g) for globals (page
+"基于Block-Sparse Attention的Longformer" §3 and §4).
+
+Counts are formed without building the L x L mask: per residue class of the
+dilation, a prefix sum over unpadded keys gives each row's window count in
+O(1), and the few global keys are checked against the window directly.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass
+class PairCounts:
+    band: int  # non-global rows, keys in their window
+    global_col: int  # non-global rows, global keys outside their window
+    global_row: int  # global rows, every unpadded key
+
+    @property
+    def total(self) -> int:
+        return self.band + self.global_col + self.global_row
+
+    @property
+    def band_kernel(self) -> int:
+        """Pairs handled by the band kernel (window plus global-column fold)."""
+        return self.band + self.global_col
+
+
+def _unique_globals(global_idx, L):
+    if global_idx is None:
+        return np.zeros(0, dtype=np.int64)
+    g = np.unique(np.asarray(global_idx, dtype=np.int64).reshape(-1))
+    if g.size and (g[0] < 0 or g[-1] >= L):
+        raise ValueError("global index out of range")
+    return g
+
+
+def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray) -> PairCounts:
+    """Pair counts for one (sequence, head).  ``valid[j]`` is True for unpadded keys."""
+    is_g = np.zeros(L, dtype=bool)
+    is_g[G] = True
+    band = 0
+    gcol = 0
+    Gv = G[valid[G]] if G.size else G  # unpadded global keys
+    for r in range(min(dil, L)):
+        pos = np.arange(r, L, dil, dtype=np.int64)  # rows/keys of this residue class
+        n = pos.size
+        pref = np.concatenate([[0], np.cumsum(valid[pos].astype(np.int64))])
+        i = np.arange(n, dtype=np.int64)
+        lo = np.maximum(i - w, 0)
+        hi = np.minimum(i + w, n - 1)
+        win = pref[hi + 1] - pref[lo]
+        rows = ~is_g[pos]
+        band += int(win[rows].sum())
+        if Gv.size:
+            # globals inside row's window: same residue and |g' - i| <= w
+            same = Gv[(Gv % dil) == r]
+            gp = (same - r) // dil
+            inside = np.zeros(n, dtype=np.int64)
+            for g in gp:
+                inside[max(0, g - w):min(n, g + w + 1)] += 1
+            gcol += int((Gv.size - inside[rows]).sum())
+    grow = int(G.size) * int(valid.sum())
+    return PairCounts(band, gcol, grow)
+
+
+def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1) -> PairCounts:
+    """Attended pairs summed over B sequences and all heads.
+
+    ``key_pad_mask`` is an array-like [B, L] (nonzero = padded) or None.
+    """
+    G = _unique_globals(global_idx, L)
+    dils = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else (np.asarray(key_pad_mask) != 0)
+    if pad is not None:
+        B = pad.shape[0]
+    tot = PairCounts(0, 0, 0)
+    cache = {}
+    for b in range(B):
+        valid = np.ones(L, dtype=bool) if pad is None else ~pad[b]
+        key_b = b if pad is not None else 0
+        for dl in dils:
+            key = (key_b, dl)
+            if key not in cache:
+                cache[key] = count_pairs_bh(L, w, dl, G, valid)
+            c = cache[key]
+            tot.band += c.band
+            tot.global_col += c.global_col
+            tot.global_row += c.global_row
+    return tot
+
+
+def effective_flops(pairs: int, d: int = 64) -> float:
+    return 4.0 * d * pairs

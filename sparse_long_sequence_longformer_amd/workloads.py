@@ -1,0 +1,107 @@
+"""Seeded synthetic workloads for the Longformer attention forward.
+
+This module only draws inputs; it holds none of the attention arithmetic, so
+both the HIP path and the fp64 oracle can take their inputs from it.
+
+Recipe (fixed, shared by every consumer):
+  1. rng = numpy.random.default_rng(seed) with seed 0;
+  2. q, k, v drawn in that order as float32 standard normals of shape
+     (B, H, L, 64); optionally scaled (0.5 for the CLS workload);
+  3. bf16 workloads are rounded to bfloat16 by torch (round to nearest even);
+  4. random global positions use numpy.random.default_rng(1).choice(L, n, replace=False), sorted;
+  5. the key padding mask is pad[b, j] = (j >= length[b]) (uint8, 1 = padded).
+
+The five shapes follow the pages' workloads: hidden size 768 = 12 heads x 64
+(page "基于Block-Sparse Attention的Longformer" §6 example model), 4096-token
+documents and windows of 512 per side (page "基于自注意力机制的长文本建模算法：
+Longformer详解" §2, §9), a CLS-like single global token and a question-span of
+global tokens (same page §2 and §7), and 8-16 global tokens with windows of
+L/8..L/4 (page "Efficient Transformers: A Survey" commentary, §3.3).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    L: int
+    w: int
+    dil: tuple
+    dtype: str  # "f32" or "bf16"
+    globals_: tuple = ()
+    random_globals: int = 0  # if > 0, draw this many distinct positions with seed 1
+    lengths: tuple = ()  # true lengths per sequence (empty: no padding)
+    scale: float = 1.0
+    seed: int = 0
+    d: int = 64
+    desc: str = field(default="", compare=False)
+
+    def global_positions(self) -> list[int]:
+        if self.random_globals:
+            g = np.random.default_rng(1).choice(self.L, self.random_globals, replace=False)
+            return sorted(int(x) for x in g)
+        return list(self.globals_)
+
+    def pad_mask(self):
+        """uint8 [B, L] (1 = padded key) or None when every sequence is full."""
+        if not self.lengths:
+            return None
+        j = np.arange(self.L)[None, :]
+        lens = np.asarray(self.lengths)[:, None]
+        return (j >= lens).astype(np.uint8)
+
+    def dil_list(self) -> list[int]:
+        return list(self.dil)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload(
+        "tiny_f32", B=1, H=1, L=256, w=32, dil=(1,), dtype="f32",
+        desc="B=1 H=1 L=256 d=64 w=32 dil=1, no globals, no padding, fp32"),
+    "cls_4k": Workload(
+        "cls_4k", B=1, H=12, L=4096, w=256, dil=(1,) * 12, dtype="bf16", globals_=(0,), scale=0.5,
+        desc="B=1 H=12 L=4096 d=64 w=256 dil=1, global {0}, bf16 0.5*N(0,1)"),
+    "qa_4k": Workload(
+        "qa_4k", B=2, H=12, L=4096, w=512, dil=(1,) * 12, dtype="bf16", globals_=tuple(range(16)),
+        desc="B=2 H=12 L=4096 d=64 w=512 dil=1, globals 0..15, bf16 N(0,1)"),
+    "dilated_8k": Workload(
+        "dilated_8k", B=1, H=12, L=8192, w=128, dil=(1,) * 6 + (2,) * 6, dtype="bf16",
+        random_globals=8,
+        desc="B=1 H=12 L=8192 d=64 w=128 dil 1 (heads 0-5) / 2 (heads 6-11), 8 random globals, bf16"),
+    "padded_32k": Workload(
+        "padded_32k", B=4, H=16, L=32768, w=256, dil=(1,) * 16, dtype="bf16",
+        globals_=tuple(range(16)), lengths=(32768, 20000, 9000, 4096),
+        desc="B=4 H=16 L=32768 d=64 w=256 dil=1, globals 0..15, lengths 32768/20000/9000/4096, bf16"),
+}
+
+# The workload the throughput metric is quoted on (L=4096, w=512).
+HEADLINE = "qa_4k"
+
+
+def make_qkv(wl: Workload):
+    """Return (q, k, v) as CPU torch tensors of the workload's dtype."""
+    import torch
+
+    rng = np.random.default_rng(wl.seed)
+    shape = (wl.B, wl.H, wl.L, wl.d)
+    arrs = []
+    for _ in range(3):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        if wl.scale != 1.0:
+            a = a * np.float32(wl.scale)
+        arrs.append(a)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    return tuple(torch.from_numpy(a).to(tdt) for a in arrs)
+
+
+def make_custom(B, H, L, dtype="bf16", seed=0, scale=1.0, d=64):
+    """Seeded q, k, v of an arbitrary shape (same recipe as the named workloads)."""
+    wl = Workload("custom", B=B, H=H, L=L, w=0, dil=(1,) * H, dtype=dtype, seed=seed, scale=scale, d=d)
+    return make_qkv(wl)

@@ -1,0 +1,262 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+what the pages or the mathematics fix.  They are collected as tests by
+``test_oracle_pins.py`` and re-run against deliberately broken copies of the
+oracle by ``test_oracle_mutations.py`` (a pin set that cannot tell a broken
+oracle from the right one proves nothing).
+"""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import brute
+from oracle import longformer_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _textbook_attention(q, k, v):
+    """softmax(Q K^T / sqrt(d)) V by torch's CPU routine in float64 (page
+    "Reformer哈希" §"core principle" formula)."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x))[None, None] for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    return out[0, 0].numpy()
+
+
+def read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- brute force
+
+BRUTE_CASES = [
+    # (L, d, w, dil, globals, pad_len or pad pattern seed, seed)
+    (1, 8, 0, 1, [], None, 1),
+    (7, 8, 2, 1, [], None, 2),
+    (16, 8, 3, 2, [5], None, 3),
+    (24, 8, 4, 3, [0, 23, 7, 7], None, 4),
+    (33, 8, 5, 1, [2, 30], "rand", 5),
+    (40, 8, 2, 4, [9, 39, 13], "rand", 6),
+    (48, 8, 60, 1, [], None, 7),
+    (31, 8, 0, 2, [4, 4, 17], "rand", 8),
+    (20, 8, 3, 2, [1], "allbut", 9),
+    (12, 64, 2, 3, [11], "suffix", 10),
+]
+
+
+def _pad_for(kind, L, seed):
+    if kind is None:
+        return None
+    if kind == "rand":
+        return np.random.default_rng(100 + seed).random(L) < 0.3
+    if kind == "suffix":
+        return np.arange(L) >= (2 * L) // 3
+    if kind == "allbut":
+        p = np.ones(L, dtype=bool)
+        p[L // 2] = False
+        return p
+    raise ValueError(kind)
+
+
+def pin_brute_force():
+    """The oracle equals element-by-element enumeration with math.fsum (L <= 64)."""
+    for L, d, w, dil, G, padk, seed in BRUTE_CASES:
+        q, k, v = (_rand((L, d), seed * 3 + t) for t in range(3))
+        pad = _pad_for(padk, L, seed)
+        got = orc.attention_bh(q, k, v, w, dil, G, pad)
+        ref = np.array(brute.attention_bh(q.tolist(), k.tolist(), v.tolist(), w, dil, G,
+                                          None if pad is None else pad.tolist()))
+        err = np.abs(got - ref).max() if L else 0.0
+        assert err < 1e-12, f"brute force mismatch {err} for L={L} w={w} dil={dil} G={G}"
+
+
+def pin_pair_counts_brute():
+    """Mask sums equal the enumerated key-set sizes."""
+    for L, d, w, dil, G, padk, seed in BRUTE_CASES:
+        pad = _pad_for(padk, L, seed)
+        n_brute = brute.pair_count(L, w, dil, G, None if pad is None else pad.tolist())
+        n_orc = orc.mask_count(L, w, [dil], G, None if pad is None else pad[None, :])
+        assert n_brute == n_orc, (L, w, dil, G, n_brute, n_orc)
+
+
+# ---------------------------------------------------------- closed-form limits
+
+def pin_full_attention_limit():
+    """w >= L with dil = 1 is full attention: the textbook formula."""
+    for L, w, seed in [(64, 64, 11), (100, 1000, 12), (37, 36, 13)]:
+        q, k, v = (_rand((L, 64), seed * 3 + t) for t in range(3))
+        got = orc.attention_bh(q, k, v, w, 1)
+        ref = _textbook_attention(q, k, v)
+        assert np.abs(got - ref).max() < 1e-12
+
+
+def pin_all_global():
+    """Every position global is full attention, whatever the window."""
+    L = 50
+    q, k, v = (_rand((L, 32), 20 + t) for t in range(3))
+    for w, dil in [(0, 1), (3, 2)]:
+        got = orc.attention_bh(q, k, v, w, dil, list(range(L)))
+        assert np.abs(got - _textbook_attention(q, k, v)).max() < 1e-12
+
+
+def pin_w0_identity():
+    """w = 0, no globals, dil = 1, no padding: each query sees only itself, O = V exactly."""
+    L = 45
+    q, k, v = (_rand((L, 64), 30 + t) for t in range(3))
+    got = orc.attention_bh(q, k, v, 0, 1)
+    assert np.array_equal(got, v)
+
+
+def pin_constant_v():
+    """Constant V along the sequence gives that constant on every row with a key."""
+    L = 70
+    q, k = _rand((L, 16), 40), _rand((L, 16), 41)
+    row = _rand((16,), 42)
+    v = np.tile(row, (L, 1))
+    pad = np.zeros(L, dtype=bool)
+    pad[60:] = True
+    got = orc.attention_bh(q, k, v, 3, 2, [5, 66], pad)
+    assert np.abs(got - row[None, :]).max() < 1e-12
+
+
+def pin_rows_sum_to_one():
+    """Attention weights: each row sums to 1, is zero off the key set, and an empty
+    key set gives a zero row (output zero)."""
+    L = 60
+    q, k, v = (_rand((L, 16), 50 + t) for t in range(3))
+    pad = np.zeros(L, dtype=bool)
+    pad[10:30] = True  # rows 10..29 with w=2, dil=1 have every window key padded
+    G = [40]
+    o, p = orc.attention_bh(q, k, v, 2, 1, G, pad, return_probs=True)
+    s = p.sum(axis=1)
+    for i in range(L):
+        keys = brute.key_set(i, L, 2, 1, G, pad.tolist())
+        off = np.ones(L, dtype=bool)
+        off[keys] = False
+        assert np.all(p[i, off] == 0.0)
+        if keys:
+            assert abs(s[i] - 1.0) < 1e-12
+        else:
+            assert s[i] == 0.0 and np.all(o[i] == 0.0)
+    # with the global key padded as well, rows 12..27 have no key at all
+    pad2 = pad.copy()
+    pad2[40] = True
+    o2 = orc.attention_bh(q, k, v, 2, 1, G, pad2)
+    assert np.all(o2[12:28] == 0.0) and np.all(np.isfinite(o2))
+
+
+# ------------------------------------------------------------- reductions
+
+def pin_dilation_residues():
+    """With no globals or padding and dil | L, the dilated window on residue class r
+    is the plain window on the subsequence r, r+dil, ... (closed-form reduction)."""
+    L, dil, w = 48, 3, 4
+    q, k, v = (_rand((L, 16), 60 + t) for t in range(3))
+    got = orc.attention_bh(q, k, v, w, dil)
+    for r in range(dil):
+        sub = orc.attention_bh(q[r::dil], k[r::dil], v[r::dil], w, 1)
+        assert np.abs(got[r::dil] - sub).max() < 1e-12
+
+
+def pin_padding_truncation():
+    """Suffix padding: the rows before the true length equal the unpadded run on the
+    truncated sequence."""
+    L, n = 64, 41
+    q, k, v = (_rand((L, 16), 70 + t) for t in range(3))
+    pad = np.arange(L) >= n
+    G = [3, 20]
+    got = orc.attention_bh(q, k, v, 5, 2, G, pad)
+    ref = orc.attention_bh(q[:n], k[:n], v[:n], 5, 2, G)
+    assert np.abs(got[:n] - ref).max() < 1e-12
+
+
+def pin_duplicate_globals():
+    """Duplicated global indices are the same set (each key counted once)."""
+    L = 40
+    q, k, v = (_rand((L, 16), 80 + t) for t in range(3))
+    a = orc.attention_bh(q, k, v, 3, 1, [7, 7, 30, 7, 30])
+    b = orc.attention_bh(q, k, v, 3, 1, [30, 7])
+    assert np.abs(a - b).max() == 0.0
+
+
+def pin_global_in_window_counted_once():
+    """A global key inside a row's window enters that row's softmax once: compare one
+    row against its hand-listed key set."""
+    L = 30
+    q, k, v = (_rand((L, 8), 90 + t) for t in range(3))
+    i, G = 10, [12]
+    o = orc.attention_bh(q, k, v, 2, 1, G, rows=[i])[0]
+    keys = [8, 9, 10, 11, 12]  # window of 10 with w=2; the global 12 already inside it
+    s = np.array([q[i] @ k[j] for j in keys]) / math.sqrt(8)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    assert np.abs(o - p @ v[keys]).max() < 1e-12
+
+
+def pin_head_permutation():
+    """Heads are independent: permuting heads together with their dilations permutes
+    the outputs."""
+    B, H, L, d = 2, 3, 24, 8
+    q, k, v = (_rand((B, H, L, d), 100 + t) for t in range(3))
+    dil = [1, 2, 3]
+    pad = np.zeros((B, L), dtype=np.uint8)
+    pad[1, 18:] = 1
+    o = orc.attention(q, k, v, 2, dil, [4], pad)
+    perm = [2, 0, 1]
+    o2 = orc.attention(q[:, perm], k[:, perm], v[:, perm], 2, [dil[p] for p in perm], [4], pad)
+    assert np.abs(o2 - o[:, perm]).max() == 0.0
+
+
+# ------------------------------------------------------------- page values
+
+def pin_dense_counts_golden():
+    """The full-attention limit reproduces the dense counts the pages print."""
+    for L, printed, rel, *_ in read_table("dense_pair_counts.txt"):
+        L, printed, rel = int(L), float(printed), float(rel)
+        n = orc.mask_count(L, L, [1])
+        assert n == L * L
+        assert abs(n - printed) <= rel * printed + 0.5, (L, n, printed)
+
+
+def pin_window_example_golden():
+    """512 keys per side: interior rows see 1025 keys, edge rows are truncated."""
+    for L, w, dil, i, expect in read_table("window_example.txt"):
+        L, w, dil, i, expect = map(int, (L, w, dil, i, expect))
+        m = orc.mask_rows(L, w, dil, np.zeros(0, dtype=np.int64), None, np.array([i]))
+        assert int(m.sum()) == expect
+        assert len(brute.key_set(i, L, w, dil, [])) == expect
+
+
+ALL_PINS = [
+    pin_brute_force,
+    pin_pair_counts_brute,
+    pin_full_attention_limit,
+    pin_all_global,
+    pin_w0_identity,
+    pin_constant_v,
+    pin_rows_sum_to_one,
+    pin_dilation_residues,
+    pin_padding_truncation,
+    pin_duplicate_globals,
+    pin_global_in_window_counted_once,
+    pin_head_permutation,
+    pin_dense_counts_golden,
+    pin_window_example_golden,
+]

@@ -1,0 +1,142 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check the pins catch each one.
+
+Every mutant replaces one helper of ``oracle.longformer_oracle`` for the duration of
+a test; the brute-force enumerator, the textbook routine and the golden tables are
+untouched, so a pin that still passes against a mutant would be blind to that mistake.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import longformer_oracle as orc
+from tests import oracle_pins as P
+
+_orig_window = orc.window_member
+_orig_mask = orc.mask_rows
+_orig_rows = orc._attention_rows
+
+
+def _window_strict(i, j, w, dil):  # off by one at the window edge
+    diff = j - i
+    return (np.abs(diff) < w * dil) & (diff % dil == 0)
+
+
+def _window_no_lattice(i, j, w, dil):  # dilation span kept, spacing dropped
+    diff = j - i
+    return np.abs(diff) <= w * dil
+
+
+def _window_no_span(i, j, w, dil):  # spacing kept, span not stretched by dil
+    diff = j - i
+    return (np.abs(diff) <= w) & (diff % dil == 0)
+
+
+def _window_sign(i, j, w, dil):  # one-sided window (a causal reading)
+    diff = j - i
+    return (diff <= 0) & (-diff <= w * dil) & (diff % dil == 0)
+
+
+def _mask_rows_only(L, w, dil, G, pad_row, rows):  # global rows only, no global columns
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(L)[None, :]
+    isg = np.zeros(L, dtype=bool)
+    isg[G] = True
+    m = orc.window_member(rows[:, None], j, w, dil) | isg[rows][:, None]
+    if pad_row is not None:
+        m &= ~np.asarray(pad_row, dtype=bool)[None, :]
+    return m
+
+
+def _mask_cols_only(L, w, dil, G, pad_row, rows):  # global columns only, no global rows
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(L)[None, :]
+    isg = np.zeros(L, dtype=bool)
+    isg[G] = True
+    m = orc.window_member(rows[:, None], j, w, dil) | isg[None, :]
+    if pad_row is not None:
+        m &= ~np.asarray(pad_row, dtype=bool)[None, :]
+    return m
+
+
+def _mask_pad_queries(L, w, dil, G, pad_row, rows):  # padding applied to query rows
+    m = _orig_mask(L, w, dil, G, None, rows)
+    if pad_row is not None:
+        m &= ~np.asarray(pad_row, dtype=bool)[np.asarray(rows)][:, None]
+    return m
+
+
+def _mask_pad_ignored(L, w, dil, G, pad_row, rows):
+    return _orig_mask(L, w, dil, G, None, rows)
+
+
+def _rows_scale_d(q, k, v, m):  # 1/d instead of 1/sqrt(d)
+    return _orig_rows(q / math.sqrt(q.shape[1]), k, v, m)
+
+
+def _rows_transposed(q, k, v, m):  # S^T = K Q^T used where S = Q K^T was meant
+    d = q.shape[1]
+    if q.shape[0] != k.shape[0]:
+        raise ValueError("transposed scores need a square block")
+    s = np.where(m, (k @ q.T) / math.sqrt(d), -np.inf)
+    mx = np.max(s, axis=1, keepdims=True)
+    ok = np.isfinite(mx)
+    e = np.where(m, np.exp(s - np.where(ok, mx, 0.0)), 0.0)
+    den = e.sum(axis=1, keepdims=True)
+    p = np.where(ok, e / np.where(ok, den, 1.0), 0.0)
+    return p @ v, p
+
+
+def _rows_pk(q, k, v, m):  # weights applied to K instead of V
+    o, p = _orig_rows(q, k, v, m)
+    return p @ k, p
+
+
+def _rows_zero_fill(q, k, v, m):  # out-of-pattern scores left at 0 instead of excluded
+    d = q.shape[1]
+    s = np.where(m, (q @ k.T) / math.sqrt(d), 0.0)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ v, p
+
+
+def _rows_nan_empty(q, k, v, m):  # no guard for rows without keys
+    d = q.shape[1]
+    s = np.where(m, (q @ k.T) / math.sqrt(d), -np.inf)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+    return p @ v, p
+
+
+MUTANTS = {
+    "window_strict_edge": ("window_member", _window_strict),
+    "window_no_lattice": ("window_member", _window_no_lattice),
+    "window_span_not_dilated": ("window_member", _window_no_span),
+    "window_one_sided": ("window_member", _window_sign),
+    "global_rows_only": ("mask_rows", _mask_rows_only),
+    "global_cols_only": ("mask_rows", _mask_cols_only),
+    "pad_on_queries": ("mask_rows", _mask_pad_queries),
+    "pad_ignored": ("mask_rows", _mask_pad_ignored),
+    "scale_1_over_d": ("_attention_rows", _rows_scale_d),
+    "transposed_scores": ("_attention_rows", _rows_transposed),
+    "weights_times_k": ("_attention_rows", _rows_pk),
+    "zero_fill_softmax": ("_attention_rows", _rows_zero_fill),
+    "nan_empty_rows": ("_attention_rows", _rows_nan_empty),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin detects mutant {name}"
