@@ -1,0 +1,222 @@
+"""Throughput of the Longformer window + global attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qa_4k]
+
+One step = one forward pass (all kernels: window band with the global-column
+fold, global-row partials, log-sum-exp merge) over one batch of seeded synthetic
+input already resident in HBM.  The metric is effective TFLOP/s: 4*d_h FLOP per
+attended (query, key) pair, pairs counted exactly (window + globals after
+de-duplication and padding), divided by the wall time of the K timed steps.
+
+Prints one JSON line.  Also reported: the band kernel's own rate against the
+bf16 MFMA peak (HIP events around each launch, on the launch stream), and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense), HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+METRIC = "window+global attn fwd effective TFLOP/s and % bf16 MFMA peak, L=4096 w=512"
+KERNEL_SRC = os.path.join(ROOT, "sparse_long_sequence_longformer_amd", "csrc", "lf_attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "band_kernel_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def traffic_for(workload: str):
+    """HBM bytes per band-kernel launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_sha") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, G, pad, target_s):
+    """The fp64 oracle on whole (b, h) slices of the workload, one after another,
+    until about target_s seconds of CPU work; BLAS limited to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import longformer_oracle as orc
+    from sparse_long_sequence_longformer_amd import pattern
+
+    pad_np = None if pad is None else pad
+    pairs = 0
+    done = []
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(wl.B):
+            for h in range(wl.H):
+                orc.attention_bh(q[b, h], k[b, h], v[b, h], wl.w, wl.dil[h], G,
+                                 None if pad_np is None else pad_np[b])
+                pr = None if pad_np is None else pad_np[b:b + 1]
+                pairs += pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr).total
+                done.append((b, h))
+                if time.perf_counter() - t0 >= target_s:
+                    break
+            if time.perf_counter() - t0 >= target_s:
+                break
+    dt = time.perf_counter() - t0
+    return {
+        "value": 256.0 * pairs / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(done)} of {wl.B * wl.H} (batch, head) slices of {wl.name}, full rows, "
+                  f"{dt:.1f} s; same effective-FLOP count as the GPU value",
+        "seconds": round(dt, 3),
+        "pairs": pairs,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (batch, head) or by sequence, which this build does not implement)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_long_sequence_longformer_amd import binding, pattern, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    binding.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}))
+        return
+
+    name = args.workload or workloads.HEADLINE
+    wl = workloads.WORKLOADS[name]
+    q, k, v = workloads.make_qkv(wl)
+    G = wl.global_positions()
+    pad = wl.pad_mask()
+    pairs = pattern.count_pairs(wl.L, wl.w, wl.dil_list(), G, pad, B=wl.B)
+    flops = pattern.effective_flops(pairs.total)
+
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    padd = None if pad is None else torch.from_numpy(pad).to(dev)
+    out = torch.empty_like(qd)
+    handle = binding.LfAttn(wl.dtype)
+    dil = wl.dil_list()
+
+    def step():
+        binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # Per-kernel durations: HIP events recorded by the library around every launch
+    # on the same stream, over a second run of K steps.
+    handle.set_stage_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    st = handle.stage_times()
+    handle.set_stage_timing(False)
+    band_ms, band_n = st["band"]
+    band_avg_ms = band_ms / max(1, band_n)
+    band_flops = pattern.effective_flops(pairs.band_kernel)
+    achieved = band_flops / (band_avg_ms * 1e-3) / 1e12
+    traffic = traffic_for(name)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, no trained weights)",
+        "config": {
+            "workload": name,
+            "B": wl.B, "H": wl.H, "seq_len": wl.L, "d_h": wl.d, "w": wl.w,
+            "dil": sorted(set(dil)), "n_global": len(G),
+            "padded_lengths": list(wl.lengths) or None,
+            "global_batch": wl.B,
+            "parallelism": "single GPU",
+        },
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "attended_pairs": pairs.total,
+        "effective_flop_per_step": flops,
+        "stage_ms_avg": {k2: round(v2[0] / max(1, v2[1]), 6) for k2, v2 in st.items()},
+        "roofline": {
+            "kernel": "band_kernel<Bf16>" if wl.dtype == "bf16" else "band_kernel<F32>",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(band_avg_ms, 6),
+            "flop_per_launch": band_flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

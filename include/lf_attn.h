@@ -1,0 +1,128 @@
+/*
+ * lf_attn.h - C ABI of the Longformer window + global sparse self-attention
+ * forward for AMD MI355X (gfx950).  Library: liblfattn.so.
+ *
+ * The operation (one softmax per query over the union of its keys):
+ *
+ *   O[b,h,i,:] = sum_j P[i,j] V[b,h,j,:],
+ *   P[i,:]     = softmax_j( Q[b,h,i,:] . K[b,h,j,:] / sqrt(d_h) )  over j in keys(i),
+ *
+ *   keys(i) = all positions                        if i is global,
+ *           = { i + m*dil[h] : m = -w..w } ∩ [0,L) ∪ globals   otherwise,
+ *   minus every padded key; a query with no key gets an all-zero row.
+ *
+ * Sources: page "基于自注意力机制的长文本建模算法：Longformer详解" (Longformer
+ * explained) §2 (sliding window with w keys on each side, dilated window
+ * i-d*w .. i+d*w, global tokens that see every position) and §4 (the patterns
+ * combined into one attention, linear cost, banded matrix products); page
+ * "基于Block-Sparse Attention的Longformer" §2 and §4 (global tokens attend to
+ * all tokens and all tokens attend to them); page "Reformer哈希" §"core
+ * principle" (softmax(QK^T/sqrt(d))V).  Key padding and the per-head dilation
+ * are conventions of this library.
+ *
+ * All entry points return an lf_status and never throw.  Validation is done on
+ * the host before anything is enqueued, so on any error no kernel runs and
+ * `out` is untouched.  Errors raised while kernels execute surface at the
+ * caller's next synchronisation of `stream`.
+ */
+#ifndef LF_ATTN_H
+#define LF_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lf_status {
+    LF_OK = 0,
+    LF_ERR_INVALID_ARG = 1, /* null pointer, bad size, index out of range, misaligned, aliasing */
+    LF_ERR_UNSUPPORTED = 2, /* d_h != 64, too many heads or globals, unknown dtype */
+    LF_ERR_HIP = 3,         /* a HIP runtime call failed (message in lf_attn_last_error) */
+    LF_ERR_OOM = 4          /* device workspace allocation failed */
+} lf_status;
+
+typedef enum lf_dtype {
+    LF_F32 = 0,  /* float32 inputs and output */
+    LF_BF16 = 1  /* bfloat16 inputs and output; fp32 accumulation and softmax */
+} lf_dtype;
+
+#define LF_MAX_HEADS 64
+#define LF_MAX_GLOBALS 256
+#define LF_HEAD_DIM 64
+
+/* Number of kernel stages timed by lf_attn_stage_times. */
+#define LF_N_STAGES 3
+#define LF_STAGE_BAND 0        /* window keys + global-column fold, all non-global rows */
+#define LF_STAGE_GLOBAL_ROWS 1 /* split-key partials for the global rows */
+#define LF_STAGE_MERGE 2       /* log-sum-exp merge of the partials, global rows written */
+
+typedef struct lf_attn_s* lf_attn_t;
+
+/*
+ * Create a handle for one element type.  Allocates only host memory; device
+ * workspace is allocated on first use, on the device current at that call.
+ * Errors: LF_ERR_INVALID_ARG (out == NULL), LF_ERR_UNSUPPORTED (unknown dtype).
+ */
+lf_status lf_attn_create(lf_attn_t* out, lf_dtype dtype);
+
+/*
+ * Enqueue one forward pass on `stream`.
+ *
+ * q, k, v, out : DEVICE pointers to contiguous [B][H][L][d_h] tensors of the
+ *                handle's dtype, 16-byte aligned, caller-owned; `out` must not
+ *                overlap q, k or v.  They must stay valid until `stream` has
+ *                finished the work.
+ * B, H, L      : batch, heads, sequence length; each >= 1, H <= LF_MAX_HEADS.
+ * d_h          : head dimension; must be 64 (else LF_ERR_UNSUPPORTED).
+ * w            : window half-width (keys on each side); >= 0.  w*dil may exceed L.
+ * dil_per_head : HOST array [H], dilation of each head, each >= 1.  Read during
+ *                the call only.
+ * global_idx   : HOST array [n_global] of positions in [0, L), shared by every
+ *                sequence and head; duplicates are allowed and ignored; NULL iff
+ *                n_global == 0.  Read during the call only.
+ * n_global     : 0 .. LF_MAX_GLOBALS.
+ * key_pad_mask : DEVICE array uint8 [B][L], nonzero = padded key, or NULL for
+ *                no padding.  Padded keys are never attended to (their K and V
+ *                contents never reach the output); padded query rows are
+ *                computed by the same rule as any other row.
+ * stream       : a hipStream_t (NULL = the null stream).  All kernels are
+ *                enqueued on it; the call does not wait for them.
+ *
+ * The handle may grow its device workspace (hipMalloc) inside this call.  One
+ * handle must not be used from two threads at once.
+ */
+lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void* v, void* out,
+                          int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                          const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
+                          void* stream);
+
+/* Free the handle and its device workspace.  NULL is a no-op.  Waits for the
+ * device before freeing (hipFree semantics). */
+lf_status lf_attn_destroy(lf_attn_t h);
+
+/* Static description of a status code. */
+const char* lf_attn_status_string(lf_status s);
+
+/* Message of the last failed call on `h` ("" if none); valid until the next call on h. */
+const char* lf_attn_last_error(lf_attn_t h);
+
+/*
+ * Per-stage kernel timing with HIP events recorded on the launch stream around
+ * each kernel.  enable != 0 starts recording (clearing earlier totals), 0 stops.
+ * Errors: LF_ERR_INVALID_ARG (h == NULL), LF_ERR_HIP.
+ */
+lf_status lf_attn_set_stage_timing(lf_attn_t h, int enable);
+
+/*
+ * Wait for every recorded event, then write the summed milliseconds and the
+ * number of timed launches per stage (arrays of LF_N_STAGES entries; either may
+ * be NULL) and clear the totals.
+ */
+lf_status lf_attn_stage_times(lf_attn_t h, double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_ATTN_H */

@@ -1,0 +1,202 @@
+"""ctypes binding of liblfattn.so (argument marshalling only).
+
+Every step of the forward runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers, Python sequences into int32 host
+arrays, and picks torch's current HIP stream.  It raises if the library has not
+been built: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_NAME = "liblfattn.so"
+
+LF_OK = 0
+LF_F32 = 0
+LF_BF16 = 1
+N_STAGES = 3
+STAGE_NAMES = ("band", "global_rows", "merge")
+MAX_HEADS = 64
+MAX_GLOBALS = 256
+
+# Every symbol declared in include/lf_attn.h.
+EXPORTS = (
+    "lf_attn_create",
+    "lf_attn_forward",
+    "lf_attn_destroy",
+    "lf_attn_status_string",
+    "lf_attn_last_error",
+    "lf_attn_set_stage_timing",
+    "lf_attn_stage_times",
+)
+
+_lib = None
+
+
+class LfAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(PKG, LIBRARY_NAME)
+
+
+def load_library():
+    """Load liblfattn.so from the package directory (built by build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise LfAttnError(-1, f"{path} is not built; run python -m sparse_long_sequence_longformer_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.lf_attn_create.argtypes = [ctypes.POINTER(vp), i32]
+    lib.lf_attn_create.restype = i32
+    lib.lf_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
+                                    vp, vp]
+    lib.lf_attn_forward.restype = i32
+    lib.lf_attn_destroy.argtypes = [vp]
+    lib.lf_attn_destroy.restype = i32
+    lib.lf_attn_status_string.argtypes = [i32]
+    lib.lf_attn_status_string.restype = ctypes.c_char_p
+    lib.lf_attn_last_error.argtypes = [vp]
+    lib.lf_attn_last_error.restype = ctypes.c_char_p
+    lib.lf_attn_set_stage_timing.argtypes = [vp, i32]
+    lib.lf_attn_set_stage_timing.restype = i32
+    lib.lf_attn_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.lf_attn_stage_times.restype = i32
+    _lib = lib
+    return lib
+
+
+def _int32_array(values):
+    vals = [int(x) for x in values]
+    arr = (ctypes.c_int32 * max(1, len(vals)))(*vals) if vals else None
+    return arr, len(vals)
+
+
+class LfAttn:
+    """One library handle (fixed element type)."""
+
+    def __init__(self, dtype: str):
+        self.lib = load_library()
+        self.dtype = dtype
+        code = {"f32": LF_F32, "bf16": LF_BF16}.get(dtype, 99)
+        h = ctypes.c_void_p()
+        st = self.lib.lf_attn_create(ctypes.byref(h), code)
+        self._check(st, h)
+        self.handle = h
+
+    def _check(self, st, h=None):
+        if st != LF_OK:
+            msg = self.lib.lf_attn_status_string(st).decode()
+            if h is not None and h.value:
+                detail = self.lib.lf_attn_last_error(h).decode()
+                if detail:
+                    msg = f"{msg}: {detail}"
+            raise LfAttnError(st, msg)
+
+    def forward_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
+        dil_arr, nd = _int32_array(dil)
+        g_arr, ng = _int32_array(global_idx if global_idx is not None else [])
+        if dil_arr is None:
+            dil_p = ctypes.POINTER(ctypes.c_int32)()
+        else:
+            dil_p = ctypes.cast(dil_arr, ctypes.POINTER(ctypes.c_int32))
+        g_p = ctypes.cast(g_arr, ctypes.POINTER(ctypes.c_int32)) if g_arr is not None \
+            else ctypes.POINTER(ctypes.c_int32)()
+        st = self.lib.lf_attn_forward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w,
+                                      dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def set_stage_timing(self, enable: bool):
+        self._check(self.lib.lf_attn_set_stage_timing(self.handle, 1 if enable else 0), self.handle)
+
+    def stage_times(self):
+        ms = (ctypes.c_double * N_STAGES)()
+        n = (ctypes.c_int64 * N_STAGES)()
+        self._check(self.lib.lf_attn_stage_times(self.handle, ms, n), self.handle)
+        return {STAGE_NAMES[i]: (ms[i], n[i]) for i in range(N_STAGES)}
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self.lib.lf_attn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_handles: dict = {}
+
+
+def _handle_for(dtype: str) -> LfAttn:
+    if dtype not in _handles:
+        _handles[dtype] = LfAttn(dtype)
+    return _handles[dtype]
+
+
+def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None):
+    """Longformer window + global attention forward on the GPU.
+
+    q, k, v: contiguous CUDA/HIP tensors [B, H, L, 64], all bfloat16 or all float32.
+    w: keys on each side of the window.  dil: one dilation per head (sequence or int).
+    global_idx: positions attended by and attending to everything (host sequence).
+    key_pad_mask: [B, L] bool/uint8 device tensor, nonzero = padded key, or None.
+    Returns ``out`` (allocated if not given), same shape and dtype as q.
+    """
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dt = "bf16"
+    elif q.dtype == torch.float32:
+        dt = "f32"
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must match q in dtype and shape")
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d_h]")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, L, d_h = q.shape
+    if isinstance(dil, int):
+        dil = [dil] * H
+    dil = [int(x) for x in (dil.tolist() if hasattr(dil, "tolist") else dil)]
+    if len(dil) != H:
+        raise ValueError("need one dilation per head")
+    if global_idx is not None and hasattr(global_idx, "tolist"):
+        global_idx = global_idx.tolist()
+    pad_ptr = None
+    if key_pad_mask is not None:
+        if key_pad_mask.dtype == torch.bool:
+            key_pad_mask = key_pad_mask.view(torch.uint8)
+        if key_pad_mask.dtype != torch.uint8 or tuple(key_pad_mask.shape) != (B, L):
+            raise ValueError("key_pad_mask must be a [B, L] bool or uint8 tensor")
+        if not key_pad_mask.is_cuda or not key_pad_mask.is_contiguous():
+            raise ValueError("key_pad_mask must be a contiguous device tensor")
+        pad_ptr = key_pad_mask.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous device tensor like q")
+    h = handle if handle is not None else _handle_for(dt)
+    if h.dtype != dt:
+        raise ValueError("handle dtype does not match the inputs")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        h.forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
+                      global_idx, pad_ptr, stream)
+    return out

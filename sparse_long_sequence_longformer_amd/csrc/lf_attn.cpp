@@ -1,0 +1,265 @@
+// Host side of liblfattn.so: argument validation, launch planning, device
+// workspace, per-stage timing.  Everything here runs before any kernel is
+// enqueued; on error nothing is launched and `out` is untouched.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "lf_attn.h"
+#include "lf_attn_internal.h"
+
+namespace {
+
+struct TimedLaunch {
+    hipEvent_t start;
+    hipEvent_t stop;
+    int stage;
+};
+
+}  // namespace
+
+struct lf_attn_s {
+    lf_dtype dtype;
+    int device = -1;
+    float* ws = nullptr;  // global-row partials
+    size_t ws_bytes = 0;
+    std::string last_error;
+    bool timing = false;
+    std::vector<TimedLaunch> pending;  // recorded, not yet read
+    std::vector<hipEvent_t> event_pool;
+    double stage_ms[LF_N_STAGES] = {0, 0, 0};
+    int64_t stage_n[LF_N_STAGES] = {0, 0, 0};
+};
+
+namespace {
+
+lf_status fail(lf_attn_t h, lf_status s, const char* fmt, ...) {
+    if (h) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        std::vsnprintf(buf, sizeof(buf), fmt, ap);
+        va_end(ap);
+        h->last_error = buf;
+    }
+    return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + n && y < x + n;
+}
+
+hipEvent_t take_event(lf_attn_t h) {
+    if (!h->event_pool.empty()) {
+        hipEvent_t e = h->event_pool.back();
+        h->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void release_events(lf_attn_t h) {
+    for (auto& t : h->pending) {
+        h->event_pool.push_back(t.start);
+        h->event_pool.push_back(t.stop);
+    }
+    h->pending.clear();
+}
+
+// Choose keys per global-row work-group so the grid has about 1024 groups.
+int plan_chunk(int L, int BH, int n_gblk) {
+    const int64_t want = (static_cast<int64_t>(L) * BH * n_gblk + 1023) / 1024;
+    int64_t c = ((want + 255) / 256) * 256;
+    c = std::max<int64_t>(c, 256);
+    c = std::min<int64_t>(c, ((static_cast<int64_t>(L) + 255) / 256) * 256);
+    return static_cast<int>(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lf_attn_status_string(lf_status s) {
+    switch (s) {
+        case LF_OK: return "ok";
+        case LF_ERR_INVALID_ARG: return "invalid argument";
+        case LF_ERR_UNSUPPORTED: return "unsupported argument";
+        case LF_ERR_HIP: return "HIP runtime error";
+        case LF_ERR_OOM: return "device memory allocation failed";
+    }
+    return "unknown status";
+}
+
+lf_status lf_attn_create(lf_attn_t* out, lf_dtype dtype) {
+    if (!out) return LF_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (dtype != LF_F32 && dtype != LF_BF16) return LF_ERR_UNSUPPORTED;
+    lf_attn_t h = new (std::nothrow) lf_attn_s;
+    if (!h) return LF_ERR_OOM;
+    h->dtype = dtype;
+    *out = h;
+    return LF_OK;
+}
+
+const char* lf_attn_last_error(lf_attn_t h) { return h ? h->last_error.c_str() : ""; }
+
+lf_status lf_attn_destroy(lf_attn_t h) {
+    if (!h) return LF_OK;
+    lf_status st = LF_OK;
+    if (h->ws && hipFree(h->ws) != hipSuccess) st = LF_ERR_HIP;
+    release_events(h);
+    for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
+    delete h;
+    return st;
+}
+
+lf_status lf_attn_set_stage_timing(lf_attn_t h, int enable) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->timing = enable != 0;
+    release_events(h);
+    for (int i = 0; i < LF_N_STAGES; ++i) {
+        h->stage_ms[i] = 0;
+        h->stage_n[i] = 0;
+    }
+    return LF_OK;
+}
+
+lf_status lf_attn_stage_times(lf_attn_t h, double* ms, int64_t* launches) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    for (auto& t : h->pending) {
+        if (hipEventSynchronize(t.stop) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventSynchronize failed");
+        float e = 0.f;
+        if (hipEventElapsedTime(&e, t.start, t.stop) != hipSuccess)
+            return fail(h, LF_ERR_HIP, "hipEventElapsedTime failed");
+        h->stage_ms[t.stage] += e;
+        h->stage_n[t.stage] += 1;
+    }
+    release_events(h);
+    for (int i = 0; i < LF_N_STAGES; ++i) {
+        if (ms) ms[i] = h->stage_ms[i];
+        if (launches) launches[i] = h->stage_n[i];
+        h->stage_ms[i] = 0;
+        h->stage_n[i] = 0;
+    }
+    return LF_OK;
+}
+
+lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void* v, void* out, int B, int H,
+                          int L, int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx,
+                          int n_global, const uint8_t* key_pad_mask, void* stream) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (!q || !k || !v || !out) return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+    if (B < 1 || H < 1 || L < 1) return fail(h, LF_ERR_INVALID_ARG, "need B, H, L >= 1 (got %d, %d, %d)", B, H, L);
+    if (d_h != LF_HEAD_DIM) return fail(h, LF_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
+    if (H > LF_MAX_HEADS) return fail(h, LF_ERR_UNSUPPORTED, "at most %d heads (got %d)", LF_MAX_HEADS, H);
+    if (w < 0) return fail(h, LF_ERR_INVALID_ARG, "need w >= 0 (got %d)", w);
+    if (!dil_per_head) return fail(h, LF_ERR_INVALID_ARG, "dil_per_head must be non-null");
+    if (n_global < 0) return fail(h, LF_ERR_INVALID_ARG, "need n_global >= 0 (got %d)", n_global);
+    if (n_global > LF_MAX_GLOBALS)
+        return fail(h, LF_ERR_UNSUPPORTED, "at most %d global indices (got %d)", LF_MAX_GLOBALS, n_global);
+    if (n_global > 0 && !global_idx) return fail(h, LF_ERR_INVALID_ARG, "global_idx is NULL but n_global > 0");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    const size_t elem = h->dtype == LF_BF16 ? 2 : 4;
+    const uint64_t n_elem = static_cast<uint64_t>(B) * H * L * LF_HEAD_DIM;
+    if (n_elem / LF_HEAD_DIM / L / H != static_cast<uint64_t>(B) || n_elem > (uint64_t(1) << 40))
+        return fail(h, LF_ERR_INVALID_ARG, "tensor size overflows");
+    const size_t bytes = static_cast<size_t>(n_elem) * elem;
+    if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+        return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q, k or v");
+
+    lf::Params p;
+    std::memset(&p, 0, sizeof(p));
+    for (int i = 0; i < H; ++i) {
+        if (dil_per_head[i] < 1) return fail(h, LF_ERR_INVALID_ARG, "dil_per_head[%d] = %d < 1", i, dil_per_head[i]);
+        p.dil[i] = dil_per_head[i];
+    }
+    std::vector<int> g(global_idx, global_idx + n_global);
+    for (int i = 0; i < n_global; ++i)
+        if (g[i] < 0 || g[i] >= L)
+            return fail(h, LF_ERR_INVALID_ARG, "global_idx[%d] = %d outside [0, %d)", i, g[i], L);
+    std::sort(g.begin(), g.end());
+    g.erase(std::unique(g.begin(), g.end()), g.end());
+
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.pad = key_pad_mask;
+    p.B = B;
+    p.H = H;
+    p.L = L;
+    p.w = std::min(w, L);  // |j - i| < L always, so a wider window changes nothing
+    p.n_g = static_cast<int>(g.size());
+    std::copy(g.begin(), g.end(), p.g);
+    p.n_gblk = (p.n_g + lf::kGlobalQueriesPerBlock - 1) / lf::kGlobalQueriesPerBlock;
+    int tiles = 0;
+    for (int i = 0; i < H; ++i) {
+        const int d = p.dil[i];
+        const int len0 = (L + d - 1) / d;
+        const int64_t t = static_cast<int64_t>(d) * ((len0 + lf::kRowsPerBlock - 1) / lf::kRowsPerBlock);
+        tiles = std::max<int>(tiles, static_cast<int>(t));
+    }
+    p.tiles_per_head = tiles;
+    if (static_cast<int64_t>(B) * H * tiles > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
+    if (p.n_g > 0) {
+        p.chunk = plan_chunk(L, B * H, p.n_gblk);
+        p.n_chunks = (L + p.chunk - 1) / p.chunk;
+    }
+
+    // Device workspace for the global-row partials.
+    if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
+    if (p.n_g > 0) {
+        const size_t n_part = static_cast<size_t>(B) * H * p.n_gblk * lf::kGlobalQueriesPerBlock * p.n_chunks;
+        const size_t need = n_part * (2 + 64) * sizeof(float);
+        if (need > h->ws_bytes) {
+            if (h->ws) (void)hipFree(h->ws);
+            h->ws = nullptr;
+            h->ws_bytes = 0;
+            if (hipMalloc(reinterpret_cast<void**>(&h->ws), need) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(h, LF_ERR_OOM, "hipMalloc of %zu workspace bytes failed", need);
+            }
+            h->ws_bytes = need;
+        }
+        p.ws_ml = h->ws;
+        p.ws_acc = h->ws + n_part * 2;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    using Launcher = hipError_t (*)(const lf::Params&, int, hipStream_t);
+    const Launcher stages[LF_N_STAGES] = {lf::launch_band, lf::launch_global_rows, lf::launch_merge};
+    for (int i = 0; i < LF_N_STAGES; ++i) {
+        if (i > 0 && p.n_g == 0) break;
+        TimedLaunch tl{nullptr, nullptr, i};
+        if (h->timing) {
+            tl.start = take_event(h);
+            tl.stop = take_event(h);
+            if (!tl.start || !tl.stop) return fail(h, LF_ERR_HIP, "hipEventCreate failed");
+            if (hipEventRecord(tl.start, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+        }
+        const hipError_t e = stages[i](p, h->dtype, s);
+        if (e != hipSuccess) return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        if (h->timing) {
+            if (hipEventRecord(tl.stop, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+            h->pending.push_back(tl);
+        }
+    }
+    return LF_OK;
+}
+
+}  // extern "C"

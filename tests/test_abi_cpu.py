@@ -1,0 +1,125 @@
+"""C-ABI library on the CPU: it loads, exports every declared symbol, and rejects
+invalid arguments on the host before any HIP call (no compute without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_long_sequence_longformer_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lf_attn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(binding.library_path()),
+                               reason="liblfattn.so not built (run __graft_entry__.build())")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(lf_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert declared_symbols() == sorted(binding.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_symbol():
+    lib = ctypes.CDLL(binding.library_path())
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_status_strings():
+    lib = binding.load_library()
+    for code in range(5):
+        assert lib.lf_attn_status_string(code)
+    assert lib.lf_attn_status_string(77) == b"unknown status"
+
+
+@needs_lib
+def test_create_destroy_and_bad_dtype():
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 5) == 2  # LF_ERR_UNSUPPORTED
+    assert lib.lf_attn_create(None, 1) == 1
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0 and h.value
+    assert lib.lf_attn_last_error(h) == b""
+    assert lib.lf_attn_set_stage_timing(h, 1) == 0
+    ms = (ctypes.c_double * 3)()
+    n = (ctypes.c_int64 * 3)()
+    assert lib.lf_attn_stage_times(h, ms, n) == 0 and list(n) == [0, 0, 0]
+    assert lib.lf_attn_destroy(h) == 0
+    assert lib.lf_attn_destroy(None) == 0
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _call(h, **kw):
+    lib = binding.load_library()
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, out=FAKE * 4, B=1, H=2, L=64, d_h=64, w=4,
+             dil=[1, 2], g=[], ng=None, pad=None)
+    a.update(kw)
+    dil = a["dil"]
+    dil_p = (ctypes.c_int32 * len(dil))(*dil) if dil is not None else None
+    g = a["g"]
+    g_p = (ctypes.c_int32 * len(g))(*g) if g else None
+    ng = len(g) if a["ng"] is None else a["ng"]
+    st = lib.lf_attn_forward(h, a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["L"], a["d_h"], a["w"],
+                             ctypes.cast(dil_p, ctypes.POINTER(ctypes.c_int32)) if dil_p else None,
+                             ctypes.cast(g_p, ctypes.POINTER(ctypes.c_int32)) if g_p else None,
+                             ng, a["pad"], None)
+    return st, lib.lf_attn_last_error(h).decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(q=None), 1, "non-null"),
+    (dict(out=None), 1, "non-null"),
+    (dict(B=0), 1, "B, H, L"),
+    (dict(L=0), 1, "B, H, L"),
+    (dict(d_h=32), 2, "d_h"),
+    (dict(H=65, dil=[1] * 65), 2, "heads"),
+    (dict(w=-1), 1, "w >= 0"),
+    (dict(dil=None), 1, "dil_per_head"),
+    (dict(dil=[1, 0]), 1, "dil_per_head[1]"),
+    (dict(g=[3, 64]), 1, "outside"),
+    (dict(g=[-1]), 1, "outside"),
+    (dict(g=[], ng=2), 1, "global_idx is NULL"),
+    (dict(g=[], ng=-1), 1, "n_global"),
+    (dict(g=list(range(64)) * 5), 2, "at most"),
+    (dict(q=FAKE + 8), 1, "aligned"),
+    (dict(out=FAKE * 3 + 64), 1, "overlap"),
+])
+def test_invalid_arguments_rejected_on_host(kw, code, frag):
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        st, msg = _call(h, **kw)
+        assert st == code, (st, msg)
+        assert frag in msg, msg
+        # the handle stays usable after an error
+        st2, _ = _call(h, B=0)
+        assert st2 == 1
+    finally:
+        lib.lf_attn_destroy(h)
+
+
+@needs_lib
+def test_null_handle():
+    lib = binding.load_library()
+    assert lib.lf_attn_forward(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None, None, 0, None, None) == 1
+    assert lib.lf_attn_last_error(None) == b""
+
+
+def test_python_forward_requires_device_tensors():
+    import torch
+
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises((ValueError, binding.LfAttnError)):
+        binding.forward(x, x, x, 2, [1])

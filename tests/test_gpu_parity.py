@@ -1,0 +1,182 @@
+"""HIP path (through the C-ABI) against the fp64 oracle on seeded inputs.
+
+Small and medium shapes are compared element by element over every output; the
+full-size workloads are compared on sampled rows the oracle computes one by one,
+plus properties that hold at any size.  Tolerances: fp32 max-abs 1e-4; bf16
+max-abs 2e-2 and mean-abs 2e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import longformer_oracle as orc
+from sparse_long_sequence_longformer_amd import workloads
+from sparse_long_sequence_longformer_amd.workloads import make_custom, make_qkv
+from tests.gpu_common import compare, full_parity, log, run_gpu, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_long_sequence_longformer_amd import binding
+
+    binding.load_library()  # fail loudly if the HIP library is missing
+    yield
+
+
+def _pad_from_lengths(B, L, lengths):
+    if lengths is None:
+        return None
+    return (np.arange(L)[None, :] >= np.asarray(lengths)[:, None]).astype(np.uint8)
+
+
+# ------------------------------------------------------------------ fp32 battery
+# (name, B, H, L, w, dil, globals, pad lengths or "rand", global-key scale)
+F32_CASES = [
+    ("w0", 1, 1, 200, 0, [1], [], None, 1.0),
+    ("w0_globals", 1, 2, 130, 0, [1, 3], [7, 7, 129], None, 1.0),
+    ("window_covers_all", 1, 2, 150, 200, [1, 2], [], None, 1.0),
+    ("wdil_ge_L", 1, 1, 96, 40, [3], [50], None, 1.0),
+    ("ragged_1000", 1, 1, 1000, 45, [1], [], None, 1.0),
+    ("global_in_window_large_score", 1, 1, 333, 20, [1], [100, 101, 300], None, 4.0),
+    ("globals_on_off_lattice", 1, 3, 400, 17, [3, 2, 4], [30, 31, 32, 33, 200], None, 3.0),
+    ("dup_globals", 1, 1, 257, 9, [1], [5, 5, 200, 5, 200, 256], None, 1.0),
+    ("band_fully_padded_rows", 2, 1, 500, 10, [1], [], [500, 120], 1.0),
+    ("global_in_padding", 2, 2, 300, 12, [1, 2], [3, 250, 299], [300, 200], 2.0),
+    ("random_padding", 2, 2, 384, 30, [1, 2], [0, 191, 383], "rand", 1.0),
+    ("many_globals_100", 1, 2, 700, 25, [1, 2], "many100", None, 1.0),
+    ("max_globals_256", 1, 1, 600, 8, [1], "many256", None, 1.0),
+    ("mixed_dilations", 1, 4, 640, 21, [1, 2, 3, 5], [10, 11, 320, 639], None, 1.0),
+    ("tiny_L1", 1, 1, 1, 3, [1], [], None, 1.0),
+    ("tiny_L2_global", 1, 1, 2, 0, [1], [1], None, 1.0),
+    ("short_L33", 2, 1, 33, 4, [2], [0], [33, 20], 1.0),
+    ("all_padded_sequence", 2, 1, 100, 5, [1], [], [100, 0], 1.0),
+]
+
+
+def _globals_for(spec, L, seed):
+    if spec == "many100":
+        return sorted(np.random.default_rng(seed).choice(L, 100, replace=False).tolist())
+    if spec == "many256":
+        return sorted(np.random.default_rng(seed).choice(L, 256, replace=False).tolist())
+    return list(spec)
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_f32_battery(case):
+    name, B, H, L, w, dil, Gs, lens, gscale = case
+    log(f"case f32 {name}: B={B} H={H} L={L} w={w} dil={dil}")
+    q, k, v = make_custom(B, H, L, dtype="f32", seed=len(name))
+    G = _globals_for(Gs, L, len(name))
+    if gscale != 1.0 and G:
+        k[:, :, G] *= gscale  # global keys with large scores
+    if lens == "rand":
+        pad = (np.random.default_rng(7).random((B, L)) < 0.3).astype(np.uint8)
+    else:
+        pad = _pad_from_lengths(B, L, lens)
+    full_parity(q, k, v, w, dil, G, pad, "f32", name)
+
+
+def test_f32_tiny_workload():
+    wl = workloads.WORKLOADS["tiny_f32"]
+    q, k, v = make_qkv(wl)
+    log("case tiny_f32 workload")
+    full_parity(q, k, v, wl.w, wl.dil_list(), wl.global_positions(), wl.pad_mask(), "f32", "tiny_f32")
+
+
+def test_f32_empty_rows_exactly_zero():
+    B, H, L = 2, 1, 160
+    q, k, v = make_custom(B, H, L, dtype="f32", seed=3)
+    pad = np.zeros((B, L), dtype=np.uint8)
+    pad[0, 40:120] = 1  # rows 50..109 of sequence 0 have no unpadded window key (w=10)
+    pad[1, :] = 1  # sequence 1: every key padded
+    got = run_gpu(q, k, v, 10, [1], [], pad)
+    assert torch.all(got[0, 0, 50:110] == 0)
+    assert torch.all(got[1] == 0)
+    ref = orc.attention(q, k, v, 10, [1], [], pad)
+    compare(got, ref, "f32", "empty rows")
+
+
+def test_f32_padded_contents_never_reach_output():
+    """Padded keys' K/V rows filled with NaN give the same output as with zeros."""
+    B, H, L = 2, 2, 300
+    q, k, v = make_custom(B, H, L, dtype="f32", seed=4)
+    pad = _pad_from_lengths(B, L, [300, 170])
+    pad[0, 40:60] = 1
+    G = [0, 100, 250]
+    a = run_gpu(q, k, v, 15, [1, 2], G, pad)
+    k2, v2 = k.clone(), v.clone()
+    mask = torch.from_numpy(pad.astype(bool))[:, None, :, None].expand_as(k2)
+    k2[mask] = float("nan")
+    v2[mask] = float("nan")
+    b = run_gpu(q, k2, v2, 15, [1, 2], G, pad)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ bf16, full compare
+
+BF16_CASES = [
+    ("ragged_1000_mixed", 2, 3, 1000, 40, [1, 2, 3], [0, 5, 500, 999], [1000, 777]),
+    ("qa_like_2048", 1, 4, 2048, 512, [1] * 4, list(range(16)), None),
+    ("cls_like_1536", 1, 2, 1536, 256, [1, 1], [0], None),
+    ("dilated_like_1100", 1, 4, 1100, 128, [1, 1, 2, 2], [13, 400, 401, 1099], None),
+    ("padded_like_1300", 3, 2, 1300, 64, [1, 1], list(range(16)), [1300, 700, 64]),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_bf16_full_compare(case):
+    name, B, H, L, w, dil, G, lens = case
+    log(f"case bf16 {name}: B={B} H={H} L={L} w={w} dil={dil}")
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=11)
+    full_parity(q, k, v, w, dil, G, _pad_from_lengths(B, L, lens), "bf16", name)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("name", ["cls_4k", "qa_4k", "dilated_8k", "padded_32k"])
+def test_workload_sampled(name):
+    wl = workloads.WORKLOADS[name]
+    log(f"case workload {name}: {wl.desc}")
+    q, k, v = make_qkv(wl)
+    G = wl.global_positions()
+    pad = wl.pad_mask()
+    got = run_gpu(q, k, v, wl.w, wl.dil_list(), G, pad)
+    assert torch.isfinite(got.float()).all()
+    samples = sample_rows(wl.B, wl.H, wl.L, G, pad, n_random=48, seed=5)
+    ref = orc.attention_sampled(q, k, v, wl.w, wl.dil_list(), G, pad, samples)
+    sel = torch.stack([got[b, h, i] for b, h, i in samples])
+    compare(sel, ref, "bf16", f"{name} ({len(samples)} sampled rows)")
+
+
+def test_bf16_deterministic():
+    wl = workloads.WORKLOADS["qa_4k"]
+    q, k, v = make_qkv(wl)
+    qd, kd, vd = to_dev(q, k, v)
+    from sparse_long_sequence_longformer_amd import binding
+
+    a = binding.forward(qd, kd, vd, wl.w, wl.dil_list(), wl.global_positions())
+    b = binding.forward(qd, kd, vd, wl.w, wl.dil_list(), wl.global_positions())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_side_stream_bool_mask_and_out_reuse():
+    from sparse_long_sequence_longformer_amd import binding
+
+    B, H, L = 2, 2, 640
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=21)
+    pad = _pad_from_lengths(B, L, [640, 333])
+    ref = run_gpu(q, k, v, 50, [1, 2], [0, 9], pad)
+    qd, kd, vd = to_dev(q, k, v)
+    padb = torch.from_numpy(pad.astype(bool)).to("cuda")
+    out = torch.full_like(qd, 7.0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        binding.forward(qd, kd, vd, 50, [1, 2], [0, 9], padb, out=out)
+    s.synchronize()
+    assert torch.equal(out.cpu(), ref)
