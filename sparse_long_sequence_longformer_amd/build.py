@@ -36,6 +36,8 @@ def compile_flags() -> list[str]:
         "-Wall",
         "-Wno-unused-result",
         "-ffp-contract=fast",
+        # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around the softmax)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=true",
         # no packed fp32 VALU instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE,

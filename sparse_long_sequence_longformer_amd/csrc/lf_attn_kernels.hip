@@ -98,6 +98,28 @@ struct Bf16 {
     static constexpr int kStageBytes = 2 * kKBytes;    // K + V^T
     struct QOp { bf16x8 v[4]; };
     struct Regs { u32x4 k[2]; u32x4 v[2]; };
+    struct PFrag { bf16x8 v[2]; };
+
+    // Round the weights to bf16 (the P^T operand) and return their sum as rounded,
+    // so the normaliser matches the weights the product uses.
+    __device__ static float make_p(const float* p, PFrag& pf) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float sum = 0.f;
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x8 t;
+            for (int j = 0; j < 8; ++j) t[j] = p[8 * kb + j];
+            const bf16x8 b = __builtin_convertvector(t, bf16x8);
+            pf.v[kb] = b;
+            // Sub-vectors by shuffle: hipcc mis-selects dot2 operands taken as words of
+            // a bit-cast of the converted vector (every word reads as the first).
+            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), one, sum, false);
+            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), one, sum, false);
+            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), one, sum, false);
+            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), one, sum, false);
+        }
+        return sum;
+    }
 
     // B operand of S^T = K Q^T: lane (query, h2) holds d = 16*kb + 8*h2 + j.
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
@@ -157,14 +179,8 @@ struct Bf16 {
     }
 
     // O^T += V^T P^T over the 32 keys of sub-tile `sub`.
-    __device__ static void pv(const char* stage, int sub, int lane, const float* p, f32x16* o) {
+    __device__ static void pv(const char* stage, int sub, int lane, const PFrag& pf, f32x16* o) {
         const int M = lane & 31, h2 = lane >> 5;
-        bf16x8 pb[2];
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x8 t;
-            for (int j = 0; j < 8; ++j) t[j] = p[8 * kb + j];
-            pb[kb] = __builtin_convertvector(t, bf16x8);
-        }
         const char* Vt = stage + kKBytes;
         for (int db = 0; db < 2; ++db) {
             const int d = 32 * db + pi_col(M);
@@ -172,7 +188,7 @@ struct Bf16 {
             const int sw = swz_v(d);
             for (int kb = 0; kb < 2; ++kb) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowp + (((4 * sub + 2 * kb + h2) ^ sw) << 4));
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb], o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.v[kb], o[db], 0, 0, 0);
             }
         }
     }
@@ -198,6 +214,16 @@ struct F32 {
     static constexpr int kStageBytes = 2 * kKBytes;    // K + V, both row-major
     struct QOp { float v[32]; };
     struct Regs { u32x4 k[4]; u32x4 v[4]; };
+    struct PFrag { float v[16]; };
+
+    __device__ static float make_p(const float* p, PFrag& pf) {
+        float sum = 0.f;
+        for (int i = 0; i < 16; ++i) {
+            pf.v[i] = p[i];
+            sum += p[i];
+        }
+        return sum;
+    }
 
     // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t.
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
@@ -241,14 +267,14 @@ struct F32 {
     }
 
     // Step u pairs lane-half h2 with key key_local(u, h2), matching the score layout.
-    __device__ static void pv(const char* stage, int sub, int lane, const float* p, f32x16* o) {
+    __device__ static void pv(const char* stage, int sub, int lane, const PFrag& pf, f32x16* o) {
         const int M = lane & 31, h2 = lane >> 5;
         const float* Vs = reinterpret_cast<const float*>(stage + kKBytes);
         for (int db = 0; db < 2; ++db) {
             const int d = 32 * db + pi_col(M);
             for (int u = 0; u < 16; ++u) {
                 const float a = Vs[(32 * sub + key_local(u, h2)) * 64 + d];
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[u], o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.v[u], o[db], 0, 0, 0);
             }
         }
     }
@@ -282,25 +308,31 @@ __device__ __forceinline__ void state_init(State& st) {
     st.o[1] = f32x16{};
 }
 
-// Fold one 32-key score block into the state; writes the unnormalised weights to p.
-__device__ __forceinline__ void online_update(State& st, const f32x16& s, float* p) {
+// Raise the running max only when a row's block max exceeds it by more than
+// 2^8 in weight: weights may then reach 256 (exact in bf16 and fp32 alike), and
+// the output/sum rescale runs only on the few blocks that raise a max.
+constexpr float kRaiseRaw = 8.0f / kScaleLog2;
+
+// Fold one 32-key score block into the state; the weights go to the P^T operand.
+template <class T>
+__device__ __forceinline__ void online_update(State& st, const f32x16& s, typename T::PFrag& pf) {
     float mx = s[0];
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = pair_max(mx);
-    const float mnew = fmaxf(st.m, mx);
-    const float mc = (mnew == kNegInf ? 0.f : mnew) * kScaleLog2;
-    const float alpha = fast_exp2(st.m * kScaleLog2 - mc);  // 0 while nothing was seen
-    float sum = 0.f;
-    for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(fmaf(s[i], kScaleLog2, -mc));
-        sum += p[i];
-    }
-    st.l = st.l * alpha + sum;
-    if (__any(alpha != 1.f)) {
+    const bool raise = mx > st.m + kRaiseRaw;  // a first finite block always raises
+    if (__any(raise)) {
+        // Lanes that keep their max keep alpha = 1 (their max may still be -inf).
+        const float mnew = raise ? mx : st.m;
+        const float alpha = raise ? fast_exp2((st.m - mnew) * kScaleLog2) : 1.f;  // 0 from -inf
+        st.l *= alpha;
         st.o[0] *= alpha;
         st.o[1] *= alpha;
+        st.m = mnew;
     }
-    st.m = mnew;
+    const float mc = (st.m == kNegInf ? 0.f : st.m) * kScaleLog2;
+    float p[16];
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], kScaleLog2, -mc));
+    st.l += T::make_p(p, pf);
 }
 
 __device__ __forceinline__ bool is_global_row(const Params& p, int row) {
@@ -355,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const Params p) {
     T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * 64 : nullptr, h2);
     State st;
     state_init(st);
-    float pw[16];
+    typename T::PFrag pw;
     typename T::Regs regs;
 
     // (b) global keys, up to 64 per stage.
@@ -383,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const Params p) {
                     const bool in_window = (unsigned)(gp - qv + w) <= (unsigned)(2 * w);
                     if (((inv32 >> kl) & 1) || in_window) s[i] = kNegInf;
                 }
-                online_update(st, s, pw);
+                online_update<T>(st, s, pw);
                 T::pv(smem, sub, lane, pw, st.o);
             }
         }
@@ -431,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const Params p) {
                         if (!ok) s[i] = kNegInf;
                     }
                 }
-                online_update(st, s, pw);
+                online_update<T>(st, s, pw);
                 T::pv(cur, sub, lane, pw, st.o);
             }
         }
@@ -476,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void global_rows_kernel(const Params p) {
     T::load_q(qop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
     State st;
     state_init(st);
-    float pw[16];
+    typename T::PFrag pw;
     typename T::Regs regs;
     const char* mybuf = smem + wv * T::kStageBytes;
 
@@ -507,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void global_rows_kernel(const Params p) {
                 if (inv32 != 0u)
                     for (int i = 0; i < 16; ++i)
                         if ((inv32 >> key_local(i, h2)) & 1) s[i] = kNegInf;
-                online_update(st, s, pw);
+                online_update<T>(st, s, pw);
                 T::pv(mybuf, sub, lane, pw, st.o);
             }
         }
