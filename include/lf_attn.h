@@ -51,11 +51,10 @@ typedef enum lf_dtype {
 #define LF_MAX_GLOBALS 256
 #define LF_HEAD_DIM 64
 
-/* Number of kernel stages timed by lf_attn_stage_times. */
-#define LF_N_STAGES 3
-#define LF_STAGE_BAND 0        /* window keys + global-column fold, all non-global rows */
-#define LF_STAGE_GLOBAL_ROWS 1 /* split-key partials for the global rows */
-#define LF_STAGE_MERGE 2       /* log-sum-exp merge of the partials, global rows written */
+/* Kernel launches timed by lf_attn_stage_times. */
+#define LF_N_STAGES 2
+#define LF_STAGE_BAND 0  /* window band, global-column fold, global-row partials */
+#define LF_STAGE_MERGE 1 /* log-sum-exp merge of the partials (only with globals) */
 
 typedef struct lf_attn_s* lf_attn_t;
 
@@ -89,8 +88,10 @@ lf_status lf_attn_create(lf_attn_t* out, lf_dtype dtype);
  * stream       : a hipStream_t (NULL = the null stream).  All kernels are
  *                enqueued on it; the call does not wait for them.
  *
- * The handle may grow its device workspace (hipMalloc) inside this call.  One
- * handle must not be used from two threads at once.
+ * The handle may grow its device workspace (hipMalloc) inside this call when
+ * global positions are given.  Calls on one
+ * handle must not overlap in time (one thread, and one stream at a time, or the
+ * caller orders the streams): they share that workspace.
  */
 lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void* v, void* out,
                           int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,

@@ -17,8 +17,8 @@ LIBRARY_NAME = "liblfattn.so"
 LF_OK = 0
 LF_F32 = 0
 LF_BF16 = 1
-N_STAGES = 3
-STAGE_NAMES = ("band", "global_rows", "merge")
+N_STAGES = 2
+STAGE_NAMES = ("band", "merge")
 MAX_HEADS = 64
 MAX_GLOBALS = 256
 

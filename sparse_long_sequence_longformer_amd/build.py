@@ -35,6 +35,8 @@ def compile_flags() -> list[str]:
         "-fPIC",
         "-Wall",
         "-Wno-unused-result",
+        "-Wno-inline-asm",
+        "-Wno-unused-const-variable",
         "-ffp-contract=fast",
         # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around the softmax)
         "-mllvm", "-amdgpu-mfma-vgpr-form=true",

@@ -29,14 +29,15 @@ struct TimedLaunch {
 struct lf_attn_s {
     lf_dtype dtype;
     int device = -1;
-    float* ws = nullptr;  // global-row partials
+    char* ws = nullptr;  // global-row partials
     size_t ws_bytes = 0;
+    int ws_device = -1;
     std::string last_error;
     bool timing = false;
     std::vector<TimedLaunch> pending;  // recorded, not yet read
     std::vector<hipEvent_t> event_pool;
-    double stage_ms[LF_N_STAGES] = {0, 0, 0};
-    int64_t stage_n[LF_N_STAGES] = {0, 0, 0};
+    double stage_ms[LF_N_STAGES] = {0, 0};
+    int64_t stage_n[LF_N_STAGES] = {0, 0};
 };
 
 namespace {
@@ -77,15 +78,6 @@ void release_events(lf_attn_t h) {
         h->event_pool.push_back(t.stop);
     }
     h->pending.clear();
-}
-
-// Choose keys per global-row work-group so the grid has about 1024 groups.
-int plan_chunk(int L, int BH, int n_gblk) {
-    const int64_t want = (static_cast<int64_t>(L) * BH * n_gblk + 1023) / 1024;
-    int64_t c = ((want + 255) / 256) * 256;
-    c = std::max<int64_t>(c, 256);
-    c = std::min<int64_t>(c, ((static_cast<int64_t>(L) + 255) / 256) * 256);
-    return static_cast<int>(c);
 }
 
 }  // namespace
@@ -210,23 +202,21 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
     int tiles = 0;
     for (int i = 0; i < H; ++i) {
         const int d = p.dil[i];
-        const int len0 = (L + d - 1) / d;
-        const int64_t t = static_cast<int64_t>(d) * ((len0 + lf::kRowsPerBlock - 1) / lf::kRowsPerBlock);
+        const int len0 = (L + d - 1) / d;  // rows of residue class 0 (the longest)
+        const int per_class = (len0 + lf::kRowsPerBlock - 1) / lf::kRowsPerBlock;
+        const int64_t t = static_cast<int64_t>(d) * per_class;
+        if (t > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
         tiles = std::max<int>(tiles, static_cast<int>(t));
     }
     p.tiles_per_head = tiles;
     if (static_cast<int64_t>(B) * H * tiles > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
-    if (p.n_g > 0) {
-        p.chunk = plan_chunk(L, B * H, p.n_gblk);
-        p.n_chunks = (L + p.chunk - 1) / p.chunk;
-    }
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
     if (p.n_g > 0) {
-        const size_t n_part = static_cast<size_t>(B) * H * p.n_gblk * lf::kGlobalQueriesPerBlock * p.n_chunks;
+        const size_t n_part = static_cast<size_t>(B) * H * tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
         const size_t need = n_part * (2 + 64) * sizeof(float);
-        if (need > h->ws_bytes) {
+        if (need > h->ws_bytes || h->ws_device != h->device) {
             if (h->ws) (void)hipFree(h->ws);
             h->ws = nullptr;
             h->ws_bytes = 0;
@@ -235,16 +225,17 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
                 return fail(h, LF_ERR_OOM, "hipMalloc of %zu workspace bytes failed", need);
             }
             h->ws_bytes = need;
+            h->ws_device = h->device;
         }
-        p.ws_ml = h->ws;
-        p.ws_acc = h->ws + n_part * 2;
+        p.ws_ml = reinterpret_cast<float*>(h->ws);
+        p.ws_acc = p.ws_ml + n_part * 2;
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     using Launcher = hipError_t (*)(const lf::Params&, int, hipStream_t);
-    const Launcher stages[LF_N_STAGES] = {lf::launch_band, lf::launch_global_rows, lf::launch_merge};
+    const Launcher stages[LF_N_STAGES] = {lf::launch_band, lf::launch_merge};
     for (int i = 0; i < LF_N_STAGES; ++i) {
-        if (i > 0 && p.n_g == 0) break;
+        if (i == LF_STAGE_MERGE && p.n_g == 0) break;
         TimedLaunch tl{nullptr, nullptr, i};
         if (h->timing) {
             tl.start = take_event(h);

@@ -1,5 +1,5 @@
 // Internal interface between the host planner (lf_attn.cpp) and the gfx950
-// kernels (lf_attn_kernels.hip).  Not part of the public ABI.
+// kernel (lf_attn_kernels.hip).  Not part of the public ABI.
 #pragma once
 
 #include <stdint.h>
@@ -10,8 +10,7 @@
 
 namespace lf {
 
-// Rows of one band work-group (4 waves x 32 query rows) and keys of one
-// staged K/V tile.
+// Rows of one work-group (4 waves x 32 query rows) and keys of one staged K/V tile.
 constexpr int kRowsPerBlock = 128;
 constexpr int kKeysPerTile = 64;
 constexpr int kWaves = 4;
@@ -25,21 +24,20 @@ struct Params {
     const void* v;
     void* out;
     const uint8_t* pad;  // [B][L] or nullptr
-    float* ws_ml;        // [B*H][n_gq][n_chunks][2]  (running max, sum) of each key chunk
-    float* ws_acc;       // [B*H][n_gq][n_chunks][64] unnormalised output of each key chunk
+    // Global-row partials: one (max, sum, 64 outputs) per (b*H + h, row tile, global
+    // query), written by every work-group for its own 128 "home" keys.
+    float* ws_ml;        // [B*H][tiles_per_head][n_gblk*32][2]
+    float* ws_acc;       // [B*H][tiles_per_head][n_gblk*32][64]
     int B, H, L, w;
     int n_g;             // number of distinct global positions
     int n_gblk;          // ceil(n_g / 32)
-    int tiles_per_head;  // band work-groups per (b, h), max over heads
-    int chunk;           // keys per global-row work-group (multiple of 256)
-    int n_chunks;        // ceil(L / chunk)
+    int tiles_per_head;  // work-groups per (b, h), max over heads (grid partition)
     int dil[LF_MAX_HEADS];
-    int g[LF_MAX_GLOBALS];  // sorted, distinct
+    int g[LF_MAX_GLOBALS];          // sorted, distinct
 };
 
 // Launchers (defined in lf_attn_kernels.hip).  Return the launch error.
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s);
-hipError_t launch_global_rows(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s);
 
 }  // namespace lf

@@ -1,11 +1,14 @@
 // gfx950 (MI355X) kernels of the Longformer window + global attention forward.
 //
-// Three kernels, all launched on the caller's stream:
-//   band_kernel        window keys of every non-global row, with the global keys
-//                      outside the window folded into the same online softmax;
-//   global_rows_kernel split-key partials (max, sum, unnormalised output) of the
-//                      global rows over every unpadded key;
-//   merge_kernel       log-sum-exp merge of those partials, global rows written.
+// band_kernel: one work-group per 128 rows of one residue class of one (b, h):
+//   (a) window band: the window keys of every row of the tile, streamed through
+//       LDS in 64-key stages;
+//   (b) global columns: the global keys outside each row's window, folded into the
+//       same online softmax before the band;
+//   (c) global rows: each work-group folds the global queries over its own 128
+//       "home" keys and writes one partial (max, sum, unnormalised output) per query.
+// merge_kernel:
+//   (d) log-sum-exp merge of those partials in tile order; writes the global rows.
 //
 // The key set of a query is the union of its dilated window and the global keys
 // (page "基于自注意力机制的长文本建模算法：Longformer详解" §2 and §4); global rows see
@@ -19,14 +22,19 @@
 // strided gather ("virtual" index i' with i = r + i'*dil).  Global keys ignore the
 // lattice and are folded with an in-window test that keeps each key counted once.
 //
+// Data movement: K and V stages of 64 keys go from HBM/L2 straight into LDS with
+// global_load_lds_dwordx4 (no VGPR round trip), into a ring of stages so that the
+// loads of the next stages are in flight while the current one is computed.  Keys
+// that are padded, out of range or unused read a static zero row, so their LDS rows
+// are zero and their contents never reach the output.  V stays row-major in LDS
+// and the P.V product reads it transposed with ds_read_b64_tr_b16.
+//
 // Register layout (v_mfma_f32_32x32x*): accumulator element i of lane l sits at
 // row 8*(i/4) + 4*(l/32) + (i%4), column l%32.  Scores are computed transposed
 // (rows = keys, columns = queries) so each lane owns one query: its row statistics
 // need one exchange with the lane 32 away, and its 16 score values feed the P^T
 // operand of the next product unchanged.  K rows are read in the order sigma(M) so
-// that accumulator element i of lane-half h2 holds key 16*(i/8) + 8*h2 + (i%8); the
-// output dimension is read in the order pi(M) so each lane ends up holding 16
-// consecutive output columns.
+// that accumulator element i of lane-half h2 holds key 16*(i/8) + 8*h2 + (i%8).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,31 +45,49 @@ namespace lf {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+#define LF_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
 // exp(x / sqrt(64)) = exp2(x * log2(e) / 8)
 constexpr float kScaleLog2 = 1.4426950408889634f * 0.125f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kStageKeys = kKeysPerTile;  // 64
 constexpr int kNoPos = -(1 << 29);        // virtual position that is in no window
+constexpr int kMaskWindow = 64;           // band stages whose pad masks are built at once
+constexpr int kMaskRing = 2 * kMaskWindow;
+constexpr int kMaxGlobalStages = LF_MAX_GLOBALS / kStageKeys;
+constexpr int kLargeW = 1 << 28;  // band test that admits every key (|key - query| < 2^28)
+
+#ifndef LF_BF16_WAVES_PER_EU
+#define LF_BF16_WAVES_PER_EU 3
+#endif
+#ifndef LF_BF16_NS
+#define LF_BF16_NS 2
+#endif
+
+// Source of every invalid key: 256 zero bytes (one fp32 row, two bf16 rows).
+__device__ __attribute__((aligned(16))) uint32_t g_zero_row[64];
 
 __device__ __forceinline__ int sigma(int M) {  // K row read by lane row M
     const int q = M >> 3, hh = (M >> 2) & 1, c = M & 3;
     return 16 * (q >> 1) + 8 * hh + 4 * (q & 1) + c;
 }
-__device__ __forceinline__ int pi_col(int M) {  // output column read by lane row M
-    const int q = M >> 3, hh = (M >> 2) & 1, c = M & 3;
-    return 16 * hh + 4 * q + c;
-}
 __device__ __forceinline__ int key_local(int i, int h2) { return 16 * (i >> 3) + 8 * h2 + (i & 7); }
 
-// LDS swizzles of 16-byte chunks (bank-conflict-free 128-bit reads of the lane
-// patterns above: every 8 consecutive lanes hit 8 distinct chunks).
+// LDS swizzles of 16-byte chunks.  K: every 8 consecutive lanes of the 128-bit
+// operand reads (rows sigma(0..7) + c) hit 8 distinct chunks.  V: the four rows of
+// each 16-lane transposed read land on four distinct 32-byte slots.
 __device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int swz_v(int d) { return (d & 3) | ((d >> 2) & 4); }
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
 
 // Lanes l and l^32 hold the two halves of one query's keys.
 __device__ __forceinline__ float pair_max(float x) {
@@ -74,6 +100,34 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ uint64_t ballot64(bool x) { return __ballot(x); }
+
+// 16 bytes per lane from global memory into LDS at base + 16 * lane (base uniform).
+// Issued as inline asm: the compiler then does not treat the in-flight copies as
+// possibly aliasing later LDS reads (it would drain every copy with vmcnt(0) before
+// each transposed read).  Completion is awaited explicitly with wait_vmcnt before
+// the barrier that publishes a stage.  The instruction has no register results.
+// M0 carries the LDS base; no other code in these kernels keeps a value in M0.
+__device__ __forceinline__ void dma16(const void* src, char* lds_base) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Work-group barrier without a memory fence: ordering of the staged LDS data is
+// established by the explicit vmcnt waits; the empty asm keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Work-groups are dispatched round-robin over the 8 XCDs; hand each XCD a
 // contiguous range of logical ids so that neighbouring row tiles of one (b, h),
@@ -88,38 +142,20 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// Element-type traits: operand loads, K/V staging and the two products.
-// A stage holds 64 keys: K row-major (64 x 64), and V row-major (fp32) or
-// transposed V^T (bf16: the P^T.V contraction wants 8 consecutive keys per lane).
+// Element-type traits: operand loads, stage DMA, the two products, output store.
+// A stage holds 64 keys: K (64 x 64) then V (64 x 64), both row-major.  Output
+// column d of lane (query, h2) accumulator element i is 32*db + 8*(i/4) + 4*h2 + i%4.
 
 struct Bf16 {
     using Elem = uint16_t;
-    static constexpr int kKBytes = kStageKeys * 128;   // 8 KiB
-    static constexpr int kStageBytes = 2 * kKBytes;    // K + V^T
+    static constexpr int kRowBytes = 128;
+    static constexpr int kTileBytes = kStageKeys * kRowBytes;  // 8 KiB
+    static constexpr int kStageBytes = 2 * kTileBytes;        // K + V
+    static constexpr int kNS = LF_BF16_NS;                    // stages in the LDS ring
+    static constexpr int kDmaPerStage = 4;                    // per wave: 2 for K, 2 for V
+    static constexpr int kWavesPerEU = LF_BF16_WAVES_PER_EU;
     struct QOp { bf16x8 v[4]; };
-    struct Regs { u32x4 k[2]; u32x4 v[2]; };
     struct PFrag { bf16x8 v[2]; };
-
-    // Round the weights to bf16 (the P^T operand) and return their sum as rounded,
-    // so the normaliser matches the weights the product uses.
-    __device__ static float make_p(const float* p, PFrag& pf) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        float sum = 0.f;
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x8 t;
-            for (int j = 0; j < 8; ++j) t[j] = p[8 * kb + j];
-            const bf16x8 b = __builtin_convertvector(t, bf16x8);
-            pf.v[kb] = b;
-            // Sub-vectors by shuffle: hipcc mis-selects dot2 operands taken as words of
-            // a bit-cast of the converted vector (every word reads as the first).
-            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), one, sum, false);
-            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), one, sum, false);
-            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), one, sum, false);
-            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), one, sum, false);
-        }
-        return sum;
-    }
 
     // B operand of S^T = K Q^T: lane (query, h2) holds d = 16*kb + 8*h2 + j.
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
@@ -129,80 +165,106 @@ struct Bf16 {
         }
     }
 
-    // Global -> registers.  row_of(kk) gives the source row of stage key kk, or -1
-    // (zero fill: padded, out of range or unused slot).
+    // Stage DMA by all four waves: wave wv fills 1-KiB blocks 2*wv and 2*wv+1 of K
+    // and of V (8 rows each).  row_of(kk) is the source row of stage key kk or -1.
     template <class RowOf>
-    __device__ static void load(Regs& r, const Elem* K, const Elem* V, RowOf row_of, int tid) {
+    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane) {
+        const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 2; ++u) {
-            const int c = tid + kThreads * u, kk = c >> 3, col = c & 7;
-            const int row = row_of(kk);
-            r.k[u] = row >= 0 ? *reinterpret_cast<const u32x4*>(K + (size_t)row * 64 + col * 8) : u32x4{0, 0, 0, 0};
-        }
-        const int kk = tid & 63;
-        const int row = row_of(kk);
-        for (int u = 0; u < 2; ++u) {
-            const int dc = (tid >> 6) + 4 * u;
-            r.v[u] = row >= 0 ? *reinterpret_cast<const u32x4*>(V + (size_t)row * 64 + dc * 8) : u32x4{0, 0, 0, 0};
+            const int blk = 2 * wv + u;
+            const int row = 8 * blk + (lane >> 3), cl = lane & 7;
+            const int src = row_of(row);
+            const Elem* kr = src >= 0 ? K + (size_t)src * 64 : zero;
+            const Elem* vr = src >= 0 ? V + (size_t)src * 64 : zero;
+            dma16(kr + 8 * (cl ^ swz_k(row)), slot + blk * 1024);
+            dma16(vr + 8 * (cl ^ swz_v(row)), slot + kTileBytes + blk * 1024);
         }
     }
 
-    __device__ static void store(char* stage, const Regs& r, int tid) {
-        char* Ks = stage;
-        char* Vt = stage + kKBytes;
-        for (int u = 0; u < 2; ++u) {
-            const int c = tid + kThreads * u, kk = c >> 3, col = c & 7;
-            *reinterpret_cast<u32x4*>(Ks + kk * 128 + ((col ^ swz_k(kk)) << 4)) = r.k[u];
-        }
-        const int kk = tid & 63;
-        for (int u = 0; u < 2; ++u) {
-            const int dc = (tid >> 6) + 4 * u;
-            for (int j = 0; j < 8; ++j) {
-                const int d = 8 * dc + j;
-                const uint32_t word = r.v[u][j >> 1];
-                const uint16_t val = (j & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xffffu);
-                *reinterpret_cast<uint16_t*>(Vt + d * 128 + (((kk >> 3) ^ swz_v(d)) << 4) + (kk & 7) * 2) = val;
-            }
+    // Per-lane LDS byte offsets of the operand reads, independent of the stage slot
+    // and of the sub-tile (the swizzles only depend on the row modulo 8).
+    struct Lane {
+        int k[4];  // K operand: row sigma(M), chunk (2*kb + h2) ^ swz_k(row)
+        int v[2];  // V^T operand: row 8*h2 + i/4 (+ 4*t + 16*kb + 32*sub), per column block db
+    };
+    __device__ static void lane_offsets(Lane& lo, int lane) {
+        const int row = sigma(lane & 31), h2 = lane >> 5;
+        for (int kb = 0; kb < 4; ++kb) lo.k[kb] = row * kRowBytes + (((2 * kb + h2) ^ swz_k(row)) << 4);
+        const int g1 = (lane >> 4) & 1, i = lane & 15;
+        const int vrow = 8 * h2 + (i >> 2);
+        for (int db = 0; db < 2; ++db) {
+            const int chunk = 4 * db + 2 * g1 + ((i & 3) >> 1);
+            lo.v[db] = kTileBytes + vrow * kRowBytes + ((chunk ^ swz_v(vrow)) << 4) + 8 * (i & 1);
         }
     }
 
     // S^T (32 keys x 32 queries) of sub-tile `sub` (keys 32*sub .. 32*sub+31 of the stage).
-    __device__ static f32x16 qk(const char* stage, int sub, int lane, const QOp& q) {
-        const int row = 32 * sub + sigma(lane & 31), h2 = lane >> 5;
-        const char* base = stage + row * 128;
-        const int sw = swz_k(row);
+    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q) {
+        const char* base = slot + sub * 32 * kRowBytes;
         f32x16 acc = {};
         for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + (((2 * kb + h2) ^ sw) << 4));
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + lo.k[kb]);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[kb], acc, 0, 0, 0);
         }
         return acc;
     }
 
-    // O^T += V^T P^T over the 32 keys of sub-tile `sub`.
-    __device__ static void pv(const char* stage, int sub, int lane, const PFrag& pf, f32x16* o) {
-        const int M = lane & 31, h2 = lane >> 5;
-        const char* Vt = stage + kKBytes;
-        for (int db = 0; db < 2; ++db) {
-            const int d = 32 * db + pi_col(M);
-            const char* rowp = Vt + d * 128;
-            const int sw = swz_v(d);
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowp + (((4 * sub + 2 * kb + h2) ^ sw) << 4));
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.v[kb], o[db], 0, 0, 0);
-            }
+    // Round the weights to bf16 (the P^T operand) and return their sum as rounded,
+    // so the normaliser matches the weights the product uses.
+    __device__ static float make_p(const float* p, PFrag& pf) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float sum[2] = {0.f, 0.f};  // two independent accumulation chains
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x8 t;
+            for (int j = 0; j < 8; ++j) t[j] = p[8 * kb + j];
+            const bf16x8 b = __builtin_convertvector(t, bf16x8);
+            pf.v[kb] = b;
+            // Sub-vectors by shuffle: hipcc mis-selects dot2 operands taken as words of
+            // a bit-cast of the converted vector (every word reads as the first).
+            float& acc = sum[kb];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), one, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), one, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), one, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), one, acc, false);
         }
+        return sum[0] + sum[1];
     }
 
-    // Lane (query, h2) holds output columns 32*db + 16*h2 + 0..15.
-    __device__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
-        for (int db = 0; db < 2; ++db) {
-            for (int half = 0; half < 2; ++half) {
-                f32x8 t;
-                for (int j = 0; j < 8; ++j) t[j] = o[db][8 * half + j] * scale;
-                const bf16x8 b = __builtin_convertvector(t, bf16x8);
-                *reinterpret_cast<u32x4*>(row + 32 * db + 16 * h2 + 8 * half) = __builtin_bit_cast(u32x4, b);
+    // O^T += V^T P^T over the 32 keys of sub-tile `sub`.  The V^T operand (lane l:
+    // column 32*db + l%32, keys 16*kb + 8*h2 + 0..7) comes from two transposed
+    // reads: within each 16-lane group, input lane i addresses row base + i/4,
+    // columns 4*(i%4)..+3, and output lane o receives column o of rows base..base+3.
+    // Rows base = 32*sub + 16*kb + 8*h2 + 4*t are multiples of 4, so the V swizzle
+    // (row modulo 4) is the same for all of them.
+    struct VOp { bf16x8 v[2][2]; };  // [db][kb]
+    __device__ static void load_v(VOp& vo, const char* slot, int sub, const Lane& lo) {
+        const char* base = slot + sub * 32 * kRowBytes;
+        for (int db = 0; db < 2; ++db)
+            for (int kb = 0; kb < 2; ++kb) {
+                const char* a = base + lo.v[db] + 16 * kb * kRowBytes;
+                const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a));
+                const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a + 4 * kRowBytes));
+                vo.v[db][kb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
             }
-        }
+    }
+    __device__ static void pv(const VOp& vo, const PFrag& pf, f32x16* o) {
+        for (int kb = 0; kb < 2; ++kb)
+            for (int db = 0; db < 2; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.v[db][kb], pf.v[kb], o[db], 0, 0, 0);
+    }
+
+    __device__ static uint32_t pack_bf16(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    }
+
+    __device__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+        for (int db = 0; db < 2; ++db)
+            for (int q = 0; q < 4; ++q) {
+                const float a = o[db][4 * q] * scale, b = o[db][4 * q + 1] * scale;
+                const float c = o[db][4 * q + 2] * scale, d = o[db][4 * q + 3] * scale;
+                const u32x2 w = {pack_bf16(a, b), pack_bf16(c, d)};
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * h2) = w;
+            }
     }
 
     __device__ static Elem from_float(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -210,11 +272,62 @@ struct Bf16 {
 
 struct F32 {
     using Elem = float;
-    static constexpr int kKBytes = kStageKeys * 256;   // 16 KiB
-    static constexpr int kStageBytes = 2 * kKBytes;    // K + V, both row-major
+    static constexpr int kRowBytes = 256;
+    static constexpr int kTileBytes = kStageKeys * kRowBytes;  // 16 KiB
+    static constexpr int kStageBytes = 2 * kTileBytes;        // K + V
+    static constexpr int kNS = 2;
+    static constexpr int kDmaPerStage = 8;                    // per wave: 4 for K, 4 for V (kNS = 2: unused)
+    static constexpr int kWavesPerEU = 1;
     struct QOp { float v[32]; };
-    struct Regs { u32x4 k[4]; u32x4 v[4]; };
     struct PFrag { float v[16]; };
+
+    // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t.
+    __device__ static void load_q(QOp& q, const Elem* row, int h2) {
+        for (int t4 = 0; t4 < 8; ++t4) {
+            f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4) : f32x4{0, 0, 0, 0};
+            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
+        }
+    }
+
+    // Wave wv fills 1-KiB blocks 4*wv .. 4*wv+3 of K and of V (4 rows each).
+    template <class RowOf>
+    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane) {
+        const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
+        for (int u = 0; u < 4; ++u) {
+            const int blk = 4 * wv + u;
+            const int row = 4 * blk + (lane >> 4), cl = lane & 15;
+            const int src = row_of(row);
+            const Elem* kr = src >= 0 ? K + (size_t)src * 64 : zero;
+            const Elem* vr = src >= 0 ? V + (size_t)src * 64 : zero;
+            dma16(kr + 4 * (cl ^ swz_k(row)), slot + blk * 1024);
+            dma16(vr + 4 * cl, slot + kTileBytes + blk * 1024);
+        }
+    }
+
+    struct Lane {
+        int k;  // K operand row sigma(M) (chunks swizzled by swz_k)
+        int sw;
+        int h2;
+        int v;  // V operand column 32*db + M of key key_local(u, h2): base of column M
+    };
+    __device__ static void lane_offsets(Lane& lo, int lane) {
+        const int row = sigma(lane & 31);
+        lo.k = row * kRowBytes;
+        lo.sw = swz_k(row);
+        lo.h2 = lane >> 5;
+        lo.v = kTileBytes + 4 * (lane & 31);
+    }
+
+    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q) {
+        const char* base = slot + sub * 32 * kRowBytes + lo.k;
+        f32x16 acc = {};
+        for (int t4 = 0; t4 < 8; ++t4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(base + (((8 * lo.h2 + t4) ^ lo.sw) << 4));
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q.v[4 * t4 + e], acc, 0, 0, 0);
+        }
+        return acc;
+    }
 
     __device__ static float make_p(const float* p, PFrag& pf) {
         float sum = 0.f;
@@ -225,71 +338,44 @@ struct F32 {
         return sum;
     }
 
-    // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t.
-    __device__ static void load_q(QOp& q, const Elem* row, int h2) {
-        for (int t4 = 0; t4 < 8; ++t4) {
-            f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4) : f32x4{0, 0, 0, 0};
-            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
-        }
-    }
-
-    template <class RowOf>
-    __device__ static void load(Regs& r, const Elem* K, const Elem* V, RowOf row_of, int tid) {
-        for (int u = 0; u < 4; ++u) {
-            const int c = tid + kThreads * u, kk = c >> 4, col = c & 15;
-            const int row = row_of(kk);
-            r.k[u] = row >= 0 ? *reinterpret_cast<const u32x4*>(K + (size_t)row * 64 + col * 4) : u32x4{0, 0, 0, 0};
-            r.v[u] = row >= 0 ? *reinterpret_cast<const u32x4*>(V + (size_t)row * 64 + col * 4) : u32x4{0, 0, 0, 0};
-        }
-    }
-
-    __device__ static void store(char* stage, const Regs& r, int tid) {
-        char* Ks = stage;
-        char* Vs = stage + kKBytes;
-        for (int u = 0; u < 4; ++u) {
-            const int c = tid + kThreads * u, kk = c >> 4, col = c & 15;
-            *reinterpret_cast<u32x4*>(Ks + kk * 256 + ((col ^ swz_k(kk)) << 4)) = r.k[u];
-            *reinterpret_cast<u32x4*>(Vs + kk * 256 + (col << 4)) = r.v[u];
-        }
-    }
-
-    __device__ static f32x16 qk(const char* stage, int sub, int lane, const QOp& q) {
-        const int row = 32 * sub + sigma(lane & 31), h2 = lane >> 5;
-        const char* base = stage + row * 256;
-        const int sw = swz_k(row);
-        f32x16 acc = {};
-        for (int t4 = 0; t4 < 8; ++t4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(base + (((8 * h2 + t4) ^ sw) << 4));
-            for (int e = 0; e < 4; ++e)
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q.v[4 * t4 + e], acc, 0, 0, 0);
-        }
-        return acc;
-    }
-
     // Step u pairs lane-half h2 with key key_local(u, h2), matching the score layout.
-    __device__ static void pv(const char* stage, int sub, int lane, const PFrag& pf, f32x16* o) {
-        const int M = lane & 31, h2 = lane >> 5;
-        const float* Vs = reinterpret_cast<const float*>(stage + kKBytes);
-        for (int db = 0; db < 2; ++db) {
-            const int d = 32 * db + pi_col(M);
+    struct VOp { const char* base; int h2; };
+    __device__ static void load_v(VOp& vo, const char* slot, int sub, const Lane& lo) {
+        vo.base = slot + sub * 32 * kRowBytes + lo.v;
+        vo.h2 = lo.h2;
+    }
+    __device__ static void pv(const VOp& vo, const PFrag& pf, f32x16* o) {
+        for (int db = 0; db < 2; ++db)
             for (int u = 0; u < 16; ++u) {
-                const float a = Vs[(32 * sub + key_local(u, h2)) * 64 + d];
+                const float a = *reinterpret_cast<const float*>(vo.base + key_local(u, vo.h2) * kRowBytes + 128 * db);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.v[u], o[db], 0, 0, 0);
             }
-        }
     }
 
     __device__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
         for (int db = 0; db < 2; ++db)
-            for (int c = 0; c < 4; ++c) {
+            for (int q = 0; q < 4; ++q) {
                 f32x4 t;
-                for (int j = 0; j < 4; ++j) t[j] = o[db][4 * c + j] * scale;
-                *reinterpret_cast<f32x4*>(row + 32 * db + 16 * h2 + 4 * c) = t;
+                for (int j = 0; j < 4; ++j) t[j] = o[db][4 * q + j] * scale;
+                *reinterpret_cast<f32x4*>(row + 32 * db + 8 * q + 4 * h2) = t;
             }
     }
 
     __device__ static Elem from_float(float x) { return x; }
 };
+
+// Wait until this wave's loads of the oldest outstanding stage have landed, given
+// that `ahead` later stages have been issued since.
+template <class T>
+__device__ __forceinline__ void wait_stage(int ahead) {
+    if constexpr (T::kNS > 2) {
+        if (ahead >= 1) {
+            wait_vmcnt<T::kDmaPerStage>();
+            return;
+        }
+    }
+    wait_vmcnt<0>();
+}
 
 // ---------------------------------------------------------------------------
 // Online softmax state of one lane: running max m (raw score units), the lane's
@@ -313,12 +399,12 @@ __device__ __forceinline__ void state_init(State& st) {
 // the output/sum rescale runs only on the few blocks that raise a max.
 constexpr float kRaiseRaw = 8.0f / kScaleLog2;
 
-// Fold one 32-key score block into the state; the weights go to the P^T operand.
+// Fold one 32-key score tile into the state; the weights go to the P^T operand.
 template <class T>
 __device__ __forceinline__ void online_update(State& st, const f32x16& s, typename T::PFrag& pf) {
-    float mx = s[0];
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = pair_max(mx);
+    float m4[4];
+    for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(s[4 * j], s[4 * j + 1]), fmaxf(s[4 * j + 2], s[4 * j + 3]));
+    const float mx = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     const bool raise = mx > st.m + kRaiseRaw;  // a first finite block always raises
     if (__any(raise)) {
         // Lanes that keep their max keep alpha = 1 (their max may still be -inf).
@@ -335,6 +421,38 @@ __device__ __forceinline__ void online_update(State& st, const f32x16& s, typena
     st.l += T::make_p(p, pf);
 }
 
+// Element i of a 32-key score tile holds stage key 32*sub + kc(i) + 8*h2.
+__device__ __forceinline__ constexpr int kc_of(int i) { return 16 * (i >> 3) + (i & 7); }
+
+// One 32-key sub-tile of a stage: scores, masks, softmax update, P.V product.
+// MODE 0: no mask needed; 1: band mask, base = (first key of the sub-tile) + 8*h2
+// - query + w; 2: global keys (gp: in-window positions of the sub-tile's keys).
+template <class T>
+__device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, const typename T::Lane& lo,
+                                         const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
+                                         int w, const int* gp, int wq) {
+    f32x16 s = T::qk(slot, sub, lo, q);
+    typename T::VOp vo;
+    T::load_v(vo, slot, sub, lo);  // in flight during the softmax
+    if (mode != 0) {
+        const uint32_t invl = inv32 >> (8 * h2);
+        if (mode == 1) {
+            for (int i = 0; i < 16; ++i) {
+                const int kc = kc_of(i);
+                if ((unsigned)(base + kc) > (unsigned)(2 * w) || ((invl >> kc) & 1)) s[i] = kNegInf;
+            }
+        } else {
+            for (int i = 0; i < 16; ++i) {
+                const int kc = kc_of(i);
+                if (((invl >> kc) & 1) || (unsigned)(gp[kc] + wq) <= (unsigned)(2 * w)) s[i] = kNegInf;
+            }
+        }
+    }
+    typename T::PFrag pf;
+    online_update<T>(st, s, pf);
+    T::pv(vo, pf, st.o);
+}
+
 __device__ __forceinline__ bool is_global_row(const Params& p, int row) {
     int lo = 0, hi = p.n_g;  // sorted, distinct
     while (lo < hi) {
@@ -346,31 +464,35 @@ __device__ __forceinline__ bool is_global_row(const Params& p, int row) {
     return false;
 }
 
-__device__ __forceinline__ uint64_t ballot64(bool x) { return __ballot(x); }
-
 // ---------------------------------------------------------------------------
 // (a)+(b): one work-group = 128 consecutive rows of one residue class of one
-// (b, h); wave wv owns rows r0 + 32*wv .. +31.  Global keys outside each row's
-// window are folded first; then the window band is streamed in 64-key stages
-// (double-buffered in LDS), each wave skipping 32-key sub-tiles outside its rows'
-// band and masking only sub-tiles that touch the band edge or hold invalid keys.
+// (b, h); wave wv owns rows r0 + 32*wv .. +31.  The stage sequence is the global
+// keys (up to 64 per stage, with an in-window test so each key counts once)
+// followed by the window band [kb0, kend) of the class in 64-key stages.  Each
+// wave skips 32-key sub-tiles outside its rows' band and masks only sub-tiles
+// that touch the band edge or hold invalid keys.
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void band_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
+void band_kernel(const Params p) {
     using Elem = typename T::Elem;
-    __shared__ __attribute__((aligned(16))) char smem[2 * T::kStageBytes + 64 * sizeof(int)];
-    int* gpos = reinterpret_cast<int*>(smem + 2 * T::kStageBytes);
+    __shared__ __attribute__((aligned(16))) char ring[T::kNS * T::kStageBytes];
+    __shared__ uint64_t band_mask[kMaskRing];        // invalid-key bits of band stages
+    __shared__ uint64_t glob_mask[kMaxGlobalStages];  // invalid-key bits of global stages
+    __shared__ int glob_src[LF_MAX_GLOBALS];          // source row of each global slot or -1
+    __shared__ int glob_pos[LF_MAX_GLOBALS];          // same-class virtual position or kNoPos
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h2 = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int pid = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = pid / p.tiles_per_head, t = pid - bh * p.tiles_per_head;
+    const int bh = pid / p.tiles_per_head, t_in = pid - bh * p.tiles_per_head;
     const int h = bh % p.H, b = bh / p.H;
     const int L = p.L, w = p.w, dil = p.dil[h];
     const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;  // tiles per residue
-    const int r = t / tpr;
+    const int r = t_in / tpr;
     if (r >= dil) return;
     const int Lr = (L - r + dil - 1) / dil;  // rows in residue class r
-    const int r0 = (t - r * tpr) * kRowsPerBlock;
+    const int r0 = (t_in - r * tpr) * kRowsPerBlock;
     if (r0 >= Lr) return;
 
     const size_t off = (size_t)bh * L * 64;
@@ -380,96 +502,110 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const Params p) {
     Elem* O = reinterpret_cast<Elem*>(p.out) + off;
     const uint8_t* pad = p.pad ? p.pad + (size_t)b * L : nullptr;
 
-    const int qa = r0 + 32 * wv;           // first virtual row of this wave
-    const int qv = qa + (lane & 31);       // this lane's virtual row
+    const int qa = r0 + 32 * wv;      // first virtual row of this wave
+    const int qv = qa + (lane & 31);  // this lane's virtual row
     const bool rows_live = qa < Lr;
     typename T::QOp qop;
     T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * 64 : nullptr, h2);
-    State st;
-    state_init(st);
-    typename T::PFrag pw;
-    typename T::Regs regs;
 
-    // (b) global keys, up to 64 per stage.
-    for (int g0 = 0; g0 < p.n_g; g0 += kStageKeys) {
-        const int gi = g0 + lane;
-        const int gphys = gi < p.n_g ? p.g[gi] : -1;
-        const bool ok = gphys >= 0 && (!pad || pad[gphys] == 0);
-        const uint64_t inv = ~ballot64(ok);
-        if (inv == ~0ull) continue;
-        T::load(regs, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : p.g[g0 + kk]; }, tid);
-        T::store(smem, regs, tid);
-        if (tid < 64) {  // same-class globals: virtual position, for the in-window test
-            const bool same = ok && gphys >= r && (gphys - r) % dil == 0;
-            gpos[tid] = same ? (gphys - r) / dil : kNoPos;
-        }
-        __syncthreads();
-        if (rows_live) {
-            for (int sub = 0; sub < 2; ++sub) {
-                const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
-                if (inv32 == ~0u) continue;
-                f32x16 s = T::qk(smem, sub, lane, qop);
-                for (int i = 0; i < 16; ++i) {
-                    const int kl = key_local(i, h2);
-                    const int gp = gpos[32 * sub + kl];
-                    const bool in_window = (unsigned)(gp - qv + w) <= (unsigned)(2 * w);
-                    if (((inv32 >> kl) & 1) || in_window) s[i] = kNegInf;
-                }
-                online_update<T>(st, s, pw);
-                T::pv(smem, sub, lane, pw, st.o);
-            }
-        }
-        __syncthreads();
-    }
-
-    // (a) window band of this tile's rows: keys [kb0, kend) of the class.
     const int kb0 = max(0, r0 - w);
     const int kend = min(Lr, r0 + kRowsPerBlock + w);
-    const int n_st = (kend - kb0 + kStageKeys - 1) / kStageKeys;
-    auto invalid_of = [&](int st_idx) -> uint64_t {
-        const int key = kb0 + kStageKeys * st_idx + lane;
-        bool ok = key < kend;
-        if (ok && pad) ok = pad[r + key * dil] == 0;
-        return ~ballot64(ok);
-    };
-    auto row_fn = [&](int ks, uint64_t inv) {
-        return [=](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; };
-    };
+    const int n_band = (kend - kb0 + kStageKeys - 1) / kStageKeys;
+    const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
+    const int n_st = n_gst + n_band;
 
-    uint64_t inv_cur = n_st > 0 ? invalid_of(0) : ~0ull;
-    if (inv_cur != ~0ull) {
-        T::load(regs, K, V, row_fn(kb0, inv_cur), tid);
-        T::store(smem, regs, tid);
+    // Global slots: source row (or -1 if unused/padded) and in-window position.
+    for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
+        const int g = gi < p.n_g ? p.g[gi] : -1;
+        const bool ok = g >= 0 && (!pad || pad[g] == 0);
+        glob_src[gi] = ok ? g : -1;
+        glob_pos[gi] = (ok && g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
     }
-    __syncthreads();
-    for (int s_i = 0; s_i < n_st; ++s_i) {
-        const int ks = kb0 + kStageKeys * s_i;
-        const uint64_t inv_next = s_i + 1 < n_st ? invalid_of(s_i + 1) : ~0ull;
-        if (inv_next != ~0ull) T::load(regs, K, V, row_fn(ks + kStageKeys, inv_next), tid);
-        const char* cur = smem + (s_i & 1) * T::kStageBytes;
-        if (rows_live && inv_cur != ~0ull) {
-            for (int sub = 0; sub < 2; ++sub) {
-                const int kss = ks + 32 * sub;
-                const uint32_t inv32 = (uint32_t)(inv_cur >> (32 * sub));
-                if (inv32 == ~0u) continue;
-                if (kss > qa + 31 + w || kss + 31 < qa - w) continue;  // outside every row's band
-                const bool interior = kss >= qa + 31 - w && kss + 31 <= qa + w;
-                f32x16 s = T::qk(cur, sub, lane, qop);
-                if (!interior || inv32 != 0u) {
-                    for (int i = 0; i < 16; ++i) {
-                        const int kl = key_local(i, h2);
-                        const int kv = kss + kl;
-                        const bool ok = (unsigned)(kv - qv + w) <= (unsigned)(2 * w) && !((inv32 >> kl) & 1);
-                        if (!ok) s[i] = kNegInf;
-                    }
-                }
-                online_update<T>(st, s, pw);
-                T::pv(cur, sub, lane, pw, st.o);
+    // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ...
+    auto fill_band_masks = [&](int W) {
+        constexpr int kPer = kMaskWindow / kWaves, kGroup = 4;
+        for (int j0 = 0; j0 < kPer; j0 += kGroup) {
+            uint32_t flag[kGroup];
+            for (int j = 0; j < kGroup; ++j) {
+                const int bs = W * kMaskWindow + wv + kWaves * (j0 + j);
+                const int key = kb0 + kStageKeys * bs + lane;
+                flag[j] = (bs < n_band && key < kend) ? pad[r + key * dil] : 1u;
+            }
+            for (int j = 0; j < kGroup; ++j) {
+                const int bs = W * kMaskWindow + wv + kWaves * (j0 + j);
+                const uint64_t inv = ballot64(flag[j] != 0);
+                if (lane == 0 && bs < n_band) band_mask[bs % kMaskRing] = inv;
             }
         }
-        if (inv_next != ~0ull) T::store(smem + ((s_i + 1) & 1) * T::kStageBytes, regs, tid);
-        __syncthreads();
-        inv_cur = inv_next;
+    };
+    if (pad) fill_band_masks(0);
+    __syncthreads();
+    if (wv == 0)
+        for (int s = 0; s < n_gst; ++s) {
+            const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
+            if (lane == 0) glob_mask[s] = inv;
+        }
+    __syncthreads();
+
+    auto band_invalid = [&](int bs) -> uint64_t {
+        if (pad) return band_mask[bs % kMaskRing];
+        const int n = kend - (kb0 + kStageKeys * bs);  // valid keys in this stage
+        return n >= 64 ? 0ull : (n <= 0 ? ~0ull : (~0ull << n));
+    };
+    auto issue = [&](int s) {
+        char* slot = ring + (s % T::kNS) * T::kStageBytes;
+        if (s < n_gst) {
+            const int* src = glob_src + kStageKeys * s;
+            T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane);
+        } else {
+            const int bs = s - n_gst;
+            const uint64_t inv = band_invalid(bs);
+            const int ks = kb0 + kStageKeys * bs;
+            T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv,
+                         lane);
+        }
+    };
+
+    State st;
+    state_init(st);
+    typename T::Lane lo;
+    T::lane_offsets(lo, lane);
+
+    // Every register load (Q operand, masks) completes here, so the compiler's own
+    // waits inside the loop have nothing left to wait for: an in-loop vmcnt wait
+    // would also drain the stage copies in flight.
+    wait_vmcnt<0>();
+    for (int s = 0; s < T::kNS - 1; ++s)
+        if (s < n_st) issue(s);
+    for (int t = 0; t < n_st; ++t) {
+        wait_stage<T>(min(T::kNS - 2, n_st - 1 - t));
+        barrier_nofence();
+        const int sn = t + T::kNS - 1;
+        if (sn < n_st) {
+            const int bn = sn - n_gst;
+            if (pad && bn > 0 && bn % kMaskWindow == 0) {
+                fill_band_masks(bn / kMaskWindow);
+                __syncthreads();
+            }
+            issue(sn);
+        }
+        const char* slot = ring + (t % T::kNS) * T::kStageBytes;
+        const bool gstage = t < n_gst;
+        const int ks = kb0 + kStageKeys * (t - n_gst);
+        const uint64_t inv = gstage ? glob_mask[t] : band_invalid(t - n_gst);
+        if (rows_live && inv != ~0ull) {
+#pragma unroll 1
+            for (int sub = 0; sub < 2; ++sub) {
+                const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
+                const int kss = ks + 32 * sub;
+                if (inv32 == ~0u) continue;
+                if (!gstage && (kss > qa + 31 + w || kss + 31 < qa - w)) continue;  // outside every row's band
+                const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + w;
+                const int mode = gstage ? 2 : (interior ? 0 : 1);
+                sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, kss + 8 * h2 - qv + w, w,
+                            glob_pos + kStageKeys * t + 32 * sub + 8 * h2, w - qv);
+            }
+        }
     }
 
     const float lt = pair_sum(st.l);
@@ -478,131 +614,137 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const Params p) {
         const int row = r + qv * dil;
         if (!is_global_row(p, row)) T::store_row(O + (size_t)row * 64, h2, st.o, scale);
     }
+    if (p.n_g == 0) return;
+
+    // (c) Global rows: every key belongs to exactly one work-group's "home" range
+    // [r0, r0 + 128) of its class, so each work-group folds the global queries over
+    // its home keys and leaves one partial (max, sum, unnormalised output) per query.
+    __shared__ float red_ml[kWaves][32][2];
+    float* red_o = reinterpret_cast<float*>(ring);  // kWaves x 32 x 64 floats = 32 KiB
+    const int home_end = min(Lr, r0 + kRowsPerBlock);
+    const size_t part0 = ((size_t)bh * p.tiles_per_head + t_in) * p.n_gblk * kGlobalQueriesPerBlock;
+    for (int gb = 0; gb < p.n_gblk; ++gb) {
+        const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
+        typename T::QOp gop;
+        T::load_q(gop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
+        uint64_t hinv[2];
+        for (int hs = 0; hs < 2; ++hs) {
+            const int key = r0 + kStageKeys * hs + lane;
+            bool ok = key < home_end;
+            if (ok && pad) ok = pad[r + key * dil] == 0;
+            hinv[hs] = ~ballot64(ok);
+        }
+        __syncthreads();  // the ring is free
+        for (int hs = 0; hs < 2; ++hs) {
+            const uint64_t iv = hinv[hs];
+            const int ks = r0 + kStageKeys * hs;
+            T::dma_stage(ring + hs * T::kStageBytes, K, V,
+                         [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        State gs;
+        state_init(gs);
+        {
+            const int hs = wv >> 1, sub = wv & 1;  // wave wv folds home keys 32*wv .. 32*wv+31
+            const uint32_t inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * sub));
+            if (inv32 != ~0u)
+                sub_step<T>(gs, ring + hs * T::kStageBytes, sub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0,
+                            kLargeW, nullptr, 0);
+        }
+        __syncthreads();  // done with the staged keys: the ring now holds the reduction
+        const float gl = pair_sum(gs.l);
+        if (lane < 32) {
+            red_ml[wv][lane][0] = gs.m;
+            red_ml[wv][lane][1] = gl;
+        }
+        for (int db = 0; db < 2; ++db)
+            for (int i = 0; i < 16; ++i)
+                red_o[(wv * 32 + (lane & 31)) * 64 + 32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)] = gs.o[db][i];
+        __syncthreads();
+        {
+            const int q = tid >> 3, dc = tid & 7;  // 32 queries x 8 column chunks
+            const int gq2 = gb * kGlobalQueriesPerBlock + q;
+            if (gq2 < p.n_g) {
+                float M = kNegInf;
+                for (int x = 0; x < kWaves; ++x) M = fmaxf(M, red_ml[x][q][0]);
+                float e[kWaves], l = 0.f;
+                for (int x = 0; x < kWaves; ++x) {
+                    e[x] = M == kNegInf ? 0.f : fast_exp2((red_ml[x][q][0] - M) * kScaleLog2);
+                    l += red_ml[x][q][1] * e[x];
+                }
+                const size_t idx = part0 + gq2;
+                if (dc == 0) {
+                    p.ws_ml[2 * idx] = M;
+                    p.ws_ml[2 * idx + 1] = l;
+                }
+                f32x4 o4[2];
+                for (int j = 0; j < 8; ++j) {
+                    float o = 0.f;
+                    for (int x = 0; x < kWaves; ++x) o += red_o[(x * 32 + q) * 64 + 8 * dc + j] * e[x];
+                    o4[j >> 2][j & 3] = o;
+                }
+                *reinterpret_cast<f32x4*>(p.ws_acc + idx * 64 + 8 * dc) = o4[0];
+                *reinterpret_cast<f32x4*>(p.ws_acc + idx * 64 + 8 * dc + 4) = o4[1];
+            }
+        }
+        __syncthreads();
+    }
+
 }
 
-// ---------------------------------------------------------------------------
-// (c): work-group (chunk, gblk, bh) runs up to 32 global queries over keys
-// [chunk*C, chunk*C + C).  Each wave takes one 64-key stage of every 256 keys;
-// the four wave states are merged in LDS and one partial (max, sum, 64 outputs)
-// per query is written for the merge kernel.
-
+// (d) Merge of the global-row partials: one work-group per (global query, b*H + h),
+// thread (wave x, column d).  Wave x folds tile groups x, x+4, ... of 8 tiles each
+// (the 8 loads of a group are issued together), then the four wave states are
+// combined in wave order; the result does not depend on timing.
 template <class T>
-__global__ __launch_bounds__(kThreads) void global_rows_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     using Elem = typename T::Elem;
-    constexpr int kRedBytes = (4 * 32 + 4 * 32 + 4 * 32 * 64) * 4;
-    constexpr int kBytes = 4 * T::kStageBytes > kRedBytes ? 4 * T::kStageBytes : kRedBytes;
-    __shared__ __attribute__((aligned(16))) char smem[kBytes];
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h2 = lane >> 5;
-    const int chunk = blockIdx.x, gblk = blockIdx.y, bh = blockIdx.z;
-    const int b = bh / p.H;
-    const int L = p.L;
-    const size_t off = (size_t)bh * L * 64;
-    const Elem* Q = reinterpret_cast<const Elem*>(p.q) + off;
-    const Elem* K = reinterpret_cast<const Elem*>(p.k) + off;
-    const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
-    const uint8_t* pad = p.pad ? p.pad + (size_t)b * L : nullptr;
-
-    const int gq = gblk * kGlobalQueriesPerBlock + (lane & 31);
-    typename T::QOp qop;
-    T::load_q(qop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
-    State st;
-    state_init(st);
-    typename T::PFrag pw;
-    typename T::Regs regs;
-    const char* mybuf = smem + wv * T::kStageBytes;
-
-    const int c0 = chunk * p.chunk;
-    const int c1 = min(L, c0 + p.chunk);
-    const int n_super = (c1 - c0 + 4 * kStageKeys - 1) / (4 * kStageKeys);
-    for (int s_i = 0; s_i < n_super; ++s_i) {
-        // Four 64-key stages per step, staged by all 256 threads; wave x computes stage x.
-        uint64_t inv_mine = ~0ull;
-        for (int x = 0; x < 4; ++x) {
-            const int ks = c0 + 4 * kStageKeys * s_i + kStageKeys * x;
-            const int key = ks + lane;
-            bool ok = key < c1;
-            if (ok && pad) ok = pad[key] == 0;
-            const uint64_t inv = ~ballot64(ok);
-            if (x == wv) inv_mine = inv;
-            if (inv != ~0ull) {
-                T::load(regs, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : ks + kk; }, tid);
-                T::store(smem + x * T::kStageBytes, regs, tid);
-            }
+    constexpr int kGroup = 8;
+    __shared__ float red[kWaves][3][64];
+    const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = bh % p.H, dil = p.dil[h], L = p.L;
+    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
+    const size_t base = (size_t)bh * p.tiles_per_head * n_gq + gi;
+    float M = kNegInf, l = 0.f, o = 0.f;
+    for (int t0 = kGroup * wv; t0 < p.tiles_per_head; t0 += kGroup * kWaves) {
+        float mt[kGroup], lt[kGroup], ot[kGroup];
+        for (int j = 0; j < kGroup; ++j) {
+            const int t = t0 + j, r = t / tpr;
+            const bool exists = t < p.tiles_per_head && r < dil && (t - r * tpr) * kRowsPerBlock < (L - r + dil - 1) / dil;
+            const size_t idx = base + (size_t)t * n_gq;
+            mt[j] = exists ? p.ws_ml[2 * idx] : kNegInf;
+            lt[j] = exists ? p.ws_ml[2 * idx + 1] : 0.f;
+            ot[j] = exists ? p.ws_acc[idx * 64 + d] : 0.f;
         }
-        __syncthreads();
-        if (inv_mine != ~0ull) {
-            for (int sub = 0; sub < 2; ++sub) {
-                const uint32_t inv32 = (uint32_t)(inv_mine >> (32 * sub));
-                if (inv32 == ~0u) continue;
-                f32x16 s = T::qk(mybuf, sub, lane, qop);
-                if (inv32 != 0u)
-                    for (int i = 0; i < 16; ++i)
-                        if ((inv32 >> key_local(i, h2)) & 1) s[i] = kNegInf;
-                online_update<T>(st, s, pw);
-                T::pv(mybuf, sub, lane, pw, st.o);
-            }
+        for (int j = 0; j < kGroup; ++j) {
+            if (mt[j] == kNegInf) continue;  // absent tile, or no valid home key in it
+            const float Mn = fmaxf(M, mt[j]);
+            const float a = fast_exp2((M - Mn) * kScaleLog2), b = fast_exp2((mt[j] - Mn) * kScaleLog2);
+            l = l * a + lt[j] * b;
+            o = o * a + ot[j] * b;
+            M = Mn;
         }
-        __syncthreads();
     }
-
-    // Merge the four waves (each saw a disjoint quarter of the chunk).
-    float* red_m = reinterpret_cast<float*>(smem);
-    float* red_l = red_m + 4 * 32;
-    float* red_o = red_l + 4 * 32;
-    const float lsum = pair_sum(st.l);
-    if (lane < 32) {
-        red_m[wv * 32 + lane] = st.m;
-        red_l[wv * 32 + lane] = lsum;
-    }
-    for (int db = 0; db < 2; ++db)
-        for (int i = 0; i < 16; ++i) red_o[(wv * 32 + (lane & 31)) * 64 + 32 * db + 16 * h2 + i] = st.o[db][i];
+    red[wv][0][d] = M;
+    red[wv][1][d] = l;
+    red[wv][2][d] = o;
     __syncthreads();
-
-    const int q = tid >> 3, dc = tid & 7;
-    const int gq2 = gblk * kGlobalQueriesPerBlock + q;
-    if (gq2 < p.n_g) {
-        float M = kNegInf;
-        for (int x = 0; x < 4; ++x) M = fmaxf(M, red_m[x * 32 + q]);
-        float e[4];
-        for (int x = 0; x < 4; ++x) e[x] = M == kNegInf ? 0.f : fast_exp2((red_m[x * 32 + q] - M) * kScaleLog2);
-        float l = 0.f;
-        for (int x = 0; x < 4; ++x) l += red_l[x * 32 + q] * e[x];
-        const size_t idx = ((size_t)bh * p.n_gblk * kGlobalQueriesPerBlock + gq2) * p.n_chunks + chunk;
-        if (dc == 0) {
-            p.ws_ml[2 * idx] = M;
-            p.ws_ml[2 * idx + 1] = l;
+    if (wv != 0) return;
+    M = kNegInf;
+    for (int x = 0; x < kWaves; ++x) M = fmaxf(M, red[x][0][d]);
+    l = 0.f;
+    o = 0.f;
+    if (M != kNegInf)
+        for (int x = 0; x < kWaves; ++x) {
+            const float e = fast_exp2((red[x][0][d] - M) * kScaleLog2);  // 0 for an empty wave
+            l += red[x][1][d] * e;
+            o += red[x][2][d] * e;
         }
-        for (int j = 0; j < 8; ++j) {
-            const int d = 8 * dc + j;
-            float o = 0.f;
-            for (int x = 0; x < 4; ++x) o += red_o[(x * 32 + q) * 64 + d] * e[x];
-            p.ws_acc[idx * 64 + d] = o;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// (d): one wave per (global query, bh); thread d merges the chunk partials of
-// output column d in chunk order (deterministic) and writes the row.
-
-template <class T>
-__global__ __launch_bounds__(64) void merge_kernel(const Params p) {
-    using Elem = typename T::Elem;
-    const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
-    const size_t base = ((size_t)bh * p.n_gblk * kGlobalQueriesPerBlock + gi) * p.n_chunks;
-    float M = kNegInf;
-    for (int c = 0; c < p.n_chunks; ++c) M = fmaxf(M, p.ws_ml[2 * (base + c)]);
-    float l = 0.f, o = 0.f;
-    if (M != kNegInf) {
-        for (int c = 0; c < p.n_chunks; ++c) {
-            const float e = fast_exp2((p.ws_ml[2 * (base + c)] - M) * kScaleLog2);
-            l += p.ws_ml[2 * (base + c) + 1] * e;
-            o += p.ws_acc[(base + c) * 64 + d] * e;
-        }
-    }
     const float res = l > 0.f ? o / l : 0.f;
-    Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bh * p.L * 64;
+    Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bh * L * 64;
     O[(size_t)p.g[gi] * 64 + d] = T::from_float(res);
 }
 
@@ -618,23 +760,13 @@ hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_global_rows(const Params& p, int dtype, hipStream_t s) {
-    if (p.n_g == 0) return hipSuccess;
-    const dim3 grid(p.n_chunks, p.n_gblk, p.B * p.H);
-    if (dtype == LF_BF16)
-        hipLaunchKernelGGL(global_rows_kernel<Bf16>, grid, dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(global_rows_kernel<F32>, grid, dim3(kThreads), 0, s, p);
-    return hipGetLastError();
-}
-
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s) {
     if (p.n_g == 0) return hipSuccess;
     const dim3 grid(p.n_g, p.B * p.H);
     if (dtype == LF_BF16)
-        hipLaunchKernelGGL(merge_kernel<Bf16>, grid, dim3(64), 0, s, p);
+        hipLaunchKernelGGL(merge_kernel<Bf16>, grid, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL(merge_kernel<F32>, grid, dim3(64), 0, s, p);
+        hipLaunchKernelGGL(merge_kernel<F32>, grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -49,9 +49,9 @@ def test_create_destroy_and_bad_dtype():
     assert lib.lf_attn_create(ctypes.byref(h), 1) == 0 and h.value
     assert lib.lf_attn_last_error(h) == b""
     assert lib.lf_attn_set_stage_timing(h, 1) == 0
-    ms = (ctypes.c_double * 3)()
-    n = (ctypes.c_int64 * 3)()
-    assert lib.lf_attn_stage_times(h, ms, n) == 0 and list(n) == [0, 0, 0]
+    ms = (ctypes.c_double * binding.N_STAGES)()
+    n = (ctypes.c_int64 * binding.N_STAGES)()
+    assert lib.lf_attn_stage_times(h, ms, n) == 0 and list(n) == [0] * binding.N_STAGES
     assert lib.lf_attn_destroy(h) == 0
     assert lib.lf_attn_destroy(None) == 0
 
