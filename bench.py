@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 METRIC = "window+global attn fwd effective TFLOP/s and % bf16 MFMA peak, L=4096 w=512"
 KERNEL_SRC = os.path.join(ROOT, "sparse_long_sequence_longformer_amd", "csrc", "lf_attn_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "band_kernel_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -53,7 +53,7 @@ def parse():
 
 
 def traffic_for(workload: str):
-    """HBM bytes per forward-kernel launch from the committed counter summary, if it was
+    """HBM bytes per band-kernel launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
