@@ -29,6 +29,13 @@
 // are zero and their contents never reach the output.  V stays row-major in LDS
 // and the P.V product reads it transposed with ds_read_b64_tr_b16.
 //
+// Softmax: Q is pre-multiplied by log2(e)/sqrt(d_h), so the score product yields
+// base-2 exponents, and the product is seeded with minus the query's running max,
+// so the weights are exp2 of the accumulators as they come out.  The running max
+// is raised lazily: a tile goes through the fast path (no max reduction) when its
+// weight sum, taken by a small matrix product, stays at most 2^8; only tiles above
+// that bound (or a query's first valid tile) compute a max and rescale.
+//
 // Register layout (v_mfma_f32_32x32x*): accumulator element i of lane l sits at
 // row 8*(i/4) + 4*(l/32) + (i%4), column l%32.  Scores are computed transposed
 // (rows = keys, columns = queries) so each lane owns one query: its row statistics
@@ -66,6 +73,7 @@ constexpr int kMaskWindow = 64;           // band stages whose pad masks are bui
 constexpr int kMaskRing = 2 * kMaskWindow;
 constexpr int kMaxGlobalStages = LF_MAX_GLOBALS / kStageKeys;
 constexpr int kLargeW = 1 << 28;  // band test that admits every key (|key - query| < 2^28)
+constexpr int kAllParts = -1;     // dma_stage: every block of the wave
 
 #ifndef LF_BF16_WAVES_PER_EU
 #define LF_BF16_WAVES_PER_EU 3
@@ -113,6 +121,25 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
 }
 
+// Wave-uniform copy of a 64-bit value in scalar registers.  The builtin returns a
+// signed int: both halves go through uint32_t so that the low half is not sign-extended.
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// 16 bytes per lane from base + off (base uniform, off a per-lane 32-bit byte offset)
+// into LDS at lds_base + 16 * lane: the scalar-base form needs no per-lane 64-bit
+// address arithmetic.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, char* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
+    const uint64_t b64 = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = uniform64(b64);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0)
+                 : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -157,20 +184,25 @@ struct Bf16 {
     struct QOp { bf16x8 v[4]; };
     struct PFrag { bf16x8 v[2]; };
 
-    // B operand of S^T = K Q^T: lane (query, h2) holds d = 16*kb + 8*h2 + j.
+    // B operand of S^T = K Q^T: lane (query, h2) holds d = 16*kb + 8*h2 + j, scaled
+    // by log2(e)/sqrt(d_h) and rounded back to bf16.
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
         for (int kb = 0; kb < 4; ++kb) {
             u32x4 x = row ? *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2) : u32x4{0, 0, 0, 0};
-            q.v[kb] = __builtin_bit_cast(bf16x8, x);
+            const f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, x), f32x8);
+            q.v[kb] = __builtin_convertvector(f * kScaleLog2, bf16x8);
         }
     }
 
     // Stage DMA by all four waves: wave wv fills 1-KiB blocks 2*wv and 2*wv+1 of K
-    // and of V (8 rows each).  row_of(kk) is the source row of stage key kk or -1.
+    // and of V (8 rows each), block 2*wv + part for part = 0, 1 (kAllParts: both).
+    // row_of(kk) is the source row of stage key kk or -1.
     template <class RowOf>
-    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane) {
+    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
+                                     int part = kAllParts) {
         const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 2; ++u) {
+            if (part != kAllParts && u != part) continue;
             const int blk = 2 * wv + u;
             const int row = 8 * blk + (lane >> 3), cl = lane & 7;
             const int src = row_of(row);
@@ -181,14 +213,49 @@ struct Bf16 {
         }
     }
 
+    // 32 rows copied to dst (row-major, 128 B each): wave wv copies rows 8*wv .. +7.
+    template <class RowPtr>
+    __device__ static void dma_rows(char* dst, RowPtr row_ptr, int wv, int lane) {
+        const int row = 8 * wv + (lane >> 3);
+        dma16(row_ptr(row) + 8 * (lane & 7), dst + wv * 1024);
+    }
+
+    // Byte offsets of this lane's stage copies (block 2*wv) relative to the stage's
+    // first source row, for stages whose 64 keys are all valid (consecutive class
+    // rows dil apart).  Block 2*wv+1 lies 8 rows further (scalar base advanced by
+    // 8*dil rows); its rows differ from block 2*wv's in bit 3 only, so swz_v is the
+    // same and swz_k differs by 4 (chunk bit 2: byte offset bit 6).
+    struct DmaLane { uint32_t k, v; int dil; };
+    __device__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
+        const int row = 16 * wv + (lane >> 3), cl = lane & 7;
+        const uint32_t r0b = (uint32_t)row * (uint32_t)dil * kRowBytes;
+        dl.k = r0b + 16u * (uint32_t)(cl ^ swz_k(row));
+        dl.v = r0b + 16u * (uint32_t)(cl ^ swz_v(row));
+        dl.dil = dil;
+    }
+    __device__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
+        for (int u = 0; u < 2; ++u) {
+            const int blk = 2 * wv + u;
+            const size_t adv = (size_t)u * 8 * dl.dil * 64;
+            dma16s(K0 + adv, u ? dl.k ^ 64u : dl.k, slot + blk * 1024);
+            dma16s(V0 + adv, dl.v, slot + kTileBytes + blk * 1024);
+        }
+    }
+
     // Per-lane LDS byte offsets of the operand reads, independent of the stage slot
     // and of the sub-tile (the swizzles only depend on the row modulo 8).
     struct Lane {
         int k[4];  // K operand: row sigma(M), chunk (2*kb + h2) ^ swz_k(row)
         int v[2];  // V^T operand: row 8*h2 + i/4 (+ 4*t + 16*kb + 32*sub), per column block db
+        bf16x8 sel;  // A operand of the weight-sum product (see tile_sum)
     };
     __device__ static void lane_offsets(Lane& lo, int lane) {
         const int row = sigma(lane & 31), h2 = lane >> 5;
+        {
+            const int m = lane & 15, g = lane >> 4;
+            const __bf16 one = (m & 3) == 0 && ((m >> 2) & 1) == (g & 1) ? (__bf16)1.0f : (__bf16)0.0f;
+            for (int j = 0; j < 8; ++j) lo.sel[j] = one;
+        }
         for (int kb = 0; kb < 4; ++kb) lo.k[kb] = row * kRowBytes + (((2 * kb + h2) ^ swz_k(row)) << 4);
         const int g1 = (lane >> 4) & 1, i = lane & 15;
         const int vrow = 8 * h2 + (i >> 2);
@@ -198,10 +265,11 @@ struct Bf16 {
         }
     }
 
-    // S^T (32 keys x 32 queries) of sub-tile `sub` (keys 32*sub .. 32*sub+31 of the stage).
-    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q) {
+    // seed + S^T (32 keys x 32 queries) of sub-tile `sub` (keys 32*sub .. 32*sub+31 of
+    // the stage).
+    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
         const char* base = slot + sub * 32 * kRowBytes;
-        f32x16 acc = {};
+        f32x16 acc = seed;
         for (int kb = 0; kb < 4; ++kb) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + lo.k[kb]);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[kb], acc, 0, 0, 0);
@@ -209,25 +277,27 @@ struct Bf16 {
         return acc;
     }
 
-    // Round the weights to bf16 (the P^T operand) and return their sum as rounded,
-    // so the normaliser matches the weights the product uses.
-    __device__ static float make_p(const float* p, PFrag& pf) {
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        float sum[2] = {0.f, 0.f};  // two independent accumulation chains
+    // Round the weights to bf16: the P^T operand.
+    __device__ static void to_p(const float* p, PFrag& pf) {
         for (int kb = 0; kb < 2; ++kb) {
             f32x8 t;
             for (int j = 0; j < 8; ++j) t[j] = p[8 * kb + j];
-            const bf16x8 b = __builtin_convertvector(t, bf16x8);
-            pf.v[kb] = b;
-            // Sub-vectors by shuffle: hipcc mis-selects dot2 operands taken as words of
-            // a bit-cast of the converted vector (every word reads as the first).
-            float& acc = sum[kb];
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), one, acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), one, acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), one, acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), one, acc, false);
+            pf.v[kb] = __builtin_convertvector(t, bf16x8);
         }
-        return sum[0] + sum[1];
+    }
+
+    // Sum of the 32 rounded weights of the lane's query (both halves), in both lanes
+    // of the pair, from two 16x16x32 products with P^T as the B operand.  In that
+    // shape lane l holds B rows 8*(l/16) .. +7 of column l%16, i.e. query l%16 +
+    // 16*((l/16)&1), key half (l/16)>>1; and result element 0 of lane l is row
+    // 4*(l/16), column l%16.  A rows 0 and 8 select the B row groups of query n =
+    // column, rows 4 and 12 those of query n + 16; so element 0 of lane l is the sum
+    // of query l%32, the lane's own query.  The bf16 vector units share the matrix
+    // cores' datapath, which makes this cheaper than a dot-product chain.
+    __device__ static float tile_sum(const PFrag& pf, const float*, const Lane& lo) {
+        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.sel, pf.v[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.sel, pf.v[1], acc, 0, 0, 0);
+        return acc[0];
     }
 
     // O^T += V^T P^T over the 32 keys of sub-tile `sub`.  The V^T operand (lane l:
@@ -281,19 +351,23 @@ struct F32 {
     struct QOp { float v[32]; };
     struct PFrag { float v[16]; };
 
-    // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t.
+    // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t,
+    // scaled by log2(e)/sqrt(d_h).
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
         for (int t4 = 0; t4 < 8; ++t4) {
             f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4) : f32x4{0, 0, 0, 0};
-            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
+            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e] * kScaleLog2;
         }
     }
 
-    // Wave wv fills 1-KiB blocks 4*wv .. 4*wv+3 of K and of V (4 rows each).
+    // Wave wv fills 1-KiB blocks 4*wv .. 4*wv+3 of K and of V (4 rows each); part
+    // p = 0, 1 fills blocks 4*wv + 2*p and 4*wv + 2*p + 1 (kAllParts: all four).
     template <class RowOf>
-    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane) {
+    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
+                                     int part = kAllParts) {
         const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 4; ++u) {
+            if (part != kAllParts && (u >> 1) != part) continue;
             const int blk = 4 * wv + u;
             const int row = 4 * blk + (lane >> 4), cl = lane & 15;
             const int src = row_of(row);
@@ -301,6 +375,32 @@ struct F32 {
             const Elem* vr = src >= 0 ? V + (size_t)src * 64 : zero;
             dma16(kr + 4 * (cl ^ swz_k(row)), slot + blk * 1024);
             dma16(vr + 4 * cl, slot + kTileBytes + blk * 1024);
+        }
+    }
+
+    // 32 rows copied to dst (row-major, 256 B each): wave wv copies rows 8*wv .. +7.
+    template <class RowPtr>
+    __device__ static void dma_rows(char* dst, RowPtr row_ptr, int wv, int lane) {
+        for (int u = 0; u < 2; ++u) {
+            const int row = 8 * wv + 4 * u + (lane >> 4);
+            dma16(row_ptr(row) + 4 * (lane & 15), dst + (2 * wv + u) * 1024);
+        }
+    }
+
+    struct DmaLane { uint32_t k[4], v[4]; };
+    __device__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
+        for (int u = 0; u < 4; ++u) {
+            const int row = 4 * (4 * wv + u) + (lane >> 4), cl = lane & 15;
+            const uint32_t r0b = (uint32_t)row * (uint32_t)dil * kRowBytes;
+            dl.k[u] = r0b + 16u * (uint32_t)(cl ^ swz_k(row));
+            dl.v[u] = r0b + 16u * (uint32_t)cl;
+        }
+    }
+    __device__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
+        for (int u = 0; u < 4; ++u) {
+            const int blk = 4 * wv + u;
+            dma16s(K0, dl.k[u], slot + blk * 1024);
+            dma16s(V0, dl.v[u], slot + kTileBytes + blk * 1024);
         }
     }
 
@@ -318,9 +418,9 @@ struct F32 {
         lo.v = kTileBytes + 4 * (lane & 31);
     }
 
-    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q) {
+    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
         const char* base = slot + sub * 32 * kRowBytes + lo.k;
-        f32x16 acc = {};
+        f32x16 acc = seed;
         for (int t4 = 0; t4 < 8; ++t4) {
             const f32x4 a = *reinterpret_cast<const f32x4*>(base + (((8 * lo.h2 + t4) ^ lo.sw) << 4));
             for (int e = 0; e < 4; ++e)
@@ -329,13 +429,14 @@ struct F32 {
         return acc;
     }
 
-    __device__ static float make_p(const float* p, PFrag& pf) {
-        float sum = 0.f;
-        for (int i = 0; i < 16; ++i) {
-            pf.v[i] = p[i];
-            sum += p[i];
-        }
-        return sum;
+    __device__ static void to_p(const float* p, PFrag& pf) {
+        for (int i = 0; i < 16; ++i) pf.v[i] = p[i];
+    }
+    // Sum of the query's 32 weights, in both lanes of the pair.
+    __device__ static float tile_sum(const PFrag&, const float* p, const Lane&) {
+        float sum[2] = {0.f, 0.f};
+        for (int i = 0; i < 16; ++i) sum[i & 1] += p[i];
+        return pair_sum(sum[0] + sum[1]);
     }
 
     // Step u pairs lane-half h2 with key key_local(u, h2), matching the score layout.
@@ -378,47 +479,69 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 }
 
 // ---------------------------------------------------------------------------
-// Online softmax state of one lane: running max m (raw score units), the lane's
-// share of the running sum l, and 32 output accumulators (two 32x32 blocks).
+// Online softmax state of one lane.  Exponents are base 2 (scores come out of the
+// product already multiplied by log2(e)/sqrt(d_h)).
 
 struct State {
-    float m;
-    float l;
-    f32x16 o[2];
+    float mc;      // running max of the query; -inf before its first valid key
+    float cofs;    // offset seeded into the score product: mc, or 0 while mc = -inf
+    float l;       // running weight sum of the query (both lane halves), relative to cofs
+    f32x16 seed;   // -cofs in every element
+    f32x16 o[2];   // unnormalised output, relative to cofs
 };
 
 __device__ __forceinline__ void state_init(State& st) {
-    st.m = kNegInf;
+    st.mc = kNegInf;
+    st.cofs = 0.f;
     st.l = 0.f;
+    st.seed = f32x16{};
     st.o[0] = f32x16{};
     st.o[1] = f32x16{};
 }
 
-// Raise the running max only when a row's block max exceeds it by more than
-// 2^8 in weight: weights may then reach 256 (exact in bf16 and fp32 alike), and
-// the output/sum rescale runs only on the few blocks that raise a max.
-constexpr float kRaiseRaw = 8.0f / kScaleLog2;
+// A tile whose weights (relative to cofs) sum to at most 2^8 has every weight at
+// most 2^8: exact in bf16 and fp32 alike, so it is folded as it is.
+constexpr float kTileSumBound = 256.0f;
 
-// Fold one 32-key score tile into the state; the weights go to the P^T operand.
+__device__ __forceinline__ bool pair_or(bool x) {
+    auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return (r[0] | r[1]) != 0u;
+}
+
+// Fold one 32-key tile of exponents x (score - cofs; -inf for masked keys) into the
+// state; the weights go to the P^T operand.
 template <class T>
-__device__ __forceinline__ void online_update(State& st, const f32x16& s, typename T::PFrag& pf) {
-    float m4[4];
-    for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(s[4 * j], s[4 * j + 1]), fmaxf(s[4 * j + 2], s[4 * j + 3]));
-    const float mx = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-    const bool raise = mx > st.m + kRaiseRaw;  // a first finite block always raises
-    if (__any(raise)) {
-        // Lanes that keep their max keep alpha = 1 (their max may still be -inf).
-        const float mnew = raise ? mx : st.m;
-        const float alpha = raise ? fast_exp2((st.m - mnew) * kScaleLog2) : 1.f;  // 0 from -inf
-        st.l *= alpha;
-        st.o[0] *= alpha;
-        st.o[1] *= alpha;
-        st.m = mnew;
-    }
-    const float mc = (st.m == kNegInf ? 0.f : st.m) * kScaleLog2;
+__device__ __forceinline__ void fold_tile(State& st, const f32x16& x, typename T::PFrag& pf,
+                                          const typename T::Lane& lo) {
     float p[16];
-    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], kScaleLog2, -mc));
-    st.l += T::make_p(p, pf);
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i]);
+    T::to_p(p, pf);
+    float ts = T::tile_sum(pf, p, lo);
+    // Fast path unless a query has no max yet or its weights may exceed the bound
+    // (a non-finite sum included).
+    const bool trig = st.mc == kNegInf || !(ts <= kTileSumBound);
+    if (__any(trig)) {
+        // The triggering queries raise their max to the tile max (both lanes of a
+        // pair take the same decision) and recompute their weights against it.
+        float m4[4];
+        for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(x[4 * j], x[4 * j + 1]), fmaxf(x[4 * j + 2], x[4 * j + 3]));
+        const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) + st.cofs;
+        if (pair_or(trig) && tmax > st.mc) {  // -inf tmax: no valid key in the tile
+            // The state so far is relative to cofs; before the first valid key it is zero.
+            const float alpha = st.mc == kNegInf ? 0.f : fast_exp2(st.cofs - tmax);
+            st.l *= alpha;
+            st.o[0] *= alpha;
+            st.o[1] *= alpha;
+            const float sh = tmax - st.cofs;
+            for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i] - sh);
+            st.mc = tmax;
+            st.cofs = tmax;
+        }
+        for (int i = 0; i < 16; ++i) st.seed[i] = -st.cofs;
+        T::to_p(p, pf);
+        ts = T::tile_sum(pf, p, lo);  // with the whole wave active
+    }
+    st.l += ts;
 }
 
 // Element i of a 32-key score tile holds stage key 32*sub + kc(i) + 8*h2.
@@ -431,7 +554,7 @@ template <class T>
 __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, const typename T::Lane& lo,
                                          const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
                                          int w, const int* gp, int wq) {
-    f32x16 s = T::qk(slot, sub, lo, q);
+    f32x16 s = T::qk(slot, sub, lo, q, st.seed);  // exponents: scores - cofs
     typename T::VOp vo;
     T::load_v(vo, slot, sub, lo);  // in flight during the softmax
     if (mode != 0) {
@@ -449,28 +572,21 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
         }
     }
     typename T::PFrag pf;
-    online_update<T>(st, s, pf);
+    fold_tile<T>(st, s, pf, lo);
     T::pv(vo, pf, st.o);
-}
-
-__device__ __forceinline__ bool is_global_row(const Params& p, int row) {
-    int lo = 0, hi = p.n_g;  // sorted, distinct
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const int g = p.g[mid];
-        if (g == row) return true;
-        if (g < row) lo = mid + 1; else hi = mid;
-    }
-    return false;
 }
 
 // ---------------------------------------------------------------------------
 // (a)+(b): one work-group = 128 consecutive rows of one residue class of one
 // (b, h); wave wv owns rows r0 + 32*wv .. +31.  The stage sequence is the global
 // keys (up to 64 per stage, with an in-window test so each key counts once)
-// followed by the window band [kb0, kend) of the class in 64-key stages.  Each
-// wave skips 32-key sub-tiles outside its rows' band and masks only sub-tiles
-// that touch the band edge or hold invalid keys.
+// followed by the window band [kb0, kend) of the class in 64-key stages.  The band
+// stages lie on a grid aligned to r0: nb stages before the tile's own rows, the two
+// "home" stages [r0, r0 + 128), na stages after; they are processed in the order
+// before, after, home (the softmax fold does not depend on the order), so that the
+// home keys are still in LDS when the band ends, for (c).  Each wave skips 32-key
+// sub-tiles outside its rows' band and masks only sub-tiles that touch the band
+// edge or hold invalid keys.
 
 template <class T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
@@ -481,6 +597,9 @@ void band_kernel(const Params p) {
     __shared__ uint64_t glob_mask[kMaxGlobalStages];  // invalid-key bits of global stages
     __shared__ int glob_src[LF_MAX_GLOBALS];          // source row of each global slot or -1
     __shared__ int glob_pos[LF_MAX_GLOBALS];          // same-class virtual position or kNoPos
+    __shared__ int glob_row[LF_MAX_GLOBALS];          // same as glob_pos, padded or not
+    __shared__ uint32_t row_glob[kRowsPerBlock / 32]; // tile rows that are global queries
+    __shared__ __attribute__((aligned(16))) char gq_rows[kGlobalQueriesPerBlock * T::kRowBytes];  // first 32 global Q rows
 
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -510,17 +629,28 @@ void band_kernel(const Params p) {
 
     const int kb0 = max(0, r0 - w);
     const int kend = min(Lr, r0 + kRowsPerBlock + w);
-    const int n_band = (kend - kb0 + kStageKeys - 1) / kStageKeys;
+    const int nb = (r0 - kb0 + kStageKeys - 1) / kStageKeys;  // stages before the home keys
+    const int gbase = r0 - kStageKeys * nb;                    // first key of the grid (<= kb0)
+    const int na = max(0, (kend - (r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
+    const int n_band = nb + 2 + na;
     const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
     const int n_st = n_gst + n_band;
+    // First key of the u-th band stage in processing order (before, after, home).
+    auto stage_key = [&](int u) {
+        const int bs = u < nb ? u : (u < nb + na ? u + 2 : u - na);
+        return gbase + kStageKeys * bs;
+    };
 
     // Global slots: source row (or -1 if unused/padded) and in-window position.
     for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
         const int g = gi < p.n_g ? p.g[gi] : -1;
         const bool ok = g >= 0 && (!pad || pad[g] == 0);
+        const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
-        glob_pos[gi] = (ok && g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
+        glob_pos[gi] = ok ? vpos : kNoPos;
+        glob_row[gi] = vpos;
     }
+    if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
     // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ...
     auto fill_band_masks = [&](int W) {
         constexpr int kPer = kMaskWindow / kWaves, kGroup = 4;
@@ -528,8 +658,8 @@ void band_kernel(const Params p) {
             uint32_t flag[kGroup];
             for (int j = 0; j < kGroup; ++j) {
                 const int bs = W * kMaskWindow + wv + kWaves * (j0 + j);
-                const int key = kb0 + kStageKeys * bs + lane;
-                flag[j] = (bs < n_band && key < kend) ? pad[r + key * dil] : 1u;
+                const int key = stage_key(bs) + lane;
+                flag[j] = (bs < n_band && key >= kb0 && key < kend) ? pad[r + key * dil] : 1u;
             }
             for (int j = 0; j < kGroup; ++j) {
                 const int bs = W * kMaskWindow + wv + kWaves * (j0 + j);
@@ -545,24 +675,43 @@ void band_kernel(const Params p) {
             const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
             if (lane == 0) glob_mask[s] = inv;
         }
+    for (int gi = tid; gi < p.n_g; gi += kThreads) {
+        const int vr = glob_row[gi] - r0;
+        if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
+    }
     __syncthreads();
 
+    // Invalid-key bits of band stage u: keys outside [kb0, kend), or padded.
     auto band_invalid = [&](int bs) -> uint64_t {
         if (pad) return band_mask[bs % kMaskRing];
-        const int n = kend - (kb0 + kStageKeys * bs);  // valid keys in this stage
-        return n >= 64 ? 0ull : (n <= 0 ? ~0ull : (~0ull << n));
+        const int ks = stage_key(bs);
+        const int lo = kb0 - ks, hi = kend - ks;  // valid keys: lo <= kk < hi
+        uint64_t m = 0;
+        if (lo > 0) m |= lo >= 64 ? ~0ull : ((1ull << lo) - 1);
+        if (hi < 64) m |= hi <= 0 ? ~0ull : (~0ull << hi);
+        return m;
     };
-    auto issue = [&](int s) {
+    typename T::DmaLane dl;
+    T::dma_lane(dl, wv, lane, dil);
+    // The scalar-base copies use 32-bit per-lane offsets of up to 64 rows dil apart.
+    const bool direct_ok = (uint64_t)dil * kStageKeys * T::kRowBytes < (1ull << 31);
+    // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
+    auto issue = [&](int s, int part) {
         char* slot = ring + (s % T::kNS) * T::kStageBytes;
         if (s < n_gst) {
             const int* src = glob_src + kStageKeys * s;
-            T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane);
+            T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane, part);
         } else {
             const int bs = s - n_gst;
-            const uint64_t inv = band_invalid(bs);
-            const int ks = kb0 + kStageKeys * bs;
-            T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv,
-                         lane);
+            const uint64_t inv = uniform64(band_invalid(bs));
+            const int ks = stage_key(bs);
+            if (inv == 0ull && part == kAllParts && direct_ok) {
+                const size_t row0 = (size_t)(r + ks * dil) * 64;
+                T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
+            } else {
+                T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
+                             wv, lane, part);
+            }
         }
     };
 
@@ -571,12 +720,17 @@ void band_kernel(const Params p) {
     typename T::Lane lo;
     T::lane_offsets(lo, lane);
 
-    // Every register load (Q operand, masks) completes here, so the compiler's own
-    // waits inside the loop have nothing left to wait for: an in-loop vmcnt wait
-    // would also drain the stage copies in flight.
-    wait_vmcnt<0>();
+    // The first stages are copied while the Q operand loads are still in flight;
+    // every register load (Q operand, masks) completes at the wait below, so the
+    // compiler's own waits inside the loop have nothing left to wait for (an
+    // in-loop vmcnt wait would also drain the stage copies in flight).
     for (int s = 0; s < T::kNS - 1; ++s)
-        if (s < n_st) issue(s);
+        if (s < n_st) issue(s, kAllParts);
+    if (p.n_g > 0) {  // Q rows of the first 32 global queries, for (c)
+        const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
+        T::dma_rows(gq_rows, [&](int j) { return j < p.n_g ? Q + (size_t)p.g[j] * 64 : zero; }, wv, lane);
+    }
+    wait_vmcnt<0>();
     for (int t = 0; t < n_st; ++t) {
         wait_stage<T>(min(T::kNS - 2, n_st - 1 - t));
         barrier_nofence();
@@ -587,12 +741,12 @@ void band_kernel(const Params p) {
                 fill_band_masks(bn / kMaskWindow);
                 __syncthreads();
             }
-            issue(sn);
+            issue(sn, kAllParts);
         }
-        const char* slot = ring + (t % T::kNS) * T::kStageBytes;
         const bool gstage = t < n_gst;
-        const int ks = kb0 + kStageKeys * (t - n_gst);
-        const uint64_t inv = gstage ? glob_mask[t] : band_invalid(t - n_gst);
+        const int ks = gstage ? 0 : stage_key(t - n_gst);
+        const uint64_t inv = uniform64(gstage ? glob_mask[t] : band_invalid(t - n_gst));
+        const char* slot = ring + (t % T::kNS) * T::kStageBytes;
         if (rows_live && inv != ~0ull) {
 #pragma unroll 1
             for (int sub = 0; sub < 2; ++sub) {
@@ -608,59 +762,70 @@ void band_kernel(const Params p) {
         }
     }
 
-    const float lt = pair_sum(st.l);
-    const float scale = lt > 0.f ? 1.f / lt : 0.f;
+    const float scale = st.l > 0.f ? 1.f / st.l : 0.f;
     if (qv < Lr) {
         const int row = r + qv * dil;
-        if (!is_global_row(p, row)) T::store_row(O + (size_t)row * 64, h2, st.o, scale);
+        const int vr = qv - r0;  // global rows are written by the merge
+        if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) T::store_row(O + (size_t)row * 64, h2, st.o, scale);
     }
     if (p.n_g == 0) return;
 
     // (c) Global rows: every key belongs to exactly one work-group's "home" range
     // [r0, r0 + 128) of its class, so each work-group folds the global queries over
     // its home keys and leaves one partial (max, sum, unnormalised output) per query.
+    // For the first 32 global queries the home keys are the last two band stages,
+    // still in the ring, and the Q rows were copied to LDS with the first stage.
     __shared__ float red_ml[kWaves][32][2];
     float* red_o = reinterpret_cast<float*>(ring);  // kWaves x 32 x 64 floats = 32 KiB
     const int home_end = min(Lr, r0 + kRowsPerBlock);
     const size_t part0 = ((size_t)bh * p.tiles_per_head + t_in) * p.n_gblk * kGlobalQueriesPerBlock;
+    const int hs = wv >> 1, hsub = wv & 1;  // wave wv folds home keys 32*wv .. 32*wv+31
     for (int gb = 0; gb < p.n_gblk; ++gb) {
-        const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
         typename T::QOp gop;
-        T::load_q(gop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
-        uint64_t hinv[2];
-        for (int hs = 0; hs < 2; ++hs) {
-            const int key = r0 + kStageKeys * hs + lane;
-            bool ok = key < home_end;
-            if (ok && pad) ok = pad[r + key * dil] == 0;
-            hinv[hs] = ~ballot64(ok);
+        const char* hslot;
+        uint32_t inv32;
+        if (gb == 0) {
+            T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
+            const int u = n_band - 2 + hs;
+            hslot = ring + ((n_gst + u) % T::kNS) * T::kStageBytes;
+            inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
+        } else {
+            const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
+            T::load_q(gop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
+            uint64_t hinv[2];
+            for (int j = 0; j < 2; ++j) {
+                const int key = r0 + kStageKeys * j + lane;
+                bool ok = key < home_end;
+                if (ok && pad) ok = pad[r + key * dil] == 0;
+                hinv[j] = ~ballot64(ok);
+            }
+            __syncthreads();  // the ring is free
+            for (int j = 0; j < 2; ++j) {
+                const uint64_t iv = hinv[j];
+                const int ks = r0 + kStageKeys * j;
+                T::dma_stage(ring + j * T::kStageBytes, K, V,
+                             [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            hslot = ring + hs * T::kStageBytes;
+            inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * hsub));
         }
-        __syncthreads();  // the ring is free
-        for (int hs = 0; hs < 2; ++hs) {
-            const uint64_t iv = hinv[hs];
-            const int ks = r0 + kStageKeys * hs;
-            T::dma_stage(ring + hs * T::kStageBytes, K, V,
-                         [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
-        }
-        wait_vmcnt<0>();
-        __syncthreads();
         State gs;
         state_init(gs);
-        {
-            const int hs = wv >> 1, sub = wv & 1;  // wave wv folds home keys 32*wv .. 32*wv+31
-            const uint32_t inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * sub));
-            if (inv32 != ~0u)
-                sub_step<T>(gs, ring + hs * T::kStageBytes, sub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0,
-                            kLargeW, nullptr, 0);
-        }
+        if (inv32 != ~0u)
+            sub_step<T>(gs, hslot, hsub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0, kLargeW, nullptr, 0);
         __syncthreads();  // done with the staged keys: the ring now holds the reduction
-        const float gl = pair_sum(gs.l);
-        if (lane < 32) {
-            red_ml[wv][lane][0] = gs.m;
-            red_ml[wv][lane][1] = gl;
+        if (lane < 32) {  // partial relative to cofs (= mc, or nothing when mc = -inf)
+            red_ml[wv][lane][0] = gs.mc;
+            red_ml[wv][lane][1] = gs.l;
         }
+        // Column c of query q sits at q*64 + (c ^ q%32): the 32 queries of one store,
+        // and the 8 queries x 8 column chunks of one load below, hit distinct banks.
         for (int db = 0; db < 2; ++db)
             for (int i = 0; i < 16; ++i)
-                red_o[(wv * 32 + (lane & 31)) * 64 + 32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)] = gs.o[db][i];
+                red_o[(wv * 32 + (lane & 31)) * 64 + ((32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)) ^ (lane & 31))] =
+                    gs.o[db][i];
         __syncthreads();
         {
             const int q = tid >> 3, dc = tid & 7;  // 32 queries x 8 column chunks
@@ -670,7 +835,7 @@ void band_kernel(const Params p) {
                 for (int x = 0; x < kWaves; ++x) M = fmaxf(M, red_ml[x][q][0]);
                 float e[kWaves], l = 0.f;
                 for (int x = 0; x < kWaves; ++x) {
-                    e[x] = M == kNegInf ? 0.f : fast_exp2((red_ml[x][q][0] - M) * kScaleLog2);
+                    e[x] = M == kNegInf ? 0.f : fast_exp2(red_ml[x][q][0] - M);
                     l += red_ml[x][q][1] * e[x];
                 }
                 const size_t idx = part0 + gq2;
@@ -681,7 +846,7 @@ void band_kernel(const Params p) {
                 f32x4 o4[2];
                 for (int j = 0; j < 8; ++j) {
                     float o = 0.f;
-                    for (int x = 0; x < kWaves; ++x) o += red_o[(x * 32 + q) * 64 + 8 * dc + j] * e[x];
+                    for (int x = 0; x < kWaves; ++x) o += red_o[(x * 32 + q) * 64 + ((8 * dc + j) ^ q)] * e[x];
                     o4[j >> 2][j & 3] = o;
                 }
                 *reinterpret_cast<f32x4*>(p.ws_acc + idx * 64 + 8 * dc) = o4[0];
@@ -722,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
         for (int j = 0; j < kGroup; ++j) {
             if (mt[j] == kNegInf) continue;  // absent tile, or no valid home key in it
             const float Mn = fmaxf(M, mt[j]);
-            const float a = fast_exp2((M - Mn) * kScaleLog2), b = fast_exp2((mt[j] - Mn) * kScaleLog2);
+            const float a = fast_exp2(M - Mn), b = fast_exp2(mt[j] - Mn);
             l = l * a + lt[j] * b;
             o = o * a + ot[j] * b;
             M = Mn;
@@ -739,7 +904,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     o = 0.f;
     if (M != kNegInf)
         for (int x = 0; x < kWaves; ++x) {
-            const float e = fast_exp2((red[x][0][d] - M) * kScaleLog2);  // 0 for an empty wave
+            const float e = fast_exp2(red[x][0][d] - M);  // 0 for an empty wave
             l += red[x][1][d] * e;
             o += red[x][2][d] * e;
         }
