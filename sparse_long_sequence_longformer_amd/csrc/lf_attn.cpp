@@ -199,11 +199,12 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
     p.n_g = static_cast<int>(g.size());
     std::copy(g.begin(), g.end(), p.g);
     p.n_gblk = (p.n_g + lf::kGlobalQueriesPerBlock - 1) / lf::kGlobalQueriesPerBlock;
+    p.rows_per_block = lf::kRowsPerBlock;
     int tiles = 0;
     for (int i = 0; i < H; ++i) {
         const int d = p.dil[i];
         const int len0 = (L + d - 1) / d;  // rows of residue class 0 (the longest)
-        const int per_class = (len0 + lf::kRowsPerBlock - 1) / lf::kRowsPerBlock;
+        const int per_class = (len0 + p.rows_per_block - 1) / p.rows_per_block;
         const int64_t t = static_cast<int64_t>(d) * per_class;
         if (t > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
         tiles = std::max<int>(tiles, static_cast<int>(t));

@@ -32,6 +32,7 @@ struct Params {
     int n_g;             // number of distinct global positions
     int n_gblk;          // ceil(n_g / 32)
     int tiles_per_head;  // work-groups per (b, h), max over heads (grid partition)
+    int rows_per_block;  // rows of one residue class per work-group
     int dil[LF_MAX_HEADS];
     int g[LF_MAX_GLOBALS];          // sorted, distinct
 };

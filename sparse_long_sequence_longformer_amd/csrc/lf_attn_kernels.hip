@@ -508,6 +508,37 @@ __device__ __forceinline__ bool pair_or(bool x) {
     return (r[0] | r[1]) != 0u;
 }
 
+// Rare path of a tile fold: the triggering queries raise their max to the tile max
+// (both lanes of a pair take the same decision) and recompute their weights against
+// it; every lane refreshes its seed and the tile sum.
+template <class T>
+__device__ __forceinline__ void fold_slow(State& st, const f32x16& x, float* p, typename T::PFrag& pf, float& ts,
+                                          bool trig, const typename T::Lane& lo) {
+    float m4[4];
+    for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(x[4 * j], x[4 * j + 1]), fmaxf(x[4 * j + 2], x[4 * j + 3]));
+    const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) + st.cofs;
+    if (pair_or(trig) && tmax > st.mc) {  // -inf tmax: no valid key in the tile
+        // The state so far is relative to cofs; before the first valid key it is zero.
+        const float alpha = st.mc == kNegInf ? 0.f : fast_exp2(st.cofs - tmax);
+        st.l *= alpha;
+        st.o[0] *= alpha;
+        st.o[1] *= alpha;
+        const float sh = tmax - st.cofs;
+        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i] - sh);
+        st.mc = tmax;
+        st.cofs = tmax;
+    }
+    for (int i = 0; i < 16; ++i) st.seed[i] = -st.cofs;
+    T::to_p(p, pf);
+    ts = T::tile_sum(pf, p, lo);  // with the whole wave active
+}
+
+// Fast path unless a query has no max yet or its weights may exceed the bound (a
+// non-finite sum included).
+__device__ __forceinline__ bool fold_trigger(const State& st, float ts) {
+    return st.mc == kNegInf || !(ts <= kTileSumBound);
+}
+
 // Fold one 32-key tile of exponents x (score - cofs; -inf for masked keys) into the
 // state; the weights go to the P^T operand.
 template <class T>
@@ -517,39 +548,42 @@ __device__ __forceinline__ void fold_tile(State& st, const f32x16& x, typename T
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i]);
     T::to_p(p, pf);
     float ts = T::tile_sum(pf, p, lo);
-    // Fast path unless a query has no max yet or its weights may exceed the bound
-    // (a non-finite sum included).
-    const bool trig = st.mc == kNegInf || !(ts <= kTileSumBound);
-    if (__any(trig)) {
-        // The triggering queries raise their max to the tile max (both lanes of a
-        // pair take the same decision) and recompute their weights against it.
-        float m4[4];
-        for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(x[4 * j], x[4 * j + 1]), fmaxf(x[4 * j + 2], x[4 * j + 3]));
-        const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) + st.cofs;
-        if (pair_or(trig) && tmax > st.mc) {  // -inf tmax: no valid key in the tile
-            // The state so far is relative to cofs; before the first valid key it is zero.
-            const float alpha = st.mc == kNegInf ? 0.f : fast_exp2(st.cofs - tmax);
-            st.l *= alpha;
-            st.o[0] *= alpha;
-            st.o[1] *= alpha;
-            const float sh = tmax - st.cofs;
-            for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i] - sh);
-            st.mc = tmax;
-            st.cofs = tmax;
-        }
-        for (int i = 0; i < 16; ++i) st.seed[i] = -st.cofs;
-        T::to_p(p, pf);
-        ts = T::tile_sum(pf, p, lo);  // with the whole wave active
-    }
+    const bool trig = fold_trigger(st, ts);
+    if (__any(trig)) fold_slow<T>(st, x, p, pf, ts, trig, lo);
     st.l += ts;
 }
 
 // Element i of a 32-key score tile holds stage key 32*sub + kc(i) + 8*h2.
 __device__ __forceinline__ constexpr int kc_of(int i) { return 16 * (i >> 3) + (i & 7); }
 
+// Masks of a 32-key score tile.  MODE 0: none; 1: band mask, base = (first key of
+// the sub-tile) + 8*h2 - query + w; 2: global keys (gp: in-window positions of the
+// sub-tile's keys).  Invalid keys (inv32 bits) are masked in modes 1 and 2.
+__device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32, int h2, int base, int w,
+                                            const int* gp, int wq) {
+    if (mode == 0) return;
+    const uint32_t invl = inv32 >> (8 * h2);
+    if (mode == 1) {
+        // Band test 0 <= base + kc <= 2w as one bit range over kc, minus invalid keys.
+        const int lo_k = max(0, -base), hi_k = min(31, 2 * w - base);
+        uint32_t keep = 0u;
+        if (hi_k >= lo_k) keep = (hi_k >= 31 ? ~0u : ((2u << hi_k) - 1u)) & ~((1u << lo_k) - 1u);
+        keep &= ~invl;
+        for (int i = 0; i < 16; ++i)
+            if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
+    } else {
+        // The lane's 16 keys are gp[0..7] and gp[16..23]: four 16-byte LDS reads.
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4* g4 = reinterpret_cast<const i32x4*>(gp);
+        const i32x4 a[4] = {g4[0], g4[1], g4[4], g4[5]};
+        for (int i = 0; i < 16; ++i) {
+            const int kc = kc_of(i);
+            if (((invl >> kc) & 1) || (unsigned)(a[i >> 2][i & 3] + wq) <= (unsigned)(2 * w)) s[i] = kNegInf;
+        }
+    }
+}
+
 // One 32-key sub-tile of a stage: scores, masks, softmax update, P.V product.
-// MODE 0: no mask needed; 1: band mask, base = (first key of the sub-tile) + 8*h2
-// - query + w; 2: global keys (gp: in-window positions of the sub-tile's keys).
 template <class T>
 __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, const typename T::Lane& lo,
                                          const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
@@ -557,20 +591,7 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
     f32x16 s = T::qk(slot, sub, lo, q, st.seed);  // exponents: scores - cofs
     typename T::VOp vo;
     T::load_v(vo, slot, sub, lo);  // in flight during the softmax
-    if (mode != 0) {
-        const uint32_t invl = inv32 >> (8 * h2);
-        if (mode == 1) {
-            for (int i = 0; i < 16; ++i) {
-                const int kc = kc_of(i);
-                if ((unsigned)(base + kc) > (unsigned)(2 * w) || ((invl >> kc) & 1)) s[i] = kNegInf;
-            }
-        } else {
-            for (int i = 0; i < 16; ++i) {
-                const int kc = kc_of(i);
-                if (((invl >> kc) & 1) || (unsigned)(gp[kc] + wq) <= (unsigned)(2 * w)) s[i] = kNegInf;
-            }
-        }
-    }
+    mask_scores(s, mode, inv32, h2, base, w, gp, wq);
     typename T::PFrag pf;
     fold_tile<T>(st, s, pf, lo);
     T::pv(vo, pf, st.o);
@@ -596,7 +617,7 @@ void band_kernel(const Params p) {
     __shared__ uint64_t band_mask[kMaskRing];        // invalid-key bits of band stages
     __shared__ uint64_t glob_mask[kMaxGlobalStages];  // invalid-key bits of global stages
     __shared__ int glob_src[LF_MAX_GLOBALS];          // source row of each global slot or -1
-    __shared__ int glob_pos[LF_MAX_GLOBALS];          // same-class virtual position or kNoPos
+    __shared__ __attribute__((aligned(16))) int glob_pos[LF_MAX_GLOBALS];  // same-class virtual position or kNoPos
     __shared__ int glob_row[LF_MAX_GLOBALS];          // same as glob_pos, padded or not
     __shared__ uint32_t row_glob[kRowsPerBlock / 32]; // tile rows that are global queries
     __shared__ __attribute__((aligned(16))) char gq_rows[kGlobalQueriesPerBlock * T::kRowBytes];  // first 32 global Q rows
@@ -870,7 +891,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = bh % p.H, dil = p.dil[h], L = p.L;
-    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int rows = p.rows_per_block;
+    const int tpr = ((L + dil - 1) / dil + rows - 1) / rows;
     const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
     const size_t base = (size_t)bh * p.tiles_per_head * n_gq + gi;
     float M = kNegInf, l = 0.f, o = 0.f;
@@ -878,7 +900,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
         float mt[kGroup], lt[kGroup], ot[kGroup];
         for (int j = 0; j < kGroup; ++j) {
             const int t = t0 + j, r = t / tpr;
-            const bool exists = t < p.tiles_per_head && r < dil && (t - r * tpr) * kRowsPerBlock < (L - r + dil - 1) / dil;
+            const bool exists = t < p.tiles_per_head && r < dil && (t - r * tpr) * rows < (L - r + dil - 1) / dil;
             const size_t idx = base + (size_t)t * n_gq;
             mt[j] = exists ? p.ws_ml[2 * idx] : kNegInf;
             lt[j] = exists ? p.ws_ml[2 * idx + 1] : 0.f;
