@@ -184,12 +184,18 @@ struct Bf16 {
     struct QOp { bf16x8 v[4]; };
     struct PFrag { bf16x8 v[2]; };
 
-    // B operand of S^T = K Q^T: lane (query, h2) holds d = 16*kb + 8*h2 + j, scaled
-    // by log2(e)/sqrt(d_h) and rounded back to bf16.
+    // B operand of S^T = K Q^T: lane (query, h2) holds d = 16*kb + 8*h2 + j.  The raw
+    // load and the scaling by log2(e)/sqrt(d_h) (rounded back to bf16) are separate, so
+    // the loads can stay in flight while other set-up work is issued.
+    // row == nullptr reads the static zero row (no branch around the loads).
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
+        if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
+        for (int kb = 0; kb < 4; ++kb)
+            q.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
+    }
+    __device__ static void scale_q(QOp& q) {
         for (int kb = 0; kb < 4; ++kb) {
-            u32x4 x = row ? *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2) : u32x4{0, 0, 0, 0};
-            const f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, x), f32x8);
+            const f32x8 f = __builtin_convertvector(q.v[kb], f32x8);
             q.v[kb] = __builtin_convertvector(f * kScaleLog2, bf16x8);
         }
     }
@@ -351,13 +357,17 @@ struct F32 {
     struct QOp { float v[32]; };
     struct PFrag { float v[16]; };
 
-    // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t,
-    // scaled by log2(e)/sqrt(d_h).
+    // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t;
+    // scale_q multiplies by log2(e)/sqrt(d_h).
     __device__ static void load_q(QOp& q, const Elem* row, int h2) {
+        if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
         for (int t4 = 0; t4 < 8; ++t4) {
-            f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4) : f32x4{0, 0, 0, 0};
-            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e] * kScaleLog2;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4);
+            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
         }
+    }
+    __device__ static void scale_q(QOp& q) {
+        for (int i = 0; i < 32; ++i) q.v[i] *= kScaleLog2;
     }
 
     // Wave wv fills 1-KiB blocks 4*wv .. 4*wv+3 of K and of V (4 rows each); part
@@ -619,6 +629,7 @@ void band_kernel(const Params p) {
     __shared__ int glob_src[LF_MAX_GLOBALS];          // source row of each global slot or -1
     __shared__ __attribute__((aligned(16))) int glob_pos[LF_MAX_GLOBALS];  // same-class virtual position or kNoPos
     __shared__ int glob_row[LF_MAX_GLOBALS];          // same as glob_pos, padded or not
+    __shared__ int glob_g[kGlobalQueriesPerBlock];    // first 32 global positions (or -1)
     __shared__ uint32_t row_glob[kRowsPerBlock / 32]; // tile rows that are global queries
     __shared__ __attribute__((aligned(16))) char gq_rows[kGlobalQueriesPerBlock * T::kRowBytes];  // first 32 global Q rows
 
@@ -656,11 +667,56 @@ void band_kernel(const Params p) {
     const int n_band = nb + 2 + na;
     const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
     const int n_st = n_gst + n_band;
+    // Stage order: one band stage (when there is one besides the home stages), the
+    // global stages, the remaining band stages.  A band stage first lets its copy be
+    // issued before the global slots are set up.
+    const int n_pre = (n_gst > 0 && nb + na > 0) ? 1 : 0;
+    auto is_glob = [&](int t) { return t >= n_pre && t < n_pre + n_gst; };
+    auto band_u = [&](int t) { return t < n_pre ? t : t - n_gst; };
     // First key of the u-th band stage in processing order (before, after, home).
     auto stage_key = [&](int u) {
         const int bs = u < nb ? u : (u < nb + na ? u + 2 : u - na);
         return gbase + kStageKeys * bs;
     };
+
+    // Invalid-key bits of band stage u: keys outside [kb0, kend), or padded.
+    auto band_invalid = [&](int bs) -> uint64_t {
+        if (pad) return band_mask[bs % kMaskRing];
+        const int ks = stage_key(bs);
+        const int lo = kb0 - ks, hi = kend - ks;  // valid keys: lo <= kk < hi
+        uint64_t m = 0;
+        if (lo > 0) m |= lo >= 64 ? ~0ull : ((1ull << lo) - 1);
+        if (hi < 64) m |= hi <= 0 ? ~0ull : (~0ull << hi);
+        return m;
+    };
+    typename T::DmaLane dl;
+    T::dma_lane(dl, wv, lane, dil);
+    // The scalar-base copies use 32-bit per-lane offsets of up to 64 rows dil apart.
+    const bool direct_ok = (uint64_t)dil * kStageKeys * T::kRowBytes < (1ull << 31);
+    // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
+    auto issue = [&](int s, int part) {
+        char* slot = ring + (s % T::kNS) * T::kStageBytes;
+        if (is_glob(s)) {
+            const int* src = glob_src + kStageKeys * (s - n_pre);
+            T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane, part);
+        } else {
+            const int bs = band_u(s);
+            const uint64_t inv = uniform64(band_invalid(bs));
+            const int ks = stage_key(bs);
+            if (inv == 0ull && part == kAllParts && direct_ok) {
+                const size_t row0 = (size_t)(r + ks * dil) * 64;
+                T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
+            } else {
+                T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
+                             wv, lane, part);
+            }
+        }
+    };
+
+    // Without padding a band stage needs nothing from LDS: its copy goes out before
+    // the set-up below, together with the Q operand loads.
+    const bool early = !pad && n_st > 0 && !is_glob(0);
+    if (early) issue(0, kAllParts);
 
     // Global slots: source row (or -1 if unused/padded) and in-window position.
     for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
@@ -670,6 +726,7 @@ void band_kernel(const Params p) {
         glob_src[gi] = ok ? g : -1;
         glob_pos[gi] = ok ? vpos : kNoPos;
         glob_row[gi] = vpos;
+        if (gi < kGlobalQueriesPerBlock) glob_g[gi] = g;
     }
     if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
     // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ...
@@ -702,40 +759,6 @@ void band_kernel(const Params p) {
     }
     __syncthreads();
 
-    // Invalid-key bits of band stage u: keys outside [kb0, kend), or padded.
-    auto band_invalid = [&](int bs) -> uint64_t {
-        if (pad) return band_mask[bs % kMaskRing];
-        const int ks = stage_key(bs);
-        const int lo = kb0 - ks, hi = kend - ks;  // valid keys: lo <= kk < hi
-        uint64_t m = 0;
-        if (lo > 0) m |= lo >= 64 ? ~0ull : ((1ull << lo) - 1);
-        if (hi < 64) m |= hi <= 0 ? ~0ull : (~0ull << hi);
-        return m;
-    };
-    typename T::DmaLane dl;
-    T::dma_lane(dl, wv, lane, dil);
-    // The scalar-base copies use 32-bit per-lane offsets of up to 64 rows dil apart.
-    const bool direct_ok = (uint64_t)dil * kStageKeys * T::kRowBytes < (1ull << 31);
-    // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
-    auto issue = [&](int s, int part) {
-        char* slot = ring + (s % T::kNS) * T::kStageBytes;
-        if (s < n_gst) {
-            const int* src = glob_src + kStageKeys * s;
-            T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane, part);
-        } else {
-            const int bs = s - n_gst;
-            const uint64_t inv = uniform64(band_invalid(bs));
-            const int ks = stage_key(bs);
-            if (inv == 0ull && part == kAllParts && direct_ok) {
-                const size_t row0 = (size_t)(r + ks * dil) * 64;
-                T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
-            } else {
-                T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
-                             wv, lane, part);
-            }
-        }
-    };
-
     State st;
     state_init(st);
     typename T::Lane lo;
@@ -745,31 +768,36 @@ void band_kernel(const Params p) {
     // every register load (Q operand, masks) completes at the wait below, so the
     // compiler's own waits inside the loop have nothing left to wait for (an
     // in-loop vmcnt wait would also drain the stage copies in flight).
-    for (int s = 0; s < T::kNS - 1; ++s)
+    for (int s = early ? 1 : 0; s < T::kNS - 1; ++s)
         if (s < n_st) issue(s, kAllParts);
-    if (p.n_g > 0) {  // Q rows of the first 32 global queries, for (c)
-        const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
-        T::dma_rows(gq_rows, [&](int j) { return j < p.n_g ? Q + (size_t)p.g[j] * 64 : zero; }, wv, lane);
-    }
     wait_vmcnt<0>();
+    T::scale_q(qop);
     for (int t = 0; t < n_st; ++t) {
         wait_stage<T>(min(T::kNS - 2, n_st - 1 - t));
         barrier_nofence();
         const int sn = t + T::kNS - 1;
         if (sn < n_st) {
-            const int bn = sn - n_gst;
+            const int bn = is_glob(sn) ? 0 : band_u(sn);
             if (pad && bn > 0 && bn % kMaskWindow == 0) {
                 fill_band_masks(bn / kMaskWindow);
                 __syncthreads();
             }
             issue(sn, kAllParts);
         }
-        const bool gstage = t < n_gst;
-        const int ks = gstage ? 0 : stage_key(t - n_gst);
-        const uint64_t inv = uniform64(gstage ? glob_mask[t] : band_invalid(t - n_gst));
+        if (t == 0 && p.n_g > 0) {  // Q rows of the first 32 global queries, for (c)
+            const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
+            T::dma_rows(gq_rows, [&](int j) { const int g = glob_g[j]; return g >= 0 ? Q + (size_t)g * 64 : zero; },
+                        wv, lane);
+        }
+        const bool gstage = is_glob(t);
+        const int gidx = t - n_pre;  // global stage index when gstage
+        const int ks = gstage ? 0 : stage_key(band_u(t));
+        const uint64_t inv = uniform64(gstage ? glob_mask[gidx] : band_invalid(band_u(t)));
         const char* slot = ring + (t % T::kNS) * T::kStageBytes;
         if (rows_live && inv != ~0ull) {
-#pragma unroll 1
+            // Both sub-tiles in straight-line code: the second one's operand reads and
+            // products can be scheduled against the first one's softmax.
+#pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
                 const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
                 const int kss = ks + 32 * sub;
@@ -778,7 +806,7 @@ void band_kernel(const Params p) {
                 const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + w;
                 const int mode = gstage ? 2 : (interior ? 0 : 1);
                 sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, kss + 8 * h2 - qv + w, w,
-                            glob_pos + kStageKeys * t + 32 * sub + 8 * h2, w - qv);
+                            glob_pos + kStageKeys * gidx + 32 * sub + 8 * h2, w - qv);
             }
         }
     }
@@ -807,12 +835,14 @@ void band_kernel(const Params p) {
         uint32_t inv32;
         if (gb == 0) {
             T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
+            T::scale_q(gop);
             const int u = n_band - 2 + hs;
             hslot = ring + ((n_gst + u) % T::kNS) * T::kStageBytes;
             inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
         } else {
             const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
             T::load_q(gop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
+            T::scale_q(gop);
             uint64_t hinv[2];
             for (int j = 0; j < 2; ++j) {
                 const int key = r0 + kStageKeys * j + lane;
