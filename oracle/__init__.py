@@ -8,6 +8,8 @@ library and never imports it.
 from .longformer_oracle import (  # noqa: F401
     attention,
     attention_bh,
+    attention_global_proj,
+    attention_global_proj_sampled,
     attention_sampled,
     global_set,
     mask_count,

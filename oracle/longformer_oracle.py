@@ -25,6 +25,12 @@ What it computes (per batch b and head h, with inputs widened to float64):
   "Reformer哈希：突破Transformer计算瓶颈的高效注意力机制详解" (Reformer hashing),
   §"core principle", restricted to the key set above.
 * A query row whose key set is empty gives an all-zero output row.
+* Variant with separate global projections (``attention_global_proj``): the page
+  "基于Block-Sparse Attention的Longformer" §4 gives global attention its own
+  query, key and value projections.  Read inside the one-softmax formulation: a
+  global query row attends every unpadded key with its own projections,
+  softmax(q_g k_g^T / sqrt(d_h)) v_g; every other row is computed exactly as above
+  from q, k, v (its global keys included).
 
 The mask is built explicitly as dense boolean rows (R rows x L keys at a time)
 directly from the set definitions above; no banding, tiling or online softmax.
@@ -177,3 +183,49 @@ def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
                 rows = np.arange(s0, min(L, s0 + ROW_BLOCK))
                 total += int(mask_rows(L, w, d, G, None if pad is None else pad[b], rows).sum())
     return total
+
+
+def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_idx=None, key_pad_mask=None):
+    """Oracle for the variant with separate global projections.  float64 [B, H, L, d].
+
+    Rows not in the global set: ``attention(q, k, v, ...)``.  A global row g:
+    masked softmax over the unpadded keys of q_g[g] . k_g^T / sqrt(d_h), times v_g
+    (page "基于Block-Sparse Attention的Longformer" §4, global attention with its own
+    projections; every global row sees every position, §2).
+    """
+    out = attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask)
+    G = global_set(global_idx)
+    if G.size == 0:
+        return out
+    q_g, k_g, v_g = _as_f64(q_g), _as_f64(k_g), _as_f64(v_g)
+    B, H, L, d = q_g.shape
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    for b in range(B):
+        keep = np.ones((G.size, L), dtype=bool)
+        if pad is not None:
+            keep &= ~pad[b][None, :]
+        for h in range(H):
+            o, _ = _attention_rows(q_g[b, h][G], k_g[b, h], v_g[b, h], keep)
+            out[b, h][G] = o
+    return out
+
+
+def attention_global_proj_sampled(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_idx, key_pad_mask,
+                                  samples):
+    """``attention_global_proj`` output rows for a list of (b, h, i) samples, one by one."""
+    G = set(int(x) for x in global_set(global_idx))
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    res = []
+    for b, h, i in samples:
+        if i in G:
+            L = k_g.shape[2]
+            keep = np.ones((1, L), dtype=bool)
+            if pad is not None:
+                keep &= ~pad[b][None, :]
+            o, _ = _attention_rows(_as_f64(q_g[b, h][i:i + 1]), _as_f64(k_g[b, h]), _as_f64(v_g[b, h]), keep)
+        else:
+            o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
+                             None if pad is None else pad[b], rows=[i])
+        res.append(o[0])
+    return np.stack(res) if res else np.zeros((0, q.shape[-1]))

@@ -244,6 +244,91 @@ def pin_window_example_golden():
         assert len(brute.key_set(i, L, w, dil, [])) == expect
 
 
+# ------------------------------------------- separate global projections
+
+GP_CASES = [
+    # (L, d, w, dils, globals, pad kind, seed)
+    (24, 8, 3, [1, 2], [0, 9], None, 200),
+    (33, 8, 2, [3, 1], [32, 4, 4], "rand", 201),
+    (16, 8, 0, [1, 1], [7], "suffix", 202),
+    (20, 8, 3, [2, 2], [], None, 203),
+]
+
+
+def _gp_inputs(L, d, H, seed):
+    return [_rand((1, H, L, d), seed * 7 + t) for t in range(6)]
+
+
+def pin_global_proj_brute():
+    """Separate global projections: global rows are brute-force attention of q_g over
+    every unpadded key of k_g, v_g; every other row is brute force over its own key
+    set with q, k, v."""
+    for L, d, w, dils, G, padk, seed in GP_CASES:
+        H = len(dils)
+        q, k, v, qg, kg, vg = _gp_inputs(L, d, H, seed)
+        pad = _pad_for(padk, L, seed)
+        got = orc.attention_global_proj(q, k, v, qg, kg, vg, w, dils, G,
+                                        None if pad is None else pad[None, :])
+        Gs = set(G)
+        padl = None if pad is None else pad.tolist()
+        for h in range(H):
+            for i in range(L):
+                keys = brute.key_set(i, L, w, dils[h], G, padl)
+                if i in Gs:
+                    ref = brute.attention_row(qg[0, h, i].tolist(), kg[0, h].tolist(), vg[0, h].tolist(), keys)
+                else:
+                    ref = brute.attention_row(q[0, h, i].tolist(), k[0, h].tolist(), v[0, h].tolist(), keys)
+                err = np.abs(got[0, h, i] - np.array(ref)).max()
+                assert err < 1e-12, (L, w, dils[h], G, i, err)
+
+
+def pin_global_proj_dependence():
+    """Global rows depend only on (q_g, k_g, v_g), the other rows only on (q, k, v):
+    perturbing one triple leaves the other rows bit-identical and moves these rows."""
+    L, d, w, dils, G = 40, 8, 3, [1, 2], [5, 31]
+    q, k, v, qg, kg, vg = _gp_inputs(L, d, 2, 210)
+    pad = np.zeros((1, L), dtype=bool)
+    pad[0, 35:] = True
+    base = orc.attention_global_proj(q, k, v, qg, kg, vg, w, dils, G, pad)
+    is_g = np.zeros(L, dtype=bool)
+    is_g[G] = True
+    a = orc.attention_global_proj(q + 1.0, k * 1.5, v - 2.0, qg, kg, vg, w, dils, G, pad)
+    assert np.array_equal(a[:, :, is_g], base[:, :, is_g])
+    assert np.abs(a[:, :, ~is_g] - base[:, :, ~is_g]).min(axis=-1).max() > 0
+    b = orc.attention_global_proj(q, k, v, qg + 1.0, kg * 1.5, vg - 2.0, w, dils, G, pad)
+    assert np.array_equal(b[:, :, ~is_g], base[:, :, ~is_g])
+    assert np.abs(b[:, :, is_g] - base[:, :, is_g]).min() > 0
+
+
+def pin_global_proj_closed_forms():
+    """k_g = 0 makes a global row the mean of the unpadded v_g rows; k_g = k, v_g = v,
+    q_g = q is the single-projection attention."""
+    L, d, w, dils, G = 30, 8, 2, [1, 3], [0, 17]
+    q, k, v, qg, kg, vg = _gp_inputs(L, d, 2, 220)
+    pad = np.zeros((1, L), dtype=bool)
+    pad[0, [3, 4, 25]] = True
+    got = orc.attention_global_proj(q, k, v, qg, np.zeros_like(kg), vg, w, dils, G, pad)
+    mean = vg[0][:, ~pad[0]].mean(axis=1)  # [H, d]
+    for g in G:
+        assert np.abs(got[0, :, g] - mean).max() < 1e-12
+    same = orc.attention_global_proj(q, k, v, q, k, v, w, dils, G, pad)
+    ref = orc.attention(q, k, v, w, dils, G, pad)
+    assert np.abs(same - ref).max() < 1e-12
+
+
+def pin_global_proj_sampled():
+    """The row-by-row sampler agrees with the full computation."""
+    L, d, w, dils, G = 36, 8, 4, [2, 1], [1, 20, 35]
+    q, k, v, qg, kg, vg = _gp_inputs(L, d, 2, 230)
+    pad = np.zeros((1, L), dtype=bool)
+    pad[0, 30:] = True
+    full = orc.attention_global_proj(q, k, v, qg, kg, vg, w, dils, G, pad)
+    samples = [(0, 0, 1), (0, 1, 20), (0, 1, 2), (0, 0, 33), (0, 1, 35)]
+    got = orc.attention_global_proj_sampled(q, k, v, qg, kg, vg, w, dils, G, pad, samples)
+    ref = np.stack([full[b, h, i] for b, h, i in samples])
+    assert np.abs(got - ref).max() < 1e-12
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -259,4 +344,8 @@ ALL_PINS = [
     pin_head_permutation,
     pin_dense_counts_golden,
     pin_window_example_golden,
+    pin_global_proj_brute,
+    pin_global_proj_dependence,
+    pin_global_proj_closed_forms,
+    pin_global_proj_sampled,
 ]

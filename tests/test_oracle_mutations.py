@@ -110,6 +110,21 @@ def _rows_nan_empty(q, k, v, m):  # no guard for rows without keys
     return p @ v, p
 
 
+_GP = orc.attention_global_proj
+
+
+def _gp_uses_k(q, k, v, q_g, k_g, v_g, *a, **kw):  # global rows scored against k, not k_g
+    return _GP(q, k, v, q_g, k, v_g, *a, **kw)
+
+
+def _gp_uses_q(q, k, v, q_g, k_g, v_g, *a, **kw):  # global rows with the window query q
+    return _GP(q, k, v, q, k_g, v_g, *a, **kw)
+
+
+def _gp_uses_v(q, k, v, q_g, k_g, v_g, *a, **kw):  # global rows weight v, not v_g
+    return _GP(q, k, v, q_g, k_g, v, *a, **kw)
+
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -124,6 +139,9 @@ MUTANTS = {
     "weights_times_k": ("_attention_rows", _rows_pk),
     "zero_fill_softmax": ("_attention_rows", _rows_zero_fill),
     "nan_empty_rows": ("_attention_rows", _rows_nan_empty),
+    "global_proj_uses_k": ("attention_global_proj", _gp_uses_k),
+    "global_proj_uses_q": ("attention_global_proj", _gp_uses_q),
+    "global_proj_uses_v": ("attention_global_proj", _gp_uses_v),
 }
 
 
