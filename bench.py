@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--global-proj", action="store_true",
+                    help="global rows use their own q/k/v projections (lf_attn_forward_global_proj)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -148,8 +150,14 @@ def main():
     handle = binding.LfAttn(wl.dtype)
     dil = wl.dil_list()
 
-    def step():
-        binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle)
+    if args.global_proj:
+        qgd, kgd, vgd = (t.to(dev) for t in workloads.make_global_proj(wl))
+
+        def step():
+            binding.forward_global_proj(qd, kd, vd, qgd, kgd, vgd, wl.w, dil, G, padd, out=out, handle=handle)
+    else:
+        def step():
+            binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle)
 
     for _ in range(args.warmup):
         step()
@@ -175,7 +183,7 @@ def main():
     stage_avg = {k2: v2[0] / max(1, v2[1]) for k2, v2 in st.items()}
     k_avg_ms = stage_avg["band"]  # the dominant kernel
     achieved = flops / (k_avg_ms * 1e-3) / 1e12  # every attended pair but the merge's arithmetic
-    traffic = traffic_for(name)
+    traffic = None if args.global_proj else traffic_for(name)
 
     res = {
         "metric": METRIC,
@@ -197,6 +205,7 @@ def main():
             "padded_lengths": list(wl.lengths) or None,
             "global_batch": wl.B,
             "parallelism": "single GPU",
+            "global_projections": "separate" if args.global_proj else "shared",
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "attended_pairs": pairs.total,

@@ -98,6 +98,33 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
                           const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
                           void* stream);
 
+/*
+ * The same forward with separate projections for the global rows.
+ *
+ * Page "基于Block-Sparse Attention的Longformer" §4 gives global attention its
+ * own query, key and value projections.  Here a global query row i attends
+ * every unpadded key with them,
+ *
+ *   O[b,h,i,:] = softmax_j( Q_g[b,h,i,:] . K_g[b,h,j,:] / sqrt(d_h) ) V_g[b,h,j,:],
+ *
+ * and every other row is computed exactly as by lf_attn_forward from q, k, v
+ * (its global keys included).
+ *
+ * q_g, k_g, v_g : DEVICE pointers to contiguous [B][H][L][d_h] tensors of the
+ *                 handle's dtype, 16-byte aligned, caller-owned, none of them
+ *                 overlapping `out` (they may alias q, k, v or each other).
+ *                 Only the global rows of q_g are read, and only when
+ *                 n_global > 0; all three must be non-null regardless.
+ * All other arguments, ownership, workspace and error behaviour: as for
+ * lf_attn_forward.  With q_g = q, k_g = k, v_g = v the result equals
+ * lf_attn_forward's up to rounding.
+ */
+lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k, const void* v,
+                                      const void* q_g, const void* k_g, const void* v_g, void* out,
+                                      int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                                      const int32_t* global_idx, int n_global,
+                                      const uint8_t* key_pad_mask, void* stream);
+
 /* Free the handle and its device workspace.  NULL is a no-op.  Waits for the
  * device before freeing (hipFree semantics). */
 lf_status lf_attn_destroy(lf_attn_t h);

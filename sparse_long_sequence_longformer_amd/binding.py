@@ -26,6 +26,7 @@ MAX_GLOBALS = 256
 EXPORTS = (
     "lf_attn_create",
     "lf_attn_forward",
+    "lf_attn_forward_global_proj",
     "lf_attn_destroy",
     "lf_attn_status_string",
     "lf_attn_last_error",
@@ -62,6 +63,10 @@ def load_library():
                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
                                     vp, vp]
     lib.lf_attn_forward.restype = i32
+    lib.lf_attn_forward_global_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                                i32, vp, vp]
+    lib.lf_attn_forward_global_proj.restype = i32
     lib.lf_attn_destroy.argtypes = [vp]
     lib.lf_attn_destroy.restype = i32
     lib.lf_attn_status_string.argtypes = [i32]
@@ -103,17 +108,26 @@ class LfAttn:
                     msg = f"{msg}: {detail}"
             raise LfAttnError(st, msg)
 
-    def forward_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
-        dil_arr, nd = _int32_array(dil)
+    @staticmethod
+    def _host_arrays(dil, global_idx):
+        dil_arr, _ = _int32_array(dil)
         g_arr, ng = _int32_array(global_idx if global_idx is not None else [])
-        if dil_arr is None:
-            dil_p = ctypes.POINTER(ctypes.c_int32)()
-        else:
-            dil_p = ctypes.cast(dil_arr, ctypes.POINTER(ctypes.c_int32))
-        g_p = ctypes.cast(g_arr, ctypes.POINTER(ctypes.c_int32)) if g_arr is not None \
-            else ctypes.POINTER(ctypes.c_int32)()
+        null = ctypes.POINTER(ctypes.c_int32)()
+        dil_p = null if dil_arr is None else ctypes.cast(dil_arr, ctypes.POINTER(ctypes.c_int32))
+        g_p = null if g_arr is None else ctypes.cast(g_arr, ctypes.POINTER(ctypes.c_int32))
+        return (dil_arr, g_arr), dil_p, g_p, ng
+
+    def forward_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
         st = self.lib.lf_attn_forward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w,
                                       dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def forward_global_proj_raw(self, q_ptr, k_ptr, v_ptr, qg_ptr, kg_ptr, vg_ptr, out_ptr, B, H, L, d_h, w,
+                                dil, global_idx, pad_ptr, stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_attn_forward_global_proj(self.handle, q_ptr, k_ptr, v_ptr, qg_ptr, kg_ptr, vg_ptr,
+                                                  out_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
     def set_stage_timing(self, enable: bool):
@@ -146,15 +160,9 @@ def _handle_for(dtype: str) -> LfAttn:
     return _handles[dtype]
 
 
-def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None):
-    """Longformer window + global attention forward on the GPU.
-
-    q, k, v: contiguous CUDA/HIP tensors [B, H, L, 64], all bfloat16 or all float32.
-    w: keys on each side of the window.  dil: one dilation per head (sequence or int).
-    global_idx: positions attended by and attending to everything (host sequence).
-    key_pad_mask: [B, L] bool/uint8 device tensor, nonzero = padded key, or None.
-    Returns ``out`` (allocated if not given), same shape and dtype as q.
-    """
+def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle):
+    """Checks shared by both entry points; returns (B, H, L, d_h, dilation list,
+    global list, pad pointer, out, handle, stream)."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -163,14 +171,14 @@ def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, 
         dt = "f32"
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
-    for name, t in (("k", k), ("v", v)):
+    for name, t in others:
         if t.dtype != q.dtype or t.shape != q.shape:
             raise ValueError(f"{name} must match q in dtype and shape")
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, L, d_h]")
-    for t in (q, k, v):
+    for name, t in [("q", q)] + list(others):
         if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+            raise ValueError(f"{name} must be a contiguous device tensor")
     B, H, L, d_h = q.shape
     if isinstance(dil, int):
         dil = [dil] * H
@@ -196,7 +204,40 @@ def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, 
     if h.dtype != dt:
         raise ValueError("handle dtype does not match the inputs")
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    return B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream
+
+
+def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None):
+    """Longformer window + global attention forward on the GPU.
+
+    q, k, v: contiguous CUDA/HIP tensors [B, H, L, 64], all bfloat16 or all float32.
+    w: keys on each side of the window.  dil: one dilation per head (sequence or int).
+    global_idx: positions attended by and attending to everything (host sequence).
+    key_pad_mask: [B, L] bool/uint8 device tensor, nonzero = padded key, or None.
+    Returns ``out`` (allocated if not given), same shape and dtype as q.
+    """
+    import torch
+
+    B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle)
     with torch.cuda.device(q.device):
         h.forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
                       global_idx, pad_ptr, stream)
+    return out
+
+
+def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, key_pad_mask=None, out=None,
+                        handle: LfAttn | None = None):
+    """As ``forward``, but the global query rows attend every unpadded key with their
+    own projections q_g, k_g, v_g (tensors shaped and typed like q); every other row
+    uses q, k, v."""
+    import torch
+
+    B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
+        q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)], w, dil, global_idx,
+        key_pad_mask, out, handle)
+    with torch.cuda.device(q.device):
+        h.forward_global_proj_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_g.data_ptr(), k_g.data_ptr(),
+                                  v_g.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil, global_idx,
+                                  pad_ptr, stream)
     return out

@@ -149,12 +149,22 @@ lf_status lf_attn_stage_times(lf_attn_t h, double* ms, int64_t* launches) {
     return LF_OK;
 }
 
-lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void* v, void* out, int B, int H,
-                          int L, int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx,
-                          int n_global, const uint8_t* key_pad_mask, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both forward entry points.  qg, kg, vg are all null (one projection for every
+// row) or all non-null (separate projections of the global rows).
+lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
+                       const void* vg, void* out, int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                       const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask, void* stream) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->last_error.clear();
     if (!q || !k || !v || !out) return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+    const bool sep = qg || kg || vg;
+    if (sep && !(qg && kg && vg)) return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g and v_g must all be non-null");
+    if (sep && (!aligned16(qg) || !aligned16(kg) || !aligned16(vg)))
+        return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g and v_g must be 16-byte aligned");
     if (B < 1 || H < 1 || L < 1) return fail(h, LF_ERR_INVALID_ARG, "need B, H, L >= 1 (got %d, %d, %d)", B, H, L);
     if (d_h != LF_HEAD_DIM) return fail(h, LF_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
     if (H > LF_MAX_HEADS) return fail(h, LF_ERR_UNSUPPORTED, "at most %d heads (got %d)", LF_MAX_HEADS, H);
@@ -173,6 +183,8 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
     const size_t bytes = static_cast<size_t>(n_elem) * elem;
     if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
         return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q, k or v");
+    if (sep && (overlaps(out, qg, bytes) || overlaps(out, kg, bytes) || overlaps(out, vg, bytes)))
+        return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q_g, k_g or v_g");
 
     lf::Params p;
     std::memset(&p, 0, sizeof(p));
@@ -191,6 +203,9 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
     p.k = k;
     p.v = v;
     p.out = out;
+    p.qg = qg;
+    p.kg = kg;
+    p.vg = vg;
     p.pad = key_pad_mask;
     p.B = B;
     p.H = H;
@@ -252,6 +267,29 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
         }
     }
     return LF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void* v, void* out, int B, int H,
+                          int L, int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx,
+                          int n_global, const uint8_t* key_pad_mask, void* stream) {
+    return forward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, B, H, L, d_h, w, dil_per_head, global_idx,
+                        n_global, key_pad_mask, stream);
+}
+
+lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k, const void* v, const void* q_g,
+                                      const void* k_g, const void* v_g, void* out, int B, int H, int L, int d_h,
+                                      int w, const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                                      const uint8_t* key_pad_mask, void* stream) {
+    if (h && (!q_g || !k_g || !v_g)) {
+        h->last_error = "q_g, k_g and v_g must be non-null";
+        return LF_ERR_INVALID_ARG;
+    }
+    return forward_impl(h, q, k, v, q_g, k_g, v_g, out, B, H, L, d_h, w, dil_per_head, global_idx, n_global,
+                        key_pad_mask, stream);
 }
 
 }  // extern "C"

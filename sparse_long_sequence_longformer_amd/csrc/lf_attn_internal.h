@@ -23,6 +23,11 @@ struct Params {
     const void* k;
     const void* v;
     void* out;
+    // Separate projections of the global query rows (same layout as q, k, v), or all
+    // nullptr: global rows then use q, k, v like every other row.
+    const void* qg;
+    const void* kg;
+    const void* vg;
     const uint8_t* pad;  // [B][L] or nullptr
     // Global-row partials: one (max, sum, 64 outputs) per (b*H + h, row tile, global
     // query), written by every work-group for its own 128 "home" keys.

@@ -652,6 +652,11 @@ void band_kernel(const Params p) {
     const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
     Elem* O = reinterpret_cast<Elem*>(p.out) + off;
     const uint8_t* pad = p.pad ? p.pad + (size_t)b * L : nullptr;
+    // Tensors of the global rows' own attention (c): the separate projections if given.
+    const bool sep = p.kg != nullptr;
+    const Elem* QG = sep ? reinterpret_cast<const Elem*>(p.qg) + off : Q;
+    const Elem* KG = sep ? reinterpret_cast<const Elem*>(p.kg) + off : K;
+    const Elem* VG = sep ? reinterpret_cast<const Elem*>(p.vg) + off : V;
 
     const int qa = r0 + 32 * wv;      // first virtual row of this wave
     const int qv = qa + (lane & 31);  // this lane's virtual row
@@ -786,7 +791,7 @@ void band_kernel(const Params p) {
         }
         if (t == 0 && p.n_g > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
-            T::dma_rows(gq_rows, [&](int j) { const int g = glob_g[j]; return g >= 0 ? Q + (size_t)g * 64 : zero; },
+            T::dma_rows(gq_rows, [&](int j) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * 64 : zero; },
                         wv, lane);
         }
         const bool gstage = is_glob(t);
@@ -822,8 +827,9 @@ void band_kernel(const Params p) {
     // (c) Global rows: every key belongs to exactly one work-group's "home" range
     // [r0, r0 + 128) of its class, so each work-group folds the global queries over
     // its home keys and leaves one partial (max, sum, unnormalised output) per query.
-    // For the first 32 global queries the home keys are the last two band stages,
-    // still in the ring, and the Q rows were copied to LDS with the first stage.
+    // The Q rows of the first 32 global queries were copied to LDS with the first
+    // stage; for them the home keys are the last two band stages, still in the ring,
+    // unless the global rows have their own key and value projections.
     __shared__ float red_ml[kWaves][32][2];
     float* red_o = reinterpret_cast<float*>(ring);  // kWaves x 32 x 64 floats = 32 KiB
     const int home_end = min(Lr, r0 + kRowsPerBlock);
@@ -835,14 +841,16 @@ void band_kernel(const Params p) {
         uint32_t inv32;
         if (gb == 0) {
             T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
-            T::scale_q(gop);
+        } else {
+            const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
+            T::load_q(gop, gq < p.n_g ? QG + (size_t)p.g[gq] * 64 : nullptr, h2);
+        }
+        T::scale_q(gop);
+        if (gb == 0 && !sep) {
             const int u = n_band - 2 + hs;
             hslot = ring + ((n_gst + u) % T::kNS) * T::kStageBytes;
             inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
         } else {
-            const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
-            T::load_q(gop, gq < p.n_g ? Q + (size_t)p.g[gq] * 64 : nullptr, h2);
-            T::scale_q(gop);
             uint64_t hinv[2];
             for (int j = 0; j < 2; ++j) {
                 const int key = r0 + kStageKeys * j + lane;
@@ -854,7 +862,7 @@ void band_kernel(const Params p) {
             for (int j = 0; j < 2; ++j) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
-                T::dma_stage(ring + j * T::kStageBytes, K, V,
+                T::dma_stage(ring + j * T::kStageBytes, KG, VG,
                              [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             }
             wait_vmcnt<0>();

@@ -9,7 +9,9 @@ Recipe (fixed, shared by every consumer):
      (B, H, L, 64); optionally scaled (0.5 for the CLS workload);
   3. bf16 workloads are rounded to bfloat16 by torch (round to nearest even);
   4. random global positions use numpy.random.default_rng(1).choice(L, n, replace=False), sorted;
-  5. the key padding mask is pad[b, j] = (j >= length[b]) (uint8, 1 = padded).
+  5. the key padding mask is pad[b, j] = (j >= length[b]) (uint8, 1 = padded);
+  6. separate global projections q_g, k_g, v_g (when used) follow steps 1-3 with
+     seed + 1000.
 
 The five shapes follow the pages' workloads: hidden size 768 = 12 heads x 64
 (page "基于Block-Sparse Attention的Longformer" §6 example model), 4096-token
@@ -99,6 +101,14 @@ def make_qkv(wl: Workload):
         arrs.append(a)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     return tuple(torch.from_numpy(a).to(tdt) for a in arrs)
+
+
+def make_global_proj(wl: Workload):
+    """Return (q_g, k_g, v_g), the global rows' own projections, drawn like make_qkv
+    with seed + 1000."""
+    from dataclasses import replace
+
+    return make_qkv(replace(wl, seed=wl.seed + 1000))
 
 
 def make_custom(B, H, L, dtype="bf16", seed=0, scale=1.0, d=64):

@@ -110,11 +110,42 @@ def test_invalid_arguments_rejected_on_host(kw, code, frag):
         lib.lf_attn_destroy(h)
 
 
+def _call_gp(h, qg=FAKE * 5, kg=FAKE * 6, vg=FAKE * 7, out=FAKE * 4):
+    lib = binding.load_library()
+    dil = (ctypes.c_int32 * 2)(1, 2)
+    g = (ctypes.c_int32 * 1)(3)
+    st = lib.lf_attn_forward_global_proj(h, FAKE, FAKE * 2, FAKE * 3, qg, kg, vg, out, 1, 2, 64, 64, 4,
+                                         ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32)),
+                                         ctypes.cast(g, ctypes.POINTER(ctypes.c_int32)), 1, None, None)
+    return st, lib.lf_attn_last_error(h).decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,frag", [
+    (dict(qg=None), "non-null"),
+    (dict(kg=None), "non-null"),
+    (dict(vg=None), "non-null"),
+    (dict(kg=FAKE * 6 + 4), "aligned"),
+    (dict(out=FAKE * 7 + 1024), "overlap q_g, k_g or v_g"),
+])
+def test_global_proj_invalid_arguments(kw, frag):
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        st, msg = _call_gp(h, **kw)
+        assert st == 1 and frag in msg, (st, msg)
+    finally:
+        lib.lf_attn_destroy(h)
+
+
 @needs_lib
 def test_null_handle():
     lib = binding.load_library()
     assert lib.lf_attn_forward(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None, None, 0, None, None) == 1
     assert lib.lf_attn_last_error(None) == b""
+    assert lib.lf_attn_forward_global_proj(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0,
+                                           None, None, 0, None, None) == 1
 
 
 def test_python_forward_requires_device_tensors():
