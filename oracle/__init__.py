@@ -7,9 +7,13 @@ library and never imports it.
 
 from .longformer_oracle import (  # noqa: F401
     attention,
+    attention_backward,
+    attention_backward_bh,
     attention_bh,
     attention_global_proj,
     attention_global_proj_sampled,
+    attention_lse,
+    attention_lse_bh,
     attention_sampled,
     global_set,
     mask_count,

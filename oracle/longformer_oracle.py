@@ -32,6 +32,17 @@ What it computes (per batch b and head h, with inputs widened to float64):
   softmax(q_g k_g^T / sqrt(d_h)) v_g; every other row is computed exactly as above
   from q, k, v (its global keys included).
 
+* Per-row log-sum-exp (``attention_lse``): log of the sum over the key set of
+  exp(S_ij); -inf for a row with no key.  It is the normaliser of the row's
+  softmax, the quantity a backward pass reuses.
+* Gradients (``attention_backward``): for an upstream gradient dO of the output,
+  the textbook derivatives of O = P V with P the row softmax of S (Reformer
+  hashing page, "core principle" formula; the same key sets):
+      dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(dP * P)),
+      dQ = dS K / sqrt(d_h),   dK = dS^T Q / sqrt(d_h),
+  with rowsum(dP * P) = rowsum(dO * O).  A row with no key has a constant zero
+  output: it contributes nothing.
+
 The mask is built explicitly as dense boolean rows (R rows x L keys at a time)
 directly from the set definitions above; no banding, tiling or online softmax.
 """
@@ -229,3 +240,80 @@ def attention_global_proj_sampled(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, 
                              None if pad is None else pad[b], rows=[i])
         res.append(o[0])
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
+
+
+def _scores_rows(q, k, m):
+    """Masked scores S = Q K^T / sqrt(d) (-inf off the mask) of the query rows in q."""
+    d = q.shape[1]
+    return np.where(m, (q @ k.T) / math.sqrt(d), -np.inf)
+
+
+def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None) -> np.ndarray:
+    """log sum_{j in keys(i)} exp(q_i . k_j / sqrt(d)) of every row; -inf without keys."""
+    q, k = _as_f64(q), _as_f64(k)
+    L = k.shape[0]
+    G = global_set(global_idx)
+    out = np.empty(L, dtype=np.float64)
+    for s0 in range(0, L, ROW_BLOCK):
+        blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
+        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk))
+        top = s.max(axis=1)
+        has = np.isfinite(top)
+        safe = np.where(has, top, 0.0)
+        tot = np.exp(s - safe[:, None]).sum(axis=1)
+        out[s0:s0 + blk.size] = np.where(has, safe + np.log(np.where(has, tot, 1.0)), -np.inf)
+    return out
+
+
+def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None) -> np.ndarray:
+    """Per-row log-sum-exp of the full problem: float64 [B, H, L]."""
+    q, k = _as_f64(q), _as_f64(k)
+    B, H, L, _ = q.shape
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    out = np.zeros((B, H, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = attention_lse_bh(q[b, h], k[b, h], w, dil[h], global_idx,
+                                         None if pad is None else pad[b])
+    return out
+
+
+def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None):
+    """Gradients (dQ, dK, dV) of one (batch, head) slice for the upstream gradient dout.
+
+    Row blocks of the explicit mask; dK and dV collect every block's contribution.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    L, d = q.shape
+    G = global_set(global_idx)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for s0 in range(0, L, ROW_BLOCK):
+        blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
+        m = mask_rows(L, w, dil, G, pad_row, blk)
+        o, p = _attention_rows(q[blk], k, v, m)
+        dv += p.T @ do[blk]
+        dp = do[blk] @ v.T
+        delta = (do[blk] * o).sum(axis=1, keepdims=True)
+        ds = p * (dp - delta)
+        dq[blk] = ds @ k / math.sqrt(d)
+        dk += ds.T @ q[blk] / math.sqrt(d)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None):
+    """Gradients of the full problem: three float64 [B, H, L, d] arrays (dQ, dK, dV)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    B, H, L, d = q.shape
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    if len(dil) != H:
+        raise ValueError("need one dilation per head")
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    dq, dk, dv = (np.zeros((B, H, L, d), dtype=np.float64) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = attention_backward_bh(
+                q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], global_idx, None if pad is None else pad[b])
+    return dq, dk, dv

@@ -329,6 +329,137 @@ def pin_global_proj_sampled():
     assert np.abs(got - ref).max() < 1e-12
 
 
+# ------------------------------------------------------- backward and log-sum-exp
+
+BWD_CASES = [
+    # (L, d, w, dil, globals, pad kind, seed)
+    (16, 8, 2, 1, [], None, 300),
+    (24, 8, 3, 2, [5], None, 301),
+    (33, 8, 4, 1, [2, 30, 30], "rand", 302),
+    (40, 8, 2, 3, [9, 39], "suffix", 303),
+    (20, 8, 3, 2, [1], "allbut", 304),
+    (30, 8, 40, 1, [], None, 305),
+]
+
+
+def _torch_dense_attention(q, k, v, keysets):
+    """softmax(Q K^T / sqrt(d)) V in torch float64 with the key sets given as lists
+    (enumerated by brute.key_set); rows without keys give zeros."""
+    L, d = q.shape
+    m = torch.zeros(L, L, dtype=torch.bool)
+    for i, ks in enumerate(keysets):
+        m[i, ks] = True
+    s = (q @ k.T) / math.sqrt(d)
+    s = s.masked_fill(~m, float("-inf"))
+    p = torch.softmax(s, dim=1)
+    p = torch.where(m.any(dim=1, keepdim=True), p, torch.zeros_like(p))
+    return p @ v
+
+
+def pin_backward_autograd():
+    """Analytic gradients equal torch autograd of a dense masked attention whose key
+    sets come from the brute-force enumerator."""
+    for L, d, w, dil, G, padk, seed in BWD_CASES:
+        q, k, v, do = (_rand((L, d), seed * 5 + t) for t in range(4))
+        pad = _pad_for(padk, L, seed)
+        padl = None if pad is None else pad.tolist()
+        keysets = [brute.key_set(i, L, w, dil, G, padl) for i in range(L)]
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        out = _torch_dense_attention(tq, tk, tv, keysets)
+        (out * torch.from_numpy(do)).sum().backward()
+        dq, dk, dv = orc.attention_backward_bh(q, k, v, do, w, dil, G, pad)
+        for name, a, b in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+            err = np.abs(a - b.numpy()).max()
+            assert err < 1e-12, (name, L, w, dil, G, padk, err)
+
+
+def pin_backward_finite_differences():
+    """Central differences of sum(O * dO) in float64 match every gradient entry."""
+    L, d, w, dil, G = 10, 4, 2, 2, [3]
+    q, k, v, do = (_rand((L, d), 320 + t) for t in range(4))
+    pad = np.zeros(L, dtype=bool)
+    pad[[1, 8]] = True
+    dq, dk, dv = orc.attention_backward_bh(q, k, v, do, w, dil, G, pad)
+
+    def loss(q_, k_, v_):
+        return float((orc.attention_bh(q_, k_, v_, w, dil, G, pad) * do).sum())
+
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for i in range(L):
+            for c in range(d):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][i, c] += eps
+                up = loss(*args)
+                args[which][i, c] -= 2 * eps
+                dn = loss(*args)
+                fd = (up - dn) / (2 * eps)
+                assert abs(fd - grad[i, c]) < 1e-7, (which, i, c, fd, grad[i, c])
+
+
+def pin_backward_structure():
+    """With dO nonzero on one row only, dK and dV vanish exactly off that row's key
+    set and not on it, and dQ vanishes on every other row."""
+    L, d, w, dil, G = 36, 8, 3, 2, [4, 30]
+    q, k, v = (_rand((L, d), 330 + t) for t in range(3))
+    pad = np.zeros(L, dtype=bool)
+    pad[[10, 25]] = True
+    for i in (0, 4, 12, 30, 35):
+        do = np.zeros((L, d))
+        do[i] = _rand((d,), 340 + i)
+        dq, dk, dv = orc.attention_backward_bh(q, k, v, do, w, dil, G, pad)
+        keys = set(brute.key_set(i, L, w, dil, G, pad.tolist()))
+        for j in range(L):
+            if j in keys:
+                assert np.abs(dv[j]).max() > 0 and np.abs(dk[j]).max() > 0, (i, j)
+            else:
+                assert np.all(dv[j] == 0) and np.all(dk[j] == 0), (i, j)
+            if j != i:
+                assert np.all(dq[j] == 0), (i, j)
+
+
+def pin_backward_invariants():
+    """Shift invariance of the softmax: adding one vector to every key leaves O
+    unchanged, so the dK rows sum to zero; adding c to every value adds c to each row
+    with a key, so the dV rows sum to the dO rows of rows with keys.  w = 0 without
+    globals or padding is O = V: dV = dO, dQ = dK = 0 (up to rounding)."""
+    L, d = 44, 8
+    q, k, v, do = (_rand((L, d), 350 + t) for t in range(4))
+    pad = np.zeros(L, dtype=bool)
+    pad[12:20] = True  # with w = 1, dil = 1, rows 13..18 have no key
+    dq, dk, dv = orc.attention_backward_bh(q, k, v, do, 1, 1, None, pad)
+    assert np.abs(dk.sum(axis=0)).max() < 1e-12
+    has = np.array([len(brute.key_set(i, L, 1, 1, [], pad.tolist())) > 0 for i in range(L)])
+    assert not has[13:19].any() and has[:12].all()
+    assert np.abs(dv.sum(axis=0) - do[has].sum(axis=0)).max() < 1e-12
+    dq0, dk0, dv0 = orc.attention_backward_bh(q, k, v, do, 0, 1)
+    # dS = 1 * (do_i . v_i - do_i . o_i) with o_i = v_i: zero up to the rounding of the
+    # two dot products
+    assert np.array_equal(dv0, do) and np.abs(dq0).max() < 1e-13 and np.abs(dk0).max() < 1e-13
+
+
+def pin_lse_brute():
+    """Per-row log-sum-exp equals log(fsum(exp)) over the enumerated key set, and
+    torch's logsumexp in the full-attention limit."""
+    for L, d, w, dil, G, padk, seed in BWD_CASES:
+        q, k = _rand((L, d), seed * 5), _rand((L, d), seed * 5 + 1)
+        pad = _pad_for(padk, L, seed)
+        got = orc.attention_lse_bh(q, k, w, dil, G, pad)
+        for i in range(L):
+            keys = brute.key_set(i, L, w, dil, G, None if pad is None else pad.tolist())
+            if not keys:
+                assert got[i] == -np.inf
+                continue
+            sc = [math.fsum(q[i, t] * k[j, t] for t in range(d)) / math.sqrt(d) for j in keys]
+            top = max(sc)
+            ref = top + math.log(math.fsum(math.exp(x - top) for x in sc))
+            assert abs(got[i] - ref) < 1e-12, (L, i, got[i], ref)
+    L = 50
+    q, k = _rand((L, 16), 360), _rand((L, 16), 361)
+    ref = torch.logsumexp(torch.from_numpy(q @ k.T / 4.0), dim=1).numpy()
+    assert np.abs(orc.attention_lse_bh(q, k, L, 1) - ref).max() < 1e-12
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -348,4 +479,9 @@ ALL_PINS = [
     pin_global_proj_dependence,
     pin_global_proj_closed_forms,
     pin_global_proj_sampled,
+    pin_backward_autograd,
+    pin_backward_finite_differences,
+    pin_backward_structure,
+    pin_backward_invariants,
+    pin_lse_brute,
 ]

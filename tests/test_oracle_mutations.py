@@ -125,6 +125,39 @@ def _gp_uses_v(q, k, v, q_g, k_g, v_g, *a, **kw):  # global rows weight v, not v
     return _GP(q, k, v, q_g, k_g, v, *a, **kw)
 
 
+def _bwd_mutant(kind):
+    """attention_backward_bh with one plausible mistake planted."""
+
+    def fn(q, k, v, dout, w, dil, global_idx=None, pad_row=None):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+        L, d = q.shape
+        G = orc.global_set(global_idx)
+        m = orc.mask_rows(L, w, dil, G, pad_row, np.arange(L))
+        o, p = orc._attention_rows(q, k, v, m)
+        dv = p.T @ do
+        dp = do @ v.T
+        delta = (do * o).sum(axis=1, keepdims=True)
+        if kind == "no_delta":
+            ds = p * dp
+        elif kind == "delta_from_dp":  # rowsum of dP instead of rowsum(P * dP)
+            ds = p * (dp - dp.sum(axis=1, keepdims=True))
+        else:
+            ds = p * (dp - delta)
+        dq = ds @ k / math.sqrt(d)
+        dk = ds.T @ q / math.sqrt(d)
+        if kind == "dk_unscaled":
+            dk = ds.T @ q
+        if kind == "dq_from_v":
+            dq = ds @ v / math.sqrt(d)
+        if kind == "dv_unmasked_softmax":  # dV from weights over every key
+            s = (q @ k.T) / math.sqrt(d)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            dv = (e / e.sum(axis=1, keepdims=True)).T @ do
+        return dq, dk, dv
+
+    return fn
+
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -142,6 +175,11 @@ MUTANTS = {
     "global_proj_uses_k": ("attention_global_proj", _gp_uses_k),
     "global_proj_uses_q": ("attention_global_proj", _gp_uses_q),
     "global_proj_uses_v": ("attention_global_proj", _gp_uses_v),
+    "bwd_no_delta": ("attention_backward_bh", _bwd_mutant("no_delta")),
+    "bwd_delta_from_dp": ("attention_backward_bh", _bwd_mutant("delta_from_dp")),
+    "bwd_dk_unscaled": ("attention_backward_bh", _bwd_mutant("dk_unscaled")),
+    "bwd_dq_from_v": ("attention_backward_bh", _bwd_mutant("dq_from_v")),
+    "bwd_dv_unmasked": ("attention_backward_bh", _bwd_mutant("dv_unmasked_softmax")),
 }
 
 
