@@ -11,6 +11,9 @@ de-duplication and padding), divided by the wall time of the K timed steps.
 Prints one JSON line.  Also reported: the kernel's own rate against the bf16 MFMA
 peak (HIP events around each launch, on the launch stream), and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
+
+Variants (not the default line): --global-proj (separate projections of the global
+rows), --backward (the backward pass alone and a forward + backward training step).
 """
 
 from __future__ import annotations
@@ -30,13 +33,18 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 METRIC = "window+global attn fwd effective TFLOP/s and % bf16 MFMA peak, L=4096 w=512"
-KERNEL_SRC = os.path.join(ROOT, "sparse_long_sequence_longformer_amd", "csrc", "lf_attn_kernels.hip")
+CSRC = os.path.join(ROOT, "sparse_long_sequence_longformer_amd", "csrc")
+# Sources of the forward kernels (the traffic counters are valid for this text only).
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("lf_attn_kernels.hip", "lf_attn_device.h", "lf_attn_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "band_kernel_traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -49,6 +57,8 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--global-proj", action="store_true",
                     help="global rows use their own q/k/v projections (lf_attn_forward_global_proj)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (lf_attn_backward) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -159,6 +169,12 @@ def main():
         def step():
             binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle)
 
+    if args.backward:
+        if wl.dtype != "bf16":
+            print("bench.py: the backward runs on bf16 workloads only", file=sys.stderr)
+            sys.exit(2)
+        return bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops, handle)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -180,7 +196,7 @@ def main():
     torch.cuda.synchronize()
     st = handle.stage_times()
     handle.set_stage_timing(False)
-    stage_avg = {k2: v2[0] / max(1, v2[1]) for k2, v2 in st.items()}
+    stage_avg = {k2: v2[0] / v2[1] for k2, v2 in st.items() if v2[1]}
     k_avg_ms = stage_avg["band"]  # the dominant kernel
     achieved = flops / (k_avg_ms * 1e-3) / 1e12  # every attended pair but the merge's arithmetic
     traffic = None if args.global_proj else traffic_for(name)
@@ -225,6 +241,108 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, handle):
+    """Backward alone (inputs, forward output and log-sum-exp resident), then a whole
+    training step (forward with log-sum-exp + backward).  Effective FLOP: 2.5 x the
+    forward's (five products per attended pair instead of two)."""
+    import numpy as np
+    import torch
+
+    from sparse_long_sequence_longformer_amd import binding
+
+    g = np.random.default_rng(7).standard_normal(tuple(qd.shape), dtype=np.float32)
+    dod = torch.from_numpy(g).to(torch.bfloat16).to(qd.device)
+    out, lse = binding.forward_lse(qd, kd, vd, wl.w, dil, G, padd, handle=handle)
+    dq, dk, dv = binding.backward(qd, kd, vd, out, dod, lse, wl.w, dil, G, padd, handle=handle)
+    torch.cuda.synchronize()
+
+    # The timed loops call the C entry points with arguments marshalled once: the
+    # backward's four launches take less host time than the Python wrapper's checks.
+    import ctypes
+
+    lib = binding.load_library()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    dil_arr = (ctypes.c_int32 * len(dil))(*dil)
+    g_arr = (ctypes.c_int32 * max(1, len(G)))(*G)
+    stream = torch.cuda.current_stream().cuda_stream
+    pad_ptr = None if padd is None else padd.data_ptr()
+    shape = (wl.B, wl.H, wl.L, wl.d, wl.w, ctypes.cast(dil_arr, i32p), ctypes.cast(g_arr, i32p), len(G), pad_ptr,
+             stream)
+    bwd_args = (handle.handle, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), dod.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + shape
+    fwd_args = (handle.handle, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr()) + shape
+
+    def bwd():
+        if lib.lf_attn_backward(*bwd_args) != 0:
+            raise RuntimeError(lib.lf_attn_last_error(handle.handle).decode())
+
+    def train_step():
+        if lib.lf_attn_forward_lse(*fwd_args) != 0:
+            raise RuntimeError(lib.lf_attn_last_error(handle.handle).decode())
+        bwd()
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    ms_bwd = timed(bwd, args.steps)
+    ms_train = timed(train_step, args.steps)
+    handle.set_stage_timing(True)
+    for _ in range(args.steps):
+        bwd()
+    torch.cuda.synchronize()
+    st = handle.stage_times()
+    handle.set_stage_timing(False)
+    stage_avg = {k2: v2[0] / v2[1] for k2, v2 in st.items() if v2[1]}
+    flops_bwd = 2.5 * flops_fwd
+    # Products per attended pair: bwd_dq 3 (S, dP, dQ), bwd_dkv 4 (S, dP, dV, dK).
+    per_pair = {"bwd_dq": 3 * 2 * wl.d, "bwd_dkv": 4 * 2 * wl.d}
+    dom = max(per_pair, key=lambda k2: stage_avg.get(k2, 0.0))
+    achieved = per_pair[dom] * pairs.total / (stage_avg[dom] * 1e-3) / 1e12
+    value = flops_bwd / (ms_bwd * 1e-3) / 1e12
+    res = {
+        "metric": "window+global attn bwd effective TFLOP/s (2.5x forward FLOP), L=4096 w=512",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_bwd, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v/dO, no trained weights)",
+        "config": {"workload": name, "B": wl.B, "H": wl.H, "seq_len": wl.L, "d_h": wl.d, "w": wl.w,
+                   "dil": sorted(set(dil)), "n_global": len(G), "padded_lengths": list(wl.lengths) or None,
+                   "global_batch": wl.B, "parallelism": "single GPU"},
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "train_step_ms": round(ms_train, 6),
+        "train_step_tflops": round(3.5 * flops_fwd / (ms_train * 1e-3) / 1e12, 3),
+        "kernel_ms_avg": {k2: round(v2, 6) for k2, v2 in stage_avg.items()},
+        "roofline": {
+            "kernel": f"lf::{dom}_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(stage_avg[dom], 6),
+            "flop_per_launch": per_pair[dom] * pairs.total,
+        },
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -52,9 +52,13 @@ typedef enum lf_dtype {
 #define LF_HEAD_DIM 64
 
 /* Kernel launches timed by lf_attn_stage_times. */
-#define LF_N_STAGES 2
-#define LF_STAGE_BAND 0  /* window band, global-column fold, global-row partials */
-#define LF_STAGE_MERGE 1 /* log-sum-exp merge of the partials (only with globals) */
+#define LF_N_STAGES 6
+#define LF_STAGE_BAND 0      /* window band, global-column fold, global-row partials */
+#define LF_STAGE_MERGE 1     /* log-sum-exp merge of the partials (only with globals) */
+#define LF_STAGE_BWD_PREP 2  /* backward: D = rowsum(dO * O), base-2 log-sum-exp */
+#define LF_STAGE_BWD_DQ 3    /* backward: dQ (row-owned), global-row partials */
+#define LF_STAGE_BWD_DKV 4   /* backward: dK, dV (key-owned), global-key partials */
+#define LF_STAGE_BWD_MERGE 5 /* backward: sums of the global partials (only with globals) */
 
 typedef struct lf_attn_s* lf_attn_t;
 
@@ -97,6 +101,47 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
                           int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
                           const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
                           void* stream);
+
+/*
+ * lf_attn_forward that also writes each row's log-sum-exp, for the backward.
+ *
+ * lse : DEVICE float32 [B][H][L], 4-byte aligned, not overlapping q, k, v or out:
+ *       lse[b,h,i] = log sum_{j in keys(i)} exp(Q[b,h,i,:] . K[b,h,j,:] / sqrt(d_h))
+ *       (natural log), -inf for a row with no key.  It is the normaliser of the
+ *       row's softmax (page "Reformer哈希" §"core principle" formula).
+ * Everything else: as lf_attn_forward.  LF_ERR_INVALID_ARG if lse is NULL.
+ */
+lf_status lf_attn_forward_lse(lf_attn_t h, const void* q, const void* k, const void* v, void* out,
+                              float* lse, int B, int H, int L, int d_h, int w,
+                              const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                              const uint8_t* key_pad_mask, void* stream);
+
+/*
+ * Gradients of the forward: given dout = dL/dO, write dq, dk, dv = dL/dQ, dL/dK,
+ * dL/dV for the same pattern (window, globals, padding), from the textbook
+ * derivatives of O = softmax(S) V, S = Q K^T / sqrt(d_h) restricted to the key
+ * sets (page "Reformer哈希" §"core principle"; the pattern as above):
+ *
+ *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . V_j - dO_i . O_i),
+ *   dQ_i = sum_j dS_ij K_j / sqrt(d_h),   dK_j = sum_i dS_ij Q_i / sqrt(d_h).
+ *
+ * q, k, v, out, dout : DEVICE [B][H][L][d_h] bf16, 16-byte aligned; out and lse as
+ *                      written by lf_attn_forward_lse for the same q, k, v and
+ *                      pattern (P is recomputed from them).
+ * lse                : DEVICE float32 [B][H][L], 4-byte aligned.
+ * dq, dk, dv         : DEVICE [B][H][L][d_h] bf16 outputs, 16-byte aligned, not
+ *                      overlapping any input or each other.  Padded keys get
+ *                      dk = dv = 0; rows with no key get dq = 0.
+ * Other arguments: as lf_attn_forward.  bf16 handles only (LF_ERR_UNSUPPORTED for
+ * fp32).  The handle grows a second device workspace (hipMalloc) for row statistics
+ * and the partial sums of global rows and keys; calls on one handle must not overlap.
+ * The result is deterministic (fixed summation order, no atomics).
+ */
+lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                           const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
+                           void* stream);
 
 /*
  * The same forward with separate projections for the global rows.

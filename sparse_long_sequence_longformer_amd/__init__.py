@@ -10,11 +10,12 @@ first use and raises if it has not been built.
 
 from __future__ import annotations
 
-__all__ = ["forward", "forward_global_proj", "LfAttn", "LfAttnError", "library_path"]
+__all__ = ["forward", "forward_lse", "backward", "forward_global_proj", "LfAttn", "LfAttnError", "library_path"]
 
 
 def __getattr__(name):
-    if name in ("forward", "forward_global_proj", "LfAttn", "LfAttnError", "library_path", "load_library"):
+    if name in ("forward", "forward_lse", "backward", "forward_global_proj", "LfAttn", "LfAttnError",
+                "library_path", "load_library"):
         from . import binding
 
         return getattr(binding, name)

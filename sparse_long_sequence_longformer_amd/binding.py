@@ -17,8 +17,8 @@ LIBRARY_NAME = "liblfattn.so"
 LF_OK = 0
 LF_F32 = 0
 LF_BF16 = 1
-N_STAGES = 2
-STAGE_NAMES = ("band", "merge")
+N_STAGES = 6
+STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge")
 MAX_HEADS = 64
 MAX_GLOBALS = 256
 
@@ -27,6 +27,8 @@ EXPORTS = (
     "lf_attn_create",
     "lf_attn_forward",
     "lf_attn_forward_global_proj",
+    "lf_attn_forward_lse",
+    "lf_attn_backward",
     "lf_attn_destroy",
     "lf_attn_status_string",
     "lf_attn_last_error",
@@ -67,6 +69,14 @@ def load_library():
                                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                                 i32, vp, vp]
     lib.lf_attn_forward_global_proj.restype = i32
+    lib.lf_attn_forward_lse.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
+                                        vp, vp]
+    lib.lf_attn_forward_lse.restype = i32
+    lib.lf_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
+                                     vp, vp]
+    lib.lf_attn_backward.restype = i32
     lib.lf_attn_destroy.argtypes = [vp]
     lib.lf_attn_destroy.restype = i32
     lib.lf_attn_status_string.argtypes = [i32]
@@ -108,14 +118,24 @@ class LfAttn:
                     msg = f"{msg}: {detail}"
             raise LfAttnError(st, msg)
 
-    @staticmethod
-    def _host_arrays(dil, global_idx):
-        dil_arr, _ = _int32_array(dil)
-        g_arr, ng = _int32_array(global_idx if global_idx is not None else [])
+    _arrays_cache: dict = {}
+
+    @classmethod
+    def _host_arrays(cls, dil, global_idx):
+        """int32 host arrays of the dilations and globals (cached per distinct value)."""
+        key = (tuple(int(x) for x in dil), tuple(int(x) for x in global_idx) if global_idx is not None else ())
+        hit = cls._arrays_cache.get(key)
+        if hit is not None:
+            return hit
+        dil_arr, _ = _int32_array(key[0])
+        g_arr, ng = _int32_array(key[1])
         null = ctypes.POINTER(ctypes.c_int32)()
         dil_p = null if dil_arr is None else ctypes.cast(dil_arr, ctypes.POINTER(ctypes.c_int32))
         g_p = null if g_arr is None else ctypes.cast(g_arr, ctypes.POINTER(ctypes.c_int32))
-        return (dil_arr, g_arr), dil_p, g_p, ng
+        res = ((dil_arr, g_arr), dil_p, g_p, ng)
+        if len(cls._arrays_cache) < 64:
+            cls._arrays_cache[key] = res
+        return res
 
     def forward_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
@@ -128,6 +148,20 @@ class LfAttn:
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
         st = self.lib.lf_attn_forward_global_proj(self.handle, q_ptr, k_ptr, v_ptr, qg_ptr, kg_ptr, vg_ptr,
                                                   out_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def forward_lse_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr,
+                        stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_attn_forward_lse(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, L, d_h, w,
+                                          dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def backward_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, L, d_h,
+                     w, dil, global_idx, pad_ptr, stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_attn_backward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr,
+                                       dk_ptr, dv_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
     def set_stage_timing(self, enable: bool):
@@ -241,3 +275,51 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
                                   v_g.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil, global_idx,
                                   pad_ptr, stream)
     return out
+
+
+def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, lse=None,
+                handle: LfAttn | None = None):
+    """``forward`` that also returns each row's log-sum-exp: (out, lse), lse a float32
+    device tensor [B, H, L] (natural log, -inf for rows without keys)."""
+    import torch
+
+    B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
+    with torch.cuda.device(q.device):
+        h.forward_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, L, d_h,
+                          int(w), dil, global_idx, pad_ptr, stream)
+    return out, lse
+
+
+def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask=None, dq=None, dk=None,
+             dv=None, handle: LfAttn | None = None):
+    """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dout``.
+
+    q, k, v, out, dout: contiguous bf16 device tensors [B, H, L, 64]; ``out`` and
+    ``lse`` as returned by ``forward_lse`` for the same inputs and pattern.
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward supports bfloat16 tensors only")
+    B, H, L, d_h, dil, global_idx, pad_ptr, _, h, stream = _marshal(
+        q, [("k", k), ("v", v), ("out", out), ("dout", dout)], w, dil, global_idx, key_pad_mask, out, handle)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
+    res = []
+    for t in (dq, dk, dv):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("dq, dk, dv must be contiguous device tensors like q")
+        res.append(t)
+    dq, dk, dv = res
+    with torch.cuda.device(q.device):
+        h.backward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d_h, int(w), dil, global_idx, pad_ptr,
+                       stream)
+    return dq, dk, dv

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 
-SOURCES = ["lf_attn.cpp", "lf_attn_kernels.hip"]
+SOURCES = ["lf_attn.cpp", "lf_attn_kernels.hip", "lf_attn_bwd.hip"]
 ARCH = "gfx950"
 
 

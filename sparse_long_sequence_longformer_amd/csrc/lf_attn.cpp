@@ -29,15 +29,18 @@ struct TimedLaunch {
 struct lf_attn_s {
     lf_dtype dtype;
     int device = -1;
-    char* ws = nullptr;  // global-row partials
+    char* ws = nullptr;  // global-row partials of the forward
     size_t ws_bytes = 0;
     int ws_device = -1;
+    char* ws_bwd = nullptr;  // row statistics and global partials of the backward
+    size_t ws_bwd_bytes = 0;
+    int ws_bwd_device = -1;
     std::string last_error;
     bool timing = false;
     std::vector<TimedLaunch> pending;  // recorded, not yet read
     std::vector<hipEvent_t> event_pool;
-    double stage_ms[LF_N_STAGES] = {0, 0};
-    int64_t stage_n[LF_N_STAGES] = {0, 0};
+    double stage_ms[LF_N_STAGES] = {};
+    int64_t stage_n[LF_N_STAGES] = {};
 };
 
 namespace {
@@ -59,6 +62,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool overlaps(const void* a, const void* b, size_t n) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + n && y < x + n;
+}
+
+// [a, a + na) and [b, b + nb) intersect.
+bool overlaps2(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
 }
 
 hipEvent_t take_event(lf_attn_t h) {
@@ -112,6 +121,7 @@ lf_status lf_attn_destroy(lf_attn_t h) {
     if (!h) return LF_OK;
     lf_status st = LF_OK;
     if (h->ws && hipFree(h->ws) != hipSuccess) st = LF_ERR_HIP;
+    if (h->ws_bwd && hipFree(h->ws_bwd) != hipSuccess) st = LF_ERR_HIP;
     release_events(h);
     for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
     delete h;
@@ -153,18 +163,19 @@ lf_status lf_attn_stage_times(lf_attn_t h, double* ms, int64_t* launches) {
 
 namespace {
 
-// Both forward entry points.  qg, kg, vg are all null (one projection for every
-// row) or all non-null (separate projections of the global rows).
-lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
-                       const void* vg, void* out, int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
-                       const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask, void* stream) {
-    if (!h) return LF_ERR_INVALID_ARG;
-    h->last_error.clear();
-    if (!q || !k || !v || !out) return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be non-null");
-    const bool sep = qg || kg || vg;
-    if (sep && !(qg && kg && vg)) return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g and v_g must all be non-null");
-    if (sep && (!aligned16(qg) || !aligned16(kg) || !aligned16(vg)))
-        return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g and v_g must be 16-byte aligned");
+// Shape, pattern and plan shared by the forward and the backward: validated
+// arguments, sorted distinct globals, per-head residue tiling.
+struct Plan {
+    int B, H, L, w;
+    int dil[LF_MAX_HEADS];
+    std::vector<int> g;
+    int n_gblk;
+    int tiles;
+    size_t bytes;  // of one [B][H][L][d_h] tensor
+};
+
+lf_status make_plan(lf_attn_t h, Plan& pl, int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                    const int32_t* global_idx, int n_global) {
     if (B < 1 || H < 1 || L < 1) return fail(h, LF_ERR_INVALID_ARG, "need B, H, L >= 1 (got %d, %d, %d)", B, H, L);
     if (d_h != LF_HEAD_DIM) return fail(h, LF_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
     if (H > LF_MAX_HEADS) return fail(h, LF_ERR_UNSUPPORTED, "at most %d heads (got %d)", LF_MAX_HEADS, H);
@@ -174,31 +185,108 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     if (n_global > LF_MAX_GLOBALS)
         return fail(h, LF_ERR_UNSUPPORTED, "at most %d global indices (got %d)", LF_MAX_GLOBALS, n_global);
     if (n_global > 0 && !global_idx) return fail(h, LF_ERR_INVALID_ARG, "global_idx is NULL but n_global > 0");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
     const size_t elem = h->dtype == LF_BF16 ? 2 : 4;
     const uint64_t n_elem = static_cast<uint64_t>(B) * H * L * LF_HEAD_DIM;
     if (n_elem / LF_HEAD_DIM / L / H != static_cast<uint64_t>(B) || n_elem > (uint64_t(1) << 40))
         return fail(h, LF_ERR_INVALID_ARG, "tensor size overflows");
-    const size_t bytes = static_cast<size_t>(n_elem) * elem;
+    pl.bytes = static_cast<size_t>(n_elem) * elem;
+    for (int i = 0; i < H; ++i) {
+        if (dil_per_head[i] < 1) return fail(h, LF_ERR_INVALID_ARG, "dil_per_head[%d] = %d < 1", i, dil_per_head[i]);
+        pl.dil[i] = dil_per_head[i];
+    }
+    pl.g.assign(global_idx, global_idx + n_global);
+    for (int i = 0; i < n_global; ++i)
+        if (pl.g[i] < 0 || pl.g[i] >= L)
+            return fail(h, LF_ERR_INVALID_ARG, "global_idx[%d] = %d outside [0, %d)", i, pl.g[i], L);
+    std::sort(pl.g.begin(), pl.g.end());
+    pl.g.erase(std::unique(pl.g.begin(), pl.g.end()), pl.g.end());
+    pl.B = B;
+    pl.H = H;
+    pl.L = L;
+    pl.w = std::min(w, L);  // |j - i| < L always, so a wider window changes nothing
+    pl.n_gblk = (static_cast<int>(pl.g.size()) + lf::kGlobalQueriesPerBlock - 1) / lf::kGlobalQueriesPerBlock;
+    int tiles = 0;
+    for (int i = 0; i < H; ++i) {
+        const int d = pl.dil[i];
+        const int len0 = (L + d - 1) / d;  // rows of residue class 0 (the longest)
+        const int per_class = (len0 + lf::kRowsPerBlock - 1) / lf::kRowsPerBlock;
+        const int64_t t = static_cast<int64_t>(d) * per_class;
+        if (t > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
+        tiles = std::max<int>(tiles, static_cast<int>(t));
+    }
+    pl.tiles = tiles;
+    if (static_cast<int64_t>(B) * H * tiles > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
+    return LF_OK;
+}
+
+// Grow one of the handle's device workspaces to at least `need` bytes.
+lf_status reserve(lf_attn_t h, char** buf, size_t* have, int* dev, size_t need) {
+    if (need <= *have && *dev == h->device) return LF_OK;
+    if (*buf) (void)hipFree(*buf);
+    *buf = nullptr;
+    *have = 0;
+    if (hipMalloc(reinterpret_cast<void**>(buf), need) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(h, LF_ERR_OOM, "hipMalloc of %zu workspace bytes failed", need);
+    }
+    *have = need;
+    *dev = h->device;
+    return LF_OK;
+}
+
+// Enqueue one launch, between timing events when timing is on.
+template <class Launch>
+lf_status launch_stage(lf_attn_t h, int stage, hipStream_t s, Launch launch) {
+    TimedLaunch tl{nullptr, nullptr, stage};
+    if (h->timing) {
+        tl.start = take_event(h);
+        tl.stop = take_event(h);
+        if (!tl.start || !tl.stop) return fail(h, LF_ERR_HIP, "hipEventCreate failed");
+        if (hipEventRecord(tl.start, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    if (h->timing) {
+        if (hipEventRecord(tl.stop, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+        h->pending.push_back(tl);
+    }
+    return LF_OK;
+}
+
+// Every forward entry point.  qg, kg, vg are all null (one projection for every
+// row) or all non-null (separate projections of the global rows); lse may be null.
+lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
+                       const void* vg, void* out, float* lse, int B, int H, int L, int d_h, int w,
+                       const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                       const uint8_t* key_pad_mask, void* stream) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (!q || !k || !v || !out) return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+    const bool sep = qg || kg || vg;
+    if (sep && !(qg && kg && vg)) return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g and v_g must all be non-null");
+    if (sep && (!aligned16(qg) || !aligned16(kg) || !aligned16(vg)))
+        return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g and v_g must be 16-byte aligned");
+    Plan pl;
+    lf_status st = make_plan(h, pl, B, H, L, d_h, w, dil_per_head, global_idx, n_global);
+    if (st != LF_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    const size_t bytes = pl.bytes;
     if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
         return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q, k or v");
     if (sep && (overlaps(out, qg, bytes) || overlaps(out, kg, bytes) || overlaps(out, vg, bytes)))
         return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q_g, k_g or v_g");
+    if (lse) {
+        const size_t lb = static_cast<size_t>(B) * H * L * sizeof(float);
+        if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(h, LF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+        if (overlaps2(lse, lb, q, bytes) || overlaps2(lse, lb, k, bytes) || overlaps2(lse, lb, v, bytes) ||
+            overlaps2(lse, lb, out, bytes))
+            return fail(h, LF_ERR_INVALID_ARG, "lse must not overlap q, k, v or out");
+    }
 
     lf::Params p;
     std::memset(&p, 0, sizeof(p));
-    for (int i = 0; i < H; ++i) {
-        if (dil_per_head[i] < 1) return fail(h, LF_ERR_INVALID_ARG, "dil_per_head[%d] = %d < 1", i, dil_per_head[i]);
-        p.dil[i] = dil_per_head[i];
-    }
-    std::vector<int> g(global_idx, global_idx + n_global);
-    for (int i = 0; i < n_global; ++i)
-        if (g[i] < 0 || g[i] >= L)
-            return fail(h, LF_ERR_INVALID_ARG, "global_idx[%d] = %d outside [0, %d)", i, g[i], L);
-    std::sort(g.begin(), g.end());
-    g.erase(std::unique(g.begin(), g.end()), g.end());
-
+    std::copy(pl.dil, pl.dil + H, p.dil);
     p.q = q;
     p.k = k;
     p.v = v;
@@ -207,66 +295,114 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     p.kg = kg;
     p.vg = vg;
     p.pad = key_pad_mask;
+    p.lse = lse;
     p.B = B;
     p.H = H;
     p.L = L;
-    p.w = std::min(w, L);  // |j - i| < L always, so a wider window changes nothing
-    p.n_g = static_cast<int>(g.size());
-    std::copy(g.begin(), g.end(), p.g);
-    p.n_gblk = (p.n_g + lf::kGlobalQueriesPerBlock - 1) / lf::kGlobalQueriesPerBlock;
+    p.w = pl.w;
+    p.n_g = static_cast<int>(pl.g.size());
+    std::copy(pl.g.begin(), pl.g.end(), p.g);
+    p.n_gblk = pl.n_gblk;
     p.rows_per_block = lf::kRowsPerBlock;
-    int tiles = 0;
-    for (int i = 0; i < H; ++i) {
-        const int d = p.dil[i];
-        const int len0 = (L + d - 1) / d;  // rows of residue class 0 (the longest)
-        const int per_class = (len0 + p.rows_per_block - 1) / p.rows_per_block;
-        const int64_t t = static_cast<int64_t>(d) * per_class;
-        if (t > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
-        tiles = std::max<int>(tiles, static_cast<int>(t));
-    }
-    p.tiles_per_head = tiles;
-    if (static_cast<int64_t>(B) * H * tiles > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "grid too large");
+    p.tiles_per_head = pl.tiles;
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
     if (p.n_g > 0) {
-        const size_t n_part = static_cast<size_t>(B) * H * tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
-        const size_t need = n_part * (2 + 64) * sizeof(float);
-        if (need > h->ws_bytes || h->ws_device != h->device) {
-            if (h->ws) (void)hipFree(h->ws);
-            h->ws = nullptr;
-            h->ws_bytes = 0;
-            if (hipMalloc(reinterpret_cast<void**>(&h->ws), need) != hipSuccess) {
-                (void)hipGetLastError();
-                return fail(h, LF_ERR_OOM, "hipMalloc of %zu workspace bytes failed", need);
-            }
-            h->ws_bytes = need;
-            h->ws_device = h->device;
-        }
+        const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
+        st = reserve(h, &h->ws, &h->ws_bytes, &h->ws_device, n_part * (2 + 64) * sizeof(float));
+        if (st != LF_OK) return st;
         p.ws_ml = reinterpret_cast<float*>(h->ws);
         p.ws_acc = p.ws_ml + n_part * 2;
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    using Launcher = hipError_t (*)(const lf::Params&, int, hipStream_t);
-    const Launcher stages[LF_N_STAGES] = {lf::launch_band, lf::launch_merge};
-    for (int i = 0; i < LF_N_STAGES; ++i) {
-        if (i == LF_STAGE_MERGE && p.n_g == 0) break;
-        TimedLaunch tl{nullptr, nullptr, i};
-        if (h->timing) {
-            tl.start = take_event(h);
-            tl.stop = take_event(h);
-            if (!tl.start || !tl.stop) return fail(h, LF_ERR_HIP, "hipEventCreate failed");
-            if (hipEventRecord(tl.start, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
-        }
-        const hipError_t e = stages[i](p, h->dtype, s);
-        if (e != hipSuccess) return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-        if (h->timing) {
-            if (hipEventRecord(tl.stop, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
-            h->pending.push_back(tl);
-        }
+    const int dt = h->dtype;
+    st = launch_stage(h, LF_STAGE_BAND, s, [&] { return lf::launch_band(p, dt, s); });
+    if (st != LF_OK || p.n_g == 0) return st;
+    return launch_stage(h, LF_STAGE_MERGE, s, [&] { return lf::launch_merge(p, dt, s); });
+}
+
+lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int L, int d_h, int w,
+                        const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                        const uint8_t* key_pad_mask, void* stream) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+        return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-null");
+    if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the backward supports bf16 handles only");
+    Plan pl;
+    lf_status st = make_plan(h, pl, B, H, L, d_h, w, dil_per_head, global_idx, n_global);
+    if (st != LF_OK) return st;
+    const void* ins[] = {q, k, v, out, dout};
+    void* outs[] = {dq, dk, dv};
+    for (const void* x : ins)
+        if (!aligned16(x)) return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out and dout must be 16-byte aligned");
+    for (const void* x : outs)
+        if (!aligned16(x)) return fail(h, LF_ERR_INVALID_ARG, "dq, dk and dv must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(h, LF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const size_t bytes = pl.bytes;
+    const size_t lb = static_cast<size_t>(B) * H * L * sizeof(float);
+    for (int i = 0; i < 3; ++i) {
+        for (const void* x : ins)
+            if (overlaps(outs[i], x, bytes)) return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv must not overlap the inputs");
+        if (overlaps2(outs[i], bytes, lse, lb))
+            return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv must not overlap the inputs");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outs[j], bytes)) return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv must not overlap");
     }
-    return LF_OK;
+
+    lf::BwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    std::copy(pl.dil, pl.dil + H, p.dil);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.pad = key_pad_mask;
+    p.lse = lse;
+    p.B = B;
+    p.H = H;
+    p.L = L;
+    p.w = pl.w;
+    p.n_g = static_cast<int>(pl.g.size());
+    std::copy(pl.g.begin(), pl.g.end(), p.g);
+    p.n_gblk = pl.n_gblk;
+    p.tiles_per_head = pl.tiles;
+
+    // Workspace: three row-statistic arrays, then the global partials.
+    if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
+    const size_t rows = static_cast<size_t>(B) * H * L;
+    const size_t ngq = static_cast<size_t>(p.n_gblk) * lf::kGlobalQueriesPerBlock;
+    const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * ngq * 64;
+    const size_t n_own = static_cast<size_t>(B) * H * ngq * 64;
+    const size_t rows_al = (rows + 63) & ~size_t(63);
+    st = reserve(h, &h->ws_bwd, &h->ws_bwd_bytes, &h->ws_bwd_device,
+                 (3 * rows_al + 3 * n_part + 2 * n_own) * sizeof(float));
+    if (st != LF_OK) return st;
+    float* f = reinterpret_cast<float*>(h->ws_bwd);
+    p.lse2 = f;
+    p.lse2_band = f + rows_al;
+    p.dsum = f + 2 * rows_al;
+    f += 3 * rows_al;
+    p.ws_dq = f;
+    p.ws_dk = f + n_part;
+    p.ws_dv = f + 2 * n_part;
+    p.ws_dkg = f + 3 * n_part;
+    p.ws_dvg = f + 3 * n_part + n_own;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launch_stage(h, LF_STAGE_BWD_PREP, s, [&] { return lf::launch_bwd_prep(p, s); });
+    if (st == LF_OK) st = launch_stage(h, LF_STAGE_BWD_DQ, s, [&] { return lf::launch_bwd_dq(p, s); });
+    if (st == LF_OK) st = launch_stage(h, LF_STAGE_BWD_DKV, s, [&] { return lf::launch_bwd_dkv(p, s); });
+    if (st == LF_OK && p.n_g > 0)
+        st = launch_stage(h, LF_STAGE_BWD_MERGE, s, [&] { return lf::launch_bwd_merge(p, s); });
+    return st;
 }
 
 }  // namespace
@@ -276,7 +412,18 @@ extern "C" {
 lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void* v, void* out, int B, int H,
                           int L, int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx,
                           int n_global, const uint8_t* key_pad_mask, void* stream) {
-    return forward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, B, H, L, d_h, w, dil_per_head, global_idx,
+    return forward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, nullptr, B, H, L, d_h, w, dil_per_head,
+                        global_idx, n_global, key_pad_mask, stream);
+}
+
+lf_status lf_attn_forward_lse(lf_attn_t h, const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                              const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask, void* stream) {
+    if (h && !lse) {
+        h->last_error = "lse must be non-null";
+        return LF_ERR_INVALID_ARG;
+    }
+    return forward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, lse, B, H, L, d_h, w, dil_per_head, global_idx,
                         n_global, key_pad_mask, stream);
 }
 
@@ -288,8 +435,16 @@ lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k,
         h->last_error = "q_g, k_g and v_g must be non-null";
         return LF_ERR_INVALID_ARG;
     }
-    return forward_impl(h, q, k, v, q_g, k_g, v_g, out, B, H, L, d_h, w, dil_per_head, global_idx, n_global,
-                        key_pad_mask, stream);
+    return forward_impl(h, q, k, v, q_g, k_g, v_g, out, nullptr, B, H, L, d_h, w, dil_per_head, global_idx,
+                        n_global, key_pad_mask, stream);
+}
+
+lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int H, int L,
+                           int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                           const uint8_t* key_pad_mask, void* stream) {
+    return backward_impl(h, q, k, v, out, dout, lse, dq, dk, dv, B, H, L, d_h, w, dil_per_head, global_idx,
+                         n_global, key_pad_mask, stream);
 }
 
 }  // extern "C"

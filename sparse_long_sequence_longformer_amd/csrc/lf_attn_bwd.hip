@@ -1,0 +1,770 @@
+// gfx950 (MI355X) kernels of the Longformer window + global attention backward
+// (bf16 tensors, fp32 accumulation).
+//
+// For O = P V with P the row softmax of S = Q K^T / sqrt(d_h) over each row's key
+// set (the forward's pattern: page "基于自注意力机制的长文本建模算法：Longformer详解"
+// §2 and §4, page "基于Block-Sparse Attention的Longformer" §2 and §4), and an
+// upstream gradient dO, the textbook derivatives of the product and the softmax
+// (page "Reformer哈希" §"core principle" formula) are
+//
+//   D_i = dO_i . O_i,   dS_ij = P_ij (dO_i . V_j - D_i),
+//   dQ_i = sum_j dS_ij K_j / sqrt(d_h),   dK_j = sum_i dS_ij Q_i / sqrt(d_h),
+//   dV_j = sum_i P_ij dO_i,
+//
+// with P recomputed from the forward's per-row log-sum-exp (no softmax statistics
+// are rebuilt).  The attended pairs (i, j) are split so that every gradient visits
+// each pair exactly once:
+//   A  i not global, j in the window of i (a global j included);
+//   B  i not global, j global outside the window of i;
+//   C  i global, every unpadded j.
+//
+// bwd_prep_kernel  D, and the log-sum-exp in base-2 units of the pre-scaled scores
+//                  (lse2; lse2_band is +inf on global rows, which removes them from
+//                  the window passes of the key-owned kernel).
+// bwd_dq_kernel    row-owned, the forward's traversal (global key stages, then the
+//                  window band): dQ of every non-global row over A and B; for the
+//                  global rows (C), one partial per (tile, global query) over the
+//                  tile's 128 home keys.
+// bwd_dkv_kernel   key-owned, the same traversal with the roles of rows and keys
+//                  exchanged (global query stages, then the band of window queries):
+//                  dK, dV of every key over A and C; for global keys, one partial per
+//                  (tile, global key) over the tile's home queries in B.
+// bwd_merge_kernel sums the partials of each global row and key in tile order and
+//                  writes dQ of the global rows and dK, dV of the global keys.
+//
+// Every product is a 32 x 32 tile on the matrix cores (v_mfma_f32_32x32x16_bf16).
+// Row-owned: S^T = K Q^T and dP^T = V dO^T with one query per lane, dQ^T += K^T dS^T.
+// Key-owned: S = Q K^T and dP = dO V^T with one key per lane, dV^T += dO^T P and
+// dK^T += Q^T dS.  The staged tiles (K and V, or Q and dO) are row-major in LDS with
+// the 16-byte-chunk XOR swizzle and are read both ways: 128-bit row reads for the
+// first operand of the score products and transposed reads (ds_read_b64_tr_b16) for
+// the first operand of the gradient products.
+
+#include "lf_attn_device.h"
+
+namespace lf {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kPosInf = __builtin_inff();
+constexpr int kBwdMaskWindow = 64;
+constexpr int kBwdMaskRing = 2 * kBwdMaskWindow;
+constexpr int kBwdMaxGlobalStages = LF_MAX_GLOBALS / kStageKeys;
+
+// One stage: tile A (64 rows x 128 B), tile B (same), 64 floats of lse2, 64 of D.
+constexpr int kRowB = 128;
+constexpr int kTileB = kStageKeys * kRowB;  // 8 KiB
+constexpr int kLseOff = 2 * kTileB;
+constexpr int kDOff = kLseOff + 256;
+constexpr int kStageB = kDOff + 256;
+
+struct Op { bf16x8 v[4]; };      // B operand of a score product: lane (n, h2) holds d = 16*kb + 8*h2 + j
+struct Frag { bf16x8 v[2]; };    // B operand of a gradient product (weights or dS)
+struct TOp { bf16x8 v[2][2]; };  // transposed A operand [db][kb]
+
+__device__ __forceinline__ void load_op(Op& o, const uint16_t* row, int h2) {
+    if (!row) row = reinterpret_cast<const uint16_t*>(g_zero_row);
+    for (int kb = 0; kb < 4; ++kb)
+        o.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
+}
+__device__ __forceinline__ void scale_op(Op& o) {
+    for (int kb = 0; kb < 4; ++kb) {
+        const f32x8 f = __builtin_convertvector(o.v[kb], f32x8);
+        o.v[kb] = __builtin_convertvector(f * kScaleLog2, bf16x8);
+    }
+}
+
+// 4 bytes per lane from global memory into LDS at lds_base + 4 * lane (see dma16).
+__device__ __forceinline__ void dma4(const void* src, char* lds_base) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory", "m0");
+}
+
+// Rows of two tensors into tiles A and B of a stage, both with the K swizzle: wave
+// wv copies 1-KiB blocks 2*wv, 2*wv+1 (8 rows each).  row_of(kk) is the source row
+// of stage row kk, or -1 for a zero row.
+template <class RowOf>
+__device__ __forceinline__ void dma_tiles(char* slot, const uint16_t* A, const uint16_t* Bt, RowOf row_of, int wv,
+                                          int lane) {
+    const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
+    for (int u = 0; u < 2; ++u) {
+        const int blk = 2 * wv + u;
+        const int row = 8 * blk + (lane >> 3), cl = lane & 7;
+        const int src = row_of(row);
+        const int c = 8 * (cl ^ swz_k(row));
+        dma16((src >= 0 ? A + (size_t)src * 64 : zero) + c, slot + blk * 1024);
+        dma16((src >= 0 ? Bt + (size_t)src * 64 : zero) + c, slot + kTileB + blk * 1024);
+    }
+}
+// lse2 and D of the 64 stage rows (one wave; zero for row -1).
+template <class RowOf>
+__device__ __forceinline__ void dma_floats(char* slot, const float* lse2, const float* dsum, RowOf row_of, int lane) {
+    const int src = row_of(lane);
+    const float* zero = reinterpret_cast<const float*>(g_zero_row);
+    dma4(src >= 0 ? lse2 + src : zero, slot + kLseOff);
+    dma4(src >= 0 ? dsum + src : zero, slot + kDOff);
+}
+
+// Per-lane LDS byte offsets.  nk: 128-bit row reads (row sigma(M), chunk
+// (2*kb + h2) ^ swz_k(row)).  tr: transposed reads; within each 16-lane group, lane i
+// addresses row 8*h2 + i/4 (+ 4*t + 16*kb + 32*sub), columns 32*db + 16*g1 + 4*(i%4)
+// .. +3, and receives one column of four consecutive rows.  Rows 8*h2 + i/4 have bit
+// 2 clear, so adding 4 (t = 1) keeps swz_k; multiples of 16 keep it as well.
+struct Lanes { int nk[4]; int tr[2]; };
+__device__ __forceinline__ void lane_setup(Lanes& lo, int lane) {
+    const int row = sigma(lane & 31), h2 = lane >> 5;
+    for (int kb = 0; kb < 4; ++kb) lo.nk[kb] = row * kRowB + (((2 * kb + h2) ^ swz_k(row)) << 4);
+    const int g1 = (lane >> 4) & 1, i = lane & 15;
+    const int vrow = 8 * h2 + (i >> 2);
+    for (int db = 0; db < 2; ++db) {
+        const int chunk = 4 * db + 2 * g1 + ((i & 3) >> 1);
+        lo.tr[db] = vrow * kRowB + ((chunk ^ swz_k(vrow)) << 4) + 8 * (i & 1);
+    }
+}
+
+// seed + (rows 32*sub .. +31 of the tile) x (lane operand): element i of lane-half h2
+// belongs to tile row 32*sub + key_local(i, h2).
+__device__ __forceinline__ f32x16 prod(const char* tile, int sub, const Lanes& lo, const Op& b, const f32x16& seed) {
+    const char* base = tile + sub * 32 * kRowB;
+    f32x16 acc = seed;
+    for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + lo.nk[kb]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.v[kb], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ void to_frag(const float* x, Frag& f) {
+    for (int kb = 0; kb < 2; ++kb) {
+        f32x8 t;
+        for (int j = 0; j < 8; ++j) t[j] = x[8 * kb + j];
+        f.v[kb] = __builtin_convertvector(t, bf16x8);
+    }
+}
+
+// Transposed operand of rows 32*sub .. +31 of a tile: lane l holds column 32*db + l%32
+// of rows 16*kb + 8*h2 + 0..7.
+__device__ __forceinline__ void load_t(TOp& t, const char* tile, int sub, const Lanes& lo) {
+    const char* base = tile + sub * 32 * kRowB;
+    for (int db = 0; db < 2; ++db)
+        for (int kb = 0; kb < 2; ++kb) {
+            const char* a = base + lo.tr[db] + 16 * kb * kRowB;
+            const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a));
+            const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a + 4 * kRowB));
+            t.v[db][kb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+}
+__device__ __forceinline__ void acc_t(const TOp& t, const Frag& f, f32x16* acc) {
+    for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < 2; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.v[db][kb], f.v[kb], acc[db], 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// Accumulator element (db, i) of lane-half h2 is column 32*db + 8*(i/4) + 4*h2 + i%4.
+__device__ __forceinline__ void store_row(uint16_t* row, int h2, const f32x16* o, float scale) {
+    for (int db = 0; db < 2; ++db)
+        for (int q = 0; q < 4; ++q) {
+            const float a = o[db][4 * q] * scale, b = o[db][4 * q + 1] * scale;
+            const float c = o[db][4 * q + 2] * scale, d = o[db][4 * q + 3] * scale;
+            const u32x2 w = {pack_bf16(a, b), pack_bf16(c, d)};
+            *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * h2) = w;
+        }
+}
+__device__ __forceinline__ void store_row_f32(float* row, int h2, const f32x16* o, float scale) {
+    for (int db = 0; db < 2; ++db)
+        for (int q = 0; q < 4; ++q) {
+            f32x4 t;
+            for (int j = 0; j < 4; ++j) t[j] = o[db][4 * q + j] * scale;
+            *reinterpret_cast<f32x4*>(row + 32 * db + 8 * q + 4 * h2) = t;
+        }
+}
+
+// Per-element seeds of a key-owned product: minus the staged floats of the 16 rows
+// the lane's elements belong to (rows 32*sub + key_local(i, h2)).
+__device__ __forceinline__ f32x16 row_seed(const char* arr, int sub, int h2) {
+    const f32x4* a = reinterpret_cast<const f32x4*>(arr) + 8 * sub + 2 * h2;
+    const f32x4 x0 = a[0], x1 = a[1], x2 = a[4], x3 = a[5];
+    f32x16 s;
+    for (int j = 0; j < 4; ++j) {
+        s[j] = -x0[j];
+        s[4 + j] = -x1[j];
+        s[8 + j] = -x2[j];
+        s[12 + j] = -x3[j];
+    }
+    return s;
+}
+
+__device__ __forceinline__ f32x16 splat(float x) {
+    f32x16 s;
+    for (int i = 0; i < 16; ++i) s[i] = x;
+    return s;
+}
+
+// Cross-wave sum of a 32 x 64 block per wave (lane-half h2 of lane (q, h2) holds
+// accumulator columns as in store_row), written as fp32 rows dst + q*64 for q < nq.
+// Uses red (32 KiB of LDS); the caller brackets it with barriers.
+__device__ __forceinline__ void wave_sum_store(float* red, const f32x16* a, int wv, int lane, int tid, float* dst,
+                                               int nq) {
+    const int q0 = lane & 31, h2 = lane >> 5;
+    for (int db = 0; db < 2; ++db)
+        for (int i = 0; i < 16; ++i) {
+            const int c = 32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3);
+            red[(wv * 32 + q0) * 64 + (c ^ q0)] = a[db][i];
+        }
+    __syncthreads();
+    const int q = tid >> 3, dc = tid & 7;  // 32 rows x 8 column chunks
+    if (q < nq) {
+        f32x4 o4[2];
+        for (int j = 0; j < 8; ++j) {
+            float o = 0.f;
+            for (int x = 0; x < kWaves; ++x) o += red[(x * 32 + q) * 64 + ((8 * dc + j) ^ q)];
+            o4[j >> 2][j & 3] = o;
+        }
+        *reinterpret_cast<f32x4*>(dst + (size_t)q * 64 + 8 * dc) = o4[0];
+        *reinterpret_cast<f32x4*>(dst + (size_t)q * 64 + 8 * dc + 4) = o4[1];
+    }
+    __syncthreads();
+}
+
+// The work-group's tile: 128 own rows [r0, r0 + 128) of residue class r of one
+// (b, h), and the other side's rows [kb0, kend) of the same class (everything within
+// w of an own row) in 64-row stages on a grid aligned to r0: nb stages before the
+// own rows, the two "home" stages [r0, r0 + 128), na stages after, processed in the
+// order before, after, home.
+struct Tile {
+    int bh, b, h, t_in, r, dil, Lr, r0, kb0, kend, nb, na, n_band, gbase;
+    __device__ int stage_row(int u) const {
+        const int bs = u < nb ? u : (u < nb + na ? u + 2 : u - na);
+        return gbase + kStageKeys * bs;
+    }
+};
+__device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p) {
+    const int pid = xcd_remap(blockIdx.x, gridDim.x);
+    t.bh = pid / p.tiles_per_head;
+    t.t_in = pid - t.bh * p.tiles_per_head;
+    t.h = t.bh % p.H;
+    t.b = t.bh / p.H;
+    t.dil = p.dil[t.h];
+    const int tpr = ((p.L + t.dil - 1) / t.dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    t.r = t.t_in / tpr;
+    if (t.r >= t.dil) return false;
+    t.Lr = (p.L - t.r + t.dil - 1) / t.dil;
+    t.r0 = (t.t_in - t.r * tpr) * kRowsPerBlock;
+    if (t.r0 >= t.Lr) return false;
+    t.kb0 = max(0, t.r0 - p.w);
+    t.kend = min(t.Lr, t.r0 + kRowsPerBlock + p.w);
+    t.nb = (t.r0 - t.kb0 + kStageKeys - 1) / kStageKeys;
+    t.gbase = t.r0 - kStageKeys * t.nb;
+    t.na = max(0, (t.kend - (t.r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
+    t.n_band = t.nb + 2 + t.na;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics: D, lse2, lse2_band.  One thread per (b, h, row).
+
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
+    const size_t n = (size_t)p.B * p.H * p.L;
+    const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const int pos = (int)(i % (size_t)p.L);
+    const u32x4* o = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + i * 64);
+    const u32x4* g = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + i * 64);
+    float acc = 0.f;
+    for (int c = 0; c < 8; ++c) {
+        const f32x8 a = __builtin_convertvector(__builtin_bit_cast(bf16x8, o[c]), f32x8);
+        const f32x8 b = __builtin_convertvector(__builtin_bit_cast(bf16x8, g[c]), f32x8);
+        for (int j = 0; j < 8; ++j) acc += a[j] * b[j];
+    }
+    const float lse = p.lse[i];
+    const float l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
+    int lo = 0, hi = p.n_g;  // binary search of the sorted global positions
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p.g[mid] < pos) lo = mid + 1;
+        else hi = mid;
+    }
+    const bool is_g = lo < p.n_g && p.g[lo] == pos;
+    p.dsum[i] = acc;
+    p.lse2[i] = l2;
+    p.lse2_band[i] = is_g ? kPosInf : l2;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one work-group per 128 rows of one residue class of one (b, h); wave wv owns
+// rows r0 + 32*wv .. +31, one per lane (both lane halves).  Stages: the global keys
+// (with the in-window test, so each key counts once), then the window band.
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(const BwdParams p) {
+    __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
+    __shared__ uint64_t band_mask[kBwdMaskRing];
+    __shared__ uint64_t glob_mask[kBwdMaxGlobalStages];
+    __shared__ int glob_src[LF_MAX_GLOBALS];
+    __shared__ __attribute__((aligned(16))) int glob_pos[LF_MAX_GLOBALS];
+    __shared__ int glob_row[LF_MAX_GLOBALS];
+    __shared__ uint32_t row_glob[kRowsPerBlock / 32];
+
+    Tile tl;
+    if (!tile_of(tl, p)) return;
+    const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
+    const size_t off = (size_t)tl.bh * L * 64;
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + off;
+    const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + off;
+    const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + off;
+    const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dout) + off;
+    uint16_t* dQ = reinterpret_cast<uint16_t*>(p.dq) + off;
+    const float* lse2 = p.lse2 + (size_t)tl.bh * L;
+    const float* dsum = p.dsum + (size_t)tl.bh * L;
+    const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
+
+    const int qa = r0 + 32 * wv, qv = qa + (lane & 31);
+    const bool rows_live = qa < Lr;
+    const int row = r + qv * dil;
+    Op qop, dop;
+    load_op(qop, qv < Lr ? Q + (size_t)row * 64 : nullptr, h2);
+    load_op(dop, qv < Lr ? dO + (size_t)row * 64 : nullptr, h2);
+    const float my_l2 = qv < Lr ? lse2[row] : kPosInf;
+    const float my_d = qv < Lr ? dsum[row] : 0.f;
+
+    const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
+    const int n_st = n_gst + tl.n_band;
+    auto band_invalid = [&](int u) -> uint64_t {
+        if (pad) return band_mask[u % kBwdMaskRing];
+        const int ks = tl.stage_row(u);
+        const int lo = tl.kb0 - ks, hi = tl.kend - ks;
+        uint64_t m = 0;
+        if (lo > 0) m |= lo >= 64 ? ~0ull : ((1ull << lo) - 1);
+        if (hi < 64) m |= hi <= 0 ? ~0ull : (~0ull << hi);
+        return m;
+    };
+    auto issue = [&](int s) {
+        char* slot = ring + (s & 1) * kStageB;
+        if (s < n_gst) {
+            const int* src = glob_src + kStageKeys * s;
+            dma_tiles(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane);
+        } else {
+            const int u = s - n_gst;
+            const uint64_t inv = uniform64(band_invalid(u));
+            const int ks = tl.stage_row(u);
+            dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
+        }
+    };
+    // Invalid-key bits (outside [kb0, kend) or padded) of band stages
+    // [64*W, 64*W + 64): wave wv builds words wv, wv + 4, ... (all loads first).
+    auto fill_band_masks = [&](int W) {
+        constexpr int kPer = kBwdMaskWindow / kWaves;
+        uint32_t flag[kPer];
+        for (int j = 0; j < kPer; ++j) {
+            const int u = W * kBwdMaskWindow + wv + kWaves * j;
+            const int key = u < tl.n_band ? tl.stage_row(u) + lane : -1;
+            flag[j] = (key >= tl.kb0 && key < tl.kend) ? pad[r + key * dil] : 1u;
+        }
+        for (int j = 0; j < kPer; ++j) {
+            const int u = W * kBwdMaskWindow + wv + kWaves * j;
+            const uint64_t inv = ballot64(flag[j] != 0);
+            if (lane == 0 && u < tl.n_band) band_mask[u % kBwdMaskRing] = inv;
+        }
+    };
+
+    for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
+        const int g = gi < p.n_g ? p.g[gi] : -1;
+        const bool ok = g >= 0 && (!pad || pad[g] == 0);
+        const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
+        glob_src[gi] = ok ? g : -1;
+        glob_pos[gi] = ok ? vpos : kNoPos;
+        glob_row[gi] = vpos;
+    }
+    if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
+    if (pad) fill_band_masks(0);
+    __syncthreads();
+    if (wv == 0)
+        for (int s = 0; s < n_gst; ++s) {
+            const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
+            if (lane == 0) glob_mask[s] = inv;
+        }
+    for (int gi = tid; gi < p.n_g; gi += kThreads) {
+        const int vr = glob_row[gi] - r0;
+        if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
+    }
+    __syncthreads();
+
+    Lanes lo;
+    lane_setup(lo, lane);
+    if (n_st > 0) issue(0);
+    wait_vmcnt<0>();
+    scale_op(qop);
+    const f32x16 seed_s = splat(-my_l2), seed_d = splat(-my_d);
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    for (int t = 0; t < n_st; ++t) {
+        wait_vmcnt<0>();
+        barrier_nofence();
+        if (t + 1 < n_st) {
+            const int bn = t + 1 - n_gst;
+            if (pad && bn > 0 && bn % kBwdMaskWindow == 0) {
+                fill_band_masks(bn / kBwdMaskWindow);
+                __syncthreads();
+            }
+            issue(t + 1);
+        }
+        const bool gstage = t < n_gst;
+        const int ks = gstage ? 0 : tl.stage_row(t - n_gst);
+        const uint64_t inv = uniform64(gstage ? glob_mask[t] : band_invalid(t - n_gst));
+        const char* slot = ring + (t & 1) * kStageB;
+        if (!rows_live || inv == ~0ull) continue;
+        for (int sub = 0; sub < 2; ++sub) {
+            const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
+            const int kss = ks + 32 * sub;
+            if (inv32 == ~0u) continue;
+            if (!gstage && (kss > qa + 31 + w || kss + 31 < qa - w)) continue;
+            const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + w;
+            const int mode = gstage ? 2 : (interior ? 0 : 1);
+            f32x16 s = prod(slot, sub, lo, qop, seed_s);  // scores - lse, base 2
+            mask_scores(s, mode, inv32, h2, kss + 8 * h2 - qv + w, w, glob_pos + kStageKeys * t + 32 * sub + 8 * h2,
+                        w - qv);
+            const f32x16 dp = prod(slot + kTileB, sub, lo, dop, seed_d);  // dO.V - D
+            float ds[16];
+            for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
+            Frag f;
+            to_frag(ds, f);
+            TOp tk;
+            load_t(tk, slot, sub, lo);
+            acc_t(tk, f, acc);
+        }
+    }
+    if (qv < Lr) {
+        const int vr = qv - r0;  // global rows: the merge
+        if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) store_row(dQ + (size_t)row * 64, h2, acc, 0.125f);
+    }
+    if (p.n_g == 0) return;
+
+    // Global rows (C): each wave takes one 32-key sub-tile of the home keys
+    // [r0, r0 + 128) (the last two band stages, still in the ring for the first 32
+    // global queries; copied again for the others).
+    const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
+    const size_t part0 = ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * ngq;
+    const int hs = wv >> 1, hsub = wv & 1;
+    const int home_end = min(Lr, r0 + kRowsPerBlock);
+    for (int gb = 0; gb < p.n_gblk; ++gb) {
+        const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
+        const int g = gq < p.n_g ? p.g[gq] : -1;
+        Op gop, gdo;
+        load_op(gop, g >= 0 ? Q + (size_t)g * 64 : nullptr, h2);
+        load_op(gdo, g >= 0 ? dO + (size_t)g * 64 : nullptr, h2);
+        const float gl = g >= 0 ? lse2[g] : kPosInf;
+        const float gd = g >= 0 ? dsum[g] : 0.f;
+        const char* hslot;
+        uint32_t inv32;
+        if (gb == 0) {
+            const int u = tl.n_band - 2 + hs;
+            hslot = ring + ((n_gst + u) & 1) * kStageB;
+            inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
+            wait_vmcnt<0>();
+        } else {
+            uint64_t hinv[2];
+            for (int j = 0; j < 2; ++j) {
+                const int key = r0 + kStageKeys * j + lane;
+                bool ok = key < home_end;
+                if (ok && pad) ok = pad[r + key * dil] == 0;
+                hinv[j] = uniform64(~ballot64(ok));
+            }
+            __syncthreads();  // the ring is free
+            for (int j = 0; j < 2; ++j) {
+                const uint64_t iv = hinv[j];
+                const int ks = r0 + kStageKeys * j;
+                dma_tiles(ring + j * kStageB, K, V, [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
+                          wv, lane);
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            hslot = ring + hs * kStageB;
+            inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * hsub));
+        }
+        scale_op(gop);
+        f32x16 gacc[2] = {f32x16{}, f32x16{}};
+        if (inv32 != ~0u) {
+            f32x16 s = prod(hslot, hsub, lo, gop, splat(-gl));
+            mask_scores(s, inv32 != 0u ? 1 : 0, inv32, h2, 0, kLargeW, nullptr, 0);
+            const f32x16 dp = prod(hslot + kTileB, hsub, lo, gdo, splat(-gd));
+            float ds[16];
+            for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
+            Frag f;
+            to_frag(ds, f);
+            TOp tk;
+            load_t(tk, hslot, hsub, lo);
+            acc_t(tk, f, gacc);
+        }
+        __syncthreads();  // done with the staged keys: the ring holds the reduction
+        const int nq = min(kGlobalQueriesPerBlock, p.n_g - gb * kGlobalQueriesPerBlock);
+        wave_sum_store(reinterpret_cast<float*>(ring), gacc, wv, lane, tid,
+                       p.ws_dq + (part0 + (size_t)gb * kGlobalQueriesPerBlock) * 64, nq);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one work-group per 128 keys of one residue class of one (b, h); wave wv
+// owns keys r0 + 32*wv .. +31, one per lane.  Stages: the global queries (every
+// unpadded key is theirs), then the window band of queries (global queries are
+// removed there by lse2_band = +inf: their weights are 0).
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkv_kernel(const BwdParams p) {
+    __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
+    __shared__ int own_gidx[kRowsPerBlock];  // index in g of each own key, or -1
+
+    Tile tl;
+    if (!tile_of(tl, p)) return;
+    const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
+    const size_t off = (size_t)tl.bh * L * 64;
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + off;
+    const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + off;
+    const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + off;
+    const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dout) + off;
+    uint16_t* dK = reinterpret_cast<uint16_t*>(p.dk) + off;
+    uint16_t* dV = reinterpret_cast<uint16_t*>(p.dv) + off;
+    const float* lse2 = p.lse2 + (size_t)tl.bh * L;
+    const float* lse2b = p.lse2_band + (size_t)tl.bh * L;
+    const float* dsum = p.dsum + (size_t)tl.bh * L;
+    const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
+
+    const int qa = r0 + 32 * wv, qv = qa + (lane & 31);  // own keys (virtual index)
+    const bool rows_live = qa < Lr;
+    const int krow = r + qv * dil;
+    const bool kvalid = qv < Lr && (!pad || pad[krow] == 0);
+    Op kop, vop;
+    load_op(kop, kvalid ? K + (size_t)krow * 64 : nullptr, h2);
+    load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
+
+    const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
+    const int n_st = n_gst + tl.n_band;
+    auto issue = [&](int s) {
+        char* slot = ring + (s & 1) * kStageB;
+        if (s < n_gst) {
+            auto row_of = [&](int kk) {
+                const int gi = kStageKeys * s + kk;
+                return gi < p.n_g ? p.g[gi] : -1;
+            };
+            dma_tiles(slot, Q, dO, row_of, wv, lane);
+            if (wv == 0) dma_floats(slot, lse2, dsum, row_of, lane);
+        } else {
+            const int ks = tl.stage_row(s - n_gst);
+            auto row_of = [&](int kk) {
+                const int x = ks + kk;
+                return (x >= tl.kb0 && x < tl.kend) ? r + x * dil : -1;
+            };
+            dma_tiles(slot, Q, dO, row_of, wv, lane);
+            if (wv == 0) dma_floats(slot, lse2b, dsum, row_of, lane);
+        }
+    };
+
+    if (tid < kRowsPerBlock) own_gidx[tid] = -1;
+    __syncthreads();
+    for (int gi = tid; gi < p.n_g; gi += kThreads) {
+        const int g = p.g[gi];
+        if (g >= r && (g - r) % dil == 0) {
+            const int vr = (g - r) / dil - r0;
+            if (vr >= 0 && vr < kRowsPerBlock) own_gidx[vr] = gi;
+        }
+    }
+    __syncthreads();
+
+    Lanes lo;
+    lane_setup(lo, lane);
+    if (n_st > 0) issue(0);
+    wait_vmcnt<0>();
+    scale_op(kop);
+    f32x16 dk[2] = {f32x16{}, f32x16{}}, dv[2] = {f32x16{}, f32x16{}};
+    for (int t = 0; t < n_st; ++t) {
+        wait_vmcnt<0>();
+        barrier_nofence();
+        if (t + 1 < n_st) issue(t + 1);
+        const bool gstage = t < n_gst;
+        const int ks = gstage ? 0 : tl.stage_row(t - n_gst);
+        const char* slot = ring + (t & 1) * kStageB;
+        if (!rows_live) continue;
+        for (int sub = 0; sub < 2; ++sub) {
+            const int kss = ks + 32 * sub;
+            if (gstage) {
+                if (kss >= p.n_g) continue;
+            } else {
+                if (kss > qa + 31 + w || kss + 31 < qa - w) continue;  // outside every own key's window
+                if (kss >= tl.kend || kss + 31 < tl.kb0) continue;     // no valid query
+            }
+            const bool interior = !gstage && kss >= qa + 31 - w && kss + 31 <= qa + w;
+            const int mode = (gstage || interior) ? 0 : 1;
+            f32x16 s = prod(slot, sub, lo, kop, row_seed(slot + kLseOff, sub, h2));  // scores - lse, base 2
+            mask_scores(s, mode, 0u, h2, kss + 8 * h2 - qv + w, w, nullptr, 0);
+            const f32x16 dp = prod(slot + kTileB, sub, lo, vop, row_seed(slot + kDOff, sub, h2));  // dO.V - D
+            float pr[16], ds[16];
+            for (int i = 0; i < 16; ++i) {
+                pr[i] = fast_exp2(s[i]);
+                ds[i] = pr[i] * dp[i];
+            }
+            Frag fp, fs;
+            to_frag(pr, fp);
+            to_frag(ds, fs);
+            TOp tt;
+            load_t(tt, slot + kTileB, sub, lo);
+            acc_t(tt, fp, dv);
+            load_t(tt, slot, sub, lo);
+            acc_t(tt, fs, dk);
+        }
+    }
+    const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
+    if (qv < Lr) {
+        const int gi = own_gidx[qv - r0];
+        const float sk = kvalid ? 0.125f : 0.f, sv = kvalid ? 1.f : 0.f;
+        if (gi < 0) {
+            store_row(dK + (size_t)krow * 64, h2, dk, sk);
+            store_row(dV + (size_t)krow * 64, h2, dv, sv);
+        } else {  // global key: completed by the merge (unscaled fp32)
+            store_row_f32(p.ws_dkg + ((size_t)tl.bh * ngq + gi) * 64, h2, dk, kvalid ? 1.f : 0.f);
+            store_row_f32(p.ws_dvg + ((size_t)tl.bh * ngq + gi) * 64, h2, dv, sv);
+        }
+    }
+    if (p.n_g == 0) return;
+
+    // Global keys (B): lane = global key, elements = the home queries of one 32-row
+    // sub-tile per wave, minus the queries whose window holds the key (those pairs
+    // are in the key's own tile) and minus global queries (lse2_band = +inf).
+    const size_t part0 = ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * ngq;
+    const int hs = wv >> 1, hsub = wv & 1;
+    const int hq = r0 + kStageKeys * hs + 32 * hsub;  // first home query of this wave
+    for (int gb = 0; gb < p.n_gblk; ++gb) {
+        const int gk = gb * kGlobalQueriesPerBlock + (lane & 31);
+        const int g = gk < p.n_g ? p.g[gk] : -1;
+        const bool gvalid = g >= 0 && (!pad || pad[g] == 0);
+        Op kg, vg;
+        load_op(kg, gvalid ? K + (size_t)g * 64 : nullptr, h2);
+        load_op(vg, gvalid ? V + (size_t)g * 64 : nullptr, h2);
+        const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
+        const char* hslot;
+        if (gb == 0) {
+            const int u = tl.n_band - 2 + hs;
+            hslot = ring + ((n_gst + u) & 1) * kStageB;
+            wait_vmcnt<0>();
+        } else {
+            __syncthreads();  // the ring is free
+            for (int j = 0; j < 2; ++j) {
+                const int ks = r0 + kStageKeys * j;
+                auto row_of = [&](int kk) {
+                    const int x = ks + kk;
+                    return x < Lr ? r + x * dil : -1;
+                };
+                dma_tiles(ring + j * kStageB, Q, dO, row_of, wv, lane);
+                if (wv == 0) dma_floats(ring + j * kStageB, lse2b, dsum, row_of, lane);
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            hslot = ring + hs * kStageB;
+        }
+        scale_op(kg);
+        f32x16 gk_acc[2] = {f32x16{}, f32x16{}}, gv_acc[2] = {f32x16{}, f32x16{}};
+        if (hq < Lr) {
+            f32x16 s = prod(hslot, hsub, lo, kg, row_seed(hslot + kLseOff, hsub, h2));
+            for (int i = 0; i < 16; ++i) {
+                const int vi = hq + 8 * h2 + kc_of(i);
+                if (!gvalid || vi >= Lr || (unsigned)(vi - vpos + w) <= (unsigned)(2 * w)) s[i] = kNegInf;
+            }
+            const f32x16 dp = prod(hslot + kTileB, hsub, lo, vg, row_seed(hslot + kDOff, hsub, h2));
+            float pr[16], ds[16];
+            for (int i = 0; i < 16; ++i) {
+                pr[i] = fast_exp2(s[i]);
+                ds[i] = pr[i] * dp[i];
+            }
+            Frag fp, fs;
+            to_frag(pr, fp);
+            to_frag(ds, fs);
+            TOp tt;
+            load_t(tt, hslot + kTileB, hsub, lo);
+            acc_t(tt, fp, gv_acc);
+            load_t(tt, hslot, hsub, lo);
+            acc_t(tt, fs, gk_acc);
+        }
+        __syncthreads();  // done with the staged queries: the ring holds the reductions
+        const int nq = min(kGlobalQueriesPerBlock, p.n_g - gb * kGlobalQueriesPerBlock);
+        const size_t dst = (part0 + (size_t)gb * kGlobalQueriesPerBlock) * 64;
+        wave_sum_store(reinterpret_cast<float*>(ring), gk_acc, wv, lane, tid, p.ws_dk + dst, nq);
+        wave_sum_store(reinterpret_cast<float*>(ring), gv_acc, wv, lane, tid, p.ws_dv + dst, nq);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Global rows and keys: one work-group per (global index, b*H + h); wave x sums the
+// partials of tiles x, x + 4, ...; the four waves are added in wave order.
+
+__global__ __launch_bounds__(kThreads) void bwd_merge_kernel(const BwdParams p) {
+    __shared__ float red[kWaves][3][64];
+    const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = bh % p.H, dil = p.dil[h], L = p.L;
+    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
+    float sq = 0.f, sk = 0.f, sv = 0.f;
+    for (int t = wv; t < p.tiles_per_head; t += kWaves) {
+        const int r = t / tpr;
+        const bool exists = r < dil && (t - r * tpr) * kRowsPerBlock < (L - r + dil - 1) / dil;
+        if (!exists) continue;
+        const size_t idx = (((size_t)bh * p.tiles_per_head + t) * ngq + gi) * 64 + d;
+        sq += p.ws_dq[idx];
+        sk += p.ws_dk[idx];
+        sv += p.ws_dv[idx];
+    }
+    red[wv][0][d] = sq;
+    red[wv][1][d] = sk;
+    red[wv][2][d] = sv;
+    __syncthreads();
+    if (wv != 0) return;
+    const size_t own = ((size_t)bh * ngq + gi) * 64 + d;
+    sq = 0.f;
+    sk = p.ws_dkg[own];
+    sv = p.ws_dvg[own];
+    for (int x = 0; x < kWaves; ++x) {
+        sq += red[x][0][d];
+        sk += red[x][1][d];
+        sv += red[x][2][d];
+    }
+    const size_t o = (size_t)bh * L * 64 + (size_t)p.g[gi] * 64 + d;
+    reinterpret_cast<uint16_t*>(p.dq)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sq * 0.125f));
+    reinterpret_cast<uint16_t*>(p.dk)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sk * 0.125f));
+    reinterpret_cast<uint16_t*>(p.dv)[o] = __builtin_bit_cast(uint16_t, (__bf16)sv);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
+    const size_t n = (size_t)p.B * p.H * p.L;
+    const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
+    const int blocks = p.B * p.H * p.tiles_per_head;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
+    const int blocks = p.B * p.H * p.tiles_per_head;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3(blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s) {
+    if (p.n_g == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_merge_kernel, dim3(p.n_g, p.B * p.H), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace lf

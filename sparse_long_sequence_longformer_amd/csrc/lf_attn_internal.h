@@ -29,6 +29,7 @@ struct Params {
     const void* kg;
     const void* vg;
     const uint8_t* pad;  // [B][L] or nullptr
+    float* lse;          // [B][H][L] natural-log sum of each row's exp(scores), or nullptr
     // Global-row partials: one (max, sum, 64 outputs) per (b*H + h, row tile, global
     // query), written by every work-group for its own 128 "home" keys.
     float* ws_ml;        // [B*H][tiles_per_head][n_gblk*32][2]
@@ -45,5 +46,42 @@ struct Params {
 // Launchers (defined in lf_attn_kernels.hip).  Return the launch error.
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s);
+
+// Backward parameters (bf16 tensors, fp32 statistics and partials).
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;     // forward output
+    const void* dout;  // gradient of the output
+    void* dq;
+    void* dk;
+    void* dv;
+    const uint8_t* pad;  // [B][L] or nullptr
+    const float* lse;    // [B][H][L] natural-log row sums of the forward
+    // Row statistics written by the prep kernel, [B][H][L] each:
+    float* lse2;       // lse in base-2 units of the pre-scaled scores; +inf for rows without keys
+    float* lse2_band;  // same, and +inf for global rows (they are not window queries)
+    float* dsum;       // D = dO . O of every row
+    // Partials of the global rows and keys, [B*H][tiles_per_head][n_gblk*32][64]:
+    float* ws_dq;  // dQ of global queries over each tile's home keys
+    float* ws_dk;  // dK of global keys from each tile's home queries outside their window
+    float* ws_dv;  // dV, same pairs
+    // [B*H][n_gblk*32][64]: dK and dV of each global key from its own tile
+    float* ws_dkg;
+    float* ws_dvg;
+    int B, H, L, w;
+    int n_g;
+    int n_gblk;
+    int tiles_per_head;
+    int dil[LF_MAX_HEADS];
+    int g[LF_MAX_GLOBALS];  // sorted, distinct
+};
+
+// Launchers (defined in lf_attn_bwd.hip).
+hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s);
 
 }  // namespace lf

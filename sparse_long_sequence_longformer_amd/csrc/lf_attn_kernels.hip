@@ -43,36 +43,14 @@
 // operand of the next product unchanged.  K rows are read in the order sigma(M) so
 // that accumulator element i of lane-half h2 holds key 16*(i/8) + 8*h2 + (i%8).
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "lf_attn_internal.h"
+#include "lf_attn_device.h"
 
 namespace lf {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-#define LF_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
-
-// exp(x / sqrt(64)) = exp2(x * log2(e) / 8)
-constexpr float kScaleLog2 = 1.4426950408889634f * 0.125f;
-constexpr float kNegInf = -__builtin_inff();
-constexpr int kStageKeys = kKeysPerTile;  // 64
-constexpr int kNoPos = -(1 << 29);        // virtual position that is in no window
 constexpr int kMaskWindow = 64;           // band stages whose pad masks are built at once
 constexpr int kMaskRing = 2 * kMaskWindow;
 constexpr int kMaxGlobalStages = LF_MAX_GLOBALS / kStageKeys;
-constexpr int kLargeW = 1 << 28;  // band test that admits every key (|key - query| < 2^28)
 constexpr int kAllParts = -1;     // dma_stage: every block of the wave
 
 #ifndef LF_BF16_WAVES_PER_EU
@@ -81,92 +59,6 @@ constexpr int kAllParts = -1;     // dma_stage: every block of the wave
 #ifndef LF_BF16_NS
 #define LF_BF16_NS 2
 #endif
-
-// Source of every invalid key: 256 zero bytes (one fp32 row, two bf16 rows).
-__device__ __attribute__((aligned(16))) uint32_t g_zero_row[64];
-
-__device__ __forceinline__ int sigma(int M) {  // K row read by lane row M
-    const int q = M >> 3, hh = (M >> 2) & 1, c = M & 3;
-    return 16 * (q >> 1) + 8 * hh + 4 * (q & 1) + c;
-}
-__device__ __forceinline__ int key_local(int i, int h2) { return 16 * (i >> 3) + 8 * h2 + (i & 7); }
-
-// LDS swizzles of 16-byte chunks.  K: every 8 consecutive lanes of the 128-bit
-// operand reads (rows sigma(0..7) + c) hit 8 distinct chunks.  V: the four rows of
-// each 16-lane transposed read land on four distinct 32-byte slots.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
-
-// Lanes l and l^32 hold the two halves of one query's keys.
-__device__ __forceinline__ float pair_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ uint64_t ballot64(bool x) { return __ballot(x); }
-
-// 16 bytes per lane from global memory into LDS at base + 16 * lane (base uniform).
-// Issued as inline asm: the compiler then does not treat the in-flight copies as
-// possibly aliasing later LDS reads (it would drain every copy with vmcnt(0) before
-// each transposed read).  Completion is awaited explicitly with wait_vmcnt before
-// the barrier that publishes a stage.  The instruction has no register results.
-// M0 carries the LDS base; no other code in these kernels keeps a value in M0.
-__device__ __forceinline__ void dma16(const void* src, char* lds_base) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
-}
-
-// Wave-uniform copy of a 64-bit value in scalar registers.  The builtin returns a
-// signed int: both halves go through uint32_t so that the low half is not sign-extended.
-__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-    return ((uint64_t)hi << 32) | (uint64_t)lo;
-}
-
-// 16 bytes per lane from base + off (base uniform, off a per-lane 32-bit byte offset)
-// into LDS at lds_base + 16 * lane: the scalar-base form needs no per-lane 64-bit
-// address arithmetic.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, char* lds_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
-    const uint64_t b64 = (uint64_t)(uintptr_t)base;
-    const uint64_t sb = uniform64(b64);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0)
-                 : "memory", "m0");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Work-group barrier without a memory fence: ordering of the staged LDS data is
-// established by the explicit vmcnt waits; the empty asm keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void barrier_nofence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Work-groups are dispatched round-robin over the 8 XCDs; hand each XCD a
-// contiguous range of logical ids so that neighbouring row tiles of one (b, h),
-// which read overlapping K/V spans, share one L2.
-__device__ __forceinline__ int xcd_remap(int pid, int n) {
-    constexpr int X = 8;
-    const int per = (n + X - 1) / X;
-    int tall = n % X;
-    if (tall == 0) tall = X;
-    const int xcd = pid % X, local = pid / X;
-    return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
-}
 
 // ---------------------------------------------------------------------------
 // Element-type traits: operand loads, stage DMA, the two products, output store.
@@ -509,6 +401,12 @@ __device__ __forceinline__ void state_init(State& st) {
     st.o[1] = f32x16{};
 }
 
+// Natural-log sum of a row's exp(scores) from its base-2 offset and the weight sum
+// relative to it; -inf for a row with no key.
+__device__ __forceinline__ float lse_of(float ofs2, float l) {
+    return l > 0.f ? (ofs2 + __builtin_log2f(l)) * 0.69314718055994531f : kNegInf;
+}
+
 // A tile whose weights (relative to cofs) sum to at most 2^8 has every weight at
 // most 2^8: exact in bf16 and fp32 alike, so it is folded as it is.
 constexpr float kTileSumBound = 256.0f;
@@ -563,35 +461,6 @@ __device__ __forceinline__ void fold_tile(State& st, const f32x16& x, typename T
     st.l += ts;
 }
 
-// Element i of a 32-key score tile holds stage key 32*sub + kc(i) + 8*h2.
-__device__ __forceinline__ constexpr int kc_of(int i) { return 16 * (i >> 3) + (i & 7); }
-
-// Masks of a 32-key score tile.  MODE 0: none; 1: band mask, base = (first key of
-// the sub-tile) + 8*h2 - query + w; 2: global keys (gp: in-window positions of the
-// sub-tile's keys).  Invalid keys (inv32 bits) are masked in modes 1 and 2.
-__device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32, int h2, int base, int w,
-                                            const int* gp, int wq) {
-    if (mode == 0) return;
-    const uint32_t invl = inv32 >> (8 * h2);
-    if (mode == 1) {
-        // Band test 0 <= base + kc <= 2w as one bit range over kc, minus invalid keys.
-        const int lo_k = max(0, -base), hi_k = min(31, 2 * w - base);
-        uint32_t keep = 0u;
-        if (hi_k >= lo_k) keep = (hi_k >= 31 ? ~0u : ((2u << hi_k) - 1u)) & ~((1u << lo_k) - 1u);
-        keep &= ~invl;
-        for (int i = 0; i < 16; ++i)
-            if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
-    } else {
-        // The lane's 16 keys are gp[0..7] and gp[16..23]: four 16-byte LDS reads.
-        typedef int i32x4 __attribute__((ext_vector_type(4)));
-        const i32x4* g4 = reinterpret_cast<const i32x4*>(gp);
-        const i32x4 a[4] = {g4[0], g4[1], g4[4], g4[5]};
-        for (int i = 0; i < 16; ++i) {
-            const int kc = kc_of(i);
-            if (((invl >> kc) & 1) || (unsigned)(a[i >> 2][i & 3] + wq) <= (unsigned)(2 * w)) s[i] = kNegInf;
-        }
-    }
-}
 
 // One 32-key sub-tile of a stage: scores, masks, softmax update, P.V product.
 template <class T>
@@ -820,7 +689,10 @@ void band_kernel(const Params p) {
     if (qv < Lr) {
         const int row = r + qv * dil;
         const int vr = qv - r0;  // global rows are written by the merge
-        if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) T::store_row(O + (size_t)row * 64, h2, st.o, scale);
+        if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) {
+            T::store_row(O + (size_t)row * 64, h2, st.o, scale);
+            if (p.lse && h2 == 0) p.lse[(size_t)bh * L + row] = lse_of(st.cofs, st.l);
+        }
     }
     if (p.n_g == 0) return;
 
@@ -971,6 +843,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     const float res = l > 0.f ? o / l : 0.f;
     Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bh * L * 64;
     O[(size_t)p.g[gi] * 64 + d] = T::from_float(res);
+    if (p.lse && d == 0) p.lse[(size_t)bh * L + p.g[gi]] = lse_of(M, l);
 }
 
 }  // namespace

@@ -140,6 +140,38 @@ def test_global_proj_invalid_arguments(kw, frag):
 
 
 @needs_lib
+def test_backward_host_validation():
+    lib = binding.load_library()
+    dil = (ctypes.c_int32 * 1)(1)
+    dil_p = ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32))
+
+    def call(h, lse=FAKE * 9, dq=FAKE * 10, dk=FAKE * 11, dv=FAKE * 12, out=FAKE * 4):
+        st = lib.lf_attn_backward(h, FAKE, FAKE * 2, FAKE * 3, out, FAKE * 5, lse, dq, dk, dv, 1, 1, 64, 64, 4,
+                                  dil_p, None, 0, None, None)
+        return st, lib.lf_attn_last_error(h).decode()
+
+    h32, h16 = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h32), 0) == 0 and lib.lf_attn_create(ctypes.byref(h16), 1) == 0
+    try:
+        st, msg = call(h32)
+        assert st == 2 and "bf16" in msg
+        for kw, frag in [(dict(lse=None), "non-null"), (dict(dv=None), "non-null"), (dict(lse=FAKE * 9 + 2), "aligned"),
+                         (dict(dq=FAKE * 10 + 8), "aligned"), (dict(dk=FAKE * 10 + 4096), "overlap"),
+                         (dict(dq=FAKE * 2 + 1024), "overlap"), (dict(dv=FAKE * 9 - 16), "overlap")]:
+            st, msg = call(h16, **kw)
+            assert st == 1 and frag in msg, (kw, st, msg)
+        st = lib.lf_attn_forward_lse(h16, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1, 1, 64, 64, 4, dil_p, None, 0,
+                                     None, None)
+        assert st == 1
+        st = lib.lf_attn_forward_lse(h16, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 3 + 64, 1, 1, 64, 64, 4, dil_p,
+                                     None, 0, None, None)
+        assert st == 1 and "lse must not overlap" in lib.lf_attn_last_error(h16).decode()
+    finally:
+        lib.lf_attn_destroy(h32)
+        lib.lf_attn_destroy(h16)
+
+
+@needs_lib
 def test_null_handle():
     lib = binding.load_library()
     assert lib.lf_attn_forward(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None, None, 0, None, None) == 1
