@@ -12,7 +12,8 @@ i-d*w ... i, ... i+d*w, global tokens that see and are seen by every position;
 §4: the patterns are combined into one attention):
   * if i is global: every position 0..L-1;
   * otherwise: {i + m*dil : m = -w..w} intersected with [0, L), plus every global;
-  * minus padded keys.
+  * minus padded keys;
+  * in the one-sided (causal) variant, minus every key after i.
 """
 
 from __future__ import annotations
@@ -20,7 +21,7 @@ from __future__ import annotations
 import math
 
 
-def key_set(i: int, L: int, w: int, dil: int, globals_, pad_row=None) -> list[int]:
+def key_set(i: int, L: int, w: int, dil: int, globals_, pad_row=None, causal: bool = False) -> list[int]:
     G = set(int(g) for g in (globals_ or []))
     if i in G:
         keys = set(range(L))
@@ -33,6 +34,8 @@ def key_set(i: int, L: int, w: int, dil: int, globals_, pad_row=None) -> list[in
         keys |= G
     if pad_row is not None:
         keys = {j for j in keys if not pad_row[j]}
+    if causal:  # one-sided variant: no key after its query
+        keys = {j for j in keys if j <= i}
     return sorted(keys)
 
 
@@ -48,11 +51,11 @@ def attention_row(q_i, k, v, keys) -> list[float]:
     return [math.fsum(weights[n] * v[j][t] for n, j in enumerate(keys)) / total for t in range(d)]
 
 
-def attention_bh(q, k, v, w: int, dil: int, globals_=None, pad_row=None) -> list[list[float]]:
+def attention_bh(q, k, v, w: int, dil: int, globals_=None, pad_row=None, causal: bool = False) -> list[list[float]]:
     """q, k, v: nested lists [L][d] of floats.  Returns [L][d]."""
     L = len(k)
-    return [attention_row(q[i], k, v, key_set(i, L, w, dil, globals_, pad_row)) for i in range(L)]
+    return [attention_row(q[i], k, v, key_set(i, L, w, dil, globals_, pad_row, causal)) for i in range(L)]
 
 
-def pair_count(L: int, w: int, dil: int, globals_=None, pad_row=None) -> int:
-    return sum(len(key_set(i, L, w, dil, globals_, pad_row)) for i in range(L))
+def pair_count(L: int, w: int, dil: int, globals_=None, pad_row=None, causal: bool = False) -> int:
+    return sum(len(key_set(i, L, w, dil, globals_, pad_row, causal)) for i in range(L))

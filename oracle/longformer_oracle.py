@@ -25,6 +25,12 @@ What it computes (per batch b and head h, with inputs widened to float64):
   "Reformer哈希：突破Transformer计算瓶颈的高效注意力机制详解" (Reformer hashing),
   §"core principle", restricted to the key set above.
 * A query row whose key set is empty gives an all-zero output row.
+* One-sided (causal) variant (``causal=True`` everywhere): every pair with a key
+  after its query is removed, i.e. the key set above intersected with {j <= i}:
+  window keys i - m*dil for m = 0..w, global keys g <= i, and a global row sees
+  the keys j <= g.  This is the pattern of autoregressive language modelling,
+  which the Longformer-explained page lists among the pretraining tasks (§6); the
+  pages give no rule for it, and a mask on top of the union is the plainest one.
 * Variant with separate global projections (``attention_global_proj``): the page
   "基于Block-Sparse Attention的Longformer" §4 gives global attention its own
   query, key and value projections.  Read inside the one-softmax formulation: a
@@ -83,10 +89,10 @@ def window_member(i: np.ndarray, j: np.ndarray, w: int, dil: int) -> np.ndarray:
     return (np.abs(diff) <= w * dil) & (diff % dil == 0)
 
 
-def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray) -> np.ndarray:
+def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray, causal: bool = False) -> np.ndarray:
     """Explicit boolean mask M[r, j] for the query rows ``rows`` over all L keys.
 
-    M[i, j] = not pad[j] and (i in G or j in G or j in window(i)).
+    M[i, j] = not pad[j] and (i in G or j in G or j in window(i)) [and j <= i if causal].
     """
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(L, dtype=np.int64)[None, :]
@@ -97,6 +103,8 @@ def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray
     m = window_member(i, j, w, dil) | is_global_key[None, :] | is_global_query
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[None, :]
+    if causal:
+        m &= j <= i
     return m
 
 
@@ -118,7 +126,7 @@ def _attention_rows(q, k, v, m):
 
 
 def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=None,
-                 return_probs: bool = False):
+                 return_probs: bool = False, causal: bool = False):
     """Oracle for one (batch, head) slice.
 
     q, k, v: [L, d] arrays (widened to float64).  ``rows`` selects query rows
@@ -137,7 +145,7 @@ def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=
     probs = np.zeros((rows.size, L), dtype=np.float64) if return_probs else None
     for s0 in range(0, rows.size, ROW_BLOCK):
         blk = rows[s0:s0 + ROW_BLOCK]
-        m = mask_rows(L, w, dil, G, pad_row, blk)
+        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal)
         o, p = _attention_rows(q[blk], k, v, m)
         out[s0:s0 + blk.size] = o
         if return_probs:
@@ -145,7 +153,7 @@ def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=
     return (out, probs) if return_probs else out
 
 
-def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None):
+def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False):
     """Oracle for the full [B, H, L, d] problem.  Returns float64 [B, H, L, d].
 
     ``dil_per_head`` has one dilation per head (w is shared by all heads);
@@ -162,11 +170,11 @@ def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None)
     for b in range(B):
         for h in range(H):
             out[b, h] = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
-                                     None if pad is None else pad[b])
+                                     None if pad is None else pad[b], causal=causal)
     return out
 
 
-def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, samples):
+def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, samples, causal: bool = False):
     """Oracle output rows for a list of (b, h, i) samples, computed one by one.
 
     Used to check full-size runs where the whole oracle would be too slow.
@@ -177,12 +185,13 @@ def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, s
     res = []
     for b, h, i in samples:
         o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
-                         None if pad is None else pad[b], rows=[i])
+                         None if pad is None else pad[b], rows=[i], causal=causal)
         res.append(o[0])
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
 
 
-def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1) -> int:
+def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1,
+               causal: bool = False) -> int:
     """Number of attended (query, key) pairs, summed over batch and heads: sum of M."""
     G = global_set(global_idx)
     dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
@@ -192,7 +201,7 @@ def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
         for d in dil:
             for s0 in range(0, L, ROW_BLOCK):
                 rows = np.arange(s0, min(L, s0 + ROW_BLOCK))
-                total += int(mask_rows(L, w, d, G, None if pad is None else pad[b], rows).sum())
+                total += int(mask_rows(L, w, d, G, None if pad is None else pad[b], rows, causal=causal).sum())
     return total
 
 
@@ -248,7 +257,7 @@ def _scores_rows(q, k, m):
     return np.where(m, (q @ k.T) / math.sqrt(d), -np.inf)
 
 
-def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None) -> np.ndarray:
+def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False) -> np.ndarray:
     """log sum_{j in keys(i)} exp(q_i . k_j / sqrt(d)) of every row; -inf without keys."""
     q, k = _as_f64(q), _as_f64(k)
     L = k.shape[0]
@@ -256,7 +265,7 @@ def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None) -> n
     out = np.empty(L, dtype=np.float64)
     for s0 in range(0, L, ROW_BLOCK):
         blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
-        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk))
+        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk, causal=causal))
         top = s.max(axis=1)
         has = np.isfinite(top)
         safe = np.where(has, top, 0.0)
@@ -265,7 +274,7 @@ def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None) -> n
     return out
 
 
-def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None) -> np.ndarray:
+def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False) -> np.ndarray:
     """Per-row log-sum-exp of the full problem: float64 [B, H, L]."""
     q, k = _as_f64(q), _as_f64(k)
     B, H, L, _ = q.shape
@@ -275,11 +284,11 @@ def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None
     for b in range(B):
         for h in range(H):
             out[b, h] = attention_lse_bh(q[b, h], k[b, h], w, dil[h], global_idx,
-                                         None if pad is None else pad[b])
+                                         None if pad is None else pad[b], causal=causal)
     return out
 
 
-def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None):
+def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False):
     """Gradients (dQ, dK, dV) of one (batch, head) slice for the upstream gradient dout.
 
     Row blocks of the explicit mask; dK and dV collect every block's contribution.
@@ -292,7 +301,7 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
     dv = np.zeros_like(v)
     for s0 in range(0, L, ROW_BLOCK):
         blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
-        m = mask_rows(L, w, dil, G, pad_row, blk)
+        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal)
         o, p = _attention_rows(q[blk], k, v, m)
         dv += p.T @ do[blk]
         dp = do[blk] @ v.T
@@ -303,7 +312,8 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None):
+def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
+                       causal: bool = False):
     """Gradients of the full problem: three float64 [B, H, L, d] arrays (dQ, dK, dV)."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
     B, H, L, d = q.shape
@@ -315,5 +325,6 @@ def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = attention_backward_bh(
-                q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], global_idx, None if pad is None else pad[b])
+                q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], global_idx, None if pad is None else pad[b],
+                causal=causal)
     return dq, dk, dv

@@ -43,8 +43,12 @@ def _unique_globals(global_idx, L):
     return g
 
 
-def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray) -> PairCounts:
-    """Pair counts for one (sequence, head).  ``valid[j]`` is True for unpadded keys."""
+def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray, causal: bool = False) -> PairCounts:
+    """Pair counts for one (sequence, head).  ``valid[j]`` is True for unpadded keys.
+
+    ``causal``: the one-sided variant, every pair with its key after its query removed
+    (window keys i - m*dil for m = 0..w, global keys g <= i, global rows see j <= g).
+    """
     is_g = np.zeros(L, dtype=bool)
     is_g[G] = True
     band = 0
@@ -56,23 +60,30 @@ def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray) -
         pref = np.concatenate([[0], np.cumsum(valid[pos].astype(np.int64))])
         i = np.arange(n, dtype=np.int64)
         lo = np.maximum(i - w, 0)
-        hi = np.minimum(i + w, n - 1)
+        hi = i if causal else np.minimum(i + w, n - 1)
         win = pref[hi + 1] - pref[lo]
         rows = ~is_g[pos]
         band += int(win[rows].sum())
         if Gv.size:
-            # globals inside row's window: same residue and |g' - i| <= w
+            # globals inside row's window: same residue and g' - i in [-w, w] ([-w, 0] causal)
             same = Gv[(Gv % dil) == r]
             gp = (same - r) // dil
             inside = np.zeros(n, dtype=np.int64)
             for g in gp:
-                inside[max(0, g - w):min(n, g + w + 1)] += 1
-            gcol += int((Gv.size - inside[rows]).sum())
-    grow = int(G.size) * int(valid.sum())
+                inside[max(0, g if causal else g - w):min(n, g + w + 1)] += 1
+            # global keys the row sees at all: every one, or those at or before it (causal)
+            seen = np.searchsorted(Gv, pos, side="right") if causal else np.full(n, Gv.size)
+            gcol += int((seen - inside)[rows].sum())
+    if causal:
+        vpref = np.concatenate([[0], np.cumsum(valid.astype(np.int64))])
+        grow = int(vpref[G + 1].sum()) if G.size else 0
+    else:
+        grow = int(G.size) * int(valid.sum())
     return PairCounts(band, gcol, grow)
 
 
-def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1) -> PairCounts:
+def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1,
+                causal: bool = False) -> PairCounts:
     """Attended pairs summed over B sequences and all heads.
 
     ``key_pad_mask`` is an array-like [B, L] (nonzero = padded) or None.
@@ -90,7 +101,7 @@ def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None
         for dl in dils:
             key = (key_b, dl)
             if key not in cache:
-                cache[key] = count_pairs_bh(L, w, dl, G, valid)
+                cache[key] = count_pairs_bh(L, w, dl, G, valid, causal)
             c = cache[key]
             tot.band += c.band
             tot.global_col += c.global_col

@@ -460,6 +460,77 @@ def pin_lse_brute():
     assert np.abs(orc.attention_lse_bh(q, k, L, 1) - ref).max() < 1e-12
 
 
+# ------------------------------------------------------ one-sided (causal) variant
+
+def pin_causal_brute():
+    """Causal variant: the oracle equals brute-force enumeration of the key sets with
+    every key after its query removed; log-sum-exp as well."""
+    for L, d, w, dil, G, padk, seed in BRUTE_CASES:
+        q, k, v = (_rand((L, d), seed * 3 + t) for t in range(3))
+        pad = _pad_for(padk, L, seed)
+        padl = None if pad is None else pad.tolist()
+        got = orc.attention_bh(q, k, v, w, dil, G, pad, causal=True)
+        ref = np.array(brute.attention_bh(q.tolist(), k.tolist(), v.tolist(), w, dil, G, padl, causal=True))
+        err = np.abs(got - ref).max() if L else 0.0
+        assert err < 1e-12, (L, w, dil, G, err)
+        assert orc.mask_count(L, w, [dil], G, None if pad is None else pad[None, :], causal=True) == \
+            brute.pair_count(L, w, dil, G, padl, causal=True)
+        lse = orc.attention_lse_bh(q, k, w, dil, G, pad, causal=True)
+        for i in range(L):
+            keys = brute.key_set(i, L, w, dil, G, padl, causal=True)
+            if not keys:
+                assert lse[i] == -np.inf
+                continue
+            sc = [math.fsum(q[i, t] * k[j, t] for t in range(d)) / math.sqrt(d) for j in keys]
+            top = max(sc)
+            assert abs(lse[i] - (top + math.log(math.fsum(math.exp(x - top) for x in sc)))) < 1e-12
+
+
+def pin_causal_textbook():
+    """w >= L, dil = 1, no globals: causal attention as computed by torch's CPU
+    scaled_dot_product_attention(is_causal=True) in float64; row 0 is V_0 exactly."""
+    for L, w in [(64, 64), (37, 100)]:
+        q, k, v = (_rand((L, 32), 400 + L + t) for t in range(3))
+        got = orc.attention_bh(q, k, v, w, 1, causal=True)
+        tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0, 0].numpy()
+        assert np.abs(got - ref).max() < 1e-12
+        assert np.array_equal(got[0], v[0])
+
+
+def pin_causal_prefix():
+    """A causal row never depends on later positions: changing Q, K, V from position n
+    on leaves rows < n bit-identical, with globals and padding."""
+    L, n, w, dil, G = 60, 35, 4, 2, [3, 40, 50]
+    q, k, v = (_rand((L, 8), 410 + t) for t in range(3))
+    pad = np.zeros(L, dtype=bool)
+    pad[[7, 45]] = True
+    a = orc.attention_bh(q, k, v, w, dil, G, pad, causal=True)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for x in (q2, k2, v2):
+        x[n:] += 3.0
+    b = orc.attention_bh(q2, k2, v2, w, dil, G, pad, causal=True)
+    assert np.array_equal(a[:n], b[:n])
+    assert np.abs(a[n:] - b[n:]).min(axis=1).max() > 0
+
+
+def pin_causal_backward_autograd():
+    """Causal gradients equal torch autograd of a dense masked attention whose key
+    sets come from the causal brute-force enumeration."""
+    for L, d, w, dil, G, padk, seed in BWD_CASES:
+        q, k, v, do = (_rand((L, d), seed * 5 + 10 + t) for t in range(4))
+        pad = _pad_for(padk, L, seed)
+        padl = None if pad is None else pad.tolist()
+        keysets = [brute.key_set(i, L, w, dil, G, padl, causal=True) for i in range(L)]
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        out = _torch_dense_attention(tq, tk, tv, keysets)
+        (out * torch.from_numpy(do)).sum().backward()
+        dq, dk, dv = orc.attention_backward_bh(q, k, v, do, w, dil, G, pad, causal=True)
+        for name, a, b in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+            err = np.abs(a - b.numpy()).max()
+            assert err < 1e-12, (name, L, w, dil, G, padk, err)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -484,4 +555,8 @@ ALL_PINS = [
     pin_backward_structure,
     pin_backward_invariants,
     pin_lse_brute,
+    pin_causal_brute,
+    pin_causal_textbook,
+    pin_causal_prefix,
+    pin_causal_backward_autograd,
 ]

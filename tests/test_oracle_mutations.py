@@ -38,7 +38,13 @@ def _window_sign(i, j, w, dil):  # one-sided window (a causal reading)
     return (diff <= 0) & (-diff <= w * dil) & (diff % dil == 0)
 
 
-def _mask_rows_only(L, w, dil, G, pad_row, rows):  # global rows only, no global columns
+def _causal(m, rows, L, causal):
+    if causal:
+        m &= np.arange(L)[None, :] <= np.asarray(rows)[:, None]
+    return m
+
+
+def _mask_rows_only(L, w, dil, G, pad_row, rows, causal=False):  # global rows only, no global columns
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(L)[None, :]
     isg = np.zeros(L, dtype=bool)
@@ -46,10 +52,10 @@ def _mask_rows_only(L, w, dil, G, pad_row, rows):  # global rows only, no global
     m = orc.window_member(rows[:, None], j, w, dil) | isg[rows][:, None]
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[None, :]
-    return m
+    return _causal(m, rows, L, causal)
 
 
-def _mask_cols_only(L, w, dil, G, pad_row, rows):  # global columns only, no global rows
+def _mask_cols_only(L, w, dil, G, pad_row, rows, causal=False):  # global columns only, no global rows
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(L)[None, :]
     isg = np.zeros(L, dtype=bool)
@@ -57,18 +63,18 @@ def _mask_cols_only(L, w, dil, G, pad_row, rows):  # global columns only, no glo
     m = orc.window_member(rows[:, None], j, w, dil) | isg[None, :]
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[None, :]
-    return m
+    return _causal(m, rows, L, causal)
 
 
-def _mask_pad_queries(L, w, dil, G, pad_row, rows):  # padding applied to query rows
-    m = _orig_mask(L, w, dil, G, None, rows)
+def _mask_pad_queries(L, w, dil, G, pad_row, rows, causal=False):  # padding applied to query rows
+    m = _orig_mask(L, w, dil, G, None, rows, causal=causal)
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[np.asarray(rows)][:, None]
     return m
 
 
-def _mask_pad_ignored(L, w, dil, G, pad_row, rows):
-    return _orig_mask(L, w, dil, G, None, rows)
+def _mask_pad_ignored(L, w, dil, G, pad_row, rows, causal=False):
+    return _orig_mask(L, w, dil, G, None, rows, causal=causal)
 
 
 def _rows_scale_d(q, k, v, m):  # 1/d instead of 1/sqrt(d)
@@ -128,11 +134,11 @@ def _gp_uses_v(q, k, v, q_g, k_g, v_g, *a, **kw):  # global rows weight v, not v
 def _bwd_mutant(kind):
     """attention_backward_bh with one plausible mistake planted."""
 
-    def fn(q, k, v, dout, w, dil, global_idx=None, pad_row=None):
+    def fn(q, k, v, dout, w, dil, global_idx=None, pad_row=None, causal=False):
         q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
         L, d = q.shape
         G = orc.global_set(global_idx)
-        m = orc.mask_rows(L, w, dil, G, pad_row, np.arange(L))
+        m = orc.mask_rows(L, w, dil, G, pad_row, np.arange(L), causal=causal)
         o, p = orc._attention_rows(q, k, v, m)
         dv = p.T @ do
         dp = do @ v.T
@@ -158,6 +164,25 @@ def _bwd_mutant(kind):
     return fn
 
 
+def _mask_causal_window_only(L, w, dil, G, pad_row, rows, causal=False):  # future global keys kept
+    m = _orig_mask(L, w, dil, G, pad_row, rows, causal=causal)
+    if causal:
+        rows = np.asarray(rows, dtype=np.int64)
+        extra = np.zeros((rows.size, L), dtype=bool)
+        extra[:, np.asarray(G, dtype=np.int64)] = True
+        if pad_row is not None:
+            extra &= ~np.asarray(pad_row, dtype=bool)[None, :]
+        m |= extra
+    return m
+
+
+def _mask_causal_strict(L, w, dil, G, pad_row, rows, causal=False):  # self excluded (j < i)
+    m = _orig_mask(L, w, dil, G, pad_row, rows, causal=causal)
+    if causal:
+        m &= np.arange(L)[None, :] != np.asarray(rows)[:, None]
+    return m
+
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -167,6 +192,8 @@ MUTANTS = {
     "global_cols_only": ("mask_rows", _mask_cols_only),
     "pad_on_queries": ("mask_rows", _mask_pad_queries),
     "pad_ignored": ("mask_rows", _mask_pad_ignored),
+    "causal_future_globals": ("mask_rows", _mask_causal_window_only),
+    "causal_excludes_self": ("mask_rows", _mask_causal_strict),
     "scale_1_over_d": ("_attention_rows", _rows_scale_d),
     "transposed_scores": ("_attention_rows", _rows_transposed),
     "weights_times_k": ("_attention_rows", _rows_pk),

@@ -73,3 +73,24 @@ def test_workload_generator_recipe():
     q, k, v = workloads.make_qkv(workloads.WORKLOADS["tiny_f32"])
     q2, _, _ = workloads.make_qkv(workloads.WORKLOADS["tiny_f32"])
     assert q.shape == (1, 1, 256, 64) and (q == q2).all() and not (q == k).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_counter_matches_mask_causal(seed):
+    """One-sided variant: closed-form counts equal the oracle's causal mask sums."""
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(1, 90))
+    w = int(rng.integers(0, 12))
+    H = int(rng.integers(1, 4))
+    dil = [int(x) for x in rng.integers(1, 4, size=H)]
+    G = [int(x) for x in rng.integers(0, L, size=int(rng.integers(0, 5)))]
+    B = int(rng.integers(1, 3))
+    pad = (rng.random((B, L)) < 0.25).astype(np.uint8) if seed % 2 else None
+    c = pattern.count_pairs(L, w, dil, G, pad, B=B, causal=True)
+    assert c.total == orc.mask_count(L, w, dil, G, pad, B=B, causal=True)
+    for b in range(B):
+        for d in dil:
+            pr = None if pad is None else pad[b].astype(bool).tolist()
+            rows = sum(len(brute.key_set(g, L, w, d, G, pr, causal=True)) for g in sorted(set(G)))
+            cb = pattern.count_pairs(L, w, [d], G, None if pad is None else pad[b:b + 1], causal=True)
+            assert cb.global_row == rows
