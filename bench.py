@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--global-proj", action="store_true",
                     help="global rows use their own q/k/v projections (lf_attn_forward_global_proj)")
+    ap.add_argument("--causal", action="store_true",
+                    help="one-sided variant: no pair with its key after its query")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (lf_attn_backward) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,23 +153,26 @@ def main():
     q, k, v = workloads.make_qkv(wl)
     G = wl.global_positions()
     pad = wl.pad_mask()
-    pairs = pattern.count_pairs(wl.L, wl.w, wl.dil_list(), G, pad, B=wl.B)
+    pairs = pattern.count_pairs(wl.L, wl.w, wl.dil_list(), G, pad, B=wl.B, causal=args.causal)
     flops = pattern.effective_flops(pairs.total)
 
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     padd = None if pad is None else torch.from_numpy(pad).to(dev)
     out = torch.empty_like(qd)
     handle = binding.LfAttn(wl.dtype)
+    if args.causal:
+        handle.set_causal(True)
     dil = wl.dil_list()
 
     if args.global_proj:
         qgd, kgd, vgd = (t.to(dev) for t in workloads.make_global_proj(wl))
 
         def step():
-            binding.forward_global_proj(qd, kd, vd, qgd, kgd, vgd, wl.w, dil, G, padd, out=out, handle=handle)
+            binding.forward_global_proj(qd, kd, vd, qgd, kgd, vgd, wl.w, dil, G, padd, out=out, handle=handle,
+                                        causal=args.causal)
     else:
         def step():
-            binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle)
+            binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle, causal=args.causal)
 
     if args.backward:
         if wl.dtype != "bf16":
@@ -199,7 +204,7 @@ def main():
     stage_avg = {k2: v2[0] / v2[1] for k2, v2 in st.items() if v2[1]}
     k_avg_ms = stage_avg["band"]  # the dominant kernel
     achieved = flops / (k_avg_ms * 1e-3) / 1e12  # every attended pair but the merge's arithmetic
-    traffic = None if args.global_proj else traffic_for(name)
+    traffic = None if (args.global_proj or args.causal) else traffic_for(name)
 
     res = {
         "metric": METRIC,
@@ -222,13 +227,14 @@ def main():
             "global_batch": wl.B,
             "parallelism": "single GPU",
             "global_projections": "separate" if args.global_proj else "shared",
+            "window": "one-sided" if args.causal else "symmetric",
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "attended_pairs": pairs.total,
         "effective_flop_per_step": flops,
         "kernel_ms_avg": {k2: round(v2, 6) for k2, v2 in stage_avg.items()},
         "roofline": {
-            "kernel": "lf::band_kernel<Bf16>" if wl.dtype == "bf16" else "lf::band_kernel<F32>",
+            "kernel": f"lf::band_kernel<{'Bf16' if wl.dtype == 'bf16' else 'F32'}, {str(args.causal).lower()}>",
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
@@ -255,8 +261,8 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
 
     g = np.random.default_rng(7).standard_normal(tuple(qd.shape), dtype=np.float32)
     dod = torch.from_numpy(g).to(torch.bfloat16).to(qd.device)
-    out, lse = binding.forward_lse(qd, kd, vd, wl.w, dil, G, padd, handle=handle)
-    dq, dk, dv = binding.backward(qd, kd, vd, out, dod, lse, wl.w, dil, G, padd, handle=handle)
+    out, lse = binding.forward_lse(qd, kd, vd, wl.w, dil, G, padd, handle=handle, causal=args.causal)
+    dq, dk, dv = binding.backward(qd, kd, vd, out, dod, lse, wl.w, dil, G, padd, handle=handle, causal=args.causal)
     torch.cuda.synchronize()
 
     # The timed loops call the C entry points with arguments marshalled once: the
@@ -313,6 +319,7 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
     value = flops_bwd / (ms_bwd * 1e-3) / 1e12
     res = {
         "metric": "window+global attn bwd effective TFLOP/s (2.5x forward FLOP), L=4096 w=512",
+        "attended_pairs": pairs.total,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -326,7 +333,8 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
         "data": "synthetic (seeded N(0,1) q/k/v/dO, no trained weights)",
         "config": {"workload": name, "B": wl.B, "H": wl.H, "seq_len": wl.L, "d_h": wl.d, "w": wl.w,
                    "dil": sorted(set(dil)), "n_global": len(G), "padded_lengths": list(wl.lengths) or None,
-                   "global_batch": wl.B, "parallelism": "single GPU"},
+                   "global_batch": wl.B, "parallelism": "single GPU",
+                   "window": "one-sided" if args.causal else "symmetric"},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "train_step_ms": round(ms_train, 6),
         "train_step_tflops": round(3.5 * flops_fwd / (ms_train * 1e-3) / 1e12, 3),

@@ -60,6 +60,10 @@ typedef enum lf_dtype {
 #define LF_STAGE_BWD_DKV 4   /* backward: dK, dV (key-owned), global-key partials */
 #define LF_STAGE_BWD_MERGE 5 /* backward: sums of the global partials (only with globals) */
 
+/* Pattern variants (lf_attn_set_window_mode). */
+#define LF_WINDOW_SYMMETRIC 0 /* keys i + m*dil, m = -w..w (default) */
+#define LF_WINDOW_CAUSAL 1    /* one-sided: every pair with its key after its query removed */
+
 typedef struct lf_attn_s* lf_attn_t;
 
 /*
@@ -169,6 +173,20 @@ lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k,
                                       int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
                                       const int32_t* global_idx, int n_global,
                                       const uint8_t* key_pad_mask, void* stream);
+
+/*
+ * Pattern variant of every later call on `h` (forward, forward_lse,
+ * forward_global_proj, backward).
+ *
+ * LF_WINDOW_SYMMETRIC (default): the pattern above.
+ * LF_WINDOW_CAUSAL: the same key sets intersected with {j <= i}: window keys
+ *   i - m*dil for m = 0..w, global keys g <= i, and a global row sees the keys
+ *   j <= g.  This is the pattern of autoregressive language modelling, which page
+ *   "基于自注意力机制的长文本建模算法：Longformer详解" §6 lists among the
+ *   pretraining tasks; the pages give no rule of their own for it.
+ * Errors: LF_ERR_INVALID_ARG (h == NULL or unknown mode); the mode is unchanged.
+ */
+lf_status lf_attn_set_window_mode(lf_attn_t h, int mode);
 
 /* Free the handle and its device workspace.  NULL is a no-op.  Waits for the
  * device before freeing (hipFree semantics). */

@@ -205,7 +205,8 @@ def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
     return total
 
 
-def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_idx=None, key_pad_mask=None):
+def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
+                          causal: bool = False):
     """Oracle for the variant with separate global projections.  float64 [B, H, L, d].
 
     Rows not in the global set: ``attention(q, k, v, ...)``.  A global row g:
@@ -213,7 +214,7 @@ def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_i
     (page "基于Block-Sparse Attention的Longformer" §4, global attention with its own
     projections; every global row sees every position, §2).
     """
-    out = attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask)
+    out = attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask, causal=causal)
     G = global_set(global_idx)
     if G.size == 0:
         return out
@@ -224,6 +225,8 @@ def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_i
         keep = np.ones((G.size, L), dtype=bool)
         if pad is not None:
             keep &= ~pad[b][None, :]
+        if causal:
+            keep &= np.arange(L)[None, :] <= G[:, None]
         for h in range(H):
             o, _ = _attention_rows(q_g[b, h][G], k_g[b, h], v_g[b, h], keep)
             out[b, h][G] = o

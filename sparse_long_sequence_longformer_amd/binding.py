@@ -17,6 +17,8 @@ LIBRARY_NAME = "liblfattn.so"
 LF_OK = 0
 LF_F32 = 0
 LF_BF16 = 1
+LF_WINDOW_SYMMETRIC = 0
+LF_WINDOW_CAUSAL = 1
 N_STAGES = 6
 STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge")
 MAX_HEADS = 64
@@ -33,6 +35,7 @@ EXPORTS = (
     "lf_attn_status_string",
     "lf_attn_last_error",
     "lf_attn_set_stage_timing",
+    "lf_attn_set_window_mode",
     "lf_attn_stage_times",
 )
 
@@ -83,6 +86,8 @@ def load_library():
     lib.lf_attn_status_string.restype = ctypes.c_char_p
     lib.lf_attn_last_error.argtypes = [vp]
     lib.lf_attn_last_error.restype = ctypes.c_char_p
+    lib.lf_attn_set_window_mode.argtypes = [vp, i32]
+    lib.lf_attn_set_window_mode.restype = i32
     lib.lf_attn_set_stage_timing.argtypes = [vp, i32]
     lib.lf_attn_set_stage_timing.restype = i32
     lib.lf_attn_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -108,6 +113,7 @@ class LfAttn:
         st = self.lib.lf_attn_create(ctypes.byref(h), code)
         self._check(st, h)
         self.handle = h
+        self.causal = False
 
     def _check(self, st, h=None):
         if st != LF_OK:
@@ -164,6 +170,12 @@ class LfAttn:
                                        dk_ptr, dv_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
+    def set_causal(self, causal: bool):
+        """One-sided (causal) variant for every later call on this handle."""
+        mode = LF_WINDOW_CAUSAL if causal else LF_WINDOW_SYMMETRIC
+        self._check(self.lib.lf_attn_set_window_mode(self.handle, mode), self.handle)
+        self.causal = bool(causal)
+
     def set_stage_timing(self, enable: bool):
         self._check(self.lib.lf_attn_set_stage_timing(self.handle, 1 if enable else 0), self.handle)
 
@@ -188,13 +200,17 @@ class LfAttn:
 _handles: dict = {}
 
 
-def _handle_for(dtype: str) -> LfAttn:
-    if dtype not in _handles:
-        _handles[dtype] = LfAttn(dtype)
-    return _handles[dtype]
+def _handle_for(dtype: str, causal: bool = False) -> LfAttn:
+    key = (dtype, bool(causal))
+    if key not in _handles:
+        h = LfAttn(dtype)
+        if causal:
+            h.set_causal(True)
+        _handles[key] = h
+    return _handles[key]
 
 
-def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle):
+def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=False):
     """Checks shared by both entry points; returns (B, H, L, d_h, dilation list,
     global list, pad pointer, out, handle, stream)."""
     import torch
@@ -234,26 +250,31 @@ def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle):
         out = torch.empty_like(q)
     elif out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous device tensor like q")
-    h = handle if handle is not None else _handle_for(dt)
+    h = handle if handle is not None else _handle_for(dt, causal)
     if h.dtype != dt:
         raise ValueError("handle dtype does not match the inputs")
+    if h.causal != bool(causal):
+        raise ValueError("handle window mode does not match causal=")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     return B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream
 
 
-def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None):
+def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None,
+            causal: bool = False):
     """Longformer window + global attention forward on the GPU.
 
     q, k, v: contiguous CUDA/HIP tensors [B, H, L, 64], all bfloat16 or all float32.
     w: keys on each side of the window.  dil: one dilation per head (sequence or int).
     global_idx: positions attended by and attending to everything (host sequence).
     key_pad_mask: [B, L] bool/uint8 device tensor, nonzero = padded key, or None.
+    causal: the one-sided variant (no key after its query); a given handle must be in
+    the same mode.
     Returns ``out`` (allocated if not given), same shape and dtype as q.
     """
     import torch
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
-        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle)
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal)
     with torch.cuda.device(q.device):
         h.forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
                       global_idx, pad_ptr, stream)
@@ -261,7 +282,7 @@ def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, 
 
 
 def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, key_pad_mask=None, out=None,
-                        handle: LfAttn | None = None):
+                        handle: LfAttn | None = None, causal: bool = False):
     """As ``forward``, but the global query rows attend every unpadded key with their
     own projections q_g, k_g, v_g (tensors shaped and typed like q); every other row
     uses q, k, v."""
@@ -269,7 +290,7 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
         q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)], w, dil, global_idx,
-        key_pad_mask, out, handle)
+        key_pad_mask, out, handle, causal)
     with torch.cuda.device(q.device):
         h.forward_global_proj_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_g.data_ptr(), k_g.data_ptr(),
                                   v_g.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil, global_idx,
@@ -278,13 +299,13 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
 
 
 def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, lse=None,
-                handle: LfAttn | None = None):
+                handle: LfAttn | None = None, causal: bool = False):
     """``forward`` that also returns each row's log-sum-exp: (out, lse), lse a float32
     device tensor [B, H, L] (natural log, -inf for rows without keys)."""
     import torch
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
-        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle)
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal)
     if lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
@@ -296,7 +317,7 @@ def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=No
 
 
 def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask=None, dq=None, dk=None,
-             dv=None, handle: LfAttn | None = None):
+             dv=None, handle: LfAttn | None = None, causal: bool = False):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dout``.
 
     q, k, v, out, dout: contiguous bf16 device tensors [B, H, L, 64]; ``out`` and
@@ -307,7 +328,8 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
     if q.dtype != torch.bfloat16:
         raise TypeError("the backward supports bfloat16 tensors only")
     B, H, L, d_h, dil, global_idx, pad_ptr, _, h, stream = _marshal(
-        q, [("k", k), ("v", v), ("out", out), ("dout", dout)], w, dil, global_idx, key_pad_mask, out, handle)
+        q, [("k", k), ("v", v), ("out", out), ("dout", dout)], w, dil, global_idx, key_pad_mask, out, handle,
+        causal)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
     res = []

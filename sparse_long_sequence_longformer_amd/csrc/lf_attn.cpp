@@ -28,6 +28,7 @@ struct TimedLaunch {
 
 struct lf_attn_s {
     lf_dtype dtype;
+    int window_mode = LF_WINDOW_SYMMETRIC;
     int device = -1;
     char* ws = nullptr;  // global-row partials of the forward
     size_t ws_bytes = 0;
@@ -126,6 +127,15 @@ lf_status lf_attn_destroy(lf_attn_t h) {
     for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
     delete h;
     return st;
+}
+
+lf_status lf_attn_set_window_mode(lf_attn_t h, int mode) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (mode != LF_WINDOW_SYMMETRIC && mode != LF_WINDOW_CAUSAL)
+        return fail(h, LF_ERR_INVALID_ARG, "unknown window mode %d", mode);
+    h->window_mode = mode;
+    return LF_OK;
 }
 
 lf_status lf_attn_set_stage_timing(lf_attn_t h, int enable) {
@@ -305,6 +315,7 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     p.n_gblk = pl.n_gblk;
     p.rows_per_block = lf::kRowsPerBlock;
     p.tiles_per_head = pl.tiles;
+    p.causal = h->window_mode == LF_WINDOW_CAUSAL;
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
@@ -374,6 +385,7 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     std::copy(pl.g.begin(), pl.g.end(), p.g);
     p.n_gblk = pl.n_gblk;
     p.tiles_per_head = pl.tiles;
+    p.causal = h->window_mode == LF_WINDOW_CAUSAL;
 
     // Workspace: three row-statistic arrays, then the global partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");

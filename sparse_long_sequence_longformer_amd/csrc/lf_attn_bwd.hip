@@ -45,6 +45,8 @@
 namespace lf {
 namespace {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPosInf = __builtin_inff();
 constexpr int kBwdMaskWindow = 64;
@@ -197,6 +199,15 @@ __device__ __forceinline__ f32x16 row_seed(const char* arr, int sub, int h2) {
     return s;
 }
 
+// Bits lo..31 of a word (lo may lie outside 0..31).
+__device__ __forceinline__ uint32_t bits_from(int lo) {
+    return lo <= 0 ? ~0u : (lo >= 32 ? 0u : (~0u << lo));
+}
+// Bits 0..hi-1 of a word (hi may lie outside 0..32).
+__device__ __forceinline__ uint32_t bits_below(int hi) {
+    return hi <= 0 ? 0u : (hi >= 32 ? ~0u : ((1u << hi) - 1u));
+}
+
 __device__ __forceinline__ f32x16 splat(float x) {
     f32x16 s;
     for (int i = 0; i < 16; ++i) s[i] = x;
@@ -230,10 +241,10 @@ __device__ __forceinline__ void wave_sum_store(float* red, const f32x16* a, int 
 }
 
 // The work-group's tile: 128 own rows [r0, r0 + 128) of residue class r of one
-// (b, h), and the other side's rows [kb0, kend) of the same class (everything within
-// w of an own row) in 64-row stages on a grid aligned to r0: nb stages before the
-// own rows, the two "home" stages [r0, r0 + 128), na stages after, processed in the
-// order before, after, home.
+// (b, h), and the other side's rows [kb0, kend) of the same class (every row whose
+// offset from an own row, other - own, lies in [-A, B]) in 64-row stages on a grid
+// aligned to r0: nb stages before the own rows, the two "home" stages
+// [r0, r0 + 128), na stages after, processed in the order before, after, home.
 struct Tile {
     int bh, b, h, t_in, r, dil, Lr, r0, kb0, kend, nb, na, n_band, gbase;
     __device__ int stage_row(int u) const {
@@ -241,7 +252,7 @@ struct Tile {
         return gbase + kStageKeys * bs;
     }
 };
-__device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p) {
+__device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int A, int B) {
     const int pid = xcd_remap(blockIdx.x, gridDim.x);
     t.bh = pid / p.tiles_per_head;
     t.t_in = pid - t.bh * p.tiles_per_head;
@@ -254,8 +265,8 @@ __device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p) {
     t.Lr = (p.L - t.r + t.dil - 1) / t.dil;
     t.r0 = (t.t_in - t.r * tpr) * kRowsPerBlock;
     if (t.r0 >= t.Lr) return false;
-    t.kb0 = max(0, t.r0 - p.w);
-    t.kend = min(t.Lr, t.r0 + kRowsPerBlock + p.w);
+    t.kb0 = max(0, t.r0 - A);
+    t.kend = min(t.Lr, t.r0 + kRowsPerBlock + B);
     t.nb = (t.r0 - t.kb0 + kStageKeys - 1) / kStageKeys;
     t.gbase = t.r0 - kStageKeys * t.nb;
     t.na = max(0, (t.kend - (t.r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
@@ -298,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // rows r0 + 32*wv .. +31, one per lane (both lane halves).  Stages: the global keys
 // (with the in-window test, so each key counts once), then the window band.
 
+template <bool kCausal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
@@ -305,11 +317,15 @@ void bwd_dq_kernel(const BwdParams p) {
     __shared__ uint64_t glob_mask[kBwdMaxGlobalStages];
     __shared__ int glob_src[LF_MAX_GLOBALS];
     __shared__ __attribute__((aligned(16))) int glob_pos[LF_MAX_GLOBALS];
+    __shared__ int glob_abs[LF_MAX_GLOBALS];
     __shared__ int glob_row[LF_MAX_GLOBALS];
     __shared__ uint32_t row_glob[kRowsPerBlock / 32];
 
+    // Keys of a row: w class steps before it and wr after (wr = 0 one-sided).
+    constexpr bool causal = kCausal;
+    const int wr = causal ? 0 : p.w, span = p.w + wr;
     Tile tl;
-    if (!tile_of(tl, p)) return;
+    if (!tile_of(tl, p, p.w, wr)) return;
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
@@ -378,6 +394,7 @@ void bwd_dq_kernel(const BwdParams p) {
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
         glob_pos[gi] = ok ? vpos : kNoPos;
+        glob_abs[gi] = g;
         glob_row[gi] = vpos;
     }
     if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
@@ -394,6 +411,8 @@ void bwd_dq_kernel(const BwdParams p) {
     }
     __syncthreads();
 
+    // One-sided variant: the global slots at or before this lane's row.
+    const int gcnt = causal ? count_le(glob_abs, p.n_g, row) : 0;
     Lanes lo;
     lane_setup(lo, lane);
     if (n_st > 0) issue(0);
@@ -421,12 +440,13 @@ void bwd_dq_kernel(const BwdParams p) {
             const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
             const int kss = ks + 32 * sub;
             if (inv32 == ~0u) continue;
-            if (!gstage && (kss > qa + 31 + w || kss + 31 < qa - w)) continue;
-            const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + w;
+            if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) continue;
+            const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
             const int mode = gstage ? 2 : (interior ? 0 : 1);
             f32x16 s = prod(slot, sub, lo, qop, seed_s);  // scores - lse, base 2
-            mask_scores(s, mode, inv32, h2, kss + 8 * h2 - qv + w, w, glob_pos + kStageKeys * t + 32 * sub + 8 * h2,
-                        w - qv);
+            const int goff = kStageKeys * t + 32 * sub + 8 * h2;
+            mask_scores(s, mode, inv32, h2, kss + 8 * h2 - qv + w, span, glob_pos + goff, w - qv,
+                        causal ? gcnt - goff : 1 << 30);
             const f32x16 dp = prod(slot + kTileB, sub, lo, dop, seed_d);  // dO.V - D
             float ds[16];
             for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
@@ -489,7 +509,13 @@ void bwd_dq_kernel(const BwdParams p) {
         f32x16 gacc[2] = {f32x16{}, f32x16{}};
         if (inv32 != ~0u) {
             f32x16 s = prod(hslot, hsub, lo, gop, splat(-gl));
-            mask_scores(s, inv32 != 0u ? 1 : 0, inv32, h2, 0, kLargeW, nullptr, 0);
+            if (causal) {  // keys of this class at or before the global row
+                const int vlim = g >= r ? (g - r) / dil : -1;
+                const int kss = r0 + kStageKeys * hs + 32 * hsub;
+                mask_scores(s, 1, inv32, h2, kss + 8 * h2 - vlim + kLargeW, kLargeW, nullptr, 0);
+            } else {
+                mask_scores(s, inv32 != 0u ? 1 : 0, inv32, h2, 0, 2 * kLargeW, nullptr, 0);
+            }
             const f32x16 dp = prod(hslot + kTileB, hsub, lo, gdo, splat(-gd));
             float ds[16];
             for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
@@ -512,13 +538,19 @@ void bwd_dq_kernel(const BwdParams p) {
 // unpadded key is theirs), then the window band of queries (global queries are
 // removed there by lse2_band = +inf: their weights are 0).
 
+template <bool kCausal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkv_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ int own_gidx[kRowsPerBlock];  // index in g of each own key, or -1
+    __shared__ int gq_pos[LF_MAX_GLOBALS];  // position of each global slot (sorted)
 
+    // Queries of a key: query - key in [-wl, w] class steps (wl = 0 one-sided: no query
+    // before its key).
+    constexpr bool causal = kCausal;
+    const int wl = causal ? 0 : p.w, span = wl + p.w;
     Tile tl;
-    if (!tile_of(tl, p)) return;
+    if (!tile_of(tl, p, wl, p.w)) return;
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
@@ -565,6 +597,7 @@ void bwd_dkv_kernel(const BwdParams p) {
     };
 
     if (tid < kRowsPerBlock) own_gidx[tid] = -1;
+    for (int gi = tid; gi < p.n_g; gi += kThreads) gq_pos[gi] = p.g[gi];
     __syncthreads();
     for (int gi = tid; gi < p.n_g; gi += kThreads) {
         const int g = p.g[gi];
@@ -575,6 +608,9 @@ void bwd_dkv_kernel(const BwdParams p) {
     }
     __syncthreads();
 
+    // One-sided variant: the first global slot at or after this lane's key (the
+    // global queries that see it; slots are sorted by position).
+    const int gfirst = causal ? count_le(gq_pos, p.n_g, krow - 1) : 0;
     Lanes lo;
     lane_setup(lo, lane);
     if (n_st > 0) issue(0);
@@ -594,13 +630,18 @@ void bwd_dkv_kernel(const BwdParams p) {
             if (gstage) {
                 if (kss >= p.n_g) continue;
             } else {
-                if (kss > qa + 31 + w || kss + 31 < qa - w) continue;  // outside every own key's window
-                if (kss >= tl.kend || kss + 31 < tl.kb0) continue;     // no valid query
+                if (kss > qa + 31 + w || kss + 31 < qa - wl) continue;  // outside every own key's window
+                if (kss >= tl.kend || kss + 31 < tl.kb0) continue;      // no valid query
             }
-            const bool interior = !gstage && kss >= qa + 31 - w && kss + 31 <= qa + w;
+            const bool interior = !gstage && kss >= qa + 31 - wl && kss + 31 <= qa + w;
             const int mode = (gstage || interior) ? 0 : 1;
             f32x16 s = prod(slot, sub, lo, kop, row_seed(slot + kLseOff, sub, h2));  // scores - lse, base 2
-            mask_scores(s, mode, 0u, h2, kss + 8 * h2 - qv + w, w, nullptr, 0);
+            mask_scores(s, mode, 0u, h2, kss + 8 * h2 - qv + wl, span, nullptr, 0);
+            if (gstage && causal) {  // a global query sees no key after it: slots from gfirst on
+                const uint32_t keep = bits_from(gfirst - (kStageKeys * t + 32 * sub + 8 * h2));
+                for (int i = 0; i < 16; ++i)
+                    if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
+            }
             const f32x16 dp = prod(slot + kTileB, sub, lo, vop, row_seed(slot + kDOff, sub, h2));  // dO.V - D
             float pr[16], ds[16];
             for (int i = 0; i < 16; ++i) {
@@ -669,10 +710,16 @@ void bwd_dkv_kernel(const BwdParams p) {
         f32x16 gk_acc[2] = {f32x16{}, f32x16{}}, gv_acc[2] = {f32x16{}, f32x16{}};
         if (hq < Lr) {
             f32x16 s = prod(hslot, hsub, lo, kg, row_seed(hslot + kLseOff, hsub, h2));
-            for (int i = 0; i < 16; ++i) {
-                const int vi = hq + 8 * h2 + kc_of(i);
-                if (!gvalid || vi >= Lr || (unsigned)(vi - vpos + w) <= (unsigned)(2 * w)) s[i] = kNegInf;
-            }
+            // Queries kept, one bit per kc (element i holds query base + kc_of(i)): below
+            // Lr, not in the window that holds the key (those pairs are in the key's own
+            // tile), and, one-sided, not before the key.  Built as bit ranges so that the
+            // selection stays branch-free.
+            const int base = hq + 8 * h2;
+            uint32_t keep = gvalid ? bits_below(Lr - base) : 0u;
+            keep &= ~(bits_from(vpos - wl - base) & bits_below(vpos + p.w + 1 - base));
+            if (causal) keep &= bits_from((g > r ? (g - r + dil - 1) / dil : 0) - base);
+            for (int i = 0; i < 16; ++i)
+                if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
             const f32x16 dp = prod(hslot + kTileB, hsub, lo, vg, row_seed(hslot + kDOff, hsub, h2));
             float pr[16], ds[16];
             for (int i = 0; i < 16; ++i) {
@@ -750,14 +797,20 @@ hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(blocks), dim3(kThreads), 0, s, p);
+    if (p.causal)
+        hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dkv_kernel, dim3(blocks), dim3(kThreads), 0, s, p);
+    if (p.causal)
+        hipLaunchKernelGGL(bwd_dkv_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(bwd_dkv_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -121,16 +121,19 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
 // Element i of a 32-key score tile holds stage key 32*sub + kc(i) + 8*h2.
 __device__ __forceinline__ constexpr int kc_of(int i) { return 16 * (i >> 3) + (i & 7); }
 
-// Masks of a 32-key score tile.  MODE 0: none; 1: band mask, base = (first key of
-// the sub-tile) + 8*h2 - query + w; 2: global keys (gp: in-window positions of the
-// sub-tile's keys).  Invalid keys (inv32 bits) are masked in modes 1 and 2.
-__device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32, int h2, int base, int w,
-                                            const int* gp, int wq) {
+// Masks of a 32-key score tile.  MODE 0: none; 1: band, keep 0 <= base + kc <= span
+// with base = (first key of the sub-tile) + 8*h2 - query + (left extent of the
+// window); 2: global keys, masked where in the window (gp: in-window positions of the
+// sub-tile's keys, test 0 <= gp + wq <= span) and from slot kc = climit on (global
+// slots are sorted by position, so in the one-sided variant the keys after the query
+// are a suffix).  Invalid keys (inv32 bits) are masked in modes 1 and 2.
+__device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32, int h2, int base, int span,
+                                            const int* gp, int wq, int climit = 1 << 30) {
     if (mode == 0) return;
     const uint32_t invl = inv32 >> (8 * h2);
     if (mode == 1) {
-        // Band test 0 <= base + kc <= 2w as one bit range over kc, minus invalid keys.
-        const int lo_k = max(0, -base), hi_k = min(31, 2 * w - base);
+        // Band test 0 <= base + kc <= span as one bit range over kc, minus invalid keys.
+        const int lo_k = max(0, -base), hi_k = min(31, span - base);
         uint32_t keep = 0u;
         if (hi_k >= lo_k) keep = (hi_k >= 31 ? ~0u : ((2u << hi_k) - 1u)) & ~((1u << lo_k) - 1u);
         keep &= ~invl;
@@ -143,9 +146,21 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32,
         const i32x4 a[4] = {g4[0], g4[1], g4[4], g4[5]};
         for (int i = 0; i < 16; ++i) {
             const int kc = kc_of(i);
-            if (((invl >> kc) & 1) || (unsigned)(a[i >> 2][i & 3] + wq) <= (unsigned)(2 * w)) s[i] = kNegInf;
+            if (((invl >> kc) & 1) || kc >= climit || (unsigned)(a[i >> 2][i & 3] + wq) <= (unsigned)span)
+                s[i] = kNegInf;
         }
     }
+}
+
+// Number of entries of the sorted array pos[0..n) that are <= x (binary search).
+__device__ __forceinline__ int count_le(const int* pos, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pos[mid] <= x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
 }
 
 }  // namespace

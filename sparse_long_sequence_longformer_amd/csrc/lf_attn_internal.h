@@ -39,6 +39,7 @@ struct Params {
     int n_gblk;          // ceil(n_g / 32)
     int tiles_per_head;  // work-groups per (b, h), max over heads (grid partition)
     int rows_per_block;  // rows of one residue class per work-group
+    int causal;          // one-sided variant: no pair with its key after its query
     int dil[LF_MAX_HEADS];
     int g[LF_MAX_GLOBALS];          // sorted, distinct
 };
@@ -74,6 +75,7 @@ struct BwdParams {
     int n_g;
     int n_gblk;
     int tiles_per_head;
+    int causal;  // one-sided variant
     int dil[LF_MAX_HEADS];
     int g[LF_MAX_GLOBALS];  // sorted, distinct
 };

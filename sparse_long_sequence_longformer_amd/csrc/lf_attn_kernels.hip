@@ -466,11 +466,11 @@ __device__ __forceinline__ void fold_tile(State& st, const f32x16& x, typename T
 template <class T>
 __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, const typename T::Lane& lo,
                                          const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
-                                         int w, const int* gp, int wq) {
+                                         int span, const int* gp, int wq, int climit = 1 << 30) {
     f32x16 s = T::qk(slot, sub, lo, q, st.seed);  // exponents: scores - cofs
     typename T::VOp vo;
     T::load_v(vo, slot, sub, lo);  // in flight during the softmax
-    mask_scores(s, mode, inv32, h2, base, w, gp, wq);
+    mask_scores(s, mode, inv32, h2, base, span, gp, wq, climit);
     typename T::PFrag pf;
     fold_tile<T>(st, s, pf, lo);
     T::pv(vo, pf, st.o);
@@ -488,7 +488,7 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 // sub-tiles outside its rows' band and masks only sub-tiles that touch the band
 // edge or hold invalid keys.
 
-template <class T>
+template <class T, bool kCausal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const Params p) {
     using Elem = typename T::Elem;
@@ -497,6 +497,7 @@ void band_kernel(const Params p) {
     __shared__ uint64_t glob_mask[kMaxGlobalStages];  // invalid-key bits of global stages
     __shared__ int glob_src[LF_MAX_GLOBALS];          // source row of each global slot or -1
     __shared__ __attribute__((aligned(16))) int glob_pos[LF_MAX_GLOBALS];  // same-class virtual position or kNoPos
+    __shared__ int glob_abs[LF_MAX_GLOBALS];          // position of each global slot (sorted)
     __shared__ int glob_row[LF_MAX_GLOBALS];          // same as glob_pos, padded or not
     __shared__ int glob_g[kGlobalQueriesPerBlock];    // first 32 global positions (or -1)
     __shared__ uint32_t row_glob[kRowsPerBlock / 32]; // tile rows that are global queries
@@ -533,8 +534,13 @@ void band_kernel(const Params p) {
     typename T::QOp qop;
     T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * 64 : nullptr, h2);
 
+    // Window of a row: keys w steps before it and wr after (wr = 0 in the one-sided
+    // variant, which also drops global keys after the row and, for a global row,
+    // every key after it).
+    constexpr bool causal = kCausal;
+    const int wr = causal ? 0 : w, span = w + wr;
     const int kb0 = max(0, r0 - w);
-    const int kend = min(Lr, r0 + kRowsPerBlock + w);
+    const int kend = min(Lr, r0 + kRowsPerBlock + wr);
     const int nb = (r0 - kb0 + kStageKeys - 1) / kStageKeys;  // stages before the home keys
     const int gbase = r0 - kStageKeys * nb;                    // first key of the grid (<= kb0)
     const int na = max(0, (kend - (r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
@@ -599,6 +605,7 @@ void band_kernel(const Params p) {
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
         glob_pos[gi] = ok ? vpos : kNoPos;
+        glob_abs[gi] = g;
         glob_row[gi] = vpos;
         if (gi < kGlobalQueriesPerBlock) glob_g[gi] = g;
     }
@@ -632,6 +639,8 @@ void band_kernel(const Params p) {
         if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
     }
     __syncthreads();
+    // One-sided variant: the global slots at or before this lane's row.
+    const int gcnt = causal ? count_le(glob_abs, p.n_g, r + qv * dil) : 0;
 
     State st;
     state_init(st);
@@ -676,11 +685,12 @@ void band_kernel(const Params p) {
                 const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
                 const int kss = ks + 32 * sub;
                 if (inv32 == ~0u) continue;
-                if (!gstage && (kss > qa + 31 + w || kss + 31 < qa - w)) continue;  // outside every row's band
-                const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + w;
+                if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) continue;  // outside every row's band
+                const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
                 const int mode = gstage ? 2 : (interior ? 0 : 1);
-                sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, kss + 8 * h2 - qv + w, w,
-                            glob_pos + kStageKeys * gidx + 32 * sub + 8 * h2, w - qv);
+                const int goff = kStageKeys * gidx + 32 * sub + 8 * h2;
+                sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, kss + 8 * h2 - qv + w, span, glob_pos + goff,
+                            w - qv, causal ? gcnt - goff : 1 << 30);
             }
         }
     }
@@ -744,8 +754,18 @@ void band_kernel(const Params p) {
         }
         State gs;
         state_init(gs);
-        if (inv32 != ~0u)
-            sub_step<T>(gs, hslot, hsub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0, kLargeW, nullptr, 0);
+        if (inv32 != ~0u) {
+            if (causal) {
+                // keys of this class at or before the global row: virtual index <= vlim
+                const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
+                const int g = gq < p.n_g ? p.g[gq] : -1;
+                const int vlim = g >= r ? (g - r) / dil : -1;
+                const int kss = r0 + kStageKeys * hs + 32 * hsub;
+                sub_step<T>(gs, hslot, hsub, lo, gop, 1, inv32, h2, kss + 8 * h2 - vlim + kLargeW, kLargeW, nullptr, 0);
+            } else {
+                sub_step<T>(gs, hslot, hsub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0, 2 * kLargeW, nullptr, 0);
+            }
+        }
         __syncthreads();  // done with the staged keys: the ring now holds the reduction
         if (lane < 32) {  // partial relative to cofs (= mc, or nothing when mc = -inf)
             red_ml[wv][lane][0] = gs.mc;
@@ -851,10 +871,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-    if (dtype == LF_BF16)
-        hipLaunchKernelGGL(band_kernel<Bf16>, dim3(blocks), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(band_kernel<F32>, dim3(blocks), dim3(kThreads), 0, s, p);
+    if (dtype == LF_BF16) {
+        if (p.causal)
+            hipLaunchKernelGGL((band_kernel<Bf16, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL((band_kernel<Bf16, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+    } else {
+        if (p.causal)
+            hipLaunchKernelGGL((band_kernel<F32, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL((band_kernel<F32, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -172,6 +172,21 @@ def test_backward_host_validation():
 
 
 @needs_lib
+def test_window_mode():
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        assert lib.lf_attn_set_window_mode(h, binding.LF_WINDOW_CAUSAL) == 0
+        assert lib.lf_attn_set_window_mode(h, binding.LF_WINDOW_SYMMETRIC) == 0
+        assert lib.lf_attn_set_window_mode(h, 7) == 1
+        assert b"window mode" in lib.lf_attn_last_error(h)
+        assert lib.lf_attn_set_window_mode(None, 0) == 1
+    finally:
+        lib.lf_attn_destroy(h)
+
+
+@needs_lib
 def test_null_handle():
     lib = binding.load_library()
     assert lib.lf_attn_forward(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None, None, 0, None, None) == 1
