@@ -5,6 +5,7 @@ Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
 library and never imports it.
 """
 
+from . import layer_oracle  # noqa: F401
 from .longformer_oracle import (  # noqa: F401
     attention,
     attention_backward,

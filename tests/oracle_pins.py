@@ -531,6 +531,74 @@ def pin_causal_backward_autograd():
             assert err < 1e-12, (name, L, w, dil, G, padk, err)
 
 
+# ------------------------------------------------------------- the layer
+
+def _layer_weights(E, F, seed, scale=0.05):
+    rng = np.random.default_rng(seed)
+    W = {
+        "w_qkv": rng.standard_normal((3 * E, E)) * scale, "b_qkv": rng.standard_normal(3 * E) * scale,
+        "w_o": rng.standard_normal((E, E)) * scale, "b_o": rng.standard_normal(E) * scale,
+        "ln1_g": 1.0 + rng.standard_normal(E) * 0.1, "ln1_b": rng.standard_normal(E) * 0.1,
+        "w_1": rng.standard_normal((F, E)) * scale, "b_1": rng.standard_normal(F) * scale,
+        "w_2": rng.standard_normal((E, F)) * scale, "b_2": rng.standard_normal(E) * scale,
+        "ln2_g": 1.0 + rng.standard_normal(E) * 0.1, "ln2_b": rng.standard_normal(E) * 0.1,
+    }
+    return W
+
+
+def pin_layer_torch_encoder():
+    """Full-attention limit (w >= L, no globals, dil = 1): the layer equals torch's
+    nn.TransformerEncoderLayer (post-LayerNorm, GELU, no dropout) in float64 with the
+    same weights, with and without key padding."""
+    from oracle import layer_oracle as lo
+
+    B, L, H, F = 2, 40, 2, 96
+    E = 64 * H
+    W = _layer_weights(E, F, 500)
+    x = _rand((B, L, E), 501)
+    enc = torch.nn.TransformerEncoderLayer(E, H, dim_feedforward=F, dropout=0.0, activation="gelu",
+                                           batch_first=True, norm_first=False, dtype=torch.float64)
+    with torch.no_grad():
+        enc.self_attn.in_proj_weight.copy_(torch.from_numpy(W["w_qkv"]))
+        enc.self_attn.in_proj_bias.copy_(torch.from_numpy(W["b_qkv"]))
+        enc.self_attn.out_proj.weight.copy_(torch.from_numpy(W["w_o"]))
+        enc.self_attn.out_proj.bias.copy_(torch.from_numpy(W["b_o"]))
+        enc.linear1.weight.copy_(torch.from_numpy(W["w_1"]))
+        enc.linear1.bias.copy_(torch.from_numpy(W["b_1"]))
+        enc.linear2.weight.copy_(torch.from_numpy(W["w_2"]))
+        enc.linear2.bias.copy_(torch.from_numpy(W["b_2"]))
+        enc.norm1.weight.copy_(torch.from_numpy(W["ln1_g"]))
+        enc.norm1.bias.copy_(torch.from_numpy(W["ln1_b"]))
+        enc.norm2.weight.copy_(torch.from_numpy(W["ln2_g"]))
+        enc.norm2.bias.copy_(torch.from_numpy(W["ln2_b"]))
+    enc.eval()
+    pad = np.zeros((B, L), dtype=bool)
+    pad[1, 30:] = True
+    for mask in (None, pad):
+        with torch.no_grad():
+            ref = enc(torch.from_numpy(x), src_key_padding_mask=None if mask is None else torch.from_numpy(mask))
+        got = lo.layer_forward(x, W, H, L, [1] * H, None, mask)
+        assert np.abs(got - ref.numpy()).max() < 1e-10
+
+
+def pin_layer_norm_rows():
+    """With unit gains and zero shifts every output row has mean 0 and variance
+    1 / (1 + eps / var): LayerNorm's own definition, checked on the layer output."""
+    from oracle import layer_oracle as lo
+
+    B, L, H, F = 1, 30, 1, 64
+    E = 64 * H
+    W = _layer_weights(E, F, 510)
+    for n in ("ln1_g", "ln2_g"):
+        W[n] = np.ones(E)
+    for n in ("ln1_b", "ln2_b"):
+        W[n] = np.zeros(E)
+    x = _rand((B, L, E), 511)
+    out = lo.layer_forward(x, W, H, 5, [2], [3], None, eps=0.0)
+    assert np.abs(out.mean(axis=-1)).max() < 1e-12
+    assert np.abs(out.var(axis=-1) - 1.0).max() < 1e-12
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -559,4 +627,6 @@ ALL_PINS = [
     pin_causal_textbook,
     pin_causal_prefix,
     pin_causal_backward_autograd,
+    pin_layer_torch_encoder,
+    pin_layer_norm_rows,
 ]

@@ -183,6 +183,26 @@ def _mask_causal_strict(L, w, dil, G, pad_row, rows, causal=False):  # self excl
     return m
 
 
+from oracle import layer_oracle as _lo  # noqa: E402
+
+_orig_ln = _lo.layer_norm
+
+
+def _ln_unbiased(y, gamma, beta, eps):  # sample variance (n - 1) instead of the biased one
+    mu = y.mean(axis=-1, keepdims=True)
+    var = ((y - mu) ** 2).sum(axis=-1, keepdims=True) / (y.shape[-1] - 1)
+    return (y - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def _gelu_tanh(t):  # the tanh approximation of GELU
+    return 0.5 * t * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (t + 0.044715 * t ** 3)))
+
+
+def _split_interleaved(t, H):  # head h takes every H-th feature
+    B, L, E = t.shape
+    return t.reshape(B, L, E // H, H).transpose(0, 3, 1, 2)
+
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -202,6 +222,9 @@ MUTANTS = {
     "global_proj_uses_k": ("attention_global_proj", _gp_uses_k),
     "global_proj_uses_q": ("attention_global_proj", _gp_uses_q),
     "global_proj_uses_v": ("attention_global_proj", _gp_uses_v),
+    "layer_ln_unbiased": ("layer:layer_norm", _ln_unbiased),
+    "layer_gelu_tanh": ("layer:gelu", _gelu_tanh),
+    "layer_heads_interleaved": ("layer:split_heads", _split_interleaved),
     "bwd_no_delta": ("attention_backward_bh", _bwd_mutant("no_delta")),
     "bwd_delta_from_dp": ("attention_backward_bh", _bwd_mutant("delta_from_dp")),
     "bwd_dk_unscaled": ("attention_backward_bh", _bwd_mutant("dk_unscaled")),
@@ -213,7 +236,10 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    monkeypatch.setattr(orc, attr, fn)
+    if attr.startswith("layer:"):
+        monkeypatch.setattr(_lo, attr[len("layer:"):], fn)
+    else:
+        monkeypatch.setattr(orc, attr, fn)
     caught = []
     for pin in P.ALL_PINS:
         try:
