@@ -59,6 +59,9 @@ def parse():
                     help="global rows use their own q/k/v projections (lf_attn_forward_global_proj)")
     ap.add_argument("--causal", action="store_true",
                     help="one-sided variant: no pair with its key after its query")
+    ap.add_argument("--layer", action="store_true",
+                    help="time one whole layer (projections, attention, LayerNorms, GELU feed-forward)")
+    ap.add_argument("--ffn", type=int, default=3072, help="feed-forward width of --layer")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (lf_attn_backward) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,6 +177,8 @@ def main():
         def step():
             binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle, causal=args.causal)
 
+    if args.layer:
+        return bench_layer(args, wl, name, padd, G, dil, flops, handle)
     if args.backward:
         if wl.dtype != "bf16":
             print("bench.py: the backward runs on bf16 workloads only", file=sys.stderr)
@@ -247,6 +252,77 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
+    """One layer on the workload's shape (hidden = 64 * H) with seeded synthetic
+    weights: the four GEMMs (rocBLAS), the attention and the pointwise passes."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from sparse_long_sequence_longformer_amd import binding
+
+    E, F = 64 * wl.H, args.ffn
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(rng.standard_normal((wl.B, wl.L, E), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    shapes = {"w_qkv": (3 * E, E), "b_qkv": (3 * E,), "w_o": (E, E), "b_o": (E,), "ln1_g": (E,), "ln1_b": (E,),
+              "w_1": (F, E), "b_1": (F,), "w_2": (E, F), "b_2": (E,), "ln2_g": (E,), "ln2_b": (E,)}
+    W = {k: (torch.from_numpy(rng.standard_normal(sh, dtype=np.float32) * 0.05) + (1.0 if k.endswith("_g") else 0.0))
+         .to(torch.bfloat16).to(dev) for k, sh in shapes.items()}
+    out = binding.layer_forward(x, W, wl.w, dil, G, padd, handle=handle, causal=args.causal)
+    torch.cuda.synchronize()
+    lib = binding.load_library()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    dil_arr = (ctypes.c_int32 * len(dil))(*dil)
+    g_arr = (ctypes.c_int32 * max(1, len(G)))(*G)
+    wts = binding.LayerWeights(*[W[n].data_ptr() for n in binding.LAYER_WEIGHTS])
+    args_c = (handle.handle, x.data_ptr(), ctypes.byref(wts), out.data_ptr(), wl.B, wl.L, E, F, ctypes.c_float(1e-5),
+              wl.w, ctypes.cast(dil_arr, i32p), ctypes.cast(g_arr, i32p), len(G),
+              None if padd is None else padd.data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        if lib.lf_layer_forward(*args_c) != 0:
+            raise RuntimeError(lib.lf_attn_last_error(handle.handle).decode())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    handle.set_stage_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    st = handle.stage_times()
+    handle.set_stage_timing(False)
+    per_call = {k2: v2[0] / args.steps for k2, v2 in st.items() if v2[1]}
+    R = wl.B * wl.L
+    gemm_flops = 2.0 * R * (3 * E * E + E * E + 2 * E * F)
+    total = gemm_flops + flops_attn
+    res = {
+        "metric": "Longformer layer fwd effective TFLOP/s (GEMMs + window+global attention), L=4096 w=512",
+        "value": round(total / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0, 0.05^2) weights)",
+        "config": {"workload": name, "B": wl.B, "seq_len": wl.L, "hidden": E, "heads": wl.H, "ffn": F, "w": wl.w,
+                   "n_global": len(G), "parallelism": "single GPU",
+                   "window": "one-sided" if args.causal else "symmetric"},
+        "tokens_per_s": round(R / (ms * 1e-3), 1),
+        "gemm_flop": gemm_flops, "attention_flop": flops_attn,
+        "stage_ms_per_layer": {k2: round(v2, 6) for k2, v2 in per_call.items()},
+        "gemm_tflops": round(gemm_flops / (per_call.get("layer_gemm", float("nan")) * 1e-3) / 1e12, 3),
+    }
     print(json.dumps(res), flush=True)
 
 

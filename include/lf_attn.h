@@ -52,13 +52,15 @@ typedef enum lf_dtype {
 #define LF_HEAD_DIM 64
 
 /* Kernel launches timed by lf_attn_stage_times. */
-#define LF_N_STAGES 6
+#define LF_N_STAGES 8
 #define LF_STAGE_BAND 0      /* window band, global-column fold, global-row partials */
 #define LF_STAGE_MERGE 1     /* log-sum-exp merge of the partials (only with globals) */
 #define LF_STAGE_BWD_PREP 2  /* backward: D = rowsum(dO * O), base-2 log-sum-exp */
 #define LF_STAGE_BWD_DQ 3    /* backward: dQ (row-owned), global-row partials */
 #define LF_STAGE_BWD_DKV 4   /* backward: dK, dV (key-owned), global-key partials */
 #define LF_STAGE_BWD_MERGE 5 /* backward: sums of the global partials (only with globals) */
+#define LF_STAGE_LAYER_GEMM 6      /* layer: the four projection / feed-forward GEMMs (rocBLAS) */
+#define LF_STAGE_LAYER_POINTWISE 7 /* layer: head split and merge, LayerNorms, GELU */
 
 /* Pattern variants (lf_attn_set_window_mode). */
 #define LF_WINDOW_SYMMETRIC 0 /* keys i + m*dil, m = -w..w (default) */
@@ -187,6 +189,57 @@ lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k,
  * Errors: LF_ERR_INVALID_ARG (h == NULL or unknown mode); the mode is unchanged.
  */
 lf_status lf_attn_set_window_mode(lf_attn_t h, int mode);
+
+/*
+ * One Longformer layer around the attention (bf16 handles only):
+ *
+ *   q, k, v = split_heads(x W_qkv^T + b_qkv)     (rows of W_qkv: q, then k, then v;
+ *                                                 head h = features 64h .. 64h+63)
+ *   a       = merge_heads(attention(q, k, v))    (this library's forward, with the
+ *                                                 handle's window mode)
+ *   x1      = LayerNorm1(x + a W_o^T + b_o)
+ *   out     = LayerNorm2(x1 + GELU(x1 W_1^T + b_1) W_2^T + b_2)
+ *
+ * LayerNorm over the features with the biased variance and eps = ln_eps;
+ * GELU(t) = 0.5 t (1 + erf(t / sqrt(2))).  The order of the steps is the layer of
+ * page "基于Block-Sparse Attention的Longformer" §6 (attention, residual, LayerNorm,
+ * feed-forward, residual, LayerNorm); the projections and the GELU feed-forward are
+ * RoBERTa's, whose weights page "基于自注意力机制的长文本建模算法：Longformer详解"
+ * §6 says Longformer starts from.
+ *
+ * x, out : DEVICE bf16 [B][L][hidden], 16-byte aligned, not overlapping.
+ * wts    : HOST struct of DEVICE bf16 pointers (16-byte aligned), nn.Linear layout
+ *          (weight [out][in]): w_qkv [3*hidden][hidden], b_qkv [3*hidden],
+ *          w_o [hidden][hidden], b_o, ln1_g, ln1_b [hidden], w_1 [ffn][hidden],
+ *          b_1 [ffn], w_2 [hidden][ffn], b_2, ln2_g, ln2_b [hidden].
+ * hidden : 64 * heads, heads <= LF_MAX_HEADS, hidden <= 2048.
+ * ffn    : feed-forward width, a positive multiple of 8.
+ * w, dil_per_head (one per head), global_idx, n_global, key_pad_mask [B][L]: as
+ * lf_attn_forward.
+ * GEMMs run in rocBLAS (bf16 inputs, fp32 accumulation and output); the handle
+ * owns a rocBLAS handle and a third device workspace for the intermediates
+ * (about (12 * hidden + 6 * ffn) bytes per token).  Errors: as lf_attn_forward;
+ * LF_ERR_UNSUPPORTED for fp32 handles or unsupported sizes.
+ */
+typedef struct lf_layer_weights {
+    const void* w_qkv;
+    const void* b_qkv;
+    const void* w_o;
+    const void* b_o;
+    const void* ln1_g;
+    const void* ln1_b;
+    const void* w_1;
+    const void* b_1;
+    const void* w_2;
+    const void* b_2;
+    const void* ln2_g;
+    const void* ln2_b;
+} lf_layer_weights;
+
+lf_status lf_layer_forward(lf_attn_t h, const void* x, const lf_layer_weights* wts, void* out, int B, int L,
+                           int hidden, int ffn, float ln_eps, int w, const int32_t* dil_per_head,
+                           const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
+                           void* stream);
 
 /* Free the handle and its device workspace.  NULL is a no-op.  Waits for the
  * device before freeing (hipFree semantics). */

@@ -19,8 +19,9 @@ LF_F32 = 0
 LF_BF16 = 1
 LF_WINDOW_SYMMETRIC = 0
 LF_WINDOW_CAUSAL = 1
-N_STAGES = 6
-STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge")
+N_STAGES = 8
+STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge", "layer_gemm", "layer_pointwise")
+LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
 MAX_HEADS = 64
 MAX_GLOBALS = 256
 
@@ -31,6 +32,7 @@ EXPORTS = (
     "lf_attn_forward_global_proj",
     "lf_attn_forward_lse",
     "lf_attn_backward",
+    "lf_layer_forward",
     "lf_attn_destroy",
     "lf_attn_status_string",
     "lf_attn_last_error",
@@ -40,6 +42,11 @@ EXPORTS = (
 )
 
 _lib = None
+
+
+class LayerWeights(ctypes.Structure):
+    """lf_layer_weights: device pointers of the layer's parameters."""
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHTS]
 
 
 class LfAttnError(RuntimeError):
@@ -80,6 +87,9 @@ def load_library():
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
                                      vp, vp]
     lib.lf_attn_backward.restype = i32
+    lib.lf_layer_forward.argtypes = [vp, vp, ctypes.POINTER(LayerWeights), vp, i32, i32, i32, i32, ctypes.c_float,
+                                     i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32, vp, vp]
+    lib.lf_layer_forward.restype = i32
     lib.lf_attn_destroy.argtypes = [vp]
     lib.lf_attn_destroy.restype = i32
     lib.lf_attn_status_string.argtypes = [i32]
@@ -175,6 +185,13 @@ class LfAttn:
         mode = LF_WINDOW_CAUSAL if causal else LF_WINDOW_SYMMETRIC
         self._check(self.lib.lf_attn_set_window_mode(self.handle, mode), self.handle)
         self.causal = bool(causal)
+
+    def layer_raw(self, x_ptr, weights: LayerWeights, out_ptr, B, L, hidden, ffn, eps, w, dil, global_idx, pad_ptr,
+                  stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_layer_forward(self.handle, x_ptr, ctypes.byref(weights), out_ptr, B, L, hidden, ffn,
+                                       float(eps), w, dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
 
     def set_stage_timing(self, enable: bool):
         self._check(self.lib.lf_attn_set_stage_timing(self.handle, 1 if enable else 0), self.handle)
@@ -345,3 +362,45 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d_h, int(w), dil, global_idx, pad_ptr,
                        stream)
     return dq, dk, dv
+
+
+def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=None, eps: float = 1e-5, out=None,
+                  handle: LfAttn | None = None, causal: bool = False):
+    """One Longformer layer (projections, this attention, LayerNorms, GELU feed-forward).
+
+    x: contiguous bf16 device tensor [B, L, hidden]; ``weights`` maps LAYER_WEIGHTS to
+    contiguous bf16 device tensors in nn.Linear layout.  Returns ``out`` [B, L, hidden].
+    """
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 device tensor [B, L, hidden]")
+    B, L, E = x.shape
+    H = E // 64
+    F = int(weights["w_1"].shape[0])
+    for n in LAYER_WEIGHTS:
+        t = weights[n]
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"weight {n} must be a contiguous bfloat16 device tensor")
+    if isinstance(dil, int):
+        dil = [dil] * H
+    dil = [int(d) for d in dil]
+    if global_idx is not None and hasattr(global_idx, "tolist"):
+        global_idx = global_idx.tolist()
+    pad_ptr = None
+    if key_pad_mask is not None:
+        if key_pad_mask.dtype == torch.bool:
+            key_pad_mask = key_pad_mask.view(torch.uint8)
+        if tuple(key_pad_mask.shape) != (B, L) or not key_pad_mask.is_cuda or not key_pad_mask.is_contiguous():
+            raise ValueError("key_pad_mask must be a contiguous [B, L] device tensor")
+        pad_ptr = key_pad_mask.data_ptr()
+    if out is None:
+        out = torch.empty_like(x)
+    h = handle if handle is not None else _handle_for("bf16", causal)
+    if h.causal != bool(causal):
+        raise ValueError("handle window mode does not match causal=")
+    wts = LayerWeights(*[weights[n].data_ptr() for n in LAYER_WEIGHTS])
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        h.layer_raw(x.data_ptr(), wts, out.data_ptr(), B, L, E, F, eps, int(w), dil, global_idx, pad_ptr, stream)
+    return out

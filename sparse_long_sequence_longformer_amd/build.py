@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 
-SOURCES = ["lf_attn.cpp", "lf_attn_kernels.hip", "lf_attn_bwd.hip"]
+SOURCES = ["lf_attn.cpp", "lf_attn_kernels.hip", "lf_attn_bwd.hip", "lf_layer.hip"]
 ARCH = "gfx950"
 
 
@@ -25,6 +25,9 @@ def hipcc() -> str:
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found (ROCm is required to build liblfattn.so)")
+
+
+ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
 
 
 def compile_flags() -> list[str]:
@@ -59,7 +62,9 @@ def build(verbose: bool = False) -> str:
         cmd = [cc, *compile_flags(), *lang, "-c", path, "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # rocBLAS serves the layer's plain GEMMs
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, f"-L{ROCM_LIB}", "-lrocblas",
+          f"-Wl,-rpath,{ROCM_LIB}"], verbose)
     os.replace(tmp, LIB)
     for obj in objs:
         os.remove(obj)

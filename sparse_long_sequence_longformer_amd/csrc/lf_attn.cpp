@@ -3,6 +3,7 @@
 // enqueued; on error nothing is launched and `out` is untouched.
 
 #include <hip/hip_runtime_api.h>
+#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -36,6 +37,11 @@ struct lf_attn_s {
     char* ws_bwd = nullptr;  // row statistics and global partials of the backward
     size_t ws_bwd_bytes = 0;
     int ws_bwd_device = -1;
+    char* ws_layer = nullptr;  // intermediates of the layer
+    size_t ws_layer_bytes = 0;
+    int ws_layer_device = -1;
+    rocblas_handle blas = nullptr;
+    int blas_device = -1;
     std::string last_error;
     bool timing = false;
     std::vector<TimedLaunch> pending;  // recorded, not yet read
@@ -123,6 +129,8 @@ lf_status lf_attn_destroy(lf_attn_t h) {
     lf_status st = LF_OK;
     if (h->ws && hipFree(h->ws) != hipSuccess) st = LF_ERR_HIP;
     if (h->ws_bwd && hipFree(h->ws_bwd) != hipSuccess) st = LF_ERR_HIP;
+    if (h->ws_layer && hipFree(h->ws_layer) != hipSuccess) st = LF_ERR_HIP;
+    if (h->blas && rocblas_destroy_handle(h->blas) != rocblas_status_success) st = LF_ERR_HIP;
     release_events(h);
     for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
     delete h;
@@ -417,6 +425,112 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     return st;
 }
 
+// Y[M][N] (fp32, row-major) = X[M][K] (bf16) W^T with W[N][K] (bf16): in rocBLAS's
+// column-major terms Y^T = W X^T.
+lf_status gemm_xwt(lf_attn_t h, const void* X, const void* Wt, float* Y, int M, int N, int K) {
+    const float one = 1.f, zero = 0.f;
+    const rocblas_status rs = rocblas_gemm_ex(
+        h->blas, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, Wt, rocblas_datatype_bf16_r, K,
+        X, rocblas_datatype_bf16_r, K, &zero, Y, rocblas_datatype_f32_r, N, Y, rocblas_datatype_f32_r, N,
+        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    if (rs != rocblas_status_success) return fail(h, LF_ERR_HIP, "rocblas_gemm_ex failed: %s", rocblas_status_to_string(rs));
+    return LF_OK;
+}
+
+lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, void* out, int B, int L, int E, int F,
+                     float eps, int w, const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                     const uint8_t* key_pad_mask, void* stream) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (!x || !wt || !out) return fail(h, LF_ERR_INVALID_ARG, "x, wts and out must be non-null");
+    if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the layer supports bf16 handles only");
+    if (B < 1 || L < 1) return fail(h, LF_ERR_INVALID_ARG, "need B, L >= 1 (got %d, %d)", B, L);
+    if (E < LF_HEAD_DIM || E % LF_HEAD_DIM != 0 || E / LF_HEAD_DIM > LF_MAX_HEADS || E > 2048)
+        return fail(h, LF_ERR_UNSUPPORTED, "hidden must be a multiple of 64, at most 2048 (got %d)", E);
+    if (F < 8 || F % 8 != 0) return fail(h, LF_ERR_UNSUPPORTED, "ffn must be a positive multiple of 8 (got %d)", F);
+    if (!(eps >= 0.f)) return fail(h, LF_ERR_INVALID_ARG, "ln_eps must be >= 0");
+    const void* ptrs[] = {wt->w_qkv, wt->b_qkv, wt->w_o, wt->b_o, wt->ln1_g, wt->ln1_b,
+                          wt->w_1,   wt->b_1,   wt->w_2, wt->b_2, wt->ln2_g, wt->ln2_b};
+    for (const void* q : ptrs)
+        if (!q || !aligned16(q)) return fail(h, LF_ERR_INVALID_ARG, "every weight pointer must be non-null and 16-byte aligned");
+    if (!aligned16(x) || !aligned16(out)) return fail(h, LF_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+    const int H = E / LF_HEAD_DIM;
+    const size_t R = static_cast<size_t>(B) * L;
+    if (R * static_cast<size_t>(std::max(3 * E, F)) > (size_t(1) << 40))
+        return fail(h, LF_ERR_INVALID_ARG, "tensor size overflows");
+    if (R > 0x7fffffff) return fail(h, LF_ERR_UNSUPPORTED, "too many tokens");
+    if (overlaps(out, x, R * E * 2)) return fail(h, LF_ERR_INVALID_ARG, "out must not overlap x");
+    Plan pl;  // validates the attention arguments before anything is enqueued
+    lf_status st = make_plan(h, pl, B, H, L, LF_HEAD_DIM, w, dil_per_head, global_idx, n_global);
+    if (st != LF_OK) return st;
+
+    if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
+    if (h->blas && h->blas_device != h->device) {
+        (void)rocblas_destroy_handle(h->blas);
+        h->blas = nullptr;
+    }
+    if (!h->blas) {
+        if (rocblas_create_handle(&h->blas) != rocblas_status_success) {
+            h->blas = nullptr;
+            return fail(h, LF_ERR_HIP, "rocblas_create_handle failed");
+        }
+        h->blas_device = h->device;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rocblas_set_stream(h->blas, s) != rocblas_status_success) return fail(h, LF_ERR_HIP, "rocblas_set_stream failed");
+
+    // Workspace: one fp32 GEMM output [R][max(3E, F)], then bf16 q, k, v, attention
+    // output, merged heads (reused for x1), and the feed-forward activations [R][F].
+    const size_t f32_elems = R * static_cast<size_t>(std::max(3 * E, F));
+    const size_t t_elems = R * static_cast<size_t>(E);
+    const size_t need = f32_elems * 4 + (5 * t_elems + R * F) * 2 + 256;
+    st = reserve(h, &h->ws_layer, &h->ws_layer_bytes, &h->ws_layer_device, need);
+    if (st != LF_OK) return st;
+    float* gout = reinterpret_cast<float*>(h->ws_layer);
+    uint16_t* bq = reinterpret_cast<uint16_t*>(h->ws_layer + f32_elems * 4);
+    uint16_t* bk = bq + t_elems;
+    uint16_t* bv = bk + t_elems;
+    uint16_t* ba = bv + t_elems;
+    uint16_t* bm = ba + t_elems;  // merged heads, then x1
+    uint16_t* bh = bm + t_elems;  // GELU activations [R][F]
+    const int M = static_cast<int>(R);
+
+    st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
+        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E) == LF_OK ? hipSuccess : hipErrorUnknown;
+    });
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
+                      [&] { return lf::launch_qkv_split(gout, wt->b_qkv, bq, bk, bv, B, L, E, s); });
+    if (st != LF_OK) return st;
+    st = forward_impl(h, bq, bk, bv, nullptr, nullptr, nullptr, ba, nullptr, B, H, L, LF_HEAD_DIM, w, dil_per_head,
+                      global_idx, n_global, key_pad_mask, stream);
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] { return lf::launch_merge_heads(ba, bm, B, L, E, s); });
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
+        return gemm_xwt(h, bm, wt->w_o, gout, M, E, E) == LF_OK ? hipSuccess : hipErrorUnknown;
+    });
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] {
+        return lf::launch_bias_residual_ln(gout, wt->b_o, x, wt->ln1_g, wt->ln1_b, eps, bm, E, (long long)R, s);
+    });
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
+        return gemm_xwt(h, bm, wt->w_1, gout, M, F, E) == LF_OK ? hipSuccess : hipErrorUnknown;
+    });
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
+                      [&] { return lf::launch_bias_gelu(gout, wt->b_1, bh, F, (long long)R, s); });
+    if (st != LF_OK) return st;
+    st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
+        return gemm_xwt(h, bh, wt->w_2, gout, M, E, F) == LF_OK ? hipSuccess : hipErrorUnknown;
+    });
+    if (st != LF_OK) return st;
+    return launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] {
+        return lf::launch_bias_residual_ln(gout, wt->b_2, bm, wt->ln2_g, wt->ln2_b, eps, out, E, (long long)R, s);
+    });
+}
+
 }  // namespace
 
 extern "C" {
@@ -457,6 +571,13 @@ lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void
                            const uint8_t* key_pad_mask, void* stream) {
     return backward_impl(h, q, k, v, out, dout, lse, dq, dk, dv, B, H, L, d_h, w, dil_per_head, global_idx,
                          n_global, key_pad_mask, stream);
+}
+
+lf_status lf_layer_forward(lf_attn_t h, const void* x, const lf_layer_weights* wts, void* out, int B, int L,
+                           int hidden, int ffn, float ln_eps, int w, const int32_t* dil_per_head,
+                           const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask, void* stream) {
+    return layer_impl(h, x, wts, out, B, L, hidden, ffn, ln_eps, w, dil_per_head, global_idx, n_global,
+                      key_pad_mask, stream);
 }
 
 }  // extern "C"

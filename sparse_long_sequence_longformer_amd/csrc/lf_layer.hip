@@ -1,0 +1,158 @@
+// gfx950 kernels of the Longformer layer around the sparse attention (bf16 tensors,
+// fp32 arithmetic): the steps between the library GEMMs.  All of them are
+// HBM-bound elementwise or row-wise passes, written for coalesced 16-byte accesses.
+//
+//   qkv_split:        x W_qkv^T (fp32) + b_qkv -> q, k, v in [B][H][L][64] (bf16)
+//   merge_heads:      attention output [B][H][L][64] -> [B][L][H*64]
+//   bias_residual_ln: LayerNorm(y + b + residual) over the features of a row
+//   bias_gelu:        GELU(h + b), GELU(t) = 0.5 t (1 + erf(t / sqrt(2)))
+//
+// The layer is the post-LayerNorm block of page "基于Block-Sparse Attention的
+// Longformer" §6 (attention, residual, LayerNorm, feed-forward, residual,
+// LayerNorm) with RoBERTa's projections and feed-forward (page "基于自注意力机制的
+// 长文本建模算法：Longformer详解" §6: Longformer starts from RoBERTa's weights).
+
+#include "lf_attn_device.h"
+
+namespace lf {
+namespace {
+
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ f32x8 load8_bf16(const uint16_t* p) {
+    return __builtin_convertvector(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p)), f32x8);
+}
+__device__ __forceinline__ void store8_bf16(uint16_t* p, const f32x8& v) {
+    *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8));
+}
+__device__ __forceinline__ f32x8 load8_f32(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// One thread per 8 consecutive features of one row of x W_qkv^T ([R][3E], R = B*L).
+__global__ __launch_bounds__(256) void qkv_split_kernel(const float* qkv, const uint16_t* bias, uint16_t* q,
+                                                        uint16_t* k, uint16_t* v, int L, int E, long long n8) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const int per_row = 3 * E / 8;
+    const long long row = i / per_row;
+    const int f = (int)(i - row * per_row) * 8;  // feature in [0, 3E)
+    const int which = f / E, fe = f - which * E, h = fe >> 6, d = fe & 63;
+    const int H = E >> 6;
+    const long long b = row / L, l = row - b * L;
+    f32x8 t = load8_f32(qkv + row * 3 * E + f) + load8_bf16(bias + f);
+    uint16_t* dst = which == 0 ? q : (which == 1 ? k : v);
+    store8_bf16(dst + (((b * H + h) * L + l) << 6) + d, t);
+}
+
+// One thread per 8 features: [B][H][L][64] -> [B][L][H*64].
+__global__ __launch_bounds__(256) void merge_heads_kernel(const uint16_t* a, uint16_t* out, int L, int E,
+                                                          long long n8) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const int per_row = E / 8;
+    const long long row = i / per_row;
+    const int fe = (int)(i - row * per_row) * 8, h = fe >> 6, d = fe & 63;
+    const int H = E >> 6;
+    const long long b = row / L, l = row - b * L;
+    *reinterpret_cast<u32x4*>(out + row * E + fe) =
+        *reinterpret_cast<const u32x4*>(a + (((b * H + h) * L + l) << 6) + d);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// One wave per row of E = 64 * n features (n <= kMaxPerLane); lane j owns features
+// 8*j + 512*c .. +7 for c < n / 8.  Two passes over registers: mean, then variance.
+constexpr int kMaxChunks = 4;  // E <= 2048
+__global__ __launch_bounds__(256) void bias_residual_ln_kernel(const float* y, const uint16_t* bias,
+                                                               const uint16_t* res, const uint16_t* gamma,
+                                                               const uint16_t* beta, float eps, uint16_t* out,
+                                                               int E, long long R) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= R) return;
+    const int chunks = E / 512 + ((E % 512) ? 1 : 0);
+    f32x8 t[kMaxChunks];
+    float s = 0.f;
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int f = 512 * c + 8 * lane;
+        if (c < chunks && f < E) {
+            t[c] = load8_f32(y + row * E + f) + load8_bf16(bias + f) + load8_bf16(res + row * E + f);
+            for (int j = 0; j < 8; ++j) s += t[c][j];
+        } else {
+            t[c] = f32x8{};
+        }
+    }
+    const float mean = wave_sum(s) / (float)E;
+    float s2 = 0.f;
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int f = 512 * c + 8 * lane;
+        if (c < chunks && f < E)
+            for (int j = 0; j < 8; ++j) {
+                const float dlt = t[c][j] - mean;
+                s2 += dlt * dlt;
+            }
+    }
+    const float rstd = 1.0f / __builtin_sqrtf(wave_sum(s2) / (float)E + eps);
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int f = 512 * c + 8 * lane;
+        if (c < chunks && f < E) {
+            const f32x8 g = load8_bf16(gamma + f), be = load8_bf16(beta + f);
+            store8_bf16(out + row * E + f, (t[c] - mean) * rstd * g + be);
+        }
+    }
+}
+
+// One thread per 8 features of h [R][F].
+__global__ __launch_bounds__(256) void bias_gelu_kernel(const float* hpre, const uint16_t* bias, uint16_t* out,
+                                                        int F, long long n8) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const int per_row = F / 8;
+    const long long row = i / per_row;
+    const int f = (int)(i - row * per_row) * 8;
+    f32x8 t = load8_f32(hpre + row * F + f) + load8_bf16(bias + f);
+    for (int j = 0; j < 8; ++j) t[j] = 0.5f * t[j] * (1.0f + erff(t[j] * 0.70710678118654752f));
+    store8_bf16(out + row * F + f, t);
+}
+
+unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
+
+}  // namespace
+
+hipError_t launch_qkv_split(const float* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
+                            hipStream_t s) {
+    const long long n8 = (long long)B * L * 3 * E / 8;
+    hipLaunchKernelGGL(qkv_split_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, qkv,
+                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
+                       static_cast<uint16_t*>(v), L, E, n8);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_heads(const void* a, void* out, int B, int L, int E, hipStream_t s) {
+    const long long n8 = (long long)B * L * E / 8;
+    hipLaunchKernelGGL(merge_heads_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a), static_cast<uint16_t*>(out), L, E, n8);
+    return hipGetLastError();
+}
+
+hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void* res, const void* gamma,
+                                   const void* beta, float eps, void* out, int E, long long R, hipStream_t s) {
+    hipLaunchKernelGGL(bias_residual_ln_kernel, dim3(blocks_for(R, 4)), dim3(256), 0, s, y,
+                       static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(res),
+                       static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta), eps,
+                       static_cast<uint16_t*>(out), E, R);
+    return hipGetLastError();
+}
+
+hipError_t launch_bias_gelu(const float* h, const void* bias, void* out, int F, long long R, hipStream_t s) {
+    const long long n8 = R * F / 8;
+    hipLaunchKernelGGL(bias_gelu_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, h,
+                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), F, n8);
+    return hipGetLastError();
+}
+
+}  // namespace lf

@@ -18,7 +18,7 @@ needs_lib = pytest.mark.skipif(not os.path.exists(binding.library_path()),
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(lf_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lf_(?:attn|layer)_\w+)\s*\(", text)))
 
 
 def test_header_declares_binding_exports():
@@ -184,6 +184,36 @@ def test_window_mode():
         assert lib.lf_attn_set_window_mode(None, 0) == 1
     finally:
         lib.lf_attn_destroy(h)
+
+
+@needs_lib
+def test_layer_host_validation():
+    lib = binding.load_library()
+    dil = (ctypes.c_int32 * 12)(*([1] * 12))
+    dil_p = ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32))
+    ok = binding.LayerWeights(*[FAKE * (20 + i) for i in range(len(binding.LAYER_WEIGHTS))])
+
+    def call(h, wts=ok, hidden=768, ffn=3072, x=FAKE, out=FAKE * 2, eps=1e-5):
+        st = lib.lf_layer_forward(h, x, ctypes.byref(wts) if wts is not None else None, out, 1, 64, hidden, ffn,
+                                  eps, 4, dil_p, None, 0, None, None)
+        return st, lib.lf_attn_last_error(h).decode()
+
+    h32, h16 = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h32), 0) == 0 and lib.lf_attn_create(ctypes.byref(h16), 1) == 0
+    try:
+        st, msg = call(h32)
+        assert st == 2 and "bf16" in msg
+        bad = binding.LayerWeights(*[FAKE * (20 + i) for i in range(len(binding.LAYER_WEIGHTS))])
+        bad.w_o = None
+        for kw, code, frag in [(dict(hidden=100), 2, "hidden"), (dict(hidden=4096), 2, "hidden"),
+                               (dict(ffn=12), 2, "ffn"), (dict(wts=None), 1, "non-null"),
+                               (dict(wts=bad), 1, "weight"), (dict(x=FAKE + 8), 1, "aligned"),
+                               (dict(out=FAKE + 4096), 1, "overlap"), (dict(eps=-1.0), 1, "ln_eps")]:
+            st, msg = call(h16, **kw)
+            assert st == code and frag in msg, (kw, st, msg)
+    finally:
+        lib.lf_attn_destroy(h32)
+        lib.lf_attn_destroy(h16)
 
 
 @needs_lib
