@@ -31,6 +31,8 @@ What it computes (per batch b and head h, with inputs widened to float64):
   the keys j <= g.  This is the pattern of autoregressive language modelling,
   which the Longformer-explained page lists among the pretraining tasks (§6); the
   pages give no rule for it, and a mask on top of the union is the plainest one.
+* Per-sequence global sets: ``global_idx`` may hold one row per sequence
+  ([B][n], negative entries unused); sequence b then uses its own row as G.
 * Variant with separate global projections (``attention_global_proj``): the page
   "基于Block-Sparse Attention的Longformer" §4 gives global attention its own
   query, key and value projections.  Read inside the one-softmax formulation: a
@@ -70,6 +72,18 @@ def _as_f64(x) -> np.ndarray:
 
         x = x.to(torch.float64).numpy()
     return np.asarray(x, dtype=np.float64)
+
+
+def globals_of(global_idx, b: int) -> np.ndarray:
+    """The global set of sequence b: ``global_idx`` is one set shared by every
+    sequence (1-D), or one row per sequence (2-D [B][n], entries < 0 unused)."""
+    if global_idx is None:
+        return np.zeros(0, dtype=np.int64)
+    arr = np.asarray(global_idx, dtype=np.int64)
+    if arr.ndim == 2:
+        row = arr[b]
+        return global_set(row[row >= 0])
+    return global_set(arr)
 
 
 def global_set(global_idx) -> np.ndarray:
@@ -169,7 +183,7 @@ def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
     out = np.zeros((B, H, L, d), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            out[b, h] = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
+            out[b, h] = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], globals_of(global_idx, b),
                                      None if pad is None else pad[b], causal=causal)
     return out
 
@@ -184,7 +198,7 @@ def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, s
     pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
     res = []
     for b, h, i in samples:
-        o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
+        o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], globals_of(global_idx, b),
                          None if pad is None else pad[b], rows=[i], causal=causal)
         res.append(o[0])
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
@@ -193,11 +207,11 @@ def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, s
 def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1,
                causal: bool = False) -> int:
     """Number of attended (query, key) pairs, summed over batch and heads: sum of M."""
-    G = global_set(global_idx)
     dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
     pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
     total = 0
     for b in range(B):
+        G = globals_of(global_idx, b)
         for d in dil:
             for s0 in range(0, L, ROW_BLOCK):
                 rows = np.arange(s0, min(L, s0 + ROW_BLOCK))
@@ -215,13 +229,13 @@ def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_i
     projections; every global row sees every position, §2).
     """
     out = attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask, causal=causal)
-    G = global_set(global_idx)
-    if G.size == 0:
-        return out
     q_g, k_g, v_g = _as_f64(q_g), _as_f64(k_g), _as_f64(v_g)
     B, H, L, d = q_g.shape
     pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
     for b in range(B):
+        G = globals_of(global_idx, b)
+        if G.size == 0:
+            continue
         keep = np.ones((G.size, L), dtype=bool)
         if pad is not None:
             keep &= ~pad[b][None, :]
@@ -236,19 +250,19 @@ def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_i
 def attention_global_proj_sampled(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_idx, key_pad_mask,
                                   samples):
     """``attention_global_proj`` output rows for a list of (b, h, i) samples, one by one."""
-    G = set(int(x) for x in global_set(global_idx))
     dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
     pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
     res = []
     for b, h, i in samples:
-        if i in G:
+        Gb = globals_of(global_idx, b)
+        if i in set(int(x) for x in Gb):
             L = k_g.shape[2]
             keep = np.ones((1, L), dtype=bool)
             if pad is not None:
                 keep &= ~pad[b][None, :]
             o, _ = _attention_rows(_as_f64(q_g[b, h][i:i + 1]), _as_f64(k_g[b, h]), _as_f64(v_g[b, h]), keep)
         else:
-            o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], global_idx,
+            o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], Gb,
                              None if pad is None else pad[b], rows=[i])
         res.append(o[0])
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
@@ -286,7 +300,7 @@ def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None
     out = np.zeros((B, H, L), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            out[b, h] = attention_lse_bh(q[b, h], k[b, h], w, dil[h], global_idx,
+            out[b, h] = attention_lse_bh(q[b, h], k[b, h], w, dil[h], globals_of(global_idx, b),
                                          None if pad is None else pad[b], causal=causal)
     return out
 
@@ -328,6 +342,6 @@ def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = attention_backward_bh(
-                q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], global_idx, None if pad is None else pad[b],
-                causal=causal)
+                q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], globals_of(global_idx, b),
+                None if pad is None else pad[b], causal=causal)
     return dq, dk, dv

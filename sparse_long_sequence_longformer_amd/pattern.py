@@ -87,17 +87,26 @@ def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None
     """Attended pairs summed over B sequences and all heads.
 
     ``key_pad_mask`` is an array-like [B, L] (nonzero = padded) or None.
+    ``global_idx``: one set for every sequence, or one row per sequence ([B][n],
+    negative entries unused).
     """
-    G = _unique_globals(global_idx, L)
+    per_seq = global_idx is not None and np.asarray(global_idx).ndim == 2
     dils = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
     pad = None if key_pad_mask is None else (np.asarray(key_pad_mask) != 0)
     if pad is not None:
         B = pad.shape[0]
+    if per_seq:
+        B = np.asarray(global_idx).shape[0]
     tot = PairCounts(0, 0, 0)
     cache = {}
     for b in range(B):
+        if per_seq:
+            row = np.asarray(global_idx, dtype=np.int64)[b]
+            G = _unique_globals(row[row >= 0], L)
+        else:
+            G = _unique_globals(global_idx, L)
         valid = np.ones(L, dtype=bool) if pad is None else ~pad[b]
-        key_b = b if pad is not None else 0
+        key_b = b if (pad is not None or per_seq) else 0
         for dl in dils:
             key = (key_b, dl)
             if key not in cache:

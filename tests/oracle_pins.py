@@ -599,6 +599,31 @@ def pin_layer_norm_rows():
     assert np.abs(out.var(axis=-1) - 1.0).max() < 1e-12
 
 
+# -------------------------------------------------------- per-sequence global sets
+
+def pin_global_sets_per_sequence():
+    """Per-sequence global sets: each sequence equals brute-force enumeration with its
+    own set; identical rows equal the shared set; -1 entries are ignored."""
+    B, H, L, d, w = 3, 2, 36, 8, 3
+    dil = [1, 2]
+    q, k, v = (_rand((B, H, L, d), 600 + t) for t in range(3))
+    sets = np.array([[0, 17, -1, -1], [5, 5, 30, 2], [-1, -1, -1, -1]])
+    pad = np.zeros((B, L), dtype=bool)
+    pad[1, 31:] = True
+    got = orc.attention(q, k, v, w, dil, sets, pad)
+    for b in range(B):
+        G = [int(g) for g in sets[b] if g >= 0]
+        for h in range(H):
+            ref = np.array(brute.attention_bh(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), w, dil[h], G,
+                                              pad[b].tolist()))
+            assert np.abs(got[b, h] - ref).max() < 1e-12, (b, h)
+    same = np.array([[4, 20]] * B)
+    assert np.array_equal(orc.attention(q, k, v, w, dil, same, pad), orc.attention(q, k, v, w, dil, [4, 20], pad))
+    n = orc.mask_count(L, w, dil, sets, pad, B=B)
+    assert n == sum(brute.pair_count(L, w, dd, [int(g) for g in sets[b] if g >= 0], pad[b].tolist())
+                    for b in range(B) for dd in dil)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -627,6 +652,7 @@ ALL_PINS = [
     pin_causal_textbook,
     pin_causal_prefix,
     pin_causal_backward_autograd,
+    pin_global_sets_per_sequence,
     pin_layer_torch_encoder,
     pin_layer_norm_rows,
 ]

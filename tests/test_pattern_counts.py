@@ -94,3 +94,18 @@ def test_counter_matches_mask_causal(seed):
             rows = sum(len(brute.key_set(g, L, w, d, G, pr, causal=True)) for g in sorted(set(G)))
             cb = pattern.count_pairs(L, w, [d], G, None if pad is None else pad[b:b + 1], causal=True)
             assert cb.global_row == rows
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_counter_per_sequence_globals(seed):
+    """Per-sequence global sets ([B][n], -1 unused): closed form against the mask sums."""
+    rng = np.random.default_rng(200 + seed)
+    L = int(rng.integers(2, 80))
+    w = int(rng.integers(0, 10))
+    dil = [int(x) for x in rng.integers(1, 4, size=2)]
+    B = int(rng.integers(1, 4))
+    sets = rng.integers(-1, L, size=(B, 4))
+    pad = (rng.random((B, L)) < 0.2).astype(np.uint8) if seed % 2 else None
+    for causal in (False, True):
+        c = pattern.count_pairs(L, w, dil, sets, pad, B=B, causal=causal)
+        assert c.total == orc.mask_count(L, w, dil, sets, pad, B=B, causal=causal)
