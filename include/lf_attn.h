@@ -66,6 +66,10 @@ typedef enum lf_dtype {
 #define LF_WINDOW_SYMMETRIC 0 /* keys i + m*dil, m = -w..w (default) */
 #define LF_WINDOW_CAUSAL 1    /* one-sided: every pair with its key after its query removed */
 
+/* Global sets (lf_attn_set_global_mode). */
+#define LF_GLOBALS_SHARED 0       /* global_idx[n_global]: one set for every sequence (default) */
+#define LF_GLOBALS_PER_SEQUENCE 1 /* global_idx[B][n_global]: one row per sequence, entries < 0 unused */
+
 typedef struct lf_attn_s* lf_attn_t;
 
 /*
@@ -240,6 +244,22 @@ lf_status lf_layer_forward(lf_attn_t h, const void* x, const lf_layer_weights* w
                            int hidden, int ffn, float ln_eps, int w, const int32_t* dil_per_head,
                            const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
                            void* stream);
+
+/*
+ * How every later call on `h` reads `global_idx`.
+ *
+ * LF_GLOBALS_SHARED (default): global_idx[n_global], one set for every sequence
+ *   and head; every entry must lie in [0, L).
+ * LF_GLOBALS_PER_SEQUENCE: global_idx[B][n_global] (HOST, row-major): row b is
+ *   the set of sequence b; negative entries are unused; other entries must lie in
+ *   [0, L); duplicates are ignored.  B * n_global <= LF_MAX_GLOBALS
+ *   (LF_ERR_UNSUPPORTED otherwise).  Different documents mark different tokens
+ *   global (a question of its own length in each, page
+ *   "基于自注意力机制的长文本建模算法：Longformer详解" §7), which one shared set
+ *   cannot express.
+ * Errors: LF_ERR_INVALID_ARG (h == NULL or unknown mode); the mode is unchanged.
+ */
+lf_status lf_attn_set_global_mode(lf_attn_t h, int mode);
 
 /* Free the handle and its device workspace.  NULL is a no-op.  Waits for the
  * device before freeing (hipFree semantics). */

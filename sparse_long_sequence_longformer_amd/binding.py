@@ -19,6 +19,8 @@ LF_F32 = 0
 LF_BF16 = 1
 LF_WINDOW_SYMMETRIC = 0
 LF_WINDOW_CAUSAL = 1
+LF_GLOBALS_SHARED = 0
+LF_GLOBALS_PER_SEQUENCE = 1
 N_STAGES = 8
 STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge", "layer_gemm", "layer_pointwise")
 LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
@@ -38,6 +40,7 @@ EXPORTS = (
     "lf_attn_last_error",
     "lf_attn_set_stage_timing",
     "lf_attn_set_window_mode",
+    "lf_attn_set_global_mode",
     "lf_attn_stage_times",
 )
 
@@ -96,6 +99,8 @@ def load_library():
     lib.lf_attn_status_string.restype = ctypes.c_char_p
     lib.lf_attn_last_error.argtypes = [vp]
     lib.lf_attn_last_error.restype = ctypes.c_char_p
+    lib.lf_attn_set_global_mode.argtypes = [vp, i32]
+    lib.lf_attn_set_global_mode.restype = i32
     lib.lf_attn_set_window_mode.argtypes = [vp, i32]
     lib.lf_attn_set_window_mode.restype = i32
     lib.lf_attn_set_stage_timing.argtypes = [vp, i32]
@@ -124,6 +129,7 @@ class LfAttn:
         self._check(st, h)
         self.handle = h
         self.causal = False
+        self.per_sequence_globals = False
 
     def _check(self, st, h=None):
         if st != LF_OK:
@@ -138,13 +144,20 @@ class LfAttn:
 
     @classmethod
     def _host_arrays(cls, dil, global_idx):
-        """int32 host arrays of the dilations and globals (cached per distinct value)."""
-        key = (tuple(int(x) for x in dil), tuple(int(x) for x in global_idx) if global_idx is not None else ())
+        """int32 host arrays of the dilations and globals (cached per distinct value).
+        ``global_idx``: a list (one shared set) or (flat row-major list, row length)."""
+        n_row = None
+        if isinstance(global_idx, tuple):
+            global_idx, n_row = global_idx
+        key = (tuple(int(x) for x in dil), tuple(int(x) for x in global_idx) if global_idx is not None else (),
+               n_row)
         hit = cls._arrays_cache.get(key)
         if hit is not None:
             return hit
         dil_arr, _ = _int32_array(key[0])
         g_arr, ng = _int32_array(key[1])
+        if n_row is not None:
+            ng = n_row
         null = ctypes.POINTER(ctypes.c_int32)()
         dil_p = null if dil_arr is None else ctypes.cast(dil_arr, ctypes.POINTER(ctypes.c_int32))
         g_p = null if g_arr is None else ctypes.cast(g_arr, ctypes.POINTER(ctypes.c_int32))
@@ -179,6 +192,12 @@ class LfAttn:
         st = self.lib.lf_attn_backward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr,
                                        dk_ptr, dv_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
+
+    def set_per_sequence_globals(self, per_seq: bool):
+        """Read global_idx as one row per sequence in every later call on this handle."""
+        mode = LF_GLOBALS_PER_SEQUENCE if per_seq else LF_GLOBALS_SHARED
+        self._check(self.lib.lf_attn_set_global_mode(self.handle, mode), self.handle)
+        self.per_sequence_globals = bool(per_seq)
 
     def set_causal(self, causal: bool):
         """One-sided (causal) variant for every later call on this handle."""
@@ -217,14 +236,33 @@ class LfAttn:
 _handles: dict = {}
 
 
-def _handle_for(dtype: str, causal: bool = False) -> LfAttn:
-    key = (dtype, bool(causal))
+def _handle_for(dtype: str, causal: bool = False, per_seq: bool = False) -> LfAttn:
+    key = (dtype, bool(causal), bool(per_seq))
     if key not in _handles:
         h = LfAttn(dtype)
         if causal:
             h.set_causal(True)
+        if per_seq:
+            h.set_per_sequence_globals(True)
         _handles[key] = h
     return _handles[key]
+
+
+def _global_arg(global_idx, B: int):
+    """Shared set -> (list, False); one set per sequence (2-D, rows may differ in
+    length) -> ((flat row-major list padded with -1, row length), True)."""
+    if global_idx is None:
+        return None, False
+    if hasattr(global_idx, "tolist"):
+        global_idx = global_idx.tolist()
+    rows = list(global_idx)
+    if rows and isinstance(rows[0], (list, tuple)):
+        if len(rows) != B:
+            raise ValueError("per-sequence global sets need one row per sequence")
+        n = max((len(r) for r in rows), default=0)
+        flat = [int(x) for r in rows for x in (list(r) + [-1] * (n - len(r)))]
+        return (flat, n), True
+    return [int(x) for x in rows], False
 
 
 def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=False):
@@ -252,8 +290,7 @@ def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=Fa
     dil = [int(x) for x in (dil.tolist() if hasattr(dil, "tolist") else dil)]
     if len(dil) != H:
         raise ValueError("need one dilation per head")
-    if global_idx is not None and hasattr(global_idx, "tolist"):
-        global_idx = global_idx.tolist()
+    global_idx, per_seq = _global_arg(global_idx, B)
     pad_ptr = None
     if key_pad_mask is not None:
         if key_pad_mask.dtype == torch.bool:
@@ -267,11 +304,13 @@ def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=Fa
         out = torch.empty_like(q)
     elif out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous device tensor like q")
-    h = handle if handle is not None else _handle_for(dt, causal)
+    h = handle if handle is not None else _handle_for(dt, causal, per_seq)
     if h.dtype != dt:
         raise ValueError("handle dtype does not match the inputs")
     if h.causal != bool(causal):
         raise ValueError("handle window mode does not match causal=")
+    if h.per_sequence_globals != per_seq:
+        raise ValueError("handle global mode does not match the shape of global_idx")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     return B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream
 
@@ -385,8 +424,7 @@ def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=N
     if isinstance(dil, int):
         dil = [dil] * H
     dil = [int(d) for d in dil]
-    if global_idx is not None and hasattr(global_idx, "tolist"):
-        global_idx = global_idx.tolist()
+    global_idx, per_seq = _global_arg(global_idx, B)
     pad_ptr = None
     if key_pad_mask is not None:
         if key_pad_mask.dtype == torch.bool:
@@ -396,9 +434,11 @@ def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=N
         pad_ptr = key_pad_mask.data_ptr()
     if out is None:
         out = torch.empty_like(x)
-    h = handle if handle is not None else _handle_for("bf16", causal)
+    h = handle if handle is not None else _handle_for("bf16", causal, per_seq)
     if h.causal != bool(causal):
         raise ValueError("handle window mode does not match causal=")
+    if h.per_sequence_globals != per_seq:
+        raise ValueError("handle global mode does not match the shape of global_idx")
     wts = LayerWeights(*[weights[n].data_ptr() for n in LAYER_WEIGHTS])
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):

@@ -30,6 +30,7 @@ struct TimedLaunch {
 struct lf_attn_s {
     lf_dtype dtype;
     int window_mode = LF_WINDOW_SYMMETRIC;
+    int global_mode = LF_GLOBALS_SHARED;
     int device = -1;
     char* ws = nullptr;  // global-row partials of the forward
     size_t ws_bytes = 0;
@@ -137,6 +138,15 @@ lf_status lf_attn_destroy(lf_attn_t h) {
     return st;
 }
 
+lf_status lf_attn_set_global_mode(lf_attn_t h, int mode) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (mode != LF_GLOBALS_SHARED && mode != LF_GLOBALS_PER_SEQUENCE)
+        return fail(h, LF_ERR_INVALID_ARG, "unknown global mode %d", mode);
+    h->global_mode = mode;
+    return LF_OK;
+}
+
 lf_status lf_attn_set_window_mode(lf_attn_t h, int mode) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->last_error.clear();
@@ -186,7 +196,10 @@ namespace {
 struct Plan {
     int B, H, L, w;
     int dil[LF_MAX_HEADS];
-    std::vector<int> g;
+    std::vector<int> g;     // shared set, or the per-sequence rows back to back (stride gstride)
+    std::vector<int> gcnt;  // per-sequence counts (per-sequence mode)
+    int n_g;                // shared count, or the largest per-sequence count
+    int gstride;            // 0: shared
     int n_gblk;
     int tiles;
     size_t bytes;  // of one [B][H][L][d_h] tensor
@@ -212,17 +225,47 @@ lf_status make_plan(lf_attn_t h, Plan& pl, int B, int H, int L, int d_h, int w, 
         if (dil_per_head[i] < 1) return fail(h, LF_ERR_INVALID_ARG, "dil_per_head[%d] = %d < 1", i, dil_per_head[i]);
         pl.dil[i] = dil_per_head[i];
     }
-    pl.g.assign(global_idx, global_idx + n_global);
-    for (int i = 0; i < n_global; ++i)
-        if (pl.g[i] < 0 || pl.g[i] >= L)
-            return fail(h, LF_ERR_INVALID_ARG, "global_idx[%d] = %d outside [0, %d)", i, pl.g[i], L);
-    std::sort(pl.g.begin(), pl.g.end());
-    pl.g.erase(std::unique(pl.g.begin(), pl.g.end()), pl.g.end());
+    if (h->global_mode == LF_GLOBALS_PER_SEQUENCE) {
+        // global_idx is [B][n_global]; negative entries are unused.
+        if (static_cast<int64_t>(B) * n_global > LF_MAX_GLOBALS || B > LF_MAX_GLOBALS)
+            return fail(h, LF_ERR_UNSUPPORTED, "per-sequence globals: at most %d entries in all (got %d x %d)",
+                        LF_MAX_GLOBALS, B, n_global);
+        std::vector<std::vector<int>> rows(B);
+        int mx = 0;
+        for (int b = 0; b < B; ++b) {
+            for (int i = 0; i < n_global; ++i) {
+                const int g = global_idx[static_cast<size_t>(b) * n_global + i];
+                if (g < 0) continue;
+                if (g >= L) return fail(h, LF_ERR_INVALID_ARG, "global_idx[%d][%d] = %d outside [0, %d)", b, i, g, L);
+                rows[b].push_back(g);
+            }
+            std::sort(rows[b].begin(), rows[b].end());
+            rows[b].erase(std::unique(rows[b].begin(), rows[b].end()), rows[b].end());
+            mx = std::max<int>(mx, static_cast<int>(rows[b].size()));
+        }
+        pl.gstride = mx;
+        pl.n_g = mx;
+        pl.g.assign(static_cast<size_t>(B) * mx, 0);
+        pl.gcnt.assign(B, 0);
+        for (int b = 0; b < B; ++b) {
+            std::copy(rows[b].begin(), rows[b].end(), pl.g.begin() + static_cast<size_t>(b) * mx);
+            pl.gcnt[b] = static_cast<int>(rows[b].size());
+        }
+    } else {
+        pl.g.assign(global_idx, global_idx + n_global);
+        for (int i = 0; i < n_global; ++i)
+            if (pl.g[i] < 0 || pl.g[i] >= L)
+                return fail(h, LF_ERR_INVALID_ARG, "global_idx[%d] = %d outside [0, %d)", i, pl.g[i], L);
+        std::sort(pl.g.begin(), pl.g.end());
+        pl.g.erase(std::unique(pl.g.begin(), pl.g.end()), pl.g.end());
+        pl.n_g = static_cast<int>(pl.g.size());
+        pl.gstride = 0;
+    }
     pl.B = B;
     pl.H = H;
     pl.L = L;
     pl.w = std::min(w, L);  // |j - i| < L always, so a wider window changes nothing
-    pl.n_gblk = (static_cast<int>(pl.g.size()) + lf::kGlobalQueriesPerBlock - 1) / lf::kGlobalQueriesPerBlock;
+    pl.n_gblk = (pl.n_g + lf::kGlobalQueriesPerBlock - 1) / lf::kGlobalQueriesPerBlock;
     int tiles = 0;
     for (int i = 0; i < H; ++i) {
         const int d = pl.dil[i];
@@ -318,8 +361,10 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     p.H = H;
     p.L = L;
     p.w = pl.w;
-    p.n_g = static_cast<int>(pl.g.size());
+    p.n_g = pl.n_g;
+    p.gstride = pl.gstride;
     std::copy(pl.g.begin(), pl.g.end(), p.g);
+    std::copy(pl.gcnt.begin(), pl.gcnt.end(), p.gcnt);
     p.n_gblk = pl.n_gblk;
     p.rows_per_block = lf::kRowsPerBlock;
     p.tiles_per_head = pl.tiles;
@@ -389,8 +434,10 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     p.H = H;
     p.L = L;
     p.w = pl.w;
-    p.n_g = static_cast<int>(pl.g.size());
+    p.n_g = pl.n_g;
+    p.gstride = pl.gstride;
     std::copy(pl.g.begin(), pl.g.end(), p.g);
+    std::copy(pl.gcnt.begin(), pl.gcnt.end(), p.gcnt);
     p.n_gblk = pl.n_gblk;
     p.tiles_per_head = pl.tiles;
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;

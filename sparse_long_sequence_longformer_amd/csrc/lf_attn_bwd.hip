@@ -282,6 +282,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
     const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= n) return;
     const int pos = (int)(i % (size_t)p.L);
+    const int b = (int)(i / ((size_t)p.L * p.H)), gofs = b * p.gstride;
+    const int ng = p.gstride ? p.gcnt[b] : p.n_g;
     const u32x4* o = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + i * 64);
     const u32x4* g = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + i * 64);
     float acc = 0.f;
@@ -292,13 +294,13 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
     }
     const float lse = p.lse[i];
     const float l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
-    int lo = 0, hi = p.n_g;  // binary search of the sorted global positions
+    int lo = 0, hi = ng;  // binary search of the sorted global positions
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (p.g[mid] < pos) lo = mid + 1;
+        if (p.g[gofs + mid] < pos) lo = mid + 1;
         else hi = mid;
     }
-    const bool is_g = lo < p.n_g && p.g[lo] == pos;
+    const bool is_g = lo < ng && p.g[gofs + lo] == pos;
     p.dsum[i] = acc;
     p.lse2[i] = l2;
     p.lse2_band[i] = is_g ? kPosInf : l2;
@@ -338,6 +340,8 @@ void bwd_dq_kernel(const BwdParams p) {
     const float* lse2 = p.lse2 + (size_t)tl.bh * L;
     const float* dsum = p.dsum + (size_t)tl.bh * L;
     const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
+    const int gofs = tl.b * p.gstride;  // this sequence's global set
+    const int ng = p.gstride ? p.gcnt[tl.b] : p.n_g;
 
     const int qa = r0 + 32 * wv, qv = qa + (lane & 31);
     const bool rows_live = qa < Lr;
@@ -348,7 +352,7 @@ void bwd_dq_kernel(const BwdParams p) {
     const float my_l2 = qv < Lr ? lse2[row] : kPosInf;
     const float my_d = qv < Lr ? dsum[row] : 0.f;
 
-    const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
+    const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
     const int n_st = n_gst + tl.n_band;
     auto band_invalid = [&](int u) -> uint64_t {
         if (pad) return band_mask[u % kBwdMaskRing];
@@ -389,7 +393,7 @@ void bwd_dq_kernel(const BwdParams p) {
     };
 
     for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
-        const int g = gi < p.n_g ? p.g[gi] : -1;
+        const int g = gi < ng ? p.g[gofs + gi] : -1;
         const bool ok = g >= 0 && (!pad || pad[g] == 0);
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
@@ -405,14 +409,14 @@ void bwd_dq_kernel(const BwdParams p) {
             const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
             if (lane == 0) glob_mask[s] = inv;
         }
-    for (int gi = tid; gi < p.n_g; gi += kThreads) {
+    for (int gi = tid; gi < ng; gi += kThreads) {
         const int vr = glob_row[gi] - r0;
         if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
     }
     __syncthreads();
 
     // One-sided variant: the global slots at or before this lane's row.
-    const int gcnt = causal ? count_le(glob_abs, p.n_g, row) : 0;
+    const int gcnt = causal ? count_le(glob_abs, ng, row) : 0;
     Lanes lo;
     lane_setup(lo, lane);
     if (n_st > 0) issue(0);
@@ -461,7 +465,7 @@ void bwd_dq_kernel(const BwdParams p) {
         const int vr = qv - r0;  // global rows: the merge
         if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) store_row(dQ + (size_t)row * 64, h2, acc, 0.125f);
     }
-    if (p.n_g == 0) return;
+    if (ng == 0) return;
 
     // Global rows (C): each wave takes one 32-key sub-tile of the home keys
     // [r0, r0 + 128) (the last two band stages, still in the ring for the first 32
@@ -470,9 +474,10 @@ void bwd_dq_kernel(const BwdParams p) {
     const size_t part0 = ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * ngq;
     const int hs = wv >> 1, hsub = wv & 1;
     const int home_end = min(Lr, r0 + kRowsPerBlock);
-    for (int gb = 0; gb < p.n_gblk; ++gb) {
+    const int n_gblk_b = (ng + kGlobalQueriesPerBlock - 1) / kGlobalQueriesPerBlock;  // this sequence's blocks
+    for (int gb = 0; gb < n_gblk_b; ++gb) {
         const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
-        const int g = gq < p.n_g ? p.g[gq] : -1;
+        const int g = gq < ng ? p.g[gofs + gq] : -1;
         Op gop, gdo;
         load_op(gop, g >= 0 ? Q + (size_t)g * 64 : nullptr, h2);
         load_op(gdo, g >= 0 ? dO + (size_t)g * 64 : nullptr, h2);
@@ -526,7 +531,7 @@ void bwd_dq_kernel(const BwdParams p) {
             acc_t(tk, f, gacc);
         }
         __syncthreads();  // done with the staged keys: the ring holds the reduction
-        const int nq = min(kGlobalQueriesPerBlock, p.n_g - gb * kGlobalQueriesPerBlock);
+        const int nq = min(kGlobalQueriesPerBlock, ng - gb * kGlobalQueriesPerBlock);
         wave_sum_store(reinterpret_cast<float*>(ring), gacc, wv, lane, tid,
                        p.ws_dq + (part0 + (size_t)gb * kGlobalQueriesPerBlock) * 64, nq);
     }
@@ -565,6 +570,8 @@ void bwd_dkv_kernel(const BwdParams p) {
     const float* lse2b = p.lse2_band + (size_t)tl.bh * L;
     const float* dsum = p.dsum + (size_t)tl.bh * L;
     const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
+    const int gofs = tl.b * p.gstride;  // this sequence's global set
+    const int ng = p.gstride ? p.gcnt[tl.b] : p.n_g;
 
     const int qa = r0 + 32 * wv, qv = qa + (lane & 31);  // own keys (virtual index)
     const bool rows_live = qa < Lr;
@@ -574,14 +581,14 @@ void bwd_dkv_kernel(const BwdParams p) {
     load_op(kop, kvalid ? K + (size_t)krow * 64 : nullptr, h2);
     load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
 
-    const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
+    const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
     const int n_st = n_gst + tl.n_band;
     auto issue = [&](int s) {
         char* slot = ring + (s & 1) * kStageB;
         if (s < n_gst) {
             auto row_of = [&](int kk) {
                 const int gi = kStageKeys * s + kk;
-                return gi < p.n_g ? p.g[gi] : -1;
+                return gi < ng ? p.g[gofs + gi] : -1;
             };
             dma_tiles(slot, Q, dO, row_of, wv, lane);
             if (wv == 0) dma_floats(slot, lse2, dsum, row_of, lane);
@@ -597,10 +604,10 @@ void bwd_dkv_kernel(const BwdParams p) {
     };
 
     if (tid < kRowsPerBlock) own_gidx[tid] = -1;
-    for (int gi = tid; gi < p.n_g; gi += kThreads) gq_pos[gi] = p.g[gi];
+    for (int gi = tid; gi < ng; gi += kThreads) gq_pos[gi] = p.g[gofs + gi];
     __syncthreads();
-    for (int gi = tid; gi < p.n_g; gi += kThreads) {
-        const int g = p.g[gi];
+    for (int gi = tid; gi < ng; gi += kThreads) {
+        const int g = p.g[gofs + gi];
         if (g >= r && (g - r) % dil == 0) {
             const int vr = (g - r) / dil - r0;
             if (vr >= 0 && vr < kRowsPerBlock) own_gidx[vr] = gi;
@@ -610,7 +617,7 @@ void bwd_dkv_kernel(const BwdParams p) {
 
     // One-sided variant: the first global slot at or after this lane's key (the
     // global queries that see it; slots are sorted by position).
-    const int gfirst = causal ? count_le(gq_pos, p.n_g, krow - 1) : 0;
+    const int gfirst = causal ? count_le(gq_pos, ng, krow - 1) : 0;
     Lanes lo;
     lane_setup(lo, lane);
     if (n_st > 0) issue(0);
@@ -628,7 +635,7 @@ void bwd_dkv_kernel(const BwdParams p) {
         for (int sub = 0; sub < 2; ++sub) {
             const int kss = ks + 32 * sub;
             if (gstage) {
-                if (kss >= p.n_g) continue;
+                if (kss >= ng) continue;
             } else {
                 if (kss > qa + 31 + w || kss + 31 < qa - wl) continue;  // outside every own key's window
                 if (kss >= tl.kend || kss + 31 < tl.kb0) continue;      // no valid query
@@ -670,7 +677,7 @@ void bwd_dkv_kernel(const BwdParams p) {
             store_row_f32(p.ws_dvg + ((size_t)tl.bh * ngq + gi) * 64, h2, dv, sv);
         }
     }
-    if (p.n_g == 0) return;
+    if (ng == 0) return;
 
     // Global keys (B): lane = global key, elements = the home queries of one 32-row
     // sub-tile per wave, minus the queries whose window holds the key (those pairs
@@ -678,9 +685,10 @@ void bwd_dkv_kernel(const BwdParams p) {
     const size_t part0 = ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * ngq;
     const int hs = wv >> 1, hsub = wv & 1;
     const int hq = r0 + kStageKeys * hs + 32 * hsub;  // first home query of this wave
-    for (int gb = 0; gb < p.n_gblk; ++gb) {
+    const int n_gblk_b = (ng + kGlobalQueriesPerBlock - 1) / kGlobalQueriesPerBlock;  // this sequence's blocks
+    for (int gb = 0; gb < n_gblk_b; ++gb) {
         const int gk = gb * kGlobalQueriesPerBlock + (lane & 31);
-        const int g = gk < p.n_g ? p.g[gk] : -1;
+        const int g = gk < ng ? p.g[gofs + gk] : -1;
         const bool gvalid = g >= 0 && (!pad || pad[g] == 0);
         Op kg, vg;
         load_op(kg, gvalid ? K + (size_t)g * 64 : nullptr, h2);
@@ -736,7 +744,7 @@ void bwd_dkv_kernel(const BwdParams p) {
             acc_t(tt, fs, gk_acc);
         }
         __syncthreads();  // done with the staged queries: the ring holds the reductions
-        const int nq = min(kGlobalQueriesPerBlock, p.n_g - gb * kGlobalQueriesPerBlock);
+        const int nq = min(kGlobalQueriesPerBlock, ng - gb * kGlobalQueriesPerBlock);
         const size_t dst = (part0 + (size_t)gb * kGlobalQueriesPerBlock) * 64;
         wave_sum_store(reinterpret_cast<float*>(ring), gk_acc, wv, lane, tid, p.ws_dk + dst, nq);
         wave_sum_store(reinterpret_cast<float*>(ring), gv_acc, wv, lane, tid, p.ws_dv + dst, nq);
@@ -752,6 +760,8 @@ __global__ __launch_bounds__(kThreads) void bwd_merge_kernel(const BwdParams p) 
     const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = bh % p.H, dil = p.dil[h], L = p.L;
+    const int bseq = bh / p.H, gofs = bseq * p.gstride;
+    if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
     const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
     float sq = 0.f, sk = 0.f, sv = 0.f;
@@ -778,7 +788,7 @@ __global__ __launch_bounds__(kThreads) void bwd_merge_kernel(const BwdParams p) 
         sk += red[x][1][d];
         sv += red[x][2][d];
     }
-    const size_t o = (size_t)bh * L * 64 + (size_t)p.g[gi] * 64 + d;
+    const size_t o = (size_t)bh * L * 64 + (size_t)p.g[gofs + gi] * 64 + d;
     reinterpret_cast<uint16_t*>(p.dq)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sq * 0.125f));
     reinterpret_cast<uint16_t*>(p.dk)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sk * 0.125f));
     reinterpret_cast<uint16_t*>(p.dv)[o] = __builtin_bit_cast(uint16_t, (__bf16)sv);

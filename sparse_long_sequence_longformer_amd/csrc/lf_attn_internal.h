@@ -40,8 +40,12 @@ struct Params {
     int tiles_per_head;  // work-groups per (b, h), max over heads (grid partition)
     int rows_per_block;  // rows of one residue class per work-group
     int causal;          // one-sided variant: no pair with its key after its query
+    // Global sets: g[0..n_g) shared by every sequence (gstride 0), or row b at
+    // g[b*gstride ..] with gcnt[b] entries (n_g = the largest count).  Sorted, distinct.
+    int gstride;
     int dil[LF_MAX_HEADS];
-    int g[LF_MAX_GLOBALS];          // sorted, distinct
+    int g[LF_MAX_GLOBALS];
+    int gcnt[LF_MAX_GLOBALS];
 };
 
 // Launchers (defined in lf_attn_kernels.hip).  Return the launch error.
@@ -76,8 +80,10 @@ struct BwdParams {
     int n_gblk;
     int tiles_per_head;
     int causal;  // one-sided variant
+    int gstride;  // global sets as in Params
     int dil[LF_MAX_HEADS];
-    int g[LF_MAX_GLOBALS];  // sorted, distinct
+    int g[LF_MAX_GLOBALS];
+    int gcnt[LF_MAX_GLOBALS];
 };
 
 // Launchers of the layer's pointwise passes (defined in lf_layer.hip).

@@ -522,6 +522,9 @@ void band_kernel(const Params p) {
     const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
     Elem* O = reinterpret_cast<Elem*>(p.out) + off;
     const uint8_t* pad = p.pad ? p.pad + (size_t)b * L : nullptr;
+    // Global set of this sequence: one shared set (gstride 0) or one row per sequence.
+    const int gofs = b * p.gstride;
+    const int ng = p.gstride ? p.gcnt[b] : p.n_g;
     // Tensors of the global rows' own attention (c): the separate projections if given.
     const bool sep = p.kg != nullptr;
     const Elem* QG = sep ? reinterpret_cast<const Elem*>(p.qg) + off : Q;
@@ -545,7 +548,7 @@ void band_kernel(const Params p) {
     const int gbase = r0 - kStageKeys * nb;                    // first key of the grid (<= kb0)
     const int na = max(0, (kend - (r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
     const int n_band = nb + 2 + na;
-    const int n_gst = (p.n_g + kStageKeys - 1) / kStageKeys;
+    const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
     const int n_st = n_gst + n_band;
     // Stage order: one band stage (when there is one besides the home stages), the
     // global stages, the remaining band stages.  A band stage first lets its copy be
@@ -600,7 +603,7 @@ void band_kernel(const Params p) {
 
     // Global slots: source row (or -1 if unused/padded) and in-window position.
     for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
-        const int g = gi < p.n_g ? p.g[gi] : -1;
+        const int g = gi < ng ? p.g[gofs + gi] : -1;
         const bool ok = g >= 0 && (!pad || pad[g] == 0);
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
@@ -634,13 +637,13 @@ void band_kernel(const Params p) {
             const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
             if (lane == 0) glob_mask[s] = inv;
         }
-    for (int gi = tid; gi < p.n_g; gi += kThreads) {
+    for (int gi = tid; gi < ng; gi += kThreads) {
         const int vr = glob_row[gi] - r0;
         if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
     }
     __syncthreads();
     // One-sided variant: the global slots at or before this lane's row.
-    const int gcnt = causal ? count_le(glob_abs, p.n_g, r + qv * dil) : 0;
+    const int gcnt = causal ? count_le(glob_abs, ng, r + qv * dil) : 0;
 
     State st;
     state_init(st);
@@ -667,7 +670,7 @@ void band_kernel(const Params p) {
             }
             issue(sn, kAllParts);
         }
-        if (t == 0 && p.n_g > 0) {  // Q rows of the first 32 global queries, for (c)
+        if (t == 0 && ng > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
             T::dma_rows(gq_rows, [&](int j) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * 64 : zero; },
                         wv, lane);
@@ -704,7 +707,7 @@ void band_kernel(const Params p) {
             if (p.lse && h2 == 0) p.lse[(size_t)bh * L + row] = lse_of(st.cofs, st.l);
         }
     }
-    if (p.n_g == 0) return;
+    if (ng == 0) return;
 
     // (c) Global rows: every key belongs to exactly one work-group's "home" range
     // [r0, r0 + 128) of its class, so each work-group folds the global queries over
@@ -717,7 +720,8 @@ void band_kernel(const Params p) {
     const int home_end = min(Lr, r0 + kRowsPerBlock);
     const size_t part0 = ((size_t)bh * p.tiles_per_head + t_in) * p.n_gblk * kGlobalQueriesPerBlock;
     const int hs = wv >> 1, hsub = wv & 1;  // wave wv folds home keys 32*wv .. 32*wv+31
-    for (int gb = 0; gb < p.n_gblk; ++gb) {
+    const int n_gblk_b = (ng + kGlobalQueriesPerBlock - 1) / kGlobalQueriesPerBlock;  // this sequence's blocks
+    for (int gb = 0; gb < n_gblk_b; ++gb) {
         typename T::QOp gop;
         const char* hslot;
         uint32_t inv32;
@@ -725,7 +729,7 @@ void band_kernel(const Params p) {
             T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
         } else {
             const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
-            T::load_q(gop, gq < p.n_g ? QG + (size_t)p.g[gq] * 64 : nullptr, h2);
+            T::load_q(gop, gq < ng ? QG + (size_t)p.g[gofs + gq] * 64 : nullptr, h2);
         }
         T::scale_q(gop);
         if (gb == 0 && !sep) {
@@ -758,7 +762,7 @@ void band_kernel(const Params p) {
             if (causal) {
                 // keys of this class at or before the global row: virtual index <= vlim
                 const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
-                const int g = gq < p.n_g ? p.g[gq] : -1;
+                const int g = gq < ng ? p.g[gofs + gq] : -1;
                 const int vlim = g >= r ? (g - r) / dil : -1;
                 const int kss = r0 + kStageKeys * hs + 32 * hsub;
                 sub_step<T>(gs, hslot, hsub, lo, gop, 1, inv32, h2, kss + 8 * h2 - vlim + kLargeW, kLargeW, nullptr, 0);
@@ -781,7 +785,7 @@ void band_kernel(const Params p) {
         {
             const int q = tid >> 3, dc = tid & 7;  // 32 queries x 8 column chunks
             const int gq2 = gb * kGlobalQueriesPerBlock + q;
-            if (gq2 < p.n_g) {
+            if (gq2 < ng) {
                 float M = kNegInf;
                 for (int x = 0; x < kWaves; ++x) M = fmaxf(M, red_ml[x][q][0]);
                 float e[kWaves], l = 0.f;
@@ -821,6 +825,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = bh % p.H, dil = p.dil[h], L = p.L;
+    const int bseq = bh / p.H, gofs = bseq * p.gstride;
+    if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
     const int rows = p.rows_per_block;
     const int tpr = ((L + dil - 1) / dil + rows - 1) / rows;
     const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
@@ -862,8 +868,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
         }
     const float res = l > 0.f ? o / l : 0.f;
     Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bh * L * 64;
-    O[(size_t)p.g[gi] * 64 + d] = T::from_float(res);
-    if (p.lse && d == 0) p.lse[(size_t)bh * L + p.g[gi]] = lse_of(M, l);
+    O[(size_t)p.g[gofs + gi] * 64 + d] = T::from_float(res);
+    if (p.lse && d == 0) p.lse[(size_t)bh * L + p.g[gofs + gi]] = lse_of(M, l);
 }
 
 }  // namespace

@@ -217,6 +217,33 @@ def test_layer_host_validation():
 
 
 @needs_lib
+def test_global_mode_validation():
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        assert lib.lf_attn_set_global_mode(h, 5) == 1 and b"global mode" in lib.lf_attn_last_error(h)
+        assert lib.lf_attn_set_global_mode(h, binding.LF_GLOBALS_PER_SEQUENCE) == 0
+        dil = (ctypes.c_int32 * 2)(1, 2)
+        dil_p = ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32))
+
+        def call(B, rows, n):
+            flat = [x for r in rows for x in r]
+            arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+            st = lib.lf_attn_forward(h, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, B, 2, 64, 64, 4, dil_p,
+                                     ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), n, None, None)
+            return st, lib.lf_attn_last_error(h).decode()
+
+        st, msg = call(2, [[1, 64], [0, -1]], 2)
+        assert st == 1 and "global_idx[0][1]" in msg, msg
+        st, msg = call(3, [list(range(100))] * 3, 100)
+        assert st == 2 and "per-sequence" in msg, msg
+        assert lib.lf_attn_set_global_mode(None, 0) == 1
+    finally:
+        lib.lf_attn_destroy(h)
+
+
+@needs_lib
 def test_null_handle():
     lib = binding.load_library()
     assert lib.lf_attn_forward(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None, None, 0, None, None) == 1
