@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="time one whole layer (projections, attention, LayerNorms, GELU feed-forward)")
     ap.add_argument("--ffn", type=int, default=3072, help="feed-forward width of --layer")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward captured in a HIP graph and replayed")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (lf_attn_backward) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -316,6 +318,28 @@ def main():
                              "p90": pct(cold_us, 0.9)},
         "env": {"numpy": np.__version__, "torch": torch.__version__},
     }
+    if args.graph:
+        # The same step captured once (the workspace already exists) and replayed.
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            if args.global_proj:
+                binding.forward_global_proj(qd, kd, vd, qgd, kgd, vgd, wl.w, dil, G, padd, out=out, handle=handle,
+                                            causal=args.causal)
+            else:
+                binding.forward(qd, kd, vd, wl.w, dil, G, padd, out=out, handle=handle, causal=args.causal)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms_g = a.elapsed_time(b) / args.steps
+        res["graph_replay"] = {"ms_per_step": round(ms_g, 6), "value": round(flops / (ms_g * 1e-3) / 1e12, 3)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds)
     print(json.dumps(res), flush=True)
