@@ -31,6 +31,11 @@ What it computes (per batch b and head h, with inputs widened to float64):
   the keys j <= g.  This is the pattern of autoregressive language modelling,
   which the Longformer-explained page lists among the pretraining tasks (§6); the
   pages give no rule for it, and a mask on top of the union is the plainest one.
+* Relative position bias (``bias``: one table of 2w+1 values per head): a window
+  pair j = i + m*dil of a non-global row i scores S_ij + beta_h[m + w]; pairs that
+  enter through the global pattern (global rows, global keys outside the window)
+  get no bias.  Page "基于自注意力机制的长文本建模算法：Longformer详解" §5 names a
+  relative position bias that strengthens the local attention.
 * Per-sequence global sets: ``global_idx`` may hold one row per sequence
   ([B][n], negative entries unused); sequence b then uses its own row as G.
 * Variant with separate global projections (``attention_global_proj``): the page
@@ -122,13 +127,30 @@ def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray
     return m
 
 
-def _attention_rows(q, k, v, m):
+def window_bias(L: int, w: int, dil: int, G: np.ndarray, rows, beta) -> np.ndarray:
+    """Additive bias [R, L]: beta[m + w] where key j = i + m*dil lies in the window of a
+    non-global row i, else 0 (validity is the mask's business)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(L, dtype=np.int64)[None, :]
+    diff = j - rows[:, None]
+    win = window_member(rows[:, None], j, w, dil)
+    is_g = np.zeros(L, dtype=bool)
+    is_g[G] = True
+    win &= ~is_g[rows][:, None]
+    m = np.where(win, diff // dil + w, 0)
+    return np.where(win, np.asarray(beta, dtype=np.float64)[m], 0.0)
+
+
+def _attention_rows(q, k, v, m, extra=None):
     """Masked softmax attention of the query rows in ``q`` against all keys.
 
-    q: [R, d], k, v: [L, d], m: [R, L] boolean.  Returns (O [R, d], P [R, L]).
+    q: [R, d], k, v: [L, d], m: [R, L] boolean, extra: additive scores or None.
+    Returns (O [R, d], P [R, L]).
     """
     d = q.shape[1]
     s = (q @ k.T) / math.sqrt(d)
+    if extra is not None:
+        s = s + extra
     s = np.where(m, s, -np.inf)
     row_max = s.max(axis=1, keepdims=True)
     has_key = np.isfinite(row_max)
@@ -140,7 +162,7 @@ def _attention_rows(q, k, v, m):
 
 
 def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=None,
-                 return_probs: bool = False, causal: bool = False):
+                 return_probs: bool = False, causal: bool = False, bias=None):
     """Oracle for one (batch, head) slice.
 
     q, k, v: [L, d] arrays (widened to float64).  ``rows`` selects query rows
@@ -160,14 +182,16 @@ def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=
     for s0 in range(0, rows.size, ROW_BLOCK):
         blk = rows[s0:s0 + ROW_BLOCK]
         m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal)
-        o, p = _attention_rows(q[blk], k, v, m)
+        extra = None if bias is None else window_bias(L, w, dil, G, blk, bias)
+        o, p = _attention_rows(q[blk], k, v, m, extra) if extra is not None else _attention_rows(q[blk], k, v, m)
         out[s0:s0 + blk.size] = o
         if return_probs:
             probs[s0:s0 + blk.size] = p
     return (out, probs) if return_probs else out
 
 
-def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False):
+def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False,
+              bias=None):
     """Oracle for the full [B, H, L, d] problem.  Returns float64 [B, H, L, d].
 
     ``dil_per_head`` has one dilation per head (w is shared by all heads);
@@ -184,11 +208,13 @@ def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
     for b in range(B):
         for h in range(H):
             out[b, h] = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], globals_of(global_idx, b),
-                                     None if pad is None else pad[b], causal=causal)
+                                     None if pad is None else pad[b], causal=causal,
+                                     bias=None if bias is None else bias[h])
     return out
 
 
-def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, samples, causal: bool = False):
+def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, samples, causal: bool = False,
+                      bias=None):
     """Oracle output rows for a list of (b, h, i) samples, computed one by one.
 
     Used to check full-size runs where the whole oracle would be too slow.
@@ -199,7 +225,8 @@ def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, s
     res = []
     for b, h, i in samples:
         o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], globals_of(global_idx, b),
-                         None if pad is None else pad[b], rows=[i], causal=causal)
+                         None if pad is None else pad[b], rows=[i], causal=causal,
+                         bias=None if bias is None else bias[h])
         res.append(o[0])
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
 
@@ -268,13 +295,17 @@ def attention_global_proj_sampled(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, 
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
 
 
-def _scores_rows(q, k, m):
-    """Masked scores S = Q K^T / sqrt(d) (-inf off the mask) of the query rows in q."""
+def _scores_rows(q, k, m, extra=None):
+    """Masked scores S = Q K^T / sqrt(d) (+ extra) (-inf off the mask) of the query rows in q."""
     d = q.shape[1]
-    return np.where(m, (q @ k.T) / math.sqrt(d), -np.inf)
+    s = (q @ k.T) / math.sqrt(d)
+    if extra is not None:
+        s = s + extra
+    return np.where(m, s, -np.inf)
 
 
-def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False) -> np.ndarray:
+def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False,
+                     bias=None) -> np.ndarray:
     """log sum_{j in keys(i)} exp(q_i . k_j / sqrt(d)) of every row; -inf without keys."""
     q, k = _as_f64(q), _as_f64(k)
     L = k.shape[0]
@@ -282,7 +313,8 @@ def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, caus
     out = np.empty(L, dtype=np.float64)
     for s0 in range(0, L, ROW_BLOCK):
         blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
-        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk, causal=causal))
+        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk, causal=causal),
+                         None if bias is None else window_bias(L, w, dil, G, blk, bias))
         top = s.max(axis=1)
         has = np.isfinite(top)
         safe = np.where(has, top, 0.0)
@@ -291,7 +323,8 @@ def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, caus
     return out
 
 
-def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False) -> np.ndarray:
+def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False,
+                  bias=None) -> np.ndarray:
     """Per-row log-sum-exp of the full problem: float64 [B, H, L]."""
     q, k = _as_f64(q), _as_f64(k)
     B, H, L, _ = q.shape
@@ -301,11 +334,13 @@ def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None
     for b in range(B):
         for h in range(H):
             out[b, h] = attention_lse_bh(q[b, h], k[b, h], w, dil[h], globals_of(global_idx, b),
-                                         None if pad is None else pad[b], causal=causal)
+                                         None if pad is None else pad[b], causal=causal,
+                                         bias=None if bias is None else bias[h])
     return out
 
 
-def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False):
+def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False,
+                          bias=None):
     """Gradients (dQ, dK, dV) of one (batch, head) slice for the upstream gradient dout.
 
     Row blocks of the explicit mask; dK and dV collect every block's contribution.
@@ -319,7 +354,8 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
     for s0 in range(0, L, ROW_BLOCK):
         blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
         m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal)
-        o, p = _attention_rows(q[blk], k, v, m)
+        extra = None if bias is None else window_bias(L, w, dil, G, blk, bias)
+        o, p = _attention_rows(q[blk], k, v, m, extra) if extra is not None else _attention_rows(q[blk], k, v, m)
         dv += p.T @ do[blk]
         dp = do[blk] @ v.T
         delta = (do[blk] * o).sum(axis=1, keepdims=True)
@@ -330,7 +366,7 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
 
 
 def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
-                       causal: bool = False):
+                       causal: bool = False, bias=None):
     """Gradients of the full problem: three float64 [B, H, L, d] arrays (dQ, dK, dV)."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
     B, H, L, d = q.shape
@@ -343,5 +379,5 @@ def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = attention_backward_bh(
                 q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], globals_of(global_idx, b),
-                None if pad is None else pad[b], causal=causal)
+                None if pad is None else pad[b], causal=causal, bias=None if bias is None else bias[h])
     return dq, dk, dv

@@ -624,6 +624,58 @@ def pin_global_sets_per_sequence():
                     for b in range(B) for dd in dil)
 
 
+# ------------------------------------------------------ relative position bias
+
+def pin_bias_sdpa():
+    """Full-window limit (no globals, dil = 1): the biased attention equals torch's CPU
+    scaled_dot_product_attention with the additive mask B[i, j] = beta[j - i + w] in
+    float64; its log-sum-exp and autograd gradients agree as well."""
+    L, w, d = 40, 40, 16
+    q, k, v, do = (_rand((L, d), 700 + t) for t in range(4))
+    beta = _rand((2 * w + 1,), 704)
+    i = np.arange(L)
+    Bm = beta[(i[None, :] - i[:, None]) + w]
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None],
+                                                           attn_mask=torch.from_numpy(Bm)[None, None])[0, 0]
+    got = orc.attention_bh(q, k, v, w, 1, bias=beta)
+    assert np.abs(got - ref.detach().numpy()).max() < 1e-12
+    lse = orc.attention_lse_bh(q, k, w, 1, bias=beta)
+    s = q @ k.T / math.sqrt(d) + Bm
+    assert np.abs(lse - (s.max(1) + np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)))).max() < 1e-12
+    (ref * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = orc.attention_backward_bh(q, k, v, do, w, 1, bias=beta)
+    for a, b in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(a - b.numpy()).max() < 1e-12
+
+
+def pin_bias_shift_and_scope():
+    """A constant bias changes nothing without globals (softmax shift invariance); with
+    globals, only window pairs of non-global rows are biased: a global row is unchanged,
+    and a brute-force listing of one non-global row's scores matches."""
+    L, w, dil, d = 36, 3, 2, 8
+    q, k, v = (_rand((L, d), 710 + t) for t in range(3))
+    pad = np.zeros(L, dtype=bool)
+    pad[[5, 30]] = True
+    base = orc.attention_bh(q, k, v, w, dil, None, pad)
+    const = orc.attention_bh(q, k, v, w, dil, None, pad, bias=np.full(2 * w + 1, 2.5))
+    assert np.abs(base - const).max() < 1e-12
+    G = [4, 33]
+    beta = _rand((2 * w + 1,), 713)
+    got = orc.attention_bh(q, k, v, w, dil, G, pad, bias=beta)
+    assert np.array_equal(got[G], orc.attention_bh(q, k, v, w, dil, G, pad)[G])
+    i = 14
+    keys = brute.key_set(i, L, w, dil, G, pad.tolist())
+    sc = []
+    for j in keys:
+        t = math.fsum(q[i, c] * k[j, c] for c in range(d)) / math.sqrt(d)
+        if (j - i) % dil == 0 and abs(j - i) <= w * dil:
+            t += beta[(j - i) // dil + w]
+        sc.append(t)
+    e = np.exp(np.array(sc) - max(sc))
+    assert np.abs(got[i] - (e / e.sum()) @ v[keys]).max() < 1e-12
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -653,6 +705,8 @@ ALL_PINS = [
     pin_causal_prefix,
     pin_causal_backward_autograd,
     pin_global_sets_per_sequence,
+    pin_bias_sdpa,
+    pin_bias_shift_and_scope,
     pin_layer_torch_encoder,
     pin_layer_norm_rows,
 ]

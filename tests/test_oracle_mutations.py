@@ -77,11 +77,11 @@ def _mask_pad_ignored(L, w, dil, G, pad_row, rows, causal=False):
     return _orig_mask(L, w, dil, G, None, rows, causal=causal)
 
 
-def _rows_scale_d(q, k, v, m):  # 1/d instead of 1/sqrt(d)
-    return _orig_rows(q / math.sqrt(q.shape[1]), k, v, m)
+def _rows_scale_d(q, k, v, m, extra=None):  # 1/d instead of 1/sqrt(d)
+    return _orig_rows(q / math.sqrt(q.shape[1]), k, v, m, extra)
 
 
-def _rows_transposed(q, k, v, m):  # S^T = K Q^T used where S = Q K^T was meant
+def _rows_transposed(q, k, v, m, extra=None):  # S^T = K Q^T used where S = Q K^T was meant
     d = q.shape[1]
     if q.shape[0] != k.shape[0]:
         raise ValueError("transposed scores need a square block")
@@ -94,12 +94,12 @@ def _rows_transposed(q, k, v, m):  # S^T = K Q^T used where S = Q K^T was meant
     return p @ v, p
 
 
-def _rows_pk(q, k, v, m):  # weights applied to K instead of V
+def _rows_pk(q, k, v, m, extra=None):  # weights applied to K instead of V
     o, p = _orig_rows(q, k, v, m)
     return p @ k, p
 
 
-def _rows_zero_fill(q, k, v, m):  # out-of-pattern scores left at 0 instead of excluded
+def _rows_zero_fill(q, k, v, m, extra=None):  # out-of-pattern scores left at 0 instead of excluded
     d = q.shape[1]
     s = np.where(m, (q @ k.T) / math.sqrt(d), 0.0)
     e = np.exp(s - s.max(axis=1, keepdims=True))
@@ -107,7 +107,7 @@ def _rows_zero_fill(q, k, v, m):  # out-of-pattern scores left at 0 instead of e
     return p @ v, p
 
 
-def _rows_nan_empty(q, k, v, m):  # no guard for rows without keys
+def _rows_nan_empty(q, k, v, m, extra=None):  # no guard for rows without keys
     d = q.shape[1]
     s = np.where(m, (q @ k.T) / math.sqrt(d), -np.inf)
     with np.errstate(invalid="ignore", divide="ignore"):
@@ -203,6 +203,16 @@ def _split_interleaved(t, H):  # head h takes every H-th feature
     return t.reshape(B, L, E // H, H).transpose(0, 3, 1, 2)
 
 
+def _bias_reversed(L, w, dil, G, rows, beta):  # table read backwards (m -> -m)
+    return _orig_bias(L, w, dil, G, rows, np.asarray(beta)[::-1])
+
+
+def _bias_on_global_rows(L, w, dil, G, rows, beta):  # global rows biased too
+    return _orig_bias(L, w, dil, np.zeros(0, dtype=np.int64), rows, beta)
+
+
+_orig_bias = orc.window_bias
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -222,6 +232,8 @@ MUTANTS = {
     "global_proj_uses_k": ("attention_global_proj", _gp_uses_k),
     "global_proj_uses_q": ("attention_global_proj", _gp_uses_q),
     "global_proj_uses_v": ("attention_global_proj", _gp_uses_v),
+    "bias_reversed": ("window_bias", _bias_reversed),
+    "bias_on_global_rows": ("window_bias", _bias_on_global_rows),
     "layer_ln_unbiased": ("layer:layer_norm", _ln_unbiased),
     "layer_gelu_tanh": ("layer:gelu", _gelu_tanh),
     "layer_heads_interleaved": ("layer:split_heads", _split_interleaved),
