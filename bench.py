@@ -59,6 +59,9 @@ def parse():
                     help="global rows use their own q/k/v projections (lf_attn_forward_global_proj)")
     ap.add_argument("--causal", action="store_true",
                     help="one-sided variant: no pair with its key after its query")
+    ap.add_argument("--bias", type=float, default=0.0, metavar="SCALE",
+                    help="relative position bias on window scores: a seeded N(0, SCALE^2) table per head "
+                         "(0: none)")
     ap.add_argument("--layer", action="store_true",
                     help="time one whole layer (projections, attention, LayerNorms, GELU feed-forward)")
     ap.add_argument("--ffn", type=int, default=3072, help="feed-forward width of --layer")
@@ -91,7 +94,7 @@ def traffic_for(workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, q, k, v, G, pad, target_s):
+def cpu_baseline(wl, q, k, v, G, pad, target_s, causal=False, bias=None):
     """The fp64 oracle on whole (b, h) slices of the workload, one after another,
     until about target_s seconds of CPU work; BLAS limited to one thread."""
     from threadpoolctl import threadpool_limits
@@ -107,9 +110,10 @@ def cpu_baseline(wl, q, k, v, G, pad, target_s):
         for b in range(wl.B):
             for h in range(wl.H):
                 orc.attention_bh(q[b, h], k[b, h], v[b, h], wl.w, wl.dil[h], G,
-                                 None if pad_np is None else pad_np[b])
+                                 None if pad_np is None else pad_np[b], causal=causal,
+                                 bias=None if bias is None else bias[h])
                 pr = None if pad_np is None else pad_np[b:b + 1]
-                pairs += pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr).total
+                pairs += pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr, causal=causal).total
                 done.append((b, h))
                 if time.perf_counter() - t0 >= target_s:
                     break
@@ -171,6 +175,10 @@ def main():
     handle = binding.LfAttn(wl.dtype)
     if args.causal:
         handle.set_causal(True)
+    bias_tab = None
+    if args.bias:
+        bias_tab = workloads.make_bias(wl.H, wl.w, seed=wl.seed, scale=args.bias)
+        handle.set_position_bias(torch.from_numpy(bias_tab).to(dev))
     dil = wl.dil_list()
 
     # One checked call through the Python wrapper, then the timed loops call the C entry
@@ -231,7 +239,7 @@ def main():
     handle.set_stage_timing(False)
     stage_avg = {k2: v2[0] / v2[1] for k2, v2 in st.items() if v2[1]}
     k_avg_ms = stage_avg["band"]  # the dominant kernel
-    traffic = None if (args.global_proj or args.causal) else traffic_for(name)
+    traffic = None if (args.global_proj or args.causal or args.bias) else traffic_for(name)
 
     # Trials (median / min / p90 of per-step time) and cold steps (Infinity Cache evicted).
     def timed(n):
@@ -297,13 +305,15 @@ def main():
             "parallelism": "single GPU",
             "global_projections": "separate" if args.global_proj else "shared",
             "window": "one-sided" if args.causal else "symmetric",
+            "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None,
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "attended_pairs": pairs.total,
         "effective_flop_per_step": flops,
         "kernel_ms_avg": {k2: round(v2, 6) for k2, v2 in stage_avg.items()},
         "roofline": {
-            "kernel": f"lf::band_kernel<{'Bf16' if wl.dtype == 'bf16' else 'F32'}, {str(args.causal).lower()}>",
+            "kernel": f"lf::band_kernel<{'Bf16' if wl.dtype == 'bf16' else 'F32'}, {str(args.causal).lower()}, "
+                      f"{str(bool(args.bias)).lower()}>",
             **roof,
             "traffic": traffic,
             "avg_launch_ms": round(k_avg_ms, 6),
@@ -341,7 +351,7 @@ def main():
         ms_g = a.elapsed_time(b) / args.steps
         res["graph_replay"] = {"ms_per_step": round(ms_g, 6), "value": round(flops / (ms_g * 1e-3) / 1e12, 3)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds, args.causal, bias_tab)
     print(json.dumps(res), flush=True)
 
 
@@ -407,7 +417,8 @@ def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
         "data": "synthetic (seeded N(0,1) activations, N(0, 0.05^2) weights)",
         "config": {"workload": name, "B": wl.B, "seq_len": wl.L, "hidden": E, "heads": wl.H, "ffn": F, "w": wl.w,
                    "n_global": len(G), "parallelism": "single GPU",
-                   "window": "one-sided" if args.causal else "symmetric"},
+                   "window": "one-sided" if args.causal else "symmetric",
+                   "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None},
         "tokens_per_s": round(R / (ms * 1e-3), 1),
         "gemm_flop": gemm_flops, "attention_flop": flops_attn,
         "stage_ms_per_layer": {k2: round(v2, 6) for k2, v2 in per_call.items()},
@@ -500,7 +511,8 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
         "config": {"workload": name, "B": wl.B, "H": wl.H, "seq_len": wl.L, "d_h": wl.d, "w": wl.w,
                    "dil": sorted(set(dil)), "n_global": len(G), "padded_lengths": list(wl.lengths) or None,
                    "global_batch": wl.B, "parallelism": "single GPU",
-                   "window": "one-sided" if args.causal else "symmetric"},
+                   "window": "one-sided" if args.causal else "symmetric",
+                   "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "train_step_ms": round(ms_train, 6),
         "train_step_tflops": round(3.5 * flops_fwd / (ms_train * 1e-3) / 1e12, 3),

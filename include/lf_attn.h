@@ -50,6 +50,7 @@ typedef enum lf_dtype {
 #define LF_MAX_HEADS 64
 #define LF_MAX_GLOBALS 256
 #define LF_HEAD_DIM 64
+#define LF_MAX_BIAS_W 1024 /* widest window with a relative position bias */
 
 /* Kernel launches timed by lf_attn_stage_times. */
 #define LF_N_STAGES 8
@@ -195,12 +196,38 @@ lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k,
 lf_status lf_attn_set_window_mode(lf_attn_t h, int mode);
 
 /*
+ * Relative position bias on the window scores of every later call on `h`
+ * (forward, forward_lse, forward_global_proj, backward, layer).
+ *
+ * Page "基于自注意力机制的长文本建模算法：Longformer详解" §5 adds a relative
+ * position bias to strengthen the local attention.  Read as a learned scalar per
+ * head and window offset: a pair (i, j = i + m*dil_h) that row i attends through
+ * its window (i not global, |m| <= w; m <= 0 in the causal mode) scores
+ *     S_ij = q_i . k_j / sqrt(d_h) + table[h][m + w];
+ * pairs that enter through the global pattern (global rows; global keys outside
+ * the row's window) get no bias.  A global key inside the window is a window pair.
+ *
+ * table   : DEVICE fp32 [n_heads][2*w + 1], 4-byte aligned, caller-owned; it is
+ *           borrowed, not copied: it must stay valid and unchanged while calls on
+ *           `h` that use it are in flight.  NULL removes the bias (n_heads and w
+ *           are then ignored).
+ * n_heads : 1 .. LF_MAX_HEADS; every later call must pass H == n_heads.
+ * w       : 0 .. LF_MAX_BIAS_W; every later call must pass the same w.
+ * The backward returns dQ, dK and dV with the bias held fixed (no gradient of
+ * the table).  Errors: LF_ERR_INVALID_ARG (h == NULL, n_heads out of range,
+ * misaligned table), LF_ERR_UNSUPPORTED (w > LF_MAX_BIAS_W); the setting is then
+ * unchanged.  A later call with another H or w fails with LF_ERR_INVALID_ARG.
+ */
+lf_status lf_attn_set_position_bias(lf_attn_t h, const float* table, int n_heads, int w);
+
+/*
  * One Longformer layer around the attention (bf16 handles only):
  *
  *   q, k, v = split_heads(x W_qkv^T + b_qkv)     (rows of W_qkv: q, then k, then v;
  *                                                 head h = features 64h .. 64h+63)
  *   a       = merge_heads(attention(q, k, v))    (this library's forward, with the
- *                                                 handle's window mode)
+ *                                                 handle's window mode and
+ *                                                 position bias)
  *   x1      = LayerNorm1(x + a W_o^T + b_o)
  *   out     = LayerNorm2(x1 + GELU(x1 W_1^T + b_1) W_2^T + b_2)
  *

@@ -26,6 +26,7 @@ STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge", "l
 LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
 MAX_HEADS = 64
 MAX_GLOBALS = 256
+MAX_BIAS_W = 1024
 
 # Every symbol declared in include/lf_attn.h.
 EXPORTS = (
@@ -41,6 +42,7 @@ EXPORTS = (
     "lf_attn_set_stage_timing",
     "lf_attn_set_window_mode",
     "lf_attn_set_global_mode",
+    "lf_attn_set_position_bias",
     "lf_attn_stage_times",
 )
 
@@ -103,6 +105,8 @@ def load_library():
     lib.lf_attn_set_global_mode.restype = i32
     lib.lf_attn_set_window_mode.argtypes = [vp, i32]
     lib.lf_attn_set_window_mode.restype = i32
+    lib.lf_attn_set_position_bias.argtypes = [vp, vp, i32, i32]
+    lib.lf_attn_set_position_bias.restype = i32
     lib.lf_attn_set_stage_timing.argtypes = [vp, i32]
     lib.lf_attn_set_stage_timing.restype = i32
     lib.lf_attn_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -130,6 +134,7 @@ class LfAttn:
         self.handle = h
         self.causal = False
         self.per_sequence_globals = False
+        self.bias = None  # the table set by set_position_bias (kept alive here)
 
     def _check(self, st, h=None):
         if st != LF_OK:
@@ -205,6 +210,24 @@ class LfAttn:
         self._check(self.lib.lf_attn_set_window_mode(self.handle, mode), self.handle)
         self.causal = bool(causal)
 
+    def set_position_bias(self, table):
+        """Relative position bias for every later call: a contiguous float32 device
+        tensor [H, 2w + 1] (entry m + w for window offset m), or None to remove it.
+        The handle keeps a reference: the library borrows the memory."""
+        if table is None:
+            self._check(self.lib.lf_attn_set_position_bias(self.handle, None, 0, 0), self.handle)
+            self.bias = None
+            return
+        import torch
+
+        if (table.dtype != torch.float32 or table.dim() != 2 or not table.is_cuda or not table.is_contiguous()
+                or table.shape[1] % 2 != 1):
+            raise ValueError("the bias table must be a contiguous float32 device tensor [H, 2w + 1]")
+        H, n = table.shape
+        self._check(self.lib.lf_attn_set_position_bias(self.handle, table.data_ptr(), H, (n - 1) // 2),
+                    self.handle)
+        self.bias = table
+
     def layer_raw(self, x_ptr, weights: LayerWeights, out_ptr, B, L, hidden, ffn, eps, w, dil, global_idx, pad_ptr,
                   stream):
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
@@ -246,6 +269,22 @@ def _handle_for(dtype: str, causal: bool = False, per_seq: bool = False) -> LfAt
             h.set_per_sequence_globals(True)
         _handles[key] = h
     return _handles[key]
+
+
+class _CallBias:
+    """Installs a per-call bias table on a handle and restores its previous one."""
+
+    def __init__(self, h: LfAttn, bias):
+        self.h, self.bias, self.prev = h, bias, h.bias
+
+    def __enter__(self):
+        if self.bias is not None:
+            self.h.set_position_bias(self.bias)
+
+    def __exit__(self, *exc):
+        if self.bias is not None:
+            self.h.set_position_bias(self.prev)
+        return False
 
 
 def _global_arg(global_idx, B: int):
@@ -316,7 +355,7 @@ def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=Fa
 
 
 def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None,
-            causal: bool = False):
+            causal: bool = False, bias=None):
     """Longformer window + global attention forward on the GPU.
 
     q, k, v: contiguous CUDA/HIP tensors [B, H, L, 64], all bfloat16 or all float32.
@@ -325,20 +364,22 @@ def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, 
     key_pad_mask: [B, L] bool/uint8 device tensor, nonzero = padded key, or None.
     causal: the one-sided variant (no key after its query); a given handle must be in
     the same mode.
+    bias: relative position bias on window scores, float32 device tensor [H, 2w + 1],
+    for this call only; None leaves the handle's own setting (none by default).
     Returns ``out`` (allocated if not given), same shape and dtype as q.
     """
     import torch
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
         q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal)
-    with torch.cuda.device(q.device):
+    with torch.cuda.device(q.device), _CallBias(h, bias):
         h.forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
                       global_idx, pad_ptr, stream)
     return out
 
 
 def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, key_pad_mask=None, out=None,
-                        handle: LfAttn | None = None, causal: bool = False):
+                        handle: LfAttn | None = None, causal: bool = False, bias=None):
     """As ``forward``, but the global query rows attend every unpadded key with their
     own projections q_g, k_g, v_g (tensors shaped and typed like q); every other row
     uses q, k, v."""
@@ -347,7 +388,7 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
         q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)], w, dil, global_idx,
         key_pad_mask, out, handle, causal)
-    with torch.cuda.device(q.device):
+    with torch.cuda.device(q.device), _CallBias(h, bias):
         h.forward_global_proj_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_g.data_ptr(), k_g.data_ptr(),
                                   v_g.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil, global_idx,
                                   pad_ptr, stream)
@@ -355,7 +396,7 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
 
 
 def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, lse=None,
-                handle: LfAttn | None = None, causal: bool = False):
+                handle: LfAttn | None = None, causal: bool = False, bias=None):
     """``forward`` that also returns each row's log-sum-exp: (out, lse), lse a float32
     device tensor [B, H, L] (natural log, -inf for rows without keys)."""
     import torch
@@ -366,18 +407,19 @@ def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=No
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
-    with torch.cuda.device(q.device):
+    with torch.cuda.device(q.device), _CallBias(h, bias):
         h.forward_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, L, d_h,
                           int(w), dil, global_idx, pad_ptr, stream)
     return out, lse
 
 
 def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask=None, dq=None, dk=None,
-             dv=None, handle: LfAttn | None = None, causal: bool = False):
+             dv=None, handle: LfAttn | None = None, causal: bool = False, bias=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dout``.
 
     q, k, v, out, dout: contiguous bf16 device tensors [B, H, L, 64]; ``out`` and
-    ``lse`` as returned by ``forward_lse`` for the same inputs and pattern.
+    ``lse`` as returned by ``forward_lse`` for the same inputs and pattern (and bias:
+    the table is held fixed, no gradient of it is returned).
     """
     import torch
 
@@ -396,7 +438,7 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
             raise ValueError("dq, dk, dv must be contiguous device tensors like q")
         res.append(t)
     dq, dk, dv = res
-    with torch.cuda.device(q.device):
+    with torch.cuda.device(q.device), _CallBias(h, bias):
         h.backward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d_h, int(w), dil, global_idx, pad_ptr,
                        stream)
@@ -404,7 +446,7 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
 
 
 def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=None, eps: float = 1e-5, out=None,
-                  handle: LfAttn | None = None, causal: bool = False):
+                  handle: LfAttn | None = None, causal: bool = False, bias=None):
     """One Longformer layer (projections, this attention, LayerNorms, GELU feed-forward).
 
     x: contiguous bf16 device tensor [B, L, hidden]; ``weights`` maps LAYER_WEIGHTS to
@@ -441,6 +483,6 @@ def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=N
         raise ValueError("handle global mode does not match the shape of global_idx")
     wts = LayerWeights(*[weights[n].data_ptr() for n in LAYER_WEIGHTS])
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    with torch.cuda.device(x.device):
+    with torch.cuda.device(x.device), _CallBias(h, bias):
         h.layer_raw(x.data_ptr(), wts, out.data_ptr(), B, L, E, F, eps, int(w), dil, global_idx, pad_ptr, stream)
     return out

@@ -31,6 +31,9 @@ struct lf_attn_s {
     lf_dtype dtype;
     int window_mode = LF_WINDOW_SYMMETRIC;
     int global_mode = LF_GLOBALS_SHARED;
+    const float* bias = nullptr;  // borrowed [bias_heads][2 * bias_w + 1], or null
+    int bias_heads = 0;
+    int bias_w = 0;
     int device = -1;
     char* ws = nullptr;  // global-row partials of the forward
     size_t ws_bytes = 0;
@@ -156,6 +159,27 @@ lf_status lf_attn_set_window_mode(lf_attn_t h, int mode) {
     return LF_OK;
 }
 
+lf_status lf_attn_set_position_bias(lf_attn_t h, const float* table, int n_heads, int w) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (!table) {
+        h->bias = nullptr;
+        h->bias_heads = h->bias_w = 0;
+        return LF_OK;
+    }
+    if (n_heads < 1 || n_heads > LF_MAX_HEADS)
+        return fail(h, LF_ERR_INVALID_ARG, "need 1 <= n_heads <= %d (got %d)", LF_MAX_HEADS, n_heads);
+    if (w < 0) return fail(h, LF_ERR_INVALID_ARG, "need w >= 0 (got %d)", w);
+    if (w > LF_MAX_BIAS_W)
+        return fail(h, LF_ERR_UNSUPPORTED, "position bias: at most w = %d (got %d)", LF_MAX_BIAS_W, w);
+    if ((reinterpret_cast<uintptr_t>(table) & 3u) != 0)
+        return fail(h, LF_ERR_INVALID_ARG, "the bias table must be 4-byte aligned");
+    h->bias = table;
+    h->bias_heads = n_heads;
+    h->bias_w = w;
+    return LF_OK;
+}
+
 lf_status lf_attn_set_stage_timing(lf_attn_t h, int enable) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->timing = enable != 0;
@@ -216,6 +240,9 @@ lf_status make_plan(lf_attn_t h, Plan& pl, int B, int H, int L, int d_h, int w, 
     if (n_global > LF_MAX_GLOBALS)
         return fail(h, LF_ERR_UNSUPPORTED, "at most %d global indices (got %d)", LF_MAX_GLOBALS, n_global);
     if (n_global > 0 && !global_idx) return fail(h, LF_ERR_INVALID_ARG, "global_idx is NULL but n_global > 0");
+    if (h->bias && (H != h->bias_heads || w != h->bias_w))
+        return fail(h, LF_ERR_INVALID_ARG, "the position bias table is for H = %d, w = %d (call: H = %d, w = %d)",
+                    h->bias_heads, h->bias_w, H, w);
     const size_t elem = h->dtype == LF_BF16 ? 2 : 4;
     const uint64_t n_elem = static_cast<uint64_t>(B) * H * L * LF_HEAD_DIM;
     if (n_elem / LF_HEAD_DIM / L / H != static_cast<uint64_t>(B) || n_elem > (uint64_t(1) << 40))
@@ -369,6 +396,8 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     p.rows_per_block = lf::kRowsPerBlock;
     p.tiles_per_head = pl.tiles;
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;
+    p.bias = h->bias;
+    p.bias_w = h->bias_w;
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
@@ -441,6 +470,8 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     p.n_gblk = pl.n_gblk;
     p.tiles_per_head = pl.tiles;
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;
+    p.bias = h->bias;
+    p.bias_w = h->bias_w;
 
     // Workspace: three row-statistic arrays, then the global partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");

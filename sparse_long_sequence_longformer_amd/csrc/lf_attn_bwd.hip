@@ -208,6 +208,19 @@ __device__ __forceinline__ uint32_t bits_below(int hi) {
     return hi <= 0 ? 0u : (hi >= 32 ? ~0u : ((1u << hi) - 1u));
 }
 
+// Relative position bias table of head h in LDS, base 2, with kBiasPad zeros on both
+// ends: entry kBiasPad + w + m holds offset m (reversed: offset -m).
+__device__ __forceinline__ void fill_bias(float* lds, const BwdParams& p, int h, int w, int tid, bool reversed) {
+    const float* tab = p.bias + (size_t)h * (2 * p.bias_w + 1) + p.bias_w;  // entry of offset 0
+    for (int t = tid; t < 2 * w + 1 + 2 * kBiasPad; t += kThreads) {
+        const int m = (reversed ? -1 : 1) * (t - kBiasPad - w);
+        lds[t] = (m >= -w && m <= w) ? tab[m] * kLog2eF : 0.f;
+    }
+}
+__device__ __forceinline__ void add_bias(f32x16& s, const float* brow) {
+    for (int i = 0; i < 16; ++i) s[i] += brow[kc_of(i)];
+}
+
 __device__ __forceinline__ f32x16 splat(float x) {
     f32x16 s;
     for (int i = 0; i < 16; ++i) s[i] = x;
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // rows r0 + 32*wv .. +31, one per lane (both lane halves).  Stages: the global keys
 // (with the in-window test, so each key counts once), then the window band.
 
-template <bool kCausal>
+template <bool kCausal, bool kBias>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
@@ -322,6 +335,7 @@ void bwd_dq_kernel(const BwdParams p) {
     __shared__ int glob_abs[LF_MAX_GLOBALS];
     __shared__ int glob_row[LF_MAX_GLOBALS];
     __shared__ uint32_t row_glob[kRowsPerBlock / 32];
+    __shared__ float bias_lds[kBias ? kBiasLds : 1];  // offset m at kBiasPad + m + w, base 2
 
     // Keys of a row: w class steps before it and wr after (wr = 0 one-sided).
     constexpr bool causal = kCausal;
@@ -403,6 +417,7 @@ void bwd_dq_kernel(const BwdParams p) {
     }
     if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
     if (pad) fill_band_masks(0);
+    if (kBias) fill_bias(bias_lds, p, tl.h, w, tid, false);
     __syncthreads();
     if (wv == 0)
         for (int s = 0; s < n_gst; ++s) {
@@ -448,6 +463,7 @@ void bwd_dq_kernel(const BwdParams p) {
             const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
             const int mode = gstage ? 2 : (interior ? 0 : 1);
             f32x16 s = prod(slot, sub, lo, qop, seed_s);  // scores - lse, base 2
+            if (kBias && !gstage) add_bias(s, bias_lds + kBiasPad + kss + 8 * h2 - qv + w);
             const int goff = kStageKeys * t + 32 * sub + 8 * h2;
             mask_scores(s, mode, inv32, h2, kss + 8 * h2 - qv + w, span, glob_pos + goff, w - qv,
                         causal ? gcnt - goff : 1 << 30);
@@ -543,12 +559,13 @@ void bwd_dq_kernel(const BwdParams p) {
 // unpadded key is theirs), then the window band of queries (global queries are
 // removed there by lse2_band = +inf: their weights are 0).
 
-template <bool kCausal>
+template <bool kCausal, bool kBias>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkv_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ int own_gidx[kRowsPerBlock];  // index in g of each own key, or -1
     __shared__ int gq_pos[LF_MAX_GLOBALS];  // position of each global slot (sorted)
+    __shared__ float bias_lds[kBias ? kBiasLds : 1];  // reversed: offset m at kBiasPad + w - m, base 2
 
     // Queries of a key: query - key in [-wl, w] class steps (wl = 0 one-sided: no query
     // before its key).
@@ -605,6 +622,7 @@ void bwd_dkv_kernel(const BwdParams p) {
 
     if (tid < kRowsPerBlock) own_gidx[tid] = -1;
     for (int gi = tid; gi < ng; gi += kThreads) gq_pos[gi] = p.g[gofs + gi];
+    if (kBias) fill_bias(bias_lds, p, tl.h, w, tid, true);
     __syncthreads();
     for (int gi = tid; gi < ng; gi += kThreads) {
         const int g = p.g[gofs + gi];
@@ -643,6 +661,8 @@ void bwd_dkv_kernel(const BwdParams p) {
             const bool interior = !gstage && kss >= qa + 31 - wl && kss + 31 <= qa + w;
             const int mode = (gstage || interior) ? 0 : 1;
             f32x16 s = prod(slot, sub, lo, kop, row_seed(slot + kLseOff, sub, h2));  // scores - lse, base 2
+            // element i: query kss + 8*h2 + kc, key qv, offset m = qv - query: reversed table
+            if (kBias && !gstage) add_bias(s, bias_lds + kBiasPad + kss + 8 * h2 - qv + w);
             mask_scores(s, mode, 0u, h2, kss + 8 * h2 - qv + wl, span, nullptr, 0);
             if (gstage && causal) {  // a global query sees no key after it: slots from gfirst on
                 const uint32_t keep = bits_from(gfirst - (kStageKeys * t + 32 * sub + 8 * h2));
@@ -807,20 +827,26 @@ hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-    if (p.causal)
-        hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, p);
+#define LF_DQ(C, Bi) hipLaunchKernelGGL((bwd_dq_kernel<C, Bi>), dim3(blocks), dim3(kThreads), 0, s, p)
+    if (p.causal) {
+        if (p.bias) LF_DQ(true, true); else LF_DQ(true, false);
+    } else {
+        if (p.bias) LF_DQ(false, true); else LF_DQ(false, false);
+    }
+#undef LF_DQ
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-    if (p.causal)
-        hipLaunchKernelGGL(bwd_dkv_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(bwd_dkv_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, p);
+#define LF_DKV(C, Bi) hipLaunchKernelGGL((bwd_dkv_kernel<C, Bi>), dim3(blocks), dim3(kThreads), 0, s, p)
+    if (p.causal) {
+        if (p.bias) LF_DKV(true, true); else LF_DKV(true, false);
+    } else {
+        if (p.bias) LF_DKV(false, true); else LF_DKV(false, false);
+    }
+#undef LF_DKV
     return hipGetLastError();
 }
 

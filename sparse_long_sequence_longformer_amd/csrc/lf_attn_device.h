@@ -30,6 +30,13 @@ constexpr float kScaleLog2 = 1.4426950408889634f * 0.125f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kStageKeys = kKeysPerTile;  // 64
 constexpr int kNoPos = -(1 << 29);        // virtual position that is in no window
+// Relative position bias tables in LDS: windows up to kMaxBiasW keys per side, with
+// kBiasPad zeros on both ends (a processed 32-key sub-tile reads at most 94 entries
+// beyond the window on either side).
+constexpr int kMaxBiasW = LF_MAX_BIAS_W;
+constexpr int kBiasPad = 96;
+constexpr int kBiasLds = 2 * kMaxBiasW + 1 + 2 * kBiasPad;
+constexpr float kLog2eF = 1.4426950408889634f;
 constexpr int kLargeW = 1 << 28;  // band test that admits every key (|key - query| < 2^28)
 
 // Source of every invalid key: 256 zero bytes (one fp32 row, two bf16 rows).

@@ -30,6 +30,8 @@ struct Params {
     const void* vg;
     const uint8_t* pad;  // [B][L] or nullptr
     float* lse;          // [B][H][L] natural-log sum of each row's exp(scores), or nullptr
+    const float* bias;   // relative position bias [H][2*bias_w + 1] of window pairs, or nullptr
+    int bias_w;
     // Global-row partials: one (max, sum, 64 outputs) per (b*H + h, row tile, global
     // query), written by every work-group for its own 128 "home" keys.
     float* ws_ml;        // [B*H][tiles_per_head][n_gblk*32][2]
@@ -64,6 +66,8 @@ struct BwdParams {
     void* dv;
     const uint8_t* pad;  // [B][L] or nullptr
     const float* lse;    // [B][H][L] natural-log row sums of the forward
+    const float* bias;   // relative position bias as in Params, or nullptr
+    int bias_w;
     // Row statistics written by the prep kernel, [B][H][L] each:
     float* lse2;       // lse in base-2 units of the pre-scaled scores; +inf for rows without keys
     float* lse2_band;  // same, and +inf for global rows (they are not window queries)

@@ -462,12 +462,20 @@ __device__ __forceinline__ void fold_tile(State& st, const f32x16& x, typename T
 }
 
 
+// Relative position bias of a window sub-tile: element i of the lane holds the key at
+// offset base + kc_of(i) in the (padded, base-2) table row starting at brow.
+__device__ __forceinline__ void add_bias_run(f32x16& s, const float* brow) {
+    for (int i = 0; i < 16; ++i) s[i] += brow[kc_of(i)];
+}
+
 // One 32-key sub-tile of a stage: scores, masks, softmax update, P.V product.
 template <class T>
 __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, const typename T::Lane& lo,
                                          const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
-                                         int span, const int* gp, int wq, int climit = 1 << 30) {
+                                         int span, const int* gp, int wq, int climit = 1 << 30,
+                                         const float* brow = nullptr) {
     f32x16 s = T::qk(slot, sub, lo, q, st.seed);  // exponents: scores - cofs
+    if (brow) add_bias_run(s, brow);
     typename T::VOp vo;
     T::load_v(vo, slot, sub, lo);  // in flight during the softmax
     mask_scores(s, mode, inv32, h2, base, span, gp, wq, climit);
@@ -488,7 +496,7 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 // sub-tiles outside its rows' band and masks only sub-tiles that touch the band
 // edge or hold invalid keys.
 
-template <class T, bool kCausal>
+template <class T, bool kCausal, bool kBias>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const Params p) {
     using Elem = typename T::Elem;
@@ -500,6 +508,9 @@ void band_kernel(const Params p) {
     __shared__ int glob_abs[LF_MAX_GLOBALS];          // position of each global slot (sorted)
     __shared__ int glob_row[LF_MAX_GLOBALS];          // same as glob_pos, padded or not
     __shared__ int glob_g[kGlobalQueriesPerBlock];    // first 32 global positions (or -1)
+    // Relative position bias of this head, base 2, offset m at kBiasPad + m + w (zero padding
+    // around it covers every lane's reads of a processed sub-tile).
+    __shared__ float bias_lds[kBias ? kBiasLds : 1];
     __shared__ uint32_t row_glob[kRowsPerBlock / 32]; // tile rows that are global queries
     __shared__ __attribute__((aligned(16))) char gq_rows[kGlobalQueriesPerBlock * T::kRowBytes];  // first 32 global Q rows
 
@@ -631,6 +642,13 @@ void band_kernel(const Params p) {
         }
     };
     if (pad) fill_band_masks(0);
+    if (kBias) {
+        const float* tab = p.bias + (size_t)h * (2 * p.bias_w + 1) + p.bias_w;  // entry of offset 0
+        for (int t = tid; t < 2 * w + 1 + 2 * kBiasPad; t += kThreads) {
+            const int m = t - kBiasPad - w;
+            bias_lds[t] = (m >= -w && m <= w) ? tab[m] * kLog2eF : 0.f;
+        }
+    }
     __syncthreads();
     if (wv == 0)
         for (int s = 0; s < n_gst; ++s) {
@@ -692,8 +710,10 @@ void band_kernel(const Params p) {
                 const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
                 const int mode = gstage ? 2 : (interior ? 0 : 1);
                 const int goff = kStageKeys * gidx + 32 * sub + 8 * h2;
-                sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, kss + 8 * h2 - qv + w, span, glob_pos + goff,
-                            w - qv, causal ? gcnt - goff : 1 << 30);
+                const int bbase = kss + 8 * h2 - qv + w;
+                sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
+                            causal ? gcnt - goff : 1 << 30,
+                            (kBias && !gstage) ? bias_lds + kBiasPad + bbase : nullptr);
             }
         }
     }
@@ -877,17 +897,22 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
+    const bool bias = p.bias != nullptr;
+#define LF_BAND(T, C, Bi) hipLaunchKernelGGL((band_kernel<T, C, Bi>), dim3(blocks), dim3(kThreads), 0, s, p)
     if (dtype == LF_BF16) {
-        if (p.causal)
-            hipLaunchKernelGGL((band_kernel<Bf16, true>), dim3(blocks), dim3(kThreads), 0, s, p);
-        else
-            hipLaunchKernelGGL((band_kernel<Bf16, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+        if (p.causal) {
+            if (bias) LF_BAND(Bf16, true, true); else LF_BAND(Bf16, true, false);
+        } else {
+            if (bias) LF_BAND(Bf16, false, true); else LF_BAND(Bf16, false, false);
+        }
     } else {
-        if (p.causal)
-            hipLaunchKernelGGL((band_kernel<F32, true>), dim3(blocks), dim3(kThreads), 0, s, p);
-        else
-            hipLaunchKernelGGL((band_kernel<F32, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+        if (p.causal) {
+            if (bias) LF_BAND(F32, true, true); else LF_BAND(F32, true, false);
+        } else {
+            if (bias) LF_BAND(F32, false, true); else LF_BAND(F32, false, false);
+        }
     }
+#undef LF_BAND
     return hipGetLastError();
 }
 

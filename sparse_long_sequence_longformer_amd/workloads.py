@@ -12,6 +12,8 @@ Recipe (fixed, shared by every consumer):
   5. the key padding mask is pad[b, j] = (j >= length[b]) (uint8, 1 = padded);
   6. separate global projections q_g, k_g, v_g (when used) follow steps 1-3 with
      seed + 1000.
+  7. a relative-position-bias table (when used) is [H, 2w + 1] float32 standard
+     normals times a scale, from numpy.random.default_rng(seed + 7919).
 
 The five shapes follow the pages' workloads: hidden size 768 = 12 heads x 64
 (page "基于Block-Sparse Attention的Longformer" §6 example model), 4096-token
@@ -115,3 +117,11 @@ def make_custom(B, H, L, dtype="bf16", seed=0, scale=1.0, d=64):
     """Seeded q, k, v of an arbitrary shape (same recipe as the named workloads)."""
     wl = Workload("custom", B=B, H=H, L=L, w=0, dil=(1,) * H, dtype=dtype, seed=seed, scale=scale, d=d)
     return make_qkv(wl)
+
+
+def make_bias(H: int, w: int, seed: int = 0, scale: float = 1.0):
+    """Seeded relative-position-bias table [H, 2w + 1] (float32): i.i.d. normal
+    values times ``scale``, the shape of a learned per-head, per-offset scalar."""
+    rng = np.random.default_rng(seed + 7919)
+    return (rng.standard_normal((H, 2 * w + 1)) * scale).astype(np.float32)
+

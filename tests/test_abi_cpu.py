@@ -258,3 +258,34 @@ def test_python_forward_requires_device_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises((ValueError, binding.LfAttnError)):
         binding.forward(x, x, x, 2, [1])
+
+
+@needs_lib
+def test_position_bias_validation():
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        err = lambda: lib.lf_attn_last_error(h).decode()  # noqa: E731
+        assert lib.lf_attn_set_position_bias(None, FAKE, 2, 4) == 1
+        assert lib.lf_attn_set_position_bias(h, FAKE, 0, 4) == 1 and "n_heads" in err()
+        assert lib.lf_attn_set_position_bias(h, FAKE, 65, 4) == 1 and "n_heads" in err()
+        assert lib.lf_attn_set_position_bias(h, FAKE, 2, -1) == 1 and "w >= 0" in err()
+        assert lib.lf_attn_set_position_bias(h, FAKE, 2, binding.MAX_BIAS_W + 1) == 2 and "at most" in err()
+        assert lib.lf_attn_set_position_bias(h, FAKE + 2, 2, 4) == 1 and "aligned" in err()
+        # a table for H = 2, w = 4: calls with another H or w are refused before any launch
+        assert lib.lf_attn_set_position_bias(h, FAKE * 5, 2, 4) == 0
+        dil = (ctypes.c_int32 * 3)(1, 1, 1)
+        dil_p = ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32))
+
+        def call(H, w):
+            return lib.lf_attn_forward(h, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, H, 64, 64, w, dil_p, None, 0,
+                                       None, None)
+
+        assert call(3, 4) == 1 and "bias table is for H = 2, w = 4" in err()
+        assert call(2, 5) == 1 and "bias table" in err()
+        # removing the table lifts the restriction (the call then fails later, on the device)
+        assert lib.lf_attn_set_position_bias(h, None, 0, 0) == 0
+        assert "bias" not in err()
+    finally:
+        lib.lf_attn_destroy(h)
