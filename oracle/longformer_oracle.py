@@ -36,6 +36,13 @@ What it computes (per batch b and head h, with inputs widened to float64):
   enter through the global pattern (global rows, global keys outside the window)
   get no bias.  Page "基于自注意力机制的长文本建模算法：Longformer详解" §5 names a
   relative position bias that strengthens the local attention.
+* Random blocks (``rand``: per head, one row of key-block indices per query block;
+  entries < 0 unused; block size ``rand_block``, 64 by default): a non-global row i
+  also attends every key of the key blocks [kb*bs, kb*bs + bs) that its query block
+  i // bs drew, in the union with its window and the globals (each key once).  The
+  survey page (commentary on "Efficient Transformers: A Survey", §3.1-§3.2) names
+  BigBird's random attention on top of window + global; the draws are inputs here
+  (the page asks for a fixed seed so that inference is repeatable).
 * Per-sequence global sets: ``global_idx`` may hold one row per sequence
   ([B][n], negative entries unused); sequence b then uses its own row as G.
 * Variant with separate global projections (``attention_global_proj``): the page
@@ -108,10 +115,25 @@ def window_member(i: np.ndarray, j: np.ndarray, w: int, dil: int) -> np.ndarray:
     return (np.abs(diff) <= w * dil) & (diff % dil == 0)
 
 
-def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray, causal: bool = False) -> np.ndarray:
+def random_member(rows: np.ndarray, L: int, rand, block: int) -> np.ndarray:
+    """R[r, j]: key j lies in one of the key blocks drawn by the query block of row
+    rows[r].  ``rand`` is [n_query_blocks, r] (entries < 0 unused)."""
+    rand = np.asarray(rand, dtype=np.int64)
+    n_kb = (L + block - 1) // block
+    drawn = np.zeros((rand.shape[0], n_kb + 1), dtype=bool)  # last column: unused entries
+    for qb in range(rand.shape[0]):
+        for kb in rand[qb]:
+            drawn[qb, kb if 0 <= kb < n_kb else n_kb] = True
+    sel = drawn[np.asarray(rows, dtype=np.int64) // block, :n_kb]  # [R, n_kb]
+    return sel[:, np.arange(L) // block]
+
+
+def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray, causal: bool = False,
+              rand=None, rand_block: int = 64) -> np.ndarray:
     """Explicit boolean mask M[r, j] for the query rows ``rows`` over all L keys.
 
-    M[i, j] = not pad[j] and (i in G or j in G or j in window(i)) [and j <= i if causal].
+    M[i, j] = not pad[j] and (i in G or j in G or j in window(i) or j in the random
+    blocks of i's block) [and j <= i if causal].
     """
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(L, dtype=np.int64)[None, :]
@@ -120,6 +142,8 @@ def mask_rows(L: int, w: int, dil: int, G: np.ndarray, pad_row, rows: np.ndarray
     is_global_key[G] = True
     is_global_query = is_global_key[rows][:, None]
     m = window_member(i, j, w, dil) | is_global_key[None, :] | is_global_query
+    if rand is not None:
+        m |= random_member(rows, L, rand, rand_block)
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[None, :]
     if causal:
@@ -162,7 +186,7 @@ def _attention_rows(q, k, v, m, extra=None):
 
 
 def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=None,
-                 return_probs: bool = False, causal: bool = False, bias=None):
+                 return_probs: bool = False, causal: bool = False, bias=None, rand=None, rand_block: int = 64):
     """Oracle for one (batch, head) slice.
 
     q, k, v: [L, d] arrays (widened to float64).  ``rows`` selects query rows
@@ -181,7 +205,7 @@ def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=
     probs = np.zeros((rows.size, L), dtype=np.float64) if return_probs else None
     for s0 in range(0, rows.size, ROW_BLOCK):
         blk = rows[s0:s0 + ROW_BLOCK]
-        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal)
+        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal, rand=rand, rand_block=rand_block)
         extra = None if bias is None else window_bias(L, w, dil, G, blk, bias)
         o, p = _attention_rows(q[blk], k, v, m, extra) if extra is not None else _attention_rows(q[blk], k, v, m)
         out[s0:s0 + blk.size] = o
@@ -191,12 +215,13 @@ def attention_bh(q, k, v, w: int, dil: int, global_idx=None, pad_row=None, rows=
 
 
 def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False,
-              bias=None):
+              bias=None, rand=None, rand_block: int = 64):
     """Oracle for the full [B, H, L, d] problem.  Returns float64 [B, H, L, d].
 
     ``dil_per_head`` has one dilation per head (w is shared by all heads);
     ``global_idx`` is one set shared by every sequence and head;
-    ``key_pad_mask`` is [B, L], nonzero meaning a padded key (or None).
+    ``key_pad_mask`` is [B, L], nonzero meaning a padded key (or None);
+    ``rand``: random key blocks per head, [H, n_query_blocks, r], or None.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, L, d = q.shape
@@ -209,12 +234,13 @@ def attention(q, k, v, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
         for h in range(H):
             out[b, h] = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], globals_of(global_idx, b),
                                      None if pad is None else pad[b], causal=causal,
-                                     bias=None if bias is None else bias[h])
+                                     bias=None if bias is None else bias[h],
+                                     rand=None if rand is None else rand[h], rand_block=rand_block)
     return out
 
 
 def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, samples, causal: bool = False,
-                      bias=None):
+                      bias=None, rand=None, rand_block: int = 64):
     """Oracle output rows for a list of (b, h, i) samples, computed one by one.
 
     Used to check full-size runs where the whole oracle would be too slow.
@@ -226,23 +252,25 @@ def attention_sampled(q, k, v, w: int, dil_per_head, global_idx, key_pad_mask, s
     for b, h, i in samples:
         o = attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], globals_of(global_idx, b),
                          None if pad is None else pad[b], rows=[i], causal=causal,
-                         bias=None if bias is None else bias[h])
+                         bias=None if bias is None else bias[h],
+                         rand=None if rand is None else rand[h], rand_block=rand_block)
         res.append(o[0])
     return np.stack(res) if res else np.zeros((0, q.shape[-1]))
 
 
 def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1,
-               causal: bool = False) -> int:
+               causal: bool = False, rand=None, rand_block: int = 64) -> int:
     """Number of attended (query, key) pairs, summed over batch and heads: sum of M."""
     dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
     pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
     total = 0
     for b in range(B):
         G = globals_of(global_idx, b)
-        for d in dil:
+        for h, d in enumerate(dil):
             for s0 in range(0, L, ROW_BLOCK):
                 rows = np.arange(s0, min(L, s0 + ROW_BLOCK))
-                total += int(mask_rows(L, w, d, G, None if pad is None else pad[b], rows, causal=causal).sum())
+                total += int(mask_rows(L, w, d, G, None if pad is None else pad[b], rows, causal=causal,
+                                       rand=None if rand is None else rand[h], rand_block=rand_block).sum())
     return total
 
 
@@ -306,7 +334,7 @@ def _scores_rows(q, k, m, extra=None):
 
 
 def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False,
-                     bias=None) -> np.ndarray:
+                     bias=None, rand=None, rand_block: int = 64) -> np.ndarray:
     """log sum_{j in keys(i)} exp(q_i . k_j / sqrt(d)) of every row; -inf without keys."""
     q, k = _as_f64(q), _as_f64(k)
     L = k.shape[0]
@@ -314,7 +342,8 @@ def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, caus
     out = np.empty(L, dtype=np.float64)
     for s0 in range(0, L, ROW_BLOCK):
         blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
-        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk, causal=causal),
+        s = _scores_rows(q[blk], k, mask_rows(L, w, dil, G, pad_row, blk, causal=causal, rand=rand,
+                                              rand_block=rand_block),
                          None if bias is None else window_bias(L, w, dil, G, blk, bias))
         top = s.max(axis=1)
         has = np.isfinite(top)
@@ -325,7 +354,7 @@ def attention_lse_bh(q, k, w: int, dil: int, global_idx=None, pad_row=None, caus
 
 
 def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None, causal: bool = False,
-                  bias=None) -> np.ndarray:
+                  bias=None, rand=None, rand_block: int = 64) -> np.ndarray:
     """Per-row log-sum-exp of the full problem: float64 [B, H, L]."""
     q, k = _as_f64(q), _as_f64(k)
     B, H, L, _ = q.shape
@@ -336,12 +365,13 @@ def attention_lse(q, k, w: int, dil_per_head, global_idx=None, key_pad_mask=None
         for h in range(H):
             out[b, h] = attention_lse_bh(q[b, h], k[b, h], w, dil[h], globals_of(global_idx, b),
                                          None if pad is None else pad[b], causal=causal,
-                                         bias=None if bias is None else bias[h])
+                                         bias=None if bias is None else bias[h],
+                                         rand=None if rand is None else rand[h], rand_block=rand_block)
     return out
 
 
 def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False,
-                          bias=None):
+                          bias=None, rand=None, rand_block: int = 64):
     """Gradients (dQ, dK, dV) of one (batch, head) slice for the upstream gradient dout.
 
     Row blocks of the explicit mask; dK and dV collect every block's contribution.
@@ -354,7 +384,7 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
     dv = np.zeros_like(v)
     for s0 in range(0, L, ROW_BLOCK):
         blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
-        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal)
+        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal, rand=rand, rand_block=rand_block)
         extra = None if bias is None else window_bias(L, w, dil, G, blk, bias)
         o, p = _attention_rows(q[blk], k, v, m, extra) if extra is not None else _attention_rows(q[blk], k, v, m)
         dv += p.T @ do[blk]
@@ -367,7 +397,7 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
 
 
 def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
-                       causal: bool = False, bias=None):
+                       causal: bool = False, bias=None, rand=None, rand_block: int = 64):
     """Gradients of the full problem: three float64 [B, H, L, d] arrays (dQ, dK, dV)."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
     B, H, L, d = q.shape
@@ -380,5 +410,6 @@ def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = attention_backward_bh(
                 q[b, h], k[b, h], v[b, h], do[b, h], w, dil[h], globals_of(global_idx, b),
-                None if pad is None else pad[b], causal=causal, bias=None if bias is None else bias[h])
+                None if pad is None else pad[b], causal=causal, bias=None if bias is None else bias[h],
+                rand=None if rand is None else rand[h], rand_block=rand_block)
     return dq, dk, dv

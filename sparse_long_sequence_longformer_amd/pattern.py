@@ -23,15 +23,16 @@ class PairCounts:
     band: int  # non-global rows, keys in their window
     global_col: int  # non-global rows, global keys outside their window
     global_row: int  # global rows, every unpadded key
+    random: int = 0  # non-global rows, keys of their random blocks outside window and globals
 
     @property
     def total(self) -> int:
-        return self.band + self.global_col + self.global_row
+        return self.band + self.global_col + self.global_row + self.random
 
     @property
     def band_kernel(self) -> int:
-        """Pairs handled by the band kernel (window plus global-column fold)."""
-        return self.band + self.global_col
+        """Pairs handled by the band kernel (window, global-column fold, random blocks)."""
+        return self.band + self.global_col + self.random
 
 
 def _unique_globals(global_idx, L):
@@ -43,7 +44,32 @@ def _unique_globals(global_idx, L):
     return g
 
 
-def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray, causal: bool = False) -> PairCounts:
+def _random_pairs(L: int, w: int, dil: int, is_g: np.ndarray, valid: np.ndarray, causal: bool, rand,
+                  block: int) -> int:
+    """Random-block pairs of non-global rows that neither the window nor the globals
+    already give: one (query block x key block) rectangle at a time."""
+    n_kb = (L + block - 1) // block
+    key_ok = valid & ~is_g
+    tot = 0
+    for qb, row in enumerate(np.asarray(rand, dtype=np.int64)):
+        i = np.arange(qb * block, min(L, qb * block + block), dtype=np.int64)
+        i = i[~is_g[i]]
+        if i.size == 0:
+            continue
+        for kb in np.unique(row[(row >= 0) & (row < n_kb)]):
+            j = np.arange(kb * block, min(L, kb * block + block), dtype=np.int64)
+            j = j[key_ok[j]]
+            diff = j[None, :] - i[:, None]
+            win = (diff % dil == 0) & (diff >= -w * dil) & (diff <= (0 if causal else w * dil))
+            ok = ~win
+            if causal:
+                ok &= diff <= 0
+            tot += int(ok.sum())
+    return tot
+
+
+def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray, causal: bool = False,
+                   rand=None, rand_block: int = 64) -> PairCounts:
     """Pair counts for one (sequence, head).  ``valid[j]`` is True for unpadded keys.
 
     ``causal``: the one-sided variant, every pair with its key after its query removed
@@ -79,16 +105,18 @@ def count_pairs_bh(L: int, w: int, dil: int, G: np.ndarray, valid: np.ndarray, c
         grow = int(vpref[G + 1].sum()) if G.size else 0
     else:
         grow = int(G.size) * int(valid.sum())
-    return PairCounts(band, gcol, grow)
+    rnd = 0 if rand is None else _random_pairs(L, w, dil, is_g, valid, causal, rand, rand_block)
+    return PairCounts(band, gcol, grow, rnd)
 
 
 def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None, B: int = 1,
-                causal: bool = False) -> PairCounts:
+                causal: bool = False, rand=None, rand_block: int = 64) -> PairCounts:
     """Attended pairs summed over B sequences and all heads.
 
     ``key_pad_mask`` is an array-like [B, L] (nonzero = padded) or None.
     ``global_idx``: one set for every sequence, or one row per sequence ([B][n],
     negative entries unused).
+    ``rand``: random key blocks per head ([H][n_query_blocks][r], negative unused).
     """
     per_seq = global_idx is not None and np.asarray(global_idx).ndim == 2
     dils = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
@@ -97,7 +125,7 @@ def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None
         B = pad.shape[0]
     if per_seq:
         B = np.asarray(global_idx).shape[0]
-    tot = PairCounts(0, 0, 0)
+    tot = PairCounts(0, 0, 0, 0)
     cache = {}
     for b in range(B):
         if per_seq:
@@ -107,14 +135,16 @@ def count_pairs(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None
             G = _unique_globals(global_idx, L)
         valid = np.ones(L, dtype=bool) if pad is None else ~pad[b]
         key_b = b if (pad is not None or per_seq) else 0
-        for dl in dils:
-            key = (key_b, dl)
+        for hh, dl in enumerate(dils):
+            key = (key_b, dl) if rand is None else (key_b, dl, hh)
             if key not in cache:
-                cache[key] = count_pairs_bh(L, w, dl, G, valid, causal)
+                cache[key] = count_pairs_bh(L, w, dl, G, valid, causal,
+                                            None if rand is None else rand[hh], rand_block)
             c = cache[key]
             tot.band += c.band
             tot.global_col += c.global_col
             tot.global_row += c.global_row
+            tot.random += c.random
     return tot
 
 

@@ -14,6 +14,9 @@ Recipe (fixed, shared by every consumer):
      seed + 1000.
   7. a relative-position-bias table (when used) is [H, 2w + 1] float32 standard
      normals times a scale, from numpy.random.default_rng(seed + 7919).
+  8. random key blocks (when used) are [H, ceil(L / 64), r] int32: for every head
+     and query block, r distinct key blocks drawn uniformly from all of them by
+     numpy.random.default_rng(seed + 104729).choice(n_blocks, r, replace=False).
 
 The five shapes follow the pages' workloads: hidden size 768 = 12 heads x 64
 (page "基于Block-Sparse Attention的Longformer" §6 example model), 4096-token
@@ -124,4 +127,18 @@ def make_bias(H: int, w: int, seed: int = 0, scale: float = 1.0):
     values times ``scale``, the shape of a learned per-head, per-offset scalar."""
     rng = np.random.default_rng(seed + 7919)
     return (rng.standard_normal((H, 2 * w + 1)) * scale).astype(np.float32)
+
+
+def make_random_blocks(H: int, L: int, r: int, seed: int = 0, block: int = 64):
+    """Seeded random key-block draws [H, ceil(L / block), r] (int32): for each head and
+    query block, r distinct key blocks chosen uniformly among all ceil(L / block)."""
+    n = (L + block - 1) // block
+    if r > n:
+        raise ValueError("more draws per query block than key blocks")
+    rng = np.random.default_rng(seed + 104729)
+    out = np.empty((H, n, r), dtype=np.int32)
+    for h in range(H):
+        for qb in range(n):
+            out[h, qb] = rng.choice(n, r, replace=False)
+    return out
 

@@ -676,6 +676,98 @@ def pin_bias_shift_and_scope():
     assert np.abs(got[i] - (e / e.sum()) @ v[keys]).max() < 1e-12
 
 
+
+# ------------------------------------------------------------- random blocks
+
+# (L, d, w, dil, globals, pad kind, block, draws per query block, causal, seed)
+RAND_CASES = [
+    (16, 8, 1, 1, [], None, 4, 1, False, 1),
+    (40, 8, 2, 1, [3, 31], None, 8, 2, False, 2),
+    (37, 8, 3, 2, [0, 36], "rand", 4, 3, False, 3),
+    (48, 8, 2, 1, [10], "suffix", 8, 2, True, 4),
+    (29, 8, 0, 1, [], "rand", 4, 4, True, 5),
+    (64, 16, 5, 3, [7, 7, 50], "rand", 16, 2, False, 6),
+]
+
+
+def _draws(L, block, r, seed):
+    """Key-block draws per query block with duplicates and unused (-1) entries."""
+    n = (L + block - 1) // block
+    return np.random.default_rng(700 + seed).integers(-1, n, size=(n, r))
+
+
+def pin_random_brute():
+    """Random blocks: the oracle (output, log-sum-exp, mask sum) equals brute-force
+    enumeration of window + globals + the key blocks each query block drew."""
+    for L, d, w, dil, G, padk, bs, r, causal, seed in RAND_CASES:
+        q, k, v = (_rand((L, d), 900 + seed * 3 + t) for t in range(3))
+        pad = _pad_for(padk, L, seed)
+        padl = None if pad is None else pad.tolist()
+        rnd = _draws(L, bs, r, seed)
+        got = orc.attention_bh(q, k, v, w, dil, G, pad, causal=causal, rand=rnd, rand_block=bs)
+        ref = np.array(brute.attention_bh(q.tolist(), k.tolist(), v.tolist(), w, dil, G, padl, causal, rnd, bs))
+        assert np.abs(got - ref).max() < 1e-12, (L, w, dil, bs, causal)
+        assert orc.mask_count(L, w, [dil], G, None if pad is None else pad[None, :], causal=causal, rand=[rnd],
+                              rand_block=bs) == brute.pair_count(L, w, dil, G, padl, causal, rnd, bs)
+        lse = orc.attention_lse_bh(q, k, w, dil, G, pad, causal=causal, rand=rnd, rand_block=bs)
+        for i in range(L):
+            keys = brute.key_set(i, L, w, dil, G, padl, causal, rnd, bs)
+            if not keys:
+                assert lse[i] == -np.inf
+                continue
+            sc = [math.fsum(q[i, t] * k[j, t] for t in range(d)) / math.sqrt(d) for j in keys]
+            top = max(sc)
+            assert abs(lse[i] - (top + math.log(math.fsum(math.exp(x - top) for x in sc)))) < 1e-12
+
+
+def pin_random_limits():
+    """Every query block drawing every key block is full attention (torch SDPA, and its
+    causal form); a draw of each row's own block with w >= block - 1 adds no key (the
+    result is bit-identical to no draws); global rows ignore the draws."""
+    L, bs = 40, 8
+    n = L // bs
+    q, k, v = (_rand((L, 16), 950 + t) for t in range(3))
+    every = np.tile(np.arange(n), (n, 1))
+    got = orc.attention_bh(q, k, v, 0, 1, rand=every, rand_block=bs)
+    assert np.abs(got - _textbook_attention(q, k, v)).max() < 1e-12
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0, 0].numpy()
+    assert np.abs(orc.attention_bh(q, k, v, 0, 1, rand=every, rand_block=bs, causal=True) - ref).max() < 1e-12
+    own = np.arange(n)[:, None]
+    pad = _pad_for("rand", L, 3)
+    for w in (bs - 1, bs + 3):
+        a = orc.attention_bh(q, k, v, w, 1, [5, 30], pad, rand=own, rand_block=bs)
+        b = orc.attention_bh(q, k, v, w, 1, [5, 30], pad)
+        assert np.array_equal(a, b)
+    # a strictly smaller window loses keys that the own-block draw puts back
+    a = orc.attention_bh(q, k, v, 1, 1, rand=own, rand_block=bs)
+    assert np.abs(a - orc.attention_bh(q, k, v, 1, 1)).max() > 1e-3
+    G = [2, 17]
+    far = np.full((n, 1), n - 1)
+    a = orc.attention_bh(q, k, v, 1, 1, G, rand=far, rand_block=bs)
+    b = orc.attention_bh(q, k, v, 1, 1, G)
+    assert np.array_equal(a[G], b[G])
+
+
+def pin_random_backward_autograd():
+    """Random-block gradients equal torch autograd of the dense masked attention whose
+    key sets come from the brute-force enumeration."""
+    for L, d, w, dil, G, padk, bs, r, causal, seed in RAND_CASES:
+        q, k, v, do = (_rand((L, d), 980 + seed * 5 + t) for t in range(4))
+        pad = _pad_for(padk, L, seed)
+        padl = None if pad is None else pad.tolist()
+        rnd = _draws(L, bs, r, seed)
+        keysets = [brute.key_set(i, L, w, dil, G, padl, causal, rnd, bs) for i in range(L)]
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        out = _torch_dense_attention(tq, tk, tv, keysets)
+        (out * torch.from_numpy(do)).sum().backward()
+        dq, dk, dv = orc.attention_backward_bh(q, k, v, do, w, dil, G, pad, causal=causal, rand=rnd,
+                                               rand_block=bs)
+        for name, a, b in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+            err = np.abs(a - b.numpy()).max()
+            assert err < 1e-12, (name, L, w, dil, G, padk, err)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -707,6 +799,9 @@ ALL_PINS = [
     pin_global_sets_per_sequence,
     pin_bias_sdpa,
     pin_bias_shift_and_scope,
+    pin_random_brute,
+    pin_random_limits,
+    pin_random_backward_autograd,
     pin_layer_torch_encoder,
     pin_layer_norm_rows,
 ]

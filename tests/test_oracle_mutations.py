@@ -44,37 +44,41 @@ def _causal(m, rows, L, causal):
     return m
 
 
-def _mask_rows_only(L, w, dil, G, pad_row, rows, causal=False):  # global rows only, no global columns
+def _mask_rows_only(L, w, dil, G, pad_row, rows, causal=False, rand=None, rand_block=64):  # global rows only, no global columns
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(L)[None, :]
     isg = np.zeros(L, dtype=bool)
     isg[G] = True
     m = orc.window_member(rows[:, None], j, w, dil) | isg[rows][:, None]
+    if rand is not None:
+        m |= orc.random_member(rows, L, rand, rand_block)
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[None, :]
     return _causal(m, rows, L, causal)
 
 
-def _mask_cols_only(L, w, dil, G, pad_row, rows, causal=False):  # global columns only, no global rows
+def _mask_cols_only(L, w, dil, G, pad_row, rows, causal=False, rand=None, rand_block=64):  # global columns only, no global rows
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(L)[None, :]
     isg = np.zeros(L, dtype=bool)
     isg[G] = True
     m = orc.window_member(rows[:, None], j, w, dil) | isg[None, :]
+    if rand is not None:
+        m |= orc.random_member(rows, L, rand, rand_block)
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[None, :]
     return _causal(m, rows, L, causal)
 
 
-def _mask_pad_queries(L, w, dil, G, pad_row, rows, causal=False):  # padding applied to query rows
-    m = _orig_mask(L, w, dil, G, None, rows, causal=causal)
+def _mask_pad_queries(L, w, dil, G, pad_row, rows, causal=False, rand=None, rand_block=64):  # padding applied to query rows
+    m = _orig_mask(L, w, dil, G, None, rows, causal=causal, rand=rand, rand_block=rand_block)
     if pad_row is not None:
         m &= ~np.asarray(pad_row, dtype=bool)[np.asarray(rows)][:, None]
     return m
 
 
-def _mask_pad_ignored(L, w, dil, G, pad_row, rows, causal=False):
-    return _orig_mask(L, w, dil, G, None, rows, causal=causal)
+def _mask_pad_ignored(L, w, dil, G, pad_row, rows, causal=False, rand=None, rand_block=64):
+    return _orig_mask(L, w, dil, G, None, rows, causal=causal, rand=rand, rand_block=rand_block)
 
 
 def _rows_scale_d(q, k, v, m, extra=None):  # 1/d instead of 1/sqrt(d)
@@ -164,8 +168,8 @@ def _bwd_mutant(kind):
     return fn
 
 
-def _mask_causal_window_only(L, w, dil, G, pad_row, rows, causal=False):  # future global keys kept
-    m = _orig_mask(L, w, dil, G, pad_row, rows, causal=causal)
+def _mask_causal_window_only(L, w, dil, G, pad_row, rows, causal=False, rand=None, rand_block=64):  # future global keys kept
+    m = _orig_mask(L, w, dil, G, pad_row, rows, causal=causal, rand=rand, rand_block=rand_block)
     if causal:
         rows = np.asarray(rows, dtype=np.int64)
         extra = np.zeros((rows.size, L), dtype=bool)
@@ -176,11 +180,29 @@ def _mask_causal_window_only(L, w, dil, G, pad_row, rows, causal=False):  # futu
     return m
 
 
-def _mask_causal_strict(L, w, dil, G, pad_row, rows, causal=False):  # self excluded (j < i)
-    m = _orig_mask(L, w, dil, G, pad_row, rows, causal=causal)
+def _mask_causal_strict(L, w, dil, G, pad_row, rows, causal=False, rand=None, rand_block=64):  # self excluded (j < i)
+    m = _orig_mask(L, w, dil, G, pad_row, rows, causal=causal, rand=rand, rand_block=rand_block)
     if causal:
         m &= np.arange(L)[None, :] != np.asarray(rows)[:, None]
     return m
+
+
+_orig_random = orc.random_member
+
+
+def _random_transposed(rows, L, rand, block):  # row i gets key j when j's block drew i's block
+    rows = np.asarray(rows, dtype=np.int64)
+    t = _orig_random(np.arange(L), L, rand, block)  # [L, L]: t[j, i] = i in the blocks j's block drew
+    return t.T[rows]
+
+
+def _random_next_block(rows, L, rand, block):  # block kb read as kb + 1
+    r = np.asarray(rand, dtype=np.int64)
+    return _orig_random(rows, L, np.where(r >= 0, r + 1, r), block)
+
+
+def _random_first_draw_only(rows, L, rand, block):  # only the first draw of each query block
+    return _orig_random(rows, L, np.asarray(rand)[:, :1], block)
 
 
 from oracle import layer_oracle as _lo  # noqa: E402
@@ -234,6 +256,9 @@ MUTANTS = {
     "global_proj_uses_v": ("attention_global_proj", _gp_uses_v),
     "bias_reversed": ("window_bias", _bias_reversed),
     "bias_on_global_rows": ("window_bias", _bias_on_global_rows),
+    "random_transposed": ("random_member", _random_transposed),
+    "random_next_block": ("random_member", _random_next_block),
+    "random_first_draw_only": ("random_member", _random_first_draw_only),
     "layer_ln_unbiased": ("layer:layer_norm", _ln_unbiased),
     "layer_gelu_tanh": ("layer:gelu", _gelu_tanh),
     "layer_heads_interleaved": ("layer:split_heads", _split_interleaved),

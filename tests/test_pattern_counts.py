@@ -109,3 +109,26 @@ def test_counter_per_sequence_globals(seed):
     for causal in (False, True):
         c = pattern.count_pairs(L, w, dil, sets, pad, B=B, causal=causal)
         assert c.total == orc.mask_count(L, w, dil, sets, pad, B=B, causal=causal)
+
+
+def test_random_block_counts_match_oracle_mask():
+    """Random-block pairs: the closed-form counter equals the oracle's mask sum and the
+    brute-force key-set sizes (window, globals, padding, causal, duplicate and unused draws)."""
+    from oracle import brute
+
+    rng = np.random.default_rng(11)
+    for _ in range(30):
+        L = int(rng.integers(1, 70))
+        bs = int(rng.choice([2, 4, 8, 16]))
+        w = int(rng.integers(0, 6))
+        dil = int(rng.integers(1, 4))
+        n = (L + bs - 1) // bs
+        rnd = rng.integers(-1, n, size=(n, int(rng.integers(1, 4))))
+        G = sorted(rng.choice(L, int(rng.integers(0, min(4, L) + 1)), replace=False).tolist())
+        pad = rng.random(L) < 0.2
+        causal = bool(rng.integers(0, 2))
+        want = brute.pair_count(L, w, dil, G, pad.tolist(), causal, rnd, bs)
+        assert orc.mask_count(L, w, [dil], G, pad[None], causal=causal, rand=[rnd], rand_block=bs) == want
+        got = pattern.count_pairs(L, w, [dil], G, pad[None].astype(np.uint8), causal=causal, rand=[rnd],
+                                  rand_block=bs)
+        assert got.total == want
