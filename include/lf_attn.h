@@ -51,6 +51,8 @@ typedef enum lf_dtype {
 #define LF_MAX_GLOBALS 256
 #define LF_HEAD_DIM 64
 #define LF_MAX_BIAS_W 1024 /* widest window with a relative position bias */
+#define LF_RANDOM_BLOCK 64 /* keys per random block (and queries per query block) */
+#define LF_MAX_RANDOM_DRAWS 16 /* random key blocks per query block */
 
 /* Kernel launches timed by lf_attn_stage_times. */
 #define LF_N_STAGES 8
@@ -219,6 +221,34 @@ lf_status lf_attn_set_window_mode(lf_attn_t h, int mode);
  * unchanged.  A later call with another H or w fails with LF_ERR_INVALID_ARG.
  */
 lf_status lf_attn_set_position_bias(lf_attn_t h, const float* table, int n_heads, int w);
+
+/*
+ * Random key blocks (BigBird-style random attention) for every later forward on
+ * `h` (forward, forward_lse, forward_global_proj, layer).
+ *
+ * The survey page (commentary on "Efficient Transformers: A Survey", §3.1-§3.2)
+ * describes BigBird as window + global + random attention and recommends fixed
+ * draws for repeatable inference; the draws are therefore inputs.  Positions are
+ * grouped in blocks of LF_RANDOM_BLOCK: a non-global row i also attends every key of
+ * the key blocks [64*kb, 64*kb + 64) that its query block i / 64 drew, in the union
+ * with its window and the global keys (a key reached several ways counts once);
+ * padded keys stay masked, and in the causal mode keys after the row are dropped.
+ *
+ * blocks    : HOST int32 [n_heads][n_qblocks][r], copied during the call (the
+ *             caller may free it on return); entry kb < 0 is unused, duplicates
+ *             count once, 0 <= kb < n_qblocks otherwise.  NULL removes the draws.
+ * n_heads   : 1 .. LF_MAX_HEADS; later calls must pass H == n_heads.
+ * n_qblocks : ceil(L / LF_RANDOM_BLOCK) of the later calls (they must match).
+ * r         : 0 .. LF_MAX_RANDOM_DRAWS draws per query block.
+ * Later calls must have every head undilated (LF_ERR_UNSUPPORTED otherwise).  The
+ * library keeps a device copy of the tables, uploaded (synchronously, after a
+ * device-wide synchronisation) by the first call after this one on each device, so
+ * that first call cannot be captured in a graph.  Do not call this while calls on
+ * `h` are in flight.  Errors: LF_ERR_INVALID_ARG (h == NULL, sizes out of range,
+ * an entry >= n_qblocks), LF_ERR_UNSUPPORTED (r > LF_MAX_RANDOM_DRAWS); the setting
+ * is then unchanged.
+ */
+lf_status lf_attn_set_random_blocks(lf_attn_t h, const int32_t* blocks, int n_heads, int n_qblocks, int r);
 
 /*
  * One Longformer layer around the attention (bf16 handles only):

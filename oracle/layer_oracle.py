@@ -61,17 +61,18 @@ def merge_heads(t):
 
 
 def layer_forward(x, weights: dict, H: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
-                  eps: float = 1e-5, causal: bool = False, bias=None):
+                  eps: float = 1e-5, causal: bool = False, bias=None, rand=None):
     """One layer on x [B, L, E]; ``weights`` maps WEIGHT_NAMES to arrays (nn.Linear
     layout: weight [out, in]); ``bias``: the attention's relative position bias
-    ([H, 2w + 1]) or None.  Returns float64 [B, L, E]."""
+    ([H, 2w + 1]) or None; ``rand``: its random key blocks ([H, n_blocks, r]) or None.
+    Returns float64 [B, L, E]."""
     x = _f64(x)
     W = {k: _f64(v) for k, v in weights.items()}
     E = x.shape[-1]
     qkv = x @ W["w_qkv"].T + W["b_qkv"]
     q, k, v = (split_heads(qkv[..., i * E:(i + 1) * E], H) for i in range(3))
     a = merge_heads(orc.attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask, causal=causal,
-                                    bias=bias))
+                                    bias=bias, rand=rand))
     x1 = layer_norm(x + a @ W["w_o"].T + W["b_o"], W["ln1_g"], W["ln1_b"], eps)
     f = gelu(x1 @ W["w_1"].T + W["b_1"]) @ W["w_2"].T + W["b_2"]
     return layer_norm(x1 + f, W["ln2_g"], W["ln2_b"], eps)

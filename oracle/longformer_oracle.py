@@ -275,16 +275,17 @@ def mask_count(L: int, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
 
 
 def attention_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
-                          causal: bool = False, bias=None):
+                          causal: bool = False, bias=None, rand=None, rand_block: int = 64):
     """Oracle for the variant with separate global projections.  float64 [B, H, L, d].
 
     Rows not in the global set: ``attention(q, k, v, ...)``.  A global row g:
     masked softmax over the unpadded keys of q_g[g] . k_g^T / sqrt(d_h), times v_g
     (page "基于Block-Sparse Attention的Longformer" §4, global attention with its own
-    projections; every global row sees every position, §2).  ``bias`` reaches only the
-    window pairs of the other rows, as in ``attention``.
+    projections; every global row sees every position, §2).  ``bias`` and ``rand``
+    reach only the other rows, as in ``attention``.
     """
-    out = attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask, causal=causal, bias=bias)
+    out = attention(q, k, v, w, dil_per_head, global_idx, key_pad_mask, causal=causal, bias=bias, rand=rand,
+                    rand_block=rand_block)
     q_g, k_g, v_g = _as_f64(q_g), _as_f64(k_g), _as_f64(v_g)
     B, H, L, d = q_g.shape
     pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)

@@ -27,6 +27,8 @@ LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1",
 MAX_HEADS = 64
 MAX_GLOBALS = 256
 MAX_BIAS_W = 1024
+RANDOM_BLOCK = 64
+MAX_RANDOM_DRAWS = 16
 
 # Every symbol declared in include/lf_attn.h.
 EXPORTS = (
@@ -43,6 +45,7 @@ EXPORTS = (
     "lf_attn_set_window_mode",
     "lf_attn_set_global_mode",
     "lf_attn_set_position_bias",
+    "lf_attn_set_random_blocks",
     "lf_attn_stage_times",
 )
 
@@ -107,6 +110,8 @@ def load_library():
     lib.lf_attn_set_window_mode.restype = i32
     lib.lf_attn_set_position_bias.argtypes = [vp, vp, i32, i32]
     lib.lf_attn_set_position_bias.restype = i32
+    lib.lf_attn_set_random_blocks.argtypes = [vp, ctypes.POINTER(i32), i32, i32, i32]
+    lib.lf_attn_set_random_blocks.restype = i32
     lib.lf_attn_set_stage_timing.argtypes = [vp, i32]
     lib.lf_attn_set_stage_timing.restype = i32
     lib.lf_attn_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -135,6 +140,7 @@ class LfAttn:
         self.causal = False
         self.per_sequence_globals = False
         self.bias = None  # the table set by set_position_bias (kept alive here)
+        self.rand = None  # the draws set by set_random_blocks (int32 [H, n_qblocks, r])
 
     def _check(self, st, h=None):
         if st != LF_OK:
@@ -228,6 +234,24 @@ class LfAttn:
                     self.handle)
         self.bias = table
 
+    def set_random_blocks(self, draws):
+        """Random key blocks for every later forward: int array [H, ceil(L / 64), r] of
+        key-block indices per (head, query block), negative = unused; None removes them.
+        The library copies the table (uploaded by the next call)."""
+        if draws is None:
+            self._check(self.lib.lf_attn_set_random_blocks(self.handle, None, 0, 0, 0), self.handle)
+            self.rand = None
+            return
+        import numpy as np
+
+        a = np.ascontiguousarray(np.asarray(draws.tolist() if hasattr(draws, "tolist") else draws, dtype=np.int32))
+        if a.ndim != 3:
+            raise ValueError("random blocks must be [H, n_query_blocks, r]")
+        H, nq, r = a.shape
+        ptr = a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self._check(self.lib.lf_attn_set_random_blocks(self.handle, ptr, H, nq, r), self.handle)
+        self.rand = a
+
     def layer_raw(self, x_ptr, weights: LayerWeights, out_ptr, B, L, hidden, ffn, eps, w, dil, global_idx, pad_ptr,
                   stream):
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
@@ -259,8 +283,8 @@ class LfAttn:
 _handles: dict = {}
 
 
-def _handle_for(dtype: str, causal: bool = False, per_seq: bool = False) -> LfAttn:
-    key = (dtype, bool(causal), bool(per_seq))
+def _handle_for(dtype: str, causal: bool = False, per_seq: bool = False, rand: bool = False) -> LfAttn:
+    key = (dtype, bool(causal), bool(per_seq), bool(rand))
     if key not in _handles:
         h = LfAttn(dtype)
         if causal:
@@ -287,6 +311,31 @@ class _CallBias:
         return False
 
 
+class _CallRandom:
+    """Installs per-call random draws on a handle.  The library's own handles for
+    calls with draws keep the last table (re-installed only when it changes); a
+    caller's handle gets its previous table back after the call."""
+
+    def __init__(self, h: LfAttn, rand, restore: bool):
+        self.h, self.rand, self.restore, self.prev = h, rand, restore, h.rand
+
+    def __enter__(self):
+        import numpy as np
+
+        if self.rand is None:
+            return
+        new = np.asarray(self.rand.tolist() if hasattr(self.rand, "tolist") else self.rand, dtype=np.int32)
+        if self.h.rand is None or not np.array_equal(self.h.rand, new):
+            self.h.set_random_blocks(new)
+        else:
+            self.restore = False
+
+    def __exit__(self, *exc):
+        if self.rand is not None and self.restore:
+            self.h.set_random_blocks(self.prev)
+        return False
+
+
 def _global_arg(global_idx, B: int):
     """Shared set -> (list, False); one set per sequence (2-D, rows may differ in
     length) -> ((flat row-major list padded with -1, row length), True)."""
@@ -304,7 +353,7 @@ def _global_arg(global_idx, B: int):
     return [int(x) for x in rows], False
 
 
-def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=False):
+def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=False, rand=False):
     """Checks shared by both entry points; returns (B, H, L, d_h, dilation list,
     global list, pad pointer, out, handle, stream)."""
     import torch
@@ -343,7 +392,7 @@ def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=Fa
         out = torch.empty_like(q)
     elif out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous device tensor like q")
-    h = handle if handle is not None else _handle_for(dt, causal, per_seq)
+    h = handle if handle is not None else _handle_for(dt, causal, per_seq, rand)
     if h.dtype != dt:
         raise ValueError("handle dtype does not match the inputs")
     if h.causal != bool(causal):
@@ -355,7 +404,7 @@ def _marshal(q, others, w, dil, global_idx, key_pad_mask, out, handle, causal=Fa
 
 
 def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, handle: LfAttn | None = None,
-            causal: bool = False, bias=None):
+            causal: bool = False, bias=None, rand=None):
     """Longformer window + global attention forward on the GPU.
 
     q, k, v: contiguous CUDA/HIP tensors [B, H, L, 64], all bfloat16 or all float32.
@@ -366,20 +415,22 @@ def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, 
     the same mode.
     bias: relative position bias on window scores, float32 device tensor [H, 2w + 1],
     for this call only; None leaves the handle's own setting (none by default).
+    rand: random key blocks [H, ceil(L / 64), r] (int, negative = unused) for this call
+    (every head undilated); None leaves the handle's own setting.
     Returns ``out`` (allocated if not given), same shape and dtype as q.
     """
     import torch
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
-        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal)
-    with torch.cuda.device(q.device), _CallBias(h, bias):
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal, rand is not None)
+    with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
                       global_idx, pad_ptr, stream)
     return out
 
 
 def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, key_pad_mask=None, out=None,
-                        handle: LfAttn | None = None, causal: bool = False, bias=None):
+                        handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
     """As ``forward``, but the global query rows attend every unpadded key with their
     own projections q_g, k_g, v_g (tensors shaped and typed like q); every other row
     uses q, k, v."""
@@ -387,8 +438,8 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
         q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)], w, dil, global_idx,
-        key_pad_mask, out, handle, causal)
-    with torch.cuda.device(q.device), _CallBias(h, bias):
+        key_pad_mask, out, handle, causal, rand is not None)
+    with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.forward_global_proj_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_g.data_ptr(), k_g.data_ptr(),
                                   v_g.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil, global_idx,
                                   pad_ptr, stream)
@@ -396,25 +447,25 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
 
 
 def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, lse=None,
-                handle: LfAttn | None = None, causal: bool = False, bias=None):
+                handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
     """``forward`` that also returns each row's log-sum-exp: (out, lse), lse a float32
     device tensor [B, H, L] (natural log, -inf for rows without keys)."""
     import torch
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
-        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal)
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal, rand is not None)
     if lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
-    with torch.cuda.device(q.device), _CallBias(h, bias):
+    with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.forward_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, L, d_h,
                           int(w), dil, global_idx, pad_ptr, stream)
     return out, lse
 
 
 def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask=None, dq=None, dk=None,
-             dv=None, handle: LfAttn | None = None, causal: bool = False, bias=None):
+             dv=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dout``.
 
     q, k, v, out, dout: contiguous bf16 device tensors [B, H, L, 64]; ``out`` and
@@ -427,7 +478,7 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
         raise TypeError("the backward supports bfloat16 tensors only")
     B, H, L, d_h, dil, global_idx, pad_ptr, _, h, stream = _marshal(
         q, [("k", k), ("v", v), ("out", out), ("dout", dout)], w, dil, global_idx, key_pad_mask, out, handle,
-        causal)
+        causal, rand is not None)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
     res = []
@@ -438,7 +489,7 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
             raise ValueError("dq, dk, dv must be contiguous device tensors like q")
         res.append(t)
     dq, dk, dv = res
-    with torch.cuda.device(q.device), _CallBias(h, bias):
+    with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.backward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d_h, int(w), dil, global_idx, pad_ptr,
                        stream)
@@ -446,7 +497,7 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
 
 
 def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=None, eps: float = 1e-5, out=None,
-                  handle: LfAttn | None = None, causal: bool = False, bias=None):
+                  handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
     """One Longformer layer (projections, this attention, LayerNorms, GELU feed-forward).
 
     x: contiguous bf16 device tensor [B, L, hidden]; ``weights`` maps LAYER_WEIGHTS to
@@ -476,13 +527,13 @@ def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=N
         pad_ptr = key_pad_mask.data_ptr()
     if out is None:
         out = torch.empty_like(x)
-    h = handle if handle is not None else _handle_for("bf16", causal, per_seq)
+    h = handle if handle is not None else _handle_for("bf16", causal, per_seq, rand is not None)
     if h.causal != bool(causal):
         raise ValueError("handle window mode does not match causal=")
     if h.per_sequence_globals != per_seq:
         raise ValueError("handle global mode does not match the shape of global_idx")
     wts = LayerWeights(*[weights[n].data_ptr() for n in LAYER_WEIGHTS])
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    with torch.cuda.device(x.device), _CallBias(h, bias):
+    with torch.cuda.device(x.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.layer_raw(x.data_ptr(), wts, out.data_ptr(), B, L, E, F, eps, int(w), dil, global_idx, pad_ptr, stream)
     return out

@@ -34,6 +34,16 @@ struct lf_attn_s {
     const float* bias = nullptr;  // borrowed [bias_heads][2 * bias_w + 1], or null
     int bias_heads = 0;
     int bias_w = 0;
+    // Random key blocks: per head and query block the sorted distinct draws (-1 after
+    // them), [rnd_heads][rnd_nq][rnd_r], and the inverse lists (query blocks per key
+    // block), [rnd_heads][rnd_nq][rnd_inv_r]; uploaded to rnd_dev on first use.
+    bool rnd_on = false;
+    int rnd_heads = 0, rnd_nq = 0, rnd_r = 0, rnd_inv_r = 0;
+    std::vector<int32_t> rnd_tab, rnd_inv_tab;
+    char* rnd_dev = nullptr;
+    size_t rnd_dev_bytes = 0;
+    int rnd_dev_device = -1;
+    int rnd_uploaded = -1;  // device holding the current tables, or -1
     int device = -1;
     char* ws = nullptr;  // global-row partials of the forward
     size_t ws_bytes = 0;
@@ -134,6 +144,7 @@ lf_status lf_attn_destroy(lf_attn_t h) {
     if (h->ws && hipFree(h->ws) != hipSuccess) st = LF_ERR_HIP;
     if (h->ws_bwd && hipFree(h->ws_bwd) != hipSuccess) st = LF_ERR_HIP;
     if (h->ws_layer && hipFree(h->ws_layer) != hipSuccess) st = LF_ERR_HIP;
+    if (h->rnd_dev && hipFree(h->rnd_dev) != hipSuccess) st = LF_ERR_HIP;
     if (h->blas && rocblas_destroy_handle(h->blas) != rocblas_status_success) st = LF_ERR_HIP;
     release_events(h);
     for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
@@ -177,6 +188,56 @@ lf_status lf_attn_set_position_bias(lf_attn_t h, const float* table, int n_heads
     h->bias = table;
     h->bias_heads = n_heads;
     h->bias_w = w;
+    return LF_OK;
+}
+
+lf_status lf_attn_set_random_blocks(lf_attn_t h, const int32_t* blocks, int n_heads, int n_qblocks, int r) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (!blocks) {
+        h->rnd_on = false;
+        h->rnd_tab.clear();
+        h->rnd_inv_tab.clear();
+        h->rnd_uploaded = -1;
+        return LF_OK;
+    }
+    if (n_heads < 1 || n_heads > LF_MAX_HEADS)
+        return fail(h, LF_ERR_INVALID_ARG, "need 1 <= n_heads <= %d (got %d)", LF_MAX_HEADS, n_heads);
+    if (n_qblocks < 1) return fail(h, LF_ERR_INVALID_ARG, "need n_qblocks >= 1 (got %d)", n_qblocks);
+    if (r < 0) return fail(h, LF_ERR_INVALID_ARG, "need r >= 0 (got %d)", r);
+    if (r > LF_MAX_RANDOM_DRAWS)
+        return fail(h, LF_ERR_UNSUPPORTED, "at most %d random blocks per query block (got %d)", LF_MAX_RANDOM_DRAWS, r);
+    const size_t rows = static_cast<size_t>(n_heads) * n_qblocks;
+    std::vector<std::vector<int>> fwd(rows), inv(rows);
+    size_t R = 1, RI = 1;
+    for (size_t row = 0; row < rows; ++row) {
+        for (int t = 0; t < r; ++t) {
+            const int kb = blocks[row * r + t];
+            if (kb < 0) continue;
+            if (kb >= n_qblocks)
+                return fail(h, LF_ERR_INVALID_ARG, "random block %d of head %zu, query block %zu outside [0, %d)", kb,
+                            row / n_qblocks, row % n_qblocks, n_qblocks);
+            fwd[row].push_back(kb);
+        }
+        std::sort(fwd[row].begin(), fwd[row].end());
+        fwd[row].erase(std::unique(fwd[row].begin(), fwd[row].end()), fwd[row].end());
+        R = std::max(R, fwd[row].size());
+        const size_t hb = (row / n_qblocks) * n_qblocks;  // first row of this head
+        for (int kb : fwd[row]) inv[hb + kb].push_back(static_cast<int>(row % n_qblocks));
+    }
+    for (const auto& v : inv) RI = std::max(RI, v.size());  // query blocks arrive in ascending order
+    h->rnd_tab.assign(rows * R, -1);
+    h->rnd_inv_tab.assign(rows * RI, -1);
+    for (size_t row = 0; row < rows; ++row) {
+        std::copy(fwd[row].begin(), fwd[row].end(), h->rnd_tab.begin() + row * R);
+        std::copy(inv[row].begin(), inv[row].end(), h->rnd_inv_tab.begin() + row * RI);
+    }
+    h->rnd_on = true;
+    h->rnd_heads = n_heads;
+    h->rnd_nq = n_qblocks;
+    h->rnd_r = static_cast<int>(R);
+    h->rnd_inv_r = static_cast<int>(RI);
+    h->rnd_uploaded = -1;
     return LF_OK;
 }
 
@@ -243,6 +304,17 @@ lf_status make_plan(lf_attn_t h, Plan& pl, int B, int H, int L, int d_h, int w, 
     if (h->bias && (H != h->bias_heads || w != h->bias_w))
         return fail(h, LF_ERR_INVALID_ARG, "the position bias table is for H = %d, w = %d (call: H = %d, w = %d)",
                     h->bias_heads, h->bias_w, H, w);
+    if (h->rnd_on) {
+        const int nq = (L + LF_RANDOM_BLOCK - 1) / LF_RANDOM_BLOCK;
+        if (H != h->rnd_heads || nq != h->rnd_nq)
+            return fail(h, LF_ERR_INVALID_ARG,
+                        "the random blocks are for H = %d, %d query blocks (call: H = %d, L = %d gives %d)",
+                        h->rnd_heads, h->rnd_nq, H, L, nq);
+        for (int i = 0; i < H; ++i)
+            if (dil_per_head[i] != 1)
+                return fail(h, LF_ERR_UNSUPPORTED, "random blocks need every head undilated (dil_per_head[%d] = %d)",
+                            i, dil_per_head[i]);
+    }
     const size_t elem = h->dtype == LF_BF16 ? 2 : 4;
     const uint64_t n_elem = static_cast<uint64_t>(B) * H * L * LF_HEAD_DIM;
     if (n_elem / LF_HEAD_DIM / L / H != static_cast<uint64_t>(B) || n_elem > (uint64_t(1) << 40))
@@ -319,6 +391,22 @@ lf_status reserve(lf_attn_t h, char** buf, size_t* have, int* dev, size_t need) 
     }
     *have = need;
     *dev = h->device;
+    return LF_OK;
+}
+
+// Device copies of the random-block tables (synchronous upload after a change).
+lf_status upload_random(lf_attn_t h) {
+    if (!h->rnd_on || h->rnd_uploaded == h->device) return LF_OK;
+    const size_t n_fwd = h->rnd_tab.size(), n_inv = h->rnd_inv_tab.size();
+    lf_status st = reserve(h, &h->rnd_dev, &h->rnd_dev_bytes, &h->rnd_dev_device, (n_fwd + n_inv) * sizeof(int32_t));
+    if (st != LF_OK) return st;
+    // Earlier calls may still read the old tables.
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(h->rnd_dev, h->rnd_tab.data(), n_fwd * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(h->rnd_dev + n_fwd * sizeof(int32_t), h->rnd_inv_tab.data(), n_inv * sizeof(int32_t),
+                  hipMemcpyHostToDevice) != hipSuccess)
+        return fail(h, LF_ERR_HIP, "upload of the random-block tables failed");
+    h->rnd_uploaded = h->device;
     return LF_OK;
 }
 
@@ -401,6 +489,13 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
+    st = upload_random(h);
+    if (st != LF_OK) return st;
+    if (h->rnd_on) {
+        p.rnd = reinterpret_cast<const int*>(h->rnd_dev);
+        p.rnd_nq = h->rnd_nq;
+        p.rnd_r = h->rnd_r;
+    }
     if (p.n_g > 0) {
         const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
         st = reserve(h, &h->ws, &h->ws_bytes, &h->ws_device, n_part * (2 + 64) * sizeof(float));
@@ -425,6 +520,7 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
         return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-null");
     if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the backward supports bf16 handles only");
+    if (h->rnd_on) return fail(h, LF_ERR_UNSUPPORTED, "the backward does not support random blocks yet");
     Plan pl;
     lf_status st = make_plan(h, pl, B, H, L, d_h, w, dil_per_head, global_idx, n_global);
     if (st != LF_OK) return st;

@@ -133,11 +133,26 @@ __device__ __forceinline__ constexpr int kc_of(int i) { return 16 * (i >> 3) + (
 // window); 2: global keys, masked where in the window (gp: in-window positions of the
 // sub-tile's keys, test 0 <= gp + wq <= span) and from slot kc = climit on (global
 // slots are sorted by position, so in the one-sided variant the keys after the query
-// are a suffix).  Invalid keys (inv32 bits) are masked in modes 1 and 2.
+// are a suffix); 3 (kRand only): random-block keys, the complement of mode 1's window
+// range, and from kc = climit on.  Invalid keys (inv32 bits) are masked in modes 1-3.
+template <bool kRand = false>
 __device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32, int h2, int base, int span,
                                             const int* gp, int wq, int climit = 1 << 30) {
     if (mode == 0) return;
     const uint32_t invl = inv32 >> (8 * h2);
+    if (kRand && mode == 3) {
+        // Random-block keys (contiguous, as in mode 1): keep those OUTSIDE the window
+        // range 0 <= base + kc <= span (the band has them), minus invalid keys, and in
+        // the one-sided variant only kc < climit (keys at or before the query).
+        const int lo_k = max(0, -base), hi_k = min(31, span - base);
+        uint32_t win = 0u;
+        if (hi_k >= lo_k) win = (hi_k >= 31 ? ~0u : ((2u << hi_k) - 1u)) & ~((1u << lo_k) - 1u);
+        uint32_t keep = ~win & ~invl;
+        if (climit < 32) keep &= climit <= 0 ? 0u : ((1u << climit) - 1u);
+        for (int i = 0; i < 16; ++i)
+            if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
+        return;
+    }
     if (mode == 1) {
         // Band test 0 <= base + kc <= span as one bit range over kc, minus invalid keys.
         const int lo_k = max(0, -base), hi_k = min(31, span - base);

@@ -16,6 +16,9 @@ constexpr int kKeysPerTile = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGlobalQueriesPerBlock = 32;
+constexpr int kRandomBlock = LF_RANDOM_BLOCK;  // keys of one random block = one staged tile
+static_assert(kRandomBlock == kKeysPerTile && kRowsPerBlock == 2 * kRandomBlock,
+              "a row tile holds two query blocks and a stage one key block");
 
 // Kernel parameters, passed by value (kernarg segment, < 2 KiB).
 struct Params {
@@ -32,6 +35,10 @@ struct Params {
     float* lse;          // [B][H][L] natural-log sum of each row's exp(scores), or nullptr
     const float* bias;   // relative position bias [H][2*bias_w + 1] of window pairs, or nullptr
     int bias_w;
+    // Random key blocks of kRandomBlock keys: row qb of head h at rnd[(h*rnd_nq + qb)*rnd_r]
+    // lists the key blocks query block qb drew, ascending, then -1; or nullptr.
+    const int* rnd;
+    int rnd_nq, rnd_r;
     // Global-row partials: one (max, sum, 64 outputs) per (b*H + h, row tile, global
     // query), written by every work-group for its own 128 "home" keys.
     float* ws_ml;        // [B*H][tiles_per_head][n_gblk*32][2]
@@ -68,6 +75,12 @@ struct BwdParams {
     const float* lse;    // [B][H][L] natural-log row sums of the forward
     const float* bias;   // relative position bias as in Params, or nullptr
     int bias_w;
+    const int* rnd;      // random key blocks as in Params, or nullptr
+    int rnd_nq, rnd_r;
+    // Inverse of rnd: row kb of head h at rnd_inv[(h*rnd_nq + kb)*rnd_inv_r] lists the
+    // query blocks that drew key block kb, ascending, then -1.
+    const int* rnd_inv;
+    int rnd_inv_r;
     // Row statistics written by the prep kernel, [B][H][L] each:
     float* lse2;       // lse in base-2 units of the pre-scaled scores; +inf for rows without keys
     float* lse2_band;  // same, and +inf for global rows (they are not window queries)

@@ -469,7 +469,7 @@ __device__ __forceinline__ void add_bias_run(f32x16& s, const float* brow) {
 }
 
 // One 32-key sub-tile of a stage: scores, masks, softmax update, P.V product.
-template <class T>
+template <class T, bool kRand = false>
 __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, const typename T::Lane& lo,
                                          const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
                                          int span, const int* gp, int wq, int climit = 1 << 30,
@@ -478,7 +478,7 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
     if (brow) add_bias_run(s, brow);
     typename T::VOp vo;
     T::load_v(vo, slot, sub, lo);  // in flight during the softmax
-    mask_scores(s, mode, inv32, h2, base, span, gp, wq, climit);
+    mask_scores<kRand>(s, mode, inv32, h2, base, span, gp, wq, climit);
     typename T::PFrag pf;
     fold_tile<T>(st, s, pf, lo);
     T::pv(vo, pf, st.o);
@@ -495,8 +495,14 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 // home keys are still in LDS when the band ends, for (c).  Each wave skips 32-key
 // sub-tiles outside its rows' band and masks only sub-tiles that touch the band
 // edge or hold invalid keys.
+//
+// Random blocks (kRandom; every head undilated, so the tile's rows are positions
+// r0 .. r0+127, i.e. query blocks r0/64 and r0/64 + 1): after the global stages come
+// the key blocks drawn by the first query block (for waves 0-1), then those drawn by
+// the second (waves 2-3), one 64-key stage each.  Their keys that lie in a row's
+// window, are global, padded or past the end are masked, so each key counts once.
 
-template <class T, bool kCausal, bool kBias>
+template <class T, bool kCausal, bool kBias, bool kRandom>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const Params p) {
     using Elem = typename T::Elem;
@@ -512,6 +518,7 @@ void band_kernel(const Params p) {
     // around it covers every lane's reads of a processed sub-tile).
     __shared__ float bias_lds[kBias ? kBiasLds : 1];
     __shared__ uint32_t row_glob[kRowsPerBlock / 32]; // tile rows that are global queries
+    __shared__ uint64_t rnd_inv[kRandom ? 2 * LF_MAX_RANDOM_DRAWS : 1];  // invalid-key bits of random stages
     __shared__ __attribute__((aligned(16))) char gq_rows[kGlobalQueriesPerBlock * T::kRowBytes];  // first 32 global Q rows
 
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
@@ -560,13 +567,29 @@ void band_kernel(const Params p) {
     const int na = max(0, (kend - (r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
     const int n_band = nb + 2 + na;
     const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
-    const int n_st = n_gst + n_band;
+    // Random stages: the draws of query block r0/64 (rnd_a, na_r of them), then those
+    // of the next query block (rnd_b, nb_r); rows are sorted with -1 after the draws.
+    const int* rnd_a = nullptr;
+    const int* rnd_b = nullptr;
+    int na_r = 0, nb_r = 0;
+    if (kRandom) {
+        const int qb0 = r0 / kRandomBlock;
+        rnd_a = p.rnd + ((size_t)h * p.rnd_nq + qb0) * p.rnd_r;
+        rnd_b = rnd_a + p.rnd_r;
+        while (na_r < p.rnd_r && rnd_a[na_r] >= 0) ++na_r;
+        if (qb0 + 1 < p.rnd_nq)
+            while (nb_r < p.rnd_r && rnd_b[nb_r] >= 0) ++nb_r;
+    }
+    const int n_rst = na_r + nb_r;
+    const int n_lst = n_gst + n_rst;  // stages of listed keys (global, then random)
+    const int n_st = n_lst + n_band;
     // Stage order: one band stage (when there is one besides the home stages), the
-    // global stages, the remaining band stages.  A band stage first lets its copy be
-    // issued before the global slots are set up.
-    const int n_pre = (n_gst > 0 && nb + na > 0) ? 1 : 0;
-    auto is_glob = [&](int t) { return t >= n_pre && t < n_pre + n_gst; };
-    auto band_u = [&](int t) { return t < n_pre ? t : t - n_gst; };
+    // global and random stages, the remaining band stages.  A band stage first lets
+    // its copy be issued before the global slots are set up.
+    const int n_pre = ((kRandom || n_gst > 0) && nb + na > 0) ? 1 : 0;
+    auto is_glob = [&](int t) { return t >= n_pre && t < n_pre + n_lst; };  // a listed-key stage
+    auto band_u = [&](int t) { return t < n_pre ? t : t - n_lst; };
+    auto rnd_block = [&](int j) { return j < na_r ? rnd_a[j] : rnd_b[j - na_r]; };  // key block of random stage j
     // First key of the u-th band stage in processing order (before, after, home).
     auto stage_key = [&](int u) {
         const int bs = u < nb ? u : (u < nb + na ? u + 2 : u - na);
@@ -590,7 +613,16 @@ void band_kernel(const Params p) {
     // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
     auto issue = [&](int s, int part) {
         char* slot = ring + (s % T::kNS) * T::kStageBytes;
-        if (is_glob(s)) {
+        if (kRandom && is_glob(s) && s - n_pre >= n_gst) {
+            const int j = s - n_pre - n_gst;
+            const int kb0 = kRandomBlock * rnd_block(j);
+            const uint64_t inv = uniform64(rnd_inv[j]);
+            if (inv == 0ull && part == kAllParts && direct_ok) {
+                T::dma_stage_direct(slot, K + (size_t)kb0 * 64, V + (size_t)kb0 * 64, dl, wv);
+            } else {
+                T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane, part);
+            }
+        } else if (is_glob(s)) {
             const int* src = glob_src + kStageKeys * (s - n_pre);
             T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane, part);
         } else {
@@ -659,6 +691,17 @@ void band_kernel(const Params p) {
         const int vr = glob_row[gi] - r0;
         if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
     }
+    if (kRandom)  // invalid keys of random stage j: past the end, padded or global
+        for (int j = wv; j < n_rst; j += kWaves) {
+            const int key = kRandomBlock * rnd_block(j) + lane;
+            bool ok = key < L && (!pad || pad[key] == 0);
+            if (ok && ng > 0) {
+                const int c = count_le(glob_abs, ng, key);
+                ok = !(c > 0 && glob_abs[c - 1] == key);
+            }
+            const uint64_t inv = ~ballot64(ok);
+            if (lane == 0) rnd_inv[j] = inv;
+        }
     __syncthreads();
     // One-sided variant: the global slots at or before this lane's row.
     const int gcnt = causal ? count_le(glob_abs, ng, r + qv * dil) : 0;
@@ -693,12 +736,18 @@ void band_kernel(const Params p) {
             T::dma_rows(gq_rows, [&](int j) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * 64 : zero; },
                         wv, lane);
         }
-        const bool gstage = is_glob(t);
-        const int gidx = t - n_pre;  // global stage index when gstage
-        const int ks = gstage ? 0 : stage_key(band_u(t));
-        const uint64_t inv = uniform64(gstage ? glob_mask[gidx] : band_invalid(band_u(t)));
         const char* slot = ring + (t % T::kNS) * T::kStageBytes;
-        if (rows_live && inv != ~0ull) {
+        // Stage kind: random (kRandom: key block rnd_block(j), for the waves of its
+        // query block), global (listed slots), or band.
+        const bool rstage = kRandom && is_glob(t) && t - n_pre >= n_gst;
+        const bool gstage = is_glob(t) && !rstage;
+        const int gidx = t - n_pre;        // global stage index when gstage
+        const int j = t - n_pre - n_gst;   // random stage index when rstage
+        const int ks = rstage ? kRandomBlock * rnd_block(j) : (gstage ? 0 : stage_key(band_u(t)));
+        const uint64_t inv =
+            uniform64(rstage ? rnd_inv[j] : (gstage ? glob_mask[gidx] : band_invalid(band_u(t))));
+        const bool wave_on = !rstage || (wv >> 1) == (j < na_r ? 0 : 1);
+        if (rows_live && wave_on && inv != ~0ull) {
             // Both sub-tiles in straight-line code: the second one's operand reads and
             // products can be scheduled against the first one's softmax.
 #pragma unroll
@@ -706,14 +755,20 @@ void band_kernel(const Params p) {
                 const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
                 const int kss = ks + 32 * sub;
                 if (inv32 == ~0u) continue;
-                if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) continue;  // outside every row's band
-                const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
-                const int mode = gstage ? 2 : (interior ? 0 : 1);
+                if (rstage) {
+                    if (kss >= qa + 31 - w && kss + 31 <= qa + wr) continue;  // inside every row's window
+                    if (causal && kss > qa + 31) continue;                    // after every row
+                } else if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) {
+                    continue;  // outside every row's band
+                }
+                const bool interior =
+                    !gstage && !rstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
+                const int mode = rstage ? 3 : (gstage ? 2 : (interior ? 0 : 1));
                 const int goff = kStageKeys * gidx + 32 * sub + 8 * h2;
                 const int bbase = kss + 8 * h2 - qv + w;
-                sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
-                            causal ? gcnt - goff : 1 << 30,
-                            (kBias && !gstage) ? bias_lds + kBiasPad + bbase : nullptr);
+                const int climit = !causal ? 1 << 30 : (rstage ? w - bbase + 1 : gcnt - goff);
+                sub_step<T, kRandom>(st, slot, sub, lo, qop, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
+                                     climit, (kBias && !gstage && !rstage) ? bias_lds + kBiasPad + bbase : nullptr);
             }
         }
     }
@@ -754,7 +809,7 @@ void band_kernel(const Params p) {
         T::scale_q(gop);
         if (gb == 0 && !sep) {
             const int u = n_band - 2 + hs;
-            hslot = ring + ((n_gst + u) % T::kNS) * T::kStageBytes;
+            hslot = ring + ((n_lst + u) % T::kNS) * T::kStageBytes;
             inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
         } else {
             uint64_t hinv[2];
@@ -897,21 +952,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-    const bool bias = p.bias != nullptr;
-#define LF_BAND(T, C, Bi) hipLaunchKernelGGL((band_kernel<T, C, Bi>), dim3(blocks), dim3(kThreads), 0, s, p)
+    const bool bias = p.bias != nullptr, rnd = p.rnd != nullptr;
+#define LF_BAND(T, C, Bi, R) hipLaunchKernelGGL((band_kernel<T, C, Bi, R>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_BAND_R(T, C, Bi) \
+    if (rnd) LF_BAND(T, C, Bi, true); else LF_BAND(T, C, Bi, false)
+#define LF_BAND_BR(T, C) \
+    if (bias) { LF_BAND_R(T, C, true); } else { LF_BAND_R(T, C, false); }
     if (dtype == LF_BF16) {
-        if (p.causal) {
-            if (bias) LF_BAND(Bf16, true, true); else LF_BAND(Bf16, true, false);
-        } else {
-            if (bias) LF_BAND(Bf16, false, true); else LF_BAND(Bf16, false, false);
-        }
+        if (p.causal) { LF_BAND_BR(Bf16, true); } else { LF_BAND_BR(Bf16, false); }
     } else {
-        if (p.causal) {
-            if (bias) LF_BAND(F32, true, true); else LF_BAND(F32, true, false);
-        } else {
-            if (bias) LF_BAND(F32, false, true); else LF_BAND(F32, false, false);
-        }
+        if (p.causal) { LF_BAND_BR(F32, true); } else { LF_BAND_BR(F32, false); }
     }
+#undef LF_BAND_BR
+#undef LF_BAND_R
 #undef LF_BAND
     return hipGetLastError();
 }

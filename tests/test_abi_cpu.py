@@ -289,3 +289,43 @@ def test_position_bias_validation():
         assert "bias" not in err()
     finally:
         lib.lf_attn_destroy(h)
+
+
+@needs_lib
+def test_random_blocks_validation():
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        err = lambda: lib.lf_attn_last_error(h).decode()  # noqa: E731
+
+        def arr(vals):
+            a = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+            return ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)), a
+
+        good, keep = arr([1, -1, 0, 0, 1, 1, -5, 0])  # H = 2, 2 query blocks, r = 2
+        assert lib.lf_attn_set_random_blocks(None, good, 2, 2, 2) == 1
+        assert lib.lf_attn_set_random_blocks(h, good, 0, 2, 2) == 1 and "n_heads" in err()
+        assert lib.lf_attn_set_random_blocks(h, good, 2, 0, 2) == 1 and "n_qblocks" in err()
+        assert lib.lf_attn_set_random_blocks(h, good, 2, 2, -1) == 1 and "r >= 0" in err()
+        assert lib.lf_attn_set_random_blocks(h, good, 2, 2, binding.MAX_RANDOM_DRAWS + 1) == 2
+        bad, keep2 = arr([1, 2, 0, 0, 1, 1, 0, 0])
+        st = lib.lf_attn_set_random_blocks(h, bad, 2, 2, 2)
+        assert st == 1 and "outside [0, 2)" in err(), err()
+        assert lib.lf_attn_set_random_blocks(h, good, 2, 2, 2) == 0
+        dil = (ctypes.c_int32 * 3)(1, 1, 1)
+        dil_p = ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32))
+
+        def call(H, L, d=None):
+            dp = dil_p if d is None else ctypes.cast((ctypes.c_int32 * H)(*d), ctypes.POINTER(ctypes.c_int32))
+            return lib.lf_attn_forward(h, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, H, L, 64, 8, dp, None, 0, None, None)
+
+        assert call(3, 128) == 1 and "random blocks are for H = 2" in err()
+        assert call(2, 129) == 1 and "L = 129 gives 3" in err(), err()
+        assert call(2, 128, [1, 2]) == 2 and "undilated" in err()
+        st = lib.lf_attn_backward(h, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8,
+                                  FAKE * 9, 1, 2, 128, 64, 8, dil_p, None, 0, None, None)
+        assert st == 2 and "random" in err(), err()
+        assert lib.lf_attn_set_random_blocks(h, None, 0, 0, 0) == 0
+    finally:
+        lib.lf_attn_destroy(h)
