@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--bias", type=float, default=0.0, metavar="SCALE",
                     help="relative position bias on window scores: a seeded N(0, SCALE^2) table per head "
                          "(0: none)")
+    ap.add_argument("--random", type=int, default=0, metavar="R",
+                    help="BigBird-style random attention: R seeded key blocks of 64 per (head, query block) "
+                         "(0: none; needs an undilated workload)")
     ap.add_argument("--layer", action="store_true",
                     help="time one whole layer (projections, attention, LayerNorms, GELU feed-forward)")
     ap.add_argument("--ffn", type=int, default=3072, help="feed-forward width of --layer")
@@ -94,7 +97,7 @@ def traffic_for(workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, q, k, v, G, pad, target_s, causal=False, bias=None):
+def cpu_baseline(wl, q, k, v, G, pad, target_s, causal=False, bias=None, rand=None):
     """The fp64 oracle on whole (b, h) slices of the workload, one after another,
     until about target_s seconds of CPU work; BLAS limited to one thread."""
     from threadpoolctl import threadpool_limits
@@ -111,9 +114,10 @@ def cpu_baseline(wl, q, k, v, G, pad, target_s, causal=False, bias=None):
             for h in range(wl.H):
                 orc.attention_bh(q[b, h], k[b, h], v[b, h], wl.w, wl.dil[h], G,
                                  None if pad_np is None else pad_np[b], causal=causal,
-                                 bias=None if bias is None else bias[h])
+                                 bias=None if bias is None else bias[h], rand=None if rand is None else rand[h])
                 pr = None if pad_np is None else pad_np[b:b + 1]
-                pairs += pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr, causal=causal).total
+                pairs += pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr, causal=causal,
+                                             rand=None if rand is None else [rand[h]]).total
                 done.append((b, h))
                 if time.perf_counter() - t0 >= target_s:
                     break
@@ -166,7 +170,13 @@ def main():
     q, k, v = workloads.make_qkv(wl)
     G = wl.global_positions()
     pad = wl.pad_mask()
-    pairs = pattern.count_pairs(wl.L, wl.w, wl.dil_list(), G, pad, B=wl.B, causal=args.causal)
+    rand_tab = None
+    if args.random:
+        if any(d != 1 for d in wl.dil_list()):
+            print("bench.py: --random needs an undilated workload", file=sys.stderr)
+            sys.exit(2)
+        rand_tab = workloads.make_random_blocks(wl.H, wl.L, args.random, seed=wl.seed)
+    pairs = pattern.count_pairs(wl.L, wl.w, wl.dil_list(), G, pad, B=wl.B, causal=args.causal, rand=rand_tab)
     flops = pattern.effective_flops(pairs.total)
 
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
@@ -179,6 +189,8 @@ def main():
     if args.bias:
         bias_tab = workloads.make_bias(wl.H, wl.w, seed=wl.seed, scale=args.bias)
         handle.set_position_bias(torch.from_numpy(bias_tab).to(dev))
+    if rand_tab is not None:
+        handle.set_random_blocks(rand_tab)
     dil = wl.dil_list()
 
     # One checked call through the Python wrapper, then the timed loops call the C entry
@@ -239,7 +251,7 @@ def main():
     handle.set_stage_timing(False)
     stage_avg = {k2: v2[0] / v2[1] for k2, v2 in st.items() if v2[1]}
     k_avg_ms = stage_avg["band"]  # the dominant kernel
-    traffic = None if (args.global_proj or args.causal or args.bias) else traffic_for(name)
+    traffic = None if (args.global_proj or args.causal or args.bias or args.random) else traffic_for(name)
 
     # Trials (median / min / p90 of per-step time) and cold steps (Infinity Cache evicted).
     def timed(n):
@@ -306,6 +318,7 @@ def main():
             "global_projections": "separate" if args.global_proj else "shared",
             "window": "one-sided" if args.causal else "symmetric",
             "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None,
+            "random_blocks": f"{args.random} of 64 keys per (head, query block)" if args.random else None,
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "attended_pairs": pairs.total,
@@ -313,7 +326,7 @@ def main():
         "kernel_ms_avg": {k2: round(v2, 6) for k2, v2 in stage_avg.items()},
         "roofline": {
             "kernel": f"lf::band_kernel<{'Bf16' if wl.dtype == 'bf16' else 'F32'}, {str(args.causal).lower()}, "
-                      f"{str(bool(args.bias)).lower()}>",
+                      f"{str(bool(args.bias)).lower()}, {str(bool(args.random)).lower()}>",
             **roof,
             "traffic": traffic,
             "avg_launch_ms": round(k_avg_ms, 6),
@@ -351,7 +364,7 @@ def main():
         ms_g = a.elapsed_time(b) / args.steps
         res["graph_replay"] = {"ms_per_step": round(ms_g, 6), "value": round(flops / (ms_g * 1e-3) / 1e12, 3)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds, args.causal, bias_tab)
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, G, pad, args.cpu_seconds, args.causal, bias_tab, rand_tab)
     print(json.dumps(res), flush=True)
 
 
@@ -418,7 +431,8 @@ def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
         "config": {"workload": name, "B": wl.B, "seq_len": wl.L, "hidden": E, "heads": wl.H, "ffn": F, "w": wl.w,
                    "n_global": len(G), "parallelism": "single GPU",
                    "window": "one-sided" if args.causal else "symmetric",
-                   "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None},
+                   "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None,
+                   "random_blocks": f"{args.random} of 64 keys per (head, query block)" if args.random else None},
         "tokens_per_s": round(R / (ms * 1e-3), 1),
         "gemm_flop": gemm_flops, "attention_flop": flops_attn,
         "stage_ms_per_layer": {k2: round(v2, 6) for k2, v2 in per_call.items()},
@@ -512,7 +526,8 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
                    "dil": sorted(set(dil)), "n_global": len(G), "padded_lengths": list(wl.lengths) or None,
                    "global_batch": wl.B, "parallelism": "single GPU",
                    "window": "one-sided" if args.causal else "symmetric",
-                   "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None},
+                   "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None,
+                   "random_blocks": f"{args.random} of 64 keys per (head, query block)" if args.random else None},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "train_step_ms": round(ms_train, 6),
         "train_step_tflops": round(3.5 * flops_fwd / (ms_train * 1e-3) / 1e12, 3),

@@ -223,8 +223,8 @@ lf_status lf_attn_set_window_mode(lf_attn_t h, int mode);
 lf_status lf_attn_set_position_bias(lf_attn_t h, const float* table, int n_heads, int w);
 
 /*
- * Random key blocks (BigBird-style random attention) for every later forward on
- * `h` (forward, forward_lse, forward_global_proj, layer).
+ * Random key blocks (BigBird-style random attention) for every later call on `h`
+ * (forward, forward_lse, forward_global_proj, backward, layer).
  *
  * The survey page (commentary on "Efficient Transformers: A Survey", §3.1-§3.2)
  * describes BigBird as window + global + random attention and recommends fixed

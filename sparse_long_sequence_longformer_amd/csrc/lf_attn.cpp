@@ -520,7 +520,6 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
         return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-null");
     if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the backward supports bf16 handles only");
-    if (h->rnd_on) return fail(h, LF_ERR_UNSUPPORTED, "the backward does not support random blocks yet");
     Plan pl;
     lf_status st = make_plan(h, pl, B, H, L, d_h, w, dil_per_head, global_idx, n_global);
     if (st != LF_OK) return st;
@@ -571,6 +570,15 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
 
     // Workspace: three row-statistic arrays, then the global partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
+    st = upload_random(h);
+    if (st != LF_OK) return st;
+    if (h->rnd_on) {
+        p.rnd = reinterpret_cast<const int*>(h->rnd_dev);
+        p.rnd_nq = h->rnd_nq;
+        p.rnd_r = h->rnd_r;
+        p.rnd_inv = p.rnd + h->rnd_tab.size();
+        p.rnd_inv_r = h->rnd_inv_r;
+    }
     const size_t rows = static_cast<size_t>(B) * H * L;
     const size_t ngq = static_cast<size_t>(p.n_gblk) * lf::kGlobalQueriesPerBlock;
     const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * ngq * 64;

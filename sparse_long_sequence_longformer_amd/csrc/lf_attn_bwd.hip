@@ -322,9 +322,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: one work-group per 128 rows of one residue class of one (b, h); wave wv owns
 // rows r0 + 32*wv .. +31, one per lane (both lane halves).  Stages: the global keys
-// (with the in-window test, so each key counts once), then the window band.
+// (with the in-window test, so each key counts once), the random key blocks of the
+// tile's two query blocks (kRandom, as in the forward), then the window band.
 
-template <bool kCausal, bool kBias>
+template <bool kCausal, bool kBias, bool kRandom>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
@@ -336,6 +337,7 @@ void bwd_dq_kernel(const BwdParams p) {
     __shared__ int glob_row[LF_MAX_GLOBALS];
     __shared__ uint32_t row_glob[kRowsPerBlock / 32];
     __shared__ float bias_lds[kBias ? kBiasLds : 1];  // offset m at kBiasPad + m + w, base 2
+    __shared__ uint64_t rnd_inv[kRandom ? 2 * LF_MAX_RANDOM_DRAWS : 1];  // invalid keys of random stages
 
     // Keys of a row: w class steps before it and wr after (wr = 0 one-sided).
     constexpr bool causal = kCausal;
@@ -367,7 +369,22 @@ void bwd_dq_kernel(const BwdParams p) {
     const float my_d = qv < Lr ? dsum[row] : 0.f;
 
     const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
-    const int n_st = n_gst + tl.n_band;
+    // Random stages (every head undilated): draws of query block r0/64, then r0/64 + 1.
+    const int* rnd_a = nullptr;
+    const int* rnd_b = nullptr;
+    int na_r = 0, nb_r = 0;
+    if (kRandom) {
+        const int qb0 = r0 / kRandomBlock;
+        rnd_a = p.rnd + ((size_t)tl.h * p.rnd_nq + qb0) * p.rnd_r;
+        rnd_b = rnd_a + p.rnd_r;
+        while (na_r < p.rnd_r && rnd_a[na_r] >= 0) ++na_r;
+        if (qb0 + 1 < p.rnd_nq)
+            while (nb_r < p.rnd_r && rnd_b[nb_r] >= 0) ++nb_r;
+    }
+    auto rnd_block = [&](int j) { return j < na_r ? rnd_a[j] : rnd_b[j - na_r]; };
+    const int n_rst = na_r + nb_r;
+    const int n_lst = n_gst + n_rst;
+    const int n_st = n_lst + tl.n_band;
     auto band_invalid = [&](int u) -> uint64_t {
         if (pad) return band_mask[u % kBwdMaskRing];
         const int ks = tl.stage_row(u);
@@ -382,8 +399,12 @@ void bwd_dq_kernel(const BwdParams p) {
         if (s < n_gst) {
             const int* src = glob_src + kStageKeys * s;
             dma_tiles(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane);
+        } else if (kRandom && s < n_lst) {
+            const int j = s - n_gst, kb0 = kRandomBlock * rnd_block(j);
+            const uint64_t inv = uniform64(rnd_inv[j]);
+            dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane);
         } else {
-            const int u = s - n_gst;
+            const int u = s - n_lst;
             const uint64_t inv = uniform64(band_invalid(u));
             const int ks = tl.stage_row(u);
             dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
@@ -428,6 +449,17 @@ void bwd_dq_kernel(const BwdParams p) {
         const int vr = glob_row[gi] - r0;
         if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
     }
+    if (kRandom)  // invalid keys of random stage j: past the end, padded or global
+        for (int j = wv; j < n_rst; j += kWaves) {
+            const int key = kRandomBlock * rnd_block(j) + lane;
+            bool ok = key < L && (!pad || pad[key] == 0);
+            if (ok && ng > 0) {
+                const int c = count_le(glob_abs, ng, key);
+                ok = !(c > 0 && glob_abs[c - 1] == key);
+            }
+            const uint64_t inv = ~ballot64(ok);
+            if (lane == 0) rnd_inv[j] = inv;
+        }
     __syncthreads();
 
     // One-sided variant: the global slots at or before this lane's row.
@@ -443,7 +475,7 @@ void bwd_dq_kernel(const BwdParams p) {
         wait_vmcnt<0>();
         barrier_nofence();
         if (t + 1 < n_st) {
-            const int bn = t + 1 - n_gst;
+            const int bn = t + 1 - n_lst;
             if (pad && bn > 0 && bn % kBwdMaskWindow == 0) {
                 fill_band_masks(bn / kBwdMaskWindow);
                 __syncthreads();
@@ -451,22 +483,31 @@ void bwd_dq_kernel(const BwdParams p) {
             issue(t + 1);
         }
         const bool gstage = t < n_gst;
-        const int ks = gstage ? 0 : tl.stage_row(t - n_gst);
-        const uint64_t inv = uniform64(gstage ? glob_mask[t] : band_invalid(t - n_gst));
+        const bool rstage = kRandom && !gstage && t < n_lst;
+        const int j = t - n_gst;  // random stage index when rstage
+        const int ks = gstage ? 0 : (rstage ? kRandomBlock * rnd_block(j) : tl.stage_row(t - n_lst));
+        const uint64_t inv = uniform64(gstage ? glob_mask[t] : (rstage ? rnd_inv[j] : band_invalid(t - n_lst)));
         const char* slot = ring + (t & 1) * kStageB;
         if (!rows_live || inv == ~0ull) continue;
+        if (rstage && (wv >> 1) != (j < na_r ? 0 : 1)) continue;  // another query block's draw
         for (int sub = 0; sub < 2; ++sub) {
             const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
             const int kss = ks + 32 * sub;
             if (inv32 == ~0u) continue;
-            if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) continue;
-            const bool interior = !gstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
-            const int mode = gstage ? 2 : (interior ? 0 : 1);
+            if (rstage) {
+                if (kss >= qa + 31 - w && kss + 31 <= qa + wr) continue;  // inside every row's window
+                if (causal && kss > qa + 31) continue;                    // after every row
+            } else if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) {
+                continue;
+            }
+            const bool interior = !gstage && !rstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
+            const int mode = rstage ? 3 : (gstage ? 2 : (interior ? 0 : 1));
             f32x16 s = prod(slot, sub, lo, qop, seed_s);  // scores - lse, base 2
-            if (kBias && !gstage) add_bias(s, bias_lds + kBiasPad + kss + 8 * h2 - qv + w);
+            const int bbase = kss + 8 * h2 - qv + w;
+            if (kBias && !gstage && !rstage) add_bias(s, bias_lds + kBiasPad + bbase);
             const int goff = kStageKeys * t + 32 * sub + 8 * h2;
-            mask_scores(s, mode, inv32, h2, kss + 8 * h2 - qv + w, span, glob_pos + goff, w - qv,
-                        causal ? gcnt - goff : 1 << 30);
+            mask_scores<kRandom>(s, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
+                                 !causal ? 1 << 30 : (rstage ? w - bbase + 1 : gcnt - goff));
             const f32x16 dp = prod(slot + kTileB, sub, lo, dop, seed_d);  // dO.V - D
             float ds[16];
             for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
@@ -503,7 +544,7 @@ void bwd_dq_kernel(const BwdParams p) {
         uint32_t inv32;
         if (gb == 0) {
             const int u = tl.n_band - 2 + hs;
-            hslot = ring + ((n_gst + u) & 1) * kStageB;
+            hslot = ring + ((n_lst + u) & 1) * kStageB;
             inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
             wait_vmcnt<0>();
         } else {
@@ -557,9 +598,14 @@ void bwd_dq_kernel(const BwdParams p) {
 // dK, dV: one work-group per 128 keys of one residue class of one (b, h); wave wv
 // owns keys r0 + 32*wv .. +31, one per lane.  Stages: the global queries (every
 // unpadded key is theirs), then the window band of queries (global queries are
-// removed there by lse2_band = +inf: their weights are 0).
+// removed there by lse2_band = +inf: their weights are 0).  With random blocks
+// (kRandom, every head undilated) the query blocks that drew the tile's first key
+// block (for waves 0-1), then those that drew its second (waves 2-3), come between
+// the global queries and the band, one 64-query stage each; pairs that the window
+// already holds, global own keys (their pairs are folded by the global-key pass) and
+// queries past the end are masked.
 
-template <bool kCausal, bool kBias>
+template <bool kCausal, bool kBias, bool kRandom>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkv_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
@@ -599,7 +645,21 @@ void bwd_dkv_kernel(const BwdParams p) {
     load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
 
     const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
-    const int n_st = n_gst + tl.n_band;
+    // Random stages: the query blocks that drew key block r0/64, then r0/64 + 1.
+    const int* inv_a = nullptr;
+    const int* inv_b = nullptr;
+    int na_r = 0, nb_r = 0;
+    if (kRandom) {
+        const int kb0 = r0 / kRandomBlock;
+        inv_a = p.rnd_inv + ((size_t)tl.h * p.rnd_nq + kb0) * p.rnd_inv_r;
+        inv_b = inv_a + p.rnd_inv_r;
+        while (na_r < p.rnd_inv_r && inv_a[na_r] >= 0) ++na_r;
+        if (kb0 + 1 < p.rnd_nq)
+            while (nb_r < p.rnd_inv_r && inv_b[nb_r] >= 0) ++nb_r;
+    }
+    auto rnd_qblock = [&](int j) { return j < na_r ? inv_a[j] : inv_b[j - na_r]; };
+    const int n_lst = n_gst + na_r + nb_r;
+    const int n_st = n_lst + tl.n_band;
     auto issue = [&](int s) {
         char* slot = ring + (s & 1) * kStageB;
         if (s < n_gst) {
@@ -609,8 +669,13 @@ void bwd_dkv_kernel(const BwdParams p) {
             };
             dma_tiles(slot, Q, dO, row_of, wv, lane);
             if (wv == 0) dma_floats(slot, lse2, dsum, row_of, lane);
+        } else if (kRandom && s < n_lst) {
+            const int x0 = kRandomBlock * rnd_qblock(s - n_gst);
+            auto row_of = [&](int kk) { return x0 + kk < L ? x0 + kk : -1; };
+            dma_tiles(slot, Q, dO, row_of, wv, lane);
+            if (wv == 0) dma_floats(slot, lse2b, dsum, row_of, lane);
         } else {
-            const int ks = tl.stage_row(s - n_gst);
+            const int ks = tl.stage_row(s - n_lst);
             auto row_of = [&](int kk) {
                 const int x = ks + kk;
                 return (x >= tl.kb0 && x < tl.kend) ? r + x * dil : -1;
@@ -642,28 +707,46 @@ void bwd_dkv_kernel(const BwdParams p) {
     wait_vmcnt<0>();
     scale_op(kop);
     f32x16 dk[2] = {f32x16{}, f32x16{}}, dv[2] = {f32x16{}, f32x16{}};
+    // Random stages: an own key that is global takes its random pairs from the
+    // global-key pass instead.
+    const bool own_global = kRandom && qv < Lr && own_gidx[qv - r0] >= 0;
     for (int t = 0; t < n_st; ++t) {
         wait_vmcnt<0>();
         barrier_nofence();
         if (t + 1 < n_st) issue(t + 1);
         const bool gstage = t < n_gst;
-        const int ks = gstage ? 0 : tl.stage_row(t - n_gst);
+        const bool rstage = kRandom && !gstage && t < n_lst;
+        const int j = t - n_gst;  // random stage index when rstage
+        const int ks = gstage ? 0 : (rstage ? kRandomBlock * rnd_qblock(j) : tl.stage_row(t - n_lst));
         const char* slot = ring + (t & 1) * kStageB;
         if (!rows_live) continue;
+        if (rstage && (wv >> 1) != (j < na_r ? 0 : 1)) continue;  // a draw of the other key block
         for (int sub = 0; sub < 2; ++sub) {
             const int kss = ks + 32 * sub;
             if (gstage) {
                 if (kss >= ng) continue;
+            } else if (rstage) {
+                if (kss >= L) continue;                                    // no valid query
+                if (kss >= qa + 31 - wl && kss + 31 <= qa + w) continue;  // every pair in the window
+                if (causal && kss + 31 < qa) continue;                     // every query before every key
             } else {
                 if (kss > qa + 31 + w || kss + 31 < qa - wl) continue;  // outside every own key's window
                 if (kss >= tl.kend || kss + 31 < tl.kb0) continue;      // no valid query
             }
-            const bool interior = !gstage && kss >= qa + 31 - wl && kss + 31 <= qa + w;
-            const int mode = (gstage || interior) ? 0 : 1;
+            const bool interior = !gstage && !rstage && kss >= qa + 31 - wl && kss + 31 <= qa + w;
+            const int mode = rstage ? 3 : ((gstage || interior) ? 0 : 1);
             f32x16 s = prod(slot, sub, lo, kop, row_seed(slot + kLseOff, sub, h2));  // scores - lse, base 2
             // element i: query kss + 8*h2 + kc, key qv, offset m = qv - query: reversed table
-            if (kBias && !gstage) add_bias(s, bias_lds + kBiasPad + kss + 8 * h2 - qv + w);
-            mask_scores(s, mode, 0u, h2, kss + 8 * h2 - qv + wl, span, nullptr, 0);
+            if (kBias && !gstage && !rstage) add_bias(s, bias_lds + kBiasPad + kss + 8 * h2 - qv + w);
+            // Random stage: invalid queries are those past the end.
+            const uint32_t rinv = rstage ? ~bits_below(L - kss) : 0u;
+            mask_scores<kRandom>(s, mode, rinv, h2, kss + 8 * h2 - qv + wl, span, nullptr, 0);
+            if (rstage) {  // one-sided: no query before the key; global own keys: none
+                uint32_t keep = own_global ? 0u : ~0u;
+                if (causal) keep &= bits_from(qv - (kss + 8 * h2));
+                for (int i = 0; i < 16; ++i)
+                    if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
+            }
             if (gstage && causal) {  // a global query sees no key after it: slots from gfirst on
                 const uint32_t keep = bits_from(gfirst - (kStageKeys * t + 32 * sub + 8 * h2));
                 for (int i = 0; i < 16; ++i)
@@ -717,7 +800,7 @@ void bwd_dkv_kernel(const BwdParams p) {
         const char* hslot;
         if (gb == 0) {
             const int u = tl.n_band - 2 + hs;
-            hslot = ring + ((n_gst + u) & 1) * kStageB;
+            hslot = ring + ((n_lst + u) & 1) * kStageB;
             wait_vmcnt<0>();
         } else {
             __syncthreads();  // the ring is free
@@ -827,12 +910,15 @@ hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-#define LF_DQ(C, Bi) hipLaunchKernelGGL((bwd_dq_kernel<C, Bi>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_DQ(C, Bi, R) hipLaunchKernelGGL((bwd_dq_kernel<C, Bi, R>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_DQ_R(C, Bi) \
+    if (p.rnd) LF_DQ(C, Bi, true); else LF_DQ(C, Bi, false)
     if (p.causal) {
-        if (p.bias) LF_DQ(true, true); else LF_DQ(true, false);
+        if (p.bias) { LF_DQ_R(true, true); } else { LF_DQ_R(true, false); }
     } else {
-        if (p.bias) LF_DQ(false, true); else LF_DQ(false, false);
+        if (p.bias) { LF_DQ_R(false, true); } else { LF_DQ_R(false, false); }
     }
+#undef LF_DQ_R
 #undef LF_DQ
     return hipGetLastError();
 }
@@ -840,12 +926,15 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-#define LF_DKV(C, Bi) hipLaunchKernelGGL((bwd_dkv_kernel<C, Bi>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_DKV(C, Bi, R) hipLaunchKernelGGL((bwd_dkv_kernel<C, Bi, R>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_DKV_R(C, Bi) \
+    if (p.rnd) LF_DKV(C, Bi, true); else LF_DKV(C, Bi, false)
     if (p.causal) {
-        if (p.bias) LF_DKV(true, true); else LF_DKV(true, false);
+        if (p.bias) { LF_DKV_R(true, true); } else { LF_DKV_R(true, false); }
     } else {
-        if (p.bias) LF_DKV(false, true); else LF_DKV(false, false);
+        if (p.bias) { LF_DKV_R(false, true); } else { LF_DKV_R(false, false); }
     }
+#undef LF_DKV_R
 #undef LF_DKV
     return hipGetLastError();
 }

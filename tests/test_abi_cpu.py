@@ -324,8 +324,8 @@ def test_random_blocks_validation():
         assert call(2, 129) == 1 and "L = 129 gives 3" in err(), err()
         assert call(2, 128, [1, 2]) == 2 and "undilated" in err()
         st = lib.lf_attn_backward(h, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8,
-                                  FAKE * 9, 1, 2, 128, 64, 8, dil_p, None, 0, None, None)
-        assert st == 2 and "random" in err(), err()
+                                  FAKE * 9, 1, 3, 128, 64, 8, dil_p, None, 0, None, None)
+        assert st == 1 and "random blocks are for H = 2" in err(), err()
         assert lib.lf_attn_set_random_blocks(h, None, 0, 0, 0) == 0
     finally:
         lib.lf_attn_destroy(h)

@@ -2,6 +2,7 @@
 draws) against the fp64 oracle with the same draws.
 
 Tolerances as everywhere: fp32 max-abs 1e-4; bf16 max-abs 2e-2 and mean-abs 2e-3;
+gradients max-abs 2e-2 and mean-abs 1e-2 of the reference scale;
 log-sum-exp max-abs 1e-4 / 2e-2.  Draws come from the seeded generator (r distinct
 key blocks per head and query block), plus hand-made tables with duplicates, unused
 entries, every block, and each row's own block.
@@ -189,3 +190,86 @@ def test_random_layer():
     err = np.abs(out.cpu().double().numpy() - ref)
     log(f"  layer + random: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
     assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN
+
+
+# (name, B, H, L, w, globals, pad lengths, causal, draws)
+BWD_CASES = [
+    ("plain_ragged", 1, 2, 300, 16, [], None, False, 2),
+    ("globals_padded", 2, 2, 384, 20, [0, 7, 200, 383], [384, 250], False, 3),
+    ("causal_globals", 1, 2, 400, 24, [0, 99, 399], None, True, 3),
+    ("causal_padded_dups", 2, 1, 333, 10, [7, 150], [333, 150], True, "dups"),
+    ("w0_every_block", 1, 1, 256, 0, [5], None, False, "every"),
+    ("many_globals", 1, 2, 640, 20, list(range(0, 640, 9)), None, False, 3),
+    ("lm_like_1024", 1, 2, 1024, 128, [0, 511], None, False, 3),
+    ("max_draws_1024", 1, 1, 1024, 32, [3], None, False, "max"),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_random_backward(case):
+    from sparse_long_sequence_longformer_amd import binding
+    from tests.test_gpu_backward import _compare_grad, _dout
+
+    name, B, H, L, w, G, lens, causal, kind = case
+    log(f"case random backward {name}: B={B} H={H} L={L} w={w} causal={causal} draws={kind}")
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=len(name) + 700)
+    do = _dout(B, H, L, len(name) + 700)
+    rnd = _draws(kind, H, L, len(name) + 1)
+    pad = _pad_from_lengths(B, L, lens)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    dil = [1] * H
+    out, lse = binding.forward_lse(qd, kd, vd, w, dil, G, _padd(pad), causal=causal, rand=rnd)
+    dq, dk, dv = binding.backward(qd, kd, vd, out, dod, lse, w, dil, G, _padd(pad), causal=causal, rand=rnd)
+    torch.cuda.synchronize()
+    rq, rk, rv = orc.attention_backward(q, k, v, do, w, dil, G, pad, causal=causal, rand=rnd)
+    _compare_grad(dq.cpu(), rq, f"{name} dq")
+    _compare_grad(dk.cpu(), rk, f"{name} dk")
+    _compare_grad(dv.cpu(), rv, f"{name} dv")
+
+
+@pytest.mark.parametrize("row", [0, 70, 200, 299])
+def test_random_backward_structure_exact(row):
+    """dO on one row only: dK, dV exactly zero off that row's key set (window, globals
+    and its query block's draws), nonzero on it; dQ zero on every other row."""
+    from oracle import brute
+    from sparse_long_sequence_longformer_amd import binding
+    from tests.test_gpu_backward import _dout
+
+    B, H, L, w, G = 1, 2, 300, 6, [7, 200]
+    pad = np.zeros((B, L), dtype=np.uint8)
+    pad[0, [20, 150, 151, 290]] = 1
+    rnd = make_random_blocks(H, L, 2, seed=11)
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=53)
+    do = torch.zeros(B, H, L, 64, dtype=torch.bfloat16)
+    do[:, :, row] = _dout(B, H, 1, row)[:, :, 0]
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    out, lse = binding.forward_lse(qd, kd, vd, w, [1, 1], G, _padd(pad), rand=rnd)
+    dq, dk, dv = (t.cpu() for t in binding.backward(qd, kd, vd, out, dod, lse, w, [1, 1], G, _padd(pad), rand=rnd))
+    for h in range(H):
+        keys = set(brute.key_set(row, L, w, 1, G, pad[0].astype(bool).tolist(), rand=rnd[h], rand_block=64))
+        off = torch.from_numpy(np.array([j not in keys for j in range(L)]))
+        assert torch.all(dk[0, h][off] == 0) and torch.all(dv[0, h][off] == 0), (h, row)
+        assert bool((dv[0, h][~off].abs().amax(dim=1) > 0).all()), (h, row)
+        others = torch.ones(L, dtype=torch.bool)
+        others[row] = False
+        assert torch.all(dq[0, h][others] == 0), (h, row)
+
+
+def test_random_backward_with_bias():
+    from sparse_long_sequence_longformer_amd import binding
+    from tests.test_gpu_backward import _compare_grad, _dout
+
+    B, H, L, w, G = 1, 2, 448, 24, [0, 250]
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=91)
+    do = _dout(B, H, L, 91)
+    rnd = make_random_blocks(H, L, 3, seed=12)
+    tab = make_bias(H, w, seed=13, scale=2.0)
+    bd = torch.from_numpy(tab).to("cuda")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    out, lse = binding.forward_lse(qd, kd, vd, w, [1, 1], G, bias=bd, rand=rnd)
+    dq, dk, dv = binding.backward(qd, kd, vd, out, dod, lse, w, [1, 1], G, bias=bd, rand=rnd)
+    torch.cuda.synchronize()
+    rq, rk, rv = orc.attention_backward(q, k, v, do, w, [1, 1], G, bias=tab, rand=rnd)
+    _compare_grad(dq.cpu(), rq, "bias+random dq")
+    _compare_grad(dk.cpu(), rk, "bias+random dk")
+    _compare_grad(dv.cpu(), rv, "bias+random dv")
