@@ -855,27 +855,47 @@ void bwd_dkv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Global rows and keys: one work-group per (global index, b*H + h); wave x sums the
-// partials of tiles x, x + 4, ...; the four waves are added in wave order.
+// Global rows and keys: one work-group of W <= kBwdMergeWaves waves per (global index,
+// b*H + h), lane = column (W = blockDim / 64, chosen by the host).  Wave x sums tiles
+// x, x + W, ... (the loads of kBwdMergeChunk tiles issued together, absent tiles read
+// tile 0 and are dropped), then the wave sums are added in wave order.
 
-__global__ __launch_bounds__(kThreads) void bwd_merge_kernel(const BwdParams p) {
-    __shared__ float red[kWaves][3][64];
+constexpr int kBwdMergeWaves = 16;
+constexpr int kBwdMergeChunk = 8;
+__global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const BwdParams p) {
+    __shared__ float red[kBwdMergeWaves][3][64];
     const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
     const int h = bh % p.H, dil = p.dil[h], L = p.L;
     const int bseq = bh / p.H, gofs = bseq * p.gstride;
     if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
     const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
+    const size_t base = (size_t)bh * p.tiles_per_head * ngq * 64 + (size_t)gi * 64 + d;
     float sq = 0.f, sk = 0.f, sv = 0.f;
-    for (int t = wv; t < p.tiles_per_head; t += kWaves) {
-        const int r = t / tpr;
-        const bool exists = r < dil && (t - r * tpr) * kRowsPerBlock < (L - r + dil - 1) / dil;
-        if (!exists) continue;
-        const size_t idx = (((size_t)bh * p.tiles_per_head + t) * ngq + gi) * 64 + d;
-        sq += p.ws_dq[idx];
-        sk += p.ws_dk[idx];
-        sv += p.ws_dv[idx];
+    for (int c0 = 0; c0 * W < p.tiles_per_head; c0 += kBwdMergeChunk) {
+        float a[kBwdMergeChunk], b[kBwdMergeChunk], c[kBwdMergeChunk];
+        bool ex[kBwdMergeChunk];
+#pragma unroll
+        for (int j = 0; j < kBwdMergeChunk; ++j) {
+            const int t = (c0 + j) * W + wv;
+            ex[j] = t < p.tiles_per_head && tile_exists(t, tpr, dil, L, kRowsPerBlock);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every test before the first load
+#pragma unroll
+        for (int j = 0; j < kBwdMergeChunk; ++j) {
+            const size_t idx = base + (ex[j] ? (size_t)((c0 + j) * W + wv) * ngq * 64 : 0);
+            a[j] = p.ws_dq[idx];
+            b[j] = p.ws_dk[idx];
+            c[j] = p.ws_dv[idx];
+        }
+#pragma unroll
+        for (int j = 0; j < kBwdMergeChunk; ++j) {
+            sq += ex[j] ? a[j] : 0.f;
+            sk += ex[j] ? b[j] : 0.f;
+            sv += ex[j] ? c[j] : 0.f;
+        }
     }
     red[wv][0][d] = sq;
     red[wv][1][d] = sk;
@@ -886,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void bwd_merge_kernel(const BwdParams p) 
     sq = 0.f;
     sk = p.ws_dkg[own];
     sv = p.ws_dvg[own];
-    for (int x = 0; x < kWaves; ++x) {
+    for (int x = 0; x < W; ++x) {
         sq += red[x][0][d];
         sk += red[x][1][d];
         sv += red[x][2][d];
@@ -941,7 +961,8 @@ hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
 
 hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s) {
     if (p.n_g == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_merge_kernel, dim3(p.n_g, p.B * p.H), dim3(kThreads), 0, s, p);
+    const int waves = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);
+    hipLaunchKernelGGL(bwd_merge_kernel, dim3(p.n_g, p.B * p.H), dim3(64 * waves), 0, s, p);
     return hipGetLastError();
 }
 

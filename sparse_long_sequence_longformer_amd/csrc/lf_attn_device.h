@@ -174,6 +174,21 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32,
     }
 }
 
+// Whether work-group tile t of a head exists: tile t covers rows [rows*(t - r*tpr), +rows)
+// of residue class r = t / tpr (tpr tiles per class, classes 0..dil-1 of a length-L
+// sequence).  Every argument is uniform, so this is scalar arithmetic.
+__device__ __forceinline__ bool tile_exists(int t, int tpr, int dil, int L, int rows) {
+    const int r = t / tpr;
+    return r < dil && (t - r * tpr) * rows < (L - r + dil - 1) / dil;
+}
+
+// Waves of a merge work-group: enough for one chunk of `chunk` tiles per wave, at most
+// `most`.
+inline int merge_waves(int tiles, int chunk, int most) {
+    const int w = (tiles + chunk - 1) / chunk;
+    return w < 1 ? 1 : (w > most ? most : w);
+}
+
 // Number of entries of the sorted array pos[0..n) that are <= x (binary search).
 __device__ __forceinline__ int count_le(const int* pos, int n, int x) {
     int lo = 0, hi = n;

@@ -49,6 +49,8 @@ namespace lf {
 namespace {
 
 constexpr int kMaskWindow = 64;           // band stages whose pad masks are built at once
+constexpr int kMergeWaves = 16;           // merge_kernel: most waves per work-group
+constexpr int kMergeChunk = 8;            // merge_kernel: tiles whose loads a wave issues together
 constexpr int kMaskRing = 2 * kMaskWindow;
 constexpr int kMaxGlobalStages = LF_MAX_GLOBALS / kStageKeys;
 constexpr int kAllParts = -1;     // dma_stage: every block of the wave
@@ -888,17 +890,20 @@ void band_kernel(const Params p) {
 
 }
 
-// (d) Merge of the global-row partials: one work-group per (global query, b*H + h),
-// thread (wave x, column d).  Wave x folds tile groups x, x+4, ... of 8 tiles each
-// (the 8 loads of a group are issued together), then the four wave states are
-// combined in wave order; the result does not depend on timing.
+// (d) Merge of the global-row partials: one work-group of W <= kMergeWaves waves per
+// (global query, b*H + h), lane = output column (W = blockDim / 64, chosen by the host
+// so that one chunk per wave covers a head's tiles).  Wave x takes tiles x, x + W, ...
+// in chunks of kMergeChunk whose loads are issued together (absent tiles read tile 0
+// and are dropped after the load, so there is no branch between the loads); within a
+// chunk the maximum comes first and the weighted sums are added in tile order, and the
+// wave states are combined in wave order: the result does not depend on timing.
 template <class T>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p) {
     using Elem = typename T::Elem;
-    constexpr int kGroup = 8;
-    __shared__ float red[kWaves][3][64];
+    __shared__ float red[kMergeWaves][3][64];
     const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
     const int h = bh % p.H, dil = p.dil[h], L = p.L;
     const int bseq = bh / p.H, gofs = bseq * p.gstride;
     if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
@@ -907,24 +912,41 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
     const size_t base = (size_t)bh * p.tiles_per_head * n_gq + gi;
     float M = kNegInf, l = 0.f, o = 0.f;
-    for (int t0 = kGroup * wv; t0 < p.tiles_per_head; t0 += kGroup * kWaves) {
-        float mt[kGroup], lt[kGroup], ot[kGroup];
-        for (int j = 0; j < kGroup; ++j) {
-            const int t = t0 + j, r = t / tpr;
-            const bool exists = t < p.tiles_per_head && r < dil && (t - r * tpr) * rows < (L - r + dil - 1) / dil;
-            const size_t idx = base + (size_t)t * n_gq;
-            mt[j] = exists ? p.ws_ml[2 * idx] : kNegInf;
-            lt[j] = exists ? p.ws_ml[2 * idx + 1] : 0.f;
-            ot[j] = exists ? p.ws_acc[idx * 64 + d] : 0.f;
+    for (int c0 = 0; c0 * W < p.tiles_per_head; c0 += kMergeChunk) {
+        float mt[kMergeChunk], lt[kMergeChunk], ot[kMergeChunk];
+        bool ex[kMergeChunk];
+#pragma unroll
+        for (int j = 0; j < kMergeChunk; ++j) {
+            const int t = (c0 + j) * W + wv;
+            ex[j] = t < p.tiles_per_head && tile_exists(t, tpr, dil, L, rows);
         }
-        for (int j = 0; j < kGroup; ++j) {
-            if (mt[j] == kNegInf) continue;  // absent tile, or no valid home key in it
-            const float Mn = fmaxf(M, mt[j]);
-            const float a = fast_exp2(M - Mn), b = fast_exp2(mt[j] - Mn);
-            l = l * a + lt[j] * b;
-            o = o * a + ot[j] * b;
-            M = Mn;
+        __builtin_amdgcn_sched_barrier(0);  // every test before the first load
+#pragma unroll
+        for (int j = 0; j < kMergeChunk; ++j) {
+            const size_t idx = base + (ex[j] ? (size_t)((c0 + j) * W + wv) * n_gq : 0);
+            mt[j] = p.ws_ml[2 * idx];
+            lt[j] = p.ws_ml[2 * idx + 1];
+            ot[j] = p.ws_acc[idx * 64 + d];
         }
+        float Mc = kNegInf;
+#pragma unroll
+        for (int j = 0; j < kMergeChunk; ++j) {
+            mt[j] = ex[j] ? mt[j] : kNegInf;
+            Mc = fmaxf(Mc, mt[j]);
+        }
+        if (Mc == kNegInf) continue;  // no tile of this chunk has a valid home key
+        float lc = 0.f, oc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMergeChunk; ++j) {
+            const float e = fast_exp2(mt[j] - Mc);  // 0 for absent tiles (mt = -inf)
+            lc += (ex[j] ? lt[j] : 0.f) * e;
+            oc += (ex[j] ? ot[j] : 0.f) * e;
+        }
+        const float Mn = fmaxf(M, Mc);
+        const float a = fast_exp2(M - Mn), b = fast_exp2(Mc - Mn);
+        l = l * a + lc * b;
+        o = o * a + oc * b;
+        M = Mn;
     }
     red[wv][0][d] = M;
     red[wv][1][d] = l;
@@ -932,19 +954,20 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p) {
     __syncthreads();
     if (wv != 0) return;
     M = kNegInf;
-    for (int x = 0; x < kWaves; ++x) M = fmaxf(M, red[x][0][d]);
+    for (int x = 0; x < W; ++x) M = fmaxf(M, red[x][0][d]);
     l = 0.f;
     o = 0.f;
     if (M != kNegInf)
-        for (int x = 0; x < kWaves; ++x) {
+        for (int x = 0; x < W; ++x) {
             const float e = fast_exp2(red[x][0][d] - M);  // 0 for an empty wave
             l += red[x][1][d] * e;
             o += red[x][2][d] * e;
         }
     const float res = l > 0.f ? o / l : 0.f;
+    const int g = p.g[gofs + gi];
     Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bh * L * 64;
-    O[(size_t)p.g[gofs + gi] * 64 + d] = T::from_float(res);
-    if (p.lse && d == 0) p.lse[(size_t)bh * L + p.g[gofs + gi]] = lse_of(M, l);
+    O[(size_t)g * 64 + d] = T::from_float(res);
+    if (p.lse && d == 0) p.lse[(size_t)bh * L + g] = lse_of(M, l);
 }
 
 }  // namespace
@@ -972,10 +995,11 @@ hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s) {
     if (p.n_g == 0) return hipSuccess;
     const dim3 grid(p.n_g, p.B * p.H);
+    const int waves = merge_waves(p.tiles_per_head, kMergeChunk, kMergeWaves);
     if (dtype == LF_BF16)
-        hipLaunchKernelGGL(merge_kernel<Bf16>, grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(merge_kernel<Bf16>, grid, dim3(64 * waves), 0, s, p);
     else
-        hipLaunchKernelGGL(merge_kernel<F32>, grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(merge_kernel<F32>, grid, dim3(64 * waves), 0, s, p);
     return hipGetLastError();
 }
 
