@@ -288,33 +288,51 @@ __device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int A, int 
 }
 
 // ---------------------------------------------------------------------------
-// Row statistics: D, lse2, lse2_band.  One thread per (b, h, row).
+// Row statistics: D, lse2, lse2_band.  One work-group per 128 rows of one (b, h): eight
+// lanes per row, each reading 16 bytes of O and of dO (a wave reads eight whole rows of
+// each per load); a lane group takes kPrepRowsPerGroup rows with all their loads in
+// flight together, adds the partial dot products across its eight lanes, and lane k of
+// the group finishes row k (log-sum-exp conversion, global test, stores).
 
+constexpr int kPrepRowsPerGroup = 4;
+constexpr int kPrepGroups = kThreads / 8;
+constexpr int kPrepRowsPerBlock = kPrepGroups * kPrepRowsPerGroup;
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
-    const size_t n = (size_t)p.B * p.H * p.L;
-    const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    const int pos = (int)(i % (size_t)p.L);
-    const int b = (int)(i / ((size_t)p.L * p.H)), gofs = b * p.gstride;
-    const int ng = p.gstride ? p.gcnt[b] : p.n_g;
-    const u32x4* o = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + i * 64);
-    const u32x4* g = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + i * 64);
-    float acc = 0.f;
-    for (int c = 0; c < 8; ++c) {
-        const f32x8 a = __builtin_convertvector(__builtin_bit_cast(bf16x8, o[c]), f32x8);
-        const f32x8 b = __builtin_convertvector(__builtin_bit_cast(bf16x8, g[c]), f32x8);
-        for (int j = 0; j < 8; ++j) acc += a[j] * b[j];
+    __shared__ int gpos[LF_MAX_GLOBALS];  // this sequence's global positions, sorted
+    const int L = p.L;
+    const int nblk = (L + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+    const int bseq = bh / p.H, gofs = bseq * p.gstride;
+    const int ng = p.gstride ? p.gcnt[bseq] : p.n_g;
+    const int c = threadIdx.x & 7;  // 16-byte chunk of a row
+    const int pos0 = blk * kPrepRowsPerBlock + (threadIdx.x >> 3);
+    const size_t off = (size_t)bh * L;
+    u32x4 o[kPrepRowsPerGroup], g[kPrepRowsPerGroup];
+    for (int k = 0; k < kPrepRowsPerGroup; ++k) {
+        const int pos = pos0 + k * kPrepGroups;
+        const size_t row = off + (pos < L ? pos : 0);
+        o[k] = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + row * 64)[c];
+        g[k] = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + row * 64)[c];
     }
+    for (int t = threadIdx.x; t < ng; t += kThreads) gpos[t] = p.g[gofs + t];
+    __syncthreads();
+    float mine = 0.f;  // the dot product of row c of this group (c < kPrepRowsPerGroup)
+    for (int k = 0; k < kPrepRowsPerGroup; ++k) {
+        const f32x8 a = __builtin_convertvector(__builtin_bit_cast(bf16x8, o[k]), f32x8);
+        const f32x8 b = __builtin_convertvector(__builtin_bit_cast(bf16x8, g[k]), f32x8);
+        float acc = 0.f;
+        for (int j = 0; j < 8; ++j) acc += a[j] * b[j];
+        for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);  // the row's eight lanes
+        mine = c == k ? acc : mine;
+    }
+    const int pos = pos0 + c * kPrepGroups;
+    if (c >= kPrepRowsPerGroup || pos >= L) return;
+    const size_t i = off + pos;
     const float lse = p.lse[i];
     const float l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
-    int lo = 0, hi = ng;  // binary search of the sorted global positions
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (p.g[gofs + mid] < pos) lo = mid + 1;
-        else hi = mid;
-    }
-    const bool is_g = lo < ng && p.g[gofs + lo] == pos;
-    p.dsum[i] = acc;
+    const int cnt = count_le(gpos, ng, pos);
+    const bool is_g = cnt > 0 && gpos[cnt - 1] == pos;
+    p.dsum[i] = mine;
     p.lse2[i] = l2;
     p.lse2_band[i] = is_g ? kPosInf : l2;
 }
@@ -920,10 +938,10 @@ __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const Bw
 }  // namespace
 
 hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
-    const size_t n = (size_t)p.B * p.H * p.L;
-    const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads);
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3(blocks), dim3(kThreads), 0, s, p);
+    const long long blocks = (long long)p.B * p.H * ((p.L + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock);
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
