@@ -277,9 +277,11 @@ lf_status lf_attn_set_random_blocks(lf_attn_t h, const int32_t* blocks, int n_he
  * ffn    : feed-forward width, a positive multiple of 8.
  * w, dil_per_head (one per head), global_idx, n_global, key_pad_mask [B][L]: as
  * lf_attn_forward.
- * GEMMs run in rocBLAS (bf16 inputs, fp32 accumulation and output); the handle
- * owns a rocBLAS handle and a third device workspace for the intermediates
- * (about (12 * hidden + 6 * ffn) bytes per token).  Errors: as lf_attn_forward;
+ * GEMMs run in rocBLAS (bf16 inputs, fp32 accumulation; the QKV and first
+ * feed-forward outputs in bf16, the two outputs that feed a LayerNorm in fp32;
+ * biases are added in fp32 by the pointwise passes); the handle owns a rocBLAS
+ * handle and a third device workspace for the intermediates (max(6 * hidden,
+ * 2 * ffn) + 10 * hidden + 2 * ffn bytes per token).  Errors: as lf_attn_forward;
  * LF_ERR_UNSUPPORTED for fp32 handles or unsupported sizes.
  */
 typedef struct lf_layer_weights {

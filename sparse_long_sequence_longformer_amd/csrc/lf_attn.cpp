@@ -607,14 +607,15 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     return st;
 }
 
-// Y[M][N] (fp32, row-major) = X[M][K] (bf16) W^T with W[N][K] (bf16): in rocBLAS's
-// column-major terms Y^T = W X^T.
-lf_status gemm_xwt(lf_attn_t h, const void* X, const void* Wt, float* Y, int M, int N, int K) {
+// Y[M][N] (row-major; bf16, or fp32 when f32_out) = X[M][K] (bf16) W^T with W[N][K]
+// (bf16), fp32 accumulation: in rocBLAS's column-major terms Y^T = W X^T.
+lf_status gemm_xwt(lf_attn_t h, const void* X, const void* Wt, void* Y, int M, int N, int K, bool f32_out) {
     const float one = 1.f, zero = 0.f;
+    const rocblas_datatype yt = f32_out ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
     const rocblas_status rs = rocblas_gemm_ex(
         h->blas, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, Wt, rocblas_datatype_bf16_r, K,
-        X, rocblas_datatype_bf16_r, K, &zero, Y, rocblas_datatype_f32_r, N, Y, rocblas_datatype_f32_r, N,
-        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+        X, rocblas_datatype_bf16_r, K, &zero, Y, yt, N, Y, yt, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
+        0, 0);
     if (rs != rocblas_status_success) return fail(h, LF_ERR_HIP, "rocblas_gemm_ex failed: %s", rocblas_status_to_string(rs));
     return LF_OK;
 }
@@ -661,15 +662,17 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (rocblas_set_stream(h->blas, s) != rocblas_status_success) return fail(h, LF_ERR_HIP, "rocblas_set_stream failed");
 
-    // Workspace: one fp32 GEMM output [R][max(3E, F)], then bf16 q, k, v, attention
-    // output, merged heads (reused for x1), and the feed-forward activations [R][F].
-    const size_t f32_elems = R * static_cast<size_t>(std::max(3 * E, F));
+    // Workspace: one GEMM output [R][3E] or [R][F] in bf16, or [R][E] in fp32, then bf16
+    // q, k, v, attention output, merged heads (reused for x1), and the feed-forward
+    // activations [R][F].
+    const size_t g_row = std::max<size_t>(std::max(3 * E, F) * size_t(2), E * size_t(4));
     const size_t t_elems = R * static_cast<size_t>(E);
-    const size_t need = f32_elems * 4 + (5 * t_elems + R * F) * 2 + 256;
+    const size_t g_bytes = (R * g_row + 255) & ~size_t(255);
+    const size_t need = g_bytes + (5 * t_elems + R * F) * 2 + 256;
     st = reserve(h, &h->ws_layer, &h->ws_layer_bytes, &h->ws_layer_device, need);
     if (st != LF_OK) return st;
-    float* gout = reinterpret_cast<float*>(h->ws_layer);
-    uint16_t* bq = reinterpret_cast<uint16_t*>(h->ws_layer + f32_elems * 4);
+    void* gout = h->ws_layer;
+    uint16_t* bq = reinterpret_cast<uint16_t*>(h->ws_layer + g_bytes);
     uint16_t* bk = bq + t_elems;
     uint16_t* bv = bk + t_elems;
     uint16_t* ba = bv + t_elems;
@@ -678,7 +681,7 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     const int M = static_cast<int>(R);
 
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E, false) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
@@ -690,26 +693,28 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] { return lf::launch_merge_heads(ba, bm, B, L, E, s); });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, bm, wt->w_o, gout, M, E, E) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, bm, wt->w_o, gout, M, E, E, true) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] {
-        return lf::launch_bias_residual_ln(gout, wt->b_o, x, wt->ln1_g, wt->ln1_b, eps, bm, E, (long long)R, s);
+        return lf::launch_bias_residual_ln(static_cast<const float*>(gout), wt->b_o, x, wt->ln1_g, wt->ln1_b, eps, bm, E,
+                                           (long long)R, s);
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, bm, wt->w_1, gout, M, F, E) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, bm, wt->w_1, gout, M, F, E, false) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
                       [&] { return lf::launch_bias_gelu(gout, wt->b_1, bh, F, (long long)R, s); });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, bh, wt->w_2, gout, M, E, F) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, bh, wt->w_2, gout, M, E, F, true) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     return launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] {
-        return lf::launch_bias_residual_ln(gout, wt->b_2, bm, wt->ln2_g, wt->ln2_b, eps, out, E, (long long)R, s);
+        return lf::launch_bias_residual_ln(static_cast<const float*>(gout), wt->b_2, bm, wt->ln2_g, wt->ln2_b, eps, out, E,
+                                           (long long)R, s);
     });
 }
 

@@ -104,12 +104,13 @@ struct BwdParams {
 };
 
 // Launchers of the layer's pointwise passes (defined in lf_layer.hip).
-hipError_t launch_qkv_split(const float* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
+// GEMM outputs: qkv and h bf16, y (the input of a LayerNorm) fp32.
+hipError_t launch_qkv_split(const void* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
                             hipStream_t s);
 hipError_t launch_merge_heads(const void* a, void* out, int B, int L, int E, hipStream_t s);
 hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void* res, const void* gamma,
                                    const void* beta, float eps, void* out, int E, long long R, hipStream_t s);
-hipError_t launch_bias_gelu(const float* h, const void* bias, void* out, int F, long long R, hipStream_t s);
+hipError_t launch_bias_gelu(const void* h, const void* bias, void* out, int F, long long R, hipStream_t s);
 
 // Launchers (defined in lf_attn_bwd.hip).
 hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s);

@@ -1,11 +1,17 @@
 // gfx950 kernels of the Longformer layer around the sparse attention (bf16 tensors,
-// fp32 arithmetic): the steps between the library GEMMs.  All of them are
-// HBM-bound elementwise or row-wise passes, written for coalesced 16-byte accesses.
+// fp32 arithmetic): the steps between the library GEMMs.  The wide GEMM outputs (the
+// QKV projection and the first feed-forward product) arrive in bf16 (fp32
+// accumulation, rounded once); the two that feed a LayerNorm stay fp32.  All passes
+// are HBM-bound elementwise or row-wise, written for coalesced 16-byte accesses.
 //
-//   qkv_split:        x W_qkv^T (fp32) + b_qkv -> q, k, v in [B][H][L][64] (bf16)
+//   qkv_split:        x W_qkv^T + b_qkv -> q, k, v in [B][H][L][64]
 //   merge_heads:      attention output [B][H][L][64] -> [B][L][H*64]
 //   bias_residual_ln: LayerNorm(y + b + residual) over the features of a row
-//   bias_gelu:        GELU(h + b), GELU(t) = 0.5 t (1 + erf(t / sqrt(2)))
+//   bias_gelu:        GELU(h + b), GELU(t) = 0.5 t (1 + erf(t / sqrt(2))), erf by the
+//                     rational approximation of Abramowitz and Stegun, Handbook of
+//                     Mathematical Functions, formula 7.1.26 (absolute error 1.5e-7;
+//                     about 5e-7 in fp32 arithmetic, far under the bf16 rounding of
+//                     the result)
 //
 // The layer is the post-LayerNorm block of page "基于Block-Sparse Attention的
 // Longformer" §6 (attention, residual, LayerNorm, feed-forward, residual,
@@ -21,16 +27,16 @@ __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint
 __device__ __forceinline__ f32x8 load8_bf16(const uint16_t* p) {
     return __builtin_convertvector(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p)), f32x8);
 }
-__device__ __forceinline__ void store8_bf16(uint16_t* p, const f32x8& v) {
-    *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8));
-}
 __device__ __forceinline__ f32x8 load8_f32(const float* p) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+__device__ __forceinline__ void store8_bf16(uint16_t* p, const f32x8& v) {
+    *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8));
+}
 
 // One thread per 8 consecutive features of one row of x W_qkv^T ([R][3E], R = B*L).
-__global__ __launch_bounds__(256) void qkv_split_kernel(const float* qkv, const uint16_t* bias, uint16_t* q,
+__global__ __launch_bounds__(256) void qkv_split_kernel(const uint16_t* qkv, const uint16_t* bias, uint16_t* q,
                                                         uint16_t* k, uint16_t* v, int L, int E, long long n8) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
@@ -40,7 +46,7 @@ __global__ __launch_bounds__(256) void qkv_split_kernel(const float* qkv, const 
     const int which = f / E, fe = f - which * E, h = fe >> 6, d = fe & 63;
     const int H = E >> 6;
     const long long b = row / L, l = row - b * L;
-    f32x8 t = load8_f32(qkv + row * 3 * E + f) + load8_bf16(bias + f);
+    f32x8 t = load8_bf16(qkv + row * 3 * E + f) + load8_bf16(bias + f);
     uint16_t* dst = which == 0 ? q : (which == 1 ? k : v);
     store8_bf16(dst + (((b * H + h) * L + l) << 6) + d, t);
 }
@@ -106,16 +112,28 @@ __global__ __launch_bounds__(256) void bias_residual_ln_kernel(const float* y, c
     }
 }
 
+// erf(x) = sign(x) (1 - (a1 k + a2 k^2 + a3 k^3 + a4 k^4 + a5 k^5) exp(-x^2)),
+// k = 1 / (1 + p |x|), with the coefficients of formula 7.1.26.
+__device__ __forceinline__ float erf_as(float x) {
+    const float ax = __builtin_fabsf(x);
+    const float k = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+    const float poly =
+        ((((1.061405429f * k - 1.453152027f) * k + 1.421413741f) * k - 0.284496736f) * k + 0.254829592f) * k;
+    const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+    const float r = 1.0f - poly * e;
+    return x < 0.f ? -r : r;
+}
+
 // One thread per 8 features of h [R][F].
-__global__ __launch_bounds__(256) void bias_gelu_kernel(const float* hpre, const uint16_t* bias, uint16_t* out,
+__global__ __launch_bounds__(256) void bias_gelu_kernel(const uint16_t* hpre, const uint16_t* bias, uint16_t* out,
                                                         int F, long long n8) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
     const int per_row = F / 8;
     const long long row = i / per_row;
     const int f = (int)(i - row * per_row) * 8;
-    f32x8 t = load8_f32(hpre + row * F + f) + load8_bf16(bias + f);
-    for (int j = 0; j < 8; ++j) t[j] = 0.5f * t[j] * (1.0f + erff(t[j] * 0.70710678118654752f));
+    f32x8 t = load8_bf16(hpre + row * F + f) + load8_bf16(bias + f);
+    for (int j = 0; j < 8; ++j) t[j] = 0.5f * t[j] * (1.0f + erf_as(t[j] * 0.70710678118654752f));
     store8_bf16(out + row * F + f, t);
 }
 
@@ -123,10 +141,10 @@ unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_blo
 
 }  // namespace
 
-hipError_t launch_qkv_split(const float* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
+hipError_t launch_qkv_split(const void* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
                             hipStream_t s) {
     const long long n8 = (long long)B * L * 3 * E / 8;
-    hipLaunchKernelGGL(qkv_split_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, qkv,
+    hipLaunchKernelGGL(qkv_split_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, static_cast<const uint16_t*>(qkv),
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
                        static_cast<uint16_t*>(v), L, E, n8);
     return hipGetLastError();
@@ -148,9 +166,9 @@ hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void*
     return hipGetLastError();
 }
 
-hipError_t launch_bias_gelu(const float* h, const void* bias, void* out, int F, long long R, hipStream_t s) {
+hipError_t launch_bias_gelu(const void* h, const void* bias, void* out, int F, long long R, hipStream_t s) {
     const long long n8 = R * F / 8;
-    hipLaunchKernelGGL(bias_gelu_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, h,
+    hipLaunchKernelGGL(bias_gelu_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, static_cast<const uint16_t*>(h),
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), F, n8);
     return hipGetLastError();
 }

@@ -3,9 +3,9 @@
 Tolerance (bf16 activations between the steps, fp32 GEMM accumulation, bf16
 output): max-abs 5e-2 and mean-abs 5e-3 over the output, whose LayerNorm rows
 have unit scale.  The output rounding alone is up to 2^-9 of |out| (about 8e-3 at
-|out| = 4), and each of the stored intermediates (q, k, v, attention output, x1,
-feed-forward activations) adds a rounding of the same relative size before the
-next product.
+|out| = 4), and each of the stored intermediates (the QKV and first feed-forward
+GEMM outputs, q, k, v, attention output, x1, feed-forward activations) adds a
+rounding of the same relative size before the next step.
 """
 
 import numpy as np
