@@ -72,3 +72,38 @@ def test_backward_graph_replays():
         torch.cuda.synchronize()
         for a, b in zip((out, lse, dq, dk, dv), ref):
             assert torch.equal(a, b), f"replay {r}"
+
+
+def test_variant_graph_replays():
+    """Causal mode, a bias table and random blocks set on the handle: after one eager call
+    (workspaces allocated, draws uploaded) the forward and backward capture and replay
+    bit for bit."""
+    from sparse_long_sequence_longformer_amd import binding
+
+    B, H, L, w = 1, 2, 1024, 96
+    q, k, v = (t.cuda() for t in make_custom(B, H, L, dtype="bf16", seed=6))
+    do = torch.from_numpy(np.random.default_rng(2).standard_normal((B, H, L, 64), dtype=np.float32)).bfloat16().cuda()
+    h = binding.LfAttn("bf16")
+    h.set_causal(True)
+    h.set_position_bias(torch.from_numpy(workloads.make_bias(H, w, seed=3)).cuda())
+    h.set_random_blocks(workloads.make_random_blocks(H, L, 2, seed=4))
+    G = [0, 500]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse = binding.forward_lse(q, k, v, w, [1] * H, G, handle=h, causal=True)
+        dq, dk, dv = binding.backward(q, k, v, out, do, lse, w, [1] * H, G, handle=h, causal=True)
+    s.synchronize()
+    ref = [t.clone() for t in (out, lse, dq, dk, dv)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.forward_lse(q, k, v, w, [1] * H, G, out=out, lse=lse, handle=h, causal=True)
+        binding.backward(q, k, v, out, do, lse, w, [1] * H, G, dq=dq, dk=dk, dv=dv, handle=h, causal=True)
+    for r in range(3):
+        for t in (out, dq, dk, dv):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((out, lse, dq, dk, dv), ref):
+            assert torch.equal(a, b), f"replay {r}"
+        _ = (q.float() * 2).sum().item()  # eager work between replays
+    h.close()
