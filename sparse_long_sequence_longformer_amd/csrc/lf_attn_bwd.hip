@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // tile's two query blocks (kRandom, as in the forward), then the window band.
 
 template <bool kCausal, bool kBias, bool kRandom>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dq_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ uint64_t band_mask[kBwdMaskRing];
@@ -487,7 +487,10 @@ void bwd_dq_kernel(const BwdParams p) {
     if (n_st > 0) issue(0);
     wait_vmcnt<0>();
     scale_op(qop);
-    const f32x16 seed_s = splat(-my_l2), seed_d = splat(-my_d);
+    // The score product is seeded with -lse2 (its exponentials are the weights); D is
+    // subtracted after the dP product instead of seeding it, which keeps one fewer
+    // 16-register vector live across the loop.
+    const f32x16 seed_s = splat(-my_l2);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     for (int t = 0; t < n_st; ++t) {
         wait_vmcnt<0>();
@@ -526,9 +529,9 @@ void bwd_dq_kernel(const BwdParams p) {
             const int goff = kStageKeys * t + 32 * sub + 8 * h2;
             mask_scores<kRandom>(s, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
                                  !causal ? 1 << 30 : (rstage ? w - bbase + 1 : gcnt - goff));
-            const f32x16 dp = prod(slot + kTileB, sub, lo, dop, seed_d);  // dO.V - D
+            const f32x16 dp = prod(slot + kTileB, sub, lo, dop, f32x16{});  // dO.V
             float ds[16];
-            for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
+            for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * (dp[i] - my_d);
             Frag f;
             to_frag(ds, f);
             TOp tk;
@@ -624,7 +627,7 @@ void bwd_dq_kernel(const BwdParams p) {
 // queries past the end are masked.
 
 template <bool kCausal, bool kBias, bool kRandom>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dkv_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ int own_gidx[kRowsPerBlock];  // index in g of each own key, or -1
