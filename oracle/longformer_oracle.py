@@ -397,6 +397,79 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
     return dq, dk, dv
 
 
+def _grads_rows(q_rows, k, v, do_rows, m, extra=None):
+    """Gradients of O = softmax(q_rows k^T / sqrt(d) (+ extra), masked by m) v for the
+    upstream gradient do_rows: (dQ of these rows, dK and dV contributions)."""
+    d = q_rows.shape[1]
+    o, p = _attention_rows(q_rows, k, v, m, extra) if extra is not None else _attention_rows(q_rows, k, v, m)
+    dv = p.T @ do_rows
+    dp = do_rows @ v.T
+    delta = (do_rows * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - delta)
+    return ds @ k / math.sqrt(d), ds.T @ q_rows / math.sqrt(d), dv
+
+
+def attention_backward_global_proj_bh(q, k, v, q_g, k_g, v_g, dout, w: int, dil: int, global_idx=None,
+                                      pad_row=None, causal: bool = False, bias=None, rand=None,
+                                      rand_block: int = 64):
+    """Gradients of one (batch, head) slice of ``attention_global_proj``: six arrays
+    (dQ, dK, dV, dQ_g, dK_g, dV_g).  Rows outside the global set attend with q, k, v
+    (their key sets as in ``attention``), so they give dQ of those rows and dK, dV; a
+    global row attends every unpadded key (up to itself in the one-sided variant) with
+    q_g, k_g, v_g, so it gives dQ_g of that row and dK_g, dV_g.  dQ of a global row and
+    dQ_g of any other row are zero (those inputs are not read)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    q_g, k_g, v_g = _as_f64(q_g), _as_f64(k_g), _as_f64(v_g)
+    L, d = q.shape
+    G = global_set(global_idx)
+    is_g = np.zeros(L, dtype=bool)
+    is_g[G] = True
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dq_g, dk_g, dv_g = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    others = np.nonzero(~is_g)[0]
+    for s0 in range(0, others.size, ROW_BLOCK):
+        blk = others[s0:s0 + ROW_BLOCK]
+        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal, rand=rand, rand_block=rand_block)
+        extra = None if bias is None else window_bias(L, w, dil, G, blk, bias)
+        a, b_, c = _grads_rows(q[blk], k, v, do[blk], m, extra)
+        dq[blk] = a
+        dk += b_
+        dv += c
+    if G.size:
+        keep = np.ones((G.size, L), dtype=bool)
+        if pad_row is not None:
+            keep &= ~np.asarray(pad_row, dtype=bool)[None, :]
+        if causal:
+            keep &= np.arange(L)[None, :] <= G[:, None]
+        a, b_, c = _grads_rows(q_g[G], k_g, v_g, do[G], keep)
+        dq_g[G] = a
+        dk_g += b_
+        dv_g += c
+    return dq, dk, dv, dq_g, dk_g, dv_g
+
+
+def attention_backward_global_proj(q, k, v, q_g, k_g, v_g, dout, w: int, dil_per_head, global_idx=None,
+                                   key_pad_mask=None, causal: bool = False, bias=None, rand=None,
+                                   rand_block: int = 64):
+    """Gradients of the full separate-projection problem: six float64 [B, H, L, d]
+    arrays (dQ, dK, dV, dQ_g, dK_g, dV_g)."""
+    q = _as_f64(q)
+    B, H, L, d = q.shape
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    res = [np.zeros((B, H, L, d), dtype=np.float64) for _ in range(6)]
+    for b in range(B):
+        for h in range(H):
+            parts = attention_backward_global_proj_bh(
+                q[b, h], k[b, h], v[b, h], q_g[b, h], k_g[b, h], v_g[b, h], dout[b, h], w, dil[h],
+                globals_of(global_idx, b), None if pad is None else pad[b], causal=causal,
+                bias=None if bias is None else bias[h], rand=None if rand is None else rand[h],
+                rand_block=rand_block)
+            for r, x in zip(res, parts):
+                r[b, h] = x
+    return tuple(res)
+
+
 def attention_backward(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
                        causal: bool = False, bias=None, rand=None, rand_block: int = 64):
     """Gradients of the full problem: three float64 [B, H, L, d] arrays (dQ, dK, dV)."""

@@ -768,6 +768,49 @@ def pin_random_backward_autograd():
             assert err < 1e-12, (name, L, w, dil, G, padk, err)
 
 
+
+# ---------------------------------------- backward of the separate global projections
+
+def pin_global_proj_backward_autograd():
+    """Gradients of the separate-projection variant equal torch autograd of a dense
+    formulation: other rows attend their brute-force key sets with q, k, v, global rows
+    every unpadded key (up to themselves when one-sided) with q_g, k_g, v_g."""
+    cases = [(24, 8, 3, 2, [0, 7, 7, 23], "rand", False), (33, 8, 4, 1, [5, 30], None, True),
+             (40, 16, 2, 3, [1, 20, 39], "suffix", False)]
+    for L, d, w, dil, G, padk, causal in cases:
+        pad = _pad_for(padk, L, L)
+        padl = None if pad is None else pad.tolist()
+        arrs = [_rand((L, d), 1300 + L + t) for t in range(7)]
+        q, k, v, qg, kg, vg, do = arrs
+        Gs = sorted(set(G))
+        keysets = [brute.key_set(i, L, w, dil, G, padl, causal=causal) for i in range(L)]
+        ts = [torch.tensor(x, requires_grad=True) for x in (q, k, v, qg, kg, vg)]
+        base = _torch_dense_attention(ts[0], ts[1], ts[2], keysets)
+        gkeys = [[j for j in range(L) if (padl is None or not padl[j]) and (not causal or j <= i)] for i in range(L)]
+        glob = _torch_dense_attention(ts[3], ts[4], ts[5], gkeys)
+        rows = torch.zeros(L, 1, dtype=torch.float64)
+        rows[Gs] = 1.0
+        out = base * (1 - rows) + glob * rows
+        (out * torch.from_numpy(do)).sum().backward()
+        got = orc.attention_backward_global_proj_bh(q, k, v, qg, kg, vg, do, w, dil, G, pad, causal=causal)
+        for name, a, t in zip(("dq", "dk", "dv", "dq_g", "dk_g", "dv_g"), got, ts):
+            err = np.abs(a - t.grad.numpy()).max()
+            assert err < 1e-12, (name, L, w, dil, G, causal, err)
+
+
+def pin_global_proj_backward_reduces():
+    """With q_g = q, k_g = k, v_g = v the two gradient sets add up to the single-projection
+    gradients (each global row's pairs move from one set to the other)."""
+    L, d, w, dil, G = 36, 8, 3, 2, [0, 11, 35]
+    pad = _pad_for("rand", L, 5)
+    q, k, v, do = (_rand((L, d), 1400 + t) for t in range(4))
+    parts = orc.attention_backward_global_proj_bh(q, k, v, q, k, v, do, w, dil, G, pad)
+    ref = orc.attention_backward_bh(q, k, v, do, w, dil, G, pad)
+    for a, b_, r in zip(parts[:3], parts[3:], ref):
+        assert np.abs(a + b_ - r).max() < 1e-12
+    assert np.all(parts[0][G] == 0) and np.all(np.delete(parts[3], G, axis=0) == 0)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -802,6 +845,8 @@ ALL_PINS = [
     pin_random_brute,
     pin_random_limits,
     pin_random_backward_autograd,
+    pin_global_proj_backward_autograd,
+    pin_global_proj_backward_reduces,
     pin_layer_torch_encoder,
     pin_layer_norm_rows,
 ]

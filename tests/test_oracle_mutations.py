@@ -205,6 +205,13 @@ def _random_first_draw_only(rows, L, rand, block):  # only the first draw of eac
     return _orig_random(rows, L, np.asarray(rand)[:, :1], block)
 
 
+def _grads_rows_no_delta(q_rows, k, v, do_rows, m, extra=None):  # dS = P * dP (the D term dropped)
+    d = q_rows.shape[1]
+    o, p = _orig_rows(q_rows, k, v, m, extra) if extra is not None else _orig_rows(q_rows, k, v, m)
+    ds = p * (do_rows @ v.T)
+    return ds @ k / math.sqrt(d), ds.T @ q_rows / math.sqrt(d), p.T @ do_rows
+
+
 from oracle import layer_oracle as _lo  # noqa: E402
 
 _orig_ln = _lo.layer_norm
@@ -259,6 +266,7 @@ MUTANTS = {
     "random_transposed": ("random_member", _random_transposed),
     "random_next_block": ("random_member", _random_next_block),
     "random_first_draw_only": ("random_member", _random_first_draw_only),
+    "gp_bwd_no_delta": ("_grads_rows", _grads_rows_no_delta),
     "layer_ln_unbiased": ("layer:layer_norm", _ln_unbiased),
     "layer_gelu_tanh": ("layer:gelu", _gelu_tanh),
     "layer_heads_interleaved": ("layer:split_heads", _split_interleaved),
