@@ -13,7 +13,8 @@ peak (HIP events around each launch, on the launch stream), and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 
 Variants (not the default line): --global-proj (separate projections of the global
-rows), --backward (the backward pass alone and a forward + backward training step).
+rows; with --backward its backward), --backward (the backward pass alone and a
+forward + backward training step).
 """
 
 from __future__ import annotations
@@ -139,8 +140,8 @@ def cpu_baseline(wl, q, k, v, G, pad, target_s, causal=False, bias=None, rand=No
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by (batch, head) or by sequence, which this build does not implement)",
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by (batch, head) or by sequence; no multi-GPU path is implemented)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -226,7 +227,8 @@ def main():
         if wl.dtype != "bf16":
             print("bench.py: the backward runs on bf16 workloads only", file=sys.stderr)
             sys.exit(2)
-        return bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops, handle)
+        gp = (qgd, kgd, vgd) if args.global_proj else None
+        return bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops, handle, gp)
 
     for _ in range(args.warmup):
         step()
@@ -441,10 +443,11 @@ def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
     print(json.dumps(res), flush=True)
 
 
-def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, handle):
+def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, handle, gp=None):
     """Backward alone (inputs, forward output and log-sum-exp resident), then a whole
     training step (forward with log-sum-exp + backward).  Effective FLOP: 2.5 x the
-    forward's (five products per attended pair instead of two)."""
+    forward's (five products per attended pair instead of two).  gp: the separate
+    projections (q_g, k_g, v_g) of the global rows, or None."""
     import numpy as np
     import torch
 
@@ -452,8 +455,14 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
 
     g = np.random.default_rng(7).standard_normal(tuple(qd.shape), dtype=np.float32)
     dod = torch.from_numpy(g).to(torch.bfloat16).to(qd.device)
-    out, lse = binding.forward_lse(qd, kd, vd, wl.w, dil, G, padd, handle=handle, causal=args.causal)
-    dq, dk, dv = binding.backward(qd, kd, vd, out, dod, lse, wl.w, dil, G, padd, handle=handle, causal=args.causal)
+    if gp is None:
+        out, lse = binding.forward_lse(qd, kd, vd, wl.w, dil, G, padd, handle=handle, causal=args.causal)
+        grads = binding.backward(qd, kd, vd, out, dod, lse, wl.w, dil, G, padd, handle=handle, causal=args.causal)
+    else:
+        out, lse = binding.forward_global_proj_lse(qd, kd, vd, *gp, wl.w, dil, G, padd, handle=handle,
+                                                   causal=args.causal)
+        grads = binding.backward_global_proj(qd, kd, vd, *gp, out, dod, lse, wl.w, dil, G, padd, handle=handle,
+                                             causal=args.causal)
     torch.cuda.synchronize()
 
     # The timed loops call the C entry points with arguments marshalled once: the
@@ -468,16 +477,20 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
     pad_ptr = None if padd is None else padd.data_ptr()
     shape = (wl.B, wl.H, wl.L, wl.d, wl.w, ctypes.cast(dil_arr, i32p), ctypes.cast(g_arr, i32p), len(G), pad_ptr,
              stream)
-    bwd_args = (handle.handle, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), dod.data_ptr(),
-                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + shape
-    fwd_args = (handle.handle, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr()) + shape
+    qkv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr())
+    gptr = () if gp is None else tuple(t.data_ptr() for t in gp)
+    bwd_args = (handle.handle, *qkv, *gptr, out.data_ptr(), dod.data_ptr(), lse.data_ptr(),
+                *(t.data_ptr() for t in grads)) + shape
+    fwd_args = (handle.handle, *qkv, *gptr, out.data_ptr(), lse.data_ptr()) + shape
+    bwd_fn = lib.lf_attn_backward if gp is None else lib.lf_attn_backward_global_proj
+    fwd_fn = lib.lf_attn_forward_lse if gp is None else lib.lf_attn_forward_global_proj_lse
 
     def bwd():
-        if lib.lf_attn_backward(*bwd_args) != 0:
+        if bwd_fn(*bwd_args) != 0:
             raise RuntimeError(lib.lf_attn_last_error(handle.handle).decode())
 
     def train_step():
-        if lib.lf_attn_forward_lse(*fwd_args) != 0:
+        if fwd_fn(*fwd_args) != 0:
             raise RuntimeError(lib.lf_attn_last_error(handle.handle).decode())
         bwd()
 
@@ -527,7 +540,8 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
                    "global_batch": wl.B, "parallelism": "single GPU",
                    "window": "one-sided" if args.causal else "symmetric",
                    "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None,
-                   "random_blocks": f"{args.random} of 64 keys per (head, query block)" if args.random else None},
+                   "random_blocks": f"{args.random} of 64 keys per (head, query block)" if args.random else None,
+                   "global_projections": "separate" if gp is not None else "shared"},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "train_step_ms": round(ms_train, 6),
         "train_step_tflops": round(3.5 * flops_fwd / (ms_train * 1e-3) / 1e12, 3),

@@ -55,7 +55,7 @@ typedef enum lf_dtype {
 #define LF_MAX_RANDOM_DRAWS 16 /* random key blocks per query block */
 
 /* Kernel launches timed by lf_attn_stage_times. */
-#define LF_N_STAGES 8
+#define LF_N_STAGES 9
 #define LF_STAGE_BAND 0      /* window band, global-column fold, global-row partials */
 #define LF_STAGE_MERGE 1     /* log-sum-exp merge of the partials (only with globals) */
 #define LF_STAGE_BWD_PREP 2  /* backward: D = rowsum(dO * O), base-2 log-sum-exp */
@@ -64,6 +64,7 @@ typedef enum lf_dtype {
 #define LF_STAGE_BWD_MERGE 5 /* backward: sums of the global partials (only with globals) */
 #define LF_STAGE_LAYER_GEMM 6      /* layer: the four projection / feed-forward GEMMs (rocBLAS) */
 #define LF_STAGE_LAYER_POINTWISE 7 /* layer: head split and merge, LayerNorms, GELU */
+#define LF_STAGE_BWD_DKV_GLOBAL 8  /* backward, separate global projections: dK_g, dV_g */
 
 /* Pattern variants (lf_attn_set_window_mode). */
 #define LF_WINDOW_SYMMETRIC 0 /* keys i + m*dil, m = -w..w (default) */
@@ -182,6 +183,47 @@ lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k,
                                       int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
                                       const int32_t* global_idx, int n_global,
                                       const uint8_t* key_pad_mask, void* stream);
+
+/*
+ * lf_attn_forward_global_proj that also writes each row's log-sum-exp, as
+ * lf_attn_forward_lse does: lse[b,h,i] = log sum_j exp(score_ij) over the row's own
+ * key set and scores, which for a global row are Q_g . K_g / sqrt(d_h) over every
+ * unpadded key (up to i in the causal mode).  lse: DEVICE float32 [B][H][L], 4-byte
+ * aligned, overlapping no input and not `out`; -inf for rows without keys.  The
+ * statistics lf_attn_backward_global_proj needs.
+ */
+lf_status lf_attn_forward_global_proj_lse(lf_attn_t h, const void* q, const void* k, const void* v,
+                                          const void* q_g, const void* k_g, const void* v_g, void* out,
+                                          float* lse, int B, int H, int L, int d_h, int w,
+                                          const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                                          const uint8_t* key_pad_mask, void* stream);
+
+/*
+ * Backward of lf_attn_forward_global_proj: the gradients of both projections.
+ *
+ * A row outside the global set attends with q, k, v (its key set as in
+ * lf_attn_forward), which gives dq of that row and dk, dv of its keys (global keys
+ * included); a global row attends every unpadded key (only the keys up to itself in
+ * the causal mode) with q_g, k_g, v_g (page "基于Block-Sparse Attention的Longformer"
+ * §4: global attention has its own projections), which gives dq_g of that row and
+ * dk_g, dv_g of every key.  dq of a global row and dq_g of any other row are written
+ * as zero; dk_g, dv_g of padded keys are zero.
+ *
+ * q_g, k_g, v_g : DEVICE bf16 [B][H][L][d_h], as passed to the forward.
+ * dq_g, dk_g, dv_g : DEVICE bf16 [B][H][L][d_h] outputs, 16-byte aligned, overlapping
+ *                    no input and no other gradient.
+ * out and lse: as returned by lf_attn_forward_global_proj_lse for the same inputs
+ * (not lse from lf_attn_forward_lse: the global rows' normaliser differs).
+ * Everything else, including the handle's settings (window mode, global mode,
+ * position bias and random blocks, which reach only the other rows), as
+ * lf_attn_backward.  One more launch than lf_attn_backward (dk_g, dv_g).
+ */
+lf_status lf_attn_backward_global_proj(lf_attn_t h, const void* q, const void* k, const void* v,
+                                       const void* q_g, const void* k_g, const void* v_g, const void* out,
+                                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                       void* dq_g, void* dk_g, void* dv_g, int B, int H, int L, int d_h, int w,
+                                       const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                                       const uint8_t* key_pad_mask, void* stream);
 
 /*
  * Pattern variant of every later call on `h` (forward, forward_lse,

@@ -1,4 +1,4 @@
-"""Longformer window + global sparse self-attention forward for AMD MI355X (gfx950).
+"""Longformer window + global sparse self-attention for AMD MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels behind the C-ABI library
 ``liblfattn.so`` (declared in ``include/lf_attn.h``); this package is a thin
@@ -10,12 +10,12 @@ first use and raises if it has not been built.
 
 from __future__ import annotations
 
-__all__ = ["forward", "forward_lse", "backward", "forward_global_proj", "LfAttn", "LfAttnError", "library_path"]
+__all__ = ["forward", "forward_lse", "backward", "forward_global_proj", "forward_global_proj_lse",
+           "backward_global_proj", "layer_forward", "LfAttn", "LfAttnError", "library_path"]
 
 
 def __getattr__(name):
-    if name in ("forward", "forward_lse", "backward", "forward_global_proj", "LfAttn", "LfAttnError",
-                "library_path", "load_library"):
+    if name in __all__ or name == "load_library":
         from . import binding
 
         return getattr(binding, name)

@@ -21,8 +21,9 @@ LF_WINDOW_SYMMETRIC = 0
 LF_WINDOW_CAUSAL = 1
 LF_GLOBALS_SHARED = 0
 LF_GLOBALS_PER_SEQUENCE = 1
-N_STAGES = 8
-STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge", "layer_gemm", "layer_pointwise")
+N_STAGES = 9
+STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge", "layer_gemm", "layer_pointwise",
+               "bwd_dkv_global")
 LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
 MAX_HEADS = 64
 MAX_GLOBALS = 256
@@ -35,8 +36,10 @@ EXPORTS = (
     "lf_attn_create",
     "lf_attn_forward",
     "lf_attn_forward_global_proj",
+    "lf_attn_forward_global_proj_lse",
     "lf_attn_forward_lse",
     "lf_attn_backward",
+    "lf_attn_backward_global_proj",
     "lf_layer_forward",
     "lf_attn_destroy",
     "lf_attn_status_string",
@@ -87,6 +90,10 @@ def load_library():
                                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                                 i32, vp, vp]
     lib.lf_attn_forward_global_proj.restype = i32
+    lib.lf_attn_forward_global_proj_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                                    i32, vp, vp]
+    lib.lf_attn_forward_global_proj_lse.restype = i32
     lib.lf_attn_forward_lse.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
                                         vp, vp]
@@ -95,6 +102,10 @@ def load_library():
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
                                      vp, vp]
     lib.lf_attn_backward.restype = i32
+    lib.lf_attn_backward_global_proj.argtypes = [vp] * 16 + [i32, i32, i32, i32, i32,
+                                                             ctypes.POINTER(ctypes.c_int32),
+                                                             ctypes.POINTER(ctypes.c_int32), i32, vp, vp]
+    lib.lf_attn_backward_global_proj.restype = i32
     lib.lf_layer_forward.argtypes = [vp, vp, ctypes.POINTER(LayerWeights), vp, i32, i32, i32, i32, ctypes.c_float,
                                      i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32, vp, vp]
     lib.lf_layer_forward.restype = i32
@@ -190,6 +201,14 @@ class LfAttn:
                                                   out_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
+    def forward_global_proj_lse_raw(self, q_ptr, k_ptr, v_ptr, qg_ptr, kg_ptr, vg_ptr, out_ptr, lse_ptr, B, H, L,
+                                    d_h, w, dil, global_idx, pad_ptr, stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_attn_forward_global_proj_lse(self.handle, q_ptr, k_ptr, v_ptr, qg_ptr, kg_ptr, vg_ptr,
+                                                      out_ptr, lse_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr,
+                                                      stream)
+        self._check(st, self.handle)
+
     def forward_lse_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr,
                         stream):
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
@@ -202,6 +221,15 @@ class LfAttn:
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
         st = self.lib.lf_attn_backward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr,
                                        dk_ptr, dv_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def backward_global_proj_raw(self, ins, grads, lse_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
+        """ins: pointers (q, k, v, q_g, k_g, v_g, out, dout); grads: (dq, dk, dv, dq_g, dk_g, dv_g)."""
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        q, k, v, qg, kg, vg, o, do = ins
+        dq, dk, dv, dqg, dkg, dvg = grads
+        st = self.lib.lf_attn_backward_global_proj(self.handle, q, k, v, qg, kg, vg, o, do, lse_ptr, dq, dk, dv,
+                                                   dqg, dkg, dvg, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
     def set_per_sequence_globals(self, per_seq: bool):
@@ -446,6 +474,33 @@ def forward_global_proj(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, ke
     return out
 
 
+def _lse_out(lse, B, H, L, device):
+    import torch
+
+    if lse is None:
+        return torch.empty((B, H, L), dtype=torch.float32, device=device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
+    return lse
+
+
+def forward_global_proj_lse(q, k, v, q_g, k_g, v_g, w: int, dil, global_idx=None, key_pad_mask=None, out=None,
+                            lse=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
+    """``forward_global_proj`` that also returns each row's log-sum-exp: (out, lse), the
+    statistics ``backward_global_proj`` needs."""
+    import torch
+
+    B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
+        q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g)], w, dil, global_idx,
+        key_pad_mask, out, handle, causal, rand is not None)
+    lse = _lse_out(lse, B, H, L, q.device)
+    with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
+        h.forward_global_proj_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_g.data_ptr(), k_g.data_ptr(),
+                                      v_g.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, L, d_h, int(w), dil,
+                                      global_idx, pad_ptr, stream)
+    return out, lse
+
+
 def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, lse=None,
                 handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
     """``forward`` that also returns each row's log-sum-exp: (out, lse), lse a float32
@@ -454,10 +509,7 @@ def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=No
 
     B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
         q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal, rand is not None)
-    if lse is None:
-        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
+    lse = _lse_out(lse, B, H, L, q.device)
     with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.forward_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, L, d_h,
                           int(w), dil, global_idx, pad_ptr, stream)
@@ -494,6 +546,37 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d_h, int(w), dil, global_idx, pad_ptr,
                        stream)
     return dq, dk, dv
+
+
+def backward_global_proj(q, k, v, q_g, k_g, v_g, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask=None,
+                         grads=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
+    """Gradients (dq, dk, dv, dq_g, dk_g, dv_g) of ``forward_global_proj`` for ``dout``.
+
+    All tensors contiguous bf16 [B, H, L, 64] on the device; ``out`` and ``lse`` as
+    returned by ``forward_global_proj_lse``.  grads: six preallocated outputs, or None.
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward supports bfloat16 tensors only")
+    B, H, L, d_h, dil, global_idx, pad_ptr, _, h, stream = _marshal(
+        q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g), ("out", out), ("dout", dout)], w, dil,
+        global_idx, key_pad_mask, out, handle, causal, rand is not None)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, L]")
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(6))
+    grads = tuple(grads)
+    if len(grads) != 6:
+        raise ValueError("grads must hold six tensors")
+    for t in grads:
+        if t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("the gradients must be contiguous device tensors like q")
+    ins = tuple(t.data_ptr() for t in (q, k, v, q_g, k_g, v_g, out, dout))
+    with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
+        h.backward_global_proj_raw(ins, tuple(t.data_ptr() for t in grads), lse.data_ptr(), B, H, L, d_h, int(w),
+                                   dil, global_idx, pad_ptr, stream)
+    return grads
 
 
 def layer_forward(x, weights: dict, w: int, dil, global_idx=None, key_pad_mask=None, eps: float = 1e-5, out=None,

@@ -458,6 +458,8 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
         if (overlaps2(lse, lb, q, bytes) || overlaps2(lse, lb, k, bytes) || overlaps2(lse, lb, v, bytes) ||
             overlaps2(lse, lb, out, bytes))
             return fail(h, LF_ERR_INVALID_ARG, "lse must not overlap q, k, v or out");
+        if (sep && (overlaps2(lse, lb, qg, bytes) || overlaps2(lse, lb, kg, bytes) || overlaps2(lse, lb, vg, bytes)))
+            return fail(h, LF_ERR_INVALID_ARG, "lse must not overlap q_g, k_g or v_g");
     }
 
     lf::Params p;
@@ -511,34 +513,43 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     return launch_stage(h, LF_STAGE_MERGE, s, [&] { return lf::launch_merge(p, dt, s); });
 }
 
-lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* out, const void* dout,
-                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int L, int d_h, int w,
+// Every backward entry point.  qg .. dvg are all null (one projection for every row) or
+// all non-null (separate projections of the global rows and their gradients).
+lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
+                        const void* vg, const void* out, const void* dout, const float* lse, void* dq, void* dk,
+                        void* dv, void* dqg, void* dkg, void* dvg, int B, int H, int L, int d_h, int w,
                         const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
                         const uint8_t* key_pad_mask, void* stream) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->last_error.clear();
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
         return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-null");
+    const bool sep = qg || kg || vg || dqg || dkg || dvg;
+    if (sep && !(qg && kg && vg && dqg && dkg && dvg))
+        return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g, v_g, dq_g, dk_g and dv_g must all be non-null");
     if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the backward supports bf16 handles only");
     Plan pl;
     lf_status st = make_plan(h, pl, B, H, L, d_h, w, dil_per_head, global_idx, n_global);
     if (st != LF_OK) return st;
-    const void* ins[] = {q, k, v, out, dout};
-    void* outs[] = {dq, dk, dv};
-    for (const void* x : ins)
-        if (!aligned16(x)) return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out and dout must be 16-byte aligned");
-    for (const void* x : outs)
-        if (!aligned16(x)) return fail(h, LF_ERR_INVALID_ARG, "dq, dk and dv must be 16-byte aligned");
+    const void* ins[] = {q, k, v, out, dout, qg, kg, vg};
+    void* outs[] = {dq, dk, dv, dqg, dkg, dvg};
+    const int n_ins = sep ? 8 : 5, n_outs = sep ? 6 : 3;
+    for (int i = 0; i < n_ins; ++i)
+        if (!aligned16(ins[i]))
+            return fail(h, LF_ERR_INVALID_ARG, "q, k, v, out, dout (and q_g, k_g, v_g) must be 16-byte aligned");
+    for (int i = 0; i < n_outs; ++i)
+        if (!aligned16(outs[i]))
+            return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv (and dq_g, dk_g, dv_g) must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(h, LF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
     const size_t bytes = pl.bytes;
     const size_t lb = static_cast<size_t>(B) * H * L * sizeof(float);
-    for (int i = 0; i < 3; ++i) {
-        for (const void* x : ins)
-            if (overlaps(outs[i], x, bytes)) return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv must not overlap the inputs");
+    for (int i = 0; i < n_outs; ++i) {
+        for (int j = 0; j < n_ins; ++j)
+            if (overlaps(outs[i], ins[j], bytes)) return fail(h, LF_ERR_INVALID_ARG, "the gradients must not overlap the inputs");
         if (overlaps2(outs[i], bytes, lse, lb))
-            return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv must not overlap the inputs");
+            return fail(h, LF_ERR_INVALID_ARG, "the gradients must not overlap the inputs");
         for (int j = 0; j < i; ++j)
-            if (overlaps(outs[i], outs[j], bytes)) return fail(h, LF_ERR_INVALID_ARG, "dq, dk, dv must not overlap");
+            if (overlaps(outs[i], outs[j], bytes)) return fail(h, LF_ERR_INVALID_ARG, "the gradients must not overlap");
     }
 
     lf::BwdParams p;
@@ -552,6 +563,13 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
+    p.sep = sep ? 1 : 0;
+    p.qg = qg;
+    p.kg = kg;
+    p.vg = vg;
+    p.dqg = dqg;
+    p.dkg = dkg;
+    p.dvg = dvg;
     p.pad = key_pad_mask;
     p.lse = lse;
     p.B = B;
@@ -602,6 +620,8 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     st = launch_stage(h, LF_STAGE_BWD_PREP, s, [&] { return lf::launch_bwd_prep(p, s); });
     if (st == LF_OK) st = launch_stage(h, LF_STAGE_BWD_DQ, s, [&] { return lf::launch_bwd_dq(p, s); });
     if (st == LF_OK) st = launch_stage(h, LF_STAGE_BWD_DKV, s, [&] { return lf::launch_bwd_dkv(p, s); });
+    if (st == LF_OK && sep)
+        st = launch_stage(h, LF_STAGE_BWD_DKV_GLOBAL, s, [&] { return lf::launch_bwd_dkv_global_proj(p, s); });
     if (st == LF_OK && p.n_g > 0)
         st = launch_stage(h, LF_STAGE_BWD_MERGE, s, [&] { return lf::launch_bwd_merge(p, s); });
     return st;
@@ -752,12 +772,35 @@ lf_status lf_attn_forward_global_proj(lf_attn_t h, const void* q, const void* k,
                         n_global, key_pad_mask, stream);
 }
 
+lf_status lf_attn_forward_global_proj_lse(lf_attn_t h, const void* q, const void* k, const void* v,
+                                          const void* q_g, const void* k_g, const void* v_g, void* out, float* lse,
+                                          int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                                          const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
+                                          void* stream) {
+    if (h && (!q_g || !k_g || !v_g || !lse)) {
+        h->last_error = "q_g, k_g, v_g and lse must be non-null";
+        return LF_ERR_INVALID_ARG;
+    }
+    return forward_impl(h, q, k, v, q_g, k_g, v_g, out, lse, B, H, L, d_h, w, dil_per_head, global_idx,
+                        n_global, key_pad_mask, stream);
+}
+
 lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void* v, const void* out,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int H, int L,
                            int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
                            const uint8_t* key_pad_mask, void* stream) {
-    return backward_impl(h, q, k, v, out, dout, lse, dq, dk, dv, B, H, L, d_h, w, dil_per_head, global_idx,
-                         n_global, key_pad_mask, stream);
+    return backward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, dout, lse, dq, dk, dv, nullptr, nullptr, nullptr,
+                         B, H, L, d_h, w, dil_per_head, global_idx, n_global, key_pad_mask, stream);
+}
+
+lf_status lf_attn_backward_global_proj(lf_attn_t h, const void* q, const void* k, const void* v, const void* q_g,
+                                       const void* k_g, const void* v_g, const void* out, const void* dout,
+                                       const float* lse, void* dq, void* dk, void* dv, void* dq_g, void* dk_g,
+                                       void* dv_g, int B, int H, int L, int d_h, int w,
+                                       const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
+                                       const uint8_t* key_pad_mask, void* stream) {
+    return backward_impl(h, q, k, v, q_g, k_g, v_g, out, dout, lse, dq, dk, dv, dq_g, dk_g, dv_g, B, H, L, d_h, w,
+                         dil_per_head, global_idx, n_global, key_pad_mask, stream);
 }
 
 lf_status lf_layer_forward(lf_attn_t h, const void* x, const lf_layer_weights* wts, void* out, int B, int L,

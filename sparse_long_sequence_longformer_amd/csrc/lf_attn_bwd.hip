@@ -541,13 +541,21 @@ void bwd_dq_kernel(const BwdParams p) {
     }
     if (qv < Lr) {
         const int vr = qv - r0;  // global rows: the merge
-        if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) store_row(dQ + (size_t)row * 64, h2, acc, 0.125f);
+        if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) {
+            store_row(dQ + (size_t)row * 64, h2, acc, 0.125f);
+            if (p.sep) store_row(reinterpret_cast<uint16_t*>(p.dqg) + off + (size_t)row * 64, h2, acc, 0.f);
+        }
     }
     if (ng == 0) return;
 
     // Global rows (C): each wave takes one 32-key sub-tile of the home keys
     // [r0, r0 + 128) (the last two band stages, still in the ring for the first 32
-    // global queries; copied again for the others).
+    // global queries; copied again for the others, and from k_g, v_g with separate
+    // projections, whose global queries are q_g).
+    const bool sep = p.sep != 0;
+    const uint16_t* QG = sep ? reinterpret_cast<const uint16_t*>(p.qg) + off : Q;
+    const uint16_t* KG = sep ? reinterpret_cast<const uint16_t*>(p.kg) + off : K;
+    const uint16_t* VG = sep ? reinterpret_cast<const uint16_t*>(p.vg) + off : V;
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
     const size_t part0 = ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * ngq;
     const int hs = wv >> 1, hsub = wv & 1;
@@ -557,13 +565,13 @@ void bwd_dq_kernel(const BwdParams p) {
         const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
         const int g = gq < ng ? p.g[gofs + gq] : -1;
         Op gop, gdo;
-        load_op(gop, g >= 0 ? Q + (size_t)g * 64 : nullptr, h2);
+        load_op(gop, g >= 0 ? QG + (size_t)g * 64 : nullptr, h2);
         load_op(gdo, g >= 0 ? dO + (size_t)g * 64 : nullptr, h2);
         const float gl = g >= 0 ? lse2[g] : kPosInf;
         const float gd = g >= 0 ? dsum[g] : 0.f;
         const char* hslot;
         uint32_t inv32;
-        if (gb == 0) {
+        if (gb == 0 && !sep) {
             const int u = tl.n_band - 2 + hs;
             hslot = ring + ((n_lst + u) & 1) * kStageB;
             inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
@@ -580,8 +588,8 @@ void bwd_dq_kernel(const BwdParams p) {
             for (int j = 0; j < 2; ++j) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
-                dma_tiles(ring + j * kStageB, K, V, [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
-                          wv, lane);
+                dma_tiles(ring + j * kStageB, KG, VG,
+                          [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             }
             wait_vmcnt<0>();
             __syncthreads();
@@ -625,8 +633,13 @@ void bwd_dq_kernel(const BwdParams p) {
 // the global queries and the band, one 64-query stage each; pairs that the window
 // already holds, global own keys (their pairs are folded by the global-key pass) and
 // queries past the end are masked.
+//
+// With separate projections of the global rows the global-query stages are left out
+// here (their pairs use q_g, k_g, v_g), and kGlobalProj instantiates the kernel that
+// computes them: own keys from k_g, v_g, the global queries from q_g as its only
+// stages, every key's dK_g, dV_g written directly.
 
-template <bool kCausal, bool kBias, bool kRandom>
+template <bool kCausal, bool kBias, bool kRandom, bool kGlobalProj = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dkv_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
@@ -644,12 +657,12 @@ void bwd_dkv_kernel(const BwdParams p) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
     const size_t off = (size_t)tl.bh * L * 64;
-    const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + off;
-    const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + off;
-    const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + off;
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(kGlobalProj ? p.qg : p.q) + off;
+    const uint16_t* K = reinterpret_cast<const uint16_t*>(kGlobalProj ? p.kg : p.k) + off;
+    const uint16_t* V = reinterpret_cast<const uint16_t*>(kGlobalProj ? p.vg : p.v) + off;
     const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dout) + off;
-    uint16_t* dK = reinterpret_cast<uint16_t*>(p.dk) + off;
-    uint16_t* dV = reinterpret_cast<uint16_t*>(p.dv) + off;
+    uint16_t* dK = reinterpret_cast<uint16_t*>(kGlobalProj ? p.dkg : p.dk) + off;
+    uint16_t* dV = reinterpret_cast<uint16_t*>(kGlobalProj ? p.dvg : p.dv) + off;
     const float* lse2 = p.lse2 + (size_t)tl.bh * L;
     const float* lse2b = p.lse2_band + (size_t)tl.bh * L;
     const float* dsum = p.dsum + (size_t)tl.bh * L;
@@ -665,7 +678,8 @@ void bwd_dkv_kernel(const BwdParams p) {
     load_op(kop, kvalid ? K + (size_t)krow * 64 : nullptr, h2);
     load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
 
-    const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
+    // global-query stages: none here with separate projections (their own launch)
+    const int n_gst = (!kGlobalProj && p.sep) ? 0 : (ng + kStageKeys - 1) / kStageKeys;
     // Random stages: the query blocks that drew key block r0/64, then r0/64 + 1.
     const int* inv_a = nullptr;
     const int* inv_b = nullptr;
@@ -680,7 +694,7 @@ void bwd_dkv_kernel(const BwdParams p) {
     }
     auto rnd_qblock = [&](int j) { return j < na_r ? inv_a[j] : inv_b[j - na_r]; };
     const int n_lst = n_gst + na_r + nb_r;
-    const int n_st = n_lst + tl.n_band;
+    const int n_st = n_lst + (kGlobalProj ? 0 : tl.n_band);
     auto issue = [&](int s) {
         char* slot = ring + (s & 1) * kStageB;
         if (s < n_gst) {
@@ -791,7 +805,7 @@ void bwd_dkv_kernel(const BwdParams p) {
     }
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
     if (qv < Lr) {
-        const int gi = own_gidx[qv - r0];
+        const int gi = kGlobalProj ? -1 : own_gidx[qv - r0];
         const float sk = kvalid ? 0.125f : 0.f, sv = kvalid ? 1.f : 0.f;
         if (gi < 0) {
             store_row(dK + (size_t)krow * 64, h2, dk, sk);
@@ -801,7 +815,7 @@ void bwd_dkv_kernel(const BwdParams p) {
             store_row_f32(p.ws_dvg + ((size_t)tl.bh * ngq + gi) * 64, h2, dv, sv);
         }
     }
-    if (ng == 0) return;
+    if (kGlobalProj || ng == 0) return;
 
     // Global keys (B): lane = global key, elements = the home queries of one 32-row
     // sub-tile per wave, minus the queries whose window holds the key (those pairs
@@ -933,7 +947,9 @@ __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const Bw
         sv += red[x][2][d];
     }
     const size_t o = (size_t)bh * L * 64 + (size_t)p.g[gofs + gi] * 64 + d;
-    reinterpret_cast<uint16_t*>(p.dq)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sq * 0.125f));
+    // with separate projections a global row's dQ goes to dq_g and its dq is zero
+    if (p.sep) reinterpret_cast<uint16_t*>(p.dqg)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sq * 0.125f));
+    reinterpret_cast<uint16_t*>(p.dq)[o] = __builtin_bit_cast(uint16_t, (__bf16)(p.sep ? 0.f : sq * 0.125f));
     reinterpret_cast<uint16_t*>(p.dk)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sk * 0.125f));
     reinterpret_cast<uint16_t*>(p.dv)[o] = __builtin_bit_cast(uint16_t, (__bf16)sv);
 }
@@ -977,6 +993,16 @@ hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
     }
 #undef LF_DKV_R
 #undef LF_DKV
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s) {
+    const int blocks = p.B * p.H * p.tiles_per_head;
+    if (blocks <= 0) return hipSuccess;
+    if (p.causal)
+        hipLaunchKernelGGL((bwd_dkv_kernel<true, false, false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((bwd_dkv_kernel<false, false, false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -81,6 +81,16 @@ struct BwdParams {
     // query blocks that drew key block kb, ascending, then -1.
     const int* rnd_inv;
     int rnd_inv_r;
+    // Separate projections of the global rows (sep != 0): q_g, k_g, v_g inputs and their
+    // gradients dq_g, dk_g, dv_g (same layout as q).  Global rows then attend with them
+    // only; the other rows, and every key they attend, use q, k, v.
+    int sep;
+    const void* qg;
+    const void* kg;
+    const void* vg;
+    void* dqg;
+    void* dkg;
+    void* dvg;
     // Row statistics written by the prep kernel, [B][H][L] each:
     float* lse2;       // lse in base-2 units of the pre-scaled scores; +inf for rows without keys
     float* lse2_band;  // same, and +inf for global rows (they are not window queries)
@@ -116,6 +126,7 @@ hipError_t launch_bias_gelu(const void* h, const void* bias, void* out, int F, l
 hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s);  // dk_g, dv_g (sep only)
 hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s);
 
 }  // namespace lf

@@ -25,6 +25,16 @@ def test_header_declares_binding_exports():
     assert declared_symbols() == sorted(binding.EXPORTS)
 
 
+def test_stage_names_match_header():
+    text = open(HEADER).read()
+    n = int(re.search(r"#define LF_N_STAGES (\d+)", text).group(1))
+    ids = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define LF_STAGE_(\w+) (\d+)", text)}
+    assert n == binding.N_STAGES == len(binding.STAGE_NAMES) == len(ids)
+    assert sorted(ids.values()) == list(range(n))
+    for name, i in ids.items():
+        assert binding.STAGE_NAMES[i] == name.lower(), (name, i)
+
+
 @needs_lib
 def test_library_exports_every_symbol():
     lib = ctypes.CDLL(binding.library_path())
@@ -329,3 +339,44 @@ def test_random_blocks_validation():
         assert lib.lf_attn_set_random_blocks(h, None, 0, 0, 0) == 0
     finally:
         lib.lf_attn_destroy(h)
+
+
+@needs_lib
+def test_global_proj_backward_host_validation():
+    lib = binding.load_library()
+    dil = (ctypes.c_int32 * 1)(1)
+    dil_p = ctypes.cast(dil, ctypes.POINTER(ctypes.c_int32))
+    # inputs q, k, v, q_g, k_g, v_g, out, dout at FAKE * 1..8; lse at FAKE * 9;
+    # gradients dq, dk, dv, dq_g, dk_g, dv_g at FAKE * 10..15
+    names = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
+
+    def call(h, lse=FAKE * 9, **kw):
+        grads = [kw.get(n, FAKE * (10 + i)) for i, n in enumerate(names)]
+        ins = [kw.get(n, FAKE * (1 + i)) for i, n in enumerate(("q", "k", "v", "qg", "kg", "vg", "out", "dout"))]
+        st = lib.lf_attn_backward_global_proj(h, *ins, lse, *grads, 1, 1, 64, 64, 4, dil_p, None, 0, None, None)
+        return st, lib.lf_attn_last_error(h).decode()
+
+    h32, h16 = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h32), 0) == 0 and lib.lf_attn_create(ctypes.byref(h16), 1) == 0
+    try:
+        st, msg = call(h32)
+        assert st == 2 and "bf16" in msg
+        for kw, frag in [(dict(qg=None), "must all be non-null"), (dict(dvg=None), "must all be non-null"),
+                         (dict(lse=None), "non-null"), (dict(kg=FAKE * 5 + 4), "aligned"),
+                         (dict(dqg=FAKE * 13 + 8), "aligned"), (dict(dkg=FAKE * 6 + 64), "overlap the inputs"),
+                         (dict(dvg=FAKE * 10 + 4096), "must not overlap"), (dict(dqg=FAKE * 9 - 32), "overlap")]:
+            st, msg = call(h16, **kw)
+            assert st == 1 and frag in msg, (kw, st, msg)
+        assert lib.lf_attn_backward_global_proj(None, *([FAKE] * 15), 1, 1, 64, 64, 4, dil_p, None, 0, None,
+                                                None) == 1
+        # the forward that returns the statistics: lse must be given and clear of q_g
+        st = lib.lf_attn_forward_global_proj_lse(h16, FAKE, FAKE * 2, FAKE * 3, FAKE * 5, FAKE * 6, FAKE * 7,
+                                                 FAKE * 4, None, 1, 1, 64, 64, 4, dil_p, None, 0, None, None)
+        assert st == 1 and "non-null" in lib.lf_attn_last_error(h16).decode()
+        st = lib.lf_attn_forward_global_proj_lse(h16, FAKE, FAKE * 2, FAKE * 3, FAKE * 5, FAKE * 6, FAKE * 7,
+                                                 FAKE * 4, FAKE * 6 + 256, 1, 1, 64, 64, 4, dil_p, None, 0, None,
+                                                 None)
+        assert st == 1 and "lse must not overlap q_g" in lib.lf_attn_last_error(h16).decode()
+    finally:
+        lib.lf_attn_destroy(h32)
+        lib.lf_attn_destroy(h16)
