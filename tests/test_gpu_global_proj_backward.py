@@ -24,12 +24,10 @@ import torch
 
 from oracle import longformer_oracle as orc
 from sparse_long_sequence_longformer_amd.workloads import make_bias, make_custom, make_random_blocks
-from tests.gpu_common import log, to_dev
+from tests.gpu_common import compare_grad, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
-GRAD_MAX_REL = 2e-2
-GRAD_MEAN_REL = 1e-2
 NAMES = ("dq", "dk", "dv", "dq_g", "dk_g", "dv_g")
 
 
@@ -52,22 +50,6 @@ def _inputs(B, H, L, seed):
     qg, kg, vg = make_custom(B, H, L, dtype="bf16", seed=seed + 1000)
     do = torch.from_numpy(np.random.default_rng(seed + 5000).standard_normal((B, H, L, 64), dtype=np.float32))
     return q, k, v, qg, kg, vg, do.to(torch.bfloat16)
-
-
-def _compare_grad(got, ref, what):
-    live_rows = int(np.count_nonzero(np.abs(ref).max(axis=-1)))
-    g = got.to(torch.float64).numpy()
-    assert np.all(np.isfinite(g)), f"{what}: non-finite"
-    err = np.abs(g - ref)
-    scale_max = float(np.abs(ref).max()) if ref.size else 0.0
-    scale_mean = float(np.abs(ref).mean()) if ref.size else 0.0
-    mx, mean = float(err.max()), float(err.mean())
-    log(f"  {what}: max-abs {mx:.3e} (scale {scale_max:.3e}) mean-abs {mean:.3e} (scale {scale_mean:.3e})")
-    tol_max, tol_mean = GRAD_MAX_REL * scale_max + 1e-6, GRAD_MEAN_REL * scale_mean + 1e-7
-    if live_rows < 16:  # few rows: the absolute bar where it is the looser one
-        tol_max, tol_mean = max(tol_max, 2e-2), max(tol_mean, 2e-3)
-    assert mx <= tol_max, f"{what}: max-abs {mx} > {tol_max}"
-    assert mean <= tol_mean, f"{what}: mean-abs {mean} > {tol_mean}"
 
 
 def _global_rows(G, B, L):
@@ -120,7 +102,7 @@ def _check(name, inputs, w, dil, G, pad, causal=False, bias=None, rand=None):
     refs = orc.attention_backward_global_proj(q, k, v, qg, kg, vg, do, w, dil, G, pad, causal=causal, bias=bias,
                                               rand=rand)
     for got, ref, n in zip(grads, refs, NAMES):
-        _compare_grad(got, ref, f"{name} {n}")
+        compare_grad(got, ref, f"{name} {n}")
     # entries that are zero by definition are exactly zero
     gm = _global_rows(G, B, L)[:, None, :, None]
     assert torch.count_nonzero(grads[0] * torch.from_numpy(gm)) == 0, "dq of a global row"

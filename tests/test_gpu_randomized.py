@@ -1,0 +1,143 @@
+"""Seeded random configurations of every pattern option at once, against the fp64
+oracle: forward (fp32 and bf16), the row log-sum-exp, and the backward (bf16), with
+and without separate global projections.
+
+Each case draws B, H, L (1 .. 700, so one to six row tiles and ragged tails), w,
+per-head dilations, a global set (empty, one, a few or many; duplicates allowed;
+shared or one row per sequence), key padding (none, suffix lengths or scattered),
+the one-sided window, a relative position bias table and random key blocks, each
+independently, from a fixed seed.  Tolerances: the forward's (fp32 max-abs 1e-4;
+bf16 max-abs 2e-2, mean-abs 2e-3), the log-sum-exp max-abs 1e-4 (fp32) / 2e-2
+(bf16) with -inf on exactly the rows without keys, and ``compare_grad`` for the
+gradients.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import longformer_oracle as orc
+from sparse_long_sequence_longformer_amd.workloads import make_bias, make_custom, make_random_blocks
+from tests.gpu_common import compare, compare_grad, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 60
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_long_sequence_longformer_amd import binding
+
+    binding.load_library()
+    yield
+
+
+def _case(seed):
+    """One configuration drawn from ``seed`` (host-side choices only)."""
+    rng = np.random.default_rng(1_000 + seed)
+    c = {"seed": seed}
+    c["dtype"] = "f32" if rng.random() < 0.3 else "bf16"
+    c["B"] = int(rng.integers(1, 4))
+    c["H"] = int(rng.integers(1, 4))
+    L = int(rng.choice([1, 2, 63, 64, 65, 127, 128, 129] + [int(x) for x in rng.integers(130, 701, 4)]))
+    c["L"] = L
+    c["w"] = int(rng.choice([0, 1, int(rng.integers(2, 64)), int(rng.integers(64, 301))]))
+    c["rand"] = rng.random() < 0.3
+    c["dil"] = [1] * c["H"] if c["rand"] else [int(x) for x in rng.choice([1, 1, 2, 3, 5], c["H"])]
+    c["causal"] = bool(rng.random() < 0.3)
+    c["bias"] = bool(rng.random() < 0.3)
+    c["sep"] = bool(rng.random() < 0.3)
+    kind = rng.choice(["none", "one", "few", "many"])
+    n = {"none": 0, "one": 1, "few": int(rng.integers(2, 6)), "many": int(rng.integers(6, 40))}[kind]
+    per_seq = bool(rng.random() < 0.3) and n > 0
+    if per_seq:
+        rows = []
+        for _ in range(c["B"]):
+            m = int(rng.integers(0, n + 1))
+            rows.append(list(rng.integers(0, L, m)) + [-1] * (n - m))  # duplicates allowed
+        c["G"] = np.array(rows, dtype=np.int64)
+    else:
+        c["G"] = [int(x) for x in rng.integers(0, L, n)]
+    pk = rng.choice(["none", "suffix", "scattered"])
+    if pk == "suffix":
+        lens = rng.integers(0, L + 1, c["B"])
+        c["pad"] = (np.arange(L)[None, :] >= lens[:, None]).astype(np.uint8)
+    elif pk == "scattered":
+        c["pad"] = (rng.random((c["B"], L)) < rng.choice([0.1, 0.5, 0.95])).astype(np.uint8)
+    else:
+        c["pad"] = None
+    return c
+
+
+def _describe(c):
+    g = c["G"].tolist() if hasattr(c["G"], "tolist") else c["G"]
+    return (f"case {c['seed']}: {c['dtype']} B={c['B']} H={c['H']} L={c['L']} w={c['w']} dil={c['dil']} "
+            f"G={g} pad={'none' if c['pad'] is None else int(c['pad'].sum())} causal={c['causal']} "
+            f"bias={c['bias']} rand={c['rand']} sep={c['sep']}")
+
+
+def _lse_check(got, ref, dtype, what):
+    g = got.numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref)), f"{what}: -inf rows differ"
+    fin = np.isfinite(ref)
+    if fin.any():
+        e = float(np.abs(g[fin] - ref[fin]).max())
+        log(f"  {what}: max-abs {e:.3e}")
+        assert e <= (1e-4 if dtype == "f32" else 2e-2), what
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_randomized_configuration(seed):
+    from sparse_long_sequence_longformer_amd import binding
+
+    c = _case(seed)
+    log(_describe(c))
+    B, H, L, w, dil, G, pad, dt = c["B"], c["H"], c["L"], c["w"], c["dil"], c["G"], c["pad"], c["dtype"]
+    q, k, v = make_custom(B, H, L, dtype=dt, seed=seed)
+    qg, kg, vg = make_custom(B, H, L, dtype=dt, seed=seed + 500) if c["sep"] else (q, k, v)
+    bias = make_bias(H, w, seed=seed, scale=1.5) if c["bias"] else None
+    rand = make_random_blocks(H, L, int(min(3, (L + 63) // 64)), seed=seed) if c["rand"] else None
+    opts = dict(causal=c["causal"], bias=bias, rand=rand)
+    padd = None if pad is None else torch.from_numpy(np.ascontiguousarray(pad)).cuda()
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    dev = to_dev(q, k, v, qg, kg, vg)
+    gpu_opts = dict(causal=c["causal"], bias=bd, rand=rand)
+
+    # forward with its row statistics
+    if c["sep"]:
+        out, lse = binding.forward_global_proj_lse(*dev, w, dil, G, padd, **gpu_opts)
+        ref = orc.attention_global_proj(q, k, v, qg, kg, vg, w, dil, G, pad, **opts)
+        plain_lse = orc.attention_lse(q, k, w, dil, G, pad, **opts)
+        glob_lse = orc.attention_lse(qg, kg, w, dil, G, pad, **opts)
+        gm = np.zeros((B, 1, L), dtype=bool)
+        for b in range(B):
+            gm[b, 0, orc.globals_of(G, b)] = True
+        ref_lse = np.where(gm, glob_lse, plain_lse)
+    else:
+        out, lse = binding.forward_lse(*dev[:3], w, dil, G, padd, **gpu_opts)
+        ref = orc.attention(q, k, v, w, dil, G, pad, **opts)
+        ref_lse = orc.attention_lse(q, k, w, dil, G, pad, **opts)
+    torch.cuda.synchronize()
+    compare(out.cpu(), ref, dt, "out")
+    _lse_check(lse.cpu(), ref_lse, dt, "lse")
+    if dt != "bf16":
+        return
+
+    # backward
+    do = torch.from_numpy(np.random.default_rng(seed + 77).standard_normal((B, H, L, 64), dtype=np.float32))
+    do = do.to(torch.bfloat16)
+    dod = do.cuda()
+    if c["sep"]:
+        grads = binding.backward_global_proj(*dev, out, dod, lse, w, dil, G, padd, **gpu_opts)
+        refs = orc.attention_backward_global_proj(q, k, v, qg, kg, vg, do, w, dil, G, pad, **opts)
+        names = ("dq", "dk", "dv", "dq_g", "dk_g", "dv_g")
+    else:
+        grads = binding.backward(*dev[:3], out, dod, lse, w, dil, G, padd, **gpu_opts)
+        refs = orc.attention_backward(q, k, v, do, w, dil, G, pad, **opts)
+        names = ("dq", "dk", "dv")
+    torch.cuda.synchronize()
+    for got, r, n in zip(grads, refs, names):
+        compare_grad(got.cpu(), r, n)
