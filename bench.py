@@ -372,7 +372,7 @@ def main():
 
 def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
     """One layer on the workload's shape (hidden = 64 * H) with seeded synthetic
-    weights: the four GEMMs (rocBLAS), the attention and the pointwise passes."""
+    weights: the four GEMMs (hipBLASLt), the attention and the pointwise passes."""
     import ctypes
 
     import numpy as np

@@ -62,8 +62,8 @@ def build(verbose: bool = False) -> str:
         cmd = [cc, *compile_flags(), *lang, "-c", path, "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    # rocBLAS serves the layer's plain GEMMs
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, f"-L{ROCM_LIB}", "-lrocblas",
+    # hipBLASLt serves the layer's plain GEMMs
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, f"-L{ROCM_LIB}", "-lhipblaslt",
           f"-Wl,-rpath,{ROCM_LIB}"], verbose)
     os.replace(tmp, LIB)
     for obj in objs:

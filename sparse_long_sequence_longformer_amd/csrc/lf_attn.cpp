@@ -3,7 +3,7 @@
 // enqueued; on error nothing is launched and `out` is untouched.
 
 #include <hip/hip_runtime_api.h>
-#include <rocblas/rocblas.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -26,6 +26,16 @@ struct TimedLaunch {
 };
 
 }  // namespace
+
+// One GEMM shape's hipBLASLt descriptors and the algorithm chosen for it.
+struct GemmPlan {
+    int M = 0, N = 0, K = 0;
+    bool f32_out = false;
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+    hipblasLtMatmulAlgo_t algo{};
+    size_t ws = 0;
+};
 
 struct lf_attn_s {
     lf_dtype dtype;
@@ -54,8 +64,13 @@ struct lf_attn_s {
     char* ws_layer = nullptr;  // intermediates of the layer
     size_t ws_layer_bytes = 0;
     int ws_layer_device = -1;
-    rocblas_handle blas = nullptr;
-    int blas_device = -1;
+    // hipBLASLt for the layer's GEMMs: one handle and plan cache per device in use.
+    hipblasLtHandle_t lt = nullptr;
+    int lt_device = -1;
+    std::vector<GemmPlan> gemm_plans;
+    char* ws_gemm = nullptr;  // hipBLASLt workspace
+    size_t ws_gemm_bytes = 0;
+    int ws_gemm_device = -1;
     std::string last_error;
     bool timing = false;
     std::vector<TimedLaunch> pending;  // recorded, not yet read
@@ -65,6 +80,8 @@ struct lf_attn_s {
 };
 
 namespace {
+
+lf_status release_gemm(lf_attn_t h);
 
 lf_status fail(lf_attn_t h, lf_status s, const char* fmt, ...) {
     if (h) {
@@ -145,7 +162,8 @@ lf_status lf_attn_destroy(lf_attn_t h) {
     if (h->ws_bwd && hipFree(h->ws_bwd) != hipSuccess) st = LF_ERR_HIP;
     if (h->ws_layer && hipFree(h->ws_layer) != hipSuccess) st = LF_ERR_HIP;
     if (h->rnd_dev && hipFree(h->rnd_dev) != hipSuccess) st = LF_ERR_HIP;
-    if (h->blas && rocblas_destroy_handle(h->blas) != rocblas_status_success) st = LF_ERR_HIP;
+    if (h->ws_gemm && hipFree(h->ws_gemm) != hipSuccess) st = LF_ERR_HIP;
+    if (release_gemm(h) != LF_OK) st = LF_ERR_HIP;
     release_events(h);
     for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
     delete h;
@@ -380,6 +398,22 @@ lf_status make_plan(lf_attn_t h, Plan& pl, int B, int H, int L, int d_h, int w, 
 }
 
 // Grow one of the handle's device workspaces to at least `need` bytes.
+// Drop the hipBLASLt plans and handle (made on another device, or at destruction).
+lf_status release_gemm(lf_attn_t h) {
+    bool ok = true;
+    for (GemmPlan& g : h->gemm_plans) {
+        ok &= hipblasLtMatrixLayoutDestroy(g.c) == HIPBLAS_STATUS_SUCCESS;
+        ok &= hipblasLtMatrixLayoutDestroy(g.b) == HIPBLAS_STATUS_SUCCESS;
+        ok &= hipblasLtMatrixLayoutDestroy(g.a) == HIPBLAS_STATUS_SUCCESS;
+        ok &= hipblasLtMatmulDescDestroy(g.desc) == HIPBLAS_STATUS_SUCCESS;
+    }
+    h->gemm_plans.clear();
+    if (h->lt) ok &= hipblasLtDestroy(h->lt) == HIPBLAS_STATUS_SUCCESS;
+    h->lt = nullptr;
+    h->lt_device = -1;
+    return ok ? LF_OK : LF_ERR_HIP;
+}
+
 lf_status reserve(lf_attn_t h, char** buf, size_t* have, int* dev, size_t need) {
     if (need <= *have && *dev == h->device) return LF_OK;
     if (*buf) (void)hipFree(*buf);
@@ -627,16 +661,68 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     return st;
 }
 
+constexpr size_t kGemmWorkspace = size_t(32) << 20;
+
+// The descriptors and algorithm of Y[M][N] = X[M][K] W^T (see gemm_xwt), made once
+// per shape and output type on the handle's current device.
+lf_status gemm_plan(lf_attn_t h, int M, int N, int K, bool f32_out, const GemmPlan** out) {
+    for (const GemmPlan& g : h->gemm_plans)
+        if (g.M == M && g.N == N && g.K == K && g.f32_out == f32_out) {
+            *out = &g;
+            return LF_OK;
+        }
+    GemmPlan g;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.f32_out = f32_out;
+    const hipDataType yt = f32_out ? HIP_R_32F : HIP_R_16BF;
+    const hipblasOperation_t opt = HIPBLAS_OP_T, opn = HIPBLAS_OP_N;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    const uint64_t ws = kGemmWorkspace;
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int n_res = 0;
+    bool ok = hipblasLtMatmulDescCreate(&g.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opt, sizeof(opt)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opn, sizeof(opn)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&g.a, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&g.b, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&g.c, yt, N, M, N) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws,
+                                                    sizeof(ws)) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulAlgoGetHeuristic(h->lt, g.desc, g.a, g.b, g.c, g.c, pref, 1, res, &n_res) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              n_res >= 1 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= kGemmWorkspace;
+    if (pref) (void)hipblasLtMatmulPreferenceDestroy(pref);
+    if (!ok) {
+        if (g.c) (void)hipblasLtMatrixLayoutDestroy(g.c);
+        if (g.b) (void)hipblasLtMatrixLayoutDestroy(g.b);
+        if (g.a) (void)hipblasLtMatrixLayoutDestroy(g.a);
+        if (g.desc) (void)hipblasLtMatmulDescDestroy(g.desc);
+        return fail(h, LF_ERR_HIP, "hipBLASLt has no algorithm for the %d x %d x %d GEMM", M, N, K);
+    }
+    g.algo = res[0].algo;
+    g.ws = res[0].workspaceSize;
+    h->gemm_plans.push_back(g);
+    *out = &h->gemm_plans.back();
+    return LF_OK;
+}
+
 // Y[M][N] (row-major; bf16, or fp32 when f32_out) = X[M][K] (bf16) W^T with W[N][K]
-// (bf16), fp32 accumulation: in rocBLAS's column-major terms Y^T = W X^T.
-lf_status gemm_xwt(lf_attn_t h, const void* X, const void* Wt, void* Y, int M, int N, int K, bool f32_out) {
+// (bf16), fp32 accumulation: in hipBLASLt's column-major terms Y^T = W X^T, i.e.
+// op(A) = A^T with A = W^T stored K x N, and B = X^T stored K x M.
+lf_status gemm_xwt(lf_attn_t h, const void* X, const void* Wt, void* Y, int M, int N, int K, bool f32_out,
+                   hipStream_t s) {
+    const GemmPlan* g = nullptr;
+    lf_status st = gemm_plan(h, M, N, K, f32_out, &g);
+    if (st != LF_OK) return st;
     const float one = 1.f, zero = 0.f;
-    const rocblas_datatype yt = f32_out ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
-    const rocblas_status rs = rocblas_gemm_ex(
-        h->blas, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, Wt, rocblas_datatype_bf16_r, K,
-        X, rocblas_datatype_bf16_r, K, &zero, Y, yt, N, Y, yt, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
-        0, 0);
-    if (rs != rocblas_status_success) return fail(h, LF_ERR_HIP, "rocblas_gemm_ex failed: %s", rocblas_status_to_string(rs));
+    const hipblasStatus_t rs = hipblasLtMatmul(h->lt, g->desc, &one, Wt, g->a, X, g->b, &zero, Y, g->c, Y, g->c,
+                                               &g->algo, h->ws_gemm, g->ws, s);
+    if (rs != HIPBLAS_STATUS_SUCCESS) return fail(h, LF_ERR_HIP, "hipblasLtMatmul failed (status %d)", (int)rs);
     return LF_OK;
 }
 
@@ -668,19 +754,18 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     if (st != LF_OK) return st;
 
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
-    if (h->blas && h->blas_device != h->device) {
-        (void)rocblas_destroy_handle(h->blas);
-        h->blas = nullptr;
-    }
-    if (!h->blas) {
-        if (rocblas_create_handle(&h->blas) != rocblas_status_success) {
-            h->blas = nullptr;
-            return fail(h, LF_ERR_HIP, "rocblas_create_handle failed");
+    if (h->lt && h->lt_device != h->device && release_gemm(h) != LF_OK)
+        return fail(h, LF_ERR_HIP, "releasing the GEMM handle of another device failed");
+    if (!h->lt) {
+        if (hipblasLtCreate(&h->lt) != HIPBLAS_STATUS_SUCCESS) {
+            h->lt = nullptr;
+            return fail(h, LF_ERR_HIP, "hipblasLtCreate failed");
         }
-        h->blas_device = h->device;
+        h->lt_device = h->device;
     }
+    st = reserve(h, &h->ws_gemm, &h->ws_gemm_bytes, &h->ws_gemm_device, kGemmWorkspace);
+    if (st != LF_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (rocblas_set_stream(h->blas, s) != rocblas_status_success) return fail(h, LF_ERR_HIP, "rocblas_set_stream failed");
 
     // Workspace: one GEMM output [R][3E] or [R][F] in bf16, or [R][E] in fp32, then bf16
     // q, k, v, attention output, merged heads (reused for x1), and the feed-forward
@@ -701,7 +786,7 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     const int M = static_cast<int>(R);
 
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E, false) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E, false, s) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
@@ -713,7 +798,7 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] { return lf::launch_merge_heads(ba, bm, B, L, E, s); });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, bm, wt->w_o, gout, M, E, E, true) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, bm, wt->w_o, gout, M, E, E, true, s) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] {
@@ -722,14 +807,14 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, bm, wt->w_1, gout, M, F, E, false) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, bm, wt->w_1, gout, M, F, E, false, s) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
                       [&] { return lf::launch_bias_gelu(gout, wt->b_1, bh, F, (long long)R, s); });
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, bh, wt->w_2, gout, M, E, F, true) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, bh, wt->w_2, gout, M, E, F, true, s) == LF_OK ? hipSuccess : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
     return launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] {
