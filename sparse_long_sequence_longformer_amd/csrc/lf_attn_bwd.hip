@@ -78,7 +78,7 @@ __device__ __forceinline__ void scale_op(Op& o) {
 
 // 4 bytes per lane from global memory into LDS at lds_base + 4 * lane (see dma16).
 __device__ __forceinline__ void dma4(const void* src, char* lds_base) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory", "m0");
 }
 

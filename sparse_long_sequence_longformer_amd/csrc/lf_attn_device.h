@@ -25,6 +25,12 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 #define LF_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
+// LDS byte address of a generic pointer into LDS.  A flat address in the shared
+// aperture is the aperture base (its high 32 bits) plus the LDS address, so the low
+// 32 bits are the LDS address itself; the address-space cast would also test for a
+// null pointer (a compare and a select per copy on the scalar unit).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 // exp(x / sqrt(64)) = exp2(x * log2(e) / 8)
 constexpr float kScaleLog2 = 1.4426950408889634f * 0.125f;
 constexpr float kNegInf = -__builtin_inff();
@@ -74,7 +80,7 @@ __device__ __forceinline__ uint64_t ballot64(bool x) { return __ballot(x); }
 // the barrier that publishes a stage.  The instruction has no register results.
 // M0 carries the LDS base; no other code in these kernels keeps a value in M0.
 __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
 }
 
@@ -90,7 +96,7 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 // into LDS at lds_base + 16 * lane: the scalar-base form needs no per-lane 64-bit
 // address arithmetic.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, char* lds_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LF_LDS(char, lds_base));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
     const uint64_t b64 = (uint64_t)(uintptr_t)base;
     const uint64_t sb = uniform64(b64);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0)
