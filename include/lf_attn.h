@@ -227,7 +227,7 @@ lf_status lf_attn_backward_global_proj(lf_attn_t h, const void* q, const void* k
 
 /*
  * Pattern variant of every later call on `h` (forward, forward_lse,
- * forward_global_proj, backward).
+ * forward_global_proj, forward_global_proj_lse, backward, backward_global_proj).
  *
  * LF_WINDOW_SYMMETRIC (default): the pattern above.
  * LF_WINDOW_CAUSAL: the same key sets intersected with {j <= i}: window keys
@@ -241,7 +241,8 @@ lf_status lf_attn_set_window_mode(lf_attn_t h, int mode);
 
 /*
  * Relative position bias on the window scores of every later call on `h`
- * (forward, forward_lse, forward_global_proj, backward, layer).
+ * (forward, forward_lse, forward_global_proj, forward_global_proj_lse, backward,
+ * backward_global_proj, layer).
  *
  * Page "基于自注意力机制的长文本建模算法：Longformer详解" §5 adds a relative
  * position bias to strengthen the local attention.  Read as a learned scalar per
@@ -266,7 +267,8 @@ lf_status lf_attn_set_position_bias(lf_attn_t h, const float* table, int n_heads
 
 /*
  * Random key blocks (BigBird-style random attention) for every later call on `h`
- * (forward, forward_lse, forward_global_proj, backward, layer).
+ * (forward, forward_lse, forward_global_proj, forward_global_proj_lse, backward,
+ * backward_global_proj, layer).
  *
  * The survey page (commentary on "Efficient Transformers: A Survey", §3.1-§3.2)
  * describes BigBird as window + global + random attention and recommends fixed
