@@ -68,7 +68,26 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     for obj in objs:
         os.remove(obj)
+    build_abi_check(verbose)
     return LIB
+
+
+ABI_CHECK = os.path.join(PKG, "lf_abi_check")
+
+
+def build_abi_check(verbose: bool = False) -> str:
+    """A plain C program that calls the library through include/lf_attn.h only (built
+    with the host C compiler against the HIP runtime; finds liblfattn.so beside it)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no C compiler for the C-ABI check program")
+    rocm_inc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
+    tmp = ABI_CHECK + ".tmp"
+    _run([cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", f"-I{rocm_inc}", f"-I{INCLUDE}",
+          os.path.join(CSRC, "lf_abi_check.c"), "-o", tmp, f"-L{PKG}", "-llfattn", f"-L{ROCM_LIB}", "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM_LIB}"], verbose)
+    os.replace(tmp, ABI_CHECK)
+    return ABI_CHECK
 
 
 def _run(cmd, verbose):

@@ -380,3 +380,16 @@ def test_global_proj_backward_host_validation():
     finally:
         lib.lf_attn_destroy(h32)
         lib.lf_attn_destroy(h16)
+
+
+def test_c_program_builds_and_links():
+    """The plain C caller exists after the build and starts without a GPU (usage error)."""
+    from sparse_long_sequence_longformer_amd import build as pkg_build
+
+    if not os.path.exists(pkg_build.ABI_CHECK):
+        pytest.skip("lf_abi_check not built (run __graft_entry__.build())")
+    import subprocess
+
+    res = subprocess.run([pkg_build.ABI_CHECK], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                         timeout=60)
+    assert res.returncode == 2 and "usage" in res.stdout
