@@ -613,7 +613,8 @@ void band_kernel(const Params p) {
     // The scalar-base copies use 32-bit per-lane offsets of up to 64 rows dil apart.
     const bool direct_ok = (uint64_t)dil * kStageKeys * T::kRowBytes < (1ull << 31);
     // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
-    auto issue = [&](int s, int part) {
+    int ks_next = 0;  // first key of the band stage copied last (see the stage loop)
+    auto issue = [&](int s, int part) -> uint64_t {
         char* slot = ring + (s % T::kNS) * T::kStageBytes;
         if (kRandom && is_glob(s) && s - n_pre >= n_gst) {
             const int j = s - n_pre - n_gst;
@@ -624,13 +625,16 @@ void band_kernel(const Params p) {
             } else {
                 T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane, part);
             }
+            return 0ull;
         } else if (is_glob(s)) {
             const int* src = glob_src + kStageKeys * (s - n_pre);
             T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane, part);
+            return 0ull;
         } else {
             const int bs = band_u(s);
             const uint64_t inv = uniform64(band_invalid(bs));
             const int ks = stage_key(bs);
+            ks_next = ks;
             if (inv == 0ull && part == kAllParts && direct_ok) {
                 const size_t row0 = (size_t)(r + ks * dil) * 64;
                 T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
@@ -638,13 +642,15 @@ void band_kernel(const Params p) {
                 T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
                              wv, lane, part);
             }
+            return inv;
         }
     };
 
     // Without padding a band stage needs nothing from LDS: its copy goes out before
     // the set-up below, together with the Q operand loads.
     const bool early = !pad && n_st > 0 && !is_glob(0);
-    if (early) issue(0, kAllParts);
+    uint64_t inv_next = 0ull;  // invalid-key bits of the next band stage, from its copy
+    if (early) inv_next = issue(0, kAllParts);
 
     // Global slots: source row (or -1 if unused/padded) and in-window position.
     for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
@@ -718,10 +724,15 @@ void band_kernel(const Params p) {
     // compiler's own waits inside the loop have nothing left to wait for (an
     // in-loop vmcnt wait would also drain the stage copies in flight).
     for (int s = early ? 1 : 0; s < T::kNS - 1; ++s)
-        if (s < n_st) issue(s, kAllParts);
+        if (s < n_st) {
+            const uint64_t x = issue(s, kAllParts);
+            if (s == 0) inv_next = x;
+        }
     wait_vmcnt<0>();
     T::scale_q(qop);
     for (int t = 0; t < n_st; ++t) {
+        const uint64_t inv_cur = inv_next;  // stage t's bits (two-slot ring: issued last)
+        const int ks_cur = ks_next;
         wait_stage<T>(min(T::kNS - 2, n_st - 1 - t));
         barrier_nofence();
         const int sn = t + T::kNS - 1;
@@ -731,7 +742,7 @@ void band_kernel(const Params p) {
                 fill_band_masks(bn / kMaskWindow);
                 __syncthreads();
             }
-            issue(sn, kAllParts);
+            inv_next = issue(sn, kAllParts);
         }
         if (t == 0 && ng > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
@@ -745,9 +756,12 @@ void band_kernel(const Params p) {
         const bool gstage = is_glob(t) && !rstage;
         const int gidx = t - n_pre;        // global stage index when gstage
         const int j = t - n_pre - n_gst;   // random stage index when rstage
-        const int ks = rstage ? kRandomBlock * rnd_block(j) : (gstage ? 0 : stage_key(band_u(t)));
-        const uint64_t inv =
-            uniform64(rstage ? rnd_inv[j] : (gstage ? glob_mask[gidx] : band_invalid(band_u(t))));
+        // A band stage's first key and invalid-key bits were computed when its copy was
+        // issued (with a two-slot ring, in the previous iteration): reused, not rebuilt.
+        const int ks_band = T::kNS == 2 ? ks_cur : stage_key(band_u(t));
+        const uint64_t inv_band = T::kNS == 2 ? inv_cur : band_invalid(band_u(t));
+        const int ks = rstage ? kRandomBlock * rnd_block(j) : (gstage ? 0 : ks_band);
+        const uint64_t inv = uniform64(rstage ? rnd_inv[j] : (gstage ? glob_mask[gidx] : inv_band));
         const bool wave_on = !rstage || (wv >> 1) == (j < na_r ? 0 : 1);
         if (rows_live && wave_on && inv != ~0ull) {
             // Both sub-tiles in straight-line code: the second one's operand reads and
