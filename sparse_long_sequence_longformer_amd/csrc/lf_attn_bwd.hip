@@ -412,7 +412,10 @@ void bwd_dq_kernel(const BwdParams p) {
         if (hi < 64) m |= hi <= 0 ? ~0ull : (~0ull << hi);
         return m;
     };
-    auto issue = [&](int s) {
+    // A band stage's first key and invalid-key bits, computed when its copy is issued
+    // (one iteration before it is computed) and reused there.
+    int ks_next = 0;
+    auto issue = [&](int s) -> uint64_t {
         char* slot = ring + (s & 1) * kStageB;
         if (s < n_gst) {
             const int* src = glob_src + kStageKeys * s;
@@ -425,8 +428,11 @@ void bwd_dq_kernel(const BwdParams p) {
             const int u = s - n_lst;
             const uint64_t inv = uniform64(band_invalid(u));
             const int ks = tl.stage_row(u);
+            ks_next = ks;
             dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
+            return inv;
         }
+        return 0ull;
     };
     // Invalid-key bits (outside [kb0, kend) or padded) of band stages
     // [64*W, 64*W + 64): wave wv builds words wv, wv + 4, ... (all loads first).
@@ -484,7 +490,8 @@ void bwd_dq_kernel(const BwdParams p) {
     const int gcnt = causal ? count_le(glob_abs, ng, row) : 0;
     Lanes lo;
     lane_setup(lo, lane);
-    if (n_st > 0) issue(0);
+    uint64_t inv_next = 0ull;
+    if (n_st > 0) inv_next = issue(0);
     wait_vmcnt<0>();
     scale_op(qop);
     // The score product is seeded with -lse2 (its exponentials are the weights); D is
@@ -493,6 +500,8 @@ void bwd_dq_kernel(const BwdParams p) {
     const f32x16 seed_s = splat(-my_l2);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     for (int t = 0; t < n_st; ++t) {
+        const uint64_t inv_cur = inv_next;
+        const int ks_cur = ks_next;
         wait_vmcnt<0>();
         barrier_nofence();
         if (t + 1 < n_st) {
@@ -501,13 +510,13 @@ void bwd_dq_kernel(const BwdParams p) {
                 fill_band_masks(bn / kBwdMaskWindow);
                 __syncthreads();
             }
-            issue(t + 1);
+            inv_next = issue(t + 1);
         }
         const bool gstage = t < n_gst;
         const bool rstage = kRandom && !gstage && t < n_lst;
         const int j = t - n_gst;  // random stage index when rstage
-        const int ks = gstage ? 0 : (rstage ? kRandomBlock * rnd_block(j) : tl.stage_row(t - n_lst));
-        const uint64_t inv = uniform64(gstage ? glob_mask[t] : (rstage ? rnd_inv[j] : band_invalid(t - n_lst)));
+        const int ks = gstage ? 0 : (rstage ? kRandomBlock * rnd_block(j) : ks_cur);
+        const uint64_t inv = uniform64(gstage ? glob_mask[t] : (rstage ? rnd_inv[j] : inv_cur));
         const char* slot = ring + (t & 1) * kStageB;
         if (!rows_live || inv == ~0ull) continue;
         if (rstage && (wv >> 1) != (j < na_r ? 0 : 1)) continue;  // another query block's draw
@@ -695,6 +704,7 @@ void bwd_dkv_kernel(const BwdParams p) {
     auto rnd_qblock = [&](int j) { return j < na_r ? inv_a[j] : inv_b[j - na_r]; };
     const int n_lst = n_gst + na_r + nb_r;
     const int n_st = n_lst + (kGlobalProj ? 0 : tl.n_band);
+    int ks_next = 0;  // first query of the band stage copied last, reused when it is computed
     auto issue = [&](int s) {
         char* slot = ring + (s & 1) * kStageB;
         if (s < n_gst) {
@@ -711,6 +721,7 @@ void bwd_dkv_kernel(const BwdParams p) {
             if (wv == 0) dma_floats(slot, lse2b, dsum, row_of, lane);
         } else {
             const int ks = tl.stage_row(s - n_lst);
+            ks_next = ks;
             auto row_of = [&](int kk) {
                 const int x = ks + kk;
                 return (x >= tl.kb0 && x < tl.kend) ? r + x * dil : -1;
@@ -746,13 +757,14 @@ void bwd_dkv_kernel(const BwdParams p) {
     // global-key pass instead.
     const bool own_global = kRandom && qv < Lr && own_gidx[qv - r0] >= 0;
     for (int t = 0; t < n_st; ++t) {
+        const int ks_cur = ks_next;
         wait_vmcnt<0>();
         barrier_nofence();
         if (t + 1 < n_st) issue(t + 1);
         const bool gstage = t < n_gst;
         const bool rstage = kRandom && !gstage && t < n_lst;
         const int j = t - n_gst;  // random stage index when rstage
-        const int ks = gstage ? 0 : (rstage ? kRandomBlock * rnd_qblock(j) : tl.stage_row(t - n_lst));
+        const int ks = gstage ? 0 : (rstage ? kRandomBlock * rnd_qblock(j) : ks_cur);
         const char* slot = ring + (t & 1) * kStageB;
         if (!rows_live) continue;
         if (rstage && (wv >> 1) != (j < na_r ? 0 : 1)) continue;  // a draw of the other key block
