@@ -811,6 +811,161 @@ def pin_global_proj_backward_reduces():
     assert np.all(parts[0][G] == 0) and np.all(np.delete(parts[3], G, axis=0) == 0)
 
 
+# ------------------------------------ full-problem wrappers (per-(b, h) indexing)
+#
+# attention_sampled, attention_lse, attention_backward and
+# attention_backward_global_proj carry the per-slice indexing themselves: pad[b],
+# dil[h], the global set of sequence b, bias[h], rand[h].  Every sequence and every
+# head below differs in each of these, and B = H, so a swapped b and h gives wrong
+# numbers (not an index error).
+
+WRAP_B, WRAP_H, WRAP_L, WRAP_D, WRAP_W, WRAP_BS = 3, 3, 40, 8, 3, 8
+WRAP_DIL = [1, 2, 3]
+
+
+def _wrap_case(seed):
+    """Inputs of the wrapper pins: per-sequence padding and global sets, per-head
+    dilation, bias table and random draws (blocks of 8 keys)."""
+    B, H, L, d, w = WRAP_B, WRAP_H, WRAP_L, WRAP_D, WRAP_W
+    arrs = [_rand((B, H, L, d), seed + t) for t in range(7)]
+    pad = np.zeros((B, L), dtype=bool)
+    pad[0, 33:] = True           # suffix
+    pad[1, [3, 17, 29]] = True   # scattered; sequence 2 unpadded
+    sets = np.array([[0, 21, -1], [5, 5, 38], [-1, -1, -1]])
+    bias = _rand((H, 2 * w + 1), seed + 20)
+    rand = np.stack([_draws(L, WRAP_BS, 2, seed + 30 + h) for h in range(H)])
+    return arrs, pad, sets, bias, rand
+
+
+def _wrap_keys(b, h, i, pad, sets, rand, causal):
+    G = [int(g) for g in sets[b] if g >= 0]
+    return brute.key_set(i, WRAP_L, WRAP_W, WRAP_DIL[h], G, pad[b].tolist(), causal, rand[h], WRAP_BS)
+
+
+def _wrap_bias(b, h, i, j, sets, bias):
+    """Bias of pair (i, j) listed from the definition: a window pair j = i + m*dil of a
+    non-global row gets beta_h[m + w]."""
+    dil, w = WRAP_DIL[h], WRAP_W
+    if i in set(int(g) for g in sets[b] if g >= 0):
+        return 0.0
+    if (j - i) % dil == 0 and abs(j - i) <= w * dil:
+        return float(bias[h][(j - i) // dil + w])
+    return 0.0
+
+
+def _wrap_scores(q, k, b, h, i, keys, sets, bias):
+    d = q.shape[-1]
+    return [math.fsum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) / math.sqrt(d)
+            + _wrap_bias(b, h, i, j, sets, bias) for j in keys]
+
+
+def pin_wrapper_sampled():
+    """attention_sampled at every (b, h, i) equals a brute-force row (listed key set,
+    listed bias, math.fsum), in both window modes."""
+    (q, k, v, *_), pad, sets, bias, rand = _wrap_case(1500)
+    samples = [(b, h, i) for b in range(WRAP_B) for h in range(WRAP_H) for i in range(WRAP_L)]
+    for causal in (False, True):
+        got = orc.attention_sampled(q, k, v, WRAP_W, WRAP_DIL, sets, pad, samples, causal=causal, bias=bias,
+                                    rand=rand, rand_block=WRAP_BS)
+        for n, (b, h, i) in enumerate(samples):
+            keys = _wrap_keys(b, h, i, pad, sets, rand, causal)
+            if not keys:
+                assert np.all(got[n] == 0), (b, h, i)
+                continue
+            sc = _wrap_scores(q, k, b, h, i, keys, sets, bias)
+            top = max(sc)
+            e = [math.exp(x - top) for x in sc]
+            tot = math.fsum(e)
+            ref = [math.fsum(e[t] * v[b, h, j, c] for t, j in enumerate(keys)) / tot for c in range(WRAP_D)]
+            assert np.abs(got[n] - np.array(ref)).max() < 1e-12, (causal, b, h, i)
+
+
+def pin_wrapper_lse():
+    """attention_lse of the full problem equals log(fsum(exp)) over each row's listed
+    key set (with the listed bias), -inf for rows without keys."""
+    (q, k, *_), pad, sets, bias, rand = _wrap_case(1600)
+    for causal in (False, True):
+        got = orc.attention_lse(q, k, WRAP_W, WRAP_DIL, sets, pad, causal=causal, bias=bias, rand=rand,
+                                rand_block=WRAP_BS)
+        for b in range(WRAP_B):
+            for h in range(WRAP_H):
+                for i in range(WRAP_L):
+                    keys = _wrap_keys(b, h, i, pad, sets, rand, causal)
+                    if not keys:
+                        assert got[b, h, i] == -np.inf, (b, h, i)
+                        continue
+                    sc = _wrap_scores(q, k, b, h, i, keys, sets, bias)
+                    top = max(sc)
+                    ref = top + math.log(math.fsum(math.exp(x - top) for x in sc))
+                    assert abs(got[b, h, i] - ref) < 1e-12, (causal, b, h, i)
+
+
+def _wrap_dense(tq, tk, tv, b, h, pad, sets, bias, rand, causal, rows=None):
+    """Dense masked attention of slice (b, h) in torch float64: listed key sets and
+    bias entries; rows without keys give zeros.  rows: restrict the queries."""
+    L = WRAP_L
+    m = torch.zeros(L, L, dtype=torch.bool)
+    extra = torch.zeros(L, L, dtype=torch.float64)
+    for i in range(L):
+        for j in _wrap_keys(b, h, i, pad, sets, rand, causal):
+            m[i, j] = True
+            extra[i, j] = _wrap_bias(b, h, i, j, sets, bias)
+    s = (tq @ tk.T) / math.sqrt(tq.shape[1]) + extra
+    s = s.masked_fill(~m, float("-inf"))
+    p = torch.softmax(s, dim=1)
+    p = torch.where(m.any(dim=1, keepdim=True), p, torch.zeros_like(p))
+    return p @ tv
+
+
+def pin_wrapper_backward():
+    """attention_backward of the full problem equals torch autograd, slice by slice, of
+    the dense masked attention built from the listed key sets and bias entries."""
+    (q, k, v, do, *_), pad, sets, bias, rand = _wrap_case(1700)
+    for causal in (False, True):
+        got = orc.attention_backward(q, k, v, do, WRAP_W, WRAP_DIL, sets, pad, causal=causal, bias=bias, rand=rand,
+                                     rand_block=WRAP_BS)
+        for b in range(WRAP_B):
+            for h in range(WRAP_H):
+                ts = [torch.tensor(x[b, h], requires_grad=True) for x in (q, k, v)]
+                out = _wrap_dense(*ts, b, h, pad, sets, bias, rand, causal)
+                (out * torch.from_numpy(do[b, h])).sum().backward()
+                for name, a, t in zip(("dq", "dk", "dv"), got, ts):
+                    err = np.abs(a[b, h] - t.grad.numpy()).max()
+                    assert err < 1e-12, (name, causal, b, h, err)
+
+
+def pin_wrapper_backward_global_proj():
+    """attention_backward_global_proj of the full problem equals torch autograd, slice by
+    slice: other rows attend their listed key sets (with the listed bias) with q, k, v;
+    global rows attend every unpadded key (up to themselves when one-sided) with q_g,
+    k_g, v_g."""
+    (q, k, v, qg, kg, vg, do), pad, sets, bias, rand = _wrap_case(1800)
+    L = WRAP_L
+    for causal in (False, True):
+        got = orc.attention_backward_global_proj(q, k, v, qg, kg, vg, do, WRAP_W, WRAP_DIL, sets, pad,
+                                                 causal=causal, bias=bias, rand=rand, rand_block=WRAP_BS)
+        for b in range(WRAP_B):
+            Gs = sorted(set(int(g) for g in sets[b] if g >= 0))
+            for h in range(WRAP_H):
+                ts = [torch.tensor(x[b, h], requires_grad=True) for x in (q, k, v, qg, kg, vg)]
+                base = _wrap_dense(ts[0], ts[1], ts[2], b, h, pad, sets, bias, rand, causal)
+                gm = torch.zeros(L, L, dtype=torch.bool)
+                for i in range(L):
+                    for j in range(L):
+                        gm[i, j] = not pad[b, j] and (not causal or j <= i)
+                s = ((ts[3] @ ts[4].T) / math.sqrt(WRAP_D)).masked_fill(~gm, float("-inf"))
+                p = torch.softmax(s, dim=1)
+                p = torch.where(gm.any(dim=1, keepdim=True), p, torch.zeros_like(p))
+                glob = p @ ts[5]
+                rows = torch.zeros(L, 1, dtype=torch.float64)
+                rows[Gs] = 1.0
+                out = base * (1 - rows) + glob * rows
+                (out * torch.from_numpy(do[b, h])).sum().backward()
+                for name, a, t in zip(("dq", "dk", "dv", "dq_g", "dk_g", "dv_g"), got, ts):
+                    err = np.abs(a[b, h] - t.grad.numpy()).max()
+                    assert err < 1e-12, (name, causal, b, h, err)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -847,6 +1002,10 @@ ALL_PINS = [
     pin_random_backward_autograd,
     pin_global_proj_backward_autograd,
     pin_global_proj_backward_reduces,
+    pin_wrapper_sampled,
+    pin_wrapper_lse,
+    pin_wrapper_backward,
+    pin_wrapper_backward_global_proj,
     pin_layer_torch_encoder,
     pin_layer_norm_rows,
 ]

@@ -242,6 +242,107 @@ def _bias_on_global_rows(L, w, dil, G, rows, beta):  # global rows biased too
 
 _orig_bias = orc.window_bias
 
+# b and h swapped in the per-slice indexing of the full-problem wrappers (one field
+# at a time): the padding row, the dilation, the global set, the bias table or the
+# random draws of the wrong slice.
+def _slice_ix(which, b, h):
+    """(pad row, dilation, global set, bias, rand) indices of slice (b, h)."""
+    ix = {"pad": b, "dil": h, "glob": b, "bias": h, "rand": h}
+    swap = {"pad": h, "dil": b, "glob": h, "bias": b, "rand": b}
+    ix[which] = swap[which]
+    return ix
+
+
+def _pad_of(key_pad_mask):
+    return None if key_pad_mask is None else np.asarray(orc._as_f64(key_pad_mask) != 0)
+
+
+def _sampled_swap(which):
+    def f(q, k, v, w, dil_per_head, global_idx, key_pad_mask, samples, causal=False, bias=None, rand=None,
+          rand_block=64):
+        dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+        pad = _pad_of(key_pad_mask)
+        res = []
+        for b, h, i in samples:
+            x = _slice_ix(which, b, h)
+            o = orc.attention_bh(q[b, h], k[b, h], v[b, h], w, dil[x["dil"]], orc.globals_of(global_idx, x["glob"]),
+                                 None if pad is None else pad[x["pad"]], rows=[i], causal=causal,
+                                 bias=None if bias is None else bias[x["bias"]],
+                                 rand=None if rand is None else rand[x["rand"]], rand_block=rand_block)
+            res.append(o[0])
+        return np.stack(res)
+    return f
+
+
+def _lse_swap(which):
+    def f(q, k, w, dil_per_head, global_idx=None, key_pad_mask=None, causal=False, bias=None, rand=None,
+          rand_block=64):
+        q, k = orc._as_f64(q), orc._as_f64(k)
+        B, H, L, _ = q.shape
+        dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+        pad = _pad_of(key_pad_mask)
+        out = np.zeros((B, H, L))
+        for b in range(B):
+            for h in range(H):
+                x = _slice_ix(which, b, h)
+                out[b, h] = orc.attention_lse_bh(q[b, h], k[b, h], w, dil[x["dil"]],
+                                                 orc.globals_of(global_idx, x["glob"]),
+                                                 None if pad is None else pad[x["pad"]], causal=causal,
+                                                 bias=None if bias is None else bias[x["bias"]],
+                                                 rand=None if rand is None else rand[x["rand"]], rand_block=rand_block)
+        return out
+    return f
+
+
+def _bwd_swap(which):
+    def f(q, k, v, dout, w, dil_per_head, global_idx=None, key_pad_mask=None, causal=False, bias=None, rand=None,
+          rand_block=64):
+        q, k, v, do = (orc._as_f64(t) for t in (q, k, v, dout))
+        B, H, L, d = q.shape
+        dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+        pad = _pad_of(key_pad_mask)
+        res = [np.zeros((B, H, L, d)) for _ in range(3)]
+        for b in range(B):
+            for h in range(H):
+                x = _slice_ix(which, b, h)
+                parts = orc.attention_backward_bh(q[b, h], k[b, h], v[b, h], do[b, h], w, dil[x["dil"]],
+                                                  orc.globals_of(global_idx, x["glob"]),
+                                                  None if pad is None else pad[x["pad"]], causal=causal,
+                                                  bias=None if bias is None else bias[x["bias"]],
+                                                  rand=None if rand is None else rand[x["rand"]],
+                                                  rand_block=rand_block)
+                for r, t in zip(res, parts):
+                    r[b, h] = t
+        return tuple(res)
+    return f
+
+
+def _gp_bwd_swap(which):
+    def f(q, k, v, q_g, k_g, v_g, dout, w, dil_per_head, global_idx=None, key_pad_mask=None, causal=False,
+          bias=None, rand=None, rand_block=64):
+        q = orc._as_f64(q)
+        B, H, L, d = q.shape
+        dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+        pad = _pad_of(key_pad_mask)
+        res = [np.zeros((B, H, L, d)) for _ in range(6)]
+        for b in range(B):
+            for h in range(H):
+                x = _slice_ix(which, b, h)
+                parts = orc.attention_backward_global_proj_bh(
+                    q[b, h], k[b, h], v[b, h], q_g[b, h], k_g[b, h], v_g[b, h], dout[b, h], w, dil[x["dil"]],
+                    orc.globals_of(global_idx, x["glob"]), None if pad is None else pad[x["pad"]], causal=causal,
+                    bias=None if bias is None else bias[x["bias"]], rand=None if rand is None else rand[x["rand"]],
+                    rand_block=rand_block)
+                for r, t in zip(res, parts):
+                    r[b, h] = t
+        return tuple(res)
+    return f
+
+
+_WRAPPERS = {"attention_sampled": _sampled_swap, "attention_lse": _lse_swap,
+             "attention_backward": _bwd_swap, "attention_backward_global_proj": _gp_bwd_swap}
+
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -276,6 +377,9 @@ MUTANTS = {
     "bwd_dq_from_v": ("attention_backward_bh", _bwd_mutant("dq_from_v")),
     "bwd_dv_unmasked": ("attention_backward_bh", _bwd_mutant("dv_unmasked_softmax")),
 }
+for _fn, _make in _WRAPPERS.items():
+    for _field in ("pad", "dil", "glob", "bias", "rand"):
+        MUTANTS[f"{_fn}_swap_{_field}"] = (_fn, _make(_field))
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
