@@ -3,6 +3,9 @@ and compare with the fp64 oracle on the same seeded inputs."""
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -106,3 +109,35 @@ def sample_rows(B, H, L, G, pad, n_random, seed, extra_rows=()):
     for _ in range(n_random):
         rows.add((int(rng.integers(0, B)), int(rng.integers(0, H)), int(rng.integers(0, L))))
     return sorted(rows)
+
+
+def oracle_threads() -> int:
+    """Host threads for the oracle: the CPU share of this process, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_slices(fn, slices):
+    """Run fn(b, h) for each (b, h) in ``slices`` on a thread pool with BLAS limited to
+    one thread per call (numpy releases the interpreter lock in its array work).
+    Returns the results in order."""
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(oracle_threads()) as ex:
+        return list(ex.map(lambda bh: fn(*bh), slices))
+
+
+def oracle_full(q, k, v, w, dil, G, pad, slices=None, causal=False):
+    """orc.attention on the (b, h) slices given (default: all), computed slice by slice
+    on a thread pool: float64 [len(slices), L, d] (or [B, H, L, d] when all)."""
+    B, H = q.shape[:2]
+    padn = None if pad is None else np.asarray(pad) != 0
+    every = slices is None
+    slices = [(b, h) for b in range(B) for h in range(H)] if every else list(slices)
+
+    def one(b, h):  # widened to float64 slice by slice (inside the oracle)
+        return orc.attention_bh(q[b, h], k[b, h], v[b, h], w, dil[h], orc.globals_of(G, b),
+                                None if padn is None else padn[b], causal=causal)
+
+    res = oracle_slices(one, slices)
+    out = np.stack(res)
+    return out.reshape(B, H, *out.shape[1:]) if every else out

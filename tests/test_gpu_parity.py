@@ -1,8 +1,9 @@
 """HIP path (through the C-ABI) against the fp64 oracle on seeded inputs.
 
 Small and medium shapes are compared element by element over every output; the
-full-size workloads are compared on sampled rows the oracle computes one by one,
-plus properties that hold at any size.  Tolerances: fp32 max-abs 1e-4; bf16
+padded L=32768 workload on sampled rows of every head (the full-size workloads are
+compared over whole tensors in test_gpu_full_size.py), plus properties that hold at
+any size.  Tolerances: fp32 max-abs 1e-4; bf16
 max-abs 2e-2 and mean-abs 2e-3.
 """
 
@@ -138,7 +139,10 @@ def test_bf16_full_compare(case):
 
 # ------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("name", ["cls_4k", "qa_4k", "dilated_8k", "padded_32k"])
+# The other three full-size workloads are compared over every output element in
+# test_gpu_full_size.py; here the padded L=32768 one on sampled rows of every head
+# (whole slices of four heads are compared there).
+@pytest.mark.parametrize("name", ["padded_32k"])
 def test_workload_sampled(name):
     wl = workloads.WORKLOADS[name]
     log(f"case workload {name}: {wl.desc}")
