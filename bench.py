@@ -4,13 +4,16 @@
 
 One step = one forward pass (two kernels: the band kernel -- window band,
 global-column fold, global-row partials -- and the log-sum-exp merge of those
-partials) over one batch of seeded synthetic input already resident in HBM.  The metric is effective TFLOP/s: 4*d_h FLOP per
-attended (query, key) pair, pairs counted exactly (window + globals after
-de-duplication and padding), divided by the wall time of the K timed steps.
+partials) over one batch of seeded synthetic input already resident in HBM.  The
+metric is effective TFLOP/s: 4*d_h FLOP per attended (query, key) pair, pairs counted
+exactly (window + globals after de-duplication and padding), divided by the wall time
+of the K timed steps.  Before the W warm-up steps, steps run back to back for at least
+--clock-warmup seconds (the GPU clock ramps up under load).
 
-Prints one JSON line.  Also reported: the kernel's own rate against the bf16 MFMA
-peak (HIP events around each launch, on the launch stream), and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+Prints one JSON line.  Also reported: the band kernel's own rate against the bf16
+MFMA peak (each launch stamped with the kernel's start and end by HIP events on the
+launch stream), and the fp64 CPU oracle timed on a bounded sample of the same
+workload on the host's cores.
 
 Variants (not the default line): --global-proj (separate projections of the global
 rows; with --backward its backward), --backward (the backward pass alone and a
@@ -55,6 +58,8 @@ def parse():
     # L=4096 workload); the defaults warm up past that and time a comparable span.
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--clock-warmup", type=float, default=0.3, metavar="SECONDS",
+                    help="back-to-back steps for at least this long before the --warmup steps")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--global-proj", action="store_true",
                     help="global rows use their own q/k/v projections (lf_attn_forward_global_proj)")
@@ -98,43 +103,83 @@ def traffic_for(workload: str):
     return ent.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, q, k, v, G, pad, target_s, causal=False, bias=None, rand=None):
-    """The fp64 oracle on whole (b, h) slices of the workload, one after another,
-    until about target_s seconds of CPU work; BLAS limited to one thread."""
+    """The fp64 oracle on whole (b, h) slices of the workload, on a pool of host threads
+    (one per core of this process's CPU share, at most 16; BLAS limited to one thread
+    per call, numpy's array work runs outside the interpreter lock).  Slices are handed
+    out in order until about target_s seconds have passed; the slices finished count."""
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
+
     from threadpoolctl import threadpool_limits
 
     from oracle import longformer_oracle as orc
     from sparse_long_sequence_longformer_amd import pattern
 
-    pad_np = None if pad is None else pad
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    slices = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+
+    def one(b, h):
+        orc.attention_bh(q[b, h], k[b, h], v[b, h], wl.w, wl.dil[h], G, None if pad is None else pad[b],
+                         causal=causal, bias=None if bias is None else bias[h],
+                         rand=None if rand is None else rand[h])
+        pr = None if pad is None else pad[b:b + 1]
+        return pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr, causal=causal,
+                                   rand=None if rand is None else [rand[h]]).total
+
     pairs = 0
-    done = []
+    done = 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        for b in range(wl.B):
-            for h in range(wl.H):
-                orc.attention_bh(q[b, h], k[b, h], v[b, h], wl.w, wl.dil[h], G,
-                                 None if pad_np is None else pad_np[b], causal=causal,
-                                 bias=None if bias is None else bias[h], rand=None if rand is None else rand[h])
-                pr = None if pad_np is None else pad_np[b:b + 1]
-                pairs += pattern.count_pairs(wl.L, wl.w, [wl.dil[h]], G, pr, causal=causal,
-                                             rand=None if rand is None else [rand[h]]).total
-                done.append((b, h))
-                if time.perf_counter() - t0 >= target_s:
-                    break
-            if time.perf_counter() - t0 >= target_s:
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
+        nxt = 0
+        running = set()
+        while nxt < len(slices) or running:
+            while nxt < len(slices) and len(running) < threads and time.perf_counter() - t0 < target_s:
+                running.add(ex.submit(one, *slices[nxt]))
+                nxt += 1
+            if not running:
                 break
+            fin, running = wait(running, return_when=FIRST_COMPLETED)
+            for f in fin:
+                pairs += f.result()
+                done += 1
     dt = time.perf_counter() - t0
     return {
         "value": 256.0 * pairs / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(done)} of {wl.B * wl.H} (batch, head) slices of {wl.name}, full rows, "
-                  f"{dt:.1f} s; same effective-FLOP count as the GPU value",
+        "sample": f"{done} of {wl.B * wl.H} (batch, head) slices of {wl.name}, full rows, {dt:.1f} s wall on "
+                  f"{threads} threads; same effective-FLOP count as the GPU value",
+        "cpu_model": cpu_model(),
         "seconds": round(dt, 3),
         "pairs": pairs,
     }
+
+
+def clock_warmup(step, seconds, torch):
+    """Back-to-back steps until at least `seconds` have passed (the GPU clock ramps up
+    over about the first 0.1 s of load), ahead of the requested warm-up steps.
+    Returns (seconds spent, steps run)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(50):
+            step()
+        n += 50
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return round(time.perf_counter() - t0, 3), n
 
 
 def main():
@@ -230,6 +275,7 @@ def main():
         gp = (qgd, kgd, vgd) if args.global_proj else None
         return bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops, handle, gp)
 
+    clock = clock_warmup(step, args.clock_warmup, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -243,8 +289,9 @@ def main():
     ms_step = ms_total / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
 
-    # Per-kernel durations: HIP events recorded by the library around every launch,
-    # on the launch stream, over a second run of K steps.
+    # Per-kernel durations over a second run of K steps: every kernel is launched with
+    # a pair of HIP events that the launch itself stamps with the kernel's start and end
+    # (hipExtLaunchKernel, on the launch stream).
     handle.set_stage_timing(True)
     for _ in range(args.steps):
         step()
@@ -304,6 +351,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup_s": clock[0],
+        "clock_warmup_steps": clock[1],
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -332,6 +381,8 @@ def main():
             **roof,
             "traffic": traffic,
             "avg_launch_ms": round(k_avg_ms, 6),
+            "avg_launch_source": "HIP events stamped by hipExtLaunchKernel with the kernel's own start and end, "
+                                 "live over a second run of the timed steps",
             "flop_per_launch": flops,
             "alg_bytes_per_launch": alg_bytes,
             "arithmetic_intensity": round(flops / alg_bytes, 1),
@@ -403,6 +454,7 @@ def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
         if lib.lf_layer_forward(*args_c) != 0:
             raise RuntimeError(lib.lf_attn_last_error(handle.handle).decode())
 
+    clock = clock_warmup(step, args.clock_warmup, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -427,7 +479,8 @@ def bench_layer(args, wl, name, padd, G, dil, flops_attn, handle):
         "metric": "Longformer layer fwd effective TFLOP/s (GEMMs + window+global attention), L=4096 w=512",
         "value": round(total / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "clock_warmup_s": clock[0],
+        "clock_warmup_steps": clock[1], "ms_per_step": round(ms, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0, 0.05^2) weights)",
         "config": {"workload": name, "B": wl.B, "seq_len": wl.L, "hidden": E, "heads": wl.H, "ffn": F, "w": wl.w,
@@ -503,6 +556,7 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    clock = clock_warmup(bwd, args.clock_warmup, torch)
     for _ in range(args.warmup):
         bwd()
     torch.cuda.synchronize()
@@ -529,6 +583,8 @@ def bench_backward(args, wl, name, qd, kd, vd, padd, G, dil, pairs, flops_fwd, h
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup_s": clock[0],
+        "clock_warmup_steps": clock[1],
         "ms_per_step": round(ms_bwd, 6),
         "higher_is_better": True,
         "scaling": "weak",

@@ -377,8 +377,10 @@ const char* lf_attn_status_string(lf_status s);
 const char* lf_attn_last_error(lf_attn_t h);
 
 /*
- * Per-stage kernel timing with HIP events recorded on the launch stream around
- * each kernel.  enable != 0 starts recording (clearing earlier totals), 0 stops.
+ * Per-stage kernel timing with HIP events on the launch stream: each kernel of this
+ * library is launched with hipExtLaunchKernel and a pair of events that it stamps with
+ * the kernel's own start and end; the layer's library GEMMs are bracketed by two
+ * recorded events.  enable != 0 starts recording (clearing earlier totals), 0 stops.
  * Errors: LF_ERR_INVALID_ARG (h == NULL), LF_ERR_HIP.
  */
 lf_status lf_attn_set_stage_timing(lf_attn_t h, int enable);

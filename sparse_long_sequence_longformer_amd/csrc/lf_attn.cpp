@@ -79,6 +79,15 @@ struct lf_attn_s {
     int64_t stage_n[LF_N_STAGES] = {};
 };
 
+namespace lf {
+
+LaunchEvents& launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
+}  // namespace lf
+
 namespace {
 
 lf_status release_gemm(lf_attn_t h);
@@ -444,21 +453,42 @@ lf_status upload_random(lf_attn_t h) {
     return LF_OK;
 }
 
-// Enqueue one launch, between timing events when timing is on.
+// Enqueue one launch.  With timing on, a kernel of this library is launched with a
+// pair of events that hipExtLaunchKernel stamps with the kernel's own start and end;
+// a library call (the layer's GEMMs) is bracketed by two recorded events instead.
 template <class Launch>
 lf_status launch_stage(lf_attn_t h, int stage, hipStream_t s, Launch launch) {
     TimedLaunch tl{nullptr, nullptr, stage};
+    const bool bracket = stage == LF_STAGE_LAYER_GEMM;
+    lf::LaunchEvents& ev = lf::launch_events();
     if (h->timing) {
         tl.start = take_event(h);
         tl.stop = take_event(h);
         if (!tl.start || !tl.stop) return fail(h, LF_ERR_HIP, "hipEventCreate failed");
-        if (hipEventRecord(tl.start, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+        if (bracket) {
+            if (hipEventRecord(tl.start, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+        } else {
+            ev = lf::LaunchEvents{tl.start, tl.stop, false};
+        }
     }
     const hipError_t e = launch();
-    if (e != hipSuccess) return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    const bool stamped = ev.used;
+    ev = lf::LaunchEvents{};
+    if (e != hipSuccess) {
+        if (h->timing) {
+            h->event_pool.push_back(tl.start);
+            h->event_pool.push_back(tl.stop);
+        }
+        return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
     if (h->timing) {
-        if (hipEventRecord(tl.stop, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
-        h->pending.push_back(tl);
+        if (bracket && hipEventRecord(tl.stop, s) != hipSuccess) return fail(h, LF_ERR_HIP, "hipEventRecord failed");
+        if (bracket || stamped) {
+            h->pending.push_back(tl);
+        } else {  // nothing was launched (an empty grid)
+            h->event_pool.push_back(tl.start);
+            h->event_pool.push_back(tl.stop);
+        }
     }
     return LF_OK;
 }

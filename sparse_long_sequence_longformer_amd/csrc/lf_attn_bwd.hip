@@ -972,14 +972,14 @@ hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
     const long long blocks = (long long)p.B * p.H * ((p.L + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    launch_kernel(bwd_prep_kernel, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-#define LF_DQ(C, Bi, R) hipLaunchKernelGGL((bwd_dq_kernel<C, Bi, R>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_DQ(C, Bi, R) launch_kernel(bwd_dq_kernel<C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
 #define LF_DQ_R(C, Bi) \
     if (p.rnd) LF_DQ(C, Bi, true); else LF_DQ(C, Bi, false)
     if (p.causal) {
@@ -995,7 +995,7 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-#define LF_DKV(C, Bi, R) hipLaunchKernelGGL((bwd_dkv_kernel<C, Bi, R>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_DKV(C, Bi, R) launch_kernel(bwd_dkv_kernel<C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
 #define LF_DKV_R(C, Bi) \
     if (p.rnd) LF_DKV(C, Bi, true); else LF_DKV(C, Bi, false)
     if (p.causal) {
@@ -1012,16 +1012,16 @@ hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
     if (p.causal)
-        hipLaunchKernelGGL((bwd_dkv_kernel<true, false, false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+        launch_kernel(bwd_dkv_kernel<true, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
     else
-        hipLaunchKernelGGL((bwd_dkv_kernel<false, false, false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+        launch_kernel(bwd_dkv_kernel<false, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s) {
     if (p.n_g == 0) return hipSuccess;
     const int waves = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);
-    hipLaunchKernelGGL(bwd_merge_kernel, dim3(p.n_g, p.B * p.H), dim3(64 * waves), 0, s, p);
+    launch_kernel(bwd_merge_kernel, dim3(p.n_g, p.B * p.H), dim3(64 * waves), s, p);
     return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 // wrappers.  Internal to liblfattn.so.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -204,6 +205,20 @@ __device__ __forceinline__ int count_le(const int* pos, int n, int x) {
         else hi = mid;
     }
     return lo;
+}
+
+// Launch a kernel on stream s, with the timing events of the launch in progress if
+// there are any (see LaunchEvents).
+template <class K, class... A>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, A... args) {
+    LaunchEvents& ev = launch_events();
+    if (ev.start) {
+        ev.used = true;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace

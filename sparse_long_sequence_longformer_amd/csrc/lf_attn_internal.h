@@ -57,6 +57,17 @@ struct Params {
     int gcnt[LF_MAX_GLOBALS];
 };
 
+// Events of the kernel launch in progress, set by the host around one launch when
+// per-launch timing is on.  The launchers pass them to hipExtLaunchKernel, which
+// stamps them with the kernel's own start and end (no separate event packets
+// between kernels); `used` tells the host that a kernel was launched with them.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+    bool used = false;
+};
+LaunchEvents& launch_events();  // this thread's (defined in lf_attn.cpp)
+
 // Launchers (defined in lf_attn_kernels.hip).  Return the launch error.
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s);

@@ -990,7 +990,7 @@ hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
     const bool bias = p.bias != nullptr, rnd = p.rnd != nullptr;
-#define LF_BAND(T, C, Bi, R) hipLaunchKernelGGL((band_kernel<T, C, Bi, R>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define LF_BAND(T, C, Bi, R) launch_kernel(band_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
 #define LF_BAND_R(T, C, Bi) \
     if (rnd) LF_BAND(T, C, Bi, true); else LF_BAND(T, C, Bi, false)
 #define LF_BAND_BR(T, C) \
@@ -1011,9 +1011,9 @@ hipError_t launch_merge(const Params& p, int dtype, hipStream_t s) {
     const dim3 grid(p.n_g, p.B * p.H);
     const int waves = merge_waves(p.tiles_per_head, kMergeChunk, kMergeWaves);
     if (dtype == LF_BF16)
-        hipLaunchKernelGGL(merge_kernel<Bf16>, grid, dim3(64 * waves), 0, s, p);
+        launch_kernel(merge_kernel<Bf16>, grid, dim3(64 * waves), s, p);
     else
-        hipLaunchKernelGGL(merge_kernel<F32>, grid, dim3(64 * waves), 0, s, p);
+        launch_kernel(merge_kernel<F32>, grid, dim3(64 * waves), s, p);
     return hipGetLastError();
 }
 

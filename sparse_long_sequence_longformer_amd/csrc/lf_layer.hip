@@ -144,7 +144,7 @@ unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_blo
 hipError_t launch_qkv_split(const void* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
                             hipStream_t s) {
     const long long n8 = (long long)B * L * 3 * E / 8;
-    hipLaunchKernelGGL(qkv_split_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, static_cast<const uint16_t*>(qkv),
+    launch_kernel(qkv_split_kernel, dim3(blocks_for(n8, 256)), dim3(256), s, static_cast<const uint16_t*>(qkv),
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
                        static_cast<uint16_t*>(v), L, E, n8);
     return hipGetLastError();
@@ -152,14 +152,14 @@ hipError_t launch_qkv_split(const void* qkv, const void* bias, void* q, void* k,
 
 hipError_t launch_merge_heads(const void* a, void* out, int B, int L, int E, hipStream_t s) {
     const long long n8 = (long long)B * L * E / 8;
-    hipLaunchKernelGGL(merge_heads_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s,
+    launch_kernel(merge_heads_kernel, dim3(blocks_for(n8, 256)), dim3(256), s,
                        static_cast<const uint16_t*>(a), static_cast<uint16_t*>(out), L, E, n8);
     return hipGetLastError();
 }
 
 hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void* res, const void* gamma,
                                    const void* beta, float eps, void* out, int E, long long R, hipStream_t s) {
-    hipLaunchKernelGGL(bias_residual_ln_kernel, dim3(blocks_for(R, 4)), dim3(256), 0, s, y,
+    launch_kernel(bias_residual_ln_kernel, dim3(blocks_for(R, 4)), dim3(256), s, y,
                        static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(res),
                        static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta), eps,
                        static_cast<uint16_t*>(out), E, R);
@@ -168,7 +168,7 @@ hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void*
 
 hipError_t launch_bias_gelu(const void* h, const void* bias, void* out, int F, long long R, hipStream_t s) {
     const long long n8 = R * F / 8;
-    hipLaunchKernelGGL(bias_gelu_kernel, dim3(blocks_for(n8, 256)), dim3(256), 0, s, static_cast<const uint16_t*>(h),
+    launch_kernel(bias_gelu_kernel, dim3(blocks_for(n8, 256)), dim3(256), s, static_cast<const uint16_t*>(h),
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), F, n8);
     return hipGetLastError();
 }
