@@ -53,6 +53,7 @@ typedef enum lf_dtype {
 #define LF_MAX_BIAS_W 1024 /* widest window with a relative position bias */
 #define LF_RANDOM_BLOCK 64 /* keys per random block (and queries per query block) */
 #define LF_MAX_RANDOM_DRAWS 16 /* random key blocks per query block */
+#define LF_STATIC_SCRATCH_BYTES (16 << 20) /* device scratch of lf_attn_forward_static */
 
 /* Kernel launches timed by lf_attn_stage_times. */
 #define LF_N_STAGES 9
@@ -115,6 +116,32 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
                           int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
                           const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
                           void* stream);
+
+/*
+ * lf_attn_forward that allocates nothing, for callers that cannot allocate device
+ * memory during the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * lf_attn_forward.  The global-row partials go to a static device array of
+ * LF_STATIC_SCRATCH_BYTES (16 MiB) that each GPU the library runs on holds until the
+ * process ends, instead of the handle's workspace; the call makes no hipMalloc,
+ * hipFree or other allocating call (the array's device address is looked up once per
+ * device, on the first call there).
+ *
+ * Limits and errors, all checked before anything is enqueued:
+ *   LF_ERR_UNSUPPORTED if the partials need more than LF_STATIC_SCRATCH_BYTES
+ *   (B * H * row tiles per head * 32 * ceil(n_global / 32) * 264 bytes, where a head of
+ *   dilation d has d * ceil(ceil(L / d) / 128) row tiles; e.g. B = 2, H = 12, L = 4096,
+ *   up to 32 globals: 6.5 MB), or if random blocks are set on the handle but their
+ *   tables were not yet uploaded to this device by another entry point (this one
+ *   uploads nothing); otherwise the errors of lf_attn_forward.
+ * Per-launch timing (lf_attn_set_stage_timing) does not record these launches.
+ * Every call on one GPU shares that GPU's array, whichever handle it comes from:
+ * calls that overlap in time on one GPU (other streams, other threads) race.
+ */
+lf_status lf_attn_forward_static(lf_attn_t h, const void* q, const void* k, const void* v, void* out,
+                                 int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                                 const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
+                                 void* stream);
 
 /*
  * lf_attn_forward that also writes each row's log-sum-exp, for the backward.

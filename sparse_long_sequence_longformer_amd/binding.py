@@ -35,6 +35,7 @@ MAX_RANDOM_DRAWS = 16
 EXPORTS = (
     "lf_attn_create",
     "lf_attn_forward",
+    "lf_attn_forward_static",
     "lf_attn_forward_global_proj",
     "lf_attn_forward_global_proj_lse",
     "lf_attn_forward_lse",
@@ -86,6 +87,8 @@ def load_library():
                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
                                     vp, vp]
     lib.lf_attn_forward.restype = i32
+    lib.lf_attn_forward_static.argtypes = lib.lf_attn_forward.argtypes
+    lib.lf_attn_forward_static.restype = i32
     lib.lf_attn_forward_global_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                                 i32, vp, vp]
@@ -192,6 +195,12 @@ class LfAttn:
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
         st = self.lib.lf_attn_forward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w,
                                       dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def forward_static_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_attn_forward_static(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, B, H, L, d_h, w,
+                                             dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
     def forward_global_proj_raw(self, q_ptr, k_ptr, v_ptr, qg_ptr, kg_ptr, vg_ptr, out_ptr, B, H, L, d_h, w,
@@ -454,6 +463,22 @@ def forward(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None, 
     with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
                       global_idx, pad_ptr, stream)
+    return out
+
+
+def forward_static(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=None,
+                   handle: LfAttn | None = None, causal: bool = False):
+    """``forward`` through lf_attn_forward_static: the library allocates no device memory
+    in the call (its global-row partials go to a static device array of
+    LF_STATIC_SCRATCH_BYTES per GPU; calls that overlap in time on one GPU race).
+    Pass ``out`` to keep the call itself free of allocations."""
+    import torch
+
+    B, H, L, d_h, dil, global_idx, pad_ptr, out, h, stream = _marshal(
+        q, [("k", k), ("v", v)], w, dil, global_idx, key_pad_mask, out, handle, causal)
+    with torch.cuda.device(q.device):
+        h.forward_static_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d_h, int(w), dil,
+                             global_idx, pad_ptr, stream)
     return out
 
 

@@ -495,10 +495,12 @@ lf_status launch_stage(lf_attn_t h, int stage, hipStream_t s, Launch launch) {
 
 // Every forward entry point.  qg, kg, vg are all null (one projection for every
 // row) or all non-null (separate projections of the global rows); lse may be null.
+// no_alloc: the partials go to the static scratch array (no allocation, no upload,
+// no per-launch timing).
 lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
                        const void* vg, void* out, float* lse, int B, int H, int L, int d_h, int w,
                        const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
-                       const uint8_t* key_pad_mask, void* stream) {
+                       const uint8_t* key_pad_mask, void* stream, bool no_alloc = false) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->last_error.clear();
     if (!q || !k || !v || !out) return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be non-null");
@@ -555,8 +557,15 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
-    st = upload_random(h);
-    if (st != LF_OK) return st;
+    if (no_alloc) {
+        if (h->rnd_on && h->rnd_uploaded != h->device)
+            return fail(h, LF_ERR_UNSUPPORTED,
+                        "random blocks are set but their tables are not on this device yet (the allocation-free "
+                        "forward uploads nothing; call another entry point once on this device first)");
+    } else {
+        st = upload_random(h);
+        if (st != LF_OK) return st;
+    }
     if (h->rnd_on) {
         p.rnd = reinterpret_cast<const int*>(h->rnd_dev);
         p.rnd_nq = h->rnd_nq;
@@ -564,14 +573,35 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     }
     if (p.n_g > 0) {
         const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
-        st = reserve(h, &h->ws, &h->ws_bytes, &h->ws_device, n_part * (2 + 64) * sizeof(float));
-        if (st != LF_OK) return st;
-        p.ws_ml = reinterpret_cast<float*>(h->ws);
+        const size_t need = n_part * (2 + 64) * sizeof(float);
+        char* base = nullptr;
+        if (no_alloc) {
+            if (need > static_cast<size_t>(LF_STATIC_SCRATCH_BYTES))
+                return fail(h, LF_ERR_UNSUPPORTED,
+                            "the global-row partials need %zu bytes; the allocation-free forward has %d",
+                            need, LF_STATIC_SCRATCH_BYTES);
+            void* sp = nullptr;
+            const hipError_t e = lf::static_scratch(&sp);
+            if (e != hipSuccess)
+                return fail(h, LF_ERR_HIP, "address of the static scratch array: %s", hipGetErrorString(e));
+            base = static_cast<char*>(sp);
+        } else {
+            st = reserve(h, &h->ws, &h->ws_bytes, &h->ws_device, need);
+            if (st != LF_OK) return st;
+            base = h->ws;
+        }
+        p.ws_ml = reinterpret_cast<float*>(base);
         p.ws_acc = p.ws_ml + n_part * 2;
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = h->dtype;
+    if (no_alloc) {  // no events: their creation could allocate
+        hipError_t e = lf::launch_band(p, dt, s);
+        if (e == hipSuccess && p.n_g > 0) e = lf::launch_merge(p, dt, s);
+        if (e != hipSuccess) return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return LF_OK;
+    }
     st = launch_stage(h, LF_STAGE_BAND, s, [&] { return lf::launch_band(p, dt, s); });
     if (st != LF_OK || p.n_g == 0) return st;
     return launch_stage(h, LF_STAGE_MERGE, s, [&] { return lf::launch_merge(p, dt, s); });
@@ -862,6 +892,13 @@ lf_status lf_attn_forward(lf_attn_t h, const void* q, const void* k, const void*
                           int n_global, const uint8_t* key_pad_mask, void* stream) {
     return forward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, nullptr, B, H, L, d_h, w, dil_per_head,
                         global_idx, n_global, key_pad_mask, stream);
+}
+
+lf_status lf_attn_forward_static(lf_attn_t h, const void* q, const void* k, const void* v, void* out, int B,
+                                 int H, int L, int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx,
+                                 int n_global, const uint8_t* key_pad_mask, void* stream) {
+    return forward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, nullptr, B, H, L, d_h, w, dil_per_head,
+                        global_idx, n_global, key_pad_mask, stream, true);
 }
 
 lf_status lf_attn_forward_lse(lf_attn_t h, const void* q, const void* k, const void* v, void* out, float* lse,

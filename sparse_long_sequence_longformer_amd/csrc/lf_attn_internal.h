@@ -71,6 +71,9 @@ LaunchEvents& launch_events();  // this thread's (defined in lf_attn.cpp)
 // Launchers (defined in lf_attn_kernels.hip).  Return the launch error.
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s);
+// This device's address of the static scratch array of LF_STATIC_SCRATCH_BYTES bytes
+// (taken with hipGetSymbolAddress on the first call per device, then cached).
+hipError_t static_scratch(void** ptr);
 
 // Backward parameters (bf16 tensors, fp32 statistics and partials).
 struct BwdParams {

@@ -43,6 +43,8 @@
 // operand of the next product unchanged.  K rows are read in the order sigma(M) so
 // that accumulator element i of lane-half h2 holds key 16*(i/8) + 8*h2 + (i%8).
 
+#include <mutex>
+
 #include "lf_attn_device.h"
 
 namespace lf {
@@ -985,6 +987,32 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p)
 }
 
 }  // namespace
+
+// Device scratch of the allocation-free forward (lf_attn_forward_static): the global-row
+// partials of a call live in this array instead of a handle workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.
+static __device__ __align__(256) char scratch[LF_STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // The host-side name `scratch` is not a device address: take this device's
+        // address of the array once, with the device current, and use only that.
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
