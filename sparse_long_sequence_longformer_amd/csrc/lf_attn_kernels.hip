@@ -44,6 +44,7 @@
 // that accumulator element i of lane-half h2 holds key 16*(i/8) + 8*h2 + (i%8).
 
 #include <mutex>
+#include <type_traits>
 
 #include "lf_attn_device.h"
 
@@ -84,12 +85,12 @@ struct Bf16 {
     // load and the scaling by log2(e)/sqrt(d_h) (rounded back to bf16) are separate, so
     // the loads can stay in flight while other set-up work is issued.
     // row == nullptr reads the static zero row (no branch around the loads).
-    __device__ static void load_q(QOp& q, const Elem* row, int h2) {
+    __device__ __forceinline__ static void load_q(QOp& q, const Elem* row, int h2) {
         if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
         for (int kb = 0; kb < 4; ++kb)
             q.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
     }
-    __device__ static void scale_q(QOp& q) {
+    __device__ __forceinline__ static void scale_q(QOp& q) {
         for (int kb = 0; kb < 4; ++kb) {
             const f32x8 f = __builtin_convertvector(q.v[kb], f32x8);
             q.v[kb] = __builtin_convertvector(f * kScaleLog2, bf16x8);
@@ -100,7 +101,7 @@ struct Bf16 {
     // and of V (8 rows each), block 2*wv + part for part = 0, 1 (kAllParts: both).
     // row_of(kk) is the source row of stage key kk or -1.
     template <class RowOf>
-    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
+    __device__ __forceinline__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
                                      int part = kAllParts) {
         const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 2; ++u) {
@@ -117,7 +118,7 @@ struct Bf16 {
 
     // 32 rows copied to dst (row-major, 128 B each): wave wv copies rows 8*wv .. +7.
     template <class RowPtr>
-    __device__ static void dma_rows(char* dst, RowPtr row_ptr, int wv, int lane) {
+    __device__ __forceinline__ static void dma_rows(char* dst, RowPtr row_ptr, int wv, int lane) {
         const int row = 8 * wv + (lane >> 3);
         dma16(row_ptr(row) + 8 * (lane & 7), dst + wv * 1024);
     }
@@ -128,14 +129,14 @@ struct Bf16 {
     // 8*dil rows); its rows differ from block 2*wv's in bit 3 only, so swz_v is the
     // same and swz_k differs by 4 (chunk bit 2: byte offset bit 6).
     struct DmaLane { uint32_t k, v; int dil; };
-    __device__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
+    __device__ __forceinline__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
         const int row = 16 * wv + (lane >> 3), cl = lane & 7;
         const uint32_t r0b = (uint32_t)row * (uint32_t)dil * kRowBytes;
         dl.k = r0b + 16u * (uint32_t)(cl ^ swz_k(row));
         dl.v = r0b + 16u * (uint32_t)(cl ^ swz_v(row));
         dl.dil = dil;
     }
-    __device__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
+    __device__ __forceinline__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
         for (int u = 0; u < 2; ++u) {
             const int blk = 2 * wv + u;
             const size_t adv = (size_t)u * 8 * dl.dil * 64;
@@ -151,7 +152,7 @@ struct Bf16 {
         int v[2];  // V^T operand: row 8*h2 + i/4 (+ 4*t + 16*kb + 32*sub), per column block db
         bf16x8 sel;  // A operand of the weight-sum product (see tile_sum)
     };
-    __device__ static void lane_offsets(Lane& lo, int lane) {
+    __device__ __forceinline__ static void lane_offsets(Lane& lo, int lane) {
         const int row = sigma(lane & 31), h2 = lane >> 5;
         {
             const int m = lane & 15, g = lane >> 4;
@@ -169,7 +170,7 @@ struct Bf16 {
 
     // seed + S^T (32 keys x 32 queries) of sub-tile `sub` (keys 32*sub .. 32*sub+31 of
     // the stage).
-    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
+    __device__ __forceinline__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
         const char* base = slot + sub * 32 * kRowBytes;
         f32x16 acc = seed;
         for (int kb = 0; kb < 4; ++kb) {
@@ -180,7 +181,7 @@ struct Bf16 {
     }
 
     // Round the weights to bf16: the P^T operand.
-    __device__ static void to_p(const float* p, PFrag& pf) {
+    __device__ __forceinline__ static void to_p(const float* p, PFrag& pf) {
         for (int kb = 0; kb < 2; ++kb) {
             f32x8 t;
             for (int j = 0; j < 8; ++j) t[j] = p[8 * kb + j];
@@ -196,7 +197,7 @@ struct Bf16 {
     // column, rows 4 and 12 those of query n + 16; so element 0 of lane l is the sum
     // of query l%32, the lane's own query.  The bf16 vector units share the matrix
     // cores' datapath, which makes this cheaper than a dot-product chain.
-    __device__ static float tile_sum(const PFrag& pf, const float*, const Lane& lo) {
+    __device__ __forceinline__ static float tile_sum(const PFrag& pf, const float*, const Lane& lo) {
         f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.sel, pf.v[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.sel, pf.v[1], acc, 0, 0, 0);
         return acc[0];
@@ -209,7 +210,7 @@ struct Bf16 {
     // Rows base = 32*sub + 16*kb + 8*h2 + 4*t are multiples of 4, so the V swizzle
     // (row modulo 4) is the same for all of them.
     struct VOp { bf16x8 v[2][2]; };  // [db][kb]
-    __device__ static void load_v(VOp& vo, const char* slot, int sub, const Lane& lo) {
+    __device__ __forceinline__ static void load_v(VOp& vo, const char* slot, int sub, const Lane& lo) {
         const char* base = slot + sub * 32 * kRowBytes;
         for (int db = 0; db < 2; ++db)
             for (int kb = 0; kb < 2; ++kb) {
@@ -219,17 +220,17 @@ struct Bf16 {
                 vo.v[db][kb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
             }
     }
-    __device__ static void pv(const VOp& vo, const PFrag& pf, f32x16* o) {
+    __device__ __forceinline__ static void pv(const VOp& vo, const PFrag& pf, f32x16* o) {
         for (int kb = 0; kb < 2; ++kb)
             for (int db = 0; db < 2; ++db)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.v[db][kb], pf.v[kb], o[db], 0, 0, 0);
     }
 
-    __device__ static uint32_t pack_bf16(float a, float b) {
+    __device__ __forceinline__ static uint32_t pack_bf16(float a, float b) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
 
-    __device__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+    __device__ __forceinline__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
         for (int db = 0; db < 2; ++db)
             for (int q = 0; q < 4; ++q) {
                 const float a = o[db][4 * q] * scale, b = o[db][4 * q + 1] * scale;
@@ -239,7 +240,7 @@ struct Bf16 {
             }
     }
 
-    __device__ static Elem from_float(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+    __device__ __forceinline__ static Elem from_float(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 };
 
 struct F32 {
@@ -255,21 +256,21 @@ struct F32 {
 
     // B operand of S^T = K Q^T for the 32x32x2 product: step t, lane-half h2 -> d = 32*h2 + t;
     // scale_q multiplies by log2(e)/sqrt(d_h).
-    __device__ static void load_q(QOp& q, const Elem* row, int h2) {
+    __device__ __forceinline__ static void load_q(QOp& q, const Elem* row, int h2) {
         if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
         for (int t4 = 0; t4 < 8; ++t4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4);
             for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
         }
     }
-    __device__ static void scale_q(QOp& q) {
+    __device__ __forceinline__ static void scale_q(QOp& q) {
         for (int i = 0; i < 32; ++i) q.v[i] *= kScaleLog2;
     }
 
     // Wave wv fills 1-KiB blocks 4*wv .. 4*wv+3 of K and of V (4 rows each); part
     // p = 0, 1 fills blocks 4*wv + 2*p and 4*wv + 2*p + 1 (kAllParts: all four).
     template <class RowOf>
-    __device__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
+    __device__ __forceinline__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
                                      int part = kAllParts) {
         const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 4; ++u) {
@@ -286,7 +287,7 @@ struct F32 {
 
     // 32 rows copied to dst (row-major, 256 B each): wave wv copies rows 8*wv .. +7.
     template <class RowPtr>
-    __device__ static void dma_rows(char* dst, RowPtr row_ptr, int wv, int lane) {
+    __device__ __forceinline__ static void dma_rows(char* dst, RowPtr row_ptr, int wv, int lane) {
         for (int u = 0; u < 2; ++u) {
             const int row = 8 * wv + 4 * u + (lane >> 4);
             dma16(row_ptr(row) + 4 * (lane & 15), dst + (2 * wv + u) * 1024);
@@ -294,7 +295,7 @@ struct F32 {
     }
 
     struct DmaLane { uint32_t k[4], v[4]; };
-    __device__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
+    __device__ __forceinline__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
         for (int u = 0; u < 4; ++u) {
             const int row = 4 * (4 * wv + u) + (lane >> 4), cl = lane & 15;
             const uint32_t r0b = (uint32_t)row * (uint32_t)dil * kRowBytes;
@@ -302,7 +303,7 @@ struct F32 {
             dl.v[u] = r0b + 16u * (uint32_t)cl;
         }
     }
-    __device__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
+    __device__ __forceinline__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
         for (int u = 0; u < 4; ++u) {
             const int blk = 4 * wv + u;
             dma16s(K0, dl.k[u], slot + blk * 1024);
@@ -316,7 +317,7 @@ struct F32 {
         int h2;
         int v;  // V operand column 32*db + M of key key_local(u, h2): base of column M
     };
-    __device__ static void lane_offsets(Lane& lo, int lane) {
+    __device__ __forceinline__ static void lane_offsets(Lane& lo, int lane) {
         const int row = sigma(lane & 31);
         lo.k = row * kRowBytes;
         lo.sw = swz_k(row);
@@ -324,7 +325,7 @@ struct F32 {
         lo.v = kTileBytes + 4 * (lane & 31);
     }
 
-    __device__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
+    __device__ __forceinline__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
         const char* base = slot + sub * 32 * kRowBytes + lo.k;
         f32x16 acc = seed;
         for (int t4 = 0; t4 < 8; ++t4) {
@@ -335,11 +336,11 @@ struct F32 {
         return acc;
     }
 
-    __device__ static void to_p(const float* p, PFrag& pf) {
+    __device__ __forceinline__ static void to_p(const float* p, PFrag& pf) {
         for (int i = 0; i < 16; ++i) pf.v[i] = p[i];
     }
     // Sum of the query's 32 weights, in both lanes of the pair.
-    __device__ static float tile_sum(const PFrag&, const float* p, const Lane&) {
+    __device__ __forceinline__ static float tile_sum(const PFrag&, const float* p, const Lane&) {
         float sum[2] = {0.f, 0.f};
         for (int i = 0; i < 16; ++i) sum[i & 1] += p[i];
         return pair_sum(sum[0] + sum[1]);
@@ -347,11 +348,11 @@ struct F32 {
 
     // Step u pairs lane-half h2 with key key_local(u, h2), matching the score layout.
     struct VOp { const char* base; int h2; };
-    __device__ static void load_v(VOp& vo, const char* slot, int sub, const Lane& lo) {
+    __device__ __forceinline__ static void load_v(VOp& vo, const char* slot, int sub, const Lane& lo) {
         vo.base = slot + sub * 32 * kRowBytes + lo.v;
         vo.h2 = lo.h2;
     }
-    __device__ static void pv(const VOp& vo, const PFrag& pf, f32x16* o) {
+    __device__ __forceinline__ static void pv(const VOp& vo, const PFrag& pf, f32x16* o) {
         for (int db = 0; db < 2; ++db)
             for (int u = 0; u < 16; ++u) {
                 const float a = *reinterpret_cast<const float*>(vo.base + key_local(u, vo.h2) * kRowBytes + 128 * db);
@@ -359,7 +360,7 @@ struct F32 {
             }
     }
 
-    __device__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+    __device__ __forceinline__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
         for (int db = 0; db < 2; ++db)
             for (int q = 0; q < 4; ++q) {
                 f32x4 t;
@@ -368,7 +369,7 @@ struct F32 {
             }
     }
 
-    __device__ static Elem from_float(float x) { return x; }
+    __device__ __forceinline__ static Elem from_float(float x) { return x; }
 };
 
 // Wait until this wave's loads of the oldest outstanding stage have landed, given
@@ -389,15 +390,14 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 // product already multiplied by log2(e)/sqrt(d_h)).
 
 struct State {
-    float mc;      // running max of the query; -inf before its first valid key
-    float cofs;    // offset seeded into the score product: mc, or 0 while mc = -inf
+    float cofs;    // offset seeded into the score product (base 2): 0 until the query's
+                   // first tile with a valid key, then that tile's largest score or more
     float l;       // running weight sum of the query (both lane halves), relative to cofs
     f32x16 seed;   // -cofs in every element
     f32x16 o[2];   // unnormalised output, relative to cofs
 };
 
 __device__ __forceinline__ void state_init(State& st) {
-    st.mc = kNegInf;
     st.cofs = 0.f;
     st.l = 0.f;
     st.seed = f32x16{};
@@ -415,29 +415,32 @@ __device__ __forceinline__ float lse_of(float ofs2, float l) {
 // most 2^8: exact in bf16 and fp32 alike, so it is folded as it is.
 constexpr float kTileSumBound = 256.0f;
 
+// Offset of a partial result for a log-sum-exp merge: -inf when it holds no weight.
+__device__ __forceinline__ float state_offset(const State& st) { return st.l > 0.f ? st.cofs : kNegInf; }
+
 __device__ __forceinline__ bool pair_or(bool x) {
     auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
     return (r[0] | r[1]) != 0u;
 }
 
-// Rare path of a tile fold: the triggering queries raise their max to the tile max
-// (both lanes of a pair take the same decision) and recompute their weights against
-// it; every lane refreshes its seed and the tile sum.
+// Rare path of a tile fold: the triggering queries (weights that may exceed 2^8) raise
+// their offset to the tile's largest score (both lanes of a pair take the same
+// decision) and recompute their weights against it; every lane refreshes its seed and
+// the tile sum.
 template <class T>
 __device__ __forceinline__ void fold_slow(State& st, const f32x16& x, float* p, typename T::PFrag& pf, float& ts,
                                           bool trig, const typename T::Lane& lo) {
     float m4[4];
     for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(x[4 * j], x[4 * j + 1]), fmaxf(x[4 * j + 2], x[4 * j + 3]));
     const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) + st.cofs;
-    if (pair_or(trig) && tmax > st.mc) {  // -inf tmax: no valid key in the tile
-        // The state so far is relative to cofs; before the first valid key it is zero.
-        const float alpha = st.mc == kNegInf ? 0.f : fast_exp2(st.cofs - tmax);
+    if (pair_or(trig) && tmax != kNegInf) {
+        // The state so far is relative to cofs; without weight it is zero.
+        const float alpha = st.l > 0.f ? fast_exp2(st.cofs - tmax) : 0.f;
         st.l *= alpha;
         st.o[0] *= alpha;
         st.o[1] *= alpha;
         const float sh = tmax - st.cofs;
         for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i] - sh);
-        st.mc = tmax;
         st.cofs = tmax;
     }
     for (int i = 0; i < 16; ++i) st.seed[i] = -st.cofs;
@@ -445,23 +448,42 @@ __device__ __forceinline__ void fold_slow(State& st, const f32x16& x, float* p, 
     ts = T::tile_sum(pf, p, lo);  // with the whole wave active
 }
 
-// Fast path unless a query has no max yet or its weights may exceed the bound (a
-// non-finite sum included).
-__device__ __forceinline__ bool fold_trigger(const State& st, float ts) {
-    return st.mc == kNegInf || !(ts <= kTileSumBound);
+// Fast path unless the weights may exceed the bound (a non-finite sum included).
+__device__ __forceinline__ bool fold_trigger(const State&, float ts) { return !(ts <= kTileSumBound); }
+
+// A query's first tile with a valid key sets its offset to the tile's largest score
+// before the exponentials (queries that already hold weight keep theirs): its largest
+// weight is then exactly 1 and no weight overflows or underflows.
+__device__ __forceinline__ void first_offset(State& st, f32x16& x) {
+    float m4[4];
+    for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(x[4 * j], x[4 * j + 1]), fmaxf(x[4 * j + 2], x[4 * j + 3]));
+    const float tm = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));  // relative to cofs
+    const bool set = st.l == 0.f && tm != kNegInf;
+    const float sh = set ? tm : 0.f;
+    for (int i = 0; i < 16; ++i) x[i] -= sh;
+    st.cofs += sh;
+    for (int i = 0; i < 16; ++i) st.seed[i] = -st.cofs;
 }
 
 // Fold one 32-key tile of exponents x (score - cofs; -inf for masked keys) into the
-// state; the weights go to the P^T operand.
-template <class T>
-__device__ __forceinline__ void fold_tile(State& st, const f32x16& x, typename T::PFrag& pf,
-                                          const typename T::Lane& lo) {
+// state; the weights go to the P^T operand.  The rare path recomputes the exponents
+// with `scores()` (the staged keys are still in LDS) instead of keeping x alive across
+// the fast path.
+template <class T, class Scores>
+__device__ __forceinline__ void fold_tile(State& st, f32x16 x, typename T::PFrag& pf,
+                                          const typename T::Lane& lo, Scores scores) {
+    if (__any(st.l == 0.f)) first_offset(st, x);
     float p[16];
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x[i]);
     T::to_p(p, pf);
     float ts = T::tile_sum(pf, p, lo);
     const bool trig = fold_trigger(st, ts);
-    if (__any(trig)) fold_slow<T>(st, x, p, pf, ts, trig, lo);
+    if (__any(trig)) {
+        asm volatile("" ::: "memory");  // re-read the staged keys: nothing stays alive for this path
+        const f32x16 x2 = scores();
+        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(x2[i]);
+        fold_slow<T>(st, x2, p, pf, ts, trig, lo);
+    }
     st.l += ts;
 }
 
@@ -478,13 +500,18 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
                                          const typename T::QOp& q, int mode, uint32_t inv32, int h2, int base,
                                          int span, const int* gp, int wq, int climit = 1 << 30,
                                          const float* brow = nullptr) {
-    f32x16 s = T::qk(slot, sub, lo, q, st.seed);  // exponents: scores - cofs
-    if (brow) add_bias_run(s, brow);
+    // exponents: scores - cofs, masked
+    auto scores = [&]() __attribute__((always_inline)) {
+        f32x16 s = T::qk(slot, sub, lo, q, st.seed);
+        if (brow) add_bias_run(s, brow);
+        mask_scores<kRand>(s, mode, inv32, h2, base, span, gp, wq, climit);
+        return s;
+    };
+    const f32x16 s = scores();
     typename T::VOp vo;
     T::load_v(vo, slot, sub, lo);  // in flight during the softmax
-    mask_scores<kRand>(s, mode, inv32, h2, base, span, gp, wq, climit);
     typename T::PFrag pf;
-    fold_tile<T>(st, s, pf, lo);
+    fold_tile<T>(st, s, pf, lo, scores);
     T::pv(vo, pf, st.o);
 }
 
@@ -591,17 +618,42 @@ void band_kernel(const Params p) {
     // global and random stages, the remaining band stages.  A band stage first lets
     // its copy be issued before the global slots are set up.
     const int n_pre = ((kRandom || n_gst > 0) && nb + na > 0) ? 1 : 0;
-    auto is_glob = [&](int t) { return t >= n_pre && t < n_pre + n_lst; };  // a listed-key stage
-    auto band_u = [&](int t) { return t < n_pre ? t : t - n_lst; };
-    auto rnd_block = [&](int j) { return j < na_r ? rnd_a[j] : rnd_b[j - na_r]; };  // key block of random stage j
-    // First key of the u-th band stage in processing order (before, after, home).
-    auto stage_key = [&](int u) {
-        const int bs = u < nb ? u : (u < nb + na ? u + 2 : u - na);
-        return gbase + kStageKeys * bs;
+    auto is_glob = [&](int t) __attribute__((always_inline)) { return t >= n_pre && t < n_pre + n_lst; };  // a listed-key stage
+    auto band_u = [&](int t) __attribute__((always_inline)) { return t < n_pre ? t : t - n_lst; };
+    auto rnd_block = [&](int j) __attribute__((always_inline)) { return j < na_r ? rnd_a[j] : rnd_b[j - na_r]; };  // key block of random stage j
+    // Processing order of the band stages: the two home stages last (the global-row pass
+    // reuses them).  A tile with the full band of P = ceil(w/64) + 2 + ceil(wr/64) grid
+    // stages takes its other stages in ascending order of their 64-key block index
+    // modulo P: each block of the class is then read at about the same step by every
+    // tile whose band holds it, so a head's K/V comes from HBM a few blocks per step
+    // instead of all of it in the first two steps.  Tiles whose band is cut by the
+    // sequence ends take before, after, home.
+    const int P = ((w + kStageKeys - 1) / kStageKeys) + 2 + ((wr + kStageKeys - 1) / kStageKeys);
+    const bool rot = n_band == P && P > 2;
+    int bs0 = 0, hlo = 0, hhi = 0;
+    if (rot) {
+        const int a0 = (gbase / kStageKeys) % P;  // gbase >= 0 here (a multiple of 64)
+        bs0 = a0 == 0 ? 0 : P - a0;                 // grid stage of the first block = 0 mod P
+        const int h0 = nb >= bs0 ? nb - bs0 : nb - bs0 + P;  // rotated positions of the home stages
+        const int h1 = h0 + 1 == P ? 0 : h0 + 1;
+        hlo = min(h0, h1);
+        hhi = max(h0, h1);
+    }
+    // Grid stage of the u-th band stage in processing order.
+    auto band_bs = [&](int u) __attribute__((always_inline)) {
+        if (!rot) return u < nb ? u : (u < nb + na ? u + 2 : u - na);
+        if (u >= P - 2) return nb + u - (P - 2);
+        int k = u;
+        if (k >= hlo) ++k;
+        if (k >= hhi) ++k;
+        const int b = bs0 + k;
+        return b >= P ? b - P : b;
     };
+    // First key of the u-th band stage.
+    auto stage_key = [&](int u) __attribute__((always_inline)) { return gbase + kStageKeys * band_bs(u); };
 
     // Invalid-key bits of band stage u: keys outside [kb0, kend), or padded.
-    auto band_invalid = [&](int bs) -> uint64_t {
+    auto band_invalid = [&](int bs) __attribute__((always_inline)) -> uint64_t {
         if (pad) return band_mask[bs % kMaskRing];
         const int ks = stage_key(bs);
         const int lo = kb0 - ks, hi = kend - ks;  // valid keys: lo <= kk < hi
@@ -616,7 +668,7 @@ void band_kernel(const Params p) {
     const bool direct_ok = (uint64_t)dil * kStageKeys * T::kRowBytes < (1ull << 31);
     // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
     int ks_next = 0;  // first key of the band stage copied last (see the stage loop)
-    auto issue = [&](int s, int part) -> uint64_t {
+    auto issue = [&](int s, int part) __attribute__((always_inline)) -> uint64_t {
         char* slot = ring + (s % T::kNS) * T::kStageBytes;
         if (kRandom && is_glob(s) && s - n_pre >= n_gst) {
             const int j = s - n_pre - n_gst;
@@ -625,12 +677,12 @@ void band_kernel(const Params p) {
             if (inv == 0ull && part == kAllParts && direct_ok) {
                 T::dma_stage_direct(slot, K + (size_t)kb0 * 64, V + (size_t)kb0 * 64, dl, wv);
             } else {
-                T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane, part);
+                T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane, part);
             }
             return 0ull;
         } else if (is_glob(s)) {
             const int* src = glob_src + kStageKeys * (s - n_pre);
-            T::dma_stage(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane, part);
+            T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return src[kk]; }, wv, lane, part);
             return 0ull;
         } else {
             const int bs = band_u(s);
@@ -641,7 +693,7 @@ void band_kernel(const Params p) {
                 const size_t row0 = (size_t)(r + ks * dil) * 64;
                 T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
             } else {
-                T::dma_stage(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
+                T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
                              wv, lane, part);
             }
             return inv;
@@ -667,7 +719,7 @@ void band_kernel(const Params p) {
     }
     if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
     // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ...
-    auto fill_band_masks = [&](int W) {
+    auto fill_band_masks = [&](int W) __attribute__((always_inline)) {
         constexpr int kPer = kMaskWindow / kWaves, kGroup = 4;
         for (int j0 = 0; j0 < kPer; j0 += kGroup) {
             uint32_t flag[kGroup];
@@ -732,7 +784,11 @@ void band_kernel(const Params p) {
         }
     wait_vmcnt<0>();
     T::scale_q(qop);
-    for (int t = 0; t < n_st; ++t) {
+    // Stages [0, n_gen): the listed-key stages (global, random) and the band stage
+    // placed ahead of them, in the general body below; stages [n_gen, n_st): band
+    // stages only, in the lean loop after it.
+    const int n_gen = n_pre + n_lst;
+    for (int t = 0; t < n_gen; ++t) {
         const uint64_t inv_cur = inv_next;  // stage t's bits (two-slot ring: issued last)
         const int ks_cur = ks_next;
         wait_stage<T>(min(T::kNS - 2, n_st - 1 - t));
@@ -748,7 +804,7 @@ void band_kernel(const Params p) {
         }
         if (t == 0 && ng > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
-            T::dma_rows(gq_rows, [&](int j) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * 64 : zero; },
+            T::dma_rows(gq_rows, [&](int j) __attribute__((always_inline)) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * 64 : zero; },
                         wv, lane);
         }
         const char* slot = ring + (t % T::kNS) * T::kStageBytes;
@@ -789,6 +845,79 @@ void band_kernel(const Params p) {
                                      climit, (kBias && !gstage && !rstage) ? bias_lds + kBiasPad + bbase : nullptr);
             }
         }
+    }
+
+    // Band stages.  Sub-tile j of the band grid holds keys gbase + 32 j .. + 31; the
+    // wave's first row is grid position 32 ja.  Some row of the wave has a window key in
+    // sub-tile j for jlo <= j <= jhi, every row has all 32 for ilo <= j <= ihi.  Per
+    // sub-tile the wave takes one of three uniform branches: skipped, interior with every
+    // key valid (no mask), or masked (band edge, invalid keys).
+    const int ja = 2 * nb + wv;
+    const int jlo = ja - ((w + 31) >> 5), jhi = ja + ((wr + 31) >> 5);
+    const int ilo = ja - ((w - 31) >> 5), ihi = ja + ((wr - 31) >> 5);
+    // Copies of band stage u into ring slot sl; returns its invalid-key bits and sets
+    // ks_next.  A stage whose 64 keys all lie in [kb0, kend) without padding needs no
+    // mask: its copy goes out in the scalar-base form at once.
+    auto issue_band = [&](int u, int sl) __attribute__((always_inline)) -> uint64_t {
+        const int ks = gbase + kStageKeys * band_bs(u);
+        ks_next = ks;
+        char* slot = ring + sl * T::kStageBytes;
+        if (!pad && ks >= kb0 && ks + kStageKeys <= kend && direct_ok) {
+            const size_t row0 = (size_t)(r + ks * dil) * 64;
+            T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
+            return 0ull;
+        }
+        const uint64_t inv = uniform64(band_invalid(u));
+        if (inv == 0ull && direct_ok) {
+            const size_t row0 = (size_t)(r + ks * dil) * 64;
+            T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
+        } else {
+            T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv,
+                         lane);
+        }
+        return inv;
+    };
+    // One band stage t in ring slot SL (t % 2), which the caller makes a compile-time
+    // constant so that the operand reads address the slot with immediate offsets.
+    auto band_step = [&](int t, auto slot_c) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot_c)::value;
+        const uint64_t inv = inv_next;  // stage t's bits (two-slot ring: issued last)
+        const int ks = ks_next;
+        wait_vmcnt<0>();
+        barrier_nofence();
+        if (t + 1 < n_st) {
+            const int bn = t + 1 - n_lst;
+            if (pad && bn % kMaskWindow == 0) {  // bn > 0: band stage 0 is never issued here
+                fill_band_masks(bn / kMaskWindow);
+                __syncthreads();
+            }
+            inv_next = issue_band(bn, SL ^ 1);
+        }
+        if (!rows_live) return;
+        const char* slot = ring + SL * T::kStageBytes;
+        const int j0 = (ks - gbase) >> 5;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int j = j0 + sub;
+            const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
+            if (j < jlo || j > jhi || inv32 == ~0u) continue;
+            const int bbase = ks + 32 * sub + 8 * h2 - qv + w;
+            const float* brow = kBias ? bias_lds + kBiasPad + bbase : nullptr;
+            const int mode = (j >= ilo && j <= ihi && inv32 == 0u) ? 0 : 1;
+            sub_step<T>(st, slot, sub, lo, qop, mode, inv32, h2, bbase, span, nullptr, 0, 1 << 30, brow);
+        }
+    };
+    static_assert(T::kNS == 2, "the band loop alternates between two ring slots");
+    {
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        int t = n_gen;
+        if (t < n_st && (t & 1)) band_step(t++, S1{});
+        for (; t + 1 < n_st; t += 2) {
+            band_step(t, S0{});
+            band_step(t + 1, S1{});
+        }
+        if (t < n_st) band_step(t, S0{});
     }
 
     const float scale = st.l > 0.f ? 1.f / st.l : 0.f;
@@ -842,7 +971,7 @@ void band_kernel(const Params p) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
                 T::dma_stage(ring + j * T::kStageBytes, KG, VG,
-                             [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
+                             [&](int kk) __attribute__((always_inline)) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             }
             wait_vmcnt<0>();
             __syncthreads();
@@ -864,8 +993,8 @@ void band_kernel(const Params p) {
             }
         }
         __syncthreads();  // done with the staged keys: the ring now holds the reduction
-        if (lane < 32) {  // partial relative to cofs (= mc, or nothing when mc = -inf)
-            red_ml[wv][lane][0] = gs.mc;
+        if (lane < 32) {  // partial relative to its offset (-inf when it holds no weight)
+            red_ml[wv][lane][0] = state_offset(gs);
             red_ml[wv][lane][1] = gs.l;
         }
         // Column c of query q sits at q*64 + (c ^ q%32): the 32 queries of one store,
