@@ -81,6 +81,12 @@ typedef struct lf_attn_s* lf_attn_t;
  * Create a handle for one element type.  Allocates only host memory; device
  * workspace is allocated on first use, on the device current at that call.
  * Errors: LF_ERR_INVALID_ARG (out == NULL), LF_ERR_UNSUPPORTED (unknown dtype).
+ *
+ * Failure injection for tests: if the environment variable LF_ATTN_FAULT is "alloc"
+ * when the handle is created, its next device-workspace allocation fails as if
+ * hipMalloc had (LF_ERR_OOM, the handle keeps its previous workspace); if it is
+ * "launch", its next kernel launch fails before anything is enqueued (LF_ERR_HIP).
+ * Each fires once; afterwards the handle works normally.
  */
 lf_status lf_attn_create(lf_attn_t* out, lf_dtype dtype);
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -72,6 +73,12 @@ struct lf_attn_s {
     size_t ws_gemm_bytes = 0;
     int ws_gemm_device = -1;
     std::string last_error;
+    // Failure injection for tests, from the environment variable LF_ATTN_FAULT when
+    // the handle is created: "alloc" fails the handle's next workspace allocation as if
+    // hipMalloc had (LF_ERR_OOM), "launch" its next kernel launch before it is enqueued
+    // (LF_ERR_HIP); once, then the handle works normally.  Anything else (or unset):
+    // none.
+    int fault = 0;
     bool timing = false;
     std::vector<TimedLaunch> pending;  // recorded, not yet read
     std::vector<hipEvent_t> event_pool;
@@ -89,6 +96,9 @@ LaunchEvents& launch_events() {
 }  // namespace lf
 
 namespace {
+
+constexpr int kFaultAlloc = 1;
+constexpr int kFaultLaunch = 2;
 
 lf_status release_gemm(lf_attn_t h);
 
@@ -158,6 +168,10 @@ lf_status lf_attn_create(lf_attn_t* out, lf_dtype dtype) {
     lf_attn_t h = new (std::nothrow) lf_attn_s;
     if (!h) return LF_ERR_OOM;
     h->dtype = dtype;
+    if (const char* f = std::getenv("LF_ATTN_FAULT")) {
+        if (std::strcmp(f, "alloc") == 0) h->fault = kFaultAlloc;
+        if (std::strcmp(f, "launch") == 0) h->fault = kFaultLaunch;
+    }
     *out = h;
     return LF_OK;
 }
@@ -425,6 +439,10 @@ lf_status release_gemm(lf_attn_t h) {
 
 lf_status reserve(lf_attn_t h, char** buf, size_t* have, int* dev, size_t need) {
     if (need <= *have && *dev == h->device) return LF_OK;
+    if (h->fault == kFaultAlloc) {  // the old buffer stays: the handle remains usable
+        h->fault = 0;
+        return fail(h, LF_ERR_OOM, "hipMalloc of %zu workspace bytes failed (LF_ATTN_FAULT=alloc)", need);
+    }
     if (*buf) (void)hipFree(*buf);
     *buf = nullptr;
     *have = 0;
@@ -458,6 +476,10 @@ lf_status upload_random(lf_attn_t h) {
 // a library call (the layer's GEMMs) is bracketed by two recorded events instead.
 template <class Launch>
 lf_status launch_stage(lf_attn_t h, int stage, hipStream_t s, Launch launch) {
+    if (h->fault == kFaultLaunch) {
+        h->fault = 0;
+        return fail(h, LF_ERR_HIP, "kernel launch failed (LF_ATTN_FAULT=launch)");
+    }
     TimedLaunch tl{nullptr, nullptr, stage};
     const bool bracket = stage == LF_STAGE_LAYER_GEMM;
     lf::LaunchEvents& ev = lf::launch_events();
@@ -597,6 +619,10 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = h->dtype;
     if (no_alloc) {  // no events: their creation could allocate
+        if (h->fault == kFaultLaunch) {
+            h->fault = 0;
+            return fail(h, LF_ERR_HIP, "kernel launch failed (LF_ATTN_FAULT=launch)");
+        }
         hipError_t e = lf::launch_band(p, dt, s);
         if (e == hipSuccess && p.n_g > 0) e = lf::launch_merge(p, dt, s);
         if (e != hipSuccess) return fail(h, LF_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
