@@ -55,6 +55,9 @@ What it computes (per batch b and head h, with inputs widened to float64):
 * Per-row log-sum-exp (``attention_lse``): log of the sum over the key set of
   exp(S_ij); -inf for a row with no key.  It is the normaliser of the row's
   softmax, the quantity a backward pass reuses.
+* Gradient of the relative position bias tables (``attention_bias_grad``): entry
+  m + w of head h's table sums dS_ij (below) over the window pairs j = i + m*dil of
+  the non-global rows, the pairs the entry is added to.
 * Gradients (``attention_backward``): for an upstream gradient dO of the output,
   the textbook derivatives of O = P V with P the row softmax of S (Reformer
   hashing page, "core principle" formula; the same key sets):
@@ -395,6 +398,51 @@ def attention_backward_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_
         dq[blk] = ds @ k / math.sqrt(d)
         dk += ds.T @ q[blk] / math.sqrt(d)
     return dq, dk, dv
+
+
+def attention_bias_grad_bh(q, k, v, dout, w: int, dil: int, global_idx=None, pad_row=None, causal: bool = False,
+                           bias=None, rand=None, rand_block: int = 64) -> np.ndarray:
+    """Gradient of sum(O * dout) with respect to one head's relative position bias table
+    (2w+1 entries, reading of page "基于自注意力机制的长文本建模算法：Longformer详解" §5):
+    entry m + w sums dS_ij over the window pairs j = i + m*dil of the non-global rows i
+    that are in the key set (the pairs the entry was added to), with dS = P (dP - D) the
+    gradient of the row's scaled scores."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    L = q.shape[0]
+    G = global_set(global_idx)
+    is_g = np.zeros(L, dtype=bool)
+    is_g[G] = True
+    beta = np.zeros(2 * w + 1) if bias is None else np.asarray(bias, dtype=np.float64)
+    db = np.zeros(2 * w + 1, dtype=np.float64)
+    for s0 in range(0, L, ROW_BLOCK):
+        blk = np.arange(s0, min(L, s0 + ROW_BLOCK))
+        m = mask_rows(L, w, dil, G, pad_row, blk, causal=causal, rand=rand, rand_block=rand_block)
+        o, p = _attention_rows(q[blk], k, v, m, window_bias(L, w, dil, G, blk, beta))
+        dp = do[blk] @ v.T
+        ds = p * (dp - (do[blk] * o).sum(axis=1, keepdims=True))
+        j = np.arange(L)[None, :]
+        win = window_member(blk[:, None], j, w, dil) & m & ~is_g[blk][:, None]
+        idx = (j - blk[:, None]) // dil + w
+        np.add.at(db, idx[win], ds[win])
+    return db
+
+
+def attention_bias_grad(q, k, v, dout, w: int, dil_per_head, global_idx=None, key_pad_mask=None,
+                        causal: bool = False, bias=None, rand=None, rand_block: int = 64) -> np.ndarray:
+    """Gradient of the relative position bias tables of the full problem: float64 [H, 2w+1],
+    summed over the batch."""
+    q = _as_f64(q)
+    B, H, L, d = q.shape
+    dil = [int(x) for x in np.asarray(dil_per_head).reshape(-1)]
+    pad = None if key_pad_mask is None else np.asarray(_as_f64(key_pad_mask) != 0)
+    out = np.zeros((H, 2 * w + 1), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[h] += attention_bias_grad_bh(q[b, h], k[b, h], v[b, h], dout[b, h], w, dil[h],
+                                             globals_of(global_idx, b), None if pad is None else pad[b],
+                                             causal=causal, bias=None if bias is None else bias[h],
+                                             rand=None if rand is None else rand[h], rand_block=rand_block)
+    return out
 
 
 def _grads_rows(q_rows, k, v, do_rows, m, extra=None):

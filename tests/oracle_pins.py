@@ -966,6 +966,98 @@ def pin_wrapper_backward_global_proj():
                     assert err < 1e-12, (name, causal, b, h, err)
 
 
+# ------------------------------------------------- gradient of the position bias table
+
+def _bias_dense_torch(q, k, v, table, L, w, dil, G, padl, causal, rand, bs):
+    """Dense masked attention in torch float64 with the bias table gathered onto the
+    window pairs of non-global rows, pairs listed by brute force."""
+    d = q.shape[1]
+    Gs = set(int(g) for g in G)
+    m = torch.zeros(L, L, dtype=torch.bool)
+    idx = torch.zeros(L, L, dtype=torch.long)
+    use = torch.zeros(L, L, dtype=torch.bool)
+    for i in range(L):
+        for j in brute.key_set(i, L, w, dil, G, padl, causal, rand, bs):
+            m[i, j] = True
+            if i not in Gs and (j - i) % dil == 0 and abs(j - i) <= w * dil:
+                use[i, j] = True
+                idx[i, j] = (j - i) // dil + w
+    s = (q @ k.T) / math.sqrt(d) + torch.where(use, table[idx], torch.zeros((), dtype=torch.float64))
+    s = s.masked_fill(~m, float("-inf"))
+    p = torch.softmax(s, dim=1)
+    p = torch.where(m.any(dim=1, keepdim=True), p, torch.zeros_like(p))
+    return p @ v
+
+
+BIAS_GRAD_CASES = [
+    # (L, d, w, dil, globals, pad kind, causal, random draws (block, r) or None)
+    (30, 8, 3, 1, [], None, False, None),
+    (36, 8, 4, 2, [4, 5, 33], "rand", False, None),
+    (40, 8, 5, 1, [0, 9, 9, 39], "suffix", True, None),
+    (48, 8, 2, 3, [7, 20], None, False, None),
+    (40, 8, 2, 1, [3, 31], "rand", False, (8, 2)),
+]
+
+
+def pin_bias_grad_autograd():
+    """The bias-table gradient equals torch autograd of the dense formulation (window
+    pairs of non-global rows listed by brute force), with dilation, globals inside and
+    outside the window, padding, the one-sided mode and random blocks (no bias on
+    them); the full-problem wrapper sums the slices of every sequence per head."""
+    for n, (L, d, w, dil, G, padk, causal, rnd) in enumerate(BIAS_GRAD_CASES):
+        q, k, v, do = (_rand((L, d), 1500 + 10 * n + t) for t in range(4))
+        beta = _rand((2 * w + 1,), 1509 + 10 * n)
+        pad = _pad_for(padk, L, n)
+        padl = None if pad is None else pad.tolist()
+        bs, draws = 64, None
+        if rnd is not None:
+            bs = rnd[0]
+            draws = _draws(L, bs, rnd[1], n)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        tb = torch.tensor(beta, requires_grad=True)
+        out = _bias_dense_torch(tq, tk, tv, tb, L, w, dil, G, padl, causal, draws, bs)
+        (out * torch.from_numpy(do)).sum().backward()
+        got = orc.attention_bias_grad_bh(q, k, v, do, w, dil, G, pad, causal=causal, bias=beta, rand=draws,
+                                         rand_block=bs)
+        err = np.abs(got - tb.grad.numpy()).max()
+        assert err < 1e-12, (n, err)
+    # wrapper: B = 2 sequences, H = 2 heads, per-sequence padding and dilation per head
+    B, H, L, d, w = 2, 2, 24, 8, 3
+    dil = [1, 2]
+    q, k, v, do = (_rand((B, H, L, d), 1590 + t) for t in range(4))
+    beta = _rand((H, 2 * w + 1), 1595)
+    pad = np.zeros((B, L), dtype=bool)
+    pad[1, 19:] = True
+    got = orc.attention_bias_grad(q, k, v, do, w, dil, [2, 15], pad, bias=beta)
+    for h in range(H):
+        ref = np.zeros(2 * w + 1)
+        for b in range(B):
+            tb = torch.tensor(beta[h], requires_grad=True)
+            out = _bias_dense_torch(*(torch.from_numpy(x[b, h]) for x in (q, k, v)), tb, L, w, dil[h], [2, 15],
+                                    pad[b].tolist(), False, None, 64)
+            (out * torch.from_numpy(do[b, h])).sum().backward()
+            ref += tb.grad.numpy()
+        assert np.abs(got[h] - ref).max() < 1e-12, h
+
+
+def pin_bias_grad_finite_differences():
+    """Central differences of sum(O * dO) with respect to each table entry."""
+    L, d, w, dil, G = 14, 4, 2, 2, [5]
+    q, k, v, do = (_rand((L, d), 1600 + t) for t in range(4))
+    beta = _rand((2 * w + 1,), 1605)
+    pad = np.zeros(L, dtype=bool)
+    pad[[2, 11]] = True
+    got = orc.attention_bias_grad_bh(q, k, v, do, w, dil, G, pad, bias=beta)
+    eps = 1e-6
+    for m in range(2 * w + 1):
+        up, dn = beta.copy(), beta.copy()
+        up[m] += eps
+        dn[m] -= eps
+        fd = (float((orc.attention_bh(q, k, v, w, dil, G, pad, bias=up) * do).sum())
+              - float((orc.attention_bh(q, k, v, w, dil, G, pad, bias=dn) * do).sum())) / (2 * eps)
+        assert abs(fd - got[m]) < 1e-7, (m, fd, got[m])
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_pair_counts_brute,
@@ -1006,6 +1098,8 @@ ALL_PINS = [
     pin_wrapper_lse,
     pin_wrapper_backward,
     pin_wrapper_backward_global_proj,
+    pin_bias_grad_autograd,
+    pin_bias_grad_finite_differences,
     pin_layer_torch_encoder,
     pin_layer_norm_rows,
 ]

@@ -343,6 +343,34 @@ _WRAPPERS = {"attention_sampled": _sampled_swap, "attention_lse": _lse_swap,
              "attention_backward": _bwd_swap, "attention_backward_global_proj": _gp_bwd_swap}
 
 
+def _bias_grad_mutant(kind):
+    """attention_bias_grad_bh with one plausible mistake."""
+    def f(q, k, v, dout, w, dil, global_idx=None, pad_row=None, causal=False, bias=None, rand=None, rand_block=64):
+        q, k, v, do = (orc._as_f64(t) for t in (q, k, v, dout))
+        L = q.shape[0]
+        G = orc.global_set(global_idx)
+        is_g = np.zeros(L, dtype=bool)
+        is_g[G] = True
+        beta = np.zeros(2 * w + 1) if bias is None else np.asarray(bias, dtype=np.float64)
+        db = np.zeros(2 * w + 1)
+        blk = np.arange(L)
+        m = orc.mask_rows(L, w, dil, G, pad_row, blk, causal=causal, rand=rand, rand_block=rand_block)
+        o, p = orc._attention_rows(q, k, v, m, orc.window_bias(L, w, dil, G, blk, beta))
+        dp = do @ v.T
+        delta = 0.0 if kind == "no_delta" else (do * o).sum(axis=1, keepdims=True)
+        ds = p * (dp - delta)
+        j = np.arange(L)[None, :]
+        win = orc.window_member(blk[:, None], j, w, dil) & m
+        if kind != "global_rows":
+            win &= ~is_g[:, None]
+        idx = (j - blk[:, None]) // dil + w
+        if kind == "reversed":
+            idx = 2 * w - idx
+        np.add.at(db, idx[win], ds[win])
+        return db
+    return f
+
+
 MUTANTS = {
     "window_strict_edge": ("window_member", _window_strict),
     "window_no_lattice": ("window_member", _window_no_lattice),
@@ -377,6 +405,8 @@ MUTANTS = {
     "bwd_dq_from_v": ("attention_backward_bh", _bwd_mutant("dq_from_v")),
     "bwd_dv_unmasked": ("attention_backward_bh", _bwd_mutant("dv_unmasked_softmax")),
 }
+for _kind in ("no_delta", "global_rows", "reversed"):
+    MUTANTS[f"bias_grad_{_kind}"] = ("attention_bias_grad_bh", _bias_grad_mutant(_kind))
 for _fn, _make in _WRAPPERS.items():
     for _field in ("pad", "dil", "glob", "bias", "rand"):
         MUTANTS[f"{_fn}_swap_{_field}"] = (_fn, _make(_field))
