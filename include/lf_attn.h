@@ -56,7 +56,7 @@ typedef enum lf_dtype {
 #define LF_STATIC_SCRATCH_BYTES (16 << 20) /* device scratch of lf_attn_forward_static */
 
 /* Kernel launches timed by lf_attn_stage_times. */
-#define LF_N_STAGES 9
+#define LF_N_STAGES 10
 #define LF_STAGE_BAND 0      /* window band, global-column fold, global-row partials */
 #define LF_STAGE_MERGE 1     /* log-sum-exp merge of the partials (only with globals) */
 #define LF_STAGE_BWD_PREP 2  /* backward: D = rowsum(dO * O), base-2 log-sum-exp */
@@ -66,6 +66,7 @@ typedef enum lf_dtype {
 #define LF_STAGE_LAYER_GEMM 6      /* layer: the four projection / feed-forward GEMMs (hipBLASLt) */
 #define LF_STAGE_LAYER_POINTWISE 7 /* layer: head split and merge, LayerNorms, GELU */
 #define LF_STAGE_BWD_DKV_GLOBAL 8  /* backward, separate global projections: dK_g, dV_g */
+#define LF_STAGE_BWD_DBIAS 9       /* backward: sums of the position-bias table gradient */
 
 /* Pattern variants (lf_attn_set_window_mode). */
 #define LF_WINDOW_SYMMETRIC 0 /* keys i + m*dil, m = -w..w (default) */
@@ -189,6 +190,34 @@ lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void
                            int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
                            const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
                            void* stream);
+
+/*
+ * lf_attn_backward that also writes the gradient of the relative position bias table
+ * set on the handle (lf_attn_set_position_bias), so that the table can be learned
+ * (page "基于自注意力机制的长文本建模算法：Longformer详解" §5 names the relative
+ * position bias, §6 the pretraining).  With the table added to the scaled score of
+ * each window pair j = i + m*dil of a non-global row i,
+ *
+ *   dbias[h][m + w] = sum over b and those pairs of dS_ij      (m = -w .. w),
+ *
+ * dS as in lf_attn_backward.  Pairs that enter through the global pattern or a random
+ * block carry no bias and add nothing.
+ *
+ * dbias : DEVICE float32 [H][2w + 1], 4-byte aligned, fully overwritten, not
+ *         overlapping any other argument.  With w >= L the entries of offsets no pair
+ *         reaches are 0.
+ * Other arguments, outputs and errors: as lf_attn_backward, whose dq, dk and dv it
+ * writes bit for bit; LF_ERR_INVALID_ARG if no table is set on the handle or dbias is
+ * NULL.  Each dQ work-group keeps per-wave offset sums in 4 * (2w' + 193) * 4 bytes of
+ * LDS (w' = min(w, L)) and writes them to the backward workspace (which grows by
+ * B * H * tiles * (2w' + 1) floats); a last kernel adds them up per head in a fixed
+ * order, so repeated calls give the same table bit for bit.
+ */
+lf_status lf_attn_backward_bias(lf_attn_t h, const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dbias,
+                                int B, int H, int L, int d_h, int w, const int32_t* dil_per_head,
+                                const int32_t* global_idx, int n_global, const uint8_t* key_pad_mask,
+                                void* stream);
 
 /*
  * The same forward with separate projections for the global rows.

@@ -21,9 +21,9 @@ LF_WINDOW_SYMMETRIC = 0
 LF_WINDOW_CAUSAL = 1
 LF_GLOBALS_SHARED = 0
 LF_GLOBALS_PER_SEQUENCE = 1
-N_STAGES = 9
+N_STAGES = 10
 STAGE_NAMES = ("band", "merge", "bwd_prep", "bwd_dq", "bwd_dkv", "bwd_merge", "layer_gemm", "layer_pointwise",
-               "bwd_dkv_global")
+               "bwd_dkv_global", "bwd_dbias")
 LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
 MAX_HEADS = 64
 MAX_GLOBALS = 256
@@ -40,6 +40,7 @@ EXPORTS = (
     "lf_attn_forward_global_proj_lse",
     "lf_attn_forward_lse",
     "lf_attn_backward",
+    "lf_attn_backward_bias",
     "lf_attn_backward_global_proj",
     "lf_layer_forward",
     "lf_attn_destroy",
@@ -105,6 +106,9 @@ def load_library():
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
                                      vp, vp]
     lib.lf_attn_backward.restype = i32
+    lib.lf_attn_backward_bias.argtypes = [vp] * 11 + [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32),
+                                                      ctypes.POINTER(ctypes.c_int32), i32, vp, vp]
+    lib.lf_attn_backward_bias.restype = i32
     lib.lf_attn_backward_global_proj.argtypes = [vp] * 16 + [i32, i32, i32, i32, i32,
                                                              ctypes.POINTER(ctypes.c_int32),
                                                              ctypes.POINTER(ctypes.c_int32), i32, vp, vp]
@@ -230,6 +234,13 @@ class LfAttn:
         keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
         st = self.lib.lf_attn_backward(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr,
                                        dk_ptr, dv_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
+        self._check(st, self.handle)
+
+    def backward_bias_raw(self, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, db_ptr, B,
+                          H, L, d_h, w, dil, global_idx, pad_ptr, stream):
+        keep, dil_p, g_p, ng = self._host_arrays(dil, global_idx)
+        st = self.lib.lf_attn_backward_bias(self.handle, q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr,
+                                            dk_ptr, dv_ptr, db_ptr, B, H, L, d_h, w, dil_p, g_p, ng, pad_ptr, stream)
         self._check(st, self.handle)
 
     def backward_global_proj_raw(self, ins, grads, lse_ptr, B, H, L, d_h, w, dil, global_idx, pad_ptr, stream):
@@ -542,12 +553,14 @@ def forward_lse(q, k, v, w: int, dil, global_idx=None, key_pad_mask=None, out=No
 
 
 def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask=None, dq=None, dk=None,
-             dv=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
+             dv=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None, dbias=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dout``.
 
     q, k, v, out, dout: contiguous bf16 device tensors [B, H, L, 64]; ``out`` and
-    ``lse`` as returned by ``forward_lse`` for the same inputs and pattern (and bias:
-    the table is held fixed, no gradient of it is returned).
+    ``lse`` as returned by ``forward_lse`` for the same inputs and pattern (and bias).
+    dbias: with a position bias table in use, True (or a float32 device tensor
+    [H, 2w + 1] to write into) also returns the gradient of the table, summed over
+    the batch, as a fourth result (lf_attn_backward_bias).
     """
     import torch
 
@@ -566,6 +579,17 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
             raise ValueError("dq, dk, dv must be contiguous device tensors like q")
         res.append(t)
     dq, dk, dv = res
+    if dbias is not None and dbias is not False:
+        if dbias is True:
+            dbias = torch.empty((H, 2 * int(w) + 1), dtype=torch.float32, device=q.device)
+        elif (dbias.dtype != torch.float32 or tuple(dbias.shape) != (H, 2 * int(w) + 1) or not dbias.is_contiguous()
+              or not dbias.is_cuda):
+            raise ValueError("dbias must be a contiguous float32 device tensor [H, 2w + 1]")
+        with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
+            h.backward_bias_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbias.data_ptr(), B, H, L,
+                                d_h, int(w), dil, global_idx, pad_ptr, stream)
+        return dq, dk, dv, dbias
     with torch.cuda.device(q.device), _CallBias(h, bias), _CallRandom(h, rand, handle is not None):
         h.backward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d_h, int(w), dil, global_idx, pad_ptr,

@@ -639,7 +639,8 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
                         const void* vg, const void* out, const void* dout, const float* lse, void* dq, void* dk,
                         void* dv, void* dqg, void* dkg, void* dvg, int B, int H, int L, int d_h, int w,
                         const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
-                        const uint8_t* key_pad_mask, void* stream) {
+                        const uint8_t* key_pad_mask, void* stream, float* dbias = nullptr,
+                        bool want_dbias = false) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->last_error.clear();
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
@@ -648,6 +649,11 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     if (sep && !(qg && kg && vg && dqg && dkg && dvg))
         return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g, v_g, dq_g, dk_g and dv_g must all be non-null");
     if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the backward supports bf16 handles only");
+    if (want_dbias && !dbias) return fail(h, LF_ERR_INVALID_ARG, "dbias must be non-null");
+    if (want_dbias && !h->bias)
+        return fail(h, LF_ERR_INVALID_ARG, "no position bias table is set on the handle (its gradient was asked for)");
+    if (want_dbias && (reinterpret_cast<uintptr_t>(dbias) & 3u) != 0)
+        return fail(h, LF_ERR_INVALID_ARG, "dbias must be 4-byte aligned");
     Plan pl;
     lf_status st = make_plan(h, pl, B, H, L, d_h, w, dil_per_head, global_idx, n_global);
     if (st != LF_OK) return st;
@@ -670,6 +676,15 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
             return fail(h, LF_ERR_INVALID_ARG, "the gradients must not overlap the inputs");
         for (int j = 0; j < i; ++j)
             if (overlaps(outs[i], outs[j], bytes)) return fail(h, LF_ERR_INVALID_ARG, "the gradients must not overlap");
+    }
+    if (want_dbias) {
+        const size_t db = static_cast<size_t>(H) * (2 * w + 1) * sizeof(float);
+        for (int i = 0; i < n_outs; ++i)
+            if (overlaps2(dbias, db, outs[i], bytes)) return fail(h, LF_ERR_INVALID_ARG, "dbias must not overlap the gradients");
+        for (int j = 0; j < n_ins; ++j)
+            if (overlaps2(dbias, db, ins[j], bytes)) return fail(h, LF_ERR_INVALID_ARG, "dbias must not overlap the inputs");
+        if (overlaps2(dbias, db, lse, lb) || overlaps2(dbias, db, h->bias, db))
+            return fail(h, LF_ERR_INVALID_ARG, "dbias must not overlap lse or the bias table");
     }
 
     lf::BwdParams p;
@@ -722,8 +737,9 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * ngq * 64;
     const size_t n_own = static_cast<size_t>(B) * H * ngq * 64;
     const size_t rows_al = (rows + 63) & ~size_t(63);
+    const size_t n_db = want_dbias ? static_cast<size_t>(B) * H * pl.tiles * (2 * pl.w + 1) : 0;
     st = reserve(h, &h->ws_bwd, &h->ws_bwd_bytes, &h->ws_bwd_device,
-                 (3 * rows_al + 3 * n_part + 2 * n_own) * sizeof(float));
+                 (3 * rows_al + 3 * n_part + 2 * n_own + n_db) * sizeof(float));
     if (st != LF_OK) return st;
     float* f = reinterpret_cast<float*>(h->ws_bwd);
     p.lse2 = f;
@@ -735,6 +751,10 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     p.ws_dv = f + 2 * n_part;
     p.ws_dkg = f + 3 * n_part;
     p.ws_dvg = f + 3 * n_part + n_own;
+    if (want_dbias) {
+        p.ws_db = f + 3 * n_part + 2 * n_own;
+        p.dbias = dbias;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = launch_stage(h, LF_STAGE_BWD_PREP, s, [&] { return lf::launch_bwd_prep(p, s); });
@@ -744,6 +764,8 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
         st = launch_stage(h, LF_STAGE_BWD_DKV_GLOBAL, s, [&] { return lf::launch_bwd_dkv_global_proj(p, s); });
     if (st == LF_OK && p.n_g > 0)
         st = launch_stage(h, LF_STAGE_BWD_MERGE, s, [&] { return lf::launch_bwd_merge(p, s); });
+    if (st == LF_OK && want_dbias)
+        st = launch_stage(h, LF_STAGE_BWD_DBIAS, s, [&] { return lf::launch_bwd_dbias(p, s); });
     return st;
 }
 
@@ -969,6 +991,14 @@ lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void
                            const uint8_t* key_pad_mask, void* stream) {
     return backward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, dout, lse, dq, dk, dv, nullptr, nullptr, nullptr,
                          B, H, L, d_h, w, dil_per_head, global_idx, n_global, key_pad_mask, stream);
+}
+
+lf_status lf_attn_backward_bias(lf_attn_t h, const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv, float* dbias, int B,
+                                int H, int L, int d_h, int w, const int32_t* dil_per_head, const int32_t* global_idx,
+                                int n_global, const uint8_t* key_pad_mask, void* stream) {
+    return backward_impl(h, q, k, v, nullptr, nullptr, nullptr, out, dout, lse, dq, dk, dv, nullptr, nullptr, nullptr,
+                         B, H, L, d_h, w, dil_per_head, global_idx, n_global, key_pad_mask, stream, dbias, true);
 }
 
 lf_status lf_attn_backward_global_proj(lf_attn_t h, const void* q, const void* k, const void* v, const void* q_g,

@@ -343,9 +343,16 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // (with the in-window test, so each key counts once), the random key blocks of the
 // tile's two query blocks (kRandom, as in the forward), then the window band.
 
-template <bool kCausal, bool kBias, bool kRandom>
+// With kBiasGrad (and kBias) each wave also sums dS of its window pairs per offset
+// m = key - query (class steps) into an LDS accumulator of its own (dynamic LDS,
+// 2w + 1 + 2*kBiasPad floats per wave); per 32-key sub-tile and score element, the 32
+// lanes of one lane half hit 32 distinct offsets, so the adds are free of conflicts and
+// their order is fixed.  The work-group's sum over its waves goes to ws_db.
+template <bool kCausal, bool kBias, bool kRandom, bool kBiasGrad = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dq_kernel(const BwdParams p) {
+    static_assert(!kBiasGrad || kBias, "the table gradient needs the table");
+    extern __shared__ float db_lds[];
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ uint64_t band_mask[kBwdMaskRing];
     __shared__ uint64_t glob_mask[kBwdMaxGlobalStages];
@@ -490,6 +497,16 @@ void bwd_dq_kernel(const BwdParams p) {
     const int gcnt = causal ? count_le(glob_abs, ng, row) : 0;
     Lanes lo;
     lane_setup(lo, lane);
+    // Per-wave sums of dS per window offset (kBiasGrad): offset m at db_acc[m + w], with
+    // kBiasPad slack entries on both sides for the offsets of masked pairs.
+    const int db_len = 2 * w + 1 + 2 * kBiasPad;
+    float* db_acc = db_lds + wv * db_len + kBiasPad;
+    bool row_is_global = false;
+    if (kBiasGrad) {
+        for (int i = lane; i < db_len; i += 64) db_lds[wv * db_len + i] = 0.f;
+        const int vr = qv - r0;
+        row_is_global = qv < Lr && ((row_glob[vr >> 5] >> (vr & 31)) & 1u);
+    }
     uint64_t inv_next = 0ull;
     if (n_st > 0) inv_next = issue(0);
     wait_vmcnt<0>();
@@ -541,11 +558,30 @@ void bwd_dq_kernel(const BwdParams p) {
             const f32x16 dp = prod(slot + kTileB, sub, lo, dop, f32x16{});  // dO.V
             float ds[16];
             for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * (dp[i] - my_d);
+            if (kBiasGrad && !gstage && !rstage) {
+                // element i of this lane: offset m = bbase - w + kc_of(i), at db_acc[m + w];
+                // global rows get no bias
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    if (h2 == half)
+                        for (int i = 0; i < 16; ++i)
+                            __hip_atomic_fetch_add(db_acc + bbase + kc_of(i), row_is_global ? 0.f : ds[i],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
             Frag f;
             to_frag(ds, f);
             TOp tk;
             load_t(tk, slot, sub, lo);
             acc_t(tk, f, acc);
+        }
+    }
+    if (kBiasGrad) {  // this tile's sums per offset, waves added in order
+        __syncthreads();
+        float* dst = p.ws_db + ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * (2 * w + 1);
+        for (int m = tid; m < 2 * w + 1; m += kThreads) {
+            float sum = 0.f;
+            for (int x = 0; x < kWaves; ++x) sum += db_lds[x * db_len + kBiasPad + m];
+            dst[m] = sum;
         }
     }
     if (qv < Lr) {
@@ -979,6 +1015,15 @@ hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
+    if (p.dbias) {  // position-bias table gradient: per-wave offset sums in dynamic LDS
+        const unsigned shm = kWaves * (2 * p.w + 1 + 2 * kBiasPad) * sizeof(float);
+        if (p.rnd) {
+            if (p.causal) return launch_kernel_shm(bwd_dq_kernel<true, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+            return launch_kernel_shm(bwd_dq_kernel<false, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+        }
+        if (p.causal) return launch_kernel_shm(bwd_dq_kernel<true, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+        return launch_kernel_shm(bwd_dq_kernel<false, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+    }
 #define LF_DQ(C, Bi, R) launch_kernel(bwd_dq_kernel<C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
 #define LF_DQ_R(C, Bi) \
     if (p.rnd) LF_DQ(C, Bi, true); else LF_DQ(C, Bi, false)
@@ -1016,6 +1061,34 @@ hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s) {
     else
         launch_kernel(bwd_dkv_kernel<false, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
     return hipGetLastError();
+}
+
+// dbias[h][m] = sum over sequences b and the existing tiles t of head h (in that order)
+// of ws_db[b*H + h][t][m]: one thread per (h, m).  The table has 2*bias_w + 1 entries;
+// the kernels ran with w = min(bias_w, L), and the offsets beyond that (no pair has
+// them) get 0.
+__global__ __launch_bounds__(256) void bwd_dbias_kernel(const BwdParams p) {
+    const int h = blockIdx.y, n = 2 * p.w + 1;
+    const int m = blockIdx.x * 256 + threadIdx.x;
+    if (m >= 2 * p.bias_w + 1) return;
+    const int mm = m - (p.bias_w - p.w);  // entry in the per-tile sums
+    float sum = 0.f;
+    if (mm >= 0 && mm < n) {
+        const int dil = p.dil[h], L = p.L;
+        const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+        for (int b = 0; b < p.B; ++b) {
+            const float* src = p.ws_db + (size_t)(b * p.H + h) * p.tiles_per_head * n + mm;
+            for (int t = 0; t < p.tiles_per_head; ++t)
+                if (tile_exists(t, tpr, dil, L, kRowsPerBlock)) sum += src[(size_t)t * n];
+        }
+    }
+    p.dbias[(size_t)h * (2 * p.bias_w + 1) + m] = sum;
+}
+
+hipError_t launch_bwd_dbias(const BwdParams& p, hipStream_t s) {
+    if (!p.dbias || p.H <= 0) return hipSuccess;
+    const int n = 2 * p.bias_w + 1;
+    return launch_kernel(bwd_dbias_kernel, dim3((n + 255) / 256, p.H), dim3(256), s, p);
 }
 
 hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s) {

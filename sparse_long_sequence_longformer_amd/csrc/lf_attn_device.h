@@ -210,15 +210,19 @@ __device__ __forceinline__ int count_le(const int* pos, int n, int x) {
 // Launch a kernel on stream s, with the timing events of the launch in progress if
 // there are any (see LaunchEvents).
 template <class K, class... A>
-hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, A... args) {
+hipError_t launch_kernel_shm(K kernel, dim3 grid, dim3 block, unsigned shm, hipStream_t s, A... args) {
     LaunchEvents& ev = launch_events();
     if (ev.start) {
         ev.used = true;
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, s, ev.start, ev.stop, 0, args...);
     } else {
-        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+        hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
     }
     return hipGetLastError();
+}
+template <class K, class... A>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, A... args) {
+    return launch_kernel_shm(kernel, grid, block, 0, s, args...);
 }
 
 }  // namespace

@@ -116,6 +116,11 @@ struct BwdParams {
     // [B*H][n_gblk*32][64]: dK and dV of each global key from its own tile
     float* ws_dkg;
     float* ws_dvg;
+    // Gradient of the relative position bias table (dbias != nullptr): each dQ work-group
+    // writes its sums of dS per window offset to ws_db [B*H][tiles_per_head][2w+1]; the
+    // reduction kernel adds them up per head into dbias [H][2w+1].
+    float* ws_db;
+    float* dbias;
     int B, H, L, w;
     int n_g;
     int n_gblk;
@@ -142,5 +147,6 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s);  // dk_g, dv_g (sep only)
 hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dbias(const BwdParams& p, hipStream_t s);  // dbias (only with p.dbias)
 
 }  // namespace lf

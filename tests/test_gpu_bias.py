@@ -214,3 +214,73 @@ def test_bias_layer():
     moved = np.abs(lorc.layer_forward(x, W, H, w, dil, G) - ref).max()
     log(f"  bias moves the layer output by {moved:.3e}")
     assert moved > 10 * TOL_MAX
+
+
+# Gradient of the table (lf_attn_backward_bias) against the oracle's, with the bars of
+# the other gradients (relative to the reference's own scale); dq, dk, dv must equal
+# those of the plain backward bit for bit (the table gradient only adds sums).
+DBIAS_CASES = BWD_CASES + [
+    ("qa_like_1500", 2, 2, 1500, 256, [1, 2], list(range(16)), [1500, 900], False, 1.0),
+    ("max_w_2300", 1, 1, 2300, 1024, [1], [100], None, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", DBIAS_CASES, ids=[c[0] for c in DBIAS_CASES])
+def test_bias_table_gradient(case):
+    from sparse_long_sequence_longformer_amd import binding
+
+    name, B, H, L, w, dil, G, lens, causal, scale = case
+    log(f"case bias table gradient {name}: B={B} H={H} L={L} w={w} dil={dil} causal={causal} scale={scale}")
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=len(name) + 600)
+    do = _dout(B, H, L, len(name) + 600)
+    tab = _table(H, w, len(name) + 2, scale)
+    pad = _pad_from_lengths(B, L, lens)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    bd = torch.from_numpy(tab).to("cuda")
+    out, lse = binding.forward_lse(qd, kd, vd, w, dil, G, _padd(pad), causal=causal, bias=bd)
+    dq, dk, dv, db = binding.backward(qd, kd, vd, out, dod, lse, w, dil, G, _padd(pad), causal=causal, bias=bd,
+                                      dbias=True)
+    pq, pk, pv = binding.backward(qd, kd, vd, out, dod, lse, w, dil, G, _padd(pad), causal=causal, bias=bd)
+    db2 = torch.full_like(db, float("nan"))
+    binding.backward(qd, kd, vd, out, dod, lse, w, dil, G, _padd(pad), causal=causal, bias=bd, dbias=db2)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, pq) and torch.equal(dk, pk) and torch.equal(dv, pv)
+    assert torch.equal(db, db2), "table gradient differs between two calls"
+    ref = orc.attention_bias_grad(q, k, v, do, w, dil, G, pad, causal=causal, bias=tab)
+    _compare_grad(db.cpu(), ref, f"{name} dbias")
+
+
+def test_bias_table_gradient_random_blocks():
+    """Pairs that enter through a random block carry no bias and add nothing."""
+    from sparse_long_sequence_longformer_amd import binding
+    from sparse_long_sequence_longformer_amd.workloads import make_random_blocks
+
+    B, H, L, w, G = 2, 2, 640, 40, [0, 333]
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=610)
+    do = _dout(B, H, L, 610)
+    tab = _table(H, w, 11, 2.0)
+    pad = _pad_from_lengths(B, L, [640, 500])
+    rnd = make_random_blocks(H, L, 3, seed=12)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    bd = torch.from_numpy(tab).to("cuda")
+    for causal in (False, True):
+        out, lse = binding.forward_lse(qd, kd, vd, w, [1, 1], G, _padd(pad), causal=causal, bias=bd, rand=rnd)
+        *_, db = binding.backward(qd, kd, vd, out, dod, lse, w, [1, 1], G, _padd(pad), causal=causal, bias=bd,
+                                  rand=rnd, dbias=True)
+        torch.cuda.synchronize()
+        ref = orc.attention_bias_grad(q, k, v, do, w, [1, 1], G, pad, causal=causal, bias=tab, rand=rnd)
+        _compare_grad(db.cpu(), ref, f"random causal={causal} dbias")
+
+
+def test_bias_table_gradient_needs_table():
+    from sparse_long_sequence_longformer_amd import binding
+
+    B, H, L, w = 1, 1, 200, 10
+    q, k, v = make_custom(B, H, L, dtype="bf16", seed=620)
+    qd, kd, vd = to_dev(q, k, v)
+    out, lse = binding.forward_lse(qd, kd, vd, w, [1], [])
+    with pytest.raises(binding.LfAttnError):
+        binding.backward(qd, kd, vd, out, out, lse, w, [1], [], dbias=True)
+    with pytest.raises(ValueError):
+        binding.backward(qd, kd, vd, out, out, lse, w, [1], [], bias=torch.zeros(H, 2 * w + 1, device="cuda"),
+                         dbias=torch.zeros(H, 2 * w, device="cuda"))
