@@ -169,14 +169,16 @@ struct Bf16 {
     }
 
     // seed + S^T (32 keys x 32 queries) of sub-tile `sub` (keys 32*sub .. 32*sub+31 of
-    // the stage).
+    // the stage).  The four K operand reads go out before the first product (left to
+    // itself the scheduler reuses one register quad and waits for each read in turn).
     __device__ __forceinline__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
         const char* base = slot + sub * 32 * kRowBytes;
+        bf16x8 a[4];
+        for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(base + lo.k[kb]);
         f32x16 acc = seed;
-        for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + lo.k[kb]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[kb], acc, 0, 0, 0);
-        }
+        for (int kb = 0; kb < 4; ++kb) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], q.v[kb], acc, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         return acc;
     }
 
