@@ -173,17 +173,19 @@ lf_status lf_attn_forward_lse(lf_attn_t h, const void* q, const void* k, const v
  *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . V_j - dO_i . O_i),
  *   dQ_i = sum_j dS_ij K_j / sqrt(d_h),   dK_j = sum_i dS_ij Q_i / sqrt(d_h).
  *
- * q, k, v, out, dout : DEVICE [B][H][L][d_h] bf16, 16-byte aligned; out and lse as
- *                      written by lf_attn_forward_lse for the same q, k, v and
- *                      pattern (P is recomputed from them).
+ * q, k, v, out, dout : DEVICE [B][H][L][d_h] of the handle's dtype (bf16 or fp32),
+ *                      16-byte aligned; out and lse as written by
+ *                      lf_attn_forward_lse for the same q, k, v and pattern (P is
+ *                      recomputed from them).
  * lse                : DEVICE float32 [B][H][L], 4-byte aligned.
- * dq, dk, dv         : DEVICE [B][H][L][d_h] bf16 outputs, 16-byte aligned, not
- *                      overlapping any input or each other.  Padded keys get
- *                      dk = dv = 0; rows with no key get dq = 0.
- * Other arguments: as lf_attn_forward.  bf16 handles only (LF_ERR_UNSUPPORTED for
- * fp32).  The handle grows a second device workspace (hipMalloc) for row statistics
- * and the partial sums of global rows and keys; calls on one handle must not overlap.
- * The result is deterministic (fixed summation order, no atomics).
+ * dq, dk, dv         : DEVICE [B][H][L][d_h] outputs of the handle's dtype, 16-byte
+ *                      aligned, not overlapping any input or each other.  Padded keys
+ *                      get dk = dv = 0; rows with no key get dq = 0.
+ * Other arguments: as lf_attn_forward.  Both dtypes run the same kernels (bf16: bf16
+ * MFMA products with fp32 accumulation; fp32: fp32 MFMA products).  The handle grows a
+ * second device workspace (hipMalloc) for row statistics and the partial sums of
+ * global rows and keys; calls on one handle must not overlap.  The result is
+ * deterministic (fixed summation order, no atomics).
  */
 lf_status lf_attn_backward(lf_attn_t h, const void* q, const void* k, const void* v, const void* out,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -271,8 +273,8 @@ lf_status lf_attn_forward_global_proj_lse(lf_attn_t h, const void* q, const void
  * dk_g, dv_g of every key.  dq of a global row and dq_g of any other row are written
  * as zero; dk_g, dv_g of padded keys are zero.
  *
- * q_g, k_g, v_g : DEVICE bf16 [B][H][L][d_h], as passed to the forward.
- * dq_g, dk_g, dv_g : DEVICE bf16 [B][H][L][d_h] outputs, 16-byte aligned, overlapping
+ * q_g, k_g, v_g : DEVICE [B][H][L][d_h] of the handle's dtype, as passed to the forward.
+ * dq_g, dk_g, dv_g : DEVICE [B][H][L][d_h] outputs of the handle's dtype, 16-byte aligned, overlapping
  *                    no input and no other gradient.
  * out and lse: as returned by lf_attn_forward_global_proj_lse for the same inputs
  * (not lse from lf_attn_forward_lse: the global rows' normaliser differs).

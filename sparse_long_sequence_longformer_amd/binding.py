@@ -556,7 +556,8 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
              dv=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None, dbias=None):
     """Gradients (dq, dk, dv) of the forward for the upstream gradient ``dout``.
 
-    q, k, v, out, dout: contiguous bf16 device tensors [B, H, L, 64]; ``out`` and
+    q, k, v, out, dout: contiguous device tensors [B, H, L, 64], all bf16 or all
+    float32 (the handle's dtype); ``out`` and
     ``lse`` as returned by ``forward_lse`` for the same inputs and pattern (and bias).
     dbias: with a position bias table in use, True (or a float32 device tensor
     [H, 2w + 1] to write into) also returns the gradient of the table, summed over
@@ -564,8 +565,6 @@ def backward(q, k, v, out, dout, lse, w: int, dil, global_idx=None, key_pad_mask
     """
     import torch
 
-    if q.dtype != torch.bfloat16:
-        raise TypeError("the backward supports bfloat16 tensors only")
     B, H, L, d_h, dil, global_idx, pad_ptr, _, h, stream = _marshal(
         q, [("k", k), ("v", v), ("out", out), ("dout", dout)], w, dil, global_idx, key_pad_mask, out, handle,
         causal, rand is not None)
@@ -601,13 +600,11 @@ def backward_global_proj(q, k, v, q_g, k_g, v_g, out, dout, lse, w: int, dil, gl
                          grads=None, handle: LfAttn | None = None, causal: bool = False, bias=None, rand=None):
     """Gradients (dq, dk, dv, dq_g, dk_g, dv_g) of ``forward_global_proj`` for ``dout``.
 
-    All tensors contiguous bf16 [B, H, L, 64] on the device; ``out`` and ``lse`` as
+    All tensors contiguous [B, H, L, 64] on the device, all bf16 or all float32; ``out`` and ``lse`` as
     returned by ``forward_global_proj_lse``.  grads: six preallocated outputs, or None.
     """
     import torch
 
-    if q.dtype != torch.bfloat16:
-        raise TypeError("the backward supports bfloat16 tensors only")
     B, H, L, d_h, dil, global_idx, pad_ptr, _, h, stream = _marshal(
         q, [("k", k), ("v", v), ("q_g", q_g), ("k_g", k_g), ("v_g", v_g), ("out", out), ("dout", dout)], w, dil,
         global_idx, key_pad_mask, out, handle, causal, rand is not None)

@@ -648,7 +648,6 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     const bool sep = qg || kg || vg || dqg || dkg || dvg;
     if (sep && !(qg && kg && vg && dqg && dkg && dvg))
         return fail(h, LF_ERR_INVALID_ARG, "q_g, k_g, v_g, dq_g, dk_g and dv_g must all be non-null");
-    if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "the backward supports bf16 handles only");
     if (want_dbias && !dbias) return fail(h, LF_ERR_INVALID_ARG, "dbias must be non-null");
     if (want_dbias && !h->bias)
         return fail(h, LF_ERR_INVALID_ARG, "no position bias table is set on the handle (its gradient was asked for)");
@@ -720,6 +719,7 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;
     p.bias = h->bias;
     p.bias_w = h->bias_w;
+    p.dtype = h->dtype;
 
     // Workspace: three row-statistic arrays, then the global partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");

@@ -1,5 +1,6 @@
 // gfx950 (MI355X) kernels of the Longformer window + global attention backward
-// (bf16 tensors, fp32 accumulation).
+// (bf16 tensors with fp32 accumulation, or fp32 tensors: one set of kernels on
+// element traits).
 //
 // For O = P V with P the row softmax of S = Q K^T / sqrt(d_h) over each row's key
 // set (the forward's pattern: page "基于自注意力机制的长文本建模算法：Longformer详解"
@@ -32,13 +33,16 @@
 // bwd_merge_kernel sums the partials of each global row and key in tile order and
 //                  writes dQ of the global rows and dK, dV of the global keys.
 //
-// Every product is a 32 x 32 tile on the matrix cores (v_mfma_f32_32x32x16_bf16).
+// Every product is a 32 x 32 tile on the matrix cores (v_mfma_f32_32x32x16_bf16 for
+// bf16, v_mfma_f32_32x32x2_f32 for fp32).
 // Row-owned: S^T = K Q^T and dP^T = V dO^T with one query per lane, dQ^T += K^T dS^T.
 // Key-owned: S = Q K^T and dP = dO V^T with one key per lane, dV^T += dO^T P and
 // dK^T += Q^T dS.  The staged tiles (K and V, or Q and dO) are row-major in LDS with
 // the 16-byte-chunk XOR swizzle and are read both ways: 128-bit row reads for the
 // first operand of the score products and transposed reads (ds_read_b64_tr_b16) for
 // the first operand of the gradient products.
+
+#include <type_traits>
 
 #include "lf_attn_device.h"
 
@@ -53,128 +57,246 @@ constexpr int kBwdMaskWindow = 64;
 constexpr int kBwdMaskRing = 2 * kBwdMaskWindow;
 constexpr int kBwdMaxGlobalStages = LF_MAX_GLOBALS / kStageKeys;
 
-// One stage: tile A (64 rows x 128 B), tile B (same), 64 floats of lse2, 64 of D.
-constexpr int kRowB = 128;
-constexpr int kTileB = kStageKeys * kRowB;  // 8 KiB
-constexpr int kLseOff = 2 * kTileB;
-constexpr int kDOff = kLseOff + 256;
-constexpr int kStageB = kDOff + 256;
-
-struct Op { bf16x8 v[4]; };      // B operand of a score product: lane (n, h2) holds d = 16*kb + 8*h2 + j
-struct Frag { bf16x8 v[2]; };    // B operand of a gradient product (weights or dS)
-struct TOp { bf16x8 v[2][2]; };  // transposed A operand [db][kb]
-
-__device__ __forceinline__ void load_op(Op& o, const uint16_t* row, int h2) {
-    if (!row) row = reinterpret_cast<const uint16_t*>(g_zero_row);
-    for (int kb = 0; kb < 4; ++kb)
-        o.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
-}
-__device__ __forceinline__ void scale_op(Op& o) {
-    for (int kb = 0; kb < 4; ++kb) {
-        const f32x8 f = __builtin_convertvector(o.v[kb], f32x8);
-        o.v[kb] = __builtin_convertvector(f * kScaleLog2, bf16x8);
-    }
-}
-
 // 4 bytes per lane from global memory into LDS at lds_base + 4 * lane (see dma16).
 __device__ __forceinline__ void dma4(const void* src, char* lds_base) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory", "m0");
 }
 
-// Rows of two tensors into tiles A and B of a stage, both with the K swizzle: wave
-// wv copies 1-KiB blocks 2*wv, 2*wv+1 (8 rows each).  row_of(kk) is the source row
-// of stage row kk, or -1 for a zero row.
-template <class RowOf>
-__device__ __forceinline__ void dma_tiles(char* slot, const uint16_t* A, const uint16_t* Bt, RowOf row_of, int wv,
-                                          int lane) {
-    const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
-    for (int u = 0; u < 2; ++u) {
-        const int blk = 2 * wv + u;
-        const int row = 8 * blk + (lane >> 3), cl = lane & 7;
-        const int src = row_of(row);
-        const int c = 8 * (cl ^ swz_k(row));
-        dma16((src >= 0 ? A + (size_t)src * 64 : zero) + c, slot + blk * 1024);
-        dma16((src >= 0 ? Bt + (size_t)src * 64 : zero) + c, slot + kTileB + blk * 1024);
+// Element traits of the backward kernels.  One stage holds tile A (64 rows), tile B
+// (64 rows), 64 floats of lse2 and 64 of D; tile rows are row-major with the K
+// swizzle of 16-byte chunks and are read both ways: by rows for the first operand of
+// the score products (prod) and by columns for the first operand of the gradient
+// products (load_t / acc_t).  Accumulator element i of lane-half h2 of a score product
+// belongs to tile row 32*sub + key_local(i, h2) in both.
+
+// bf16 tensors: v_mfma_f32_32x32x16_bf16, transposed reads with ds_read_b64_tr_b16.
+struct BBf16 {
+    using Elem = uint16_t;
+    static constexpr int kRowB = 128;
+    static constexpr int kTileB = kStageKeys * kRowB;  // 8 KiB
+    static constexpr int kLseOff = 2 * kTileB;
+    static constexpr int kDOff = kLseOff + 256;
+    static constexpr int kStageB = kDOff + 256;
+    static constexpr int kWavesPerEU = 3;
+
+    struct Op { bf16x8 v[4]; };      // B operand of a score product: lane (n, h2) holds d = 16*kb + 8*h2 + j
+    struct Frag { bf16x8 v[2]; };    // B operand of a gradient product (weights or dS)
+    struct TOp { bf16x8 v[2][2]; };  // transposed A operand [db][kb]
+
+    __device__ __forceinline__ static void load_op(Op& o, const Elem* row, int h2) {
+        if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
+        for (int kb = 0; kb < 4; ++kb)
+            o.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
     }
+    __device__ __forceinline__ static void scale_op(Op& o) {
+        for (int kb = 0; kb < 4; ++kb) {
+            const f32x8 f = __builtin_convertvector(o.v[kb], f32x8);
+            o.v[kb] = __builtin_convertvector(f * kScaleLog2, bf16x8);
+        }
+    }
+
+    // Rows of two tensors into tiles A and B of a stage: wave wv copies 1-KiB blocks
+    // 2*wv, 2*wv+1 (8 rows each).  row_of(kk) is the source row of stage row kk, or -1
+    // for a zero row.
+    template <class RowOf>
+    __device__ __forceinline__ static void dma_tiles(char* slot, const Elem* A, const Elem* Bt, RowOf row_of, int wv,
+                                                     int lane) {
+        const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
+        for (int u = 0; u < 2; ++u) {
+            const int blk = 2 * wv + u;
+            const int row = 8 * blk + (lane >> 3), cl = lane & 7;
+            const int src = row_of(row);
+            const int c = 8 * (cl ^ swz_k(row));
+            dma16((src >= 0 ? A + (size_t)src * 64 : zero) + c, slot + blk * 1024);
+            dma16((src >= 0 ? Bt + (size_t)src * 64 : zero) + c, slot + kTileB + blk * 1024);
+        }
+    }
+
+    // Per-lane LDS byte offsets.  nk: 128-bit row reads (row sigma(M), chunk
+    // (2*kb + h2) ^ swz_k(row)).  tr: transposed reads; within each 16-lane group, lane i
+    // addresses row 8*h2 + i/4 (+ 4*t + 16*kb + 32*sub), columns 32*db + 16*g1 + 4*(i%4)
+    // .. +3, and receives one column of four consecutive rows.  Rows 8*h2 + i/4 have bit
+    // 2 clear, so adding 4 (t = 1) keeps swz_k; multiples of 16 keep it as well.
+    struct Lanes { int nk[4]; int tr[2]; };
+    __device__ __forceinline__ static void lane_setup(Lanes& lo, int lane) {
+        const int row = sigma(lane & 31), h2 = lane >> 5;
+        for (int kb = 0; kb < 4; ++kb) lo.nk[kb] = row * kRowB + (((2 * kb + h2) ^ swz_k(row)) << 4);
+        const int g1 = (lane >> 4) & 1, i = lane & 15;
+        const int vrow = 8 * h2 + (i >> 2);
+        for (int db = 0; db < 2; ++db) {
+            const int chunk = 4 * db + 2 * g1 + ((i & 3) >> 1);
+            lo.tr[db] = vrow * kRowB + ((chunk ^ swz_k(vrow)) << 4) + 8 * (i & 1);
+        }
+    }
+
+    // seed + (rows 32*sub .. +31 of the tile) x (lane operand).
+    __device__ __forceinline__ static f32x16 prod(const char* tile, int sub, const Lanes& lo, const Op& b,
+                                                  const f32x16& seed) {
+        const char* base = tile + sub * 32 * kRowB;
+        f32x16 acc = seed;
+        for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + lo.nk[kb]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.v[kb], acc, 0, 0, 0);
+        }
+        return acc;
+    }
+
+    __device__ __forceinline__ static void to_frag(const float* x, Frag& f) {
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x8 t;
+            for (int j = 0; j < 8; ++j) t[j] = x[8 * kb + j];
+            f.v[kb] = __builtin_convertvector(t, bf16x8);
+        }
+    }
+
+    // Transposed operand of rows 32*sub .. +31 of a tile: lane l holds column 32*db + l%32
+    // of rows 16*kb + 8*h2 + 0..7.
+    __device__ __forceinline__ static void load_t(TOp& t, const char* tile, int sub, const Lanes& lo) {
+        const char* base = tile + sub * 32 * kRowB;
+        for (int db = 0; db < 2; ++db)
+            for (int kb = 0; kb < 2; ++kb) {
+                const char* a = base + lo.tr[db] + 16 * kb * kRowB;
+                const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a));
+                const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a + 4 * kRowB));
+                t.v[db][kb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+    }
+    __device__ __forceinline__ static void acc_t(const TOp& t, const Frag& f, f32x16* acc) {
+        for (int kb = 0; kb < 2; ++kb)
+            for (int db = 0; db < 2; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.v[db][kb], f.v[kb], acc[db], 0, 0, 0);
+    }
+
+    __device__ __forceinline__ static uint32_t pack_bf16(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    }
+    // Accumulator element (db, i) of lane-half h2 is column 32*db + 8*(i/4) + 4*h2 + i%4.
+    __device__ __forceinline__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+        for (int db = 0; db < 2; ++db)
+            for (int q = 0; q < 4; ++q) {
+                const float a = o[db][4 * q] * scale, b = o[db][4 * q + 1] * scale;
+                const float c = o[db][4 * q + 2] * scale, d = o[db][4 * q + 3] * scale;
+                const u32x2 w = {pack_bf16(a, b), pack_bf16(c, d)};
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * h2) = w;
+            }
+    }
+    __device__ __forceinline__ static Elem from_float(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+};
+
+// fp32 tensors: v_mfma_f32_32x32x2_f32 (step t of a score product pairs lane-half h2
+// with d = 32*h2 + t; step u of a gradient product with tile row key_local(u, h2)),
+// single-float column reads for the transposed operand.
+struct BF32 {
+    using Elem = float;
+    static constexpr int kRowB = 256;
+    static constexpr int kTileB = kStageKeys * kRowB;  // 16 KiB
+    static constexpr int kLseOff = 2 * kTileB;
+    static constexpr int kDOff = kLseOff + 256;
+    static constexpr int kStageB = kDOff + 256;
+    static constexpr int kWavesPerEU = 2;
+
+    struct Op { float v[32]; };
+    struct Frag { float v[16]; };
+    struct TOp { const char* base; };  // rows 32*sub .. of the tile, read inside acc_t
+    struct Lanes { int nk; int sw; int h2; int col; };
+
+    __device__ __forceinline__ static void load_op(Op& o, const Elem* row, int h2) {
+        if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
+        for (int t4 = 0; t4 < 8; ++t4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4);
+            for (int e = 0; e < 4; ++e) o.v[4 * t4 + e] = x[e];
+        }
+    }
+    __device__ __forceinline__ static void scale_op(Op& o) {
+        for (int i = 0; i < 32; ++i) o.v[i] *= kScaleLog2;
+    }
+
+    // Wave wv copies 1-KiB blocks 4*wv .. 4*wv+3 of each tile (4 rows each).
+    template <class RowOf>
+    __device__ __forceinline__ static void dma_tiles(char* slot, const Elem* A, const Elem* Bt, RowOf row_of, int wv,
+                                                     int lane) {
+        const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
+        for (int u = 0; u < 4; ++u) {
+            const int blk = 4 * wv + u;
+            const int row = 4 * blk + (lane >> 4), cl = lane & 15;
+            const int src = row_of(row);
+            const int c = 4 * (cl ^ swz_k(row));
+            dma16((src >= 0 ? A + (size_t)src * 64 : zero) + c, slot + blk * 1024);
+            dma16((src >= 0 ? Bt + (size_t)src * 64 : zero) + c, slot + kTileB + blk * 1024);
+        }
+    }
+
+    __device__ __forceinline__ static void lane_setup(Lanes& lo, int lane) {
+        const int row = sigma(lane & 31);
+        lo.nk = row * kRowB;
+        lo.sw = swz_k(row);
+        lo.h2 = lane >> 5;
+        lo.col = lane & 31;
+    }
+
+    __device__ __forceinline__ static f32x16 prod(const char* tile, int sub, const Lanes& lo, const Op& b,
+                                                  const f32x16& seed) {
+        const char* base = tile + sub * 32 * kRowB + lo.nk;
+        f32x16 acc = seed;
+        for (int t4 = 0; t4 < 8; ++t4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(base + (((8 * lo.h2 + t4) ^ lo.sw) << 4));
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b.v[4 * t4 + e], acc, 0, 0, 0);
+        }
+        return acc;
+    }
+
+    __device__ __forceinline__ static void to_frag(const float* x, Frag& f) {
+        for (int i = 0; i < 16; ++i) f.v[i] = x[i];
+    }
+
+    __device__ __forceinline__ static void load_t(TOp& t, const char* tile, int sub, const Lanes&) {
+        t.base = tile + sub * 32 * kRowB;
+    }
+    // acc[db] (column 32*db + l%32 of the tile, lane's column of f) += sum over the 32
+    // rows of the sub-tile: step u takes row key_local(u, h2) for lane-half h2.
+    __device__ __forceinline__ static void acc_t(const TOp& t, const Frag& f, f32x16* acc, const Lanes& lo) {
+        for (int u = 0; u < 16; ++u) {
+            const int row = key_local(u, lo.h2);
+            const char* rb = t.base + row * kRowB + 4 * (lo.col & 3);
+            for (int db = 0; db < 2; ++db) {
+                const int c = 32 * db + lo.col;
+                const float a = *reinterpret_cast<const float*>(rb + (((c >> 2) ^ swz_k(row)) << 4));
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.v[u], acc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+        for (int db = 0; db < 2; ++db)
+            for (int q = 0; q < 4; ++q) {
+                f32x4 t;
+                for (int j = 0; j < 4; ++j) t[j] = o[db][4 * q + j] * scale;
+                *reinterpret_cast<f32x4*>(row + 32 * db + 8 * q + 4 * h2) = t;
+            }
+    }
+    __device__ __forceinline__ static Elem from_float(float x) { return x; }
+};
+
+// Gradient product through the traits (the fp32 form also needs the lane layout).
+template <class T>
+__device__ __forceinline__ void acc_t(const typename T::TOp& t, const typename T::Frag& f, f32x16* acc,
+                                      const typename T::Lanes& lo) {
+    if constexpr (std::is_same_v<T, BF32>)
+        T::acc_t(t, f, acc, lo);
+    else
+        T::acc_t(t, f, acc);
 }
+
 // lse2 and D of the 64 stage rows (one wave; zero for row -1).
-template <class RowOf>
+template <class T, class RowOf>
 __device__ __forceinline__ void dma_floats(char* slot, const float* lse2, const float* dsum, RowOf row_of, int lane) {
     const int src = row_of(lane);
     const float* zero = reinterpret_cast<const float*>(g_zero_row);
-    dma4(src >= 0 ? lse2 + src : zero, slot + kLseOff);
-    dma4(src >= 0 ? dsum + src : zero, slot + kDOff);
+    dma4(src >= 0 ? lse2 + src : zero, slot + T::kLseOff);
+    dma4(src >= 0 ? dsum + src : zero, slot + T::kDOff);
 }
 
-// Per-lane LDS byte offsets.  nk: 128-bit row reads (row sigma(M), chunk
-// (2*kb + h2) ^ swz_k(row)).  tr: transposed reads; within each 16-lane group, lane i
-// addresses row 8*h2 + i/4 (+ 4*t + 16*kb + 32*sub), columns 32*db + 16*g1 + 4*(i%4)
-// .. +3, and receives one column of four consecutive rows.  Rows 8*h2 + i/4 have bit
-// 2 clear, so adding 4 (t = 1) keeps swz_k; multiples of 16 keep it as well.
-struct Lanes { int nk[4]; int tr[2]; };
-__device__ __forceinline__ void lane_setup(Lanes& lo, int lane) {
-    const int row = sigma(lane & 31), h2 = lane >> 5;
-    for (int kb = 0; kb < 4; ++kb) lo.nk[kb] = row * kRowB + (((2 * kb + h2) ^ swz_k(row)) << 4);
-    const int g1 = (lane >> 4) & 1, i = lane & 15;
-    const int vrow = 8 * h2 + (i >> 2);
-    for (int db = 0; db < 2; ++db) {
-        const int chunk = 4 * db + 2 * g1 + ((i & 3) >> 1);
-        lo.tr[db] = vrow * kRowB + ((chunk ^ swz_k(vrow)) << 4) + 8 * (i & 1);
-    }
-}
-
-// seed + (rows 32*sub .. +31 of the tile) x (lane operand): element i of lane-half h2
-// belongs to tile row 32*sub + key_local(i, h2).
-__device__ __forceinline__ f32x16 prod(const char* tile, int sub, const Lanes& lo, const Op& b, const f32x16& seed) {
-    const char* base = tile + sub * 32 * kRowB;
-    f32x16 acc = seed;
-    for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + lo.nk[kb]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.v[kb], acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ void to_frag(const float* x, Frag& f) {
-    for (int kb = 0; kb < 2; ++kb) {
-        f32x8 t;
-        for (int j = 0; j < 8; ++j) t[j] = x[8 * kb + j];
-        f.v[kb] = __builtin_convertvector(t, bf16x8);
-    }
-}
-
-// Transposed operand of rows 32*sub .. +31 of a tile: lane l holds column 32*db + l%32
-// of rows 16*kb + 8*h2 + 0..7.
-__device__ __forceinline__ void load_t(TOp& t, const char* tile, int sub, const Lanes& lo) {
-    const char* base = tile + sub * 32 * kRowB;
-    for (int db = 0; db < 2; ++db)
-        for (int kb = 0; kb < 2; ++kb) {
-            const char* a = base + lo.tr[db] + 16 * kb * kRowB;
-            const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a));
-            const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LF_LDS(s16x4, a + 4 * kRowB));
-            t.v[db][kb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-}
-__device__ __forceinline__ void acc_t(const TOp& t, const Frag& f, f32x16* acc) {
-    for (int kb = 0; kb < 2; ++kb)
-        for (int db = 0; db < 2; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.v[db][kb], f.v[kb], acc[db], 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-// Accumulator element (db, i) of lane-half h2 is column 32*db + 8*(i/4) + 4*h2 + i%4.
-__device__ __forceinline__ void store_row(uint16_t* row, int h2, const f32x16* o, float scale) {
-    for (int db = 0; db < 2; ++db)
-        for (int q = 0; q < 4; ++q) {
-            const float a = o[db][4 * q] * scale, b = o[db][4 * q + 1] * scale;
-            const float c = o[db][4 * q + 2] * scale, d = o[db][4 * q + 3] * scale;
-            const u32x2 w = {pack_bf16(a, b), pack_bf16(c, d)};
-            *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * h2) = w;
-        }
-}
 __device__ __forceinline__ void store_row_f32(float* row, int h2, const f32x16* o, float scale) {
     for (int db = 0; db < 2; ++db)
         for (int q = 0; q < 4; ++q) {
@@ -297,31 +419,44 @@ __device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int A, int 
 constexpr int kPrepRowsPerGroup = 4;
 constexpr int kPrepGroups = kThreads / 8;
 constexpr int kPrepRowsPerBlock = kPrepGroups * kPrepRowsPerGroup;
+template <class T>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
+    using Elem = typename T::Elem;
     __shared__ int gpos[LF_MAX_GLOBALS];  // this sequence's global positions, sorted
     const int L = p.L;
     const int nblk = (L + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
     const int bseq = bh / p.H, gofs = bseq * p.gstride;
     const int ng = p.gstride ? p.gcnt[bseq] : p.n_g;
-    const int c = threadIdx.x & 7;  // 16-byte chunk of a row
+    const int c = threadIdx.x & 7;  // eighth of a row
     const int pos0 = blk * kPrepRowsPerBlock + (threadIdx.x >> 3);
     const size_t off = (size_t)bh * L;
-    u32x4 o[kPrepRowsPerGroup], g[kPrepRowsPerGroup];
+    // a lane's eighth of a row: 16 bytes (bf16) or 32 bytes (fp32)
+    constexpr int kV = sizeof(Elem) == 2 ? 1 : 2;
+    u32x4 o[kPrepRowsPerGroup][kV], g[kPrepRowsPerGroup][kV];
     for (int k = 0; k < kPrepRowsPerGroup; ++k) {
         const int pos = pos0 + k * kPrepGroups;
         const size_t row = off + (pos < L ? pos : 0);
-        o[k] = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.o) + row * 64)[c];
-        g[k] = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.dout) + row * 64)[c];
+        for (int v = 0; v < kV; ++v) {
+            o[k][v] = reinterpret_cast<const u32x4*>(reinterpret_cast<const Elem*>(p.o) + row * 64)[kV * c + v];
+            g[k][v] = reinterpret_cast<const u32x4*>(reinterpret_cast<const Elem*>(p.dout) + row * 64)[kV * c + v];
+        }
     }
     for (int t = threadIdx.x; t < ng; t += kThreads) gpos[t] = p.g[gofs + t];
     __syncthreads();
     float mine = 0.f;  // the dot product of row c of this group (c < kPrepRowsPerGroup)
     for (int k = 0; k < kPrepRowsPerGroup; ++k) {
-        const f32x8 a = __builtin_convertvector(__builtin_bit_cast(bf16x8, o[k]), f32x8);
-        const f32x8 b = __builtin_convertvector(__builtin_bit_cast(bf16x8, g[k]), f32x8);
         float acc = 0.f;
-        for (int j = 0; j < 8; ++j) acc += a[j] * b[j];
+        if constexpr (kV == 1) {
+            const f32x8 a = __builtin_convertvector(__builtin_bit_cast(bf16x8, o[k][0]), f32x8);
+            const f32x8 b = __builtin_convertvector(__builtin_bit_cast(bf16x8, g[k][0]), f32x8);
+            for (int j = 0; j < 8; ++j) acc += a[j] * b[j];
+        } else {
+            for (int v = 0; v < kV; ++v) {
+                const f32x4 a = __builtin_bit_cast(f32x4, o[k][v]), b = __builtin_bit_cast(f32x4, g[k][v]);
+                for (int j = 0; j < 4; ++j) acc += a[j] * b[j];
+            }
+        }
         for (int m = 1; m < 8; m <<= 1) acc += __shfl_xor(acc, m);  // the row's eight lanes
         mine = c == k ? acc : mine;
     }
@@ -348,10 +483,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // 2w + 1 + 2*kBiasPad floats per wave); per 32-key sub-tile and score element, the 32
 // lanes of one lane half hit 32 distinct offsets, so the adds are free of conflicts and
 // their order is fixed.  The work-group's sum over its waves goes to ws_db.
-template <bool kCausal, bool kBias, bool kRandom, bool kBiasGrad = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+template <class T, bool kCausal, bool kBias, bool kRandom, bool kBiasGrad = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void bwd_dq_kernel(const BwdParams p) {
     static_assert(!kBiasGrad || kBias, "the table gradient needs the table");
+    using Elem = typename T::Elem;
+    constexpr int kStageB = T::kStageB, kTileB = T::kTileB;
     extern __shared__ float db_lds[];
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ uint64_t band_mask[kBwdMaskRing];
@@ -373,11 +510,11 @@ void bwd_dq_kernel(const BwdParams p) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
     const size_t off = (size_t)tl.bh * L * 64;
-    const uint16_t* Q = reinterpret_cast<const uint16_t*>(p.q) + off;
-    const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k) + off;
-    const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v) + off;
-    const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dout) + off;
-    uint16_t* dQ = reinterpret_cast<uint16_t*>(p.dq) + off;
+    const Elem* Q = reinterpret_cast<const Elem*>(p.q) + off;
+    const Elem* K = reinterpret_cast<const Elem*>(p.k) + off;
+    const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
+    const Elem* dO = reinterpret_cast<const Elem*>(p.dout) + off;
+    Elem* dQ = reinterpret_cast<Elem*>(p.dq) + off;
     const float* lse2 = p.lse2 + (size_t)tl.bh * L;
     const float* dsum = p.dsum + (size_t)tl.bh * L;
     const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
@@ -387,9 +524,9 @@ void bwd_dq_kernel(const BwdParams p) {
     const int qa = r0 + 32 * wv, qv = qa + (lane & 31);
     const bool rows_live = qa < Lr;
     const int row = r + qv * dil;
-    Op qop, dop;
-    load_op(qop, qv < Lr ? Q + (size_t)row * 64 : nullptr, h2);
-    load_op(dop, qv < Lr ? dO + (size_t)row * 64 : nullptr, h2);
+    typename T::Op qop, dop;
+    T::load_op(qop, qv < Lr ? Q + (size_t)row * 64 : nullptr, h2);
+    T::load_op(dop, qv < Lr ? dO + (size_t)row * 64 : nullptr, h2);
     const float my_l2 = qv < Lr ? lse2[row] : kPosInf;
     const float my_d = qv < Lr ? dsum[row] : 0.f;
 
@@ -426,17 +563,17 @@ void bwd_dq_kernel(const BwdParams p) {
         char* slot = ring + (s & 1) * kStageB;
         if (s < n_gst) {
             const int* src = glob_src + kStageKeys * s;
-            dma_tiles(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane);
+            T::dma_tiles(slot, K, V, [&](int kk) { return src[kk]; }, wv, lane);
         } else if (kRandom && s < n_lst) {
             const int j = s - n_gst, kb0 = kRandomBlock * rnd_block(j);
             const uint64_t inv = uniform64(rnd_inv[j]);
-            dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane);
+            T::dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane);
         } else {
             const int u = s - n_lst;
             const uint64_t inv = uniform64(band_invalid(u));
             const int ks = tl.stage_row(u);
             ks_next = ks;
-            dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
+            T::dma_tiles(slot, K, V, [&](int kk) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             return inv;
         }
         return 0ull;
@@ -495,8 +632,8 @@ void bwd_dq_kernel(const BwdParams p) {
 
     // One-sided variant: the global slots at or before this lane's row.
     const int gcnt = causal ? count_le(glob_abs, ng, row) : 0;
-    Lanes lo;
-    lane_setup(lo, lane);
+    typename T::Lanes lo;
+    T::lane_setup(lo, lane);
     // Per-wave sums of dS per window offset (kBiasGrad): offset m at db_acc[m + w], with
     // kBiasPad slack entries on both sides for the offsets of masked pairs.
     const int db_len = 2 * w + 1 + 2 * kBiasPad;
@@ -510,7 +647,7 @@ void bwd_dq_kernel(const BwdParams p) {
     uint64_t inv_next = 0ull;
     if (n_st > 0) inv_next = issue(0);
     wait_vmcnt<0>();
-    scale_op(qop);
+    T::scale_op(qop);
     // The score product is seeded with -lse2 (its exponentials are the weights); D is
     // subtracted after the dP product instead of seeding it, which keeps one fewer
     // 16-register vector live across the loop.
@@ -549,13 +686,13 @@ void bwd_dq_kernel(const BwdParams p) {
             }
             const bool interior = !gstage && !rstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
             const int mode = rstage ? 3 : (gstage ? 2 : (interior ? 0 : 1));
-            f32x16 s = prod(slot, sub, lo, qop, seed_s);  // scores - lse, base 2
+            f32x16 s = T::prod(slot, sub, lo, qop, seed_s);  // scores - lse, base 2
             const int bbase = kss + 8 * h2 - qv + w;
             if (kBias && !gstage && !rstage) add_bias(s, bias_lds + kBiasPad + bbase);
             const int goff = kStageKeys * t + 32 * sub + 8 * h2;
             mask_scores<kRandom>(s, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
                                  !causal ? 1 << 30 : (rstage ? w - bbase + 1 : gcnt - goff));
-            const f32x16 dp = prod(slot + kTileB, sub, lo, dop, f32x16{});  // dO.V
+            const f32x16 dp = T::prod(slot + kTileB, sub, lo, dop, f32x16{});  // dO.V
             float ds[16];
             for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * (dp[i] - my_d);
             if (kBiasGrad && !gstage && !rstage) {
@@ -568,11 +705,11 @@ void bwd_dq_kernel(const BwdParams p) {
                             __hip_atomic_fetch_add(db_acc + bbase + kc_of(i), row_is_global ? 0.f : ds[i],
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            Frag f;
-            to_frag(ds, f);
-            TOp tk;
-            load_t(tk, slot, sub, lo);
-            acc_t(tk, f, acc);
+            typename T::Frag f;
+            T::to_frag(ds, f);
+            typename T::TOp tk;
+            T::load_t(tk, slot, sub, lo);
+            acc_t<T>(tk, f, acc, lo);
         }
     }
     if (kBiasGrad) {  // this tile's sums per offset, waves added in order
@@ -587,8 +724,8 @@ void bwd_dq_kernel(const BwdParams p) {
     if (qv < Lr) {
         const int vr = qv - r0;  // global rows: the merge
         if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) {
-            store_row(dQ + (size_t)row * 64, h2, acc, 0.125f);
-            if (p.sep) store_row(reinterpret_cast<uint16_t*>(p.dqg) + off + (size_t)row * 64, h2, acc, 0.f);
+            T::store_row(dQ + (size_t)row * 64, h2, acc, 0.125f);
+            if (p.sep) T::store_row(reinterpret_cast<Elem*>(p.dqg) + off + (size_t)row * 64, h2, acc, 0.f);
         }
     }
     if (ng == 0) return;
@@ -598,9 +735,9 @@ void bwd_dq_kernel(const BwdParams p) {
     // global queries; copied again for the others, and from k_g, v_g with separate
     // projections, whose global queries are q_g).
     const bool sep = p.sep != 0;
-    const uint16_t* QG = sep ? reinterpret_cast<const uint16_t*>(p.qg) + off : Q;
-    const uint16_t* KG = sep ? reinterpret_cast<const uint16_t*>(p.kg) + off : K;
-    const uint16_t* VG = sep ? reinterpret_cast<const uint16_t*>(p.vg) + off : V;
+    const Elem* QG = sep ? reinterpret_cast<const Elem*>(p.qg) + off : Q;
+    const Elem* KG = sep ? reinterpret_cast<const Elem*>(p.kg) + off : K;
+    const Elem* VG = sep ? reinterpret_cast<const Elem*>(p.vg) + off : V;
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
     const size_t part0 = ((size_t)tl.bh * p.tiles_per_head + tl.t_in) * ngq;
     const int hs = wv >> 1, hsub = wv & 1;
@@ -609,9 +746,9 @@ void bwd_dq_kernel(const BwdParams p) {
     for (int gb = 0; gb < n_gblk_b; ++gb) {
         const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
         const int g = gq < ng ? p.g[gofs + gq] : -1;
-        Op gop, gdo;
-        load_op(gop, g >= 0 ? QG + (size_t)g * 64 : nullptr, h2);
-        load_op(gdo, g >= 0 ? dO + (size_t)g * 64 : nullptr, h2);
+        typename T::Op gop, gdo;
+        T::load_op(gop, g >= 0 ? QG + (size_t)g * 64 : nullptr, h2);
+        T::load_op(gdo, g >= 0 ? dO + (size_t)g * 64 : nullptr, h2);
         const float gl = g >= 0 ? lse2[g] : kPosInf;
         const float gd = g >= 0 ? dsum[g] : 0.f;
         const char* hslot;
@@ -633,7 +770,7 @@ void bwd_dq_kernel(const BwdParams p) {
             for (int j = 0; j < 2; ++j) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
-                dma_tiles(ring + j * kStageB, KG, VG,
+                T::dma_tiles(ring + j * kStageB, KG, VG,
                           [&](int kk) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             }
             wait_vmcnt<0>();
@@ -641,10 +778,10 @@ void bwd_dq_kernel(const BwdParams p) {
             hslot = ring + hs * kStageB;
             inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * hsub));
         }
-        scale_op(gop);
+        T::scale_op(gop);
         f32x16 gacc[2] = {f32x16{}, f32x16{}};
         if (inv32 != ~0u) {
-            f32x16 s = prod(hslot, hsub, lo, gop, splat(-gl));
+            f32x16 s = T::prod(hslot, hsub, lo, gop, splat(-gl));
             if (causal) {  // keys of this class at or before the global row
                 const int vlim = g >= r ? (g - r) / dil : -1;
                 const int kss = r0 + kStageKeys * hs + 32 * hsub;
@@ -652,14 +789,14 @@ void bwd_dq_kernel(const BwdParams p) {
             } else {
                 mask_scores(s, inv32 != 0u ? 1 : 0, inv32, h2, 0, 2 * kLargeW, nullptr, 0);
             }
-            const f32x16 dp = prod(hslot + kTileB, hsub, lo, gdo, splat(-gd));
+            const f32x16 dp = T::prod(hslot + kTileB, hsub, lo, gdo, splat(-gd));
             float ds[16];
             for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
-            Frag f;
-            to_frag(ds, f);
-            TOp tk;
-            load_t(tk, hslot, hsub, lo);
-            acc_t(tk, f, gacc);
+            typename T::Frag f;
+            T::to_frag(ds, f);
+            typename T::TOp tk;
+            T::load_t(tk, hslot, hsub, lo);
+            acc_t<T>(tk, f, gacc, lo);
         }
         __syncthreads();  // done with the staged keys: the ring holds the reduction
         const int nq = min(kGlobalQueriesPerBlock, ng - gb * kGlobalQueriesPerBlock);
@@ -684,9 +821,11 @@ void bwd_dq_kernel(const BwdParams p) {
 // computes them: own keys from k_g, v_g, the global queries from q_g as its only
 // stages, every key's dK_g, dV_g written directly.
 
-template <bool kCausal, bool kBias, bool kRandom, bool kGlobalProj = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+template <class T, bool kCausal, bool kBias, bool kRandom, bool kGlobalProj = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void bwd_dkv_kernel(const BwdParams p) {
+    using Elem = typename T::Elem;
+    constexpr int kStageB = T::kStageB, kTileB = T::kTileB, kLseOff = T::kLseOff, kDOff = T::kDOff;
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
     __shared__ int own_gidx[kRowsPerBlock];  // index in g of each own key, or -1
     __shared__ int gq_pos[LF_MAX_GLOBALS];  // position of each global slot (sorted)
@@ -702,12 +841,12 @@ void bwd_dkv_kernel(const BwdParams p) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
     const size_t off = (size_t)tl.bh * L * 64;
-    const uint16_t* Q = reinterpret_cast<const uint16_t*>(kGlobalProj ? p.qg : p.q) + off;
-    const uint16_t* K = reinterpret_cast<const uint16_t*>(kGlobalProj ? p.kg : p.k) + off;
-    const uint16_t* V = reinterpret_cast<const uint16_t*>(kGlobalProj ? p.vg : p.v) + off;
-    const uint16_t* dO = reinterpret_cast<const uint16_t*>(p.dout) + off;
-    uint16_t* dK = reinterpret_cast<uint16_t*>(kGlobalProj ? p.dkg : p.dk) + off;
-    uint16_t* dV = reinterpret_cast<uint16_t*>(kGlobalProj ? p.dvg : p.dv) + off;
+    const Elem* Q = reinterpret_cast<const Elem*>(kGlobalProj ? p.qg : p.q) + off;
+    const Elem* K = reinterpret_cast<const Elem*>(kGlobalProj ? p.kg : p.k) + off;
+    const Elem* V = reinterpret_cast<const Elem*>(kGlobalProj ? p.vg : p.v) + off;
+    const Elem* dO = reinterpret_cast<const Elem*>(p.dout) + off;
+    Elem* dK = reinterpret_cast<Elem*>(kGlobalProj ? p.dkg : p.dk) + off;
+    Elem* dV = reinterpret_cast<Elem*>(kGlobalProj ? p.dvg : p.dv) + off;
     const float* lse2 = p.lse2 + (size_t)tl.bh * L;
     const float* lse2b = p.lse2_band + (size_t)tl.bh * L;
     const float* dsum = p.dsum + (size_t)tl.bh * L;
@@ -719,9 +858,9 @@ void bwd_dkv_kernel(const BwdParams p) {
     const bool rows_live = qa < Lr;
     const int krow = r + qv * dil;
     const bool kvalid = qv < Lr && (!pad || pad[krow] == 0);
-    Op kop, vop;
-    load_op(kop, kvalid ? K + (size_t)krow * 64 : nullptr, h2);
-    load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
+    typename T::Op kop, vop;
+    T::load_op(kop, kvalid ? K + (size_t)krow * 64 : nullptr, h2);
+    T::load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
 
     // global-query stages: none here with separate projections (their own launch)
     const int n_gst = (!kGlobalProj && p.sep) ? 0 : (ng + kStageKeys - 1) / kStageKeys;
@@ -748,13 +887,13 @@ void bwd_dkv_kernel(const BwdParams p) {
                 const int gi = kStageKeys * s + kk;
                 return gi < ng ? p.g[gofs + gi] : -1;
             };
-            dma_tiles(slot, Q, dO, row_of, wv, lane);
-            if (wv == 0) dma_floats(slot, lse2, dsum, row_of, lane);
+            T::dma_tiles(slot, Q, dO, row_of, wv, lane);
+            if (wv == 0) dma_floats<T>(slot, lse2, dsum, row_of, lane);
         } else if (kRandom && s < n_lst) {
             const int x0 = kRandomBlock * rnd_qblock(s - n_gst);
             auto row_of = [&](int kk) { return x0 + kk < L ? x0 + kk : -1; };
-            dma_tiles(slot, Q, dO, row_of, wv, lane);
-            if (wv == 0) dma_floats(slot, lse2b, dsum, row_of, lane);
+            T::dma_tiles(slot, Q, dO, row_of, wv, lane);
+            if (wv == 0) dma_floats<T>(slot, lse2b, dsum, row_of, lane);
         } else {
             const int ks = tl.stage_row(s - n_lst);
             ks_next = ks;
@@ -762,8 +901,8 @@ void bwd_dkv_kernel(const BwdParams p) {
                 const int x = ks + kk;
                 return (x >= tl.kb0 && x < tl.kend) ? r + x * dil : -1;
             };
-            dma_tiles(slot, Q, dO, row_of, wv, lane);
-            if (wv == 0) dma_floats(slot, lse2b, dsum, row_of, lane);
+            T::dma_tiles(slot, Q, dO, row_of, wv, lane);
+            if (wv == 0) dma_floats<T>(slot, lse2b, dsum, row_of, lane);
         }
     };
 
@@ -783,11 +922,11 @@ void bwd_dkv_kernel(const BwdParams p) {
     // One-sided variant: the first global slot at or after this lane's key (the
     // global queries that see it; slots are sorted by position).
     const int gfirst = causal ? count_le(gq_pos, ng, krow - 1) : 0;
-    Lanes lo;
-    lane_setup(lo, lane);
+    typename T::Lanes lo;
+    T::lane_setup(lo, lane);
     if (n_st > 0) issue(0);
     wait_vmcnt<0>();
-    scale_op(kop);
+    T::scale_op(kop);
     f32x16 dk[2] = {f32x16{}, f32x16{}}, dv[2] = {f32x16{}, f32x16{}};
     // Random stages: an own key that is global takes its random pairs from the
     // global-key pass instead.
@@ -818,7 +957,7 @@ void bwd_dkv_kernel(const BwdParams p) {
             }
             const bool interior = !gstage && !rstage && kss >= qa + 31 - wl && kss + 31 <= qa + w;
             const int mode = rstage ? 3 : ((gstage || interior) ? 0 : 1);
-            f32x16 s = prod(slot, sub, lo, kop, row_seed(slot + kLseOff, sub, h2));  // scores - lse, base 2
+            f32x16 s = T::prod(slot, sub, lo, kop, row_seed(slot + kLseOff, sub, h2));  // scores - lse, base 2
             // element i: query kss + 8*h2 + kc, key qv, offset m = qv - query: reversed table
             if (kBias && !gstage && !rstage) add_bias(s, bias_lds + kBiasPad + kss + 8 * h2 - qv + w);
             // Random stage: invalid queries are those past the end.
@@ -835,20 +974,20 @@ void bwd_dkv_kernel(const BwdParams p) {
                 for (int i = 0; i < 16; ++i)
                     if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
             }
-            const f32x16 dp = prod(slot + kTileB, sub, lo, vop, row_seed(slot + kDOff, sub, h2));  // dO.V - D
+            const f32x16 dp = T::prod(slot + kTileB, sub, lo, vop, row_seed(slot + kDOff, sub, h2));  // dO.V - D
             float pr[16], ds[16];
             for (int i = 0; i < 16; ++i) {
                 pr[i] = fast_exp2(s[i]);
                 ds[i] = pr[i] * dp[i];
             }
-            Frag fp, fs;
-            to_frag(pr, fp);
-            to_frag(ds, fs);
-            TOp tt;
-            load_t(tt, slot + kTileB, sub, lo);
-            acc_t(tt, fp, dv);
-            load_t(tt, slot, sub, lo);
-            acc_t(tt, fs, dk);
+            typename T::Frag fp, fs;
+            T::to_frag(pr, fp);
+            T::to_frag(ds, fs);
+            typename T::TOp tt;
+            T::load_t(tt, slot + kTileB, sub, lo);
+            acc_t<T>(tt, fp, dv, lo);
+            T::load_t(tt, slot, sub, lo);
+            acc_t<T>(tt, fs, dk, lo);
         }
     }
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
@@ -856,8 +995,8 @@ void bwd_dkv_kernel(const BwdParams p) {
         const int gi = kGlobalProj ? -1 : own_gidx[qv - r0];
         const float sk = kvalid ? 0.125f : 0.f, sv = kvalid ? 1.f : 0.f;
         if (gi < 0) {
-            store_row(dK + (size_t)krow * 64, h2, dk, sk);
-            store_row(dV + (size_t)krow * 64, h2, dv, sv);
+            T::store_row(dK + (size_t)krow * 64, h2, dk, sk);
+            T::store_row(dV + (size_t)krow * 64, h2, dv, sv);
         } else {  // global key: completed by the merge (unscaled fp32)
             store_row_f32(p.ws_dkg + ((size_t)tl.bh * ngq + gi) * 64, h2, dk, kvalid ? 1.f : 0.f);
             store_row_f32(p.ws_dvg + ((size_t)tl.bh * ngq + gi) * 64, h2, dv, sv);
@@ -876,9 +1015,9 @@ void bwd_dkv_kernel(const BwdParams p) {
         const int gk = gb * kGlobalQueriesPerBlock + (lane & 31);
         const int g = gk < ng ? p.g[gofs + gk] : -1;
         const bool gvalid = g >= 0 && (!pad || pad[g] == 0);
-        Op kg, vg;
-        load_op(kg, gvalid ? K + (size_t)g * 64 : nullptr, h2);
-        load_op(vg, gvalid ? V + (size_t)g * 64 : nullptr, h2);
+        typename T::Op kg, vg;
+        T::load_op(kg, gvalid ? K + (size_t)g * 64 : nullptr, h2);
+        T::load_op(vg, gvalid ? V + (size_t)g * 64 : nullptr, h2);
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         const char* hslot;
         if (gb == 0) {
@@ -893,17 +1032,17 @@ void bwd_dkv_kernel(const BwdParams p) {
                     const int x = ks + kk;
                     return x < Lr ? r + x * dil : -1;
                 };
-                dma_tiles(ring + j * kStageB, Q, dO, row_of, wv, lane);
-                if (wv == 0) dma_floats(ring + j * kStageB, lse2b, dsum, row_of, lane);
+                T::dma_tiles(ring + j * kStageB, Q, dO, row_of, wv, lane);
+                if (wv == 0) dma_floats<T>(ring + j * kStageB, lse2b, dsum, row_of, lane);
             }
             wait_vmcnt<0>();
             __syncthreads();
             hslot = ring + hs * kStageB;
         }
-        scale_op(kg);
+        T::scale_op(kg);
         f32x16 gk_acc[2] = {f32x16{}, f32x16{}}, gv_acc[2] = {f32x16{}, f32x16{}};
         if (hq < Lr) {
-            f32x16 s = prod(hslot, hsub, lo, kg, row_seed(hslot + kLseOff, hsub, h2));
+            f32x16 s = T::prod(hslot, hsub, lo, kg, row_seed(hslot + kLseOff, hsub, h2));
             // Queries kept, one bit per kc (element i holds query base + kc_of(i)): below
             // Lr, not in the window that holds the key (those pairs are in the key's own
             // tile), and, one-sided, not before the key.  Built as bit ranges so that the
@@ -914,20 +1053,20 @@ void bwd_dkv_kernel(const BwdParams p) {
             if (causal) keep &= bits_from((g > r ? (g - r + dil - 1) / dil : 0) - base);
             for (int i = 0; i < 16; ++i)
                 if (!((keep >> kc_of(i)) & 1u)) s[i] = kNegInf;
-            const f32x16 dp = prod(hslot + kTileB, hsub, lo, vg, row_seed(hslot + kDOff, hsub, h2));
+            const f32x16 dp = T::prod(hslot + kTileB, hsub, lo, vg, row_seed(hslot + kDOff, hsub, h2));
             float pr[16], ds[16];
             for (int i = 0; i < 16; ++i) {
                 pr[i] = fast_exp2(s[i]);
                 ds[i] = pr[i] * dp[i];
             }
-            Frag fp, fs;
-            to_frag(pr, fp);
-            to_frag(ds, fs);
-            TOp tt;
-            load_t(tt, hslot + kTileB, hsub, lo);
-            acc_t(tt, fp, gv_acc);
-            load_t(tt, hslot, hsub, lo);
-            acc_t(tt, fs, gk_acc);
+            typename T::Frag fp, fs;
+            T::to_frag(pr, fp);
+            T::to_frag(ds, fs);
+            typename T::TOp tt;
+            T::load_t(tt, hslot + kTileB, hsub, lo);
+            acc_t<T>(tt, fp, gv_acc, lo);
+            T::load_t(tt, hslot, hsub, lo);
+            acc_t<T>(tt, fs, gk_acc, lo);
         }
         __syncthreads();  // done with the staged queries: the ring holds the reductions
         const int nq = min(kGlobalQueriesPerBlock, ng - gb * kGlobalQueriesPerBlock);
@@ -945,7 +1084,9 @@ void bwd_dkv_kernel(const BwdParams p) {
 
 constexpr int kBwdMergeWaves = 16;
 constexpr int kBwdMergeChunk = 8;
+template <class T>
 __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const BwdParams p) {
+    using Elem = typename T::Elem;
     __shared__ float red[kBwdMergeWaves][3][64];
     const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -996,35 +1137,39 @@ __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const Bw
     }
     const size_t o = (size_t)bh * L * 64 + (size_t)p.g[gofs + gi] * 64 + d;
     // with separate projections a global row's dQ goes to dq_g and its dq is zero
-    if (p.sep) reinterpret_cast<uint16_t*>(p.dqg)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sq * 0.125f));
-    reinterpret_cast<uint16_t*>(p.dq)[o] = __builtin_bit_cast(uint16_t, (__bf16)(p.sep ? 0.f : sq * 0.125f));
-    reinterpret_cast<uint16_t*>(p.dk)[o] = __builtin_bit_cast(uint16_t, (__bf16)(sk * 0.125f));
-    reinterpret_cast<uint16_t*>(p.dv)[o] = __builtin_bit_cast(uint16_t, (__bf16)sv);
+    if (p.sep) reinterpret_cast<Elem*>(p.dqg)[o] = T::from_float(sq * 0.125f);
+    reinterpret_cast<Elem*>(p.dq)[o] = T::from_float(p.sep ? 0.f : sq * 0.125f);
+    reinterpret_cast<Elem*>(p.dk)[o] = T::from_float(sk * 0.125f);
+    reinterpret_cast<Elem*>(p.dv)[o] = T::from_float(sv);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
+namespace {
+
+template <class T>
+hipError_t bwd_prep_t(const BwdParams& p, hipStream_t s) {
     const long long blocks = (long long)p.B * p.H * ((p.L + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    launch_kernel(bwd_prep_kernel, dim3((unsigned)blocks), dim3(kThreads), s, p);
+    launch_kernel(bwd_prep_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
+template <class T>
+hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
     if (p.dbias) {  // position-bias table gradient: per-wave offset sums in dynamic LDS
         const unsigned shm = kWaves * (2 * p.w + 1 + 2 * kBiasPad) * sizeof(float);
         if (p.rnd) {
-            if (p.causal) return launch_kernel_shm(bwd_dq_kernel<true, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
-            return launch_kernel_shm(bwd_dq_kernel<false, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+            if (p.causal) return launch_kernel_shm(bwd_dq_kernel<T, true, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+            return launch_kernel_shm(bwd_dq_kernel<T, false, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
         }
-        if (p.causal) return launch_kernel_shm(bwd_dq_kernel<true, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
-        return launch_kernel_shm(bwd_dq_kernel<false, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+        if (p.causal) return launch_kernel_shm(bwd_dq_kernel<T, true, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+        return launch_kernel_shm(bwd_dq_kernel<T, false, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
     }
-#define LF_DQ(C, Bi, R) launch_kernel(bwd_dq_kernel<C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
+#define LF_DQ(C, Bi, R) launch_kernel(bwd_dq_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
 #define LF_DQ_R(C, Bi) \
     if (p.rnd) LF_DQ(C, Bi, true); else LF_DQ(C, Bi, false)
     if (p.causal) {
@@ -1037,10 +1182,11 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
+template <class T>
+hipError_t bwd_dkv_t(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-#define LF_DKV(C, Bi, R) launch_kernel(bwd_dkv_kernel<C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
+#define LF_DKV(C, Bi, R) launch_kernel(bwd_dkv_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
 #define LF_DKV_R(C, Bi) \
     if (p.rnd) LF_DKV(C, Bi, true); else LF_DKV(C, Bi, false)
     if (p.causal) {
@@ -1053,14 +1199,38 @@ hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s) {
+template <class T>
+hipError_t bwd_dkv_global_proj_t(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
     if (p.causal)
-        launch_kernel(bwd_dkv_kernel<true, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
+        launch_kernel(bwd_dkv_kernel<T, true, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
     else
-        launch_kernel(bwd_dkv_kernel<false, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
+        launch_kernel(bwd_dkv_kernel<T, false, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
     return hipGetLastError();
+}
+
+template <class T>
+hipError_t bwd_merge_t(const BwdParams& p, hipStream_t s) {
+    if (p.n_g == 0) return hipSuccess;
+    const int waves = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);
+    launch_kernel(bwd_merge_kernel<T>, dim3(p.n_g, p.B * p.H), dim3(64 * waves), s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const BwdParams& p, hipStream_t s) {
+    return p.dtype == LF_F32 ? bwd_prep_t<BF32>(p, s) : bwd_prep_t<BBf16>(p, s);
+}
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t s) {
+    return p.dtype == LF_F32 ? bwd_dq_t<BF32>(p, s) : bwd_dq_t<BBf16>(p, s);
+}
+hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t s) {
+    return p.dtype == LF_F32 ? bwd_dkv_t<BF32>(p, s) : bwd_dkv_t<BBf16>(p, s);
+}
+hipError_t launch_bwd_dkv_global_proj(const BwdParams& p, hipStream_t s) {
+    return p.dtype == LF_F32 ? bwd_dkv_global_proj_t<BF32>(p, s) : bwd_dkv_global_proj_t<BBf16>(p, s);
 }
 
 // dbias[h][m] = sum over sequences b and the existing tiles t of head h (in that order)
@@ -1092,10 +1262,7 @@ hipError_t launch_bwd_dbias(const BwdParams& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_merge(const BwdParams& p, hipStream_t s) {
-    if (p.n_g == 0) return hipSuccess;
-    const int waves = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);
-    launch_kernel(bwd_merge_kernel, dim3(p.n_g, p.B * p.H), dim3(64 * waves), s, p);
-    return hipGetLastError();
+    return p.dtype == LF_F32 ? bwd_merge_t<BF32>(p, s) : bwd_merge_t<BBf16>(p, s);
 }
 
 }  // namespace lf

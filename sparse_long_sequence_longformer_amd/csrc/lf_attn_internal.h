@@ -130,6 +130,7 @@ struct BwdParams {
     int dil[LF_MAX_HEADS];
     int g[LF_MAX_GLOBALS];
     int gcnt[LF_MAX_GLOBALS];
+    int dtype;  // LF_BF16 or LF_F32 tensors
 };
 
 // Launchers of the layer's pointwise passes (defined in lf_layer.hip).

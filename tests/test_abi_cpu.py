@@ -163,13 +163,13 @@ def test_backward_host_validation():
     h32, h16 = ctypes.c_void_p(), ctypes.c_void_p()
     assert lib.lf_attn_create(ctypes.byref(h32), 0) == 0 and lib.lf_attn_create(ctypes.byref(h16), 1) == 0
     try:
-        st, msg = call(h32)
-        assert st == 2 and "bf16" in msg
-        for kw, frag in [(dict(lse=None), "non-null"), (dict(dv=None), "non-null"), (dict(lse=FAKE * 9 + 2), "aligned"),
-                         (dict(dq=FAKE * 10 + 8), "aligned"), (dict(dk=FAKE * 10 + 4096), "overlap"),
-                         (dict(dq=FAKE * 2 + 1024), "overlap"), (dict(dv=FAKE * 9 - 16), "overlap")]:
-            st, msg = call(h16, **kw)
-            assert st == 1 and frag in msg, (kw, st, msg)
+        for h in (h16, h32):  # both dtypes run the same validation
+            for kw, frag in [(dict(lse=None), "non-null"), (dict(dv=None), "non-null"),
+                             (dict(lse=FAKE * 9 + 2), "aligned"), (dict(dq=FAKE * 10 + 8), "aligned"),
+                             (dict(dk=FAKE * 10 + 4096), "overlap"), (dict(dq=FAKE * 2 + 1024), "overlap"),
+                             (dict(dv=FAKE * 9 - 16), "overlap")]:
+                st, msg = call(h, **kw)
+                assert st == 1 and frag in msg, (kw, st, msg)
         st = lib.lf_attn_forward_lse(h16, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1, 1, 64, 64, 4, dil_p, None, 0,
                                      None, None)
         assert st == 1
@@ -359,14 +359,13 @@ def test_global_proj_backward_host_validation():
     h32, h16 = ctypes.c_void_p(), ctypes.c_void_p()
     assert lib.lf_attn_create(ctypes.byref(h32), 0) == 0 and lib.lf_attn_create(ctypes.byref(h16), 1) == 0
     try:
-        st, msg = call(h32)
-        assert st == 2 and "bf16" in msg
-        for kw, frag in [(dict(qg=None), "must all be non-null"), (dict(dvg=None), "must all be non-null"),
-                         (dict(lse=None), "non-null"), (dict(kg=FAKE * 5 + 4), "aligned"),
-                         (dict(dqg=FAKE * 13 + 8), "aligned"), (dict(dkg=FAKE * 6 + 64), "overlap the inputs"),
-                         (dict(dvg=FAKE * 10 + 4096), "must not overlap"), (dict(dqg=FAKE * 9 - 32), "overlap")]:
-            st, msg = call(h16, **kw)
-            assert st == 1 and frag in msg, (kw, st, msg)
+        for h in (h16, h32):  # both dtypes run the same validation
+            for kw, frag in [(dict(qg=None), "must all be non-null"), (dict(dvg=None), "must all be non-null"),
+                             (dict(lse=None), "non-null"), (dict(kg=FAKE * 5 + 4), "aligned"),
+                             (dict(dqg=FAKE * 13 + 8), "aligned"), (dict(dkg=FAKE * 6 + 64), "overlap the inputs"),
+                             (dict(dvg=FAKE * 10 + 4096), "must not overlap"), (dict(dqg=FAKE * 9 - 32), "overlap")]:
+                st, msg = call(h, **kw)
+                assert st == 1 and frag in msg, (kw, st, msg)
         assert lib.lf_attn_backward_global_proj(None, *([FAKE] * 15), 1, 1, 64, 64, 4, dil_p, None, 0, None,
                                                 None) == 1
         # the forward that returns the statistics: lse must be given and clear of q_g
