@@ -64,7 +64,7 @@ typedef enum lf_dtype {
 #define LF_STAGE_BWD_DKV 4   /* backward: dK, dV (key-owned), global-key partials */
 #define LF_STAGE_BWD_MERGE 5 /* backward: sums of the global partials (only with globals) */
 #define LF_STAGE_LAYER_GEMM 6      /* layer: the four projection / feed-forward GEMMs (hipBLASLt) */
-#define LF_STAGE_LAYER_POINTWISE 7 /* layer: head split and merge, LayerNorms, GELU */
+#define LF_STAGE_LAYER_POINTWISE 7 /* layer: bias + residual + LayerNorm, bias + GELU */
 #define LF_STAGE_BWD_DKV_GLOBAL 8  /* backward, separate global projections: dK_g, dV_g */
 #define LF_STAGE_BWD_DBIAS 9       /* backward: sums of the position-bias table gradient */
 
@@ -387,11 +387,13 @@ lf_status lf_attn_set_random_blocks(lf_attn_t h, const int32_t* blocks, int n_he
  * lf_attn_forward.
  * GEMMs run in hipBLASLt (bf16 inputs, fp32 accumulation; the QKV and first
  * feed-forward outputs in bf16, the two outputs that feed a LayerNorm in fp32;
- * biases are added in fp32 by the pointwise passes; the algorithm is hipBLASLt's
- * first heuristic choice, fixed per shape at its first call on the handle); the
- * handle owns a hipBLASLt handle, a 32 MiB GEMM workspace and a device workspace
- * for the intermediates (max(6 * hidden, 2 * ffn) + 10 * hidden + 2 * ffn bytes per
- * token).  Errors: as lf_attn_forward; LF_ERR_UNSUPPORTED for fp32 handles or
+ * b_qkv is added in the QKV GEMM's epilogue, the other biases in fp32 by the
+ * pointwise passes; the algorithm is hipBLASLt's first heuristic choice, fixed per
+ * shape at its first call on the handle).  The attention reads q, k, v where the QKV
+ * GEMM leaves them (row stride 3 * hidden) and writes its output with the heads
+ * merged (row stride hidden), so no pass splits or merges heads.  The handle owns a
+ * hipBLASLt handle, a 32 MiB GEMM workspace and a device workspace for the
+ * intermediates (max(6 * hidden, 2 * ffn) + 2 * hidden + 2 * ffn bytes per token).  Errors: as lf_attn_forward; LF_ERR_UNSUPPORTED for fp32 handles or
  * unsupported sizes.
  */
 typedef struct lf_layer_weights {

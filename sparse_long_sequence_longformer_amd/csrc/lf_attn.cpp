@@ -32,6 +32,7 @@ struct TimedLaunch {
 struct GemmPlan {
     int M = 0, N = 0, K = 0;
     bool f32_out = false;
+    bool bias = false;  // epilogue adds a bf16 bias vector of N entries (pointer set per call)
     hipblasLtMatmulDesc_t desc = nullptr;
     hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
     hipblasLtMatmulAlgo_t algo{};
@@ -519,10 +520,19 @@ lf_status launch_stage(lf_attn_t h, int stage, hipStream_t s, Launch launch) {
 // row) or all non-null (separate projections of the global rows); lse may be null.
 // no_alloc: the partials go to the static scratch array (no allocation, no upload,
 // no per-launch timing).
+// Element strides of q, k, v and of out (see lf::Params); nullptr: [B][H][L][64] each.
+struct Strides {
+    long long s_b, s_h;
+    int s_r;
+    long long o_b, o_h;
+    int o_r;
+};
+
 lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
                        const void* vg, void* out, float* lse, int B, int H, int L, int d_h, int w,
                        const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
-                       const uint8_t* key_pad_mask, void* stream, bool no_alloc = false) {
+                       const uint8_t* key_pad_mask, void* stream, bool no_alloc = false,
+                       const Strides* strides = nullptr) {
     if (!h) return LF_ERR_INVALID_ARG;
     h->last_error.clear();
     if (!q || !k || !v || !out) return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be non-null");
@@ -536,7 +546,7 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(h, LF_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
     const size_t bytes = pl.bytes;
-    if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+    if (!strides && (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes)))
         return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q, k or v");
     if (sep && (overlaps(out, qg, bytes) || overlaps(out, kg, bytes) || overlaps(out, vg, bytes)))
         return fail(h, LF_ERR_INVALID_ARG, "out must not overlap q_g, k_g or v_g");
@@ -576,6 +586,20 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;
     p.bias = h->bias;
     p.bias_w = h->bias_w;
+    if (strides) {
+        if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "strided tensors need a bf16 handle");
+        p.strided = 1;
+        p.s_b = strides->s_b;
+        p.s_h = strides->s_h;
+        p.s_r = strides->s_r;
+        p.o_b = strides->o_b;
+        p.o_h = strides->o_h;
+        p.o_r = strides->o_r;
+    } else {
+        p.s_h = p.o_h = static_cast<long long>(L) * LF_HEAD_DIM;
+        p.s_b = p.o_b = p.s_h * H;
+        p.s_r = p.o_r = LF_HEAD_DIM;
+    }
 
     // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
@@ -773,9 +797,9 @@ constexpr size_t kGemmWorkspace = size_t(32) << 20;
 
 // The descriptors and algorithm of Y[M][N] = X[M][K] W^T (see gemm_xwt), made once
 // per shape and output type on the handle's current device.
-lf_status gemm_plan(lf_attn_t h, int M, int N, int K, bool f32_out, const GemmPlan** out) {
+lf_status gemm_plan(lf_attn_t h, int M, int N, int K, bool f32_out, bool bias, const GemmPlan** out) {
     for (const GemmPlan& g : h->gemm_plans)
-        if (g.M == M && g.N == N && g.K == K && g.f32_out == f32_out) {
+        if (g.M == M && g.N == N && g.K == K && g.f32_out == f32_out && g.bias == bias) {
             *out = &g;
             return LF_OK;
         }
@@ -784,6 +808,9 @@ lf_status gemm_plan(lf_attn_t h, int M, int N, int K, bool f32_out, const GemmPl
     g.N = N;
     g.K = K;
     g.f32_out = f32_out;
+    g.bias = bias;
+    const hipblasLtEpilogue_t epi = bias ? HIPBLASLT_EPILOGUE_BIAS : HIPBLASLT_EPILOGUE_DEFAULT;
+    const hipDataType bias_t = HIP_R_16BF;
     const hipDataType yt = f32_out ? HIP_R_32F : HIP_R_16BF;
     const hipblasOperation_t opt = HIPBLAS_OP_T, opn = HIPBLAS_OP_N;
     hipblasLtMatmulPreference_t pref = nullptr;
@@ -795,6 +822,10 @@ lf_status gemm_plan(lf_attn_t h, int M, int N, int K, bool f32_out, const GemmPl
                   HIPBLAS_STATUS_SUCCESS &&
               hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opn, sizeof(opn)) ==
                   HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof(epi)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              (!bias || hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_t,
+                                                        sizeof(bias_t)) == HIPBLAS_STATUS_SUCCESS) &&
               hipblasLtMatrixLayoutCreate(&g.a, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS &&
               hipblasLtMatrixLayoutCreate(&g.b, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
               hipblasLtMatrixLayoutCreate(&g.c, yt, N, M, N) == HIPBLAS_STATUS_SUCCESS &&
@@ -823,10 +854,13 @@ lf_status gemm_plan(lf_attn_t h, int M, int N, int K, bool f32_out, const GemmPl
 // (bf16), fp32 accumulation: in hipBLASLt's column-major terms Y^T = W X^T, i.e.
 // op(A) = A^T with A = W^T stored K x N, and B = X^T stored K x M.
 lf_status gemm_xwt(lf_attn_t h, const void* X, const void* Wt, void* Y, int M, int N, int K, bool f32_out,
-                   hipStream_t s) {
+                   hipStream_t s, const void* bias = nullptr) {
     const GemmPlan* g = nullptr;
-    lf_status st = gemm_plan(h, M, N, K, f32_out, &g);
+    lf_status st = gemm_plan(h, M, N, K, f32_out, bias != nullptr, &g);
     if (st != LF_OK) return st;
+    if (bias && hipblasLtMatmulDescSetAttribute(g->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
+                    HIPBLAS_STATUS_SUCCESS)
+        return fail(h, LF_ERR_HIP, "setting the GEMM bias pointer failed");
     const float one = 1.f, zero = 0.f;
     const hipblasStatus_t rs = hipblasLtMatmul(h->lt, g->desc, &one, Wt, g->a, X, g->b, &zero, Y, g->c, Y, g->c,
                                                &g->algo, h->ws_gemm, g->ws, s);
@@ -875,35 +909,41 @@ lf_status layer_impl(lf_attn_t h, const void* x, const lf_layer_weights* wt, voi
     if (st != LF_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // Workspace: one GEMM output [R][3E] or [R][F] in bf16, or [R][E] in fp32, then bf16
-    // q, k, v, attention output, merged heads (reused for x1), and the feed-forward
-    // activations [R][F].
+    // Workspace: one GEMM output ([R][3E] or [R][F] in bf16, or [R][E] in fp32), the
+    // attention output in merged-heads layout [R][E] (reused for x1), and the
+    // feed-forward activations [R][F], bf16.
     const size_t g_row = std::max<size_t>(std::max(3 * E, F) * size_t(2), E * size_t(4));
     const size_t t_elems = R * static_cast<size_t>(E);
     const size_t g_bytes = (R * g_row + 255) & ~size_t(255);
-    const size_t need = g_bytes + (5 * t_elems + R * F) * 2 + 256;
+    const size_t need = g_bytes + (t_elems + R * F) * 2 + 256;
     st = reserve(h, &h->ws_layer, &h->ws_layer_bytes, &h->ws_layer_device, need);
     if (st != LF_OK) return st;
     void* gout = h->ws_layer;
-    uint16_t* bq = reinterpret_cast<uint16_t*>(h->ws_layer + g_bytes);
-    uint16_t* bk = bq + t_elems;
-    uint16_t* bv = bk + t_elems;
-    uint16_t* ba = bv + t_elems;
-    uint16_t* bm = ba + t_elems;  // merged heads, then x1
-    uint16_t* bh = bm + t_elems;  // GELU activations [R][F]
+    uint16_t* bm = reinterpret_cast<uint16_t*>(h->ws_layer + g_bytes);  // attention output [R][E], then x1
+    uint16_t* bh = bm + t_elems;                                         // GELU activations [R][F]
     const int M = static_cast<int>(R);
 
+    // QKV projection with its bias added in the GEMM epilogue: row t of gout holds
+    // q, k, v of token t, head h at features 64h (+E, +2E).  The attention reads them
+    // there and writes its output with the heads merged, ready for the output
+    // projection: no split or merge passes.
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
-        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E, false, s) == LF_OK ? hipSuccess : hipErrorUnknown;
+        return gemm_xwt(h, x, wt->w_qkv, gout, M, 3 * E, E, false, s, wt->b_qkv) == LF_OK ? hipSuccess
+                                                                                         : hipErrorUnknown;
     });
     if (st != LF_OK) return st;
-    st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s,
-                      [&] { return lf::launch_qkv_split(gout, wt->b_qkv, bq, bk, bv, B, L, E, s); });
-    if (st != LF_OK) return st;
-    st = forward_impl(h, bq, bk, bv, nullptr, nullptr, nullptr, ba, nullptr, B, H, L, LF_HEAD_DIM, w, dil_per_head,
-                      global_idx, n_global, key_pad_mask, stream);
-    if (st != LF_OK) return st;
-    st = launch_stage(h, LF_STAGE_LAYER_POINTWISE, s, [&] { return lf::launch_merge_heads(ba, bm, B, L, E, s); });
+    {
+        const uint16_t* g16 = static_cast<const uint16_t*>(gout);
+        Strides sd;
+        sd.s_b = 3LL * L * E;
+        sd.s_h = LF_HEAD_DIM;
+        sd.s_r = 3 * E;
+        sd.o_b = static_cast<long long>(L) * E;
+        sd.o_h = LF_HEAD_DIM;
+        sd.o_r = E;
+        st = forward_impl(h, g16, g16 + E, g16 + 2 * E, nullptr, nullptr, nullptr, bm, nullptr, B, H, L, LF_HEAD_DIM,
+                          w, dil_per_head, global_idx, n_global, key_pad_mask, stream, false, &sd);
+    }
     if (st != LF_OK) return st;
     st = launch_stage(h, LF_STAGE_LAYER_GEMM, s, [&] {
         return gemm_xwt(h, bm, wt->w_o, gout, M, E, E, true, s) == LF_OK ? hipSuccess : hipErrorUnknown;

@@ -55,6 +55,13 @@ struct Params {
     int dil[LF_MAX_HEADS];
     int g[LF_MAX_GLOBALS];
     int gcnt[LF_MAX_GLOBALS];
+    // Element strides: row i of (b, h) of q, k, v (and q_g, k_g, v_g) at
+    // b*s_b + h*s_h + i*s_r, of out at b*o_b + h*o_h + i*o_r.  [B][H][L][64]:
+    // (H*L*64, L*64, 64); the layer's QKV projection output [B][L][3][H][64]:
+    // (3*L*E, 64, 3*E) with E = 64*H, and its merged-heads output (L*E, 64, E).
+    long long s_b, s_h, o_b, o_h;
+    int s_r, o_r;
+    int strided;  // strides other than [B][H][L][64] (bf16 only)
 };
 
 // Events of the kernel launch in progress, set by the host around one launch when
@@ -134,10 +141,7 @@ struct BwdParams {
 };
 
 // Launchers of the layer's pointwise passes (defined in lf_layer.hip).
-// GEMM outputs: qkv and h bf16, y (the input of a LayerNorm) fp32.
-hipError_t launch_qkv_split(const void* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
-                            hipStream_t s);
-hipError_t launch_merge_heads(const void* a, void* out, int B, int L, int E, hipStream_t s);
+// GEMM outputs: h bf16, y (the input of a LayerNorm) fp32.
 hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void* res, const void* gamma,
                                    const void* beta, float eps, void* out, int E, long long R, hipStream_t s);
 hipError_t launch_bias_gelu(const void* h, const void* bias, void* out, int F, long long R, hipStream_t s);

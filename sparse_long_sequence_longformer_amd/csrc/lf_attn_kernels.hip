@@ -99,18 +99,19 @@ struct Bf16 {
 
     // Stage DMA by all four waves: wave wv fills 1-KiB blocks 2*wv and 2*wv+1 of K
     // and of V (8 rows each), block 2*wv + part for part = 0, 1 (kAllParts: both).
-    // row_of(kk) is the source row of stage key kk or -1.
+    // row_of(kk) is the source row of stage key kk or -1; rs the row stride of K and
+    // V in elements.
     template <class RowOf>
-    __device__ __forceinline__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
-                                     int part = kAllParts) {
+    __device__ __forceinline__ static void dma_stage(char* slot, const Elem* K, const Elem* V, int rs, RowOf row_of, int wv,
+                                                     int lane, int part = kAllParts) {
         const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 2; ++u) {
             if (part != kAllParts && u != part) continue;
             const int blk = 2 * wv + u;
             const int row = 8 * blk + (lane >> 3), cl = lane & 7;
             const int src = row_of(row);
-            const Elem* kr = src >= 0 ? K + (size_t)src * 64 : zero;
-            const Elem* vr = src >= 0 ? V + (size_t)src * 64 : zero;
+            const Elem* kr = src >= 0 ? K + (size_t)src * rs : zero;
+            const Elem* vr = src >= 0 ? V + (size_t)src * rs : zero;
             dma16(kr + 8 * (cl ^ swz_k(row)), slot + blk * 1024);
             dma16(vr + 8 * (cl ^ swz_v(row)), slot + kTileBytes + blk * 1024);
         }
@@ -125,21 +126,22 @@ struct Bf16 {
 
     // Byte offsets of this lane's stage copies (block 2*wv) relative to the stage's
     // first source row, for stages whose 64 keys are all valid (consecutive class
-    // rows dil apart).  Block 2*wv+1 lies 8 rows further (scalar base advanced by
-    // 8*dil rows); its rows differ from block 2*wv's in bit 3 only, so swz_v is the
-    // same and swz_k differs by 4 (chunk bit 2: byte offset bit 6).
-    struct DmaLane { uint32_t k, v; int dil; };
-    __device__ __forceinline__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
+    // rows `step` elements apart: dil times the row stride).  Block 2*wv+1 lies 8 rows
+    // further (scalar base advanced by 8 steps); its rows differ from block 2*wv's in
+    // bit 3 only, so swz_v is the same and swz_k differs by 4 (chunk bit 2: byte offset
+    // bit 6).
+    struct DmaLane { uint32_t k, v; int step; };
+    __device__ __forceinline__ static void dma_lane(DmaLane& dl, int wv, int lane, int step) {
         const int row = 16 * wv + (lane >> 3), cl = lane & 7;
-        const uint32_t r0b = (uint32_t)row * (uint32_t)dil * kRowBytes;
+        const uint32_t r0b = (uint32_t)row * (uint32_t)step * (uint32_t)sizeof(Elem);
         dl.k = r0b + 16u * (uint32_t)(cl ^ swz_k(row));
         dl.v = r0b + 16u * (uint32_t)(cl ^ swz_v(row));
-        dl.dil = dil;
+        dl.step = step;
     }
     __device__ __forceinline__ static void dma_stage_direct(char* slot, const Elem* K0, const Elem* V0, const DmaLane& dl, int wv) {
         for (int u = 0; u < 2; ++u) {
             const int blk = 2 * wv + u;
-            const size_t adv = (size_t)u * 8 * dl.dil * 64;
+            const size_t adv = (size_t)u * 8 * dl.step;
             dma16s(K0 + adv, u ? dl.k ^ 64u : dl.k, slot + blk * 1024);
             dma16s(V0 + adv, dl.v, slot + kTileBytes + blk * 1024);
         }
@@ -272,16 +274,16 @@ struct F32 {
     // Wave wv fills 1-KiB blocks 4*wv .. 4*wv+3 of K and of V (4 rows each); part
     // p = 0, 1 fills blocks 4*wv + 2*p and 4*wv + 2*p + 1 (kAllParts: all four).
     template <class RowOf>
-    __device__ __forceinline__ static void dma_stage(char* slot, const Elem* K, const Elem* V, RowOf row_of, int wv, int lane,
-                                     int part = kAllParts) {
+    __device__ __forceinline__ static void dma_stage(char* slot, const Elem* K, const Elem* V, int rs, RowOf row_of, int wv,
+                                                     int lane, int part = kAllParts) {
         const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
         for (int u = 0; u < 4; ++u) {
             if (part != kAllParts && (u >> 1) != part) continue;
             const int blk = 4 * wv + u;
             const int row = 4 * blk + (lane >> 4), cl = lane & 15;
             const int src = row_of(row);
-            const Elem* kr = src >= 0 ? K + (size_t)src * 64 : zero;
-            const Elem* vr = src >= 0 ? V + (size_t)src * 64 : zero;
+            const Elem* kr = src >= 0 ? K + (size_t)src * rs : zero;
+            const Elem* vr = src >= 0 ? V + (size_t)src * rs : zero;
             dma16(kr + 4 * (cl ^ swz_k(row)), slot + blk * 1024);
             dma16(vr + 4 * cl, slot + kTileBytes + blk * 1024);
         }
@@ -297,10 +299,10 @@ struct F32 {
     }
 
     struct DmaLane { uint32_t k[4], v[4]; };
-    __device__ __forceinline__ static void dma_lane(DmaLane& dl, int wv, int lane, int dil) {
+    __device__ __forceinline__ static void dma_lane(DmaLane& dl, int wv, int lane, int step) {
         for (int u = 0; u < 4; ++u) {
             const int row = 4 * (4 * wv + u) + (lane >> 4), cl = lane & 15;
-            const uint32_t r0b = (uint32_t)row * (uint32_t)dil * kRowBytes;
+            const uint32_t r0b = (uint32_t)row * (uint32_t)step * (uint32_t)sizeof(Elem);
             dl.k[u] = r0b + 16u * (uint32_t)(cl ^ swz_k(row));
             dl.v[u] = r0b + 16u * (uint32_t)cl;
         }
@@ -535,7 +537,7 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 // the second (waves 2-3), one 64-key stage each.  Their keys that lie in a row's
 // window, are global, padded or past the end are masked, so each key counts once.
 
-template <class T, bool kCausal, bool kBias, bool kRandom>
+template <class T, bool kCausal, bool kBias, bool kRandom, bool kStrided = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const Params p) {
     using Elem = typename T::Elem;
@@ -567,11 +569,15 @@ void band_kernel(const Params p) {
     const int r0 = (t_in - r * tpr) * kRowsPerBlock;
     if (r0 >= Lr) return;
 
-    const size_t off = (size_t)bh * L * 64;
+    // q, k, v (and q_g, k_g, v_g): row i of (b, h) at b*s_b + h*s_h + i*rs elements,
+    // out at b*o_b + h*o_h + i*o_r (kStrided); else [B][H][L][64] with constant strides.
+    const int rs = kStrided ? p.s_r : 64, ors = kStrided ? p.o_r : 64;
+    const size_t off = kStrided ? (size_t)b * p.s_b + (size_t)h * p.s_h : (size_t)bh * L * 64;
+    const size_t ooff = kStrided ? (size_t)b * p.o_b + (size_t)h * p.o_h : (size_t)bh * L * 64;
     const Elem* Q = reinterpret_cast<const Elem*>(p.q) + off;
     const Elem* K = reinterpret_cast<const Elem*>(p.k) + off;
     const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
-    Elem* O = reinterpret_cast<Elem*>(p.out) + off;
+    Elem* O = reinterpret_cast<Elem*>(p.out) + ooff;
     const uint8_t* pad = p.pad ? p.pad + (size_t)b * L : nullptr;
     // Global set of this sequence: one shared set (gstride 0) or one row per sequence.
     const int gofs = b * p.gstride;
@@ -586,7 +592,7 @@ void band_kernel(const Params p) {
     const int qv = qa + (lane & 31);  // this lane's virtual row
     const bool rows_live = qa < Lr;
     typename T::QOp qop;
-    T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * 64 : nullptr, h2);
+    T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * rs : nullptr, h2);
 
     // Window of a row: keys w steps before it and wr after (wr = 0 in the one-sided
     // variant, which also drops global keys after the row and, for a global row,
@@ -665,9 +671,9 @@ void band_kernel(const Params p) {
         return m;
     };
     typename T::DmaLane dl;
-    T::dma_lane(dl, wv, lane, dil);
+    T::dma_lane(dl, wv, lane, dil * rs);
     // The scalar-base copies use 32-bit per-lane offsets of up to 64 rows dil apart.
-    const bool direct_ok = (uint64_t)dil * kStageKeys * T::kRowBytes < (1ull << 31);
+    const bool direct_ok = (uint64_t)dil * rs * kStageKeys * sizeof(Elem) < (1ull << 31);
     // Copies of stage s into its ring slot: part 0 or 1 of this wave's share, or all.
     int ks_next = 0;  // first key of the band stage copied last (see the stage loop)
     auto issue = [&](int s, int part) __attribute__((always_inline)) -> uint64_t {
@@ -677,14 +683,14 @@ void band_kernel(const Params p) {
             const int kb0 = kRandomBlock * rnd_block(j);
             const uint64_t inv = uniform64(rnd_inv[j]);
             if (inv == 0ull && part == kAllParts && direct_ok) {
-                T::dma_stage_direct(slot, K + (size_t)kb0 * 64, V + (size_t)kb0 * 64, dl, wv);
+                T::dma_stage_direct(slot, K + (size_t)kb0 * rs, V + (size_t)kb0 * rs, dl, wv);
             } else {
-                T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane, part);
+                T::dma_stage(slot, K, V, rs, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : kb0 + kk; }, wv, lane, part);
             }
             return 0ull;
         } else if (is_glob(s)) {
             const int* src = glob_src + kStageKeys * (s - n_pre);
-            T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return src[kk]; }, wv, lane, part);
+            T::dma_stage(slot, K, V, rs, [&](int kk) __attribute__((always_inline)) { return src[kk]; }, wv, lane, part);
             return 0ull;
         } else {
             const int bs = band_u(s);
@@ -692,10 +698,10 @@ void band_kernel(const Params p) {
             const int ks = stage_key(bs);
             ks_next = ks;
             if (inv == 0ull && part == kAllParts && direct_ok) {
-                const size_t row0 = (size_t)(r + ks * dil) * 64;
+                const size_t row0 = (size_t)(r + ks * dil) * rs;
                 T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
             } else {
-                T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
+                T::dma_stage(slot, K, V, rs, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; },
                              wv, lane, part);
             }
             return inv;
@@ -806,7 +812,7 @@ void band_kernel(const Params p) {
         }
         if (t == 0 && ng > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
-            T::dma_rows(gq_rows, [&](int j) __attribute__((always_inline)) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * 64 : zero; },
+            T::dma_rows(gq_rows, [&](int j) __attribute__((always_inline)) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * rs : zero; },
                         wv, lane);
         }
         const char* slot = ring + (t % T::kNS) * T::kStageBytes;
@@ -865,16 +871,16 @@ void band_kernel(const Params p) {
         ks_next = ks;
         char* slot = ring + sl * T::kStageBytes;
         if (!pad && ks >= kb0 && ks + kStageKeys <= kend && direct_ok) {
-            const size_t row0 = (size_t)(r + ks * dil) * 64;
+            const size_t row0 = (size_t)(r + ks * dil) * rs;
             T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
             return 0ull;
         }
         const uint64_t inv = uniform64(band_invalid(u));
         if (inv == 0ull && direct_ok) {
-            const size_t row0 = (size_t)(r + ks * dil) * 64;
+            const size_t row0 = (size_t)(r + ks * dil) * rs;
             T::dma_stage_direct(slot, K + row0, V + row0, dl, wv);
         } else {
-            T::dma_stage(slot, K, V, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv,
+            T::dma_stage(slot, K, V, rs, [&](int kk) __attribute__((always_inline)) { return ((inv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv,
                          lane);
         }
         return inv;
@@ -927,7 +933,7 @@ void band_kernel(const Params p) {
         const int row = r + qv * dil;
         const int vr = qv - r0;  // global rows are written by the merge
         if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) {
-            T::store_row(O + (size_t)row * 64, h2, st.o, scale);
+            T::store_row(O + (size_t)row * ors, h2, st.o, scale);
             if (p.lse && h2 == 0) p.lse[(size_t)bh * L + row] = lse_of(st.cofs, st.l);
         }
     }
@@ -953,7 +959,7 @@ void band_kernel(const Params p) {
             T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
         } else {
             const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
-            T::load_q(gop, gq < ng ? QG + (size_t)p.g[gofs + gq] * 64 : nullptr, h2);
+            T::load_q(gop, gq < ng ? QG + (size_t)p.g[gofs + gq] * rs : nullptr, h2);
         }
         T::scale_q(gop);
         if (gb == 0 && !sep) {
@@ -972,7 +978,7 @@ void band_kernel(const Params p) {
             for (int j = 0; j < 2; ++j) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
-                T::dma_stage(ring + j * T::kStageBytes, KG, VG,
+                T::dma_stage(ring + j * T::kStageBytes, KG, VG, rs,
                              [&](int kk) __attribute__((always_inline)) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             }
             wait_vmcnt<0>();
@@ -1112,8 +1118,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p)
         }
     const float res = l > 0.f ? o / l : 0.f;
     const int g = p.g[gofs + gi];
-    Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bh * L * 64;
-    O[(size_t)g * 64 + d] = T::from_float(res);
+    Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bseq * p.o_b + (size_t)h * p.o_h;
+    O[(size_t)g * p.o_r + d] = T::from_float(res);
     if (p.lse && d == 0) p.lse[(size_t)bh * L + g] = lse_of(M, l);
 }
 
@@ -1145,11 +1151,24 @@ hipError_t static_scratch(void** ptr) {
     return hipSuccess;
 }
 
+namespace {
+template <class T, bool kCausal, bool kBias, bool kRandom>
+void launch_band_t(const Params& p, int blocks, hipStream_t s) {
+    if constexpr (std::is_same_v<T, Bf16>) {
+        if (p.strided) {
+            (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom, true>, dim3(blocks), dim3(kThreads), s, p);
+            return;
+        }
+    }
+    (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom>, dim3(blocks), dim3(kThreads), s, p);
+}
+}  // namespace
+
 hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
     const bool bias = p.bias != nullptr, rnd = p.rnd != nullptr;
-#define LF_BAND(T, C, Bi, R) launch_kernel(band_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
+#define LF_BAND(T, C, Bi, R) launch_band_t<T, C, Bi, R>(p, blocks, s)
 #define LF_BAND_R(T, C, Bi) \
     if (rnd) LF_BAND(T, C, Bi, true); else LF_BAND(T, C, Bi, false)
 #define LF_BAND_BR(T, C) \

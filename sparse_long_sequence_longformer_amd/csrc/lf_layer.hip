@@ -1,11 +1,11 @@
 // gfx950 kernels of the Longformer layer around the sparse attention (bf16 tensors,
 // fp32 arithmetic): the steps between the library GEMMs.  The wide GEMM outputs (the
-// QKV projection and the first feed-forward product) arrive in bf16 (fp32
-// accumulation, rounded once); the two that feed a LayerNorm stay fp32.  All passes
-// are HBM-bound elementwise or row-wise, written for coalesced 16-byte accesses.
+// QKV projection, its bias added in the GEMM epilogue, and the first feed-forward
+// product) arrive in bf16 (fp32 accumulation, rounded once); the two that feed a
+// LayerNorm stay fp32.  The attention reads q, k, v from the QKV output in place and
+// writes its output with the heads merged.  All passes are HBM-bound elementwise or
+// row-wise, written for coalesced 16-byte accesses.
 //
-//   qkv_split:        x W_qkv^T + b_qkv -> q, k, v in [B][H][L][64]
-//   merge_heads:      attention output [B][H][L][64] -> [B][L][H*64]
 //   bias_residual_ln: LayerNorm(y + b + residual) over the features of a row
 //   bias_gelu:        GELU(h + b), GELU(t) = 0.5 t (1 + erf(t / sqrt(2))), erf by the
 //                     rational approximation of Abramowitz and Stegun, Handbook of
@@ -33,36 +33,6 @@ __device__ __forceinline__ f32x8 load8_f32(const float* p) {
 }
 __device__ __forceinline__ void store8_bf16(uint16_t* p, const f32x8& v) {
     *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8));
-}
-
-// One thread per 8 consecutive features of one row of x W_qkv^T ([R][3E], R = B*L).
-__global__ __launch_bounds__(256) void qkv_split_kernel(const uint16_t* qkv, const uint16_t* bias, uint16_t* q,
-                                                        uint16_t* k, uint16_t* v, int L, int E, long long n8) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const int per_row = 3 * E / 8;
-    const long long row = i / per_row;
-    const int f = (int)(i - row * per_row) * 8;  // feature in [0, 3E)
-    const int which = f / E, fe = f - which * E, h = fe >> 6, d = fe & 63;
-    const int H = E >> 6;
-    const long long b = row / L, l = row - b * L;
-    f32x8 t = load8_bf16(qkv + row * 3 * E + f) + load8_bf16(bias + f);
-    uint16_t* dst = which == 0 ? q : (which == 1 ? k : v);
-    store8_bf16(dst + (((b * H + h) * L + l) << 6) + d, t);
-}
-
-// One thread per 8 features: [B][H][L][64] -> [B][L][H*64].
-__global__ __launch_bounds__(256) void merge_heads_kernel(const uint16_t* a, uint16_t* out, int L, int E,
-                                                          long long n8) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const int per_row = E / 8;
-    const long long row = i / per_row;
-    const int fe = (int)(i - row * per_row) * 8, h = fe >> 6, d = fe & 63;
-    const int H = E >> 6;
-    const long long b = row / L, l = row - b * L;
-    *reinterpret_cast<u32x4*>(out + row * E + fe) =
-        *reinterpret_cast<const u32x4*>(a + (((b * H + h) * L + l) << 6) + d);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -140,22 +110,6 @@ __global__ __launch_bounds__(256) void bias_gelu_kernel(const uint16_t* hpre, co
 unsigned blocks_for(long long n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
 
 }  // namespace
-
-hipError_t launch_qkv_split(const void* qkv, const void* bias, void* q, void* k, void* v, int B, int L, int E,
-                            hipStream_t s) {
-    const long long n8 = (long long)B * L * 3 * E / 8;
-    launch_kernel(qkv_split_kernel, dim3(blocks_for(n8, 256)), dim3(256), s, static_cast<const uint16_t*>(qkv),
-                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
-                       static_cast<uint16_t*>(v), L, E, n8);
-    return hipGetLastError();
-}
-
-hipError_t launch_merge_heads(const void* a, void* out, int B, int L, int E, hipStream_t s) {
-    const long long n8 = (long long)B * L * E / 8;
-    launch_kernel(merge_heads_kernel, dim3(blocks_for(n8, 256)), dim3(256), s,
-                       static_cast<const uint16_t*>(a), static_cast<uint16_t*>(out), L, E, n8);
-    return hipGetLastError();
-}
 
 hipError_t launch_bias_residual_ln(const float* y, const void* bias, const void* res, const void* gamma,
                                    const void* beta, float eps, void* out, int E, long long R, hipStream_t s) {
