@@ -234,14 +234,30 @@ struct Bf16 {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
 
-    __device__ __forceinline__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+    // Output row of the lane's query: accumulator group (db, q) of lane-half h2 holds
+    // columns 32*db + 8*q + 4*h2 .. +3.  For each pair of groups q = 2m, 2m+1 the two
+    // lanes of a query swap one group (lane-half 0 keeps q = 2m and takes the other
+    // half's, lane-half 1 keeps q = 2m+1 and takes the other half's), so each lane holds
+    // 8 consecutive columns 32*db + 16*m + 8*h2 .. +7: four 16-byte stores per lane, 32
+    // contiguous bytes per row and instruction.  Every lane takes part in the swaps.
+    struct RowOut { u32x4 c[2][2]; };  // [db][m]
+    __device__ __forceinline__ static void pack_row(RowOut& ro, const f32x16* o, float scale) {
         for (int db = 0; db < 2; ++db)
-            for (int q = 0; q < 4; ++q) {
-                const float a = o[db][4 * q] * scale, b = o[db][4 * q + 1] * scale;
-                const float c = o[db][4 * q + 2] * scale, d = o[db][4 * q + 3] * scale;
-                const u32x2 w = {pack_bf16(a, b), pack_bf16(c, d)};
-                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * h2) = w;
+            for (int m = 0; m < 2; ++m) {
+                const int qe = 2 * m, qo = 2 * m + 1;
+                const uint32_t e0 = pack_bf16(o[db][4 * qe] * scale, o[db][4 * qe + 1] * scale);
+                const uint32_t e1 = pack_bf16(o[db][4 * qe + 2] * scale, o[db][4 * qe + 3] * scale);
+                const uint32_t d0 = pack_bf16(o[db][4 * qo] * scale, o[db][4 * qo + 1] * scale);
+                const uint32_t d1 = pack_bf16(o[db][4 * qo + 2] * scale, o[db][4 * qo + 3] * scale);
+                // lanes 32-63 of the first operand swap with lanes 0-31 of the second
+                const auto x0 = __builtin_amdgcn_permlane32_swap(e0, d0, false, false);
+                const auto x1 = __builtin_amdgcn_permlane32_swap(e1, d1, false, false);
+                ro.c[db][m] = u32x4{x0[0], x1[0], x0[1], x1[1]};
             }
+    }
+    __device__ __forceinline__ static void store_row(Elem* row, int h2, const RowOut& ro) {
+        for (int db = 0; db < 2; ++db)
+            for (int m = 0; m < 2; ++m) *reinterpret_cast<u32x4*>(row + 32 * db + 16 * m + 8 * h2) = ro.c[db][m];
     }
 
     __device__ __forceinline__ static Elem from_float(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -364,11 +380,16 @@ struct F32 {
             }
     }
 
-    __device__ __forceinline__ static void store_row(Elem* row, int h2, const f32x16* o, float scale) {
+    struct RowOut { f32x16 o[2]; };
+    __device__ __forceinline__ static void pack_row(RowOut& ro, const f32x16* o, float scale) {
+        for (int db = 0; db < 2; ++db)
+            for (int i = 0; i < 16; ++i) ro.o[db][i] = o[db][i] * scale;
+    }
+    __device__ __forceinline__ static void store_row(Elem* row, int h2, const RowOut& ro) {
         for (int db = 0; db < 2; ++db)
             for (int q = 0; q < 4; ++q) {
                 f32x4 t;
-                for (int j = 0; j < 4; ++j) t[j] = o[db][4 * q + j] * scale;
+                for (int j = 0; j < 4; ++j) t[j] = ro.o[db][4 * q + j];
                 *reinterpret_cast<f32x4*>(row + 32 * db + 8 * q + 4 * h2) = t;
             }
     }
@@ -929,11 +950,13 @@ void band_kernel(const Params p) {
     }
 
     const float scale = st.l > 0.f ? 1.f / st.l : 0.f;
+    typename T::RowOut ro;
+    T::pack_row(ro, st.o, scale);
     if (qv < Lr) {
         const int row = r + qv * dil;
         const int vr = qv - r0;  // global rows are written by the merge
         if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) {
-            T::store_row(O + (size_t)row * ors, h2, st.o, scale);
+            T::store_row(O + (size_t)row * ors, h2, ro);
             if (p.lse && h2 == 0) p.lse[(size_t)bh * L + row] = lse_of(st.cofs, st.l);
         }
     }
