@@ -394,12 +394,7 @@ __device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int A, int 
     t.h = t.bh % p.H;
     t.b = t.bh / p.H;
     t.dil = p.dil[t.h];
-    const int tpr = ((p.L + t.dil - 1) / t.dil + kRowsPerBlock - 1) / kRowsPerBlock;
-    t.r = t.t_in / tpr;
-    if (t.r >= t.dil) return false;
-    t.Lr = (p.L - t.r + t.dil - 1) / t.dil;
-    t.r0 = (t.t_in - t.r * tpr) * kRowsPerBlock;
-    if (t.r0 >= t.Lr) return false;
+    if (!decode_tile(t.t_in, p.L, t.dil, t.r, t.Lr, t.r0)) return false;
     t.kb0 = max(0, t.r0 - A);
     t.kend = min(t.Lr, t.r0 + kRowsPerBlock + B);
     t.nb = (t.r0 - t.kb0 + kStageKeys - 1) / kStageKeys;

@@ -185,8 +185,27 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int mode, uint32_t inv32,
 // of residue class r = t / tpr (tpr tiles per class, classes 0..dil-1 of a length-L
 // sequence).  Every argument is uniform, so this is scalar arithmetic.
 __device__ __forceinline__ bool tile_exists(int t, int tpr, int dil, int L, int rows) {
+    if (dil == 1) return t * rows < L;  // one class: no division
     const int r = t / tpr;
     return r < dil && (t - r * tpr) * rows < (L - r + dil - 1) / dil;
+}
+
+// Residue class r, class length Lr and first class row r0 of work-group slot t_in of a
+// head with dilation dil (tiles of kRowsPerBlock class rows, ceil(ceil(L/dil)/rows)
+// per class); false when the slot holds no tile.  dil == 1 needs no division.
+__device__ __forceinline__ bool decode_tile(int t_in, int L, int dil, int& r, int& Lr, int& r0) {
+    if (dil == 1) {
+        r = 0;
+        Lr = L;
+        r0 = t_in * kRowsPerBlock;
+        return r0 < L;
+    }
+    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    r = t_in / tpr;
+    if (r >= dil) return false;
+    Lr = (L - r + dil - 1) / dil;
+    r0 = (t_in - r * tpr) * kRowsPerBlock;
+    return r0 < Lr;
 }
 
 // Waves of a merge work-group: enough for one chunk of `chunk` tiles per wave, at most

@@ -583,12 +583,8 @@ void band_kernel(const Params p) {
     const int bh = pid / p.tiles_per_head, t_in = pid - bh * p.tiles_per_head;
     const int h = bh % p.H, b = bh / p.H;
     const int L = p.L, w = p.w, dil = p.dil[h];
-    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;  // tiles per residue
-    const int r = t_in / tpr;
-    if (r >= dil) return;
-    const int Lr = (L - r + dil - 1) / dil;  // rows in residue class r
-    const int r0 = (t_in - r * tpr) * kRowsPerBlock;
-    if (r0 >= Lr) return;
+    int r, Lr, r0;  // residue class, its length, the tile's first class row
+    if (!decode_tile(t_in, L, dil, r, Lr, r0)) return;
 
     // q, k, v (and q_g, k_g, v_g): row i of (b, h) at b*s_b + h*s_h + i*rs elements,
     // out at b*o_b + h*o_h + i*o_r (kStrided); else [B][H][L][64] with constant strides.
