@@ -122,6 +122,14 @@ bool overlaps(const void* a, const void* b, size_t n) {
     return x < y + n && y < x + n;
 }
 
+// The dilation shared by every head of dil[0..H), or 0 when the heads differ (the
+// kernels then read each head's own entry).
+int uniform_dilation(const int* dil, int H) {
+    for (int i = 1; i < H; ++i)
+        if (dil[i] != dil[0]) return 0;
+    return H > 0 ? dil[0] : 0;
+}
+
 // [a, a + na) and [b, b + nb) intersect.
 bool overlaps2(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -586,6 +594,7 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;
     p.bias = h->bias;
     p.bias_w = h->bias_w;
+    p.dil_u = uniform_dilation(pl.dil, H);
     if (strides) {
         if (h->dtype != LF_BF16) return fail(h, LF_ERR_UNSUPPORTED, "strided tensors need a bf16 handle");
         p.strided = 1;
@@ -744,6 +753,7 @@ lf_status backward_impl(lf_attn_t h, const void* q, const void* k, const void* v
     p.bias = h->bias;
     p.bias_w = h->bias_w;
     p.dtype = h->dtype;
+    p.dil_u = uniform_dilation(pl.dil, H);
 
     // Workspace: three row-statistic arrays, then the global partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");

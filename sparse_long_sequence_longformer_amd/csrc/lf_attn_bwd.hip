@@ -393,7 +393,7 @@ __device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int A, int 
     t.t_in = pid - t.bh * p.tiles_per_head;
     t.h = t.bh % p.H;
     t.b = t.bh / p.H;
-    t.dil = p.dil[t.h];
+    t.dil = head_dil(p.dil_u, p.dil, t.h);
     if (!decode_tile(t.t_in, p.L, t.dil, t.r, t.Lr, t.r0)) return false;
     t.kb0 = max(0, t.r0 - A);
     t.kend = min(t.Lr, t.r0 + kRowsPerBlock + B);
@@ -499,6 +499,10 @@ void bwd_dq_kernel(const BwdParams p) {
     // Keys of a row: w class steps before it and wr after (wr = 0 one-sided).
     constexpr bool causal = kCausal;
     const int wr = causal ? 0 : p.w, span = p.w + wr;
+    // The kernel arguments of the set-up, read in one batch: left alone, the compiler
+    // waits for each argument load at its first use, one round trip after another.
+    asm volatile("" ::"s"(gridDim.x), "s"(p.tiles_per_head), "s"(p.H), "s"(p.L), "s"(p.w), "s"(p.dil_u),
+                 "s"(p.gstride), "s"(p.n_g), "s"(p.q), "s"(p.dout), "s"(p.lse2), "s"(p.dsum), "s"(p.pad));
     Tile tl;
     if (!tile_of(tl, p, p.w, wr)) return;
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
@@ -830,6 +834,10 @@ void bwd_dkv_kernel(const BwdParams p) {
     // before its key).
     constexpr bool causal = kCausal;
     const int wl = causal ? 0 : p.w, span = wl + p.w;
+    // The kernel arguments of the set-up, read in one batch (as in the dQ kernel).
+    asm volatile("" ::"s"(gridDim.x), "s"(p.tiles_per_head), "s"(p.H), "s"(p.L), "s"(p.w), "s"(p.dil_u),
+                 "s"(p.gstride), "s"(p.n_g), "s"(kGlobalProj ? p.kg : p.k), "s"(kGlobalProj ? p.vg : p.v), "s"(p.pad),
+                 "s"(p.sep));
     Tile tl;
     if (!tile_of(tl, p, wl, p.w)) return;
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
@@ -1073,7 +1081,7 @@ void bwd_dkv_kernel(const BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // Global rows and keys: one work-group of W <= kBwdMergeWaves waves per (global index,
-// b*H + h), lane = column (W = blockDim / 64, chosen by the host).  Wave x sums tiles
+// h, b) (grid x, y, z), lane = column (W = blockDim / 64, chosen by the host).  Wave x sums tiles
 // x, x + W, ... (the loads of kBwdMergeChunk tiles issued together, absent tiles read
 // tile 0 and are dropped), then the wave sums are added in wave order.
 
@@ -1083,15 +1091,22 @@ template <class T>
 __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const BwdParams p) {
     using Elem = typename T::Elem;
     __shared__ float red[kBwdMergeWaves][3][64];
-    const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
+    const int gi = blockIdx.x, h = blockIdx.y, bseq = blockIdx.z, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int W = blockDim.x >> 6;
-    const int h = bh % p.H, dil = p.dil[h], L = p.L;
-    const int bseq = bh / p.H, gofs = bseq * p.gstride;
+    // Kernel arguments read in one batch (every index is a grid coordinate); the output
+    // row's global position and pointers too, so that the end waits for none of them.
+    asm volatile("" ::"s"(p.H), "s"(p.L), "s"(p.n_g), "s"(p.gstride), "s"(p.tiles_per_head), "s"(p.n_gblk),
+                 "s"(p.dil[h]), "s"(p.gcnt[bseq]), "s"(p.g[gi]), "s"(p.ws_dq), "s"(p.ws_dk), "s"(p.ws_dv), "s"(p.ws_dkg),
+                 "s"(p.ws_dvg), "s"(p.sep), "s"(p.dq), "s"(p.dk), "s"(p.dv), "s"(p.dqg));
+    const int bh = bseq * p.H + h, dil = p.dil[h], L = p.L, gofs = bseq * p.gstride;
     if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
-    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int W = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);  // = blockDim.x / 64
+    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;  // unused when dil == 1
     const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
     const size_t base = (size_t)bh * p.tiles_per_head * ngq * 64 + (size_t)gi * 64 + d;
+    // the global key's own-tile dK and dV (wave 0 adds them), loaded with the first chunk
+    const size_t own = ((size_t)bh * ngq + gi) * 64 + d;
+    const float own_k = wv == 0 ? p.ws_dkg[own] : 0.f, own_v = wv == 0 ? p.ws_dvg[own] : 0.f;
     float sq = 0.f, sk = 0.f, sv = 0.f;
     for (int c0 = 0; c0 * W < p.tiles_per_head; c0 += kBwdMergeChunk) {
         float a[kBwdMergeChunk], b[kBwdMergeChunk], c[kBwdMergeChunk];
@@ -1121,10 +1136,9 @@ __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const Bw
     red[wv][2][d] = sv;
     __syncthreads();
     if (wv != 0) return;
-    const size_t own = ((size_t)bh * ngq + gi) * 64 + d;
     sq = 0.f;
-    sk = p.ws_dkg[own];
-    sv = p.ws_dvg[own];
+    sk = own_k;
+    sv = own_v;
     for (int x = 0; x < W; ++x) {
         sq += red[x][0][d];
         sk += red[x][1][d];
@@ -1207,9 +1221,10 @@ hipError_t bwd_dkv_global_proj_t(const BwdParams& p, hipStream_t s) {
 
 template <class T>
 hipError_t bwd_merge_t(const BwdParams& p, hipStream_t s) {
-    if (p.n_g == 0) return hipSuccess;
+    if (p.n_g == 0 || p.B == 0) return hipSuccess;
+    if (p.B > 65535) return hipErrorInvalidConfiguration;  // grid z
     const int waves = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);
-    launch_kernel(bwd_merge_kernel<T>, dim3(p.n_g, p.B * p.H), dim3(64 * waves), s, p);
+    launch_kernel(bwd_merge_kernel<T>, dim3(p.n_g, p.H, p.B), dim3(64 * waves), s, p);
     return hipGetLastError();
 }
 

@@ -190,6 +190,18 @@ __device__ __forceinline__ bool tile_exists(int t, int tpr, int dil, int L, int 
     return r < dil && (t - r * tpr) * rows < (L - r + dil - 1) / dil;
 }
 
+// Dilation of head h: the one every head shares (dil_u != 0, no memory access), else
+// the head's own entry.  The empty asm keeps the load inside the branch: the compiler
+// would otherwise issue it (and wait for it) unconditionally.
+__device__ __forceinline__ int head_dil(int dil_u, const int* dil, int h) {
+    int d = dil_u;
+    if (d == 0) {
+        asm volatile("");
+        d = dil[h];
+    }
+    return d;
+}
+
 // Residue class r, class length Lr and first class row r0 of work-group slot t_in of a
 // head with dilation dil (tiles of kRowsPerBlock class rows, ceil(ceil(L/dil)/rows)
 // per class); false when the slot holds no tile.  dil == 1 needs no division.
@@ -209,8 +221,9 @@ __device__ __forceinline__ bool decode_tile(int t_in, int L, int dil, int& r, in
 }
 
 // Waves of a merge work-group: enough for one chunk of `chunk` tiles per wave, at most
-// `most`.
-inline int merge_waves(int tiles, int chunk, int most) {
+// `most`.  The launch uses it for the block size and the kernel recomputes it from the
+// same arguments (no read of the block size).
+__host__ __device__ inline int merge_waves(int tiles, int chunk, int most) {
     const int w = (tiles + chunk - 1) / chunk;
     return w < 1 ? 1 : (w > most ? most : w);
 }

@@ -62,6 +62,7 @@ struct Params {
     long long s_b, s_h, o_b, o_h;
     int s_r, o_r;
     int strided;  // strides other than [B][H][L][64] (bf16 only)
+    int dil_u;    // the dilation of every head when they share one, else 0
 };
 
 // Events of the kernel launch in progress, set by the host around one launch when
@@ -138,6 +139,7 @@ struct BwdParams {
     int g[LF_MAX_GLOBALS];
     int gcnt[LF_MAX_GLOBALS];
     int dtype;  // LF_BF16 or LF_F32 tensors
+    int dil_u;  // the dilation of every head when they share one, else 0
 };
 
 // Launchers of the layer's pointwise passes (defined in lf_layer.hip).

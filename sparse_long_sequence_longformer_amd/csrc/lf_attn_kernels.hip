@@ -579,10 +579,23 @@ void band_kernel(const Params p) {
 
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    const int pid = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = pid / p.tiles_per_head, t_in = pid - bh * p.tiles_per_head;
-    const int h = bh % p.H, b = bh / p.H;
-    const int L = p.L, w = p.w, dil = p.dil[h];
+    // The kernel arguments of the set-up, read in one batch: left alone, the compiler
+    // waits for each argument load at its first use, one memory round trip after
+    // another across the set-up's branches.
+    const int nblk = gridDim.x, tph = p.tiles_per_head, H = p.H, L = p.L, w = p.w, dil_u = p.dil_u;
+    const int gstride = p.gstride, n_g = p.n_g;
+    const void* const q_arg = p.q;
+    const void* const k_arg = p.k;
+    const void* const v_arg = p.v;
+    const void* const kg_arg = p.kg;
+    const uint8_t* const pad_arg = p.pad;
+    asm volatile("" ::"s"(nblk), "s"(tph), "s"(H), "s"(L), "s"(w), "s"(dil_u), "s"(gstride), "s"(n_g), "s"(q_arg),
+                 "s"(k_arg), "s"(v_arg), "s"(kg_arg), "s"(pad_arg));
+    if constexpr (kStrided) asm volatile("" ::"s"(p.s_b), "s"(p.s_h), "s"(p.s_r), "s"(p.o_b), "s"(p.o_h), "s"(p.o_r));
+    const int pid = xcd_remap(blockIdx.x, nblk);
+    const int bh = pid / tph, t_in = pid - bh * tph;
+    const int h = bh % H, b = bh / H;
+    const int dil = head_dil(dil_u, p.dil, h);
     int r, Lr, r0;  // residue class, its length, the tile's first class row
     if (!decode_tile(t_in, L, dil, r, Lr, r0)) return;
 
@@ -591,18 +604,18 @@ void band_kernel(const Params p) {
     const int rs = kStrided ? p.s_r : 64, ors = kStrided ? p.o_r : 64;
     const size_t off = kStrided ? (size_t)b * p.s_b + (size_t)h * p.s_h : (size_t)bh * L * 64;
     const size_t ooff = kStrided ? (size_t)b * p.o_b + (size_t)h * p.o_h : (size_t)bh * L * 64;
-    const Elem* Q = reinterpret_cast<const Elem*>(p.q) + off;
-    const Elem* K = reinterpret_cast<const Elem*>(p.k) + off;
-    const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
+    const Elem* Q = reinterpret_cast<const Elem*>(q_arg) + off;
+    const Elem* K = reinterpret_cast<const Elem*>(k_arg) + off;
+    const Elem* V = reinterpret_cast<const Elem*>(v_arg) + off;
     Elem* O = reinterpret_cast<Elem*>(p.out) + ooff;
-    const uint8_t* pad = p.pad ? p.pad + (size_t)b * L : nullptr;
+    const uint8_t* pad = pad_arg ? pad_arg + (size_t)b * L : nullptr;
     // Global set of this sequence: one shared set (gstride 0) or one row per sequence.
-    const int gofs = b * p.gstride;
-    const int ng = p.gstride ? p.gcnt[b] : p.n_g;
+    const int gofs = b * gstride;
+    const int ng = gstride ? p.gcnt[b] : n_g;
     // Tensors of the global rows' own attention (c): the separate projections if given.
-    const bool sep = p.kg != nullptr;
+    const bool sep = kg_arg != nullptr;
     const Elem* QG = sep ? reinterpret_cast<const Elem*>(p.qg) + off : Q;
-    const Elem* KG = sep ? reinterpret_cast<const Elem*>(p.kg) + off : K;
+    const Elem* KG = sep ? reinterpret_cast<const Elem*>(kg_arg) + off : K;
     const Elem* VG = sep ? reinterpret_cast<const Elem*>(p.vg) + off : V;
 
     const int qa = r0 + 32 * wv;      // first virtual row of this wave
@@ -967,7 +980,7 @@ void band_kernel(const Params p) {
     __shared__ float red_ml[kWaves][32][2];
     float* red_o = reinterpret_cast<float*>(ring);  // kWaves x 32 x 64 floats = 32 KiB
     const int home_end = min(Lr, r0 + kRowsPerBlock);
-    const size_t part0 = ((size_t)bh * p.tiles_per_head + t_in) * p.n_gblk * kGlobalQueriesPerBlock;
+    const size_t part0 = ((size_t)bh * tph + t_in) * p.n_gblk * kGlobalQueriesPerBlock;
     const int hs = wv >> 1, hsub = wv & 1;  // wave wv folds home keys 32*wv .. 32*wv+31
     const int n_gblk_b = (ng + kGlobalQueriesPerBlock - 1) / kGlobalQueriesPerBlock;  // this sequence's blocks
     for (int gb = 0; gb < n_gblk_b; ++gb) {
@@ -1063,7 +1076,7 @@ void band_kernel(const Params p) {
 }
 
 // (d) Merge of the global-row partials: one work-group of W <= kMergeWaves waves per
-// (global query, b*H + h), lane = output column (W = blockDim / 64, chosen by the host
+// (global query, h, b) (grid x, y, z), lane = output column (W = blockDim / 64, chosen by the host
 // so that one chunk per wave covers a head's tiles).  Wave x takes tiles x, x + W, ...
 // in chunks of kMergeChunk whose loads are issued together (absent tiles read tile 0
 // and are dropped after the load, so there is no branch between the loads); within a
@@ -1073,33 +1086,46 @@ template <class T>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p) {
     using Elem = typename T::Elem;
     __shared__ float red[kMergeWaves][3][64];
-    const int gi = blockIdx.x, bh = blockIdx.y, d = threadIdx.x & 63;
+    const int gi = blockIdx.x, h = blockIdx.y, bseq = blockIdx.z, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int W = blockDim.x >> 6;
-    const int h = bh % p.H, dil = p.dil[h], L = p.L;
-    const int bseq = bh / p.H, gofs = bseq * p.gstride;
-    if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
-    const int rows = p.rows_per_block;
-    const int tpr = ((L + dil - 1) / dil + rows - 1) / rows;
-    const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
-    const size_t base = (size_t)bh * p.tiles_per_head * n_gq + gi;
+    // Kernel arguments, read in one batch: the compiler would wait for each at its first
+    // use.  Every index is a grid coordinate, so none waits for another argument.
+    const int H = p.H, L = p.L, n_g = p.n_g, gstride = p.gstride, tph = p.tiles_per_head;
+    const int rows = p.rows_per_block, n_gblk = p.n_gblk, dil = p.dil[h], cnt = p.gcnt[bseq], g_shared = p.g[gi];
+    const float* const ws_ml = p.ws_ml;
+    const float* const ws_acc = p.ws_acc;
+    Elem* const out_arg = reinterpret_cast<Elem*>(p.out);
+    float* const lse_arg = p.lse;
+    const long long o_b = p.o_b, o_h = p.o_h;
+    const int o_r = p.o_r;
+    asm volatile("" ::"s"(H), "s"(L), "s"(n_g), "s"(gstride), "s"(tph), "s"(rows), "s"(n_gblk), "s"(dil),
+                 "s"(cnt), "s"(g_shared), "s"(ws_ml), "s"(ws_acc), "s"(out_arg), "s"(lse_arg), "s"(o_b), "s"(o_h),
+                 "s"(o_r));
+    const int bh = bseq * H + h, gofs = bseq * gstride;
+    if (gi >= (gstride ? cnt : n_g)) return;  // this sequence has fewer globals
+    const int W = merge_waves(tph, kMergeChunk, kMergeWaves);  // = blockDim.x / 64
+    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + rows - 1) / rows;  // unused when dil == 1
+    const int n_gq = n_gblk * kGlobalQueriesPerBlock;
+    const size_t base = (size_t)bh * tph * n_gq + gi;
+    const int g = gstride ? p.g[gofs + gi] : g_shared;  // loaded while the partials are in flight
     float M = kNegInf, l = 0.f, o = 0.f;
-    for (int c0 = 0; c0 * W < p.tiles_per_head; c0 += kMergeChunk) {
+    for (int c0 = 0; c0 * W < tph; c0 += kMergeChunk) {
         float mt[kMergeChunk], lt[kMergeChunk], ot[kMergeChunk];
         bool ex[kMergeChunk];
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
             const int t = (c0 + j) * W + wv;
-            ex[j] = t < p.tiles_per_head && tile_exists(t, tpr, dil, L, rows);
+            ex[j] = t < tph && tile_exists(t, tpr, dil, L, rows);
         }
         __builtin_amdgcn_sched_barrier(0);  // every test before the first load
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
             const size_t idx = base + (ex[j] ? (size_t)((c0 + j) * W + wv) * n_gq : 0);
-            mt[j] = p.ws_ml[2 * idx];
-            lt[j] = p.ws_ml[2 * idx + 1];
-            ot[j] = p.ws_acc[idx * 64 + d];
+            mt[j] = ws_ml[2 * idx];
+            lt[j] = ws_ml[2 * idx + 1];
+            ot[j] = ws_acc[idx * 64 + d];
         }
+        if (c0 == 0) asm volatile("" ::"s"(g));
         float Mc = kNegInf;
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
@@ -1136,10 +1162,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p)
             o += red[x][2][d] * e;
         }
     const float res = l > 0.f ? o / l : 0.f;
-    const int g = p.g[gofs + gi];
-    Elem* O = reinterpret_cast<Elem*>(p.out) + (size_t)bseq * p.o_b + (size_t)h * p.o_h;
-    O[(size_t)g * p.o_r + d] = T::from_float(res);
-    if (p.lse && d == 0) p.lse[(size_t)bh * L + g] = lse_of(M, l);
+    Elem* O = out_arg + (size_t)bseq * o_b + (size_t)h * o_h;
+    O[(size_t)g * o_r + d] = T::from_float(res);
+    if (lse_arg && d == 0) lse_arg[(size_t)bh * L + g] = lse_of(M, l);
 }
 
 }  // namespace
@@ -1204,8 +1229,9 @@ hipError_t launch_band(const Params& p, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_merge(const Params& p, int dtype, hipStream_t s) {
-    if (p.n_g == 0) return hipSuccess;
-    const dim3 grid(p.n_g, p.B * p.H);
+    if (p.n_g == 0 || p.B == 0) return hipSuccess;
+    if (p.B > 65535) return hipErrorInvalidConfiguration;  // grid z
+    const dim3 grid(p.n_g, p.H, p.B);
     const int waves = merge_waves(p.tiles_per_head, kMergeChunk, kMergeWaves);
     if (dtype == LF_BF16)
         launch_kernel(merge_kernel<Bf16>, grid, dim3(64 * waves), s, p);
