@@ -17,6 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfattn.so")
 
 SOURCES = ["lf_attn.cpp", "lf_attn_kernels.hip", "lf_attn_bwd.hip", "lf_layer.hip"]
+# Kernel arguments preloaded into scalar registers at wave launch (the leading scalar
+# arguments of each kernel of the file, up to this many; a kernel whose first argument
+# is a parameter struct gets none).  Firmware without preloading runs the compiler's
+# own fallback, which loads them.
+PRELOAD_ARGS = {"lf_attn_kernels.hip": 7}
 ARCH = "gfx950"
 
 
@@ -59,7 +64,8 @@ def build(verbose: bool = False) -> str:
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *compile_flags(), *lang, "-c", path, "-o", obj]
+        pre = ["-mllvm", f"-amdgpu-kernarg-preload-count={PRELOAD_ARGS[src]}"] if src in PRELOAD_ARGS else []
+        cmd = [cc, *compile_flags(), *pre, *lang, "-c", path, "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
     # hipBLASLt serves the layer's plain GEMMs

@@ -560,7 +560,8 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 
 template <class T, bool kCausal, bool kBias, bool kRandom, bool kStrided = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
-void band_kernel(const Params p) {
+void band_kernel(const int nblk, const int tph, const int H, const int L, const int dil_u, const void* const q_arg,
+                 const Params p) {
     using Elem = typename T::Elem;
     __shared__ __attribute__((aligned(16))) char ring[T::kNS * T::kStageBytes];
     __shared__ uint64_t band_mask[kMaskRing];        // invalid-key bits of band stages
@@ -579,18 +580,12 @@ void band_kernel(const Params p) {
 
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    // The kernel arguments of the set-up, read in one batch: left alone, the compiler
-    // waits for each argument load at its first use, one memory round trip after
-    // another across the set-up's branches.
-    const int nblk = gridDim.x, tph = p.tiles_per_head, H = p.H, L = p.L, w = p.w, dil_u = p.dil_u;
-    const int gstride = p.gstride, n_g = p.n_g;
-    const void* const q_arg = p.q;
-    const void* const k_arg = p.k;
-    const void* const v_arg = p.v;
-    const void* const kg_arg = p.kg;
-    const uint8_t* const pad_arg = p.pad;
-    asm volatile("" ::"s"(nblk), "s"(tph), "s"(H), "s"(L), "s"(w), "s"(dil_u), "s"(gstride), "s"(n_g), "s"(q_arg),
-                 "s"(k_arg), "s"(v_arg), "s"(kg_arg), "s"(pad_arg));
+    // The leading arguments (the grid size, p.tiles_per_head, p.H, p.L, p.dil_u, p.q)
+    // are the tile decode's and the Q load's; the build preloads them into scalar
+    // registers, so neither waits for memory.  The other arguments of the set-up are read
+    // in one batch after the Q load is issued: left alone, the compiler waits for each
+    // argument load at its first use, one memory round trip after another across the
+    // set-up's branches.
     if constexpr (kStrided) asm volatile("" ::"s"(p.s_b), "s"(p.s_h), "s"(p.s_r), "s"(p.o_b), "s"(p.o_h), "s"(p.o_r));
     const int pid = xcd_remap(blockIdx.x, nblk);
     const int bh = pid / tph, t_in = pid - bh * tph;
@@ -605,6 +600,18 @@ void band_kernel(const Params p) {
     const size_t off = kStrided ? (size_t)b * p.s_b + (size_t)h * p.s_h : (size_t)bh * L * 64;
     const size_t ooff = kStrided ? (size_t)b * p.o_b + (size_t)h * p.o_h : (size_t)bh * L * 64;
     const Elem* Q = reinterpret_cast<const Elem*>(q_arg) + off;
+    const int qa = r0 + 32 * wv;      // first virtual row of this wave
+    const int qv = qa + (lane & 31);  // this lane's virtual row
+    const bool rows_live = qa < Lr;
+    typename T::QOp qop;
+    T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * rs : nullptr, h2);
+
+    const int w = p.w, gstride = p.gstride, n_g = p.n_g;
+    const void* const k_arg = p.k;
+    const void* const v_arg = p.v;
+    const void* const kg_arg = p.kg;
+    const uint8_t* const pad_arg = p.pad;
+    asm volatile("" ::"s"(w), "s"(gstride), "s"(n_g), "s"(k_arg), "s"(v_arg), "s"(kg_arg), "s"(pad_arg));
     const Elem* K = reinterpret_cast<const Elem*>(k_arg) + off;
     const Elem* V = reinterpret_cast<const Elem*>(v_arg) + off;
     Elem* O = reinterpret_cast<Elem*>(p.out) + ooff;
@@ -617,12 +624,6 @@ void band_kernel(const Params p) {
     const Elem* QG = sep ? reinterpret_cast<const Elem*>(p.qg) + off : Q;
     const Elem* KG = sep ? reinterpret_cast<const Elem*>(kg_arg) + off : K;
     const Elem* VG = sep ? reinterpret_cast<const Elem*>(p.vg) + off : V;
-
-    const int qa = r0 + 32 * wv;      // first virtual row of this wave
-    const int qv = qa + (lane & 31);  // this lane's virtual row
-    const bool rows_live = qa < Lr;
-    typename T::QOp qop;
-    T::load_q(qop, qv < Lr ? Q + (size_t)(r + qv * dil) * rs : nullptr, h2);
 
     // Window of a row: keys w steps before it and wr after (wr = 0 in the one-sided
     // variant, which also drops global keys after the row and, for a global row,
@@ -1076,38 +1077,39 @@ void band_kernel(const Params p) {
 }
 
 // (d) Merge of the global-row partials: one work-group of W <= kMergeWaves waves per
-// (global query, h, b) (grid x, y, z), lane = output column (W = blockDim / 64, chosen by the host
+// (global query, h, b) (grid x, y, z), lane = output column (W = blockDim / 64, chosen
 // so that one chunk per wave covers a head's tiles).  Wave x takes tiles x, x + W, ...
 // in chunks of kMergeChunk whose loads are issued together (absent tiles read tile 0
 // and are dropped after the load, so there is no branch between the loads); within a
 // chunk the maximum comes first and the weighted sums are added in tile order, and the
 // wave states are combined in wave order: the result does not depend on timing.
-template <class T>
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p) {
+//
+// The leading arguments (p.tiles_per_head, the partial rows per tile n_gblk * 32, p.H,
+// p.L, p.dil_u, p.ws_ml, p.ws_acc) are preloaded into scalar registers by the build, so
+// the first partial loads wait for no argument; the other arguments are read while
+// those loads are in flight.  kDilU: every head has dilation dil_u (no read of p.dil,
+// whose wait would come before the partial loads).
+template <class T, bool kDilU>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const int tph, const int n_gq, const int H,
+                                                                 const int L, const int dil_u,
+                                                                 const float* const ws_ml,
+                                                                 const float* const ws_acc, const Params p) {
     using Elem = typename T::Elem;
     __shared__ float red[kMergeWaves][3][64];
     const int gi = blockIdx.x, h = blockIdx.y, bseq = blockIdx.z, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Kernel arguments, read in one batch: the compiler would wait for each at its first
-    // use.  Every index is a grid coordinate, so none waits for another argument.
-    const int H = p.H, L = p.L, n_g = p.n_g, gstride = p.gstride, tph = p.tiles_per_head;
-    const int rows = p.rows_per_block, n_gblk = p.n_gblk, dil = p.dil[h], cnt = p.gcnt[bseq], g_shared = p.g[gi];
-    const float* const ws_ml = p.ws_ml;
-    const float* const ws_acc = p.ws_acc;
+    const int dil = kDilU ? dil_u : p.dil[h];
+    const int bh = bseq * H + h;
+    const int W = merge_waves(tph, kMergeChunk, kMergeWaves);  // = blockDim.x / 64
+    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;  // unused when dil == 1
+    // gi < n_g <= n_gq: the partial loads below stay in bounds even for a sequence with
+    // fewer globals, whose work-groups drop what they loaded and return after the loop.
+    const size_t base = (size_t)bh * tph * n_gq + gi;
+    const int n_g = p.n_g, gstride = p.gstride, cnt = p.gcnt[bseq], g_shared = p.g[gi];
     Elem* const out_arg = reinterpret_cast<Elem*>(p.out);
     float* const lse_arg = p.lse;
     const long long o_b = p.o_b, o_h = p.o_h;
     const int o_r = p.o_r;
-    asm volatile("" ::"s"(H), "s"(L), "s"(n_g), "s"(gstride), "s"(tph), "s"(rows), "s"(n_gblk), "s"(dil),
-                 "s"(cnt), "s"(g_shared), "s"(ws_ml), "s"(ws_acc), "s"(out_arg), "s"(lse_arg), "s"(o_b), "s"(o_h),
-                 "s"(o_r));
-    const int bh = bseq * H + h, gofs = bseq * gstride;
-    if (gi >= (gstride ? cnt : n_g)) return;  // this sequence has fewer globals
-    const int W = merge_waves(tph, kMergeChunk, kMergeWaves);  // = blockDim.x / 64
-    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + rows - 1) / rows;  // unused when dil == 1
-    const int n_gq = n_gblk * kGlobalQueriesPerBlock;
-    const size_t base = (size_t)bh * tph * n_gq + gi;
-    const int g = gstride ? p.g[gofs + gi] : g_shared;  // loaded while the partials are in flight
     float M = kNegInf, l = 0.f, o = 0.f;
     for (int c0 = 0; c0 * W < tph; c0 += kMergeChunk) {
         float mt[kMergeChunk], lt[kMergeChunk], ot[kMergeChunk];
@@ -1115,7 +1117,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p)
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
             const int t = (c0 + j) * W + wv;
-            ex[j] = t < tph && tile_exists(t, tpr, dil, L, rows);
+            ex[j] = t < tph && tile_exists(t, tpr, dil, L, kRowsPerBlock);
         }
         __builtin_amdgcn_sched_barrier(0);  // every test before the first load
 #pragma unroll
@@ -1125,7 +1127,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p)
             lt[j] = ws_ml[2 * idx + 1];
             ot[j] = ws_acc[idx * 64 + d];
         }
-        if (c0 == 0) asm volatile("" ::"s"(g));
         float Mc = kNegInf;
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
@@ -1146,6 +1147,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Params p)
         o = o * a + oc * b;
         M = Mn;
     }
+    if (gi >= (gstride ? cnt : n_g)) return;  // this sequence has fewer globals
+    const int g = gstride ? p.g[bseq * gstride + gi] : g_shared;  // position of this global row
     red[wv][0][d] = M;
     red[wv][1][d] = l;
     red[wv][2][d] = o;
@@ -1200,11 +1203,13 @@ template <class T, bool kCausal, bool kBias, bool kRandom>
 void launch_band_t(const Params& p, int blocks, hipStream_t s) {
     if constexpr (std::is_same_v<T, Bf16>) {
         if (p.strided) {
-            (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom, true>, dim3(blocks), dim3(kThreads), s, p);
+            (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom, true>, dim3(blocks), dim3(kThreads), s, blocks,
+                                p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p);
             return;
         }
     }
-    (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom>, dim3(blocks), dim3(kThreads), s, p);
+    (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom>, dim3(blocks), dim3(kThreads), s, blocks,
+                        p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p);
 }
 }  // namespace
 
@@ -1233,10 +1238,16 @@ hipError_t launch_merge(const Params& p, int dtype, hipStream_t s) {
     if (p.B > 65535) return hipErrorInvalidConfiguration;  // grid z
     const dim3 grid(p.n_g, p.H, p.B);
     const int waves = merge_waves(p.tiles_per_head, kMergeChunk, kMergeWaves);
-    if (dtype == LF_BF16)
-        launch_kernel(merge_kernel<Bf16>, grid, dim3(64 * waves), s, p);
-    else
-        launch_kernel(merge_kernel<F32>, grid, dim3(64 * waves), s, p);
+    const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
+#define LF_MERGE(T, U)                                                                                     \
+    launch_kernel(merge_kernel<T, U>, grid, dim3(64 * waves), s, p.tiles_per_head, n_gq, p.H, p.L, p.dil_u, \
+                  (const float*)p.ws_ml, (const float*)p.ws_acc, p)
+    if (dtype == LF_BF16) {
+        if (p.dil_u) LF_MERGE(Bf16, true); else LF_MERGE(Bf16, false);
+    } else {
+        if (p.dil_u) LF_MERGE(F32, true); else LF_MERGE(F32, false);
+    }
+#undef LF_MERGE
     return hipGetLastError();
 }
 
