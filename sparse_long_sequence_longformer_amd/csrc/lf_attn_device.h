@@ -111,6 +111,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Work-group barrier once this wave's LDS accesses (and scalar loads) are done, its
+// vector-memory loads still in flight: __syncthreads would also wait for every load
+// this wave has issued (the Q rows and stage copies of a kernel's set-up).  The
+// values an LDS write stores are awaited by the compiler before that write.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Work-group barrier without a memory fence: ordering of the staged LDS data is
 // established by the explicit vmcnt waits; the empty asm keeps the compiler from
 // moving LDS accesses across it.

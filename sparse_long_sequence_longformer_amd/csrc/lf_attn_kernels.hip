@@ -600,6 +600,11 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     const size_t off = kStrided ? (size_t)b * p.s_b + (size_t)h * p.s_h : (size_t)bh * L * 64;
     const size_t ooff = kStrided ? (size_t)b * p.o_b + (size_t)h * p.o_h : (size_t)bh * L * 64;
     const Elem* Q = reinterpret_cast<const Elem*>(q_arg) + off;
+    // Position of global slot tid of a shared set, loaded ahead of the Q rows so that the
+    // slot set-up waits for this load alone (a per-sequence set is read there).
+    static_assert(kThreads <= LF_MAX_GLOBALS && kMaxGlobalStages * kStageKeys <= kThreads,
+                  "one slot per thread covers every global stage");
+    const int g_shared = p.g[tid];
     const int qa = r0 + 32 * wv;      // first virtual row of this wave
     const int qv = qa + (lane & 31);  // this lane's virtual row
     const bool rows_live = qa < Lr;
@@ -745,9 +750,14 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     uint64_t inv_next = 0ull;  // invalid-key bits of the next band stage, from its copy
     if (early) inv_next = issue(0, kAllParts);
 
-    // Global slots: source row (or -1 if unused/padded) and in-window position.
-    for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
-        const int g = gi < ng ? p.g[gofs + gi] : -1;
+    // Global slots: source row (or -1 if unused/padded) and in-window position; slot gi
+    // is thread gi's.
+    if (const int gi = tid; gi < n_gst * kStageKeys) {
+        int g = gi < ng ? g_shared : -1;
+        if (gstride) {
+            g = gi < ng ? p.g[gofs + gi] : -1;
+            asm volatile("" ::"v"(g));  // awaited here: a wait after the branch would wait for the Q rows too
+        }
         const bool ok = g >= 0 && (!pad || pad[g] == 0);
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
@@ -782,7 +792,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             bias_lds[t] = (m >= -w && m <= w) ? tab[m] * kLog2eF : 0.f;
         }
     }
-    __syncthreads();
+    barrier_lds();  // the Q rows and the first stage stay in flight
     if (wv == 0)
         for (int s = 0; s < n_gst; ++s) {
             const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
@@ -803,7 +813,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             const uint64_t inv = ~ballot64(ok);
             if (lane == 0) rnd_inv[j] = inv;
         }
-    __syncthreads();
+    barrier_lds();
     // One-sided variant: the global slots at or before this lane's row.
     const int gcnt = causal ? count_le(glob_abs, ng, r + qv * dil) : 0;
 
@@ -1040,10 +1050,12 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         }
         // Column c of query q sits at q*64 + (c ^ q%32): the 32 queries of one store,
         // and the 8 queries x 8 column chunks of one load below, hit distinct banks.
-        for (int db = 0; db < 2; ++db)
-            for (int i = 0; i < 16; ++i)
-                red_o[(wv * 32 + (lane & 31)) * 64 + ((32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)) ^ (lane & 31))] =
-                    gs.o[db][i];
+        // Slots past the sequence's global count are never read.
+        if (gb * kGlobalQueriesPerBlock + (lane & 31) < ng)
+            for (int db = 0; db < 2; ++db)
+                for (int i = 0; i < 16; ++i)
+                    red_o[(wv * 32 + (lane & 31)) * 64 + ((32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)) ^ (lane & 31))] =
+                        gs.o[db][i];
         __syncthreads();
         {
             const int q = tid >> 3, dc = tid & 7;  // 32 queries x 8 column chunks
