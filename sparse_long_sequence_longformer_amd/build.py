@@ -21,7 +21,7 @@ SOURCES = ["lf_attn.cpp", "lf_attn_kernels.hip", "lf_attn_bwd.hip", "lf_layer.hi
 # arguments of each kernel of the file, up to this many; a kernel whose first argument
 # is a parameter struct gets none).  Firmware without preloading runs the compiler's
 # own fallback, which loads them.
-PRELOAD_ARGS = {"lf_attn_kernels.hip": 7}
+PRELOAD_ARGS = {"lf_attn_kernels.hip": 7, "lf_attn_bwd.hip": 9}
 ARCH = "gfx950"
 
 

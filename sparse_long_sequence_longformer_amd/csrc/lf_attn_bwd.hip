@@ -387,21 +387,25 @@ struct Tile {
         return gbase + kStageKeys * bs;
     }
 };
-__device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int A, int B) {
-    const int pid = xcd_remap(blockIdx.x, gridDim.x);
-    t.bh = pid / p.tiles_per_head;
-    t.t_in = pid - t.bh * p.tiles_per_head;
-    t.h = t.bh % p.H;
-    t.b = t.bh / p.H;
-    t.dil = head_dil(p.dil_u, p.dil, t.h);
-    if (!decode_tile(t.t_in, p.L, t.dil, t.r, t.Lr, t.r0)) return false;
+// The tile of this work-group from the grid size, tiles per head, heads, length and
+// shared dilation (the kernels' leading arguments, preloaded into scalar registers);
+// false when the slot holds no tile.  tile_extent adds the other side's rows.
+__device__ __forceinline__ bool tile_of(Tile& t, const BwdParams& p, int nblk, int tph, int H, int L, int dil_u) {
+    const int pid = xcd_remap(blockIdx.x, nblk);
+    t.bh = pid / tph;
+    t.t_in = pid - t.bh * tph;
+    t.h = t.bh % H;
+    t.b = t.bh / H;
+    t.dil = head_dil(dil_u, p.dil, t.h);
+    return decode_tile(t.t_in, L, t.dil, t.r, t.Lr, t.r0);
+}
+__device__ __forceinline__ void tile_extent(Tile& t, int A, int B) {
     t.kb0 = max(0, t.r0 - A);
     t.kend = min(t.Lr, t.r0 + kRowsPerBlock + B);
     t.nb = (t.r0 - t.kb0 + kStageKeys - 1) / kStageKeys;
     t.gbase = t.r0 - kStageKeys * t.nb;
     t.na = max(0, (t.kend - (t.r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
     t.n_band = t.nb + 2 + t.na;
-    return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -480,7 +484,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // their order is fixed.  The work-group's sum over its waves goes to ws_db.
 template <class T, bool kCausal, bool kBias, bool kRandom, bool kBiasGrad = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
-void bwd_dq_kernel(const BwdParams p) {
+void bwd_dq_kernel(const int nblk, const int tph, const int H, const int L, const int dil_u, const void* const q_arg,
+                   const void* const dout_arg, const float* const lse2_arg, const float* const dsum_arg,
+                   const BwdParams p) {
     static_assert(!kBiasGrad || kBias, "the table gradient needs the table");
     using Elem = typename T::Elem;
     constexpr int kStageB = T::kStageB, kTileB = T::kTileB;
@@ -498,28 +504,24 @@ void bwd_dq_kernel(const BwdParams p) {
 
     // Keys of a row: w class steps before it and wr after (wr = 0 one-sided).
     constexpr bool causal = kCausal;
-    const int wr = causal ? 0 : p.w, span = p.w + wr;
-    // The kernel arguments of the set-up, read in one batch: left alone, the compiler
-    // waits for each argument load at its first use, one round trip after another.
-    asm volatile("" ::"s"(gridDim.x), "s"(p.tiles_per_head), "s"(p.H), "s"(p.L), "s"(p.w), "s"(p.dil_u),
-                 "s"(p.gstride), "s"(p.n_g), "s"(p.q), "s"(p.dout), "s"(p.lse2), "s"(p.dsum), "s"(p.pad));
+    // The leading arguments (grid size, p.tiles_per_head, p.H, p.L, p.dil_u and the
+    // pointers of the row loads) are preloaded into scalar registers by the build: the
+    // tile decode and the first loads wait for no memory.  The shared global set's
+    // positions are loaded first (the slot set-up then waits for them alone), and the
+    // other arguments are read in one batch after the row loads are issued.
     Tile tl;
-    if (!tile_of(tl, p, p.w, wr)) return;
+    if (!tile_of(tl, p, nblk, tph, H, L, dil_u)) return;
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
+    const int dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
     const size_t off = (size_t)tl.bh * L * 64;
-    const Elem* Q = reinterpret_cast<const Elem*>(p.q) + off;
-    const Elem* K = reinterpret_cast<const Elem*>(p.k) + off;
-    const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
-    const Elem* dO = reinterpret_cast<const Elem*>(p.dout) + off;
-    Elem* dQ = reinterpret_cast<Elem*>(p.dq) + off;
-    const float* lse2 = p.lse2 + (size_t)tl.bh * L;
-    const float* dsum = p.dsum + (size_t)tl.bh * L;
-    const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
-    const int gofs = tl.b * p.gstride;  // this sequence's global set
-    const int ng = p.gstride ? p.gcnt[tl.b] : p.n_g;
-
+    static_assert(kThreads <= LF_MAX_GLOBALS && kBwdMaxGlobalStages * kStageKeys <= kThreads,
+                  "one slot per thread covers every global stage");
+    const int g_shared = p.g[tid];
+    const Elem* Q = reinterpret_cast<const Elem*>(q_arg) + off;
+    const Elem* dO = reinterpret_cast<const Elem*>(dout_arg) + off;
+    const float* lse2 = lse2_arg + (size_t)tl.bh * L;
+    const float* dsum = dsum_arg + (size_t)tl.bh * L;
     const int qa = r0 + 32 * wv, qv = qa + (lane & 31);
     const bool rows_live = qa < Lr;
     const int row = r + qv * dil;
@@ -528,6 +530,18 @@ void bwd_dq_kernel(const BwdParams p) {
     T::load_op(dop, qv < Lr ? dO + (size_t)row * 64 : nullptr, h2);
     const float my_l2 = qv < Lr ? lse2[row] : kPosInf;
     const float my_d = qv < Lr ? dsum[row] : 0.f;
+
+    asm volatile("" ::"s"(p.w), "s"(p.gstride), "s"(p.n_g), "s"(p.k), "s"(p.v), "s"(p.pad), "s"(p.dq));
+    const int w = p.w;
+    const int wr = causal ? 0 : w, span = w + wr;
+    tile_extent(tl, w, wr);
+    const Elem* K = reinterpret_cast<const Elem*>(p.k) + off;
+    const Elem* V = reinterpret_cast<const Elem*>(p.v) + off;
+    Elem* dQ = reinterpret_cast<Elem*>(p.dq) + off;
+    const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
+    const int gstride = p.gstride;
+    const int gofs = tl.b * gstride;  // this sequence's global set
+    const int ng = seq_globals(gstride, p.n_g, p.gcnt, tl.b);
 
     const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
     // Random stages (every head undilated): draws of query block r0/64, then r0/64 + 1.
@@ -594,8 +608,12 @@ void bwd_dq_kernel(const BwdParams p) {
         }
     };
 
-    for (int gi = tid; gi < n_gst * kStageKeys; gi += kThreads) {
-        const int g = gi < ng ? p.g[gofs + gi] : -1;
+    if (const int gi = tid; gi < n_gst * kStageKeys) {  // slot gi is thread gi's
+        int g = gi < ng ? g_shared : -1;
+        if (gstride) {
+            g = gi < ng ? p.g[gofs + gi] : -1;
+            asm volatile("" ::"v"(g));  // awaited here: a wait after the branch would wait for the row loads too
+        }
         const bool ok = g >= 0 && (!pad || pad[g] == 0);
         const int vpos = (g >= r && (g - r) % dil == 0) ? (g - r) / dil : kNoPos;
         glob_src[gi] = ok ? g : -1;
@@ -606,7 +624,7 @@ void bwd_dq_kernel(const BwdParams p) {
     if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
     if (pad) fill_band_masks(0);
     if (kBias) fill_bias(bias_lds, p, tl.h, w, tid, false);
-    __syncthreads();
+    barrier_lds();  // the row loads stay in flight
     if (wv == 0)
         for (int s = 0; s < n_gst; ++s) {
             const uint64_t inv = ~ballot64(glob_src[kStageKeys * s + lane] >= 0);
@@ -627,7 +645,7 @@ void bwd_dq_kernel(const BwdParams p) {
             const uint64_t inv = ~ballot64(ok);
             if (lane == 0) rnd_inv[j] = inv;
         }
-    __syncthreads();
+    barrier_lds();
 
     // One-sided variant: the global slots at or before this lane's row.
     const int gcnt = causal ? count_le(glob_abs, ng, row) : 0;
@@ -822,7 +840,8 @@ void bwd_dq_kernel(const BwdParams p) {
 
 template <class T, bool kCausal, bool kBias, bool kRandom, bool kGlobalProj = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
-void bwd_dkv_kernel(const BwdParams p) {
+void bwd_dkv_kernel(const int nblk, const int tph, const int H, const int L, const int dil_u, const void* const k_arg,
+                    const void* const v_arg, const uint8_t* const pad_arg, const BwdParams p) {
     using Elem = typename T::Elem;
     constexpr int kStageB = T::kStageB, kTileB = T::kTileB, kLseOff = T::kLseOff, kDOff = T::kDOff;
     __shared__ __attribute__((aligned(16))) char ring[2 * kStageB];
@@ -833,30 +852,21 @@ void bwd_dkv_kernel(const BwdParams p) {
     // Queries of a key: query - key in [-wl, w] class steps (wl = 0 one-sided: no query
     // before its key).
     constexpr bool causal = kCausal;
-    const int wl = causal ? 0 : p.w, span = wl + p.w;
-    // The kernel arguments of the set-up, read in one batch (as in the dQ kernel).
-    asm volatile("" ::"s"(gridDim.x), "s"(p.tiles_per_head), "s"(p.H), "s"(p.L), "s"(p.w), "s"(p.dil_u),
-                 "s"(p.gstride), "s"(p.n_g), "s"(kGlobalProj ? p.kg : p.k), "s"(kGlobalProj ? p.vg : p.v), "s"(p.pad),
-                 "s"(p.sep));
+    // The leading arguments (grid size, p.tiles_per_head, p.H, p.L, p.dil_u, the own
+    // key and value rows' tensors and p.pad) are preloaded into scalar registers by the
+    // build, as in the dQ kernel; the shared global positions are loaded first and the
+    // other arguments in one batch after the row loads are issued.
     Tile tl;
-    if (!tile_of(tl, p, wl, p.w)) return;
+    if (!tile_of(tl, p, nblk, tph, H, L, dil_u)) return;
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int L = p.L, w = p.w, dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
+    const int dil = tl.dil, r = tl.r, r0 = tl.r0, Lr = tl.Lr;
     const size_t off = (size_t)tl.bh * L * 64;
-    const Elem* Q = reinterpret_cast<const Elem*>(kGlobalProj ? p.qg : p.q) + off;
-    const Elem* K = reinterpret_cast<const Elem*>(kGlobalProj ? p.kg : p.k) + off;
-    const Elem* V = reinterpret_cast<const Elem*>(kGlobalProj ? p.vg : p.v) + off;
-    const Elem* dO = reinterpret_cast<const Elem*>(p.dout) + off;
-    Elem* dK = reinterpret_cast<Elem*>(kGlobalProj ? p.dkg : p.dk) + off;
-    Elem* dV = reinterpret_cast<Elem*>(kGlobalProj ? p.dvg : p.dv) + off;
-    const float* lse2 = p.lse2 + (size_t)tl.bh * L;
-    const float* lse2b = p.lse2_band + (size_t)tl.bh * L;
-    const float* dsum = p.dsum + (size_t)tl.bh * L;
-    const uint8_t* pad = p.pad ? p.pad + (size_t)tl.b * L : nullptr;
-    const int gofs = tl.b * p.gstride;  // this sequence's global set
-    const int ng = p.gstride ? p.gcnt[tl.b] : p.n_g;
-
+    static_assert(kThreads == LF_MAX_GLOBALS, "one global slot per thread");
+    const int g_shared = p.g[tid];
+    const Elem* K = reinterpret_cast<const Elem*>(k_arg) + off;
+    const Elem* V = reinterpret_cast<const Elem*>(v_arg) + off;
+    const uint8_t* pad = pad_arg ? pad_arg + (size_t)tl.b * L : nullptr;
     const int qa = r0 + 32 * wv, qv = qa + (lane & 31);  // own keys (virtual index)
     const bool rows_live = qa < Lr;
     const int krow = r + qv * dil;
@@ -864,6 +874,22 @@ void bwd_dkv_kernel(const BwdParams p) {
     typename T::Op kop, vop;
     T::load_op(kop, kvalid ? K + (size_t)krow * 64 : nullptr, h2);
     T::load_op(vop, kvalid ? V + (size_t)krow * 64 : nullptr, h2);
+
+    asm volatile("" ::"s"(p.w), "s"(p.gstride), "s"(p.n_g), "s"(p.sep), "s"(kGlobalProj ? p.qg : p.q), "s"(p.dout),
+                 "s"(p.lse2), "s"(p.lse2_band), "s"(p.dsum));
+    const int w = p.w;
+    const int wl = causal ? 0 : w, span = wl + w;
+    tile_extent(tl, wl, w);
+    const Elem* Q = reinterpret_cast<const Elem*>(kGlobalProj ? p.qg : p.q) + off;
+    const Elem* dO = reinterpret_cast<const Elem*>(p.dout) + off;
+    Elem* dK = reinterpret_cast<Elem*>(kGlobalProj ? p.dkg : p.dk) + off;
+    Elem* dV = reinterpret_cast<Elem*>(kGlobalProj ? p.dvg : p.dv) + off;
+    const float* lse2 = p.lse2 + (size_t)tl.bh * L;
+    const float* lse2b = p.lse2_band + (size_t)tl.bh * L;
+    const float* dsum = p.dsum + (size_t)tl.bh * L;
+    const int gstride = p.gstride;
+    const int gofs = tl.b * gstride;  // this sequence's global set
+    const int ng = seq_globals(gstride, p.n_g, p.gcnt, tl.b);
 
     // global-query stages: none here with separate projections (their own launch)
     const int n_gst = (!kGlobalProj && p.sep) ? 0 : (ng + kStageKeys - 1) / kStageKeys;
@@ -888,7 +914,7 @@ void bwd_dkv_kernel(const BwdParams p) {
         if (s < n_gst) {
             auto row_of = [&](int kk) {
                 const int gi = kStageKeys * s + kk;
-                return gi < ng ? p.g[gofs + gi] : -1;
+                return gi < ng ? gq_pos[gi] : -1;
             };
             T::dma_tiles(slot, Q, dO, row_of, wv, lane);
             if (wv == 0) dma_floats<T>(slot, lse2, dsum, row_of, lane);
@@ -910,17 +936,24 @@ void bwd_dkv_kernel(const BwdParams p) {
     };
 
     if (tid < kRowsPerBlock) own_gidx[tid] = -1;
-    for (int gi = tid; gi < ng; gi += kThreads) gq_pos[gi] = p.g[gofs + gi];
+    if (const int gi = tid; gi < ng) {  // slot gi is thread gi's (ng <= LF_MAX_GLOBALS)
+        int g = g_shared;
+        if (gstride) {
+            g = p.g[gofs + gi];
+            asm volatile("" ::"v"(g));  // awaited here: a wait after the branch would wait for the row loads too
+        }
+        gq_pos[gi] = g;
+    }
     if (kBias) fill_bias(bias_lds, p, tl.h, w, tid, true);
-    __syncthreads();
+    barrier_lds();  // the row loads stay in flight
     for (int gi = tid; gi < ng; gi += kThreads) {
-        const int g = p.g[gofs + gi];
+        const int g = gq_pos[gi];
         if (g >= r && (g - r) % dil == 0) {
             const int vr = (g - r) / dil - r0;
             if (vr >= 0 && vr < kRowsPerBlock) own_gidx[vr] = gi;
         }
     }
-    __syncthreads();
+    barrier_lds();
 
     // One-sided variant: the first global slot at or after this lane's key (the
     // global queries that see it; slots are sorted by position).
@@ -1087,42 +1120,47 @@ void bwd_dkv_kernel(const BwdParams p) {
 
 constexpr int kBwdMergeWaves = 16;
 constexpr int kBwdMergeChunk = 8;
-template <class T>
-__global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const BwdParams p) {
+//
+// The leading arguments (p.tiles_per_head, the partial rows per tile n_gblk * 32, p.H,
+// p.L, p.dil_u and the three partial arrays) are preloaded into scalar registers by the
+// build, so the partial loads wait for no argument; the others are read while those
+// loads are in flight.  kDilU: every head has dilation dil_u (no read of p.dil).
+template <class T, bool kDilU>
+__global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const int tph, const int ngq, const int H,
+                                                                        const int L, const int dil_u,
+                                                                        const float* const ws_dq,
+                                                                        const float* const ws_dk,
+                                                                        const float* const ws_dv, const BwdParams p) {
     using Elem = typename T::Elem;
     __shared__ float red[kBwdMergeWaves][3][64];
     const int gi = blockIdx.x, h = blockIdx.y, bseq = blockIdx.z, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Kernel arguments read in one batch (every index is a grid coordinate); the output
-    // row's global position and pointers too, so that the end waits for none of them.
-    asm volatile("" ::"s"(p.H), "s"(p.L), "s"(p.n_g), "s"(p.gstride), "s"(p.tiles_per_head), "s"(p.n_gblk),
-                 "s"(p.dil[h]), "s"(p.gcnt[bseq]), "s"(p.g[gi]), "s"(p.ws_dq), "s"(p.ws_dk), "s"(p.ws_dv), "s"(p.ws_dkg),
-                 "s"(p.ws_dvg), "s"(p.sep), "s"(p.dq), "s"(p.dk), "s"(p.dv), "s"(p.dqg));
-    const int bh = bseq * p.H + h, dil = p.dil[h], L = p.L, gofs = bseq * p.gstride;
-    if (gi >= (p.gstride ? p.gcnt[bseq] : p.n_g)) return;  // this sequence has fewer globals
-    const int W = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);  // = blockDim.x / 64
+    const int bh = bseq * H + h, dil = kDilU ? dil_u : p.dil[h];
+    const int W = merge_waves(tph, kBwdMergeChunk, kBwdMergeWaves);  // = blockDim.x / 64
     const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;  // unused when dil == 1
-    const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
-    const size_t base = (size_t)bh * p.tiles_per_head * ngq * 64 + (size_t)gi * 64 + d;
+    // gi < n_g <= ngq: the loads below stay in bounds even for a sequence with fewer
+    // globals, whose work-groups drop what they loaded and return after the loop.
+    const size_t base = (size_t)bh * tph * ngq * 64 + (size_t)gi * 64 + d;
+    const int n_g = p.n_g, gstride = p.gstride, cnt = p.gcnt[bseq], g_shared = p.g[gi];
     // the global key's own-tile dK and dV (wave 0 adds them), loaded with the first chunk
     const size_t own = ((size_t)bh * ngq + gi) * 64 + d;
     const float own_k = wv == 0 ? p.ws_dkg[own] : 0.f, own_v = wv == 0 ? p.ws_dvg[own] : 0.f;
     float sq = 0.f, sk = 0.f, sv = 0.f;
-    for (int c0 = 0; c0 * W < p.tiles_per_head; c0 += kBwdMergeChunk) {
+    for (int c0 = 0; c0 * W < tph; c0 += kBwdMergeChunk) {
         float a[kBwdMergeChunk], b[kBwdMergeChunk], c[kBwdMergeChunk];
         bool ex[kBwdMergeChunk];
 #pragma unroll
         for (int j = 0; j < kBwdMergeChunk; ++j) {
             const int t = (c0 + j) * W + wv;
-            ex[j] = t < p.tiles_per_head && tile_exists(t, tpr, dil, L, kRowsPerBlock);
+            ex[j] = t < tph && tile_exists(t, tpr, dil, L, kRowsPerBlock);
         }
         __builtin_amdgcn_sched_barrier(0);  // every test before the first load
 #pragma unroll
         for (int j = 0; j < kBwdMergeChunk; ++j) {
             const size_t idx = base + (ex[j] ? (size_t)((c0 + j) * W + wv) * ngq * 64 : 0);
-            a[j] = p.ws_dq[idx];
-            b[j] = p.ws_dk[idx];
-            c[j] = p.ws_dv[idx];
+            a[j] = ws_dq[idx];
+            b[j] = ws_dk[idx];
+            c[j] = ws_dv[idx];
         }
 #pragma unroll
         for (int j = 0; j < kBwdMergeChunk; ++j) {
@@ -1131,6 +1169,8 @@ __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const Bw
             sv += ex[j] ? c[j] : 0.f;
         }
     }
+    if (gi >= (gstride ? cnt : n_g)) return;  // this sequence has fewer globals
+    const int g = gstride ? p.g[bseq * gstride + gi] : g_shared;  // position of this global row
     red[wv][0][d] = sq;
     red[wv][1][d] = sk;
     red[wv][2][d] = sv;
@@ -1144,7 +1184,7 @@ __global__ __launch_bounds__(64 * kBwdMergeWaves) void bwd_merge_kernel(const Bw
         sk += red[x][1][d];
         sv += red[x][2][d];
     }
-    const size_t o = (size_t)bh * L * 64 + (size_t)p.g[gofs + gi] * 64 + d;
+    const size_t o = (size_t)bh * L * 64 + (size_t)g * 64 + d;
     // with separate projections a global row's dQ goes to dq_g and its dq is zero
     if (p.sep) reinterpret_cast<Elem*>(p.dqg)[o] = T::from_float(sq * 0.125f);
     reinterpret_cast<Elem*>(p.dq)[o] = T::from_float(p.sep ? 0.f : sq * 0.125f);
@@ -1169,16 +1209,20 @@ template <class T>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
+    // leading arguments, preloaded into scalar registers (see the kernel)
+#define LF_DQ_ARGS blocks, p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.dout, (const float*)p.lse2, (const float*)p.dsum, p
     if (p.dbias) {  // position-bias table gradient: per-wave offset sums in dynamic LDS
         const unsigned shm = kWaves * (2 * p.w + 1 + 2 * kBiasPad) * sizeof(float);
         if (p.rnd) {
-            if (p.causal) return launch_kernel_shm(bwd_dq_kernel<T, true, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
-            return launch_kernel_shm(bwd_dq_kernel<T, false, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+            if (p.causal)
+                return launch_kernel_shm(bwd_dq_kernel<T, true, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, LF_DQ_ARGS);
+            return launch_kernel_shm(bwd_dq_kernel<T, false, true, true, true>, dim3(blocks), dim3(kThreads), shm, s, LF_DQ_ARGS);
         }
-        if (p.causal) return launch_kernel_shm(bwd_dq_kernel<T, true, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
-        return launch_kernel_shm(bwd_dq_kernel<T, false, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, p);
+        if (p.causal)
+            return launch_kernel_shm(bwd_dq_kernel<T, true, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, LF_DQ_ARGS);
+        return launch_kernel_shm(bwd_dq_kernel<T, false, true, false, true>, dim3(blocks), dim3(kThreads), shm, s, LF_DQ_ARGS);
     }
-#define LF_DQ(C, Bi, R) launch_kernel(bwd_dq_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
+#define LF_DQ(C, Bi, R) launch_kernel(bwd_dq_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, LF_DQ_ARGS)
 #define LF_DQ_R(C, Bi) \
     if (p.rnd) LF_DQ(C, Bi, true); else LF_DQ(C, Bi, false)
     if (p.causal) {
@@ -1188,6 +1232,7 @@ hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
     }
 #undef LF_DQ_R
 #undef LF_DQ
+#undef LF_DQ_ARGS
     return hipGetLastError();
 }
 
@@ -1195,7 +1240,9 @@ template <class T>
 hipError_t bwd_dkv_t(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
-#define LF_DKV(C, Bi, R) launch_kernel(bwd_dkv_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, p)
+#define LF_DKV(C, Bi, R)                                                                                   \
+    launch_kernel(bwd_dkv_kernel<T, C, Bi, R>, dim3(blocks), dim3(kThreads), s, blocks, p.tiles_per_head, p.H, p.L, \
+                  p.dil_u, p.k, p.v, p.pad, p)
 #define LF_DKV_R(C, Bi) \
     if (p.rnd) LF_DKV(C, Bi, true); else LF_DKV(C, Bi, false)
     if (p.causal) {
@@ -1213,9 +1260,11 @@ hipError_t bwd_dkv_global_proj_t(const BwdParams& p, hipStream_t s) {
     const int blocks = p.B * p.H * p.tiles_per_head;
     if (blocks <= 0) return hipSuccess;
     if (p.causal)
-        launch_kernel(bwd_dkv_kernel<T, true, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
+        launch_kernel(bwd_dkv_kernel<T, true, false, false, true>, dim3(blocks), dim3(kThreads), s, blocks,
+                      p.tiles_per_head, p.H, p.L, p.dil_u, p.kg, p.vg, p.pad, p);
     else
-        launch_kernel(bwd_dkv_kernel<T, false, false, false, true>, dim3(blocks), dim3(kThreads), s, p);
+        launch_kernel(bwd_dkv_kernel<T, false, false, false, true>, dim3(blocks), dim3(kThreads), s, blocks,
+                      p.tiles_per_head, p.H, p.L, p.dil_u, p.kg, p.vg, p.pad, p);
     return hipGetLastError();
 }
 
@@ -1224,7 +1273,13 @@ hipError_t bwd_merge_t(const BwdParams& p, hipStream_t s) {
     if (p.n_g == 0 || p.B == 0) return hipSuccess;
     if (p.B > 65535) return hipErrorInvalidConfiguration;  // grid z
     const int waves = merge_waves(p.tiles_per_head, kBwdMergeChunk, kBwdMergeWaves);
-    launch_kernel(bwd_merge_kernel<T>, dim3(p.n_g, p.H, p.B), dim3(64 * waves), s, p);
+    const int ngq = p.n_gblk * kGlobalQueriesPerBlock;
+    if (p.dil_u)
+        launch_kernel(bwd_merge_kernel<T, true>, dim3(p.n_g, p.H, p.B), dim3(64 * waves), s, p.tiles_per_head, ngq, p.H,
+                      p.L, p.dil_u, (const float*)p.ws_dq, (const float*)p.ws_dk, (const float*)p.ws_dv, p);
+    else
+        launch_kernel(bwd_merge_kernel<T, false>, dim3(p.n_g, p.H, p.B), dim3(64 * waves), s, p.tiles_per_head, ngq,
+                      p.H, p.L, p.dil_u, (const float*)p.ws_dq, (const float*)p.ws_dk, (const float*)p.ws_dv, p);
     return hipGetLastError();
 }
 

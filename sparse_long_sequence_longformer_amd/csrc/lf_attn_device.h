@@ -213,6 +213,18 @@ __device__ __forceinline__ int head_dil(int dil_u, const int* dil, int h) {
     return d;
 }
 
+// Global count of sequence b: n_g for a set shared by every sequence (gstride 0), else
+// gcnt[b], read only then (the empty asm keeps the compiler from issuing and awaiting
+// that load unconditionally).
+__device__ __forceinline__ int seq_globals(int gstride, int n_g, const int* gcnt, int b) {
+    int n = n_g;
+    if (gstride) {
+        asm volatile("");
+        n = gcnt[b];
+    }
+    return n;
+}
+
 // Residue class r, class length Lr and first class row r0 of work-group slot t_in of a
 // head with dilation dil (tiles of kRowsPerBlock class rows, ceil(ceil(L/dil)/rows)
 // per class); false when the slot holds no tile.  dil == 1 needs no division.

@@ -623,7 +623,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     const uint8_t* pad = pad_arg ? pad_arg + (size_t)b * L : nullptr;
     // Global set of this sequence: one shared set (gstride 0) or one row per sequence.
     const int gofs = b * gstride;
-    const int ng = gstride ? p.gcnt[b] : n_g;
+    const int ng = seq_globals(gstride, n_g, p.gcnt, b);
     // Tensors of the global rows' own attention (c): the separate projections if given.
     const bool sep = kg_arg != nullptr;
     const Elem* QG = sep ? reinterpret_cast<const Elem*>(p.qg) + off : Q;
