@@ -658,12 +658,9 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     const int n_rst = na_r + nb_r;
     const int n_lst = n_gst + n_rst;  // stages of listed keys (global, then random)
     const int n_st = n_lst + n_band;
-    // Stage order: one band stage (when there is one besides the home stages), the
-    // global and random stages, the remaining band stages.  A band stage first lets
-    // its copy be issued before the global slots are set up.
-    const int n_pre = ((kRandom || n_gst > 0) && nb + na > 0) ? 1 : 0;
-    auto is_glob = [&](int t) __attribute__((always_inline)) { return t >= n_pre && t < n_pre + n_lst; };  // a listed-key stage
-    auto band_u = [&](int t) __attribute__((always_inline)) { return t < n_pre ? t : t - n_lst; };
+    // Stage order: the global and random stages (listed keys), then the band stages.
+    auto is_glob = [&](int t) __attribute__((always_inline)) { return t < n_lst; };  // a listed-key stage
+    auto band_u = [&](int t) __attribute__((always_inline)) { return t - n_lst; };
     auto rnd_block = [&](int j) __attribute__((always_inline)) { return j < na_r ? rnd_a[j] : rnd_b[j - na_r]; };  // key block of random stage j
     // Processing order of the band stages: the two home stages last (the global-row pass
     // reuses them).  A tile with the full band of P = ceil(w/64) + 2 + ceil(wr/64) grid
@@ -714,8 +711,8 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     int ks_next = 0;  // first key of the band stage copied last (see the stage loop)
     auto issue = [&](int s, int part) __attribute__((always_inline)) -> uint64_t {
         char* slot = ring + (s % T::kNS) * T::kStageBytes;
-        if (kRandom && is_glob(s) && s - n_pre >= n_gst) {
-            const int j = s - n_pre - n_gst;
+        if (kRandom && is_glob(s) && s >= n_gst) {
+            const int j = s - n_gst;
             const int kb0 = kRandomBlock * rnd_block(j);
             const uint64_t inv = uniform64(rnd_inv[j]);
             if (inv == 0ull && part == kAllParts && direct_ok) {
@@ -725,7 +722,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             }
             return 0ull;
         } else if (is_glob(s)) {
-            const int* src = glob_src + kStageKeys * (s - n_pre);
+            const int* src = glob_src + kStageKeys * s;
             T::dma_stage(slot, K, V, rs, [&](int kk) __attribute__((always_inline)) { return src[kk]; }, wv, lane, part);
             return 0ull;
         } else {
@@ -833,24 +830,15 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         }
     wait_vmcnt<0>();
     T::scale_q(qop);
-    // Stages [0, n_gen): the listed-key stages (global, random) and the band stage
-    // placed ahead of them, in the general body below; stages [n_gen, n_st): band
-    // stages only, in the lean loop after it.
-    const int n_gen = n_pre + n_lst;
+    // Stages [0, n_gen): the listed-key stages (global, random), in the general body
+    // below; stages [n_gen, n_st): band stages only, in the lean loop after it.
+    const int n_gen = n_lst;
+    static_assert(T::kNS == 2, "stage t + 1 is issued while stage t is computed");
     for (int t = 0; t < n_gen; ++t) {
-        const uint64_t inv_cur = inv_next;  // stage t's bits (two-slot ring: issued last)
-        const int ks_cur = ks_next;
-        wait_stage<T>(min(T::kNS - 2, n_st - 1 - t));
+        wait_stage<T>(0);
         barrier_nofence();
-        const int sn = t + T::kNS - 1;
-        if (sn < n_st) {
-            const int bn = is_glob(sn) ? 0 : band_u(sn);
-            if (pad && bn > 0 && bn % kMaskWindow == 0) {
-                fill_band_masks(bn / kMaskWindow);
-                __syncthreads();
-            }
-            inv_next = issue(sn, kAllParts);
-        }
+        // The next stage: listed, or band stage 0 (whose pad masks are already built).
+        if (t + 1 < n_st) inv_next = issue(t + 1, kAllParts);
         if (t == 0 && ng > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
             T::dma_rows(gq_rows, [&](int j) __attribute__((always_inline)) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * rs : zero; },
@@ -858,17 +846,11 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         }
         const char* slot = ring + (t % T::kNS) * T::kStageBytes;
         // Stage kind: random (kRandom: key block rnd_block(j), for the waves of its
-        // query block), global (listed slots), or band.
-        const bool rstage = kRandom && is_glob(t) && t - n_pre >= n_gst;
-        const bool gstage = is_glob(t) && !rstage;
-        const int gidx = t - n_pre;        // global stage index when gstage
-        const int j = t - n_pre - n_gst;   // random stage index when rstage
-        // A band stage's first key and invalid-key bits were computed when its copy was
-        // issued (with a two-slot ring, in the previous iteration): reused, not rebuilt.
-        const int ks_band = T::kNS == 2 ? ks_cur : stage_key(band_u(t));
-        const uint64_t inv_band = T::kNS == 2 ? inv_cur : band_invalid(band_u(t));
-        const int ks = rstage ? kRandomBlock * rnd_block(j) : (gstage ? 0 : ks_band);
-        const uint64_t inv = uniform64(rstage ? rnd_inv[j] : (gstage ? glob_mask[gidx] : inv_band));
+        // query block) or global (listed slots).
+        const bool rstage = kRandom && t >= n_gst;
+        const int j = t - n_gst;  // random stage index when rstage
+        const int ks = rstage ? kRandomBlock * rnd_block(j) : 0;
+        const uint64_t inv = uniform64(rstage ? rnd_inv[j] : glob_mask[t]);
         const bool wave_on = !rstage || (wv >> 1) == (j < na_r ? 0 : 1);
         if (rows_live && wave_on && inv != ~0ull) {
             // Both sub-tiles in straight-line code: the second one's operand reads and
@@ -881,17 +863,13 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                 if (rstage) {
                     if (kss >= qa + 31 - w && kss + 31 <= qa + wr) continue;  // inside every row's window
                     if (causal && kss > qa + 31) continue;                    // after every row
-                } else if (!gstage && (kss > qa + 31 + wr || kss + 31 < qa - w)) {
-                    continue;  // outside every row's band
                 }
-                const bool interior =
-                    !gstage && !rstage && inv32 == 0u && kss >= qa + 31 - w && kss + 31 <= qa + wr;
-                const int mode = rstage ? 3 : (gstage ? 2 : (interior ? 0 : 1));
-                const int goff = kStageKeys * gidx + 32 * sub + 8 * h2;
+                const int mode = rstage ? 3 : 2;
+                const int goff = kStageKeys * t + 32 * sub + 8 * h2;
                 const int bbase = kss + 8 * h2 - qv + w;
                 const int climit = !causal ? 1 << 30 : (rstage ? w - bbase + 1 : gcnt - goff);
                 sub_step<T, kRandom>(st, slot, sub, lo, qop, mode, inv32, h2, bbase, span, glob_pos + goff, w - qv,
-                                     climit, (kBias && !gstage && !rstage) ? bias_lds + kBiasPad + bbase : nullptr);
+                                     climit, nullptr);
             }
         }
     }
