@@ -182,6 +182,22 @@ def clock_warmup(step, seconds, torch):
             return round(time.perf_counter() - t0, 3), n
 
 
+def split_tiling(wl, args) -> bool:
+    """Whether the library runs this forward on 64-row split work-groups: its rule for
+    a handle left at tile rows 0 (the 128-row grid fills at most half of the
+    work-group slots, three bf16 or one fp32 work-group per compute unit; never with a
+    position bias or random blocks)."""
+    import torch
+
+    if args.bias or args.random or args.layer:
+        return False
+    tiles = 0
+    for d in wl.dil_list():
+        tiles = max(tiles, d * (((wl.L + d - 1) // d + 127) // 128))
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * (3 if wl.dtype == "bf16" else 1)
+    return 2 * wl.B * wl.H * tiles <= slots
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -377,7 +393,8 @@ def main():
         "kernel_ms_avg": {k2: round(v2, 6) for k2, v2 in stage_avg.items()},
         "roofline": {
             "kernel": f"lf::band_kernel<{'Bf16' if wl.dtype == 'bf16' else 'F32'}, {str(args.causal).lower()}, "
-                      f"{str(bool(args.bias)).lower()}, {str(bool(args.random)).lower()}, false>",
+                      f"{str(bool(args.bias)).lower()}, {str(bool(args.random)).lower()}, false"
+                      + (", false, true>" if split_tiling(wl, args) else ">"),
             **roof,
             "traffic": traffic,
             "avg_launch_ms": round(k_avg_ms, 6),

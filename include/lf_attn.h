@@ -432,6 +432,23 @@ lf_status lf_layer_forward(lf_attn_t h, const void* x, const lf_layer_weights* w
  */
 lf_status lf_attn_set_global_mode(lf_attn_t h, int mode);
 
+/*
+ * Query rows per work-group of the forward kernels (a tuning setting; results agree
+ * within rounding either way).  rows = 128: four waves of 32 rows each.  rows = 64:
+ * two 32-row blocks, each computed by two waves that take alternate 32-key sub-tiles
+ * of every staged tile of keys and merge their partial softmax states (each part's
+ * largest score, weight sum and weighted values rescaled to the larger of the two),
+ * i.e. twice the waves for the same rows.  rows = 0
+ * (the default): 64 when the 128-row grid (B * H * tiles) would fill at most half of
+ * the device's work-group slots (three bf16 or one fp32 work-group per compute unit),
+ * else 128.  The 64-row form has no variant with a position bias, random blocks or
+ * strided tensors (the layer's in-place attention); those always use 128.  The
+ * backward keeps its own 128-row tiling.
+ * Errors: LF_ERR_INVALID_ARG (h == NULL, or rows not 0, 64 or 128); the setting is
+ * unchanged.
+ */
+lf_status lf_attn_set_tile_rows(lf_attn_t h, int rows);
+
 /* Free the handle and its device workspace.  NULL is a no-op.  Waits for the
  * device before freeing (hipFree semantics). */
 lf_status lf_attn_destroy(lf_attn_t h);

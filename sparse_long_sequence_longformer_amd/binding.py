@@ -49,6 +49,7 @@ EXPORTS = (
     "lf_attn_set_stage_timing",
     "lf_attn_set_window_mode",
     "lf_attn_set_global_mode",
+    "lf_attn_set_tile_rows",
     "lf_attn_set_position_bias",
     "lf_attn_set_random_blocks",
     "lf_attn_stage_times",
@@ -124,6 +125,8 @@ def load_library():
     lib.lf_attn_last_error.restype = ctypes.c_char_p
     lib.lf_attn_set_global_mode.argtypes = [vp, i32]
     lib.lf_attn_set_global_mode.restype = i32
+    lib.lf_attn_set_tile_rows.argtypes = [vp, i32]
+    lib.lf_attn_set_tile_rows.restype = i32
     lib.lf_attn_set_window_mode.argtypes = [vp, i32]
     lib.lf_attn_set_window_mode.restype = i32
     lib.lf_attn_set_position_bias.argtypes = [vp, vp, i32, i32]
@@ -257,6 +260,11 @@ class LfAttn:
         mode = LF_GLOBALS_PER_SEQUENCE if per_seq else LF_GLOBALS_SHARED
         self._check(self.lib.lf_attn_set_global_mode(self.handle, mode), self.handle)
         self.per_sequence_globals = bool(per_seq)
+
+    def set_tile_rows(self, rows: int):
+        """Forward work-group rows for every later call on this handle: 0 chooses, 64 or
+        128 forces (64: two waves per 32 rows, alternate sub-tiles of every stage)."""
+        self._check(self.lib.lf_attn_set_tile_rows(self.handle, int(rows)), self.handle)
 
     def set_causal(self, causal: bool):
         """One-sided (causal) variant for every later call on this handle."""

@@ -80,6 +80,9 @@ struct lf_attn_s {
     // (LF_ERR_HIP); once, then the handle works normally.  Anything else (or unset):
     // none.
     int fault = 0;
+    // Rows per forward work-group (lf_attn_set_tile_rows): 0 chooses, 64 or 128 forces.
+    int tile_rows = 0;
+    int n_cu = 0, n_cu_device = -1;  // compute units of the device last asked
     bool timing = false;
     std::vector<TimedLaunch> pending;  // recorded, not yet read
     std::vector<hipEvent_t> event_pool;
@@ -208,6 +211,16 @@ lf_status lf_attn_set_global_mode(lf_attn_t h, int mode) {
     if (mode != LF_GLOBALS_SHARED && mode != LF_GLOBALS_PER_SEQUENCE)
         return fail(h, LF_ERR_INVALID_ARG, "unknown global mode %d", mode);
     h->global_mode = mode;
+    return LF_OK;
+}
+
+lf_status lf_attn_set_tile_rows(lf_attn_t h, int rows) {
+    if (!h) return LF_ERR_INVALID_ARG;
+    h->last_error.clear();
+    if (rows != 0 && rows != lf::kSplitRows && rows != lf::kRowsPerBlock)
+        return fail(h, LF_ERR_INVALID_ARG, "tile rows must be 0, %d or %d (got %d)", lf::kSplitRows,
+                    lf::kRowsPerBlock, rows);
+    h->tile_rows = rows;
     return LF_OK;
 }
 
@@ -536,6 +549,44 @@ struct Strides {
     int o_r;
 };
 
+// Work-groups per head of a forward tiling of `rows` rows per residue class.
+int forward_tiles(const Plan& pl, int rows) {
+    int tiles = 0;
+    for (int i = 0; i < pl.H; ++i) {
+        const int d = pl.dil[i];
+        const int per_class = ((pl.L + d - 1) / d + rows - 1) / rows;
+        tiles = std::max(tiles, d * per_class);
+    }
+    return tiles;
+}
+
+// Rows per forward work-group.  A 128-row work-group gives each of its four waves 32
+// rows; when the whole grid would fill at most half of the work-group slots of the
+// device (three bf16 work-groups per compute unit, one fp32), the 64-row split tiling
+// runs two waves per 32 rows instead (each takes every other 32-key sub-tile of a
+// stage), i.e. twice the waves for the same work.  The split form has no variant with a
+// position bias, random blocks or strided tensors; the handle setting forces either
+// tiling where both exist.
+lf_status forward_rows(lf_attn_t h, const Plan& pl, bool strided, int& rows) {
+    rows = lf::kRowsPerBlock;
+    if (h->bias || h->rnd_on || strided || h->tile_rows == lf::kRowsPerBlock) return LF_OK;
+    if (h->tile_rows == lf::kSplitRows) {
+        rows = lf::kSplitRows;
+        return LF_OK;
+    }
+    if (h->n_cu_device != h->device) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess)
+            return fail(h, LF_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+        h->n_cu = n;
+        h->n_cu_device = h->device;
+    }
+    const int64_t slots = static_cast<int64_t>(h->n_cu) * (h->dtype == LF_BF16 ? 3 : 1);
+    const int64_t blocks = static_cast<int64_t>(pl.B) * pl.H * pl.tiles;
+    if (2 * blocks <= slots) rows = lf::kSplitRows;
+    return LF_OK;
+}
+
 lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v, const void* qg, const void* kg,
                        const void* vg, void* out, float* lse, int B, int H, int L, int d_h, int w,
                        const int32_t* dil_per_head, const int32_t* global_idx, int n_global,
@@ -589,8 +640,6 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
     std::copy(pl.g.begin(), pl.g.end(), p.g);
     std::copy(pl.gcnt.begin(), pl.gcnt.end(), p.gcnt);
     p.n_gblk = pl.n_gblk;
-    p.rows_per_block = lf::kRowsPerBlock;
-    p.tiles_per_head = pl.tiles;
     p.causal = h->window_mode == LF_WINDOW_CAUSAL;
     p.bias = h->bias;
     p.bias_w = h->bias_w;
@@ -610,8 +659,15 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
         p.s_r = p.o_r = LF_HEAD_DIM;
     }
 
-    // Device workspace for the global-row partials.
     if (hipGetDevice(&h->device) != hipSuccess) return fail(h, LF_ERR_HIP, "hipGetDevice failed");
+    int rows = lf::kRowsPerBlock;
+    st = forward_rows(h, pl, p.strided != 0, rows);
+    if (st != LF_OK) return st;
+    const int tiles = rows == lf::kRowsPerBlock ? pl.tiles : forward_tiles(pl, rows);
+    p.rows_per_block = rows;
+    p.tiles_per_head = tiles;
+
+    // Device workspace for the global-row partials.
     if (no_alloc) {
         if (h->rnd_on && h->rnd_uploaded != h->device)
             return fail(h, LF_ERR_UNSUPPORTED,
@@ -627,7 +683,7 @@ lf_status forward_impl(lf_attn_t h, const void* q, const void* k, const void* v,
         p.rnd_r = h->rnd_r;
     }
     if (p.n_g > 0) {
-        const size_t n_part = static_cast<size_t>(B) * H * pl.tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
+        const size_t n_part = static_cast<size_t>(B) * H * tiles * p.n_gblk * lf::kGlobalQueriesPerBlock;
         const size_t need = n_part * (2 + 64) * sizeof(float);
         char* base = nullptr;
         if (no_alloc) {

@@ -226,20 +226,21 @@ __device__ __forceinline__ int seq_globals(int gstride, int n_g, const int* gcnt
 }
 
 // Residue class r, class length Lr and first class row r0 of work-group slot t_in of a
-// head with dilation dil (tiles of kRowsPerBlock class rows, ceil(ceil(L/dil)/rows)
-// per class); false when the slot holds no tile.  dil == 1 needs no division.
+// head with dilation dil (tiles of kRows class rows, ceil(ceil(L/dil)/kRows) per
+// class); false when the slot holds no tile.  dil == 1 needs no division.
+template <int kRows = kRowsPerBlock>
 __device__ __forceinline__ bool decode_tile(int t_in, int L, int dil, int& r, int& Lr, int& r0) {
     if (dil == 1) {
         r = 0;
         Lr = L;
-        r0 = t_in * kRowsPerBlock;
+        r0 = t_in * kRows;
         return r0 < L;
     }
-    const int tpr = ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int tpr = ((L + dil - 1) / dil + kRows - 1) / kRows;
     r = t_in / tpr;
     if (r >= dil) return false;
     Lr = (L - r + dil - 1) / dil;
-    r0 = (t_in - r * tpr) * kRowsPerBlock;
+    r0 = (t_in - r * tpr) * kRows;
     return r0 < Lr;
 }
 

@@ -12,6 +12,10 @@ namespace lf {
 
 // Rows of one work-group (4 waves x 32 query rows) and keys of one staged K/V tile.
 constexpr int kRowsPerBlock = 128;
+// Rows of a work-group of the split forward: two 32-row blocks, each computed by two
+// waves that take alternate 32-key sub-tiles of every stage (twice the waves of a
+// 128-row tiling for the same rows, for grids that would fill half the GPU or less).
+constexpr int kSplitRows = 64;
 constexpr int kKeysPerTile = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -47,7 +51,7 @@ struct Params {
     int n_g;             // number of distinct global positions
     int n_gblk;          // ceil(n_g / 32)
     int tiles_per_head;  // work-groups per (b, h), max over heads (grid partition)
-    int rows_per_block;  // rows of one residue class per work-group
+    int rows_per_block;  // rows of one residue class per forward work-group (128, or 64 split)
     int causal;          // one-sided variant: no pair with its key after its query
     // Global sets: g[0..n_g) shared by every sequence (gstride 0), or row b at
     // g[b*gstride ..] with gcnt[b] entries (n_g = the largest count).  Sorted, distinct.

@@ -169,6 +169,12 @@ struct Bf16 {
             lo.v[db] = kTileBytes + vrow * kRowBytes + ((chunk ^ swz_v(vrow)) << 4) + 8 * (i & 1);
         }
     }
+    // Operand reads of sub-tile `sub` with sub = 0 arguments (a wave that only ever
+    // reads one sub-tile of each stage; the swizzles repeat every 8 rows).
+    __device__ __forceinline__ static void shift_lane(Lane& lo, int sub) {
+        for (int kb = 0; kb < 4; ++kb) lo.k[kb] += sub * 32 * kRowBytes;
+        for (int db = 0; db < 2; ++db) lo.v[db] += sub * 32 * kRowBytes;
+    }
 
     // seed + S^T (32 keys x 32 queries) of sub-tile `sub` (keys 32*sub .. 32*sub+31 of
     // the stage).  The four K operand reads go out before the first product (left to
@@ -343,6 +349,10 @@ struct F32 {
         lo.sw = swz_k(row);
         lo.h2 = lane >> 5;
         lo.v = kTileBytes + 4 * (lane & 31);
+    }
+    __device__ __forceinline__ static void shift_lane(Lane& lo, int sub) {
+        lo.k += sub * 32 * kRowBytes;
+        lo.v += sub * 32 * kRowBytes;
     }
 
     __device__ __forceinline__ static f32x16 qk(const char* slot, int sub, const Lane& lo, const QOp& q, const f32x16& seed) {
@@ -558,11 +568,16 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 // the second (waves 2-3), one 64-key stage each.  Their keys that lie in a row's
 // window, are global, padded or past the end are masked, so each key counts once.
 
-template <class T, bool kCausal, bool kBias, bool kRandom, bool kStrided = false>
+template <class T, bool kCausal, bool kBias, bool kRandom, bool kStrided = false, bool kSplit = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const int nblk, const int tph, const int H, const int L, const int dil_u, const void* const q_arg,
-                 const Params p) {
+                 const int nseq, const Params p) {
     using Elem = typename T::Elem;
+    // kSplit: 64-row tiles; waves 2 rb and 2 rb + 1 share row block rb and take the
+    // even and the odd 32-key sub-tiles of every stage, then merge their states.
+    static_assert(!(kSplit && (kRandom || kStrided)), "the split tiling has no random-block or strided form");
+    constexpr int kRows = kSplit ? kSplitRows : kRowsPerBlock;  // rows of the tile
+    constexpr int kHome = kRows / kStageKeys;                   // stages of its own rows as keys
     __shared__ __attribute__((aligned(16))) char ring[T::kNS * T::kStageBytes];
     __shared__ uint64_t band_mask[kMaskRing];        // invalid-key bits of band stages
     __shared__ uint64_t glob_mask[kMaxGlobalStages];  // invalid-key bits of global stages
@@ -580,19 +595,25 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
 
     const int tid = threadIdx.x, lane = tid & 63, h2 = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    // The leading arguments (the grid size, p.tiles_per_head, p.H, p.L, p.dil_u, p.q)
-    // are the tile decode's and the Q load's; the build preloads them into scalar
+    const int rb = kSplit ? wv >> 1 : wv;  // the wave's 32-row block of the tile
+    const int kh = kSplit ? wv & 1 : 0;    // kSplit: the sub-tile of each stage it takes
+    // The leading arguments (the grid size, p.tiles_per_head, p.H, p.L, p.dil_u, p.q,
+    // p.B) are the tile decode's and the Q load's; the build preloads them into scalar
     // registers, so neither waits for memory.  The other arguments of the set-up are read
     // in one batch after the Q load is issued: left alone, the compiler waits for each
     // argument load at its first use, one memory round trip after another across the
     // set-up's branches.
     if constexpr (kStrided) asm volatile("" ::"s"(p.s_b), "s"(p.s_h), "s"(p.s_r), "s"(p.o_b), "s"(p.o_h), "s"(p.o_r));
     const int pid = xcd_remap(blockIdx.x, nblk);
-    const int bh = pid / tph, t_in = pid - bh * tph;
-    const int h = bh % H, b = bh / H;
+    // Slice j = pid / tph holds sequence j % nseq, head j / nseq: one XCD's contiguous
+    // range of slices then takes every sequence in turn, so sequences of different
+    // true lengths (padding) load the XCDs evenly.
+    const int j_bh = pid / tph, t_in = pid - j_bh * tph;
+    const int h = j_bh / nseq, b = j_bh - h * nseq;
+    const int bh = b * H + h;
     const int dil = head_dil(dil_u, p.dil, h);
     int r, Lr, r0;  // residue class, its length, the tile's first class row
-    if (!decode_tile(t_in, L, dil, r, Lr, r0)) return;
+    if (!decode_tile<kRows>(t_in, L, dil, r, Lr, r0)) return;
 
     // q, k, v (and q_g, k_g, v_g): row i of (b, h) at b*s_b + h*s_h + i*rs elements,
     // out at b*o_b + h*o_h + i*o_r (kStrided); else [B][H][L][64] with constant strides.
@@ -605,7 +626,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     static_assert(kThreads <= LF_MAX_GLOBALS && kMaxGlobalStages * kStageKeys <= kThreads,
                   "one slot per thread covers every global stage");
     const int g_shared = p.g[tid];
-    const int qa = r0 + 32 * wv;      // first virtual row of this wave
+    const int qa = r0 + 32 * rb;      // first virtual row of this wave
     const int qv = qa + (lane & 31);  // this lane's virtual row
     const bool rows_live = qa < Lr;
     typename T::QOp qop;
@@ -636,11 +657,11 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     constexpr bool causal = kCausal;
     const int wr = causal ? 0 : w, span = w + wr;
     const int kb0 = max(0, r0 - w);
-    const int kend = min(Lr, r0 + kRowsPerBlock + wr);
+    const int kend = min(Lr, r0 + kRows + wr);
     const int nb = (r0 - kb0 + kStageKeys - 1) / kStageKeys;  // stages before the home keys
     const int gbase = r0 - kStageKeys * nb;                    // first key of the grid (<= kb0)
-    const int na = max(0, (kend - (r0 + 2 * kStageKeys) + kStageKeys - 1) / kStageKeys);
-    const int n_band = nb + 2 + na;
+    const int na = max(0, (kend - (r0 + kHome * kStageKeys) + kStageKeys - 1) / kStageKeys);
+    const int n_band = nb + kHome + na;
     const int n_gst = (ng + kStageKeys - 1) / kStageKeys;
     // Random stages: the draws of query block r0/64 (rnd_a, na_r of them), then those
     // of the next query block (rnd_b, nb_r); rows are sorted with -1 after the draws.
@@ -669,21 +690,21 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     // tile whose band holds it, so a head's K/V comes from HBM a few blocks per step
     // instead of all of it in the first two steps.  Tiles whose band is cut by the
     // sequence ends take before, after, home.
-    const int P = ((w + kStageKeys - 1) / kStageKeys) + 2 + ((wr + kStageKeys - 1) / kStageKeys);
-    const bool rot = n_band == P && P > 2;
+    const int P = ((w + kStageKeys - 1) / kStageKeys) + kHome + ((wr + kStageKeys - 1) / kStageKeys);
+    const bool rot = n_band == P && P > kHome;
     int bs0 = 0, hlo = 0, hhi = 0;
     if (rot) {
         const int a0 = (gbase / kStageKeys) % P;  // gbase >= 0 here (a multiple of 64)
         bs0 = a0 == 0 ? 0 : P - a0;                 // grid stage of the first block = 0 mod P
         const int h0 = nb >= bs0 ? nb - bs0 : nb - bs0 + P;  // rotated positions of the home stages
         const int h1 = h0 + 1 == P ? 0 : h0 + 1;
-        hlo = min(h0, h1);
-        hhi = max(h0, h1);
+        hlo = kHome == 2 ? min(h0, h1) : h0;
+        hhi = kHome == 2 ? max(h0, h1) : P;  // one home stage: no second position to skip
     }
     // Grid stage of the u-th band stage in processing order.
     auto band_bs = [&](int u) __attribute__((always_inline)) {
-        if (!rot) return u < nb ? u : (u < nb + na ? u + 2 : u - na);
-        if (u >= P - 2) return nb + u - (P - 2);
+        if (!rot) return u < nb ? u : (u < nb + na ? u + kHome : u - na);
+        if (u >= P - kHome) return nb + u - (P - kHome);
         int k = u;
         if (k >= hlo) ++k;
         if (k >= hhi) ++k;
@@ -763,7 +784,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         glob_row[gi] = vpos;
         if (gi < kGlobalQueriesPerBlock) glob_g[gi] = g;
     }
-    if (tid < kRowsPerBlock / 32) row_glob[tid] = 0u;
+    if (tid < kRows / 32) row_glob[tid] = 0u;
     // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ...
     auto fill_band_masks = [&](int W) __attribute__((always_inline)) {
         constexpr int kPer = kMaskWindow / kWaves, kGroup = 4;
@@ -797,7 +818,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         }
     for (int gi = tid; gi < ng; gi += kThreads) {
         const int vr = glob_row[gi] - r0;
-        if (vr >= 0 && vr < kRowsPerBlock) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
+        if (vr >= 0 && vr < kRows) atomicOr(&row_glob[vr >> 5], 1u << (vr & 31));
     }
     if (kRandom)  // invalid keys of random stage j: past the end, padded or global
         for (int j = wv; j < n_rst; j += kWaves) {
@@ -818,6 +839,8 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     state_init(st);
     typename T::Lane lo;
     T::lane_offsets(lo, lane);
+    // kSplit: the wave reads only sub-tile kh of each stage, addressed as sub-tile 0.
+    if (kSplit) T::shift_lane(lo, kh);
 
     // The first stages are copied while the Q operand loads are still in flight;
     // every register load (Q operand, masks) completes at the wait below, so the
@@ -852,7 +875,16 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         const int ks = rstage ? kRandomBlock * rnd_block(j) : 0;
         const uint64_t inv = uniform64(rstage ? rnd_inv[j] : glob_mask[t]);
         const bool wave_on = !rstage || (wv >> 1) == (j < na_r ? 0 : 1);
-        if (rows_live && wave_on && inv != ~0ull) {
+        if (kSplit) {
+            const int sub = kh;
+            const uint32_t inv32 = (uint32_t)(inv >> (32 * sub));
+            if (rows_live && inv32 != ~0u) {
+                const int goff = kStageKeys * t + 32 * sub + 8 * h2;
+                const int bbase = 32 * sub + 8 * h2 - qv + w;
+                const int climit = !causal ? 1 << 30 : gcnt - goff;
+                sub_step<T>(st, slot, 0, lo, qop, 2, inv32, h2, bbase, span, glob_pos + goff, w - qv, climit, nullptr);
+            }
+        } else if (rows_live && wave_on && inv != ~0ull) {
             // Both sub-tiles in straight-line code: the second one's operand reads and
             // products can be scheduled against the first one's softmax.
 #pragma unroll
@@ -879,7 +911,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     // sub-tile j for jlo <= j <= jhi, every row has all 32 for ilo <= j <= ihi.  Per
     // sub-tile the wave takes one of three uniform branches: skipped, interior with every
     // key valid (no mask), or masked (band edge, invalid keys).
-    const int ja = 2 * nb + wv;
+    const int ja = 2 * nb + rb;
     const int jlo = ja - ((w + 31) >> 5), jhi = ja + ((wr + 31) >> 5);
     const int ilo = ja - ((w - 31) >> 5), ihi = ja + ((wr - 31) >> 5);
     // Copies of band stage u into ring slot sl; returns its invalid-key bits and sets
@@ -923,6 +955,15 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         if (!rows_live) return;
         const char* slot = ring + SL * T::kStageBytes;
         const int j0 = (ks - gbase) >> 5;
+        if constexpr (kSplit) {
+            const int j = j0 + kh;
+            const uint32_t inv32 = (uint32_t)(inv >> (32 * kh));
+            if (j < jlo || j > jhi || inv32 == ~0u) return;
+            const int bbase = ks + 32 * kh + 8 * h2 - qv + w;
+            const int mode = (j >= ilo && j <= ihi && inv32 == 0u) ? 0 : 1;
+            sub_step<T>(st, slot, 0, lo, qop, mode, inv32, h2, bbase, span, nullptr, 0, 1 << 30, nullptr);
+            return;
+        }
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int j = j0 + sub;
@@ -947,10 +988,36 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         if (t < n_st) band_step(t, S0{});
     }
 
+    if constexpr (kSplit) {
+        // The odd wave of each row block hands its state (offset, weight sum, 32 output
+        // values per lane) to the even one through the ring slot of the second-to-last
+        // stage, which every wave is done with; the even wave combines the two
+        // log-sum-exp style and stores the rows.
+        __shared__ float x_ml[2][2][64];
+        float* xo = reinterpret_cast<float*>(ring + (n_st & 1) * T::kStageBytes);  // [2 rb][32][64 lanes]
+        if (kh == 1) {
+            x_ml[rb][0][lane] = state_offset(st);
+            x_ml[rb][1][lane] = st.l;
+            for (int db = 0; db < 2; ++db)
+                for (int i = 0; i < 16; ++i) xo[(rb * 32 + db * 16 + i) * 64 + lane] = st.o[db][i];
+        }
+        barrier_lds();
+        if (kh == 0) {
+            const float c1 = x_ml[rb][0][lane], l1 = x_ml[rb][1][lane];
+            const float c0 = state_offset(st);
+            const float m = fmaxf(c0, c1);
+            const float M = m == kNegInf ? 0.f : m;  // both empty: weights 0, sum 0
+            const float a0 = fast_exp2(c0 - M), a1 = fast_exp2(c1 - M);
+            st.l = st.l * a0 + l1 * a1;
+            for (int db = 0; db < 2; ++db)
+                for (int i = 0; i < 16; ++i) st.o[db][i] = st.o[db][i] * a0 + xo[(rb * 32 + db * 16 + i) * 64 + lane] * a1;
+            st.cofs = M;
+        }
+    }
     const float scale = st.l > 0.f ? 1.f / st.l : 0.f;
     typename T::RowOut ro;
     T::pack_row(ro, st.o, scale);
-    if (qv < Lr) {
+    if (qv < Lr && kh == 0) {
         const int row = r + qv * dil;
         const int vr = qv - r0;  // global rows are written by the merge
         if (!((row_glob[vr >> 5] >> (vr & 31)) & 1u)) {
@@ -968,9 +1035,10 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     // unless the global rows have their own key and value projections.
     __shared__ float red_ml[kWaves][32][2];
     float* red_o = reinterpret_cast<float*>(ring);  // kWaves x 32 x 64 floats = 32 KiB
-    const int home_end = min(Lr, r0 + kRowsPerBlock);
+    const int home_end = min(Lr, r0 + kRows);
     const size_t part0 = ((size_t)bh * tph + t_in) * p.n_gblk * kGlobalQueriesPerBlock;
-    const int hs = wv >> 1, hsub = wv & 1;  // wave wv folds home keys 32*wv .. 32*wv+31
+    // wave wv folds home keys 32*wv .. 32*wv+31 (kSplit: waves 0 and 1, the tile's 64)
+    const int hs = kSplit ? 0 : wv >> 1, hsub = kSplit ? kh : wv & 1;
     const int n_gblk_b = (ng + kGlobalQueriesPerBlock - 1) / kGlobalQueriesPerBlock;  // this sequence's blocks
     for (int gb = 0; gb < n_gblk_b; ++gb) {
         typename T::QOp gop;
@@ -984,19 +1052,19 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         }
         T::scale_q(gop);
         if (gb == 0 && !sep) {
-            const int u = n_band - 2 + hs;
+            const int u = n_band - kHome + hs;
             hslot = ring + ((n_lst + u) % T::kNS) * T::kStageBytes;
             inv32 = (uint32_t)(band_invalid(u) >> (32 * hsub));
         } else {
-            uint64_t hinv[2];
-            for (int j = 0; j < 2; ++j) {
+            uint64_t hinv[2] = {~0ull, ~0ull};
+            for (int j = 0; j < kHome; ++j) {
                 const int key = r0 + kStageKeys * j + lane;
                 bool ok = key < home_end;
                 if (ok && pad) ok = pad[r + key * dil] == 0;
                 hinv[j] = ~ballot64(ok);
             }
             __syncthreads();  // the ring is free
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kHome; ++j) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
                 T::dma_stage(ring + j * T::kStageBytes, KG, VG, rs,
@@ -1007,6 +1075,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             hslot = ring + hs * T::kStageBytes;
             inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * hsub));
         }
+        if (kSplit && rb == 1) inv32 = ~0u;  // the tile's 64 home keys are waves 0 and 1's
         State gs;
         state_init(gs);
         if (inv32 != ~0u) {
@@ -1016,9 +1085,11 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                 const int g = gq < ng ? p.g[gofs + gq] : -1;
                 const int vlim = g >= r ? (g - r) / dil : -1;
                 const int kss = r0 + kStageKeys * hs + 32 * hsub;
-                sub_step<T>(gs, hslot, hsub, lo, gop, 1, inv32, h2, kss + 8 * h2 - vlim + kLargeW, kLargeW, nullptr, 0);
+                sub_step<T>(gs, hslot, kSplit ? 0 : hsub, lo, gop, 1, inv32, h2, kss + 8 * h2 - vlim + kLargeW, kLargeW,
+                            nullptr, 0);
             } else {
-                sub_step<T>(gs, hslot, hsub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0, 2 * kLargeW, nullptr, 0);
+                sub_step<T>(gs, hslot, kSplit ? 0 : hsub, lo, gop, inv32 != 0u ? 1 : 0, inv32, h2, 0, 2 * kLargeW,
+                            nullptr, 0);
             }
         }
         __syncthreads();  // done with the staged keys: the ring now holds the reduction
@@ -1091,7 +1162,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const int tph, 
     const int dil = kDilU ? dil_u : p.dil[h];
     const int bh = bseq * H + h;
     const int W = merge_waves(tph, kMergeChunk, kMergeWaves);  // = blockDim.x / 64
-    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + kRowsPerBlock - 1) / kRowsPerBlock;  // unused when dil == 1
+    const int rows = p.rows_per_block;
+    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + rows - 1) / rows;  // unused when dil == 1
     // gi < n_g <= n_gq: the partial loads below stay in bounds even for a sequence with
     // fewer globals, whose work-groups drop what they loaded and return after the loop.
     const size_t base = (size_t)bh * tph * n_gq + gi;
@@ -1107,7 +1179,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const int tph, 
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
             const int t = (c0 + j) * W + wv;
-            ex[j] = t < tph && tile_exists(t, tpr, dil, L, kRowsPerBlock);
+            ex[j] = t < tph && tile_exists(t, tpr, dil, L, rows);
         }
         __builtin_amdgcn_sched_barrier(0);  // every test before the first load
 #pragma unroll
@@ -1191,15 +1263,22 @@ hipError_t static_scratch(void** ptr) {
 namespace {
 template <class T, bool kCausal, bool kBias, bool kRandom>
 void launch_band_t(const Params& p, int blocks, hipStream_t s) {
+    if constexpr (!kBias && !kRandom) {
+        if (p.rows_per_block == kSplitRows && !p.strided) {
+            (void)launch_kernel(band_kernel<T, kCausal, false, false, false, true>, dim3(blocks), dim3(kThreads), s,
+                                blocks, p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.B, p);
+            return;
+        }
+    }
     if constexpr (std::is_same_v<T, Bf16>) {
         if (p.strided) {
             (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom, true>, dim3(blocks), dim3(kThreads), s, blocks,
-                                p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p);
+                                p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.B, p);
             return;
         }
     }
     (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom>, dim3(blocks), dim3(kThreads), s, blocks,
-                        p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p);
+                        p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.B, p);
 }
 }  // namespace
 

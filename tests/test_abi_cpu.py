@@ -254,6 +254,21 @@ def test_global_mode_validation():
 
 
 @needs_lib
+def test_tile_rows_validation():
+    lib = binding.load_library()
+    h = ctypes.c_void_p()
+    assert lib.lf_attn_create(ctypes.byref(h), 1) == 0
+    try:
+        for rows in (0, 64, 128, 0):
+            assert lib.lf_attn_set_tile_rows(h, rows) == 0, rows
+        for rows in (-1, 32, 96, 256):
+            assert lib.lf_attn_set_tile_rows(h, rows) == 1 and b"tile rows" in lib.lf_attn_last_error(h), rows
+        assert lib.lf_attn_set_tile_rows(None, 64) == 1
+    finally:
+        lib.lf_attn_destroy(h)
+
+
+@needs_lib
 def test_null_handle():
     lib = binding.load_library()
     assert lib.lf_attn_forward(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None, None, 0, None, None) == 1

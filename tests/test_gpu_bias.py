@@ -103,15 +103,18 @@ def test_bias_forward(case):
 
 
 def test_bias_zero_table_is_unbiased():
-    """A zero table gives the unbiased result bit for bit (a zero add changes no score)."""
+    """A zero table gives the unbiased result bit for bit (a zero add changes no score)
+    on the same tiling (the biased forward always runs 128-row work-groups)."""
     from sparse_long_sequence_longformer_amd import binding
 
     B, H, L, w, dil, G = 1, 2, 600, 40, [1, 2], [0, 299]
     q, k, v = make_custom(B, H, L, dtype="bf16", seed=77)
     qd, kd, vd = to_dev(q, k, v)
     zero = torch.zeros(H, 2 * w + 1, dtype=torch.float32, device="cuda")
-    a = binding.forward(qd, kd, vd, w, dil, G, bias=zero)
-    b = binding.forward(qd, kd, vd, w, dil, G)
+    h = binding.LfAttn("bf16")
+    h.set_tile_rows(128)
+    a = binding.forward(qd, kd, vd, w, dil, G, bias=zero, handle=h)
+    b = binding.forward(qd, kd, vd, w, dil, G, handle=h)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
