@@ -768,6 +768,34 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     uint64_t inv_next = 0ull;  // invalid-key bits of the next band stage, from its copy
     if (early) inv_next = issue(0, kAllParts);
 
+    // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ... of
+    // the stages that exist; every pad load of a window is issued before the first is
+    // used (the ballots), and those of window 0 before the global slots' own loads.
+    constexpr int kPadWords = kMaskWindow / kWaves;
+    auto load_band_pad = [&](int W, uint32_t* flag) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kPadWords; ++j) {
+            const int bs = W * kMaskWindow + wv + kWaves * j;
+            flag[j] = 1u;
+            if (bs < n_band) {
+                const int key = stage_key(bs) + lane;
+                if (key >= kb0 && key < kend) flag[j] = pad[r + key * dil];
+            }
+        }
+    };
+    auto store_band_masks = [&](int W, const uint32_t* flag) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kPadWords; ++j) {
+            const int bs = W * kMaskWindow + wv + kWaves * j;
+            if (bs < n_band) {
+                const uint64_t inv = ballot64(flag[j] != 0);
+                if (lane == 0) band_mask[bs % kMaskRing] = inv;
+            }
+        }
+    };
+    uint32_t pflag[kPadWords];
+    if (pad) load_band_pad(0, pflag);
+
     // Global slots: source row (or -1 if unused/padded) and in-window position; slot gi
     // is thread gi's.
     if (const int gi = tid; gi < n_gst * kStageKeys) {
@@ -785,10 +813,12 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         if (gi < kGlobalQueriesPerBlock) glob_g[gi] = g;
     }
     if (tid < kRows / 32) row_glob[tid] = 0u;
-    // Pad masks of band stages [64*W, 64*W + 64): wave wv builds words wv, wv+4, ...
+    // Windows after the first (a band of more than 64 stages), from inside the stage
+    // loop: four words at a time, which keeps the registers of the loads few.
     auto fill_band_masks = [&](int W) __attribute__((always_inline)) {
-        constexpr int kPer = kMaskWindow / kWaves, kGroup = 4;
-        for (int j0 = 0; j0 < kPer; j0 += kGroup) {
+        constexpr int kGroup = 4;
+        for (int j0 = 0; j0 < kPadWords; j0 += kGroup) {
+            if (W * kMaskWindow + wv + kWaves * j0 >= n_band) break;
             uint32_t flag[kGroup];
             for (int j = 0; j < kGroup; ++j) {
                 const int bs = W * kMaskWindow + wv + kWaves * (j0 + j);
@@ -802,7 +832,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             }
         }
     };
-    if (pad) fill_band_masks(0);
+    if (pad) store_band_masks(0, pflag);
     if (kBias) {
         const float* tab = p.bias + (size_t)h * (2 * p.bias_w + 1) + p.bias_w;  // entry of offset 0
         for (int t = tid; t < 2 * w + 1 + 2 * kBiasPad; t += kThreads) {
@@ -1063,7 +1093,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                 if (ok && pad) ok = pad[r + key * dil] == 0;
                 hinv[j] = ~ballot64(ok);
             }
-            __syncthreads();  // the ring is free
+            barrier_lds();  // the ring is free (every wave's reads of it are done)
             for (int j = 0; j < kHome; ++j) {
                 const uint64_t iv = hinv[j];
                 const int ks = r0 + kStageKeys * j;
@@ -1071,7 +1101,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                              [&](int kk) __attribute__((always_inline)) { return ((iv >> kk) & 1) ? -1 : r + (ks + kk) * dil; }, wv, lane);
             }
             wait_vmcnt<0>();
-            __syncthreads();
+            barrier_lds();
             hslot = ring + hs * T::kStageBytes;
             inv32 = (uint32_t)((hs ? hinv[1] : hinv[0]) >> (32 * hsub));
         }
@@ -1092,7 +1122,9 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                             nullptr, 0);
             }
         }
-        __syncthreads();  // done with the staged keys: the ring now holds the reduction
+        // Done with the staged keys: the ring now holds the reduction.  The barriers of
+        // this pass order LDS accesses only; the output rows stored above stay in flight.
+        barrier_lds();
         if (lane < 32) {  // partial relative to its offset (-inf when it holds no weight)
             red_ml[wv][lane][0] = state_offset(gs);
             red_ml[wv][lane][1] = gs.l;
@@ -1105,7 +1137,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                 for (int i = 0; i < 16; ++i)
                     red_o[(wv * 32 + (lane & 31)) * 64 + ((32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)) ^ (lane & 31))] =
                         gs.o[db][i];
-        __syncthreads();
+        barrier_lds();
         {
             const int q = tid >> 3, dc = tid & 7;  // 32 queries x 8 column chunks
             const int gq2 = gb * kGlobalQueriesPerBlock + q;
@@ -1132,7 +1164,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                 *reinterpret_cast<f32x4*>(p.ws_acc + idx * 64 + 8 * dc + 4) = o4[1];
             }
         }
-        __syncthreads();
+        if (gb + 1 < n_gblk_b) barrier_lds();  // red_ml and the ring are reused
     }
 
 }
