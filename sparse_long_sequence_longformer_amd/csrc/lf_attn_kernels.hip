@@ -90,6 +90,11 @@ struct Bf16 {
         for (int kb = 0; kb < 4; ++kb)
             q.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
     }
+    // The same from a row staged in LDS (LDS reads only: a generic load would also wait
+    // for the wave's outstanding stores).
+    __device__ __forceinline__ static void load_q_lds(QOp& q, const char* row, int h2) {
+        for (int kb = 0; kb < 4; ++kb) q.v[kb] = __builtin_bit_cast(bf16x8, *LF_LDS(const u32x4, row + 32 * kb + 16 * h2));
+    }
     __device__ __forceinline__ static void scale_q(QOp& q) {
         for (int kb = 0; kb < 4; ++kb) {
             const f32x8 f = __builtin_convertvector(q.v[kb], f32x8);
@@ -286,6 +291,12 @@ struct F32 {
         if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
         for (int t4 = 0; t4 < 8; ++t4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4);
+            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
+        }
+    }
+    __device__ __forceinline__ static void load_q_lds(QOp& q, const char* row, int h2) {
+        for (int t4 = 0; t4 < 8; ++t4) {
+            const f32x4 x = *LF_LDS(const f32x4, row + 128 * h2 + 16 * t4);
             for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
         }
     }
@@ -783,15 +794,21 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             }
         }
     };
+    // Also whether any of this wave's words has a valid key (a band longer than one
+    // window counts as live).
+    __shared__ uint32_t band_live[kWaves];
     auto store_band_masks = [&](int W, const uint32_t* flag) __attribute__((always_inline)) {
+        bool live = n_band > kMaskWindow;
 #pragma unroll
         for (int j = 0; j < kPadWords; ++j) {
             const int bs = W * kMaskWindow + wv + kWaves * j;
             if (bs < n_band) {
                 const uint64_t inv = ballot64(flag[j] != 0);
                 if (lane == 0) band_mask[bs % kMaskRing] = inv;
+                live |= inv != ~0ull;
             }
         }
+        if (lane == 0) band_live[wv] = live;
     };
     uint32_t pflag[kPadWords];
     if (pad) load_band_pad(0, pflag);
@@ -864,6 +881,11 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     barrier_lds();
     // One-sided variant: the global slots at or before this lane's row.
     const int gcnt = causal ? count_le(glob_abs, ng, r + qv * dil) : 0;
+    // A band whose keys are all padded (rows past a sequence's end by more than w) is
+    // neither copied nor visited: stages [0, n_run) are the ones run.  Its home keys
+    // are padded too, so the global-row pass below has nothing to fold either.
+    const bool band_dead = pad && !(band_live[0] | band_live[1] | band_live[2] | band_live[3]);
+    const int n_run = band_dead ? n_lst : n_st;
 
     State st;
     state_init(st);
@@ -877,7 +899,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     // compiler's own waits inside the loop have nothing left to wait for (an
     // in-loop vmcnt wait would also drain the stage copies in flight).
     for (int s = early ? 1 : 0; s < T::kNS - 1; ++s)
-        if (s < n_st) {
+        if (s < n_run) {
             const uint64_t x = issue(s, kAllParts);
             if (s == 0) inv_next = x;
         }
@@ -891,7 +913,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         wait_stage<T>(0);
         barrier_nofence();
         // The next stage: listed, or band stage 0 (whose pad masks are already built).
-        if (t + 1 < n_st) inv_next = issue(t + 1, kAllParts);
+        if (t + 1 < n_run) inv_next = issue(t + 1, kAllParts);
         if (t == 0 && ng > 0) {  // Q rows of the first 32 global queries, for (c)
             const Elem* zero = reinterpret_cast<const Elem*>(g_zero_row);
             T::dma_rows(gq_rows, [&](int j) __attribute__((always_inline)) { const int g = glob_g[j]; return g >= 0 ? QG + (size_t)g * rs : zero; },
@@ -974,7 +996,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         const int ks = ks_next;
         wait_vmcnt<0>();
         barrier_nofence();
-        if (t + 1 < n_st) {
+        if (t + 1 < n_run) {
             const int bn = t + 1 - n_lst;
             if (pad && bn % kMaskWindow == 0) {  // bn > 0: band stage 0 is never issued here
                 fill_band_masks(bn / kMaskWindow);
@@ -1010,21 +1032,21 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
         int t = n_gen;
-        if (t < n_st && (t & 1)) band_step(t++, S1{});
-        for (; t + 1 < n_st; t += 2) {
+        if (t < n_run && (t & 1)) band_step(t++, S1{});
+        for (; t + 1 < n_run; t += 2) {
             band_step(t, S0{});
             band_step(t + 1, S1{});
         }
-        if (t < n_st) band_step(t, S0{});
+        if (t < n_run) band_step(t, S0{});
     }
 
     if constexpr (kSplit) {
         // The odd wave of each row block hands its state (offset, weight sum, 32 output
         // values per lane) to the even one through the ring slot of the second-to-last
-        // stage, which every wave is done with; the even wave combines the two
+        // stage run, which every wave is done with; the even wave combines the two
         // log-sum-exp style and stores the rows.
         __shared__ float x_ml[2][2][64];
-        float* xo = reinterpret_cast<float*>(ring + (n_st & 1) * T::kStageBytes);  // [2 rb][32][64 lanes]
+        float* xo = reinterpret_cast<float*>(ring + (n_run & 1) * T::kStageBytes);  // [2 rb][32][64 lanes]
         if (kh == 1) {
             x_ml[rb][0][lane] = state_offset(st);
             x_ml[rb][1][lane] = st.l;
@@ -1075,7 +1097,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         const char* hslot;
         uint32_t inv32;
         if (gb == 0) {
-            T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
+            T::load_q_lds(gop, gq_rows + (lane & 31) * T::kRowBytes, h2);
         } else {
             const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
             T::load_q(gop, gq < ng ? QG + (size_t)p.g[gofs + gq] * rs : nullptr, h2);
