@@ -90,11 +90,6 @@ struct Bf16 {
         for (int kb = 0; kb < 4; ++kb)
             q.v[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * kb + 8 * h2));
     }
-    // The same from a row staged in LDS (LDS reads only: a generic load would also wait
-    // for the wave's outstanding stores).
-    __device__ __forceinline__ static void load_q_lds(QOp& q, const char* row, int h2) {
-        for (int kb = 0; kb < 4; ++kb) q.v[kb] = __builtin_bit_cast(bf16x8, *LF_LDS(const u32x4, row + 32 * kb + 16 * h2));
-    }
     __device__ __forceinline__ static void scale_q(QOp& q) {
         for (int kb = 0; kb < 4; ++kb) {
             const f32x8 f = __builtin_convertvector(q.v[kb], f32x8);
@@ -291,12 +286,6 @@ struct F32 {
         if (!row) row = reinterpret_cast<const Elem*>(g_zero_row);
         for (int t4 = 0; t4 < 8; ++t4) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(row + 32 * h2 + 4 * t4);
-            for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
-        }
-    }
-    __device__ __forceinline__ static void load_q_lds(QOp& q, const char* row, int h2) {
-        for (int t4 = 0; t4 < 8; ++t4) {
-            const f32x4 x = *LF_LDS(const f32x4, row + 128 * h2 + 16 * t4);
             for (int e = 0; e < 4; ++e) q.v[4 * t4 + e] = x[e];
         }
     }
@@ -1097,7 +1086,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         const char* hslot;
         uint32_t inv32;
         if (gb == 0) {
-            T::load_q_lds(gop, gq_rows + (lane & 31) * T::kRowBytes, h2);
+            T::load_q(gop, reinterpret_cast<const Elem*>(gq_rows) + (size_t)(lane & 31) * 64, h2);
         } else {
             const int gq = gb * kGlobalQueriesPerBlock + (lane & 31);
             T::load_q(gop, gq < ng ? QG + (size_t)p.g[gofs + gq] * rs : nullptr, h2);
