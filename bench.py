@@ -78,6 +78,8 @@ def parse():
                     help="also time the forward captured in a HIP graph and replayed")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (lf_attn_backward) instead of the forward")
+    ap.add_argument("--tile-rows", type=int, default=0, choices=(0, 64, 128),
+                    help="forward rows per work-group (lf_attn_set_tile_rows; 0: the library chooses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--trials", type=int, default=15, help="timing trials after the main window (median/min/p90)")
@@ -189,8 +191,10 @@ def split_tiling(wl, args) -> bool:
     position bias or random blocks)."""
     import torch
 
-    if args.bias or args.random or args.layer:
+    if args.bias or args.random or args.layer or args.tile_rows == 128:
         return False
+    if args.tile_rows == 64:
+        return True
     tiles = 0
     for d in wl.dil_list():
         tiles = max(tiles, d * (((wl.L + d - 1) // d + 127) // 128))
@@ -245,6 +249,7 @@ def main():
     padd = None if pad is None else torch.from_numpy(pad).to(dev)
     out = torch.empty_like(qd)
     handle = binding.LfAttn(wl.dtype)
+    handle.set_tile_rows(args.tile_rows)
     if args.causal:
         handle.set_causal(True)
     bias_tab = None
@@ -386,6 +391,7 @@ def main():
             "window": "one-sided" if args.causal else "symmetric",
             "position_bias": f"N(0, {args.bias:g}^2) table" if args.bias else None,
             "random_blocks": f"{args.random} of 64 keys per (head, query block)" if args.random else None,
+            "tile_rows": 64 if split_tiling(wl, args) else 128,
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "attended_pairs": pairs.total,

@@ -77,12 +77,22 @@ def _refill_pad():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_refill_forward(dtype):
+    """Both forward tilings (64-row split work-groups, which the library picks for this
+    grid, and 128-row ones) against one oracle result."""
+    from sparse_long_sequence_longformer_amd import binding
+
     log(f"case refill forward {dtype}: B={REFILL_B} H={REFILL_H} L={REFILL_L} w={REFILL_W} dil={REFILL_DIL}")
     q, k, v = make_custom(REFILL_B, REFILL_H, REFILL_L, dtype=dtype, seed=31)
     pad = _refill_pad()
-    got = run_gpu(q, k, v, REFILL_W, REFILL_DIL, REFILL_G, pad)
     ref = oracle_full(q, k, v, REFILL_W, REFILL_DIL, REFILL_G, pad)
-    compare(got, ref, dtype, f"refill forward {dtype}")
+    qd, kd, vd = to_dev(q, k, v)
+    padd = torch.from_numpy(pad).to("cuda")
+    for rows in (64, 128):
+        h = binding.LfAttn(dtype)
+        h.set_tile_rows(rows)
+        got = binding.forward(qd, kd, vd, REFILL_W, REFILL_DIL, REFILL_G, padd, handle=h)
+        torch.cuda.synchronize()
+        compare(got.cpu(), ref, dtype, f"refill forward {dtype} rows={rows}")
 
 
 def test_refill_backward():
