@@ -1140,14 +1140,18 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             red_ml[wv][lane][0] = state_offset(gs);
             red_ml[wv][lane][1] = gs.l;
         }
-        // Column c of query q sits at q*64 + (c ^ q%32): the 32 queries of one store,
-        // and the 8 queries x 8 column chunks of one load below, hit distinct banks.
-        // Slots past the sequence's global count are never read.
-        if (gb * kGlobalQueriesPerBlock + (lane & 31) < ng)
+        // Four columns 4c .. 4c+3 of query q (a 16-byte chunk c) sit at chunk c ^ (q % 16)
+        // of row q: one 16-byte store per accumulator group, two 16-byte loads per
+        // column block below.  Slots past the sequence's global count are never read.
+        if (gb * kGlobalQueriesPerBlock + (lane & 31) < ng) {
+            const int q = lane & 31;
             for (int db = 0; db < 2; ++db)
-                for (int i = 0; i < 16; ++i)
-                    red_o[(wv * 32 + (lane & 31)) * 64 + ((32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3)) ^ (lane & 31))] =
-                        gs.o[db][i];
+                for (int m = 0; m < 4; ++m) {
+                    const int c = 8 * db + 2 * m + h2;  // columns 32 db + 8 m + 4 h2 .. + 3
+                    *reinterpret_cast<f32x4*>(red_o + (wv * 32 + q) * 64 + 4 * (c ^ (q & 15))) =
+                        f32x4{gs.o[db][4 * m], gs.o[db][4 * m + 1], gs.o[db][4 * m + 2], gs.o[db][4 * m + 3]};
+                }
+        }
         barrier_lds();
         {
             const int q = tid >> 3, dc = tid & 7;  // 32 queries x 8 column chunks
@@ -1165,12 +1169,10 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
                     p.ws_ml[2 * idx] = M;
                     p.ws_ml[2 * idx + 1] = l;
                 }
-                f32x4 o4[2];
-                for (int j = 0; j < 8; ++j) {
-                    float o = 0.f;
-                    for (int x = 0; x < kWaves; ++x) o += red_o[(x * 32 + q) * 64 + ((8 * dc + j) ^ q)] * e[x];
-                    o4[j >> 2][j & 3] = o;
-                }
+                f32x4 o4[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+                for (int x = 0; x < kWaves; ++x)
+                    for (int u = 0; u < 2; ++u)
+                        o4[u] += *reinterpret_cast<const f32x4*>(red_o + (x * 32 + q) * 64 + 4 * ((2 * dc + u) ^ (q & 15))) * e[x];
                 *reinterpret_cast<f32x4*>(p.ws_acc + idx * 64 + 8 * dc) = o4[0];
                 *reinterpret_cast<f32x4*>(p.ws_acc + idx * 64 + 8 * dc + 4) = o4[1];
             }
