@@ -1035,12 +1035,15 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         // stage run, which every wave is done with; the even wave combines the two
         // log-sum-exp style and stores the rows.
         __shared__ float x_ml[2][2][64];
-        float* xo = reinterpret_cast<float*>(ring + (n_run & 1) * T::kStageBytes);  // [2 rb][32][64 lanes]
+        // [2 rb][64 lanes][8 chunks of 4 values], chunk k of a lane at k ^ (lane % 8)
+        float* xo = reinterpret_cast<float*>(ring + (n_run & 1) * T::kStageBytes);
         if (kh == 1) {
             x_ml[rb][0][lane] = state_offset(st);
             x_ml[rb][1][lane] = st.l;
-            for (int db = 0; db < 2; ++db)
-                for (int i = 0; i < 16; ++i) xo[(rb * 32 + db * 16 + i) * 64 + lane] = st.o[db][i];
+            for (int k = 0; k < 8; ++k)
+                *reinterpret_cast<f32x4*>(xo + ((rb * 64 + lane) * 8 + (k ^ (lane & 7))) * 4) =
+                    f32x4{st.o[k >> 2][4 * (k & 3)], st.o[k >> 2][4 * (k & 3) + 1], st.o[k >> 2][4 * (k & 3) + 2],
+                          st.o[k >> 2][4 * (k & 3) + 3]};
         }
         barrier_lds();
         if (kh == 0) {
@@ -1050,8 +1053,10 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
             const float M = m == kNegInf ? 0.f : m;  // both empty: weights 0, sum 0
             const float a0 = fast_exp2(c0 - M), a1 = fast_exp2(c1 - M);
             st.l = st.l * a0 + l1 * a1;
-            for (int db = 0; db < 2; ++db)
-                for (int i = 0; i < 16; ++i) st.o[db][i] = st.o[db][i] * a0 + xo[(rb * 32 + db * 16 + i) * 64 + lane] * a1;
+            for (int k = 0; k < 8; ++k) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(xo + ((rb * 64 + lane) * 8 + (k ^ (lane & 7))) * 4);
+                for (int j = 0; j < 4; ++j) st.o[k >> 2][4 * (k & 3) + j] = st.o[k >> 2][4 * (k & 3) + j] * a0 + x[j] * a1;
+            }
             st.cofs = M;
         }
     }
