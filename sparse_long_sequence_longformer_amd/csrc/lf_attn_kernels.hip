@@ -613,7 +613,22 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     const int bh = b * H + h;
     const int dil = head_dil(dil_u, p.dil, h);
     int r, Lr, r0;  // residue class, its length, the tile's first class row
-    if (!decode_tile<kRows>(t_in, L, dil, r, Lr, r0)) return;
+    if (!decode_tile<kRows>(t_in, L, dil, r, Lr, r0)) {
+        // A slot without a tile (a head or residue class with fewer tiles than the
+        // grid's per-head count): its global-row partials say "no weight", so the merge
+        // reads every slot without working out which hold tiles.
+        if (p.n_g > 0) {
+            const int n = p.n_gblk * kGlobalQueriesPerBlock;
+            const size_t part0 = ((size_t)bh * tph + t_in) * n;
+            for (int i = tid; i < n; i += kThreads) {
+                p.ws_ml[2 * (part0 + i)] = kNegInf;
+                p.ws_ml[2 * (part0 + i) + 1] = 0.f;
+            }
+            for (int i = tid; i < n * 16; i += kThreads)
+                reinterpret_cast<f32x4*>(p.ws_acc + part0 * 64)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
 
     // q, k, v (and q_g, k_g, v_g): row i of (b, h) at b*s_b + h*s_h + i*rs elements,
     // out at b*o_b + h*o_h + i*o_r (kStrided); else [B][H][L][64] with constant strides.
@@ -1190,17 +1205,18 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
 // (d) Merge of the global-row partials: one work-group of W <= kMergeWaves waves per
 // (global query, h, b) (grid x, y, z), lane = output column (W = blockDim / 64, chosen
 // so that one chunk per wave covers a head's tiles).  Wave x takes tiles x, x + W, ...
-// in chunks of kMergeChunk whose loads are issued together (absent tiles read tile 0
-// and are dropped after the load, so there is no branch between the loads); within a
-// chunk the maximum comes first and the weighted sums are added in tile order, and the
-// wave states are combined in wave order: the result does not depend on timing.
+// in chunks of kMergeChunk whose loads are issued together (slots past the head's tile
+// count read tile 0 and are dropped after the load, so there is no branch between the
+// loads; a slot the band grid holds no tile for carries an empty partial written by its
+// work-group, so no slot needs a test of the head's tiling); within a chunk the maximum
+// comes first and the weighted sums are added in tile order, and the wave states are
+// combined in wave order: the result does not depend on timing.
 //
 // The leading arguments (p.tiles_per_head, the partial rows per tile n_gblk * 32, p.H,
 // p.L, p.dil_u, p.ws_ml, p.ws_acc) are preloaded into scalar registers by the build, so
 // the first partial loads wait for no argument; the other arguments are read while
-// those loads are in flight.  kDilU: every head has dilation dil_u (no read of p.dil,
-// whose wait would come before the partial loads).
-template <class T, bool kDilU>
+// those loads are in flight.
+template <class T>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const int tph, const int n_gq, const int H,
                                                                  const int L, const int dil_u,
                                                                  const float* const ws_ml,
@@ -1209,11 +1225,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const int tph, 
     __shared__ float red[kMergeWaves][3][64];
     const int gi = blockIdx.x, h = blockIdx.y, bseq = blockIdx.z, d = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int dil = kDilU ? dil_u : p.dil[h];
     const int bh = bseq * H + h;
     const int W = merge_waves(tph, kMergeChunk, kMergeWaves);  // = blockDim.x / 64
-    const int rows = p.rows_per_block;
-    const int tpr = dil == 1 ? 0 : ((L + dil - 1) / dil + rows - 1) / rows;  // unused when dil == 1
     // gi < n_g <= n_gq: the partial loads below stay in bounds even for a sequence with
     // fewer globals, whose work-groups drop what they loaded and return after the loop.
     const size_t base = (size_t)bh * tph * n_gq + gi;
@@ -1229,7 +1242,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const int tph, 
 #pragma unroll
         for (int j = 0; j < kMergeChunk; ++j) {
             const int t = (c0 + j) * W + wv;
-            ex[j] = t < tph && tile_exists(t, tpr, dil, L, rows);
+            ex[j] = t < tph;  // slots without a tile hold empty partials
         }
         __builtin_amdgcn_sched_barrier(0);  // every test before the first load
 #pragma unroll
@@ -1358,13 +1371,13 @@ hipError_t launch_merge(const Params& p, int dtype, hipStream_t s) {
     const dim3 grid(p.n_g, p.H, p.B);
     const int waves = merge_waves(p.tiles_per_head, kMergeChunk, kMergeWaves);
     const int n_gq = p.n_gblk * kGlobalQueriesPerBlock;
-#define LF_MERGE(T, U)                                                                                     \
-    launch_kernel(merge_kernel<T, U>, grid, dim3(64 * waves), s, p.tiles_per_head, n_gq, p.H, p.L, p.dil_u, \
+#define LF_MERGE(T)                                                                                        \
+    launch_kernel(merge_kernel<T>, grid, dim3(64 * waves), s, p.tiles_per_head, n_gq, p.H, p.L, p.dil_u, \
                   (const float*)p.ws_ml, (const float*)p.ws_acc, p)
     if (dtype == LF_BF16) {
-        if (p.dil_u) LF_MERGE(Bf16, true); else LF_MERGE(Bf16, false);
+        LF_MERGE(Bf16);
     } else {
-        if (p.dil_u) LF_MERGE(F32, true); else LF_MERGE(F32, false);
+        LF_MERGE(F32);
     }
 #undef LF_MERGE
     return hipGetLastError();
