@@ -568,6 +568,15 @@ __device__ __forceinline__ void sub_step(State& st, const char* slot, int sub, c
 // the second (waves 2-3), one 64-key stage each.  Their keys that lie in a row's
 // window, are global, padded or past the end are masked, so each key counts once.
 
+// Dilation of head h from the band kernel's dilation code (dil_code below): the value
+// every head shares (> 0), two bits per head (< 0), or else the head's own entry.
+__device__ __forceinline__ int head_dil_code(int code, const int* dil, int h) {
+    if (code > 0) return code;
+    if (code < 0) return (((-code - 1) >> (2 * h)) & 3) + 1;
+    asm volatile("");
+    return dil[h];
+}
+
 template <class T, bool kCausal, bool kBias, bool kRandom, bool kStrided = false, bool kSplit = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const int nblk, const int tph, const int H, const int L, const int dil_u, const void* const q_arg,
@@ -611,7 +620,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
     const int j_bh = pid / tph, t_in = pid - j_bh * tph;
     const int h = j_bh / nseq, b = j_bh - h * nseq;
     const int bh = b * H + h;
-    const int dil = head_dil(dil_u, p.dil, h);
+    const int dil = head_dil_code(dil_u, p.dil, h);
     int r, Lr, r0;  // residue class, its length, the tile's first class row
     if (!decode_tile<kRows>(t_in, L, dil, r, Lr, r0)) {
         // A slot without a tile (a head or residue class with fewer tiles than the
@@ -1324,24 +1333,38 @@ hipError_t static_scratch(void** ptr) {
 }
 
 namespace {
+// The band kernel's dilation argument: the dilation every head shares; else, for at
+// most 15 heads with dilations 1..4, -(1 + sum of (dil[h] - 1) << 2h) (decoded without a
+// memory read); else 0 (each head's entry is read from the arguments).
+int dil_code(const Params& p) {
+    if (p.dil_u) return p.dil_u;
+    if (p.H > 15) return 0;
+    int packed = 0;
+    for (int h = 0; h < p.H; ++h) {
+        if (p.dil[h] < 1 || p.dil[h] > 4) return 0;
+        packed |= (p.dil[h] - 1) << (2 * h);
+    }
+    return -(1 + packed);
+}
+
 template <class T, bool kCausal, bool kBias, bool kRandom>
 void launch_band_t(const Params& p, int blocks, hipStream_t s) {
     if constexpr (!kBias && !kRandom) {
         if (p.rows_per_block == kSplitRows && !p.strided) {
             (void)launch_kernel(band_kernel<T, kCausal, false, false, false, true>, dim3(blocks), dim3(kThreads), s,
-                                blocks, p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.B, p);
+                                blocks, p.tiles_per_head, p.H, p.L, dil_code(p), p.q, p.B, p);
             return;
         }
     }
     if constexpr (std::is_same_v<T, Bf16>) {
         if (p.strided) {
             (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom, true>, dim3(blocks), dim3(kThreads), s, blocks,
-                                p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.B, p);
+                                p.tiles_per_head, p.H, p.L, dil_code(p), p.q, p.B, p);
             return;
         }
     }
     (void)launch_kernel(band_kernel<T, kCausal, kBias, kRandom>, dim3(blocks), dim3(kThreads), s, blocks,
-                        p.tiles_per_head, p.H, p.L, p.dil_u, p.q, p.B, p);
+                        p.tiles_per_head, p.H, p.L, dil_code(p), p.q, p.B, p);
 }
 }  // namespace
 
