@@ -399,8 +399,8 @@ def main():
         "kernel_ms_avg": {k2: round(v2, 6) for k2, v2 in stage_avg.items()},
         "roofline": {
             "kernel": f"lf::band_kernel<{'Bf16' if wl.dtype == 'bf16' else 'F32'}, {str(args.causal).lower()}, "
-                      f"{str(bool(args.bias)).lower()}, {str(bool(args.random)).lower()}, false"
-                      + (", false, true>" if split_tiling(wl, args) else ">"),
+                      f"{str(bool(args.bias)).lower()}, {str(bool(args.random)).lower()}, false, "
+                      f"{str(split_tiling(wl, args)).lower()}>",
             **roof,
             "traffic": traffic,
             "avg_launch_ms": round(k_avg_ms, 6),
