@@ -577,6 +577,19 @@ __device__ __forceinline__ int head_dil_code(int code, const int* dil, int h) {
     return dil[h];
 }
 
+// Global-row partials of tile slot t_in of slice bh that hold no weight (no tile, or
+// no valid home key): the merge reads every slot of a head.
+__device__ __forceinline__ void empty_partials(const Params& p, int bh, int tph, int t_in, int tid) {
+    const int n = p.n_gblk * kGlobalQueriesPerBlock;
+    const size_t part0 = ((size_t)bh * tph + t_in) * n;
+    for (int i = tid; i < n; i += kThreads) {
+        p.ws_ml[2 * (part0 + i)] = kNegInf;
+        p.ws_ml[2 * (part0 + i) + 1] = 0.f;
+    }
+    for (int i = tid; i < n * 16; i += kThreads)
+        reinterpret_cast<f32x4*>(p.ws_acc + part0 * 64)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 template <class T, bool kCausal, bool kBias, bool kRandom, bool kStrided = false, bool kSplit = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::kWavesPerEU)))
 void band_kernel(const int nblk, const int tph, const int H, const int L, const int dil_u, const void* const q_arg,
@@ -626,16 +639,7 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         // A slot without a tile (a head or residue class with fewer tiles than the
         // grid's per-head count): its global-row partials say "no weight", so the merge
         // reads every slot without working out which hold tiles.
-        if (p.n_g > 0) {
-            const int n = p.n_gblk * kGlobalQueriesPerBlock;
-            const size_t part0 = ((size_t)bh * tph + t_in) * n;
-            for (int i = tid; i < n; i += kThreads) {
-                p.ws_ml[2 * (part0 + i)] = kNegInf;
-                p.ws_ml[2 * (part0 + i) + 1] = 0.f;
-            }
-            for (int i = tid; i < n * 16; i += kThreads)
-                reinterpret_cast<f32x4*>(p.ws_acc + part0 * 64)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        if (p.n_g > 0) empty_partials(p, bh, tph, t_in, tid);
         return;
     }
 
@@ -1096,6 +1100,10 @@ void band_kernel(const int nblk, const int tph, const int H, const int L, const 
         }
     }
     if (ng == 0) return;
+    if (band_dead) {  // every home key is padded: nothing to fold
+        empty_partials(p, bh, tph, t_in, tid);
+        return;
+    }
 
     // (c) Global rows: every key belongs to exactly one work-group's "home" range
     // [r0, r0 + 128) of its class, so each work-group folds the global queries over
