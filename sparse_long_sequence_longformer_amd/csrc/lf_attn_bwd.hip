@@ -354,21 +354,22 @@ __device__ __forceinline__ f32x16 splat(float x) {
 // Uses red (32 KiB of LDS); the caller brackets it with barriers.
 __device__ __forceinline__ void wave_sum_store(float* red, const f32x16* a, int wv, int lane, int tid, float* dst,
                                                int nq) {
+    // Four columns 4c .. 4c+3 of row q (a 16-byte chunk c) sit at chunk c ^ (q % 16) of
+    // row q: one 16-byte store per accumulator group, two 16-byte loads per column block.
     const int q0 = lane & 31, h2 = lane >> 5;
     for (int db = 0; db < 2; ++db)
-        for (int i = 0; i < 16; ++i) {
-            const int c = 32 * db + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            red[(wv * 32 + q0) * 64 + (c ^ q0)] = a[db][i];
+        for (int m = 0; m < 4; ++m) {
+            const int c = 8 * db + 2 * m + h2;  // columns 32 db + 8 m + 4 h2 .. + 3
+            *reinterpret_cast<f32x4*>(red + (wv * 32 + q0) * 64 + 4 * (c ^ (q0 & 15))) =
+                f32x4{a[db][4 * m], a[db][4 * m + 1], a[db][4 * m + 2], a[db][4 * m + 3]};
         }
     __syncthreads();
     const int q = tid >> 3, dc = tid & 7;  // 32 rows x 8 column chunks
     if (q < nq) {
-        f32x4 o4[2];
-        for (int j = 0; j < 8; ++j) {
-            float o = 0.f;
-            for (int x = 0; x < kWaves; ++x) o += red[(x * 32 + q) * 64 + ((8 * dc + j) ^ q)];
-            o4[j >> 2][j & 3] = o;
-        }
+        f32x4 o4[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int x = 0; x < kWaves; ++x)
+            for (int u = 0; u < 2; ++u)
+                o4[u] += *reinterpret_cast<const f32x4*>(red + (x * 32 + q) * 64 + 4 * ((2 * dc + u) ^ (q & 15)));
         *reinterpret_cast<f32x4*>(dst + (size_t)q * 64 + 8 * dc) = o4[0];
         *reinterpret_cast<f32x4*>(dst + (size_t)q * 64 + 8 * dc + 4) = o4[1];
     }
