@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -58,16 +59,19 @@ def compile_flags() -> list[str]:
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     cc = hipcc()
-    objs = []
     tmp = LIB + ".tmp"
-    for src in SOURCES:
+
+    def compile_one(src):
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         pre = ["-mllvm", f"-amdgpu-kernarg-preload-count={PRELOAD_ARGS[src]}"] if src in PRELOAD_ARGS else []
-        cmd = [cc, *compile_flags(), *pre, *lang, "-c", path, "-o", obj]
-        _run(cmd, verbose)
-        objs.append(obj)
+        _run([cc, *compile_flags(), *pre, *lang, "-c", path, "-o", obj], verbose)
+        return obj
+
+    # the sources compile independently: one hipcc process each, at once
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     # hipBLASLt serves the layer's plain GEMMs
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, f"-L{ROCM_LIB}", "-lhipblaslt",
           f"-Wl,-rpath,{ROCM_LIB}"], verbose)
